@@ -1,0 +1,197 @@
+/*
+ * sg.h -- C ABI of sparse_gemm_layers_amd: FP8 (OCP e4m3) groupwise-scaled and
+ * 2:4-sparse linear-layer GEMMs for AMD Instinct MI355X (gfx950, CDNA4).
+ *
+ * Sources (web pages; cited by title and by position in the thread):
+ *   [I2029] CUTLASS issue #2029, "[QST] CUTLASS support for fp8 sparse matrix
+ *           (for W) multiplication for A*W=Y with GPU (SM90a/89) sparse tensor core"
+ *   [P2095] CUTLASS PR #2095, "Improvements for: Groupwise scaling along M for
+ *           FP8 gemm"
+ *   [I2058] CUTLASS issue #2058, "[QST] How to implement a fused mixed precision
+ *           matrix multiplication such as w4a4 + w16a16?"
+ *   [T3258] torchao PR #3258, "Introduce new W8A8-FP-CSR quantization API"
+ *
+ * Conventions for every entry point
+ *   - All matrices are row-major.  A leading dimension (ld*) is the distance in
+ *     ELEMENTS between consecutive rows (bytes for uint8 buffers; for packed int4
+ *     buffers it is in bytes, i.e. pairs of elements).
+ *   - Scale arrays are fp32 and addressed through two strides in floats, so both
+ *     the "M-major" layout of [P2095] (PR description: scales contiguous along M,
+ *     one column per K tile) and a row-major layout can be passed.
+ *   - Every pointer is caller-owned device memory.  The library allocates
+ *     nothing, needs no workspace, keeps no mutable global state, and may be
+ *     called from several host threads at once.
+ *   - Work is enqueued on `stream` (0 = the null stream) and runs asynchronously;
+ *     nothing is copied back to the host and no call synchronises.
+ *   - Arguments are validated on the host BEFORE any HIP call; an invalid call
+ *     returns an error status and enqueues nothing.  A launch failure reported
+ *     by the HIP runtime returns SG_ERR_HIP.
+ *   - An empty problem (rows == 0, or M == 0 or N == 0) is valid: SG_OK, nothing
+ *     is enqueued.
+ *   - Inputs must be finite; the results for NaN or infinite inputs are
+ *     unspecified (but every access stays within the described buffers).
+ */
+#ifndef SPARSE_GEMM_LAYERS_AMD_SG_H
+#define SPARSE_GEMM_LAYERS_AMD_SG_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SG_OK = 0,
+  SG_ERR_NULL = 1,        /* a required pointer is NULL                          */
+  SG_ERR_SHAPE = 2,       /* a size or leading dimension is out of range         */
+  SG_ERR_UNSUPPORTED = 3, /* granularity, dtype or output form not supported     */
+  SG_ERR_ALIGN = 4,       /* a pointer or leading dimension is misaligned        */
+  SG_ERR_HIP = 5          /* the HIP runtime reported an error at launch         */
+} sg_status;
+
+typedef enum { SG_F32 = 0, SG_BF16 = 1, SG_E4M3 = 2 } sg_dtype;
+
+/* Output form of the GEMMs.  Both compute the same numbers.
+ *   SG_OUT_Y : Y   [M, N] row-major, element (m, n) at y[m * ldy + n]
+ *   SG_OUT_YT: Y^T [N, M] row-major, element (m, n) at y[n * ldy + m]
+ * SG_OUT_YT is the swap+transpose form C^T = B^T . A^T of [I2029] (klevzoff's
+ * answer: swap the operands and flip the layout of C/D), which puts the sparse
+ * weight on the left. */
+typedef enum { SG_OUT_Y = 0, SG_OUT_YT = 1 } sg_form;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* sg_status_str(sg_status s);
+
+/* Version of this ABI; bumped on any incompatible change. */
+int sg_abi_version(void);
+
+/*
+ * sg_fp8_quant_groupwise -- per-block amax -> scale -> e4m3 codes.
+ * [P2095] hwu36's comment (ScaleGranularityM/N: 1 or 128 rows share one scale
+ * per 128-wide K block); [T3258] jcaip's review (scale must be positive, an
+ * all-zero tensor must be supported, activations are scaled then cast to
+ * float8_e4m3fn).
+ *
+ * For each block of gr rows x gc columns (the last row block may be partial):
+ *   amax = max |x|;  s = amax / 448 in fp32 (s = 1 if amax == 0);
+ *   q    = e4m3(x / s): IEEE fp32 divide, round to nearest even, saturate at
+ *          +-448, a negative value that rounds to zero gives -0 (0x80).
+ *   x   : [rows, cols], dtype x_dt (SG_F32 or SG_BF16), leading dim ldx.
+ *   gr  : 1 or 128.   gc: 128 or 64 (64 serves the compressed 2:4 values, whose
+ *         128 x 64 blocks are the 128 x 128 blocks of the dense weight).
+ *   q   : [rows, cols] e4m3 codes (uint8), leading dim ldq (bytes).
+ *   s   : block (rb, cb) at s[rb * s_stride_r + cb * s_stride_c],
+ *         rb < ceil(rows / gr), cb < cols / gc.
+ * Requires cols % gc == 0, ldx >= cols, ldq >= cols; x, q 16-byte aligned,
+ * ldx * sizeof(x_dt) and ldq multiples of 16; s 4-byte aligned.
+ */
+sg_status sg_fp8_quant_groupwise(const void* x, sg_dtype x_dt, int64_t rows, int64_t cols,
+                                 int64_t ldx, int gr, int gc, uint8_t* q, int64_t ldq, float* s,
+                                 int64_t s_stride_r, int64_t s_stride_c, hipStream_t stream);
+
+/*
+ * sg_int4_quant_groupwise -- symmetric int4 codes with one fp32 scale per
+ * (row, 128-column group), the input format of sg_mixed_gemm_add ([I2058]
+ * hyx1999: X1 and W1 are quantised to 4 bit; the page fixes no scheme).
+ *   s = amax / 7 in fp32 (1 if amax == 0);  q = clamp(rint(x / s), -7, 7),
+ *   rint = round half to even, IEEE fp32 divide.
+ *   Packed two's-complement nibbles: element 2j in the low nibble of byte j.
+ *   x : [rows, cols] (SG_F32 or SG_BF16), ld ldx.  q: [rows, cols/2] bytes, ld ldq.
+ *   s : (r, cb) at s[r * s_stride_r + cb * s_stride_c], cb < cols / 128.
+ * Requires cols % 128 == 0; x 16-byte aligned, ldx * sizeof(x_dt) % 16 == 0;
+ * q 4-byte aligned, ldq % 4 == 0, ldq >= cols / 2.
+ */
+sg_status sg_int4_quant_groupwise(const void* x, sg_dtype x_dt, int64_t rows, int64_t cols,
+                                  int64_t ldx, uint8_t* q, int64_t ldq, float* s,
+                                  int64_t s_stride_r, int64_t s_stride_c, hipStream_t stream);
+
+/*
+ * sg_sparse24_prune_compress -- 2:4 magnitude pruning along K, then packing of
+ * the kept values and their metadata.  [T3258] jcaip's review: groups of 4
+ * along a row, the two smallest |w| are dropped; store only the specified
+ * values and the sparsity metadata.  [I2029] klevzoff: the sparse operand is
+ * passed as values + metadata E.
+ *   Kept: the two largest |w| of each group; equal magnitudes -> lower index.
+ *   vals[r, 2g + j] = w[r, 4g + i_j] with i_0 < i_1 (bits copied unchanged);
+ *   meta[r, b]      = nib(2b) | nib(2b + 1) << 4,  nib(g) = i_0 | i_1 << 2.
+ *   w    : [rows, k], dtype dt (SG_F32 or SG_BF16), leading dim ldw.
+ *   vals : [rows, k/2], same dtype, leading dim ldv.
+ *   meta : [rows, k/8] bytes, leading dim ldm.
+ * Requires k % 8 == 0, ldw >= k, ldv >= k/2, ldm >= k/8; w and vals 16-byte
+ * aligned, ldw * sizeof(dt) a multiple of 16 and ldv a multiple of 4.
+ */
+sg_status sg_sparse24_prune_compress(const void* w, sg_dtype dt, int64_t rows, int64_t k,
+                                     int64_t ldw, void* vals, int64_t ldv, uint8_t* meta,
+                                     int64_t ldm, hipStream_t stream);
+
+/*
+ * sg_fp8_gemm_groupwise -- Y = X . W^T with groupwise dequantisation scales.
+ * [P2095] hwu36's comment (the four ScaleGranularityM/N modes) and the
+ * promotion-interval review (products of a K tile start from zero and are
+ * promoted into fp32 accumulators with the tile's scales); here once per
+ * 128-wide K block:
+ *   y[m, n] = sum_kb sx[m/gran_m, kb] * sw[n/gran_n, kb] * sum_{k in kb} x[m,k] w[n,k]
+ *   xq : [M, K] e4m3, ld ldx.   sx: (m/gran_m, kb) at sx[(m/gran_m)*sx_sm + kb*sx_sk].
+ *   wq : [N, K] e4m3, ld ldw.   sw: (n/gran_n, kb) at sw[(n/gran_n)*sw_sn + kb*sw_sk].
+ *   gran_m, gran_n : 1 or 128.
+ *   y  : SG_F32 or SG_BF16 (round to nearest even) in the layout `form` selects.
+ * Requires K % 128 == 0, K > 0, M, N >= 0, ldx, ldw >= K; xq, wq 16-byte aligned,
+ * ldx, ldw multiples of 16; ldy >= N (SG_OUT_Y) or >= M (SG_OUT_YT); y aligned to
+ * its element size.  M and N need not be multiples of any tile (the partial M
+ * and N tiles of [P2095] are predicated).
+ */
+sg_status sg_fp8_gemm_groupwise(int64_t M, int64_t N, int64_t K, const uint8_t* xq, int64_t ldx,
+                                const float* sx, int64_t sx_sm, int64_t sx_sk, int gran_m,
+                                const uint8_t* wq, int64_t ldw, const float* sw, int64_t sw_sn,
+                                int64_t sw_sk, int gran_n, void* y, sg_dtype y_dt, int64_t ldy,
+                                sg_form form, hipStream_t stream);
+
+/*
+ * sg_fp8_sparse24_gemm_groupwise -- the same GEMM with W stored 2:4-compressed
+ * (values + metadata as produced by sg_sparse24_prune_compress then quantised
+ * with sg_fp8_quant_groupwise at gr = 128, gc = 64).  The result equals
+ * sg_fp8_gemm_groupwise on the decompressed weight.  [I2029] (hwu36: the sparse
+ * FP8 operand must be the row-major left operand; klevzoff: swap+transpose);
+ * [T3258] jcaip's review (fused scale multiplication in the sparse FP8 kernel).
+ *   wv    : [N, K/2] e4m3 codes, ld ldwv (bytes).
+ *   wmeta : [N, K/8] metadata bytes, ld ldwm.
+ *   other arguments as sg_fp8_gemm_groupwise.
+ * Requires in addition ldwv >= K/2, ldwm >= K/8, wv and wmeta 16-byte aligned,
+ * ldwv and ldwm multiples of 16.  Metadata nibbles must be legal
+ * (0x4, 0x8, 0x9, 0xC, 0xD, 0xE); others give unspecified values in range.
+ */
+sg_status sg_fp8_sparse24_gemm_groupwise(int64_t M, int64_t N, int64_t K, const uint8_t* xq,
+                                         int64_t ldx, const float* sx, int64_t sx_sm,
+                                         int64_t sx_sk, int gran_m, const uint8_t* wv,
+                                         int64_t ldwv, const uint8_t* wmeta, int64_t ldwm,
+                                         const float* sw, int64_t sw_sn, int64_t sw_sk,
+                                         int gran_n, void* y, sg_dtype y_dt, int64_t ldy,
+                                         sg_form form, hipStream_t stream);
+
+/*
+ * sg_mixed_gemm_add -- Y = X1 . W1^T + X2 . W2^T in one kernel ([I2058],
+ * hyx1999: a w4a4 GEMM plus a small w16a16 GEMM whose results are added, with
+ * L = 2048, D1 = 4096, D2 = 64, D = 4096 as the example shape).
+ *   y[m, n] = sum_kb sx1[m, kb] sw1[n, kb] sum_{k in kb} int4(x1) int4(w1)
+ *           + sum_{k < K2} bf16(x2[m, k]) bf16(w2[n, k]),   fp32 accumulation.
+ *   x1 : [M, K1/2] packed int4 (sg_int4_quant_groupwise), ld ldx1 bytes;
+ *        sx1 (m, kb) at sx1[m * sx1_sm + kb * sx1_sk].
+ *   w1 : [N, K1/2] packed int4, ld ldw1; sw1 (n, kb) at sw1[n * sw1_sn + kb * sw1_sk].
+ *   x2 : [M, K2] bf16 bits, ld ldx2.   w2: [N, K2] bf16 bits, ld ldw2.
+ *   y  : [M, N] bf16 (round to nearest even), ld ldy.
+ * Requires K1 % 128 == 0, K1 > 0, K2 % 32 == 0, K2 >= 0; ldx1, ldw1 >= K1/2 and
+ * multiples of 16; ldx2, ldw2 >= K2 with rows a multiple of 16 bytes; x1, w1, x2,
+ * w2 16-byte aligned (x2, w2 may be NULL when K2 == 0); y 2-byte aligned.
+ */
+sg_status sg_mixed_gemm_add(int64_t M, int64_t N, int64_t K1, int64_t K2, const uint8_t* x1,
+                            int64_t ldx1, const float* sx1, int64_t sx1_sm, int64_t sx1_sk,
+                            const uint8_t* w1, int64_t ldw1, const float* sw1, int64_t sw1_sn,
+                            int64_t sw1_sk, const uint16_t* x2, int64_t ldx2, const uint16_t* w2,
+                            int64_t ldw2, uint16_t* y, int64_t ldy, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_GEMM_LAYERS_AMD_SG_H */

@@ -1,0 +1,26 @@
+"""sparse_gemm_layers_amd: FP8 (e4m3) groupwise-scaled and 2:4-sparse
+linear-layer GEMMs for AMD Instinct MI355X (gfx950).
+
+A thin Python binding over the C ABI of ``libsg.so`` (declared in
+``include/sg.h``).  The functions only marshal arguments: PyTorch supplies
+device memory and the current HIP stream; every step runs in the library's
+HIP kernels.  There is no CPU fallback: if ``libsg.so`` is missing or the
+tensors are not on a GPU, the call raises.
+"""
+
+from ._binding import (
+    SgError,
+    lib,
+    fp8_quant_groupwise,
+    int4_quant_groupwise,
+    sparse24_prune_compress,
+    fp8_gemm_groupwise,
+    fp8_sparse24_gemm_groupwise,
+    mixed_gemm_add,
+)
+
+__all__ = [
+    "SgError", "lib", "fp8_quant_groupwise", "int4_quant_groupwise",
+    "sparse24_prune_compress", "fp8_gemm_groupwise", "fp8_sparse24_gemm_groupwise",
+    "mixed_gemm_add",
+]

@@ -1,0 +1,210 @@
+"""ctypes binding of libsg.so.  Argument marshalling only.
+
+Scale tensors are 2-D views [row_blocks, k_blocks] with arbitrary strides; by
+default they are allocated "M-major" (contiguous along rows, one column per K
+block), the layout CUTLASS PR #2095 ("Improvements for: Groupwise scaling
+along M for FP8 gemm", PR description) moved to.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsg.so")
+
+SG_F32, SG_BF16, SG_E4M3 = 0, 1, 2
+SG_OUT_Y, SG_OUT_YT = 0, 1
+
+_i64 = ctypes.c_int64
+_int = ctypes.c_int
+_ptr = ctypes.c_void_p
+
+_SIGS = {
+    "sg_status_str": ([_int], ctypes.c_char_p),
+    "sg_abi_version": ([], _int),
+    "sg_fp8_quant_groupwise": ([_ptr, _int, _i64, _i64, _i64, _int, _int, _ptr, _i64, _ptr, _i64, _i64, _ptr], _int),
+    "sg_int4_quant_groupwise": ([_ptr, _int, _i64, _i64, _i64, _ptr, _i64, _ptr, _i64, _i64, _ptr], _int),
+    "sg_sparse24_prune_compress": ([_ptr, _int, _i64, _i64, _i64, _ptr, _i64, _ptr, _i64, _ptr], _int),
+    "sg_fp8_gemm_groupwise": ([_i64, _i64, _i64, _ptr, _i64, _ptr, _i64, _i64, _int, _ptr, _i64, _ptr, _i64, _i64,
+                               _int, _ptr, _int, _i64, _int, _ptr], _int),
+    "sg_fp8_sparse24_gemm_groupwise": ([_i64, _i64, _i64, _ptr, _i64, _ptr, _i64, _i64, _int, _ptr, _i64, _ptr,
+                                        _i64, _ptr, _i64, _i64, _int, _ptr, _int, _i64, _int, _ptr], _int),
+    "sg_mixed_gemm_add": ([_i64, _i64, _i64, _i64, _ptr, _i64, _ptr, _i64, _i64, _ptr, _i64, _ptr, _i64, _i64,
+                           _ptr, _i64, _ptr, _i64, _ptr, _i64, _ptr], _int),
+}
+
+_lib = None
+
+
+class SgError(RuntimeError):
+    pass
+
+
+def lib():
+    """The loaded libsg.so (ctypes.CDLL) with every entry point typed."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run `python -m sparse_gemm_layers_amd.build`")
+        h = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            fn = getattr(h, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = h
+    return _lib
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise SgError(f"{what}: {lib().sg_status_str(status).decode()}")
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _gpu2d(t, name):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise SgError(f"{name} must be a GPU tensor")
+    if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+        raise SgError(f"{name} must be 2-D with unit column stride")
+    return t
+
+
+def _dtype_code(t, name):
+    if t.dtype == torch.float32:
+        return SG_F32
+    if t.dtype == torch.bfloat16:
+        return SG_BF16
+    raise SgError(f"{name}: dtype {t.dtype} not supported (float32 or bfloat16)")
+
+
+def _row_stride(t):
+    return t.stride(0) if t.shape[0] > 1 else max(t.shape[1], 1)
+
+
+def _scales(rows, cols, device):
+    """Empty fp32 scale view [rows, cols] stored M-major (contiguous along rows)."""
+    return torch.empty((cols, rows), dtype=torch.float32, device=device).t()
+
+
+def fp8_quant_groupwise(x, gr: int = 1, gc: int = 128, q=None, s=None):
+    """x [rows, cols] float32/bfloat16 -> (codes uint8 [rows, cols], scales fp32
+    [ceil(rows/gr), cols/gc]).  One scale per gr x gc block: amax / 448."""
+    _gpu2d(x, "x")
+    rows, cols = x.shape
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    if s is None:
+        s = _scales(-(-rows // gr), cols // gc if gc else 0, x.device)
+    _gpu2d(q, "q")
+    st = lib().sg_fp8_quant_groupwise(_p(x), _dtype_code(x, "x"), rows, cols, _row_stride(x), gr, gc,
+                                      _p(q), _row_stride(q), _p(s), s.stride(0), s.stride(1), _stream(x))
+    _check(st, "sg_fp8_quant_groupwise")
+    return q, s
+
+
+def int4_quant_groupwise(x, q=None, s=None):
+    """x [rows, cols] -> (packed int4 uint8 [rows, cols/2], scales fp32 [rows, cols/128])."""
+    _gpu2d(x, "x")
+    rows, cols = x.shape
+    if q is None:
+        q = torch.empty((rows, cols // 2), dtype=torch.uint8, device=x.device)
+    if s is None:
+        s = _scales(rows, cols // 128, x.device)
+    _gpu2d(q, "q")
+    st = lib().sg_int4_quant_groupwise(_p(x), _dtype_code(x, "x"), rows, cols, _row_stride(x), _p(q),
+                                       _row_stride(q), _p(s), s.stride(0), s.stride(1), _stream(x))
+    _check(st, "sg_int4_quant_groupwise")
+    return q, s
+
+
+def sparse24_prune_compress(w, vals=None, meta=None):
+    """w [rows, k] float32/bfloat16 -> (values [rows, k/2] same dtype, metadata uint8 [rows, k/8])."""
+    _gpu2d(w, "w")
+    rows, k = w.shape
+    if vals is None:
+        vals = torch.empty((rows, k // 2), dtype=w.dtype, device=w.device)
+    if meta is None:
+        meta = torch.empty((rows, k // 8), dtype=torch.uint8, device=w.device)
+    _gpu2d(vals, "vals")
+    _gpu2d(meta, "meta")
+    st = lib().sg_sparse24_prune_compress(_p(w), _dtype_code(w, "w"), rows, k, _row_stride(w), _p(vals),
+                                          _row_stride(vals), _p(meta), _row_stride(meta), _stream(w))
+    _check(st, "sg_sparse24_prune_compress")
+    return vals, meta
+
+
+def _out(y, M, N, out_dtype, form, device):
+    yt = form in ("yt", SG_OUT_YT)
+    if y is None:
+        y = torch.empty((N, M) if yt else (M, N), dtype=out_dtype, device=device)
+    _gpu2d(y, "y")
+    return y, (SG_OUT_YT if yt else SG_OUT_Y), _dtype_code(y, "y")
+
+
+def fp8_gemm_groupwise(xq, sx, wq, sw, gran_m: int = 1, gran_n: int = 128, out_dtype=torch.bfloat16,
+                       form: str = "y", y=None):
+    """Y = X . W^T with groupwise scales.  xq uint8 [M, K], sx fp32 [ceil(M/gran_m), K/128],
+    wq uint8 [N, K], sw fp32 [ceil(N/gran_n), K/128].  form "y" -> Y [M, N], "yt" -> Y^T [N, M]."""
+    _gpu2d(xq, "xq")
+    _gpu2d(wq, "wq")
+    M, K = xq.shape
+    N = wq.shape[0]
+    y, f, ydt = _out(y, M, N, out_dtype, form, xq.device)
+    st = lib().sg_fp8_gemm_groupwise(M, N, K, _p(xq), _row_stride(xq), _p(sx), sx.stride(0), sx.stride(1),
+                                     gran_m, _p(wq), _row_stride(wq), _p(sw), sw.stride(0), sw.stride(1),
+                                     gran_n, _p(y), ydt, _row_stride(y), f, _stream(xq))
+    _check(st, "sg_fp8_gemm_groupwise")
+    return y
+
+
+def fp8_sparse24_gemm_groupwise(xq, sx, wv, wmeta, sw, gran_m: int = 1, gran_n: int = 128,
+                                out_dtype=torch.bfloat16, form: str = "y", y=None):
+    """The same GEMM with W as 2:4-compressed codes wv uint8 [N, K/2] and metadata
+    wmeta uint8 [N, K/8]."""
+    _gpu2d(xq, "xq")
+    _gpu2d(wv, "wv")
+    _gpu2d(wmeta, "wmeta")
+    M, K = xq.shape
+    N = wv.shape[0]
+    y, f, ydt = _out(y, M, N, out_dtype, form, xq.device)
+    st = lib().sg_fp8_sparse24_gemm_groupwise(M, N, K, _p(xq), _row_stride(xq), _p(sx), sx.stride(0),
+                                              sx.stride(1), gran_m, _p(wv), _row_stride(wv), _p(wmeta),
+                                              _row_stride(wmeta), _p(sw), sw.stride(0), sw.stride(1), gran_n,
+                                              _p(y), ydt, _row_stride(y), f, _stream(xq))
+    _check(st, "sg_fp8_sparse24_gemm_groupwise")
+    return y
+
+
+def mixed_gemm_add(x1, sx1, w1, sw1, x2, w2, y=None):
+    """Y = X1 . W1^T (int4, per-(row, 128) scales) + X2 . W2^T (bf16), bf16 out [M, N].
+    x1 uint8 [M, K1/2], w1 uint8 [N, K1/2], x2 bf16 [M, K2], w2 bf16 [N, K2]."""
+    _gpu2d(x1, "x1")
+    _gpu2d(w1, "w1")
+    M, K1 = x1.shape[0], x1.shape[1] * 2
+    N = w1.shape[0]
+    K2 = x2.shape[1] if x2 is not None else 0
+    if K2:
+        _gpu2d(x2, "x2")
+        _gpu2d(w2, "w2")
+        for t, nm in ((x2, "x2"), (w2, "w2")):
+            if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+                raise SgError(f"{nm} must hold bf16 values")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=x1.device)
+    _gpu2d(y, "y")
+    st = lib().sg_mixed_gemm_add(M, N, K1, K2, _p(x1), _row_stride(x1), _p(sx1), sx1.stride(0), sx1.stride(1),
+                                 _p(w1), _row_stride(w1), _p(sw1), sw1.stride(0), sw1.stride(1),
+                                 _p(x2) if K2 else None, _row_stride(x2) if K2 else 0,
+                                 _p(w2) if K2 else None, _row_stride(w2) if K2 else 0,
+                                 _p(y), _row_stride(y), _stream(x1))
+    _check(st, "sg_mixed_gemm_add")
+    return y

@@ -1,0 +1,96 @@
+// Shared host/device helpers of the gfx950 kernels: vector types, the e4m3 and
+// bf16 encoders, wave reductions and the host-side argument checks.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sg.h"
+
+namespace sg {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+// ---------------------------------------------------------------- encoders
+
+// fp32 -> OCP e4m3 ("e4m3fn") code: round to nearest, ties to even mantissa,
+// saturate at +-448, keep the sign (a negative value that rounds to zero
+// gives 0x80).  NaN gives 0x7F with its sign.  Pure integer/ALU code so the
+// result does not depend on any conversion instruction's rounding mode.
+__device__ __forceinline__ uint32_t e4m3_encode(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return sign | 0x7fu;          // NaN
+  if (a >= 0x43e00000u) return sign | 0x7eu;         // |v| >= 448: saturate
+  if (a >= 0x3c800000u) {                            // |v| >= 2^-6: normal
+    // Round the 23-bit mantissa to 3 bits, half to even; a carry moves into
+    // the exponent field by itself.  |v| < 448 keeps the result <= 448.
+    const uint32_t t = a + 0x7ffffu + ((a >> 20) & 1u);
+    const uint32_t e = (t >> 23) - 120u;             // fp32 bias 127 -> e4m3 bias 7
+    const uint32_t m = (t >> 20) & 7u;
+    return sign | (e << 3) | m;
+  }
+  // Subnormal range: value = m * 2^-9, m = round_half_even(|v| * 512) in 0..8
+  // (m == 8 is code 0x08, the smallest normal 2^-6).  The scaling is exact.
+  const uint32_t m = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+  return sign | m;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float((uint32_t)b << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// ---------------------------------------------------------------- loads
+
+// Four consecutive inputs as fp32.  float: one 16-byte load; bf16: one 8-byte load.
+__device__ __forceinline__ void load4(const float* p, float v[4]) {
+  const float4 t = *reinterpret_cast<const float4*>(p);
+  v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+}
+__device__ __forceinline__ void load4(const uint16_t* p, float v[4]) {
+  const uint2 t = *reinterpret_cast<const uint2*>(p);
+  v[0] = __uint_as_float(t.x << 16);
+  v[1] = __uint_as_float(t.x & 0xffff0000u);
+  v[2] = __uint_as_float(t.y << 16);
+  v[3] = __uint_as_float(t.y & 0xffff0000u);
+}
+
+// Max over groups of `width` consecutive lanes (width a power of two <= 64).
+template <int WIDTH>
+__device__ __forceinline__ float group_max(float a) {
+#pragma unroll
+  for (int o = WIDTH / 2; o >= 1; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, 64));
+  return a;
+}
+
+// ---------------------------------------------------------------- host checks
+
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+inline size_t dtype_size(sg_dtype d) { return d == SG_F32 ? 4 : d == SG_BF16 ? 2 : 1; }
+
+// Clears any stale error of this host thread, so that the check after a
+// launch reports the launch itself.
+inline void clear_hip_error() { (void)hipGetLastError(); }
+
+inline sg_status launch_status() { return hipGetLastError() == hipSuccess ? SG_OK : SG_ERR_HIP; }
+
+// Workgroup count for grid-stride loops: enough to fill 256 CUs several times.
+inline unsigned grid_for(int64_t items, int per_group, unsigned cap = 4096) {
+  const int64_t g = cdiv(items, per_group);
+  return (unsigned)(g < 1 ? 1 : (g > cap ? cap : g));
+}
+
+}  // namespace sg

@@ -1,0 +1,181 @@
+// Groupwise quantisers: fp32/bf16 -> e4m3 codes + one fp32 scale per block
+// (1 x gc or 128 x gc), and fp32/bf16 -> packed int4 + one scale per
+// (row, 128 columns).  Both are HBM-bound streaming kernels: every input
+// byte is read once with 16- or 8-byte loads, codes are written once with
+// 4- or 2-byte stores per lane, scales once per block.
+//
+// Block amax -> scale -> quantise follows CUTLASS PR #2095 "Improvements for:
+// Groupwise scaling along M for FP8 gemm" (hwu36's comment on the
+// ScaleGranularityM/N modes) and torchao PR #3258 "Introduce new W8A8-FP-CSR
+// quantization API" (jcaip's review: positive scales, all-zero input allowed,
+// scale then cast to float8_e4m3fn).
+#include "common.h"
+
+namespace sg {
+
+// ------------------------------------------------------------------ 1 x GC
+// LPB = GC/4 lanes share one block, 4 consecutive elements per lane; a wave
+// covers 64/LPB blocks per iteration of a grid-stride loop.
+template <typename TIn, int GC, bool INT4>
+__global__ void __launch_bounds__(256) k_quant_rowblock(const TIn* __restrict__ x, int64_t rows,
+                                                        int64_t cols, int64_t ldx,
+                                                        uint8_t* __restrict__ q, int64_t ldq,
+                                                        float* __restrict__ s, int64_t ssr,
+                                                        int64_t ssc) {
+  constexpr int LPB = GC / 4;
+  constexpr int BPW = 64 / LPB;
+  const int64_t nbc = cols / GC;
+  const int64_t nblk = rows * nbc;
+  const int lane = threadIdx.x & 63;
+  const int sub = lane / LPB;
+  const int li = lane % LPB;
+  const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+  for (int64_t b0 = wave * BPW; b0 < nblk; b0 += nwaves * BPW) {
+    const int64_t b = b0 + sub;
+    const bool valid = b < nblk;
+    const int64_t r = valid ? b / nbc : 0;
+    const int64_t cb = valid ? b % nbc : 0;
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    if (valid) load4(x + r * ldx + cb * GC + li * 4, v);
+    float a = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+    a = group_max<LPB>(a);
+    if (!INT4) {
+      const float sc = a > 0.f ? a / 448.0f : 1.0f;             // IEEE divide
+      uint32_t packed = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) packed |= e4m3_encode(v[i] / sc) << (8 * i);
+      if (valid) {
+        *reinterpret_cast<uint32_t*>(q + r * ldq + cb * GC + li * 4) = packed;
+        if (li == 0) s[r * ssr + cb * ssc] = sc;
+      }
+    } else {
+      const float sc = a > 0.f ? a / 7.0f : 1.0f;
+      uint32_t packed = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float t = __builtin_rintf(v[i] / sc);                    // half to even
+        t = fminf(fmaxf(t, -7.0f), 7.0f);
+        packed |= ((uint32_t)(int)t & 0xfu) << (4 * i);
+      }
+      if (valid) {
+        *reinterpret_cast<uint16_t*>(q + r * ldq + cb * (GC / 2) + li * 2) = (uint16_t)packed;
+        if (li == 0) s[r * ssr + cb * ssc] = sc;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ 128 x GC
+// One 256-thread workgroup per block.  LPR = GC/4 lanes cover one row of the
+// block; each thread keeps its STEPS x 4 inputs in registers between the amax
+// reduction and the encode, so the block is read from HBM once.
+template <typename TIn, int GC>
+__global__ void __launch_bounds__(256) k_quant_block128(const TIn* __restrict__ x, int64_t rows,
+                                                        int64_t ldx, uint8_t* __restrict__ q,
+                                                        int64_t ldq, float* __restrict__ s,
+                                                        int64_t ssr, int64_t ssc) {
+  constexpr int LPR = GC / 4;
+  constexpr int RPS = 256 / LPR;
+  constexpr int STEPS = 128 / RPS;
+  __shared__ float red[4];
+  const int64_t cb = blockIdx.x, rb = blockIdx.y;
+  const int t = threadIdx.x;
+  const int lr = t / LPR, li = t % LPR;
+  float v[STEPS][4];
+  float a = 0.f;
+#pragma unroll
+  for (int st = 0; st < STEPS; ++st) {
+    const int64_t r = rb * 128 + st * RPS + lr;
+    if (r < rows) {
+      load4(x + r * ldx + cb * GC + li * 4, v[st]);
+    } else {
+      v[st][0] = v[st][1] = v[st][2] = v[st][3] = 0.f;
+    }
+    a = fmaxf(a, fmaxf(fmaxf(fabsf(v[st][0]), fabsf(v[st][1])), fmaxf(fabsf(v[st][2]), fabsf(v[st][3]))));
+  }
+  a = group_max<64>(a);
+  if ((t & 63) == 0) red[t >> 6] = a;
+  __syncthreads();
+  a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float sc = a > 0.f ? a / 448.0f : 1.0f;
+#pragma unroll
+  for (int st = 0; st < STEPS; ++st) {
+    const int64_t r = rb * 128 + st * RPS + lr;
+    uint32_t packed = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) packed |= e4m3_encode(v[st][i] / sc) << (8 * i);
+    if (r < rows) *reinterpret_cast<uint32_t*>(q + r * ldq + cb * GC + li * 4) = packed;
+  }
+  if (t == 0) s[rb * ssr + cb * ssc] = sc;
+}
+
+template <typename TIn>
+static void launch_fp8_quant(const TIn* x, int64_t rows, int64_t cols, int64_t ldx, int gr, int gc,
+                             uint8_t* q, int64_t ldq, float* s, int64_t ssr, int64_t ssc,
+                             hipStream_t st) {
+  if (gr == 1) {
+    const int64_t blocks = rows * (cols / gc);
+    const int per_wg = 4 * (64 / (gc / 4));
+    const unsigned g = grid_for(blocks, per_wg);
+    if (gc == 128)
+      k_quant_rowblock<TIn, 128, false><<<g, 256, 0, st>>>(x, rows, cols, ldx, q, ldq, s, ssr, ssc);
+    else
+      k_quant_rowblock<TIn, 64, false><<<g, 256, 0, st>>>(x, rows, cols, ldx, q, ldq, s, ssr, ssc);
+  } else {
+    const dim3 grid((unsigned)(cols / gc), (unsigned)cdiv(rows, 128));
+    if (gc == 128)
+      k_quant_block128<TIn, 128><<<grid, 256, 0, st>>>(x, rows, ldx, q, ldq, s, ssr, ssc);
+    else
+      k_quant_block128<TIn, 64><<<grid, 256, 0, st>>>(x, rows, ldx, q, ldq, s, ssr, ssc);
+  }
+}
+
+}  // namespace sg
+
+using namespace sg;
+
+extern "C" sg_status sg_fp8_quant_groupwise(const void* x, sg_dtype x_dt, int64_t rows,
+                                            int64_t cols, int64_t ldx, int gr, int gc, uint8_t* q,
+                                            int64_t ldq, float* s, int64_t s_stride_r,
+                                            int64_t s_stride_c, hipStream_t stream) {
+  if (!x || !q || !s) return SG_ERR_NULL;
+  if (x_dt != SG_F32 && x_dt != SG_BF16) return SG_ERR_UNSUPPORTED;
+  if ((gr != 1 && gr != 128) || (gc != 128 && gc != 64)) return SG_ERR_UNSUPPORTED;
+  if (rows < 0 || cols <= 0 || cols % gc != 0 || ldx < cols || ldq < cols) return SG_ERR_SHAPE;
+  if (cdiv(rows, gr) > 65535 && gr == 128) return SG_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(s, 4) || (ldx * (int64_t)dtype_size(x_dt)) % 16 ||
+      ldq % 16)
+    return SG_ERR_ALIGN;
+  if (rows == 0) return SG_OK;
+  clear_hip_error();
+  if (x_dt == SG_F32)
+    launch_fp8_quant((const float*)x, rows, cols, ldx, gr, gc, q, ldq, s, s_stride_r, s_stride_c, stream);
+  else
+    launch_fp8_quant((const uint16_t*)x, rows, cols, ldx, gr, gc, q, ldq, s, s_stride_r, s_stride_c,
+                     stream);
+  return launch_status();
+}
+
+extern "C" sg_status sg_int4_quant_groupwise(const void* x, sg_dtype x_dt, int64_t rows,
+                                             int64_t cols, int64_t ldx, uint8_t* q, int64_t ldq,
+                                             float* s, int64_t s_stride_r, int64_t s_stride_c,
+                                             hipStream_t stream) {
+  if (!x || !q || !s) return SG_ERR_NULL;
+  if (x_dt != SG_F32 && x_dt != SG_BF16) return SG_ERR_UNSUPPORTED;
+  if (rows < 0 || cols <= 0 || cols % 128 != 0 || ldx < cols || ldq < cols / 2) return SG_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(q, 4) || !aligned(s, 4) || (ldx * (int64_t)dtype_size(x_dt)) % 16 ||
+      ldq % 4)
+    return SG_ERR_ALIGN;
+  if (rows == 0) return SG_OK;
+  clear_hip_error();
+  const int64_t blocks = rows * (cols / 128);
+  const unsigned g = grid_for(blocks, 8);
+  if (x_dt == SG_F32)
+    k_quant_rowblock<float, 128, true><<<g, 256, 0, stream>>>((const float*)x, rows, cols, ldx, q, ldq, s,
+                                                             s_stride_r, s_stride_c);
+  else
+    k_quant_rowblock<uint16_t, 128, true><<<g, 256, 0, stream>>>((const uint16_t*)x, rows, cols, ldx, q,
+                                                                ldq, s, s_stride_r, s_stride_c);
+  return launch_status();
+}

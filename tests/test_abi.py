@@ -1,0 +1,171 @@
+"""The C-ABI library loads, exports every entry point include/sg.h declares,
+and rejects invalid arguments on the host before any HIP call.
+
+These tests pass fake (never dereferenced) device addresses, so they only run
+where no GPU is visible: every call here must return before touching HIP."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import sparse_gemm_layers_amd as sg
+from sparse_gemm_layers_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sg.h")
+
+OK, NULL, SHAPE, UNSUP, ALIGN, HIP = range(6)
+P = ctypes.c_void_p(0x100000)          # 16-byte aligned fake address
+P2 = ctypes.c_void_p(0x200000)
+P3 = ctypes.c_void_p(0x300000)
+ODD = ctypes.c_void_p(0x100004)        # 4- but not 16-byte aligned
+
+no_gpu = pytest.mark.skipif(torch.cuda.is_available(), reason="fake-pointer checks run only without a GPU")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(sg_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted([
+        "sg_abi_version", "sg_status_str", "sg_fp8_quant_groupwise", "sg_int4_quant_groupwise",
+        "sg_sparse24_prune_compress", "sg_fp8_gemm_groupwise", "sg_fp8_sparse24_gemm_groupwise",
+        "sg_mixed_gemm_add"])
+
+
+def test_library_exports_every_declared_symbol():
+    lib = sg.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(B._SIGS) == set(declared_functions())
+
+
+def test_status_strings_and_version():
+    lib = sg.lib()
+    assert lib.sg_abi_version() == 1
+    for code, word in [(OK, b"SG_OK"), (NULL, b"SG_ERR_NULL"), (SHAPE, b"SG_ERR_SHAPE"),
+                       (UNSUP, b"SG_ERR_UNSUPPORTED"), (ALIGN, b"SG_ERR_ALIGN"), (HIP, b"SG_ERR_HIP")]:
+        assert lib.sg_status_str(code).startswith(word)
+    assert lib.sg_status_str(99) == b"unknown sg_status"
+
+
+def quant(**kw):
+    a = dict(x=P, dt=0, rows=4, cols=256, ldx=256, gr=1, gc=128, q=P2, ldq=256, s=P3, ssr=1, ssc=4)
+    a.update(kw)
+    return sg.lib().sg_fp8_quant_groupwise(a["x"], a["dt"], a["rows"], a["cols"], a["ldx"], a["gr"], a["gc"],
+                                           a["q"], a["ldq"], a["s"], a["ssr"], a["ssc"], None)
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), NULL), (dict(q=None), NULL), (dict(s=None), NULL),
+    (dict(dt=2), UNSUP), (dict(dt=7), UNSUP), (dict(gr=2), UNSUP), (dict(gc=32), UNSUP),
+    (dict(cols=200), SHAPE), (dict(cols=0), SHAPE), (dict(rows=-1), SHAPE), (dict(ldx=128), SHAPE),
+    (dict(ldq=100), SHAPE), (dict(x=ODD), ALIGN), (dict(ldx=258), ALIGN), (dict(ldq=264), ALIGN),
+    (dict(rows=0), OK),
+])
+def test_fp8_quant_validation(kw, code):
+    assert quant(**kw) == code
+
+
+def int4q(**kw):
+    a = dict(x=P, dt=1, rows=4, cols=256, ldx=256, q=P2, ldq=128, s=P3, ssr=2, ssc=1)
+    a.update(kw)
+    return sg.lib().sg_int4_quant_groupwise(a["x"], a["dt"], a["rows"], a["cols"], a["ldx"], a["q"], a["ldq"],
+                                            a["s"], a["ssr"], a["ssc"], None)
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(dt=2), UNSUP), (dict(cols=64), SHAPE), (dict(ldq=64), SHAPE),
+    (dict(ldq=130), ALIGN), (dict(x=ODD), ALIGN), (dict(rows=0), OK),
+])
+def test_int4_quant_validation(kw, code):
+    assert int4q(**kw) == code
+
+
+def prune(**kw):
+    a = dict(w=P, dt=0, rows=8, k=64, ldw=64, v=P2, ldv=32, m=P3, ldm=8)
+    a.update(kw)
+    return sg.lib().sg_sparse24_prune_compress(a["w"], a["dt"], a["rows"], a["k"], a["ldw"], a["v"], a["ldv"],
+                                               a["m"], a["ldm"], None)
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,code", [
+    (dict(w=None), NULL), (dict(v=None), NULL), (dict(m=None), NULL), (dict(dt=2), UNSUP),
+    (dict(k=12), SHAPE), (dict(k=0), SHAPE), (dict(ldw=32), SHAPE), (dict(ldv=16), SHAPE), (dict(ldm=4), SHAPE),
+    (dict(v=ODD), ALIGN), (dict(ldw=66), ALIGN), (dict(ldv=34), ALIGN), (dict(rows=0), OK),
+])
+def test_prune_validation(kw, code):
+    assert prune(**kw) == code
+
+
+def gemm(sparse=False, **kw):
+    a = dict(M=64, N=256, K=256, x=P, ldx=256, sx=P3, sxm=1, sxk=64, gm=1, w=P2, ldw=256, meta=P3, ldm=32,
+             sw=P3, swn=2, swk=1, gn=128, y=P, ydt=1, ldy=256, form=0)
+    a.update(kw)
+    lib = sg.lib()
+    if sparse:
+        ldw = a["ldw"] if "ldw" in kw else a["K"] // 2
+        return lib.sg_fp8_sparse24_gemm_groupwise(a["M"], a["N"], a["K"], a["x"], a["ldx"], a["sx"], a["sxm"],
+                                                  a["sxk"], a["gm"], a["w"], ldw, a["meta"], a["ldm"], a["sw"],
+                                                  a["swn"], a["swk"], a["gn"], a["y"], a["ydt"], a["ldy"],
+                                                  a["form"], None)
+    return lib.sg_fp8_gemm_groupwise(a["M"], a["N"], a["K"], a["x"], a["ldx"], a["sx"], a["sxm"], a["sxk"],
+                                     a["gm"], a["w"], a["ldw"], a["sw"], a["swn"], a["swk"], a["gn"], a["y"],
+                                     a["ydt"], a["ldy"], a["form"], None)
+
+
+GEMM_CASES = [
+    (dict(x=None), NULL), (dict(sx=None), NULL), (dict(w=None), NULL), (dict(sw=None), NULL), (dict(y=None), NULL),
+    (dict(gm=64), UNSUP), (dict(gn=2), UNSUP), (dict(ydt=2), UNSUP), (dict(form=2), UNSUP),
+    (dict(K=0), SHAPE), (dict(K=200), SHAPE), (dict(M=-1), SHAPE), (dict(ldx=128), SHAPE),
+    (dict(ldy=100), SHAPE), (dict(form=1, ldy=32), SHAPE),
+    (dict(x=ODD), ALIGN), (dict(ldx=264), ALIGN), (dict(y=ctypes.c_void_p(0x100001)), ALIGN),
+    (dict(M=0), OK), (dict(N=0), OK),
+]
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,code", GEMM_CASES + [(dict(ldw=128), SHAPE), (dict(w=ODD), ALIGN)])
+def test_dense_gemm_validation(kw, code):
+    assert gemm(False, **kw) == code
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,code", GEMM_CASES + [
+    (dict(meta=None), NULL), (dict(ldw=64), SHAPE), (dict(ldm=16), SHAPE), (dict(meta=ODD), ALIGN),
+    (dict(ldm=40), ALIGN)])
+def test_sparse_gemm_validation(kw, code):
+    assert gemm(True, **kw) == code
+
+
+def mixed(**kw):
+    a = dict(M=16, N=256, K1=256, K2=64, x1=P, ldx1=128, sx1=P3, sxm=2, sxk=1, w1=P2, ldw1=128, sw1=P3, swn=2,
+             swk=1, x2=P, ldx2=64, w2=P2, ldw2=64, y=P, ldy=256)
+    a.update(kw)
+    return sg.lib().sg_mixed_gemm_add(a["M"], a["N"], a["K1"], a["K2"], a["x1"], a["ldx1"], a["sx1"], a["sxm"],
+                                      a["sxk"], a["w1"], a["ldw1"], a["sw1"], a["swn"], a["swk"], a["x2"],
+                                      a["ldx2"], a["w2"], a["ldw2"], a["y"], a["ldy"], None)
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,code", [
+    (dict(x1=None), NULL), (dict(x2=None), NULL), (dict(K2=0, x2=None, w2=None, M=0), OK),
+    (dict(K1=100), SHAPE), (dict(K2=48), SHAPE), (dict(ldx1=64), SHAPE), (dict(ldx2=32), SHAPE),
+    (dict(ldy=100), SHAPE), (dict(x1=ODD), ALIGN), (dict(ldw2=68), ALIGN), (dict(N=0), OK),
+])
+def test_mixed_validation(kw, code):
+    assert mixed(**kw) == code
+
+
+def test_binding_rejects_cpu_tensors():
+    x = torch.zeros(4, 128)
+    with pytest.raises(sg.SgError):
+        sg.fp8_quant_groupwise(x)

@@ -1,0 +1,139 @@
+"""GPU parity of the FP8 groupwise GEMMs (dense and 2:4-sparse W) against the
+oracle, within |y - y_ref| <= 1e-2 |y_ref| + 1e-3 T (T = sum over K blocks of
+the scale product times sum |x w|).  Operands are quantised (and pruned) by
+the oracle, so these tests check the GEMM alone; the quantiser and pruning
+kernels are checked bit-exactly in test_gpu_quant_prune.py."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_gemm_layers_amd as sg
+import workloads
+from gpu_helpers import DEV, assert_within_tolerance, down, oracle_operands, say, up, up_scales
+
+pytestmark = pytest.mark.gpu
+
+
+def run_gemm(sparse, xq, sx, gm, wq, meta, sw, gn, out_dtype, form, m_major=True):
+    args = (up(xq), up_scales(sx, m_major))
+    if sparse:
+        return sg.fp8_sparse24_gemm_groupwise(*args, up(wq), up(meta), up_scales(sw, m_major), gm, gn,
+                                              out_dtype=out_dtype, form=form)
+    return sg.fp8_gemm_groupwise(*args, up(wq), up_scales(sw, m_major), gm, gn, out_dtype=out_dtype, form=form)
+
+
+def check(sparse, m, n, k, gm=1, gn=128, out_dtype=torch.bfloat16, forms=("y", "yt"), seed=0, dist="sparse",
+          m_major=True):
+    say(f"{'sparse' if sparse else 'dense'} M={m} N={n} K={k} gm={gm} gn={gn} {out_dtype} {forms} seed={seed}")
+    d = (workloads.dense_outliers if dist == "outliers" else workloads.sparse_large)(seed=seed, m=m, n=n, k=k)
+    xq, sx, wq, meta, sw = oracle_operands(d["x"], d["w"], gm, gn, sparse)
+    if sparse:
+        ref, bound = oracle.fp8_sparse24_gemm_groupwise(xq, sx, gm, wq, meta, sw, gn, bound=True)
+    else:
+        ref, bound = oracle.fp8_gemm_groupwise(xq, sx, gm, wq, sw, gn, bound=True)
+    outs = {}
+    for form in forms:
+        y = run_gemm(sparse, xq, sx, gm, wq, meta, sw, gn, out_dtype, form, m_major)
+        got = down(y)
+        got = got.T if form == "yt" else got
+        assert got.shape == (m, n)
+        assert_within_tolerance(got.astype(np.float64), ref, bound, f"form={form}")
+        outs[form] = got
+    if len(outs) == 2:   # both forms store the same numbers
+        assert np.array_equal(outs["y"], outs["yt"])
+    return outs
+
+
+RAGGED = [(1, 256, 128), (15, 100, 256), (16, 256, 128), (17, 300, 384), (37, 512, 256), (64, 128, 256),
+          (65, 256, 128), (127, 257, 256), (128, 512, 128), (129, 256, 256), (200, 700, 384), (300, 1000, 512)]
+
+
+@pytest.mark.parametrize("sparse", [False, True])
+@pytest.mark.parametrize("m,n,k", RAGGED)
+def test_ragged_shapes(sparse, m, n, k):
+    check(sparse, m, n, k, seed=m * 7 + n)
+
+
+@pytest.mark.parametrize("sparse", [False, True])
+@pytest.mark.parametrize("gm,gn", [(1, 1), (128, 1), (128, 128), (1, 128)])
+@pytest.mark.parametrize("m", [37, 300])
+def test_granularity_modes(sparse, gm, gn, m):
+    check(sparse, m, 384, 256, gm=gm, gn=gn, seed=11 + gm + gn)
+
+
+@pytest.mark.parametrize("sparse", [False, True])
+@pytest.mark.parametrize("m", [20, 257])
+def test_fp32_output_and_row_major_scales(sparse, m):
+    check(sparse, m, 260, 256, out_dtype=torch.float32, seed=5, m_major=False)
+
+
+def test_tiny_config_fp32():
+    """64 x 128 x 256 2:4 FP8, fp32 out (the tiny workload), sparse and dense on
+    the decompressed weight."""
+    d = workloads.tiny_sparse()
+    xq, sx, wq, meta, sw = oracle_operands(d["x"], d["w"], 1, 128, True)
+    ref, bound = oracle.fp8_sparse24_gemm_groupwise(xq, sx, 1, wq, meta, sw, 128, bound=True)
+    for form in ("y", "yt"):
+        y = down(run_gemm(True, xq, sx, 1, wq, meta, sw, 128, torch.float32, form))
+        assert_within_tolerance(y.T if form == "yt" else y, ref, bound, f"tiny sparse {form}")
+    wd = oracle.decompress24(wq, meta)
+    y = down(run_gemm(False, xq, sx, 1, wd, None, sw, 128, torch.float32, "y"))
+    assert_within_tolerance(y, ref, bound, "tiny dense(decompressed)")
+
+
+def test_dense_full_size_with_outliers():
+    """2048 x 4096 x 4096, X with 1% outliers x20, X 1x128 / W 128x128 scales, bf16."""
+    check(False, 2048, 4096, 4096, seed=2, dist="outliers", forms=("y",))
+
+
+def test_sparse_full_size_both_forms():
+    """2048 x 4096 x 4096 2:4 FP8: Y = X W^T and the swapped Y^T = W X^T."""
+    check(True, 2048, 4096, 4096, seed=3)
+
+
+@pytest.mark.parametrize("m,n,k", workloads.DECODE_SHAPES)
+def test_decode_shapes(m, n, k):
+    check(True, m, n, k, seed=4, forms=("y", "yt"))
+
+
+def test_deterministic_and_all_zero_operands():
+    d = workloads.sparse_large(seed=8, m=300, n=512, k=512)
+    xq, sx, wq, meta, sw = oracle_operands(d["x"], d["w"], 1, 128, True)
+    a = down(run_gemm(True, xq, sx, 1, wq, meta, sw, 128, torch.bfloat16, "y"))
+    b = down(run_gemm(True, xq, sx, 1, wq, meta, sw, 128, torch.bfloat16, "y"))
+    assert np.array_equal(a, b)
+    z = np.zeros_like(wq)
+    y = down(run_gemm(True, xq, sx, 1, z, meta, np.ones_like(sw), 128, torch.float32, "y"))
+    assert not y.any()
+
+
+def test_outputs_outside_the_problem_are_untouched():
+    """Partial tiles never store past M or N: a padded output buffer keeps its
+    sentinel outside the [M, N] window."""
+    m, n, k = 37, 300, 256
+    d = workloads.sparse_large(seed=12, m=m, n=n, k=k)
+    xq, sx, wq, meta, sw = oracle_operands(d["x"], d["w"], 1, 128, True)
+    for mm in (37, 200):     # decode path and large-M path
+        xqq = np.concatenate([xq] * (mm // m + 1))[:mm]
+        sxx = np.concatenate([sx] * (mm // m + 1))[:mm]
+        ybuf = torch.full((mm + 3, n + 8), 7.0, dtype=torch.float32, device=DEV)
+        sg.fp8_sparse24_gemm_groupwise(up(xqq), up_scales(sxx), up(wq), up(meta), up_scales(sw), 1, 128,
+                                       y=ybuf[:mm, :n])
+        yb = down(ybuf)
+        assert np.all(yb[mm:, :] == 7.0) and np.all(yb[:, n:] == 7.0)
+        ref, bound = oracle.fp8_sparse24_gemm_groupwise(xqq, sxx, 1, wq, meta, sw, 128, bound=True)
+        assert_within_tolerance(yb[:mm, :n], ref, bound, f"padded M={mm}")
+
+
+def test_end_to_end_gpu_chain_matches_oracle_chain():
+    """GPU prune + GPU quantisers + GPU GEMM on raw fp32 inputs equals the oracle
+    chain: the intermediate codes are bit-exact, so the GEMM inputs agree."""
+    d = workloads.sparse_large(seed=13, m=256, n=512, k=1024)
+    wv, meta = sg.sparse24_prune_compress(up(d["w"]))
+    wq, sw = sg.fp8_quant_groupwise(wv, gr=128, gc=64)
+    xq, sx = sg.fp8_quant_groupwise(up(d["x"]), gr=1, gc=128)
+    y = down(sg.fp8_sparse24_gemm_groupwise(xq, sx, wq, meta, sw, 1, 128))
+    oxq, osx, owq, ometa, osw = oracle_operands(d["x"], d["w"], 1, 128, True)
+    ref, bound = oracle.fp8_sparse24_gemm_groupwise(oxq, osx, 1, owq, ometa, osw, 128, bound=True)
+    assert_within_tolerance(y, ref, bound, "end-to-end")

@@ -1,0 +1,141 @@
+"""GPU parity of the quantisers and of 2:4 pruning + packing against the
+oracle: codes, scales, kept values and metadata must match bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_gemm_layers_amd as sg
+import workloads
+from gpu_helpers import DEV, say, up
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("gr,gc,rows,cols,dist", [
+    (1, 128, 1, 128, "normal"), (1, 128, 37, 256, "outliers"), (1, 128, 2048, 4096, "outliers"),
+    (128, 128, 4096, 4096, "weight"), (128, 128, 130, 384, "weight"), (128, 64, 4096, 2048, "weight"),
+    (128, 64, 37, 64, "normal"), (1, 64, 300, 192, "normal"),
+])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_fp8_quant_matches_oracle(gr, gc, rows, cols, dist, dtype):
+    say(f"fp8_quant gr={gr} gc={gc} {rows}x{cols} {dist} {dtype}")
+    if dist == "outliers":
+        x = workloads.dense_outliers(seed=100 + rows, m=rows, n=8, k=cols)["x"]
+    else:
+        x = workloads.sparse_large(seed=200 + rows, m=rows, n=rows, k=cols)["w" if dist == "weight" else "x"]
+    if dtype == "bf16":
+        bits = workloads.to_bf16_bits(x)
+        x_or = (bits.astype(np.uint32) << 16).view(np.float32)
+        xt = up(bits)
+    else:
+        x_or, xt = x, up(x)
+    q, s = sg.fp8_quant_groupwise(xt, gr=gr, gc=gc)
+    oq, os_ = oracle.fp8_quant_groupwise(x_or, gr, gc)
+    torch.cuda.synchronize()
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), os_.view(np.uint32))
+    assert np.array_equal(q.cpu().numpy(), oq)
+
+
+def test_fp8_encoder_on_every_midpoint_and_neighbour():
+    """Blocks whose amax is 448 have scale 1, so the codes are the encoder's
+    output for the raw values: every e4m3 midpoint, its fp32 neighbours, every
+    finite e4m3 value, signed zeros, subnormals and a million random values."""
+    pos = oracle.e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+    mid = ((pos[:-1] + pos[1:]) / 2).astype(np.float32)
+    vals = np.concatenate([mid, np.nextafter(mid, np.float32(1e9)), np.nextafter(mid, np.float32(0)),
+                           pos.astype(np.float32), np.array([0.0, 2.0 ** -10, 2.0 ** -12, 1e-30, 2.0 ** -6], np.float32)])
+    vals = np.concatenate([vals, -vals])
+    rng = np.random.default_rng(7)
+    rnd = (np.exp2(rng.uniform(-14, np.log2(448.0), 1_000_000)) *
+           np.where(rng.random(1_000_000) < 0.5, -1, 1)).astype(np.float32)
+    vals = np.concatenate([vals, rnd])
+    n = -(-len(vals) // 127) * 127
+    v = np.zeros(n, np.float32)
+    v[:len(vals)] = vals
+    x = np.concatenate([np.full((n // 127, 1), 448.0, np.float32), v.reshape(-1, 127)], axis=1)
+    say(f"encoder sweep: {x.shape}")
+    q, s = sg.fp8_quant_groupwise(up(x), gr=1, gc=128)
+    torch.cuda.synchronize()
+    assert np.all(s.cpu().numpy() == 1.0)
+    assert np.array_equal(q.cpu().numpy(), oracle.e4m3_encode(x))
+
+
+def test_fp8_quant_all_zero_and_scale_layouts():
+    x = np.zeros((5, 384), np.float32)
+    x[2, 130:140] = -3.5
+    x[4, 0] = -0.0
+    xt = up(x)
+    q, s = sg.fp8_quant_groupwise(xt, gr=1, gc=128)
+    oq, os_ = oracle.fp8_quant_groupwise(x, 1, 128)
+    assert np.array_equal(q.cpu().numpy(), oq) and np.array_equal(s.cpu().numpy(), os_)
+    # row-major scales through explicit strides
+    s_rm = torch.empty((5, 3), dtype=torch.float32, device=DEV)
+    sg.fp8_quant_groupwise(xt, gr=1, gc=128, s=s_rm)
+    assert np.array_equal(s_rm.cpu().numpy(), os_)
+
+
+def test_fp8_quant_strided_rows():
+    x = workloads.sparse_large(seed=9, m=40, n=8, k=512)["x"]
+    big = torch.zeros((40, 640), dtype=torch.float32, device=DEV)
+    big[:, :512] = up(x)
+    q = torch.zeros((40, 528), dtype=torch.uint8, device=DEV)
+    qv, s = sg.fp8_quant_groupwise(big[:, :512], gr=1, gc=128, q=q[:, :512])
+    oq, os_ = oracle.fp8_quant_groupwise(x, 1, 128)
+    assert np.array_equal(q[:, :512].cpu().numpy(), oq) and np.array_equal(s.cpu().numpy(), os_)
+    assert not q[:, 512:].any()
+
+
+@pytest.mark.parametrize("rows,cols,dtype", [(9, 384, "f32"), (2048, 4096, "f32"), (4096, 4096, "bf16"),
+                                             (1, 128, "bf16")])
+def test_int4_quant_matches_oracle(rows, cols, dtype):
+    say(f"int4_quant {rows}x{cols} {dtype}")
+    x = workloads.mixed_add(seed=300 + rows, m=rows, n=4, k1=cols, k2=32)["x1"]
+    if dtype == "bf16":
+        bits = workloads.to_bf16_bits(x)
+        x_or, xt = (bits.astype(np.uint32) << 16).view(np.float32), up(bits)
+    else:
+        x_or, xt = x, up(x)
+    q, s = sg.int4_quant_groupwise(xt)
+    oq, os_ = oracle.int4_quant_groupwise(x_or, 128)
+    torch.cuda.synchronize()
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), os_.view(np.uint32))
+    assert np.array_equal(q.cpu().numpy(), oq)
+
+
+def test_int4_quant_ties_round_to_even():
+    x = np.zeros((1, 128), np.float32)
+    x[0, :8] = [7.0, 0.5, 1.5, 2.5, -0.5, -1.5, -2.5, 3.5]
+    q, s = sg.int4_quant_groupwise(up(x))
+    oq, _ = oracle.int4_quant_groupwise(x, 128)
+    assert np.array_equal(q.cpu().numpy(), oq)
+    assert oracle.int4_decode(oq)[0, :8].tolist() == [7, 0, 2, 2, 0, -2, -2, 4]
+
+
+@pytest.mark.parametrize("rows,k,dtype", [(128, 256, "f32"), (4096, 4096, "f32"), (333, 520, "f32"),
+                                          (4096, 4096, "bf16"), (1, 8, "bf16")])
+def test_prune_compress_matches_oracle(rows, k, dtype):
+    say(f"prune {rows}x{k} {dtype}")
+    w = workloads.sparse_large(seed=400 + rows, m=4, n=rows, k=k)["w"]
+    wo = workloads.to_bf16_bits(w) if dtype == "bf16" else w
+    v, m = sg.sparse24_prune_compress(up(wo))
+    ov, om = oracle.prune_compress24(wo)
+    torch.cuda.synchronize()
+    got = v.cpu()
+    got = got.view(torch.int16).numpy().view(np.uint16) if dtype == "bf16" else got.numpy().view(np.uint32)
+    want = ov.view(np.uint16) if dtype == "bf16" else ov.view(np.uint32)
+    assert np.array_equal(m.cpu().numpy(), om)
+    assert np.array_equal(got, want)
+
+
+def test_prune_ties_signed_zeros_and_all_zero_rows():
+    """Every group of the 8-letter alphabet {+-0, +-1, +-2, +-3}^4 (4096
+    groups), plus an all-zero row: exact agreement with the oracle's ranking."""
+    import itertools
+    alphabet = np.array([0.0, -0.0, 1.0, -1.0, 2.0, -2.0, 3.0, -3.0], np.float32)
+    groups = alphabet[np.array(list(itertools.product(range(8), repeat=4)))].reshape(512, 32)
+    w = np.concatenate([groups, np.zeros((1, 32), np.float32)])
+    v, m = sg.sparse24_prune_compress(up(w))
+    ov, om = oracle.prune_compress24(w)
+    assert np.array_equal(m.cpu().numpy(), om)
+    assert np.array_equal(v.cpu().numpy().view(np.uint32), ov.view(np.uint32))
