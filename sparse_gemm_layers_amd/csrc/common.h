@@ -7,6 +7,14 @@
 
 #include "sg.h"
 
+// Device-only code (buffer resources and the kernel bodies that use them) is
+// hidden from the host compilation pass, which only needs the kernel stubs.
+#if defined(__HIP_DEVICE_COMPILE__)
+#define SG_DEVICE_PASS 1
+#else
+#define SG_DEVICE_PASS 0
+#endif
+
 namespace sg {
 
 typedef int v4i __attribute__((ext_vector_type(4)));

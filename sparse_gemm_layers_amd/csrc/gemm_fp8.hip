@@ -78,122 +78,241 @@ __device__ __forceinline__ int sp_a_off(int g) { return 32 * (g & 1) + 8 * (g >>
 // ============================================================ large-M kernel
 // Workgroup tile: 256 W rows (n) x 128 X rows (m), 4 waves in a 2 x 2 grid,
 // each wave 128 n x 64 m = 8 x 4 sub-tiles of 16 x 16.  One 128-wide K block
-// per stage, two stages in LDS (register-staged double buffering: the global
-// loads of block kb+1 are in flight while block kb is multiplied).
+// per pipeline stage.  Operands travel HBM -> LDS with buffer loads that
+// write LDS directly (no staging registers); NST stages are in flight, and a
+// wave waits only for the stage it is about to multiply.  Buffer resources
+// are based at the tile's first row and sized to the rows that exist, so rows
+// past M or N read as zero (the partial tiles) without any branch.
 //
 // LDS stage layout (bytes):
-//   X    : 128 rows x 128 B; 16-byte chunk c of row r at chunk c ^ (r & 7)
+//   X    : 128 rows x 128 B; 16-byte chunk c of row r stored at chunk c ^ (r & 7)
 //   W    : dense 256 rows x 128 B (same swizzle as X), or
-//          sparse 256 rows x 64 B of values; 16-byte slot s holds lane group
-//          s's operand bytes; slot s of row r at s ^ ((r >> 1) & 3)
-//   meta : sparse only, 256 rows x 16 B, word g = lane group g's index
-//   sx   : 128 floats (scale of X row r for this K block)
-//   sw   : 256 floats (scale of W row r for this K block)
+//          sparse 256 rows x 64 B of values; chunk c of row r at c ^ ((r >> 1) & 3)
+//   meta : sparse only, 256 rows x 16 B, unswizzled
+//   sx   : 128 floats, scale of X row r for the stage's K block (+ a copy slot)
+//   sw   : 256 floats, scale of W row r
 constexpr int BN = 256, BM = 128;
-constexpr int X_BYTES = BM * 128;
+constexpr unsigned RSRC_WORD3 = 0x00020000u;   // gfx9-family raw buffer, 32-bit dwords
+
+typedef __attribute__((address_space(3))) void lds_void;
 
 template <bool SPARSE>
 struct Stage {
-  static constexpr int W_BYTES = SPARSE ? BN * 64 : BN * 128;
-  static constexpr int M_BYTES = SPARSE ? BN * 16 : 0;
+  static constexpr int NST = SPARSE ? 4 : 3;                   // pipeline depth
   static constexpr int X_OFF = 0;
-  static constexpr int W_OFF = X_OFF + X_BYTES;
+  static constexpr int W_OFF = BM * 128;
+  static constexpr int W_BYTES = SPARSE ? BN * 64 : BN * 128;
   static constexpr int M_OFF = W_OFF + W_BYTES;
-  static constexpr int SX_OFF = M_OFF + M_BYTES;
-  static constexpr int SW_OFF = SX_OFF + BM * 4;
+  static constexpr int M_BYTES = SPARSE ? BN * 16 : 0;
+  static constexpr int SX_OFF = M_OFF + M_BYTES;               // 2 x 128 floats (second is a dummy copy)
+  static constexpr int SW_OFF = SX_OFF + 2 * BM * 4;
   static constexpr int BYTES = SW_OFF + BN * 4;
+  // buffer-load instructions per wave per stage (identical for every wave)
+  static constexpr int LOADS = 4 + (SPARSE ? 4 + 1 : 8) + 2;
+};
+
+#if SG_DEVICE_PASS
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, (int)RSRC_WORD3);
+}
+
+// Per-thread source offsets, fixed for the whole K loop (the K block enters
+// through the scalar offset).
+template <bool SPARSE>
+struct LoadPlan {
+  uint32_t xo[4], wo[SPARSE ? 4 : 8], mo, sxo, swo;
 };
 
 template <bool SPARSE>
-struct Staged {
-  uint4 x[4];
-  uint4 w[SPARSE ? 4 : 8];
-  uint4 m;
-  float sx, sw;
-};
-
-template <bool SPARSE>
-__device__ __forceinline__ void stage_load(const GemmArgs& a, int64_t n0, int64_t m0, int kb, int t,
-                                           Staged<SPARSE>& s) {
-  const uint4 zero = {0u, 0u, 0u, 0u};
-  // X: 1024 chunks of 16 B, 8 per row
+__device__ __forceinline__ LoadPlan<SPARSE> make_plan(const GemmArgs& a, int64_t n0, int64_t m0, int wave, int l) {
+  LoadPlan<SPARSE> p;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int i = t + 256 * j;
-    const int r = i >> 3, c = i & 7;
-    const int64_t m = m0 + r;
-    s.x[j] = m < a.M ? *reinterpret_cast<const uint4*>(a.x + m * a.ldx + (int64_t)kb * 128 + c * 16) : zero;
+  for (int j = 0; j < 4; ++j) {              // X: wave-load q = 4 j + wave covers 16-byte slots 64 q .. 64 q + 63
+    const int s = (4 * j + wave) * 64 + l;
+    const int r = s >> 3, c = (s & 7) ^ (r & 7);
+    p.xo[j] = (uint32_t)(r * a.ldx + c * 16);
   }
   if (SPARSE) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int i = t + 256 * j;
-      const int r = i >> 2, c = i & 3;
-      const int64_t n = n0 + r;
-      s.w[j] = n < a.N ? *reinterpret_cast<const uint4*>(a.w + n * a.ldw + (int64_t)kb * 64 + c * 16) : zero;
+      const int s = (4 * j + wave) * 64 + l;
+      const int r = s >> 2, c = (s & 3) ^ ((r >> 1) & 3);
+      p.wo[j] = (uint32_t)(r * a.ldw + c * 16);
     }
-    const int64_t n = n0 + t;
-    s.m = n < a.N ? *reinterpret_cast<const uint4*>(a.meta + n * a.ldm + (int64_t)kb * 16) : zero;
+    p.mo = (uint32_t)((wave * 64 + l) * a.ldm);
   } else {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int i = t + 256 * j;
-      const int r = i >> 3, c = i & 7;
-      const int64_t n = n0 + r;
-      s.w[j] = n < a.N ? *reinterpret_cast<const uint4*>(a.w + n * a.ldw + (int64_t)kb * 128 + c * 16) : zero;
+      const int s = (4 * j + wave) * 64 + l;
+      const int r = s >> 3, c = (s & 7) ^ (r & 7);
+      p.wo[j] = (uint32_t)(r * a.ldw + c * 16);
     }
+    p.mo = 0;
   }
-  {
-    const int64_t m = m0 + (t & 127);
-    s.sx = (t < 128 && m < a.M) ? a.sx[(m >> a.gm_shift) * a.sx_sm + (int64_t)kb * a.sx_sk] : 0.f;
-    const int64_t n = n0 + t;
-    s.sw = n < a.N ? a.sw[(n >> a.gn_shift) * a.sw_sn + (int64_t)kb * a.sw_sk] : 0.f;
-  }
+  // scales: rows past M / N are clamped to the last row (their results are never stored)
+  const int64_t m = min(m0 + (int64_t)(wave & 1) * 64 + l, a.M - 1);
+  const int64_t n = min(n0 + (int64_t)wave * 64 + l, a.N - 1);
+  p.sxo = (uint32_t)(((m >> a.gm_shift) * a.sx_sm) * 4);
+  p.swo = (uint32_t)(((n >> a.gn_shift) * a.sw_sn) * 4);
+  return p;
 }
 
 template <bool SPARSE>
-__device__ __forceinline__ void stage_store(uint8_t* st, int t, const Staged<SPARSE>& s) {
+__device__ __forceinline__ void issue_stage(uint8_t* st, const LoadPlan<SPARSE>& p, __amdgpu_buffer_rsrc_t rx,
+                                            __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t rm,
+                                            __amdgpu_buffer_rsrc_t rsx, __amdgpu_buffer_rsrc_t rsw,
+                                            const GemmArgs& a, int kb, int wave) {
   using L = Stage<SPARSE>;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int i = t + 256 * j;
-    const int r = i >> 3, c = i & 7;
-    *reinterpret_cast<uint4*>(st + L::X_OFF + r * 128 + ((c ^ (r & 7)) << 4)) = s.x[j];
-  }
+  for (int j = 0; j < 4; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(st + L::X_OFF + (4 * j + wave) * 1024), 16, p.xo[j],
+                                             kb * 128, 0, 0);
   if (SPARSE) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int i = t + 256 * j;
-      const int r = i >> 2, c = i & 3;
-      const int sw = (r >> 1) & 3;
-      // low 8 B = 8-byte chunk 2c -> slot c>>1; high 8 B = chunk 2c+1 -> slot 2 + (c>>1);
-      // both in half (c & 1) of their slot
-      uint8_t* row = st + L::W_OFF + r * 64 + ((c & 1) << 3);
-      *reinterpret_cast<uint2*>(row + ((((c >> 1)) ^ sw) << 4)) = make_uint2(s.w[j].x, s.w[j].y);
-      *reinterpret_cast<uint2*>(row + (((2 + (c >> 1)) ^ sw) << 4)) = make_uint2(s.w[j].z, s.w[j].w);
-    }
-    uint4 o;
-    o.x = sp_meta_word(s.m, 0);
-    o.y = sp_meta_word(s.m, 1);
-    o.z = sp_meta_word(s.m, 2);
-    o.w = sp_meta_word(s.m, 3);
-    *reinterpret_cast<uint4*>(st + L::M_OFF + t * 16) = o;
+    for (int j = 0; j < 4; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(st + L::W_OFF + (4 * j + wave) * 1024), 16, p.wo[j],
+                                               kb * 64, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rm, (lds_void*)(st + L::M_OFF + wave * 1024), 16, p.mo, kb * 16, 0, 0);
   } else {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int i = t + 256 * j;
-      const int r = i >> 3, c = i & 7;
-      *reinterpret_cast<uint4*>(st + L::W_OFF + r * 128 + ((c ^ (r & 7)) << 4)) = s.w[j];
+    for (int j = 0; j < 8; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(st + L::W_OFF + (4 * j + wave) * 1024), 16, p.wo[j],
+                                               kb * 128, 0, 0);
+  }
+  // waves 0,1 fill sx[0..127]; waves 2,3 load the same values into the dummy copy
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsx, (lds_void*)(st + L::SX_OFF + wave * 256), 4, p.sxo,
+                                           (int)(kb * a.sx_sk * 4), 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, (lds_void*)(st + L::SW_OFF + wave * 256), 4, p.swo,
+                                           (int)(kb * a.sw_sk * 4), 0, 0);
+}
+
+#endif  // SG_DEVICE_PASS
+
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <bool SPARSE>
+__device__ __forceinline__ void wait_stage(int later_stages) {
+  constexpr int L = Stage<SPARSE>::LOADS;
+  if (later_stages >= 2) wait_vmcnt<2 * L>();
+  else if (later_stages == 1) wait_vmcnt<L>();
+  else wait_vmcnt<0>();
+}
+
+// Lane-constant LDS byte offsets of the wave's operands within a stage.  The
+// swizzles only depend on the row modulo 8 (X, dense W) or on (row >> 1) & 3
+// (sparse W), and every sub-tile starts at a multiple of 16 rows, so each
+// lane's swizzled offset is fixed; sub-tiles are reached by immediate offsets.
+template <bool SPARSE>
+struct LaneOffsets {
+  uint32_t x0, x1;   // X row wm*64 + lr: the two 16-byte chunks of lane group g
+  uint32_t w0, w1;   // W row wn*128 + lr: dense 16-byte chunks / sparse 8-byte halves
+  uint32_t mt;       // metadata word pair of lane group g
+  uint32_t sx;       // X scale of row wm*64 + lr
+};
+
+template <bool SPARSE>
+__device__ __forceinline__ LaneOffsets<SPARSE> lane_offsets(int wn, int wm, int g, int lr) {
+  using L = Stage<SPARSE>;
+  LaneOffsets<SPARSE> o;
+  const int xr = wm * 64 + lr, wr = wn * 128 + lr;
+  o.x0 = L::X_OFF + xr * 128 + (((2 * g) ^ (lr & 7)) << 4);
+  o.x1 = L::X_OFF + xr * 128 + (((2 * g + 1) ^ (lr & 7)) << 4);
+  if (SPARSE) {
+    const int sw = (lr >> 1) & 3;
+    const int a0 = sp_a_off(g), a1 = a0 + 16;
+    o.w0 = L::W_OFF + wr * 64 + ((((a0 >> 4) ^ sw) << 4) | (a0 & 15));
+    o.w1 = L::W_OFF + wr * 64 + ((((a1 >> 4) ^ sw) << 4) | (a1 & 15));
+    o.mt = L::M_OFF + wr * 16 + 8 * (g & 1);
+  } else {
+    o.w0 = L::W_OFF + wr * 128 + (((2 * g) ^ (lr & 7)) << 4);
+    o.w1 = L::W_OFF + wr * 128 + (((2 * g + 1) ^ (lr & 7)) << 4);
+    o.mt = 0;
+  }
+  o.sx = L::SX_OFF + xr * 4;
+  return o;
+}
+
+template <typename T>
+__device__ __forceinline__ T lds_ld(const uint8_t* st, uint32_t off) {
+  return *reinterpret_cast<const T*>(st + off);
+}
+
+// Multiplies one LDS stage into the wave's 8 x 4 sub-tiles and promotes.
+template <bool SPARSE, int GRAN_N>
+__device__ __forceinline__ void compute_stage(const uint8_t* st, v4f (&acc)[8][4], const LaneOffsets<SPARSE>& o,
+                                              int wn, int g, uint32_t msel) {
+  using L = Stage<SPARSE>;
+  float sxj[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) sxj[j] = lds_ld<float>(st, o.sx + j * 64);
+
+  v8i bx[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint4 lo = lds_ld<uint4>(st, o.x0 + j * 2048);
+    const uint4 hi = lds_ld<uint4>(st, o.x1 + j * 2048);
+    bx[j] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  }
+  float s128[4];
+  if (GRAN_N == 128) {
+    const float swv = lds_ld<float>(st, L::SW_OFF + wn * 512);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s128[j] = sxj[j] * swv;
+  }
+
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float4 swr = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (GRAN_N == 1) swr = lds_ld<float4>(st, L::SW_OFF + (wn * 128 + i * 16 + 4 * g) * 4);
+    v4f p[4];
+    if (SPARSE) {
+      const uint2 v0 = lds_ld<uint2>(st, o.w0 + i * 1024);
+      const uint2 v1 = lds_ld<uint2>(st, o.w1 + i * 1024);
+      const uint2 mw = lds_ld<uint2>(st, o.mt + i * 256);
+      const int idx = (int)__builtin_amdgcn_perm(mw.y, mw.x, msel);
+      const v4i aa = {(int)v0.x, (int)v0.y, (int)v1.x, (int)v1.y};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) p[j] = mma_sparse(aa, bx[j], idx);
+    } else {
+      const uint4 lo = lds_ld<uint4>(st, o.w0 + i * 2048);
+      const uint4 hi = lds_ld<uint4>(st, o.w1 + i * 2048);
+      const v8i aa = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) p[j] = mma_dense(aa, bx[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (GRAN_N == 128) {
+        acc[i][j] += p[j] * s128[j];
+      } else {
+        acc[i][j][0] = fmaf(p[j][0] * swr.x, sxj[j], acc[i][j][0]);
+        acc[i][j][1] = fmaf(p[j][1] * swr.y, sxj[j], acc[i][j][1]);
+        acc[i][j][2] = fmaf(p[j][2] * swr.z, sxj[j], acc[i][j][2]);
+        acc[i][j][3] = fmaf(p[j][3] * swr.w, sxj[j], acc[i][j][3]);
+      }
     }
   }
-  if (t < 128) reinterpret_cast<float*>(st + L::SX_OFF)[t] = s.sx;
-  reinterpret_cast<float*>(st + L::SW_OFF)[t] = s.sw;
 }
 
 template <bool SPARSE, int GRAN_N, bool OUT_BF16, bool OUT_T>
 __global__ void __launch_bounds__(256, 1) k_gemm_large(GemmArgs a, int tiles_m, int tiles_n) {
+#if SG_DEVICE_PASS
   using L = Stage<SPARSE>;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * L::BYTES];
+  constexpr int NST = L::NST;
+  static_assert(NST >= 3 && NST <= 4, "wait_stage handles at most two later stages");
+  // One array per stage: LDS reads of one stage then provably do not alias the
+  // buffer loads in flight into the others, so no extra wait is inserted.
+  __shared__ __attribute__((aligned(1024))) uint8_t sm0[L::BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t sm1[L::BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t sm2[L::BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t sm3[NST > 3 ? L::BYTES : 16];
+  uint8_t* const buf[4] = {sm0, sm1, sm2, sm3};
 
   // Workgroups go to the 8 XCDs round-robin.  Renumber so that each XCD owns
   // a contiguous range of tile ids, then walk tiles in groups of 4 n-tiles so
@@ -210,10 +329,21 @@ __global__ void __launch_bounds__(256, 1) k_gemm_large(GemmArgs a, int tiles_m, 
   const int tm = in_g / gsize;
   const int64_t n0 = (int64_t)tn * BN, m0 = (int64_t)tm * BM;
 
-  const int t = threadIdx.x, l = t & 63, wave = t >> 6;
+  const int t = threadIdx.x, l = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wn = wave & 1, wm = wave >> 1;
   const int g = l >> 4, lr = l & 15;
   const int KB = (int)(a.K >> 7);
+
+  const int64_t mrows = min((int64_t)BM, a.M - m0), nrows = min((int64_t)BN, a.N - n0);
+  const __amdgpu_buffer_rsrc_t rx = rsrc(a.x + m0 * a.ldx, (uint32_t)(mrows * a.ldx));
+  const __amdgpu_buffer_rsrc_t rw = rsrc(a.w + n0 * a.ldw, (uint32_t)(nrows * a.ldw));
+  const __amdgpu_buffer_rsrc_t rm = rsrc(SPARSE ? a.meta + n0 * a.ldm : a.w, SPARSE ? (uint32_t)(nrows * a.ldm) : 0u);
+  const __amdgpu_buffer_rsrc_t rsx = rsrc(a.sx, 0xffffffffu);
+  const __amdgpu_buffer_rsrc_t rsw = rsrc(a.sw, 0xffffffffu);
+  const LoadPlan<SPARSE> plan = make_plan<SPARSE>(a, n0, m0, wave, l);
+  const uint32_t msel = (g >> 1) ? 0x07060302u : 0x05040100u;   // metadata halves of this lane group
+  const LaneOffsets<SPARSE> lo = lane_offsets<SPARSE>(wn, wm, g, lr);
 
   v4f acc[8][4];
 #pragma unroll
@@ -221,83 +351,22 @@ __global__ void __launch_bounds__(256, 1) k_gemm_large(GemmArgs a, int tiles_m, 
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-  Staged<SPARSE> stg;
-  stage_load<SPARSE>(a, n0, m0, 0, t, stg);
-  stage_store<SPARSE>(smem, t, stg);
-  __syncthreads();
+#pragma unroll
+  for (int s = 0; s < NST - 1; ++s)
+    if (s < KB) issue_stage<SPARSE>(buf[s], plan, rx, rw, rm, rsx, rsw, a, s, wave);
 
-  for (int kb = 0; kb < KB; ++kb) {
-    const uint8_t* st = smem + (kb & 1) * L::BYTES;
-    if (kb + 1 < KB) stage_load<SPARSE>(a, n0, m0, kb + 1, t, stg);
-
-    // scales of this K block
-    const float* sxs = reinterpret_cast<const float*>(st + L::SX_OFF);
-    const float* sws = reinterpret_cast<const float*>(st + L::SW_OFF);
-    float sxj[4];
+  for (int kb0 = 0; kb0 < KB; kb0 += NST) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) sxj[j] = sxs[wm * 64 + j * 16 + lr];
-
-    // X operands (B side) of the wave's 4 column sub-tiles
-    v8i bx[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = wm * 64 + j * 16 + lr;
-      const uint8_t* row = st + L::X_OFF + r * 128;
-      const uint4 lo = *reinterpret_cast<const uint4*>(row + (((2 * g) ^ (r & 7)) << 4));
-      const uint4 hi = *reinterpret_cast<const uint4*>(row + (((2 * g + 1) ^ (r & 7)) << 4));
-      bx[j] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    }
-
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = wn * 128 + i * 16 + lr;
-      float s[4];
-      if (GRAN_N == 128) {
-        const float swv = sws[wn * 128];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) s[j] = sxj[j] * swv;
-      }
-      float4 swr;
-      if (GRAN_N == 1) swr = *reinterpret_cast<const float4*>(sws + wn * 128 + i * 16 + 4 * g);
-      if (SPARSE) {
-        const int sl = g ^ ((r >> 1) & 3);
-        const uint4 av = *reinterpret_cast<const uint4*>(st + L::W_OFF + r * 64 + (sl << 4));
-        const int idx = *reinterpret_cast<const int*>(st + L::M_OFF + r * 16 + g * 4);
-        const v4i aa = {(int)av.x, (int)av.y, (int)av.z, (int)av.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const v4f p = mma_sparse(aa, bx[j], idx);
-          if (GRAN_N == 128) {
-            acc[i][j] += p * s[j];
-          } else {
-            acc[i][j][0] = fmaf(p[0] * swr.x, sxj[j], acc[i][j][0]);
-            acc[i][j][1] = fmaf(p[1] * swr.y, sxj[j], acc[i][j][1]);
-            acc[i][j][2] = fmaf(p[2] * swr.z, sxj[j], acc[i][j][2]);
-            acc[i][j][3] = fmaf(p[3] * swr.w, sxj[j], acc[i][j][3]);
-          }
-        }
-      } else {
-        const uint8_t* row = st + L::W_OFF + r * 128;
-        const uint4 lo = *reinterpret_cast<const uint4*>(row + (((2 * g) ^ (r & 7)) << 4));
-        const uint4 hi = *reinterpret_cast<const uint4*>(row + (((2 * g + 1) ^ (r & 7)) << 4));
-        const v8i aa = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const v4f p = mma_dense(aa, bx[j]);
-          if (GRAN_N == 128) {
-            acc[i][j] += p * s[j];
-          } else {
-            acc[i][j][0] = fmaf(p[0] * swr.x, sxj[j], acc[i][j][0]);
-            acc[i][j][1] = fmaf(p[1] * swr.y, sxj[j], acc[i][j][1]);
-            acc[i][j][2] = fmaf(p[2] * swr.z, sxj[j], acc[i][j][2]);
-            acc[i][j][3] = fmaf(p[3] * swr.w, sxj[j], acc[i][j][3]);
-          }
-        }
+    for (int u = 0; u < NST; ++u) {
+      const int kb = kb0 + u;
+      if (kb < KB) {
+        wait_stage<SPARSE>(min(NST - 2, KB - 1 - kb));
+        __syncthreads();
+        if (kb + NST - 1 < KB)
+          issue_stage<SPARSE>(buf[(u + NST - 1) % NST], plan, rx, rw, rm, rsx, rsw, a, kb + NST - 1, wave);
+        compute_stage<SPARSE, GRAN_N>(buf[u], acc, lo, wn, g, msel);
       }
     }
-
-    if (kb + 1 < KB) stage_store<SPARSE>(smem + ((kb + 1) & 1) * L::BYTES, t, stg);
-    __syncthreads();
   }
 
   // Epilogue: lane holds D[n = n0 + wn*128 + 16 i + 4 g + e][m = m0 + wm*64 + 16 j + lr].
@@ -306,6 +375,7 @@ __global__ void __launch_bounds__(256, 1) k_gemm_large(GemmArgs a, int tiles_m, 
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       store_quad<OUT_BF16, OUT_T>(a, m0 + wm * 64 + j * 16 + lr, n0 + wn * 128 + i * 16 + 4 * g, acc[i][j]);
+#endif  // SG_DEVICE_PASS
 }
 
 // ============================================================ decode kernel
@@ -451,8 +521,9 @@ static void launch_gemm(const GemmArgs& a, int gran_n, bool bf16, bool yt, hipSt
 
 // Common argument checks of both GEMM entry points (host only, before any HIP call).
 static sg_status check_common(int64_t M, int64_t N, int64_t K, const uint8_t* xq, int64_t ldx,
-                              const float* sx, int gran_m, const float* sw, int gran_n, void* y,
-                              sg_dtype y_dt, int64_t ldy, sg_form form) {
+                              const float* sx, int64_t sx_sm, int64_t sx_sk, int gran_m, const float* sw,
+                              int64_t sw_sn, int64_t sw_sk, int gran_n, void* y, sg_dtype y_dt, int64_t ldy,
+                              sg_form form) {
   if (!xq || !sx || !sw || !y) return SG_ERR_NULL;
   if ((gran_m != 1 && gran_m != 128) || (gran_n != 1 && gran_n != 128)) return SG_ERR_UNSUPPORTED;
   if (y_dt != SG_F32 && y_dt != SG_BF16) return SG_ERR_UNSUPPORTED;
@@ -460,6 +531,10 @@ static sg_status check_common(int64_t M, int64_t N, int64_t K, const uint8_t* xq
   if (M < 0 || N < 0 || K <= 0 || K % 128 != 0 || ldx < K) return SG_ERR_SHAPE;
   if (ldy < (form == SG_OUT_Y ? N : M)) return SG_ERR_SHAPE;
   if (cdiv(M, 128) * cdiv(N, 256) > 0x7fffffffLL || cdiv(N, 16) > 0x7fffffffLL) return SG_ERR_SHAPE;
+  // The large-M kernel addresses tiles and scales with 32-bit buffer offsets.
+  if (ldx > (1LL << 24) || sx_sm < 0 || sx_sk < 0 || sw_sn < 0 || sw_sk < 0) return SG_ERR_SHAPE;
+  if (((cdiv(M, gran_m) - 1) * sx_sm + (K / 128 - 1) * sx_sk) * 4 >= (1LL << 31)) return SG_ERR_SHAPE;
+  if (((cdiv(N, gran_n) - 1) * sw_sn + (K / 128 - 1) * sw_sk) * 4 >= (1LL << 31)) return SG_ERR_SHAPE;
   if (!aligned(xq, 16) || ldx % 16 || !aligned(sx, 4) || !aligned(sw, 4) || !aligned(y, dtype_size(y_dt)))
     return SG_ERR_ALIGN;
   return SG_OK;
@@ -491,10 +566,10 @@ extern "C" sg_status sg_fp8_gemm_groupwise(int64_t M, int64_t N, int64_t K, cons
                                            int64_t ldw, const float* sw, int64_t sw_sn,
                                            int64_t sw_sk, int gran_n, void* y, sg_dtype y_dt,
                                            int64_t ldy, sg_form form, hipStream_t stream) {
-  sg_status st = check_common(M, N, K, xq, ldx, sx, gran_m, sw, gran_n, y, y_dt, ldy, form);
+  sg_status st = check_common(M, N, K, xq, ldx, sx, sx_sm, sx_sk, gran_m, sw, sw_sn, sw_sk, gran_n, y, y_dt, ldy, form);
   if (st != SG_OK) return st;
   if (!wq) return SG_ERR_NULL;
-  if (ldw < K) return SG_ERR_SHAPE;
+  if (ldw < K || ldw > (1LL << 24)) return SG_ERR_SHAPE;
   if (!aligned(wq, 16) || ldw % 16) return SG_ERR_ALIGN;
   if (M == 0 || N == 0) return SG_OK;
   const GemmArgs a = make_args(M, N, K, xq, ldx, sx, sx_sm, sx_sk, gran_m, wq, ldw, nullptr, 0, sw, sw_sn,
@@ -511,10 +586,10 @@ extern "C" sg_status sg_fp8_sparse24_gemm_groupwise(int64_t M, int64_t N, int64_
                                                     const float* sw, int64_t sw_sn, int64_t sw_sk,
                                                     int gran_n, void* y, sg_dtype y_dt, int64_t ldy,
                                                     sg_form form, hipStream_t stream) {
-  sg_status st = check_common(M, N, K, xq, ldx, sx, gran_m, sw, gran_n, y, y_dt, ldy, form);
+  sg_status st = check_common(M, N, K, xq, ldx, sx, sx_sm, sx_sk, gran_m, sw, sw_sn, sw_sk, gran_n, y, y_dt, ldy, form);
   if (st != SG_OK) return st;
   if (!wv || !wmeta) return SG_ERR_NULL;
-  if (ldwv < K / 2 || ldwm < K / 8) return SG_ERR_SHAPE;
+  if (ldwv < K / 2 || ldwm < K / 8 || ldwv > (1LL << 24) || ldwm > (1LL << 24)) return SG_ERR_SHAPE;
   if (!aligned(wv, 16) || !aligned(wmeta, 16) || ldwv % 16 || ldwm % 16) return SG_ERR_ALIGN;
   if (M == 0 || N == 0) return SG_OK;
   const GemmArgs a = make_args(M, N, K, xq, ldx, sx, sx_sm, sx_sk, gran_m, wv, ldwv, wmeta, ldwm, sw, sw_sn,
