@@ -300,6 +300,22 @@ __device__ __forceinline__ void compute_stage(const uint8_t* st, v4f (&acc)[8][4
   }
 }
 
+// Workgroups go to the 8 XCDs round-robin.  Renumber so that each XCD owns a
+// contiguous range of tile ids, then walk tiles in groups of 4 n-tiles so that
+// the tiles resident on one XCD share W rows and X rows in its L2.
+__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tn, int& tm) {
+  const int T = tiles_m * tiles_n;
+  int b = blockIdx.x;
+  if ((T & 7) == 0) b = (b & 7) * (T >> 3) + (b >> 3);
+  const int G = 4;
+  const int group = b / (G * tiles_m);
+  const int first_n = group * G;
+  const int gsize = min(tiles_n - first_n, G);
+  const int in_g = b - group * G * tiles_m;
+  tn = first_n + in_g % gsize;
+  tm = in_g / gsize;
+}
+
 template <bool SPARSE, int GRAN_N, bool OUT_BF16, bool OUT_T>
 __global__ void __launch_bounds__(256, 1) k_gemm_large(GemmArgs a, int tiles_m, int tiles_n) {
 #if SG_DEVICE_PASS
@@ -314,19 +330,8 @@ __global__ void __launch_bounds__(256, 1) k_gemm_large(GemmArgs a, int tiles_m, 
   __shared__ __attribute__((aligned(1024))) uint8_t sm3[NST > 3 ? L::BYTES : 16];
   uint8_t* const buf[4] = {sm0, sm1, sm2, sm3};
 
-  // Workgroups go to the 8 XCDs round-robin.  Renumber so that each XCD owns
-  // a contiguous range of tile ids, then walk tiles in groups of 4 n-tiles so
-  // that an XCD's tiles share W rows and X rows in its L2.
-  const int T = tiles_m * tiles_n;
-  int b = blockIdx.x;
-  if ((T & 7) == 0) b = (b & 7) * (T >> 3) + (b >> 3);
-  const int G = 4;
-  const int group = b / (G * tiles_m);
-  const int first_n = group * G;
-  const int gsize = min(tiles_n - first_n, G);
-  const int in_g = b - group * G * tiles_m;
-  const int tn = first_n + in_g % gsize;
-  const int tm = in_g / gsize;
+  int tn, tm;
+  tile_coords(tiles_m, tiles_n, tn, tm);
   const int64_t n0 = (int64_t)tn * BN, m0 = (int64_t)tm * BM;
 
   const int t = threadIdx.x, l = t & 63;
@@ -375,6 +380,195 @@ __global__ void __launch_bounds__(256, 1) k_gemm_large(GemmArgs a, int tiles_m, 
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       store_quad<OUT_BF16, OUT_T>(a, m0 + wm * 64 + j * 16 + lr, n0 + wn * 128 + i * 16 + 4 * g, acc[i][j]);
+#endif  // SG_DEVICE_PASS
+}
+
+// ================================================ sparse kernel, 2 waves / SIMD
+// Same 256 x 128 workgroup tile and the same per-wave 128 x 64 sub-tile as
+// k_gemm_large, but 8 waves: two K groups of 4 waves.  Group q multiplies the
+// K blocks kb = 2 it + q, so two waves share every SIMD and one wave's LDS,
+// barrier and matrix-core latencies hide behind the other's work.  A "double
+// stage" holds K blocks 2 it and 2 it + 1 (two copies of the single-stage
+// layout); two double stages alternate in LDS.  At the end the two groups add
+// their partial tiles through LDS, each group finishing half of the rows.
+namespace x2 {
+constexpr int HALF = Stage<true>::BYTES;   // one K block
+constexpr int DBL = 2 * HALF;              // double stage
+}  // namespace x2
+
+#if SG_DEVICE_PASS
+struct PlanX2 {
+  uint32_t xo[4], wo[4], mo, so[2];
+  uint32_t sdst[2];     // LDS offsets (within the double stage) of the two scale loads
+  int sk[2];            // which scale: 0 = sx, 1 = sw
+};
+
+__device__ __forceinline__ PlanX2 make_plan_x2(const GemmArgs& a, int64_t n0, int64_t m0, int wave, int l) {
+  using L = Stage<true>;
+  PlanX2 p;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int slot = (8 * j + wave) & 15;      // 1 KB slot within the K block's X / W area
+    {
+      const int s = slot * 64 + l;
+      const int r = s >> 3, c = (s & 7) ^ (r & 7);
+      p.xo[j] = (uint32_t)(r * a.ldx + c * 16);
+    }
+    {
+      const int s = slot * 64 + l;
+      const int r = s >> 2, c = (s & 3) ^ ((r >> 1) & 3);
+      p.wo[j] = (uint32_t)(r * a.ldw + c * 16);
+    }
+  }
+  p.mo = (uint32_t)((((wave & 3) * 64) + l) * a.ldm);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int sidx = 2 * wave + j, h = sidx >> 3, t = sidx & 7;
+    if (t < 2 || t >= 6) {         // sx rows 64 t' .. 64 t' + 63 (t >= 6: the dummy copy)
+      const int tp = t < 2 ? t : t - 6;
+      const int64_t m = min(m0 + tp * 64 + l, a.M - 1);
+      p.so[j] = (uint32_t)(((m >> a.gm_shift) * a.sx_sm) * 4);
+      p.sdst[j] = h * x2::HALF + L::SX_OFF + (t < 2 ? 0 : BM * 4) + tp * 256;
+      p.sk[j] = 0;
+    } else {                       // sw rows 64 (t - 2) ..
+      const int64_t n = min(n0 + (t - 2) * 64 + l, a.N - 1);
+      p.so[j] = (uint32_t)(((n >> a.gn_shift) * a.sw_sn) * 4);
+      p.sdst[j] = h * x2::HALF + L::SW_OFF + (t - 2) * 256;
+      p.sk[j] = 1;
+    }
+  }
+  return p;
+}
+
+// Loads K blocks kb0 and kb0 + 1 (clamped to the last block) into a double stage.
+__device__ __forceinline__ void issue_double(uint8_t* st, const PlanX2& p, __amdgpu_buffer_rsrc_t rx,
+                                             __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t rm,
+                                             __amdgpu_buffer_rsrc_t rsx, __amdgpu_buffer_rsrc_t rsw,
+                                             const GemmArgs& a, int kb0, int KB, int wave) {
+  using L = Stage<true>;
+  const int kbh[2] = {min(kb0, KB - 1), min(kb0 + 1, KB - 1)};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int h = j >> 1, slot = (8 * j + wave) & 15;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(st + h * x2::HALF + L::X_OFF + slot * 1024), 16,
+                                             p.xo[j], kbh[h] * 128, 0, 0);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int h = j >> 1, slot = (8 * j + wave) & 15;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(st + h * x2::HALF + L::W_OFF + slot * 1024), 16,
+                                             p.wo[j], kbh[h] * 64, 0, 0);
+  }
+  {
+    const int h = wave >> 2;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rm, (lds_void*)(st + h * x2::HALF + L::M_OFF + (wave & 3) * 1024), 16,
+                                             p.mo, kbh[h] * 16, 0, 0);
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int h = (2 * wave + j) >> 3;
+    if (p.sk[j] == 0)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsx, (lds_void*)(st + p.sdst[j]), 4, p.so[j],
+                                               (int)(kbh[h] * a.sx_sk * 4), 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, (lds_void*)(st + p.sdst[j]), 4, p.so[j],
+                                               (int)(kbh[h] * a.sw_sk * 4), 0, 0);
+  }
+}
+#endif  // SG_DEVICE_PASS
+
+// Partial-tile exchange between the two K groups (rows I0 .. I0+3 of the
+// wave's 8 x 4 sub-tiles).
+template <int I0>
+__device__ __forceinline__ void xchg_out(float4* dst, const v4f (&acc)[8][4], int w4, int l) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const v4f v = acc[I0 + i][j];
+      dst[((w4 * 16 + i * 4 + j) << 6) + l] = make_float4(v[0], v[1], v[2], v[3]);
+    }
+}
+
+template <int I0, bool OUT_BF16, bool OUT_T>
+__device__ __forceinline__ void xchg_in_store(const float4* src, const v4f (&acc)[8][4], const GemmArgs& a, int w4,
+                                              int l, int64_t m0, int64_t n0, int wn, int wm, int g, int lr) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4 o = src[((w4 * 16 + i * 4 + j) << 6) + l];
+      v4f v = acc[I0 + i][j];
+      v[0] += o.x; v[1] += o.y; v[2] += o.z; v[3] += o.w;
+      store_quad<OUT_BF16, OUT_T>(a, m0 + wm * 64 + j * 16 + lr, n0 + wn * 128 + (I0 + i) * 16 + 4 * g, v);
+    }
+}
+
+template <int GRAN_N, bool OUT_BF16, bool OUT_T>
+__global__ void __launch_bounds__(512) k_gemm_sparse_x2(GemmArgs a, int tiles_m, int tiles_n) {
+#if SG_DEVICE_PASS
+  __shared__ __attribute__((aligned(1024))) uint8_t db0[x2::DBL];
+  __shared__ __attribute__((aligned(1024))) uint8_t db1[x2::DBL];
+
+  int tn, tm;
+  tile_coords(tiles_m, tiles_n, tn, tm);
+  const int64_t n0 = (int64_t)tn * BN, m0 = (int64_t)tm * BM;
+
+  const int t = threadIdx.x, l = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int q = wave >> 2, w4 = wave & 3;
+  const int wn = w4 & 1, wm = w4 >> 1;
+  const int g = l >> 4, lr = l & 15;
+  const int KB = (int)(a.K >> 7);
+  const int NIT = (KB + 1) >> 1;
+
+  const int64_t mrows = min((int64_t)BM, a.M - m0), nrows = min((int64_t)BN, a.N - n0);
+  const __amdgpu_buffer_rsrc_t rx = rsrc(a.x + m0 * a.ldx, (uint32_t)(mrows * a.ldx));
+  const __amdgpu_buffer_rsrc_t rw = rsrc(a.w + n0 * a.ldw, (uint32_t)(nrows * a.ldw));
+  const __amdgpu_buffer_rsrc_t rm = rsrc(a.meta + n0 * a.ldm, (uint32_t)(nrows * a.ldm));
+  const __amdgpu_buffer_rsrc_t rsx = rsrc(a.sx, 0xffffffffu);
+  const __amdgpu_buffer_rsrc_t rsw = rsrc(a.sw, 0xffffffffu);
+  const PlanX2 plan = make_plan_x2(a, n0, m0, wave, l);
+  const uint32_t msel = (g >> 1) ? 0x07060302u : 0x05040100u;
+  const LaneOffsets<true> lo = lane_offsets<true>(wn, wm, g, lr);
+  const uint32_t qoff = (uint32_t)q * x2::HALF;
+
+  v4f acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+  issue_double(db0, plan, rx, rw, rm, rsx, rsw, a, 0, KB, wave);
+  for (int it0 = 0; it0 < NIT; it0 += 2) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int it = it0 + u;
+      if (it < NIT) {
+        wait_vmcnt<0>();
+        __syncthreads();
+        if (it + 1 < NIT)
+          issue_double(u == 0 ? db1 : db0, plan, rx, rw, rm, rsx, rsw, a, 2 * (it + 1), KB, wave);
+        if (2 * it + q < KB) compute_stage<true, GRAN_N>((u == 0 ? db0 : db1) + qoff, acc, lo, wn, g, msel);
+      }
+    }
+  }
+
+  // Add the two groups' partial tiles: group 0 finishes sub-tile rows i < 4,
+  // group 1 rows i >= 4; each hands the other half to its partner through LDS.
+  // (Uniform branches with constant indices keep acc in registers.)
+  __syncthreads();
+  if (q == 0) {
+    xchg_out<4>(reinterpret_cast<float4*>(db0), acc, w4, l);
+  } else {
+    xchg_out<0>(reinterpret_cast<float4*>(db1), acc, w4, l);
+  }
+  __syncthreads();
+  if (q == 0) {
+    xchg_in_store<0, OUT_BF16, OUT_T>(reinterpret_cast<const float4*>(db1), acc, a, w4, l, m0, n0, wn, wm, g, lr);
+  } else {
+    xchg_in_store<4, OUT_BF16, OUT_T>(reinterpret_cast<const float4*>(db0), acc, a, w4, l, m0, n0, wn, wm, g, lr);
+  }
 #endif  // SG_DEVICE_PASS
 }
 
@@ -480,7 +674,10 @@ __global__ void __launch_bounds__(512) k_gemm_decode(GemmArgs a) {
 template <bool SPARSE, int GRAN_N, bool OUT_BF16, bool OUT_T>
 static void launch_large(const GemmArgs& a, hipStream_t st) {
   const int tm = (int)cdiv(a.M, BM), tn = (int)cdiv(a.N, BN);
-  k_gemm_large<SPARSE, GRAN_N, OUT_BF16, OUT_T><<<tm * tn, 256, 0, st>>>(a, tm, tn);
+  if (SPARSE)
+    k_gemm_sparse_x2<GRAN_N, OUT_BF16, OUT_T><<<tm * tn, 512, 0, st>>>(a, tm, tn);
+  else
+    k_gemm_large<SPARSE, GRAN_N, OUT_BF16, OUT_T><<<tm * tn, 256, 0, st>>>(a, tm, tn);
 }
 
 template <bool SPARSE, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
