@@ -69,7 +69,8 @@ def gen_layer(seed, m, n, k, on_gpu_rng=False):
         x, w = torch.from_numpy(d["x"]).to(DEV), torch.from_numpy(d["w"]).to(DEV)
     wv, meta = sg.sparse24_prune_compress(w)
     wq, sw = sg.fp8_quant_groupwise(wv, gr=128, gc=64)
-    return x, wq, meta, sw
+    wp = sg.sparse24_pack_gfx950(wq, meta)
+    return x, wq, meta, sw, wp
 
 
 class Timer:
@@ -113,13 +114,13 @@ def headline(steps, warmup):
     gemm_t = Timer()
 
     def step(i, timed):
-        x, wq, meta, sw = sets[i % ROTATE]
+        x, _, _, sw, wp = sets[i % ROTATE]
         sg.fp8_quant_groupwise(x, gr=1, gc=128, q=xq, s=sx)
         if timed:
             with gemm_t:
-                sg.fp8_sparse24_gemm_groupwise(xq, sx, wq, meta, sw, 1, 128, y=y)
+                sg.fp8_sparse24_gemm_groupwise_packed(xq, sx, wp, n, sw, 1, 128, y=y)
         else:
-            sg.fp8_sparse24_gemm_groupwise(xq, sx, wq, meta, sw, 1, 128, y=y)
+            sg.fp8_sparse24_gemm_groupwise_packed(xq, sx, wp, n, sw, 1, 128, y=y)
 
     for i in range(warmup):
         step(i, False)
@@ -138,7 +139,7 @@ def headline(steps, warmup):
 def rows_report():
     out = {}
     m, n, k = 2048, 4096, 4096
-    x, wq, meta, sw = gen_layer(3, m, n, k)
+    x, wq, meta, sw, wp = gen_layer(3, m, n, k)
     w = torch.from_numpy(workloads.sparse_large(seed=3, m=8, n=n, k=k)["w"]).to(DEV)
     xq, sx = sg.fp8_quant_groupwise(x)
     # a1: activation quantisation (fp32 in, e4m3 + scales out)
@@ -156,13 +157,22 @@ def rows_report():
     ms = time_fn(lambda i: sg.fp8_quant_groupwise(wv, gr=128, gc=64, q=q, s=s))
     b = n * k // 2 * 4 + n * k // 2 + 4 * (n // 128) * (k // 128)
     out["a3_quant_w_4096x2048_128x64"] = {"ms": ms, "GB/s": b / ms / 1e6}
-    # a5 + a6: sparse GEMM, both output forms
+    # packing the compressed weight into the gfx950 layout
+    wpk = torch.empty_like(wp)
+    ms = time_fn(lambda i: sg.sparse24_pack_gfx950(wq, meta, packed=wpk))
+    b = n * k // 2 + n * k // 8 + wp.numel()
+    out["a3b_pack_gfx950_4096x4096"] = {"ms": ms, "GB/s": b / ms / 1e6}
+    # a5 + a6: sparse GEMM, both output forms, packed weight; and the canonical form
     flops = 2.0 * m * n * k
     for form in ("y", "yt"):
         y = torch.empty((m, n) if form == "y" else (n, m), dtype=torch.bfloat16, device=DEV)
-        ms = time_fn(lambda i: sg.fp8_sparse24_gemm_groupwise(xq, sx, wq, meta, sw, 1, 128, form=form, y=y))
-        out[f"a5_sparse_gemm_2048x4096x4096_{form}"] = {
+        ms = time_fn(lambda i: sg.fp8_sparse24_gemm_groupwise_packed(xq, sx, wp, n, sw, 1, 128, form=form, y=y))
+        out[f"a5_sparse_gemm_packed_2048x4096x4096_{form}"] = {
             "ms": ms, "TFLOP/s": flops / ms / 1e9, "frac_fp8_peak": flops / ms / 1e9 / PEAK_FP8_TFLOPS}
+    y = torch.empty((m, n), dtype=torch.bfloat16, device=DEV)
+    ms = time_fn(lambda i: sg.fp8_sparse24_gemm_groupwise(xq, sx, wq, meta, sw, 1, 128, y=y))
+    out["a5_sparse_gemm_canonical_2048x4096x4096_y"] = {
+        "ms": ms, "TFLOP/s": flops / ms / 1e9, "frac_fp8_peak": flops / ms / 1e9 / PEAK_FP8_TFLOPS}
     # a4: dense GEMM with outliers
     d = workloads.dense_outliers(seed=2, m=m, n=n, k=k)
     xd, wd = torch.from_numpy(d["x"]).to(DEV), torch.from_numpy(d["w"]).to(DEV)
@@ -175,14 +185,14 @@ def rows_report():
     del xd, wd, xdq, wdq
     # decode shapes, rotating weight copies so the 256 MB MALL cannot serve repeats
     for (dm, dn, dk) in workloads.DECODE_SHAPES:
-        wsets = [gen_layer(2000 + i, 8, dn, dk, on_gpu_rng=True)[1:] for i in range(ROTATE_DECODE)]
+        wsets = [gen_layer(2000 + i, 8, dn, dk, on_gpu_rng=True)[3:] for i in range(ROTATE_DECODE)]
         xdd = torch.from_numpy(workloads.decode(seed=4, m=dm, n=8, k=dk)["x"]).to(DEV)
         xq4, sx4 = sg.fp8_quant_groupwise(xdd)
         for form in ("y", "yt"):
             y = torch.empty((dm, dn) if form == "y" else (dn, dm), dtype=torch.bfloat16, device=DEV)
-            ms = time_fn(lambda i: sg.fp8_sparse24_gemm_groupwise(
-                xq4, sx4, wsets[i % ROTATE_DECODE][0], wsets[i % ROTATE_DECODE][1], wsets[i % ROTATE_DECODE][2],
-                1, 128, form=form, y=y), reps=64, warm=16)
+            ms = time_fn(lambda i: sg.fp8_sparse24_gemm_groupwise_packed(
+                xq4, sx4, wsets[i % ROTATE_DECODE][1], dn, wsets[i % ROTATE_DECODE][0], 1, 128, form=form, y=y),
+                reps=64, warm=16)
             b = sparse_bytes(dm, dn, dk)
             out[f"decode_M{dm}_N{dn}_K{dk}_{form}"] = {"ms": ms, "GB/s": b / ms / 1e6,
                                                      "frac_hbm": b / ms / 1e6 / PEAK_HBM_GBS}
@@ -295,13 +305,14 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": "2:4-sparse FP8 linear layer forward: fp32 X[2048,4096] quantised to e4m3 (1x128 "
-                        "scales), W[4096,4096] pruned 2:4 + e4m3 (128x128 scales), Y=X.W^T bf16",
+                        "scales), W[4096,4096] pruned 2:4 + e4m3 (128x128 scales) in the gfx950 packed form, "
+                        "Y=X.W^T bf16",
             "M": h["m"], "N": h["n"], "K": h["k"], "rotated_input_sets": ROTATE,
         },
         "roofline": {
             "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": tb,
-            "kernel": "k_gemm_large<sparse> (2:4 FP8 GEMM, Y form)", "avg_launch_ms": round(h["gemm_ms"], 5),
+            "kernel": "k_gemm_sparse_x2<packed> (2:4 FP8 GEMM, Y form)", "avg_launch_ms": round(h["gemm_ms"], 5),
         },
         "rows": {k: {kk: round(vv, 5) for kk, vv in v.items()} for k, v in rows.items()},
     }

@@ -170,6 +170,51 @@ sg_status sg_fp8_sparse24_gemm_groupwise(int64_t M, int64_t N, int64_t K, const 
                                          sg_form form, hipStream_t stream);
 
 /*
+ * sg_sparse24_packed_bytes -- size in bytes of the gfx950 packed form of an
+ * N x K 2:4-compressed weight: ceil(N / 256) * (K / 128) * 20480.  Returns -1 if
+ * N < 0, K <= 0 or K % 128 != 0.
+ */
+int64_t sg_sparse24_packed_bytes(int64_t N, int64_t K);
+
+/*
+ * sg_sparse24_pack_gfx950 -- rearranges a 2:4-compressed FP8 weight (codes
+ * wv [N, K/2], metadata wmeta [N, K/8], as produced by
+ * sg_sparse24_prune_compress + sg_fp8_quant_groupwise) into the layout the
+ * sparse GEMM kernels stream from HBM straight into LDS.  [T3258] jcaip's
+ * review (FP8 semi-structured weights are packed by the hardware's packing
+ * kernel); [I2029] klevzoff (values and metadata E reach the mainloop in the
+ * hardware's layout).  A pure byte permutation:
+ *   for 256-row tile t and 128-wide K block kb the 20480-byte block at
+ *   (t * K/128 + kb) * 20480 holds, for tile row r and lane group g = 0..3
+ *   (b = 32 (g & 1) + 8 (g >> 1)):
+ *     - at r*64 + 16 (g ^ ((r >> 1) & 3)): compressed bytes [b, b+8) and
+ *       [b+16, b+24) of the row's 64 bytes of block kb;
+ *     - at 16384 + r*16 + 4 ((g + 2 ((r >> 3) & 1)) & 3): metadata bytes b/4,
+ *       b/4+1, b/4+4, b/4+5 of the row's 16 bytes of block kb;
+ *   rows past N are zero.
+ *   packed : sg_sparse24_packed_bytes(N, K) bytes, 16-byte aligned, written fully.
+ * Requires K % 128 == 0, ldwv >= K/2, ldwm >= K/8, multiples of 16; wv, wmeta
+ * 16-byte aligned.
+ */
+sg_status sg_sparse24_pack_gfx950(const uint8_t* wv, int64_t ldwv, const uint8_t* wmeta, int64_t ldwm,
+                                  int64_t N, int64_t K, uint8_t* packed, hipStream_t stream);
+
+/*
+ * sg_fp8_sparse24_gemm_groupwise_packed -- sg_fp8_sparse24_gemm_groupwise with
+ * the weight given in the packed form of sg_sparse24_pack_gfx950 (same
+ * results; the form whose loads are contiguous 1 KB per wave instruction).
+ *   wpacked : sg_sparse24_packed_bytes(N, K) bytes, 16-byte aligned.
+ *   other arguments as sg_fp8_sparse24_gemm_groupwise.
+ * Requires in addition (K / 128) * 20480 < 2^31.
+ */
+sg_status sg_fp8_sparse24_gemm_groupwise_packed(int64_t M, int64_t N, int64_t K, const uint8_t* xq,
+                                                int64_t ldx, const float* sx, int64_t sx_sm,
+                                                int64_t sx_sk, int gran_m, const uint8_t* wpacked,
+                                                const float* sw, int64_t sw_sn, int64_t sw_sk,
+                                                int gran_n, void* y, sg_dtype y_dt, int64_t ldy,
+                                                sg_form form, hipStream_t stream);
+
+/*
  * sg_mixed_gemm_add -- Y = X1 . W1^T + X2 . W2^T in one kernel ([I2058],
  * hyx1999: a w4a4 GEMM plus a small w16a16 GEMM whose results are added, with
  * L = 2048, D1 = 4096, D2 = 64, D = 4096 as the example shape).

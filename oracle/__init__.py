@@ -17,6 +17,9 @@ of the source pages it follows; the pages are
   w4a4 + w16a16?" (CUTLASS issue #2058),
 * "Introduce new W8A8-FP-CSR quantization API" (torchao PR #3258).
 
+``pack.py`` additionally defines this build's gfx950 packed weight layout (a
+byte permutation of the compressed values and metadata).
+
 Parity status: every public function here is pinned by a ``-m "not gpu"`` test
 against something other than itself (an independent codec, closed forms,
 exact rational brute force, or identities the pages state).  None is
@@ -27,6 +30,7 @@ from .e4m3 import E4M3_MAX, e4m3_decode, e4m3_encode
 from .bf16 import bf16_decode
 from .quant import fp8_quant_groupwise, int4_quant_groupwise, int4_decode
 from .sparse24 import prune24, compress24, decompress24, prune_compress24
+from .pack import pack24_gfx950, unpack24_gfx950, packed_bytes
 from .gemm import (
     expand_scales,
     fp8_gemm_groupwise,
@@ -39,6 +43,7 @@ __all__ = [
     "E4M3_MAX", "e4m3_decode", "e4m3_encode", "bf16_decode",
     "fp8_quant_groupwise", "int4_quant_groupwise", "int4_decode",
     "prune24", "compress24", "decompress24", "prune_compress24",
+    "pack24_gfx950", "unpack24_gfx950", "packed_bytes",
     "expand_scales", "fp8_gemm_groupwise", "fp8_sparse24_gemm_groupwise",
     "mixed_gemm_add", "within_tolerance",
 ]

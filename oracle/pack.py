@@ -1,0 +1,96 @@
+"""The gfx950 packed layout of a 2:4-compressed FP8 weight, and its inverse.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
+
+The pages keep the sparse operand in a hardware-specific arrangement produced
+by a packing kernel: torchao PR #3258 "Introduce new W8A8-FP-CSR quantization
+API" (jcaip: use the CUTLASS packing kernel for FP8 semi-structured weights
+rather than the generic conversion) and CUTLASS issue #2029 (klevzoff: the
+mainloop takes the values together with the metadata tensor E in its own
+layout).  This module defines that arrangement for gfx950's SMFMAC and the
+LDS image the GEMM kernels read; it is a pure byte permutation of the
+canonical values [N, K/2] and metadata [N, K/8] (``sparse24.py``), with rows
+padded to a multiple of 256 with zeros.
+
+For 256-row tile t (rows 256 t .. 256 t + 255) and 128-wide K block kb, the
+block starts at byte (t * KB + kb) * 20480 (KB = K / 128) and holds, for
+tile row r and lane group g = 0..3 (b = 32 (g & 1) + 8 (g >> 1)):
+  * values, 16 bytes at r * 64 + 16 * (g ^ ((r >> 1) & 3)):
+        compressed bytes [b, b + 8) and [b + 16, b + 24) of the row's 64
+        compressed bytes of block kb (the SMFMAC A operand of lane group g);
+  * metadata, 4 bytes at 16384 + r * 16 + 4 * ((g + 2 * ((r >> 3) & 1)) & 3):
+        metadata bytes b/4, b/4 + 1, b/4 + 4, b/4 + 5 of the row's 16 metadata
+        bytes of block kb (the SMFMAC index word of lane group g).
+"""
+
+import numpy as np
+
+TILE_N = 256
+BLOCK_BYTES = 20480
+META_OFF = 16384
+
+
+def packed_bytes(n: int, k: int) -> int:
+    return -(-n // TILE_N) * (k // 128) * BLOCK_BYTES
+
+
+def _positions(n: int, kb_count: int):
+    """Byte positions in the packed buffer, per (row, kb, g): values start and
+    metadata word start."""
+    rows = np.arange(n)
+    t, r = rows // TILE_N, rows % TILE_N
+    kb = np.arange(kb_count)
+    g = np.arange(4)
+    base = (t[:, None] * kb_count + kb[None, :]) * BLOCK_BYTES                     # [n, KB]
+    vpos = base[:, :, None] + (r * 64)[:, None, None] + 16 * (g[None, None, :] ^ ((r[:, None, None] >> 1) & 3))
+    mslot = (g[None, None, :] + 2 * ((r[:, None, None] >> 3) & 1)) & 3
+    mpos = base[:, :, None] + META_OFF + (r * 16)[:, None, None] + 4 * mslot
+    return vpos, mpos                                                                # [n, KB, 4]
+
+
+def _lane_group_bytes():
+    """For each lane group g: the 16 value-byte indices and the 4 metadata-byte
+    indices it takes from a row's K block."""
+    vidx, midx = [], []
+    for g in range(4):
+        b = 32 * (g & 1) + 8 * (g >> 1)
+        vidx.append(list(range(b, b + 8)) + list(range(b + 16, b + 24)))
+        midx.append([b // 4, b // 4 + 1, b // 4 + 4, b // 4 + 5])
+    return np.array(vidx), np.array(midx)
+
+
+def pack24_gfx950(vals, meta) -> np.ndarray:
+    """vals uint8 [N, K/2] (e4m3 codes), meta uint8 [N, K/8] -> packed uint8."""
+    vals = np.asarray(vals, dtype=np.uint8)
+    meta = np.asarray(meta, dtype=np.uint8)
+    n, half = vals.shape
+    k = 2 * half
+    assert k % 128 == 0 and meta.shape == (n, k // 8)
+    kbc = k // 128
+    out = np.zeros(packed_bytes(n, k), dtype=np.uint8)
+    vpos, mpos = _positions(n, kbc)
+    vidx, midx = _lane_group_bytes()
+    vb = vals.reshape(n, kbc, 64)
+    mb = meta.reshape(n, kbc, 16)
+    for g in range(4):
+        for j in range(16):
+            out[vpos[:, :, g] + j] = vb[:, :, vidx[g, j]]
+        for j in range(4):
+            out[mpos[:, :, g] + j] = mb[:, :, midx[g, j]]
+    return out
+
+
+def unpack24_gfx950(packed, n: int, k: int):
+    """Inverse of ``pack24_gfx950``: -> (vals [N, K/2], meta [N, K/8])."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    kbc = k // 128
+    vpos, mpos = _positions(n, kbc)
+    vidx, midx = _lane_group_bytes()
+    vb = np.zeros((n, kbc, 64), dtype=np.uint8)
+    mb = np.zeros((n, kbc, 16), dtype=np.uint8)
+    for g in range(4):
+        for j in range(16):
+            vb[:, :, vidx[g, j]] = packed[vpos[:, :, g] + j]
+        for j in range(4):
+            mb[:, :, midx[g, j]] = packed[mpos[:, :, g] + j]
+    return vb.reshape(n, k // 2), mb.reshape(n, k // 8)

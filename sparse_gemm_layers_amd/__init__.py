@@ -16,11 +16,15 @@ from ._binding import (
     sparse24_prune_compress,
     fp8_gemm_groupwise,
     fp8_sparse24_gemm_groupwise,
+    sparse24_packed_bytes,
+    sparse24_pack_gfx950,
+    fp8_sparse24_gemm_groupwise_packed,
     mixed_gemm_add,
 )
 
 __all__ = [
     "SgError", "lib", "fp8_quant_groupwise", "int4_quant_groupwise",
     "sparse24_prune_compress", "fp8_gemm_groupwise", "fp8_sparse24_gemm_groupwise",
+    "sparse24_packed_bytes", "sparse24_pack_gfx950", "fp8_sparse24_gemm_groupwise_packed",
     "mixed_gemm_add",
 ]

@@ -31,6 +31,10 @@ _SIGS = {
                                _int, _ptr, _int, _i64, _int, _ptr], _int),
     "sg_fp8_sparse24_gemm_groupwise": ([_i64, _i64, _i64, _ptr, _i64, _ptr, _i64, _i64, _int, _ptr, _i64, _ptr,
                                         _i64, _ptr, _i64, _i64, _int, _ptr, _int, _i64, _int, _ptr], _int),
+    "sg_sparse24_packed_bytes": ([_i64, _i64], _i64),
+    "sg_sparse24_pack_gfx950": ([_ptr, _i64, _ptr, _i64, _i64, _i64, _ptr, _ptr], _int),
+    "sg_fp8_sparse24_gemm_groupwise_packed": ([_i64, _i64, _i64, _ptr, _i64, _ptr, _i64, _i64, _int, _ptr, _ptr,
+                                               _i64, _i64, _int, _ptr, _int, _i64, _int, _ptr], _int),
     "sg_mixed_gemm_add": ([_i64, _i64, _i64, _i64, _ptr, _i64, _ptr, _i64, _i64, _ptr, _i64, _ptr, _i64, _i64,
                            _ptr, _i64, _ptr, _i64, _ptr, _i64, _ptr], _int),
 }
@@ -181,6 +185,45 @@ def fp8_sparse24_gemm_groupwise(xq, sx, wv, wmeta, sw, gran_m: int = 1, gran_n: 
                                               _row_stride(wmeta), _p(sw), sw.stride(0), sw.stride(1), gran_n,
                                               _p(y), ydt, _row_stride(y), f, _stream(xq))
     _check(st, "sg_fp8_sparse24_gemm_groupwise")
+    return y
+
+
+def sparse24_packed_bytes(n: int, k: int) -> int:
+    return int(lib().sg_sparse24_packed_bytes(n, k))
+
+
+def sparse24_pack_gfx950(wv, wmeta, packed=None):
+    """Compressed codes wv uint8 [N, K/2] + metadata uint8 [N, K/8] -> the gfx950
+    packed weight (uint8, sparse24_packed_bytes(N, K) bytes)."""
+    _gpu2d(wv, "wv")
+    _gpu2d(wmeta, "wmeta")
+    n, k = wv.shape[0], wv.shape[1] * 2
+    nbytes = sparse24_packed_bytes(n, k)
+    if nbytes < 0:
+        raise SgError("sparse24_pack_gfx950: K must be a positive multiple of 128")
+    if packed is None:
+        packed = torch.empty(nbytes, dtype=torch.uint8, device=wv.device)
+    if packed.numel() < nbytes or not packed.is_cuda:
+        raise SgError("packed buffer too small or not on the GPU")
+    st = lib().sg_sparse24_pack_gfx950(_p(wv), _row_stride(wv), _p(wmeta), _row_stride(wmeta), n, k, _p(packed),
+                                       _stream(wv))
+    _check(st, "sg_sparse24_pack_gfx950")
+    return packed
+
+
+def fp8_sparse24_gemm_groupwise_packed(xq, sx, wpacked, n: int, sw, gran_m: int = 1, gran_n: int = 128,
+                                       out_dtype=torch.bfloat16, form: str = "y", y=None):
+    """2:4-sparse FP8 GEMM with the weight in the gfx950 packed form (N rows)."""
+    _gpu2d(xq, "xq")
+    M, K = xq.shape
+    if not wpacked.is_cuda or wpacked.numel() < sparse24_packed_bytes(n, K):
+        raise SgError("wpacked too small or not on the GPU")
+    y, f, ydt = _out(y, M, n, out_dtype, form, xq.device)
+    st = lib().sg_fp8_sparse24_gemm_groupwise_packed(M, n, K, _p(xq), _row_stride(xq), _p(sx), sx.stride(0),
+                                                     sx.stride(1), gran_m, _p(wpacked), _p(sw), sw.stride(0),
+                                                     sw.stride(1), gran_n, _p(y), ydt, _row_stride(y), f,
+                                                     _stream(xq))
+    _check(st, "sg_fp8_sparse24_gemm_groupwise_packed")
     return y
 
 

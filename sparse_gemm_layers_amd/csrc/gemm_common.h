@@ -7,6 +7,31 @@
 
 namespace sg {
 
+// SMFMAC (v_smfmac_f32_16x16x128_fp8_fp8) A-operand layout: lane group g
+// (lanes 16 g .. 16 g + 15) takes, from a row's 64 compressed bytes of a
+// 128-wide K block, bytes [b, b + 8) and [b + 16, b + 24) with
+// b = 32 (g & 1) + 8 (g >> 1); its 32-bit index holds the metadata nibbles of
+// those 8 groups of 4, i.e. metadata bytes b/4, b/4 + 1, b/4 + 4, b/4 + 5 of
+// the row's 16 metadata bytes, nibble order unchanged.
+// Lane group g's 32-bit SMFMAC index from one row's 16 metadata bytes of a K block.
+__device__ __forceinline__ int sp_meta_word(uint4 w, int g) {
+  const uint32_t a = (g & 1) ? w.z : w.x;
+  const uint32_t b = (g & 1) ? w.w : w.y;
+  return (int)((g >> 1) ? __builtin_amdgcn_perm(b, a, 0x07060302u)
+                        : __builtin_amdgcn_perm(b, a, 0x05040100u));
+}
+
+__device__ __forceinline__ int sp_a_off(int g) { return 32 * (g & 1) + 8 * (g >> 1); }
+
+// gfx950 packed weight layout (one 20480-byte block per 256-row tile and
+// 128-wide K block): values of row r, lane group g at r * 64 + 16 (g ^ ((r >> 1) & 3));
+// index word at 16384 + r * 16 + 4 ((g + 2 ((r >> 3) & 1)) & 3).
+constexpr int PK_TILE = 256, PK_BLOCK = 20480, PK_META = 16384;
+__device__ __host__ __forceinline__ int pk_val_off(int r, int g) { return r * 64 + 16 * (g ^ ((r >> 1) & 3)); }
+__device__ __host__ __forceinline__ int pk_meta_off(int r, int g) {
+  return PK_META + r * 16 + 4 * ((g + 2 * ((r >> 3) & 1)) & 3);
+}
+
 template <bool OUT_BF16>
 __device__ __forceinline__ void store1(void* y, int64_t off, float v) {
   if (OUT_BF16)

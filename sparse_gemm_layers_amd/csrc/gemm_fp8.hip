@@ -65,15 +65,6 @@ __device__ __forceinline__ v4f mma_sparse(const v4i& a, const v8i& b, int idx) {
   return __builtin_amdgcn_smfmac_f32_16x16x128_fp8_fp8(a, b, p, idx, 0, 0);
 }
 
-// Lane group g's 32-bit SMFMAC index from one row's 16 metadata bytes of a K block.
-__device__ __forceinline__ int sp_meta_word(uint4 w, int g) {
-  const uint32_t a = (g & 1) ? w.z : w.x;
-  const uint32_t b = (g & 1) ? w.w : w.y;
-  return (int)((g >> 1) ? __builtin_amdgcn_perm(b, a, 0x07060302u)
-                        : __builtin_amdgcn_perm(b, a, 0x05040100u));
-}
-
-__device__ __forceinline__ int sp_a_off(int g) { return 32 * (g & 1) + 8 * (g >> 1); }
 
 // ============================================================ large-M kernel
 // Workgroup tile: 256 W rows (n) x 128 X rows (m), 4 waves in a 2 x 2 grid,
@@ -238,13 +229,24 @@ __device__ __forceinline__ LaneOffsets<SPARSE> lane_offsets(int wn, int wm, int 
   return o;
 }
 
+// Packed weights: the stage's W area holds the packed block verbatim, so a
+// lane's A operand is one 16-byte read and its index one 4-byte read.
+__device__ __forceinline__ LaneOffsets<true> lane_offsets_packed(int wn, int wm, int g, int lr) {
+  using L = Stage<true>;
+  LaneOffsets<true> o = lane_offsets<true>(wn, wm, g, lr);
+  o.w0 = L::W_OFF + pk_val_off(wn * 128 + lr, g);
+  o.w1 = 0;
+  o.mt = L::W_OFF + pk_meta_off(wn * 128 + lr, g);
+  return o;
+}
+
 template <typename T>
 __device__ __forceinline__ T lds_ld(const uint8_t* st, uint32_t off) {
   return *reinterpret_cast<const T*>(st + off);
 }
 
 // Multiplies one LDS stage into the wave's 8 x 4 sub-tiles and promotes.
-template <bool SPARSE, int GRAN_N>
+template <bool SPARSE, int GRAN_N, bool PACKED = false>
 __device__ __forceinline__ void compute_stage(const uint8_t* st, v4f (&acc)[8][4], const LaneOffsets<SPARSE>& o,
                                               int wn, int g, uint32_t msel) {
   using L = Stage<SPARSE>;
@@ -271,7 +273,13 @@ __device__ __forceinline__ void compute_stage(const uint8_t* st, v4f (&acc)[8][4
     float4 swr = make_float4(0.f, 0.f, 0.f, 0.f);
     if (GRAN_N == 1) swr = lds_ld<float4>(st, L::SW_OFF + (wn * 128 + i * 16 + 4 * g) * 4);
     v4f p[4];
-    if (SPARSE) {
+    if (SPARSE && PACKED) {
+      const uint4 av = lds_ld<uint4>(st, o.w0 + i * 1024);
+      const int idx = lds_ld<int>(st, o.mt + i * 256);
+      const v4i aa = {(int)av.x, (int)av.y, (int)av.z, (int)av.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) p[j] = mma_sparse(aa, bx[j], idx);
+    } else if (SPARSE) {
       const uint2 v0 = lds_ld<uint2>(st, o.w0 + i * 1024);
       const uint2 v1 = lds_ld<uint2>(st, o.w1 + i * 1024);
       const uint2 mw = lds_ld<uint2>(st, o.mt + i * 256);
@@ -398,14 +406,19 @@ constexpr int DBL = 2 * HALF;              // double stage
 
 #if SG_DEVICE_PASS
 struct PlanX2 {
-  uint32_t xo[4], wo[4], mo, so[2];
+  uint32_t xo[4], wo[5], mo, so[2];
   uint32_t sdst[2];     // LDS offsets (within the double stage) of the two scale loads
   int sk[2];            // which scale: 0 = sx, 1 = sw
 };
 
+template <bool PACKED>
 __device__ __forceinline__ PlanX2 make_plan_x2(const GemmArgs& a, int64_t n0, int64_t m0, int wave, int l) {
   using L = Stage<true>;
   PlanX2 p;
+  // packed weights: 20 contiguous 1 KB slots (values + metadata) per K block,
+  // 40 per double stage, 5 per wave: slot q = 8 j + wave
+#pragma unroll
+  for (int j = 0; j < 5; ++j) p.wo[j] = (uint32_t)((((8 * j + wave) % 20) * 1024) + l * 16);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int slot = (8 * j + wave) & 15;      // 1 KB slot within the K block's X / W area
@@ -414,13 +427,13 @@ __device__ __forceinline__ PlanX2 make_plan_x2(const GemmArgs& a, int64_t n0, in
       const int r = s >> 3, c = (s & 7) ^ (r & 7);
       p.xo[j] = (uint32_t)(r * a.ldx + c * 16);
     }
-    {
+    if (!PACKED) {
       const int s = slot * 64 + l;
       const int r = s >> 2, c = (s & 3) ^ ((r >> 1) & 3);
       p.wo[j] = (uint32_t)(r * a.ldw + c * 16);
     }
   }
-  p.mo = (uint32_t)((((wave & 3) * 64) + l) * a.ldm);
+  p.mo = PACKED ? 0u : (uint32_t)((((wave & 3) * 64) + l) * a.ldm);
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int sidx = 2 * wave + j, h = sidx >> 3, t = sidx & 7;
@@ -441,6 +454,7 @@ __device__ __forceinline__ PlanX2 make_plan_x2(const GemmArgs& a, int64_t n0, in
 }
 
 // Loads K blocks kb0 and kb0 + 1 (clamped to the last block) into a double stage.
+template <bool PACKED>
 __device__ __forceinline__ void issue_double(uint8_t* st, const PlanX2& p, __amdgpu_buffer_rsrc_t rx,
                                              __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t rm,
                                              __amdgpu_buffer_rsrc_t rsx, __amdgpu_buffer_rsrc_t rsw,
@@ -453,13 +467,20 @@ __device__ __forceinline__ void issue_double(uint8_t* st, const PlanX2& p, __amd
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(st + h * x2::HALF + L::X_OFF + slot * 1024), 16,
                                              p.xo[j], kbh[h] * 128, 0, 0);
   }
+  if (PACKED) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int h = j >> 1, slot = (8 * j + wave) & 15;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(st + h * x2::HALF + L::W_OFF + slot * 1024), 16,
-                                             p.wo[j], kbh[h] * 64, 0, 0);
-  }
-  {
+    for (int j = 0; j < 5; ++j) {
+      const int q = 8 * j + wave, h = q / 20, slot = q % 20;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(st + h * x2::HALF + L::W_OFF + slot * 1024), 16,
+                                               p.wo[j], kbh[h] * PK_BLOCK, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int h = j >> 1, slot = (8 * j + wave) & 15;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(st + h * x2::HALF + L::W_OFF + slot * 1024), 16,
+                                               p.wo[j], kbh[h] * 64, 0, 0);
+    }
     const int h = wave >> 2;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rm, (lds_void*)(st + h * x2::HALF + L::M_OFF + (wave & 3) * 1024), 16,
                                              p.mo, kbh[h] * 16, 0, 0);
@@ -504,7 +525,7 @@ __device__ __forceinline__ void xchg_in_store(const float4* src, const v4f (&acc
     }
 }
 
-template <int GRAN_N, bool OUT_BF16, bool OUT_T>
+template <bool PACKED, int GRAN_N, bool OUT_BF16, bool OUT_T>
 __global__ void __launch_bounds__(512) k_gemm_sparse_x2(GemmArgs a, int tiles_m, int tiles_n) {
 #if SG_DEVICE_PASS
   __shared__ __attribute__((aligned(1024))) uint8_t db0[x2::DBL];
@@ -524,13 +545,16 @@ __global__ void __launch_bounds__(512) k_gemm_sparse_x2(GemmArgs a, int tiles_m,
 
   const int64_t mrows = min((int64_t)BM, a.M - m0), nrows = min((int64_t)BN, a.N - n0);
   const __amdgpu_buffer_rsrc_t rx = rsrc(a.x + m0 * a.ldx, (uint32_t)(mrows * a.ldx));
-  const __amdgpu_buffer_rsrc_t rw = rsrc(a.w + n0 * a.ldw, (uint32_t)(nrows * a.ldw));
-  const __amdgpu_buffer_rsrc_t rm = rsrc(a.meta + n0 * a.ldm, (uint32_t)(nrows * a.ldm));
+  // packed weights: the tile's blocks are contiguous, KB * 20480 bytes from tile tn
+  const __amdgpu_buffer_rsrc_t rw =
+      PACKED ? rsrc(a.w + (int64_t)tn * KB * PK_BLOCK, (uint32_t)(KB * PK_BLOCK))
+             : rsrc(a.w + n0 * a.ldw, (uint32_t)(nrows * a.ldw));
+  const __amdgpu_buffer_rsrc_t rm = PACKED ? rw : rsrc(a.meta + n0 * a.ldm, (uint32_t)(nrows * a.ldm));
   const __amdgpu_buffer_rsrc_t rsx = rsrc(a.sx, 0xffffffffu);
   const __amdgpu_buffer_rsrc_t rsw = rsrc(a.sw, 0xffffffffu);
-  const PlanX2 plan = make_plan_x2(a, n0, m0, wave, l);
+  const PlanX2 plan = make_plan_x2<PACKED>(a, n0, m0, wave, l);
   const uint32_t msel = (g >> 1) ? 0x07060302u : 0x05040100u;
-  const LaneOffsets<true> lo = lane_offsets<true>(wn, wm, g, lr);
+  const LaneOffsets<true> lo = PACKED ? lane_offsets_packed(wn, wm, g, lr) : lane_offsets<true>(wn, wm, g, lr);
   const uint32_t qoff = (uint32_t)q * x2::HALF;
 
   v4f acc[8][4];
@@ -539,7 +563,7 @@ __global__ void __launch_bounds__(512) k_gemm_sparse_x2(GemmArgs a, int tiles_m,
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-  issue_double(db0, plan, rx, rw, rm, rsx, rsw, a, 0, KB, wave);
+  issue_double<PACKED>(db0, plan, rx, rw, rm, rsx, rsw, a, 0, KB, wave);
   for (int it0 = 0; it0 < NIT; it0 += 2) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -548,8 +572,9 @@ __global__ void __launch_bounds__(512) k_gemm_sparse_x2(GemmArgs a, int tiles_m,
         wait_vmcnt<0>();
         __syncthreads();
         if (it + 1 < NIT)
-          issue_double(u == 0 ? db1 : db0, plan, rx, rw, rm, rsx, rsw, a, 2 * (it + 1), KB, wave);
-        if (2 * it + q < KB) compute_stage<true, GRAN_N>((u == 0 ? db0 : db1) + qoff, acc, lo, wn, g, msel);
+          issue_double<PACKED>(u == 0 ? db1 : db0, plan, rx, rw, rm, rsx, rsw, a, 2 * (it + 1), KB, wave);
+        if (2 * it + q < KB)
+          compute_stage<true, GRAN_N, PACKED>((u == 0 ? db0 : db1) + qoff, acc, lo, wn, g, msel);
       }
     }
   }
@@ -581,7 +606,7 @@ __global__ void __launch_bounds__(512) k_gemm_sparse_x2(GemmArgs a, int tiles_m,
 // Columns m >= M are zero-filled (the partial M tile).
 constexpr int DEC_WAVES = 8;
 
-template <bool SPARSE, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
+template <bool SPARSE, bool PACKED, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
 __global__ void __launch_bounds__(512) k_gemm_decode(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) float red[DEC_WAVES][MT][64][4];
   const int t = threadIdx.x, l = t & 63, wave = t >> 6;
@@ -601,7 +626,14 @@ __global__ void __launch_bounds__(512) k_gemm_decode(GemmArgs a) {
     v4i asp;
     v8i ad;
     int idx = 0;
-    if (SPARSE) {
+    if (SPARSE && PACKED) {
+      // rows past N are zero padding inside the packed buffer: no predicate
+      const uint8_t* blk = a.w + ((n0 / PK_TILE) * KB + kb) * (int64_t)PK_BLOCK;
+      const int r = (int)(n0 % PK_TILE) + lr;
+      const uint4 av = *reinterpret_cast<const uint4*>(blk + pk_val_off(r, g));
+      asp = (v4i){(int)av.x, (int)av.y, (int)av.z, (int)av.w};
+      idx = *reinterpret_cast<const int*>(blk + pk_meta_off(r, g));
+    } else if (SPARSE) {
       uint2 lo = {0u, 0u}, hi = {0u, 0u};
       uint4 mw = {0u, 0u, 0u, 0u};
       if (n_ok) {
@@ -671,47 +703,51 @@ __global__ void __launch_bounds__(512) k_gemm_decode(GemmArgs a) {
 
 // ------------------------------------------------------------------ dispatch
 
-template <bool SPARSE, int GRAN_N, bool OUT_BF16, bool OUT_T>
+template <bool SPARSE, bool PACKED, int GRAN_N, bool OUT_BF16, bool OUT_T>
 static void launch_large(const GemmArgs& a, hipStream_t st) {
   const int tm = (int)cdiv(a.M, BM), tn = (int)cdiv(a.N, BN);
   if (SPARSE)
-    k_gemm_sparse_x2<GRAN_N, OUT_BF16, OUT_T><<<tm * tn, 512, 0, st>>>(a, tm, tn);
+    k_gemm_sparse_x2<PACKED, GRAN_N, OUT_BF16, OUT_T><<<tm * tn, 512, 0, st>>>(a, tm, tn);
   else
     k_gemm_large<SPARSE, GRAN_N, OUT_BF16, OUT_T><<<tm * tn, 256, 0, st>>>(a, tm, tn);
 }
 
-template <bool SPARSE, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
+template <bool SPARSE, bool PACKED, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
 static void launch_decode_mt(const GemmArgs& a, hipStream_t st) {
-  k_gemm_decode<SPARSE, MT, GRAN_N, OUT_BF16, OUT_T><<<(unsigned)cdiv(a.N, 16), 512, 0, st>>>(a);
+  k_gemm_decode<SPARSE, PACKED, MT, GRAN_N, OUT_BF16, OUT_T><<<(unsigned)cdiv(a.N, 16), 512, 0, st>>>(a);
 }
 
-template <bool SPARSE, int GRAN_N, bool OUT_BF16, bool OUT_T>
+template <bool SPARSE, bool PACKED, int GRAN_N, bool OUT_BF16, bool OUT_T>
 static void launch_shape(const GemmArgs& a, hipStream_t st) {
   if (a.M <= 16)
-    launch_decode_mt<SPARSE, 1, GRAN_N, OUT_BF16, OUT_T>(a, st);
+    launch_decode_mt<SPARSE, PACKED, 1, GRAN_N, OUT_BF16, OUT_T>(a, st);
   else if (a.M <= 32)
-    launch_decode_mt<SPARSE, 2, GRAN_N, OUT_BF16, OUT_T>(a, st);
+    launch_decode_mt<SPARSE, PACKED, 2, GRAN_N, OUT_BF16, OUT_T>(a, st);
   else if (a.M <= 48)
-    launch_decode_mt<SPARSE, 3, GRAN_N, OUT_BF16, OUT_T>(a, st);
+    launch_decode_mt<SPARSE, PACKED, 3, GRAN_N, OUT_BF16, OUT_T>(a, st);
   else if (a.M <= 64)
-    launch_decode_mt<SPARSE, 4, GRAN_N, OUT_BF16, OUT_T>(a, st);
+    launch_decode_mt<SPARSE, PACKED, 4, GRAN_N, OUT_BF16, OUT_T>(a, st);
   else
-    launch_large<SPARSE, GRAN_N, OUT_BF16, OUT_T>(a, st);
+    launch_large<SPARSE, PACKED, GRAN_N, OUT_BF16, OUT_T>(a, st);
 }
 
-template <bool SPARSE>
+template <bool SPARSE, bool PACKED>
 static void launch_gemm(const GemmArgs& a, int gran_n, bool bf16, bool yt, hipStream_t st) {
   if (gran_n == 128) {
     if (bf16) {
-      if (yt) launch_shape<SPARSE, 128, true, true>(a, st); else launch_shape<SPARSE, 128, true, false>(a, st);
+      if (yt) launch_shape<SPARSE, PACKED, 128, true, true>(a, st);
+      else launch_shape<SPARSE, PACKED, 128, true, false>(a, st);
     } else {
-      if (yt) launch_shape<SPARSE, 128, false, true>(a, st); else launch_shape<SPARSE, 128, false, false>(a, st);
+      if (yt) launch_shape<SPARSE, PACKED, 128, false, true>(a, st);
+      else launch_shape<SPARSE, PACKED, 128, false, false>(a, st);
     }
   } else {
     if (bf16) {
-      if (yt) launch_shape<SPARSE, 1, true, true>(a, st); else launch_shape<SPARSE, 1, true, false>(a, st);
+      if (yt) launch_shape<SPARSE, PACKED, 1, true, true>(a, st);
+      else launch_shape<SPARSE, PACKED, 1, true, false>(a, st);
     } else {
-      if (yt) launch_shape<SPARSE, 1, false, true>(a, st); else launch_shape<SPARSE, 1, false, false>(a, st);
+      if (yt) launch_shape<SPARSE, PACKED, 1, false, true>(a, st);
+      else launch_shape<SPARSE, PACKED, 1, false, false>(a, st);
     }
   }
 }
@@ -772,7 +808,7 @@ extern "C" sg_status sg_fp8_gemm_groupwise(int64_t M, int64_t N, int64_t K, cons
   const GemmArgs a = make_args(M, N, K, xq, ldx, sx, sx_sm, sx_sk, gran_m, wq, ldw, nullptr, 0, sw, sw_sn,
                                sw_sk, gran_n, y, y_dt, ldy);
   clear_hip_error();
-  launch_gemm<false>(a, gran_n, y_dt == SG_BF16, form == SG_OUT_YT, stream);
+  launch_gemm<false, false>(a, gran_n, y_dt == SG_BF16, form == SG_OUT_YT, stream);
   return launch_status();
 }
 
@@ -792,6 +828,25 @@ extern "C" sg_status sg_fp8_sparse24_gemm_groupwise(int64_t M, int64_t N, int64_
   const GemmArgs a = make_args(M, N, K, xq, ldx, sx, sx_sm, sx_sk, gran_m, wv, ldwv, wmeta, ldwm, sw, sw_sn,
                                sw_sk, gran_n, y, y_dt, ldy);
   clear_hip_error();
-  launch_gemm<true>(a, gran_n, y_dt == SG_BF16, form == SG_OUT_YT, stream);
+  launch_gemm<true, false>(a, gran_n, y_dt == SG_BF16, form == SG_OUT_YT, stream);
+  return launch_status();
+}
+
+extern "C" sg_status sg_fp8_sparse24_gemm_groupwise_packed(int64_t M, int64_t N, int64_t K, const uint8_t* xq,
+                                                           int64_t ldx, const float* sx, int64_t sx_sm,
+                                                           int64_t sx_sk, int gran_m, const uint8_t* wpacked,
+                                                           const float* sw, int64_t sw_sn, int64_t sw_sk,
+                                                           int gran_n, void* y, sg_dtype y_dt, int64_t ldy,
+                                                           sg_form form, hipStream_t stream) {
+  sg_status st = check_common(M, N, K, xq, ldx, sx, sx_sm, sx_sk, gran_m, sw, sw_sn, sw_sk, gran_n, y, y_dt, ldy, form);
+  if (st != SG_OK) return st;
+  if (!wpacked) return SG_ERR_NULL;
+  if (!aligned(wpacked, 16)) return SG_ERR_ALIGN;
+  if ((K / 128) * (int64_t)PK_BLOCK > 0x7fffffffLL) return SG_ERR_SHAPE;
+  if (M == 0 || N == 0) return SG_OK;
+  const GemmArgs a = make_args(M, N, K, xq, ldx, sx, sx_sm, sx_sk, gran_m, wpacked, 0, nullptr, 0, sw, sw_sn,
+                               sw_sk, gran_n, y, y_dt, ldy);
+  clear_hip_error();
+  launch_gemm<true, true>(a, gran_n, y_dt == SG_BF16, form == SG_OUT_YT, stream);
   return launch_status();
 }

@@ -35,7 +35,8 @@ def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
         "sg_abi_version", "sg_status_str", "sg_fp8_quant_groupwise", "sg_int4_quant_groupwise",
         "sg_sparse24_prune_compress", "sg_fp8_gemm_groupwise", "sg_fp8_sparse24_gemm_groupwise",
-        "sg_mixed_gemm_add"])
+        "sg_mixed_gemm_add", "sg_sparse24_packed_bytes", "sg_sparse24_pack_gfx950",
+        "sg_fp8_sparse24_gemm_groupwise_packed"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -169,3 +170,34 @@ def test_binding_rejects_cpu_tensors():
     x = torch.zeros(4, 128)
     with pytest.raises(sg.SgError):
         sg.fp8_quant_groupwise(x)
+
+
+def test_packed_bytes():
+    lib = sg.lib()
+    assert lib.sg_sparse24_packed_bytes(4096, 4096) == 16 * 32 * 20480
+    assert lib.sg_sparse24_packed_bytes(300, 384) == 2 * 3 * 20480
+    assert lib.sg_sparse24_packed_bytes(0, 128) == 0
+    assert lib.sg_sparse24_packed_bytes(10, 100) == -1 and lib.sg_sparse24_packed_bytes(-1, 128) == -1
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,code", [
+    (dict(wv=None), NULL), (dict(packed=None), NULL), (dict(K=100), SHAPE), (dict(ldwv=32), SHAPE),
+    (dict(ldwm=24), ALIGN), (dict(packed=ODD), ALIGN), (dict(N=0), OK),
+])
+def test_pack_validation(kw, code):
+    a = dict(wv=P, ldwv=64, meta=P2, ldwm=16, N=8, K=128, packed=P3)
+    a.update(kw)
+    assert sg.lib().sg_sparse24_pack_gfx950(a["wv"], a["ldwv"], a["meta"], a["ldwm"], a["N"], a["K"],
+                                            a["packed"], None) == code
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,code", [(dict(w=None), NULL), (dict(w=ODD), ALIGN), (dict(K=200), SHAPE),
+                                     (dict(M=0), OK)])
+def test_packed_gemm_validation(kw, code):
+    a = dict(M=64, N=256, K=256, x=P, ldx=256, sx=P3, w=P2, sw=P3, y=P)
+    a.update(kw)
+    assert sg.lib().sg_fp8_sparse24_gemm_groupwise_packed(a["M"], a["N"], a["K"], a["x"], a["ldx"], a["sx"], 1, 64,
+                                                          1, a["w"], a["sw"], 2, 1, 128, a["y"], 1, 256, 0,
+                                                          None) == code

@@ -15,8 +15,12 @@ from gpu_helpers import DEV, assert_within_tolerance, down, oracle_operands, say
 pytestmark = pytest.mark.gpu
 
 
-def run_gemm(sparse, xq, sx, gm, wq, meta, sw, gn, out_dtype, form, m_major=True):
+def run_gemm(sparse, xq, sx, gm, wq, meta, sw, gn, out_dtype, form, m_major=True, packed=False):
     args = (up(xq), up_scales(sx, m_major))
+    if packed:
+        wp = up(oracle.pack24_gfx950(wq, meta))
+        return sg.fp8_sparse24_gemm_groupwise_packed(*args, wp, wq.shape[0], up_scales(sw, m_major), gm, gn,
+                                                     out_dtype=out_dtype, form=form)
     if sparse:
         return sg.fp8_sparse24_gemm_groupwise(*args, up(wq), up(meta), up_scales(sw, m_major), gm, gn,
                                               out_dtype=out_dtype, form=form)
@@ -24,8 +28,9 @@ def run_gemm(sparse, xq, sx, gm, wq, meta, sw, gn, out_dtype, form, m_major=True
 
 
 def check(sparse, m, n, k, gm=1, gn=128, out_dtype=torch.bfloat16, forms=("y", "yt"), seed=0, dist="sparse",
-          m_major=True):
-    say(f"{'sparse' if sparse else 'dense'} M={m} N={n} K={k} gm={gm} gn={gn} {out_dtype} {forms} seed={seed}")
+          m_major=True, packed=False):
+    kind = "packed" if packed else ("sparse" if sparse else "dense")
+    say(f"{kind} M={m} N={n} K={k} gm={gm} gn={gn} {out_dtype} {forms} seed={seed}")
     d = (workloads.dense_outliers if dist == "outliers" else workloads.sparse_large)(seed=seed, m=m, n=n, k=k)
     xq, sx, wq, meta, sw = oracle_operands(d["x"], d["w"], gm, gn, sparse)
     if sparse:
@@ -34,7 +39,7 @@ def check(sparse, m, n, k, gm=1, gn=128, out_dtype=torch.bfloat16, forms=("y", "
         ref, bound = oracle.fp8_gemm_groupwise(xq, sx, gm, wq, sw, gn, bound=True)
     outs = {}
     for form in forms:
-        y = run_gemm(sparse, xq, sx, gm, wq, meta, sw, gn, out_dtype, form, m_major)
+        y = run_gemm(sparse, xq, sx, gm, wq, meta, sw, gn, out_dtype, form, m_major, packed)
         got = down(y)
         got = got.T if form == "yt" else got
         assert got.shape == (m, n)
@@ -137,3 +142,48 @@ def test_end_to_end_gpu_chain_matches_oracle_chain():
     oxq, osx, owq, ometa, osw = oracle_operands(d["x"], d["w"], 1, 128, True)
     ref, bound = oracle.fp8_sparse24_gemm_groupwise(oxq, osx, 1, owq, ometa, osw, 128, bound=True)
     assert_within_tolerance(y, ref, bound, "end-to-end")
+
+
+# --- the packed weight form -------------------------------------------------
+
+@pytest.mark.parametrize("m,n,k", RAGGED)
+def test_packed_ragged_shapes(m, n, k):
+    check(True, m, n, k, seed=m * 7 + n, packed=True)
+
+
+@pytest.mark.parametrize("gm,gn", [(1, 1), (128, 1), (128, 128), (1, 128)])
+@pytest.mark.parametrize("m", [37, 300])
+def test_packed_granularity_modes(gm, gn, m):
+    check(True, m, 384, 256, gm=gm, gn=gn, seed=11 + gm + gn, packed=True)
+
+
+def test_packed_full_size_both_forms():
+    check(True, 2048, 4096, 4096, seed=3, packed=True)
+
+
+@pytest.mark.parametrize("m,n,k", workloads.DECODE_SHAPES)
+def test_packed_decode_shapes(m, n, k):
+    check(True, m, n, k, seed=4, forms=("y", "yt"), packed=True)
+
+
+def test_packed_fp32_row_major_scales_and_equal_to_unpacked():
+    d = workloads.sparse_large(seed=21, m=300, n=700, k=512)
+    xq, sx, wq, meta, sw = oracle_operands(d["x"], d["w"], 1, 128, True)
+    a = down(run_gemm(True, xq, sx, 1, wq, meta, sw, 128, torch.float32, "y", m_major=False))
+    b = down(run_gemm(True, xq, sx, 1, wq, meta, sw, 128, torch.float32, "y", m_major=False, packed=True))
+    ref, bound = oracle.fp8_sparse24_gemm_groupwise(xq, sx, 1, wq, meta, sw, 128, bound=True)
+    assert_within_tolerance(b, ref, bound, "packed fp32")
+    assert_within_tolerance(a, ref, bound, "unpacked fp32")
+
+
+def test_packed_end_to_end_gpu_prep_chain():
+    """GPU prune + quantise + pack, then the packed GEMM, against the oracle chain."""
+    d = workloads.sparse_large(seed=22, m=512, n=1024, k=1024)
+    wv, meta = sg.sparse24_prune_compress(up(d["w"]))
+    wq, sw = sg.fp8_quant_groupwise(wv, gr=128, gc=64)
+    wp = sg.sparse24_pack_gfx950(wq, meta)
+    xq, sx = sg.fp8_quant_groupwise(up(d["x"]), gr=1, gc=128)
+    y = down(sg.fp8_sparse24_gemm_groupwise_packed(xq, sx, wp, 1024, sw, 1, 128))
+    oxq, osx, owq, ometa, osw = oracle_operands(d["x"], d["w"], 1, 128, True)
+    ref, bound = oracle.fp8_sparse24_gemm_groupwise(oxq, osx, 1, owq, ometa, osw, 128, bound=True)
+    assert_within_tolerance(y, ref, bound, "packed end-to-end")

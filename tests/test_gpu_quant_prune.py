@@ -139,3 +139,28 @@ def test_prune_ties_signed_zeros_and_all_zero_rows():
     ov, om = oracle.prune_compress24(w)
     assert np.array_equal(m.cpu().numpy(), om)
     assert np.array_equal(v.cpu().numpy().view(np.uint32), ov.view(np.uint32))
+
+
+@pytest.mark.parametrize("n,k", [(256, 128), (300, 384), (4096, 4096), (14336, 4096), (1, 128), (37, 14336)])
+def test_pack_gfx950_matches_oracle(n, k):
+    say(f"pack {n}x{k}")
+    rng = np.random.default_rng(n + k)
+    vals = workloads.random_e4m3_codes(rng, (n, k // 2))
+    meta = rng.integers(0, 256, size=(n, k // 8)).astype(np.uint8)
+    packed = sg.sparse24_pack_gfx950(up(vals), up(meta))
+    want = oracle.pack24_gfx950(vals, meta)
+    torch.cuda.synchronize()
+    assert packed.numel() == want.size == sg.sparse24_packed_bytes(n, k)
+    assert np.array_equal(packed.cpu().numpy(), want)
+
+
+def test_pack_strided_inputs():
+    rng = np.random.default_rng(5)
+    vals = workloads.random_e4m3_codes(rng, (40, 256))
+    meta = rng.integers(0, 256, size=(40, 64)).astype(np.uint8)
+    vb = torch.zeros((40, 320), dtype=torch.uint8, device=DEV)
+    vb[:, :256] = up(vals)
+    mb = torch.zeros((40, 80), dtype=torch.uint8, device=DEV)
+    mb[:, :64] = up(meta)
+    packed = sg.sparse24_pack_gfx950(vb[:, :256], mb[:, :64])
+    assert np.array_equal(packed.cpu().numpy(), oracle.pack24_gfx950(vals, meta))

@@ -1,0 +1,65 @@
+"""Pins of the oracle's gfx950 packed weight layout: hand-derived bytes, a
+bijective round trip with zero padding, and the per-block sizes."""
+import os
+
+import numpy as np
+
+import oracle
+import workloads
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def test_golden_row0():
+    vals = np.zeros((1, 64), np.uint8)
+    vals[0] = np.arange(64)
+    meta = np.zeros((1, 16), np.uint8)
+    meta[0] = np.arange(200, 216)
+    p = oracle.pack24_gfx950(vals, meta)
+    assert p.size == 20480
+    seen = 0
+    for line in open(os.path.join(GOLDEN, "pack_gfx950_row0.txt")):
+        line = line.split("#")[0].strip()
+        if not line:
+            continue
+        off, *bs = [int(v) for v in line.split()]
+        assert list(p[off:off + len(bs)]) == bs, off
+        seen += len(bs)
+    assert seen == 80 and np.count_nonzero(p) == 79      # one value byte is 0
+
+
+def test_roundtrip_and_zero_padding():
+    rng = np.random.default_rng(41)
+    n, k = 300, 384
+    vals = workloads.random_e4m3_codes(rng, (n, k // 2))
+    meta = rng.integers(0, 256, size=(n, k // 8)).astype(np.uint8)
+    p = oracle.pack24_gfx950(vals, meta)
+    assert p.size == oracle.packed_bytes(n, k) == 2 * 3 * 20480
+    v2, m2 = oracle.unpack24_gfx950(p, n, k)
+    assert np.array_equal(v2, vals) and np.array_equal(m2, meta)
+    # padded rows 300..511 of tile 1 hold zeros only
+    pv, pm = oracle.unpack24_gfx950(p, 512, k)
+    assert not pv[300:].any() and not pm[300:].any()
+    # every byte of the 256-row tiles is used exactly once by the first 512 rows
+    assert np.count_nonzero(oracle.pack24_gfx950(np.full((512, k // 2), 7, np.uint8),
+                                                 np.full((512, k // 8), 9, np.uint8))) == p.size
+
+
+def test_each_lane_group_word_is_its_smfmac_index():
+    """The metadata word of lane group g covers the groups of 4 at dense k =
+    b + 4 j (j < 4) and b + 32 + 4 j, b = 64 (g & 1) + 16 (g >> 1): nibble j of
+    the word is the canonical nibble of group (b / 4 + j), then (b / 4 + 8 + j)."""
+    rng = np.random.default_rng(42)
+    meta = rng.integers(0, 256, size=(16, 16)).astype(np.uint8)
+    vals = np.zeros((16, 64), np.uint8)
+    p = oracle.pack24_gfx950(vals, meta)
+    nib = np.empty((16, 32), np.int64)
+    nib[:, 0::2] = meta & 15
+    nib[:, 1::2] = meta >> 4
+    for r in range(16):
+        for g in range(4):
+            slot = (g + 2 * ((r >> 3) & 1)) & 3
+            w = int.from_bytes(bytes(p[16384 + r * 16 + 4 * slot:16384 + r * 16 + 4 * slot + 4]), "little")
+            base = 64 * (g & 1) + 16 * (g >> 1)
+            groups = [base // 4 + j for j in range(4)] + [base // 4 + 8 + j for j in range(4)]
+            assert [(w >> (4 * j)) & 15 for j in range(8)] == [nib[r, q] for q in groups]
