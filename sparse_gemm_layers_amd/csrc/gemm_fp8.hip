@@ -51,6 +51,7 @@ struct GemmArgs {
   void* y;
   int64_t ldy;
   int vec_store;  // Y-form: 4 consecutive n may be stored as one vector
+  int vec16;      // y is 16-byte aligned and a row of y is a multiple of 16 bytes
 };
 
 // ------------------------------------------------------------------ helpers
@@ -398,7 +399,8 @@ __global__ void __launch_bounds__(256, 1) k_gemm_large(GemmArgs a, int tiles_m, 
 // barrier and matrix-core latencies hide behind the other's work.  A "double
 // stage" holds K blocks 2 it and 2 it + 1 (two copies of the single-stage
 // layout); two double stages alternate in LDS.  At the end the two groups add
-// their partial tiles through LDS, each group finishing half of the rows.
+// their partial tiles through LDS, each group finishing half of the rows, and
+// the finished tile is staged in LDS once more for whole-row stores.
 namespace x2 {
 constexpr int HALF = Stage<true>::BYTES;   // one K block
 constexpr int DBL = 2 * HALF;              // double stage
@@ -511,18 +513,92 @@ __device__ __forceinline__ void xchg_out(float4* dst, const v4f (&acc)[8][4], in
     }
 }
 
-template <int I0, bool OUT_BF16, bool OUT_T>
-__device__ __forceinline__ void xchg_in_store(const float4* src, const v4f (&acc)[8][4], const GemmArgs& a, int w4,
-                                              int l, int64_t m0, int64_t n0, int wn, int wm, int g, int lr) {
+// The finished 256 x 128 tile is staged in LDS in the stored layout (rows of
+// Y are m, rows of Y^T are n), 16 bytes of padding per row, the first half of
+// the rows in one double-stage buffer and the second half in the other, so
+// that the stores are whole, 16-byte aligned row segments.
+template <bool OUT_BF16, bool OUT_T>
+struct OutTile {
+  static constexpr int ES = OUT_BF16 ? 2 : 4;
+  static constexpr int ROWS = OUT_T ? BN : BM;
+  static constexpr int COLS = OUT_T ? BM : BN;
+  static constexpr int PITCH = COLS * ES + 16;
+  static constexpr int RPH = ROWS / 2;          // rows per buffer
+  static constexpr int CPR = COLS * ES / 16;    // 16-byte chunks per row
+  static_assert(RPH * PITCH <= x2::DBL, "half of the output tile must fit one buffer");
+};
+
+// Group Q's finished rows (Q = 0: sub-tile rows i < 4, Q = 1: i >= 4): adds
+// the partner group's partial tile (16 float4 per lane in buffer `src`) and
+// writes the result into the staged output tile.  Lane holds
+// D[n = wn*128 + 16 i + 4 g + e][m = wm*64 + 16 j + lr].
+template <int Q, bool OUT_BF16, bool OUT_T>
+__device__ __forceinline__ void x2_finish(const uint8_t* src, uint8_t* t0, uint8_t* t1, const v4f (&acc)[8][4],
+                                          int w4, int l, int wn, int wm, int g, int lr) {
+  using OT = OutTile<OUT_BF16, OUT_T>;
+  float4 part[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) part[k] = reinterpret_cast<const float4*>(src)[((w4 * 16 + k) << 6) + l];
+  __syncthreads();   // every wave has its partner's partials: the buffers may be overwritten
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float4 o = src[((w4 * 16 + i * 4 + j) << 6) + l];
-      v4f v = acc[I0 + i][j];
-      v[0] += o.x; v[1] += o.y; v[2] += o.z; v[3] += o.w;
-      store_quad<OUT_BF16, OUT_T>(a, m0 + wm * 64 + j * 16 + lr, n0 + wn * 128 + (I0 + i) * 16 + 4 * g, v);
+      const float4 o = part[i * 4 + j];
+      const v4f av = acc[4 * Q + i][j];
+      const float v[4] = {av[0] + o.x, av[1] + o.y, av[2] + o.z, av[3] + o.w};
+      const int nl = wn * 128 + (4 * Q + i) * 16 + 4 * g, ml = wm * 64 + j * 16 + lr;
+      if (!OUT_T) {
+        uint8_t* row = (ml < OT::RPH ? t0 : t1) + (ml % OT::RPH) * OT::PITCH;
+        if (OUT_BF16) {
+          uint2 pk;
+          pk.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
+          pk.y = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
+          *reinterpret_cast<uint2*>(row + nl * 2) = pk;
+        } else {
+          *reinterpret_cast<float4*>(row + nl * 4) = make_float4(v[0], v[1], v[2], v[3]);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          uint8_t* row = (nl + e < OT::RPH ? t0 : t1) + ((nl + e) % OT::RPH) * OT::PITCH;
+          if (OUT_BF16) *reinterpret_cast<uint16_t*>(row + ml * 2) = (uint16_t)f32_to_bf16(v[e]);
+          else *reinterpret_cast<float*>(row + ml * 4) = v[e];
+        }
+      }
     }
+}
+
+// Stores the staged tile: 16-byte chunks of whole rows, non-temporal (the
+// output is not read again by this kernel).  Partial tiles and outputs
+// without 16-byte rows store element by element with bounds checks.
+template <bool OUT_BF16, bool OUT_T>
+__device__ __forceinline__ void store_staged(const GemmArgs& a, const uint8_t* t0, const uint8_t* t1, int64_t m0,
+                                             int64_t n0, int t) {
+  using OT = OutTile<OUT_BF16, OUT_T>;
+  const int64_t r0 = OUT_T ? n0 : m0, c0 = OUT_T ? m0 : n0;
+  const int64_t rlim = OUT_T ? a.N : a.M, clim = OUT_T ? a.M : a.N;
+  const bool full = r0 + OT::ROWS <= rlim && c0 + OT::COLS <= clim && a.vec16;
+  constexpr int CHUNKS = OT::ROWS * OT::CPR;
+#pragma unroll
+  for (int u = 0; u < CHUNKS / 512; ++u) {
+    const int c = u * 512 + t, row = c / OT::CPR, col = c % OT::CPR;
+    const uint4 v = *reinterpret_cast<const uint4*>((row < OT::RPH ? t0 : t1) + (row % OT::RPH) * OT::PITCH + col * 16);
+    uint8_t* const yp = reinterpret_cast<uint8_t*>(a.y) + ((r0 + row) * a.ldy + c0 + col * (16 / OT::ES)) * OT::ES;
+    if (full) {
+      typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+      __builtin_nontemporal_store((u4v){v.x, v.y, v.z, v.w}, reinterpret_cast<u4v*>(yp));
+    } else if (r0 + row < rlim) {
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 16 / OT::ES; ++e) {
+        if (c0 + col * (16 / OT::ES) + e < clim) {
+          if (OUT_BF16) reinterpret_cast<uint16_t*>(yp)[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+          else reinterpret_cast<uint32_t*>(yp)[e] = w[e];
+        }
+      }
+    }
+  }
 }
 
 template <bool PACKED, int GRAN_N, bool OUT_BF16, bool OUT_T>
@@ -589,11 +665,12 @@ __global__ void __launch_bounds__(512) k_gemm_sparse_x2(GemmArgs a, int tiles_m,
     xchg_out<0>(reinterpret_cast<float4*>(db1), acc, w4, l);
   }
   __syncthreads();
-  if (q == 0) {
-    xchg_in_store<0, OUT_BF16, OUT_T>(reinterpret_cast<const float4*>(db1), acc, a, w4, l, m0, n0, wn, wm, g, lr);
-  } else {
-    xchg_in_store<4, OUT_BF16, OUT_T>(reinterpret_cast<const float4*>(db0), acc, a, w4, l, m0, n0, wn, wm, g, lr);
-  }
+  if (q == 0)
+    x2_finish<0, OUT_BF16, OUT_T>(db1, db0, db1, acc, w4, l, wn, wm, g, lr);
+  else
+    x2_finish<1, OUT_BF16, OUT_T>(db0, db0, db1, acc, w4, l, wn, wm, g, lr);
+  __syncthreads();
+  store_staged<OUT_BF16, OUT_T>(a, db0, db1, m0, n0, t);
 #endif  // SG_DEVICE_PASS
 }
 
@@ -786,6 +863,7 @@ static GemmArgs make_args(int64_t M, int64_t N, int64_t K, const uint8_t* xq, in
   a.y = y; a.ldy = ldy;
   const size_t vb = 4 * dtype_size(y_dt);
   a.vec_store = (ldy % 4 == 0) && aligned(y, vb);
+  a.vec16 = ((ldy * (int64_t)dtype_size(y_dt)) % 16 == 0) && aligned(y, 16);
   return a;
 }
 
