@@ -171,7 +171,7 @@ sg_status sg_fp8_sparse24_gemm_groupwise(int64_t M, int64_t N, int64_t K, const 
 
 /*
  * sg_sparse24_packed_bytes -- size in bytes of the gfx950 packed form of an
- * N x K 2:4-compressed weight: ceil(N / 256) * (K / 128) * 20480.  Returns -1 if
+ * N x K 2:4-compressed weight: ceil(N / 16) * (K / 128) * 1280.  Returns -1 if
  * N < 0, K <= 0 or K % 128 != 0.
  */
 int64_t sg_sparse24_packed_bytes(int64_t N, int64_t K);
@@ -184,14 +184,15 @@ int64_t sg_sparse24_packed_bytes(int64_t N, int64_t K);
  * review (FP8 semi-structured weights are packed by the hardware's packing
  * kernel); [I2029] klevzoff (values and metadata E reach the mainloop in the
  * hardware's layout).  A pure byte permutation:
- *   for 256-row tile t and 128-wide K block kb the 20480-byte block at
- *   (t * K/128 + kb) * 20480 holds, for tile row r and lane group g = 0..3
+ *   for 16-row block R (rows 16 R .. 16 R + 15) and 128-wide K block kb the
+ *   1280-byte chunk at (R * K/128 + kb) * 1280 (one row block's chunks follow
+ *   each other along K) holds, for local row lr and lane group g = 0..3
  *   (b = 32 (g & 1) + 8 (g >> 1)):
- *     - at r*64 + 16 (g ^ ((r >> 1) & 3)): compressed bytes [b, b+8) and
+ *     - at lr*64 + 16 (g ^ ((lr >> 1) & 3)): compressed bytes [b, b+8) and
  *       [b+16, b+24) of the row's 64 bytes of block kb;
- *     - at 16384 + r*16 + 4 ((g + 2 ((r >> 3) & 1)) & 3): metadata bytes b/4,
+ *     - at 1024 + lr*16 + 4 ((g + 2 ((lr >> 3) & 1)) & 3): metadata bytes b/4,
  *       b/4+1, b/4+4, b/4+5 of the row's 16 bytes of block kb;
- *   rows past N are zero.
+ *   rows past N (up to the next multiple of 16) are zero.
  *   packed : sg_sparse24_packed_bytes(N, K) bytes, 16-byte aligned, written fully.
  * Requires K % 128 == 0, ldwv >= K/2, ldwm >= K/8, multiples of 16; wv, wmeta
  * 16-byte aligned.
@@ -202,10 +203,11 @@ sg_status sg_sparse24_pack_gfx950(const uint8_t* wv, int64_t ldwv, const uint8_t
 /*
  * sg_fp8_sparse24_gemm_groupwise_packed -- sg_fp8_sparse24_gemm_groupwise with
  * the weight given in the packed form of sg_sparse24_pack_gfx950 (same
- * results; the form whose loads are contiguous 1 KB per wave instruction).
+ * results; the form whose loads are contiguous 1 KB per wave instruction, and
+ * that the M <= 64 path streams row block by row block).
  *   wpacked : sg_sparse24_packed_bytes(N, K) bytes, 16-byte aligned.
  *   other arguments as sg_fp8_sparse24_gemm_groupwise.
- * Requires in addition (K / 128) * 20480 < 2^31.
+ * Requires in addition (K / 128) * 16 * 1280 < 2^31.
  */
 sg_status sg_fp8_sparse24_gemm_groupwise_packed(int64_t M, int64_t N, int64_t K, const uint8_t* xq,
                                                 int64_t ldx, const float* sx, int64_t sx_sm,

@@ -10,38 +10,40 @@ mainloop takes the values together with the metadata tensor E in its own
 layout).  This module defines that arrangement for gfx950's SMFMAC and the
 LDS image the GEMM kernels read; it is a pure byte permutation of the
 canonical values [N, K/2] and metadata [N, K/8] (``sparse24.py``), with rows
-padded to a multiple of 256 with zeros.
+padded to a multiple of 16 with zeros.
 
-For 256-row tile t (rows 256 t .. 256 t + 255) and 128-wide K block kb, the
-block starts at byte (t * KB + kb) * 20480 (KB = K / 128) and holds, for
-tile row r and lane group g = 0..3 (b = 32 (g & 1) + 8 (g >> 1)):
-  * values, 16 bytes at r * 64 + 16 * (g ^ ((r >> 1) & 3)):
+The weight is cut into 16-row blocks R (rows 16 R .. 16 R + 15); for block R
+and 128-wide K block kb a 1280-byte chunk starts at byte (R * KB + kb) * 1280
+(KB = K / 128), so that the chunks of one row block follow each other along K.
+For local row lr = 0..15 and lane group g = 0..3 (b = 32 (g & 1) + 8 (g >> 1))
+the chunk holds
+  * values, 16 bytes at lr * 64 + 16 * (g ^ ((lr >> 1) & 3)):
         compressed bytes [b, b + 8) and [b + 16, b + 24) of the row's 64
         compressed bytes of block kb (the SMFMAC A operand of lane group g);
-  * metadata, 4 bytes at 16384 + r * 16 + 4 * ((g + 2 * ((r >> 3) & 1)) & 3):
+  * metadata, 4 bytes at 1024 + lr * 16 + 4 * ((g + 2 * ((lr >> 3) & 1)) & 3):
         metadata bytes b/4, b/4 + 1, b/4 + 4, b/4 + 5 of the row's 16 metadata
         bytes of block kb (the SMFMAC index word of lane group g).
 """
 
 import numpy as np
 
-TILE_N = 256
-BLOCK_BYTES = 20480
-META_OFF = 16384
+ROWS = 16
+CHUNK_BYTES = 1280
+META_OFF = 1024
 
 
 def packed_bytes(n: int, k: int) -> int:
-    return -(-n // TILE_N) * (k // 128) * BLOCK_BYTES
+    return -(-n // ROWS) * (k // 128) * CHUNK_BYTES
 
 
 def _positions(n: int, kb_count: int):
     """Byte positions in the packed buffer, per (row, kb, g): values start and
     metadata word start."""
     rows = np.arange(n)
-    t, r = rows // TILE_N, rows % TILE_N
+    t, r = rows // ROWS, rows % ROWS
     kb = np.arange(kb_count)
     g = np.arange(4)
-    base = (t[:, None] * kb_count + kb[None, :]) * BLOCK_BYTES                     # [n, KB]
+    base = (t[:, None] * kb_count + kb[None, :]) * CHUNK_BYTES                     # [n, KB]
     vpos = base[:, :, None] + (r * 64)[:, None, None] + 16 * (g[None, None, :] ^ ((r[:, None, None] >> 1) & 3))
     mslot = (g[None, None, :] + 2 * ((r[:, None, None] >> 3) & 1)) & 3
     mpos = base[:, :, None] + META_OFF + (r * 16)[:, None, None] + 4 * mslot

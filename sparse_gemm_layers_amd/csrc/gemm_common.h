@@ -23,14 +23,16 @@ __device__ __forceinline__ int sp_meta_word(uint4 w, int g) {
 
 __device__ __forceinline__ int sp_a_off(int g) { return 32 * (g & 1) + 8 * (g >> 1); }
 
-// gfx950 packed weight layout (one 20480-byte block per 256-row tile and
-// 128-wide K block): values of row r, lane group g at r * 64 + 16 (g ^ ((r >> 1) & 3));
-// index word at 16384 + r * 16 + 4 ((g + 2 ((r >> 3) & 1)) & 3).
-constexpr int PK_TILE = 256, PK_BLOCK = 20480, PK_META = 16384;
+// gfx950 packed weight layout: one 1280-byte chunk per 16-row block R and
+// 128-wide K block kb, at (R * KB + kb) * 1280, so that one row block's chunks
+// follow each other along K.  Inside a chunk, local row lr's values for lane
+// group g sit at pk_val_off(lr, g) and its index word at
+// PK_META + pk_meta_word(lr, g).  The GEMM kernels' LDS image of a 256-row
+// tile uses the same swizzle with the tile row r (it depends on r mod 16
+// only): values at pk_val_off(r, g), index words at LDS_META + pk_meta_word(r, g).
+constexpr int PK_ROWS = 16, PK_CHUNK = 1280, PK_META = 1024, LDS_META = 16384;
 __device__ __host__ __forceinline__ int pk_val_off(int r, int g) { return r * 64 + 16 * (g ^ ((r >> 1) & 3)); }
-__device__ __host__ __forceinline__ int pk_meta_off(int r, int g) {
-  return PK_META + r * 16 + 4 * ((g + 2 * ((r >> 3) & 1)) & 3);
-}
+__device__ __host__ __forceinline__ int pk_meta_word(int r, int g) { return r * 16 + 4 * ((g + 2 * ((r >> 3) & 1)) & 3); }
 
 template <bool OUT_BF16>
 __device__ __forceinline__ void store1(void* y, int64_t off, float v) {

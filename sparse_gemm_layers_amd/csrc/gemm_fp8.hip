@@ -237,7 +237,7 @@ __device__ __forceinline__ LaneOffsets<true> lane_offsets_packed(int wn, int wm,
   LaneOffsets<true> o = lane_offsets<true>(wn, wm, g, lr);
   o.w0 = L::W_OFF + pk_val_off(wn * 128 + lr, g);
   o.w1 = 0;
-  o.mt = L::W_OFF + pk_meta_off(wn * 128 + lr, g);
+  o.mt = L::W_OFF + LDS_META + pk_meta_word(wn * 128 + lr, g);
   return o;
 }
 
@@ -417,10 +417,18 @@ template <bool PACKED>
 __device__ __forceinline__ PlanX2 make_plan_x2(const GemmArgs& a, int64_t n0, int64_t m0, int wave, int l) {
   using L = Stage<true>;
   PlanX2 p;
-  // packed weights: 20 contiguous 1 KB slots (values + metadata) per K block,
-  // 40 per double stage, 5 per wave: slot q = 8 j + wave
+  // packed weights: 20 LDS slots of 1 KB per K block, 40 per double stage,
+  // 5 per wave (q = 8 j + wave).  Slot s < 16 takes the values of the tile's
+  // row block s (the first 1024 bytes of its chunk), slot 16 + s the index
+  // words of row blocks 4 s .. 4 s + 3 (the last 256 bytes of their chunks).
+  // Offsets are relative to the tile's first chunk of K block 0.
+  const uint32_t rbs = (uint32_t)(a.K >> 7) * PK_CHUNK;     // bytes per row block
 #pragma unroll
-  for (int j = 0; j < 5; ++j) p.wo[j] = (uint32_t)((((8 * j + wave) % 20) * 1024) + l * 16);
+  for (int j = 0; j < 5; ++j) {
+    const int slot = (8 * j + wave) % 20;
+    p.wo[j] = slot < 16 ? slot * rbs + l * 16
+                        : (4 * (slot - 16) + (l >> 4)) * rbs + PK_META + (l & 15) * 16;
+  }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int slot = (8 * j + wave) & 15;      // 1 KB slot within the K block's X / W area
@@ -474,7 +482,7 @@ __device__ __forceinline__ void issue_double(uint8_t* st, const PlanX2& p, __amd
     for (int j = 0; j < 5; ++j) {
       const int q = 8 * j + wave, h = q / 20, slot = q % 20;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(st + h * x2::HALF + L::W_OFF + slot * 1024), 16,
-                                               p.wo[j], kbh[h] * PK_BLOCK, 0, 0);
+                                               p.wo[j], kbh[h] * PK_CHUNK, 0, 0);
     }
   } else {
 #pragma unroll
@@ -621,9 +629,11 @@ __global__ void __launch_bounds__(512) k_gemm_sparse_x2(GemmArgs a, int tiles_m,
 
   const int64_t mrows = min((int64_t)BM, a.M - m0), nrows = min((int64_t)BN, a.N - n0);
   const __amdgpu_buffer_rsrc_t rx = rsrc(a.x + m0 * a.ldx, (uint32_t)(mrows * a.ldx));
-  // packed weights: the tile's blocks are contiguous, KB * 20480 bytes from tile tn
+  // packed weights: the tile's row blocks are contiguous, KB * 1280 bytes each;
+  // row blocks past N do not exist and read as zero
+  const int64_t tile_rbs = min((int64_t)(BN / PK_ROWS), (a.N + PK_ROWS - 1) / PK_ROWS - (int64_t)tn * (BN / PK_ROWS));
   const __amdgpu_buffer_rsrc_t rw =
-      PACKED ? rsrc(a.w + (int64_t)tn * KB * PK_BLOCK, (uint32_t)(KB * PK_BLOCK))
+      PACKED ? rsrc(a.w + (int64_t)tn * (BN / PK_ROWS) * KB * PK_CHUNK, (uint32_t)(tile_rbs * KB * PK_CHUNK))
              : rsrc(a.w + n0 * a.ldw, (uint32_t)(nrows * a.ldw));
   const __amdgpu_buffer_rsrc_t rm = PACKED ? rw : rsrc(a.meta + n0 * a.ldm, (uint32_t)(nrows * a.ldm));
   const __amdgpu_buffer_rsrc_t rsx = rsrc(a.sx, 0xffffffffu);
@@ -675,107 +685,171 @@ __global__ void __launch_bounds__(512) k_gemm_sparse_x2(GemmArgs a, int tiles_m,
 }
 
 // ============================================================ decode kernel
-// For M <= 64 (decode-sized batches).  A workgroup owns 16 W rows and all M
-// columns (MT sub-tiles of 16); its 8 waves split the K blocks (wave w takes
-// kb = w, w + 8, ...), read their operands straight from global memory into
-// the matrix-core layout (the weight is streamed once from HBM; X is small
-// and stays in L2), and finally add their partial tiles through LDS.
-// Columns m >= M are zero-filled (the partial M tile).
-constexpr int DEC_WAVES = 8;
+// For M <= 64 (decode-sized batches).  A workgroup owns RB blocks of 16 W
+// rows and all M columns (MT sub-tiles of 16); its 8 waves split the K blocks
+// (wave w takes kb = w, w + 8, ...), read their operands straight from global
+// memory into the matrix-core layout, and finally add their partial tiles
+// through LDS.  The weight is streamed once from HBM; X is small and stays in
+// L2, and each X fragment a wave reads serves RB row blocks (RB is chosen at
+// launch so that the grid still covers the 256 CUs).  A wave issues the loads
+// of DEC_U K blocks before it multiplies them; all loads are unconditional
+// (buffer loads read zeros past the rows that exist), so nothing waits for a
+// load until its K block is multiplied.  (Measured on MI355X: two K blocks in
+// flight per wave stream fastest; deeper batches or double buffering are
+// slower.)  Columns m >= M are zero-filled (the partial M tile).
+constexpr int DEC_WAVES = 8, DEC_U = 2;
 
-template <bool SPARSE, bool PACKED, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
-__global__ void __launch_bounds__(512) k_gemm_decode(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) float red[DEC_WAVES][MT][64][4];
-  const int t = threadIdx.x, l = t & 63, wave = t >> 6;
-  const int g = l >> 4, lr = l & 15;
-  const int64_t n0 = (int64_t)blockIdx.x * 16;
-  const int64_t n = n0 + lr;            // this lane's W row (A operand)
-  const bool n_ok = n < a.N;
-  const int KB = (int)(a.K >> 7);
+// Operands of one K block for one wave.
+template <int RB, int MT>
+struct DecOps {
+  v4i asp[RB];    // sparse A operands (W rows n0 + 16 r .. + 15)
+  v8i ad[RB];     // dense A operands
+  int idx[RB];    // sparse index words
+  v8i bx[MT];     // X columns 16 j + lr
+  float sxv[MT];  // their scales
+  float sw4[RB][4];  // W scales of this lane's 4 output rows in each row block
+};
 
-  v4f acc[MT];
+#if SG_DEVICE_PASS
+// Buffer resources of a decode workgroup: reads past the rows that exist
+// return zeros, so every load is unconditional (a conditional load would make
+// the compiler wait for it where the branches join).
+struct DecRes {
+  __amdgpu_buffer_rsrc_t rx, rw, rm;
+};
+
+__device__ __forceinline__ v4i buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off, int soff) {
+  return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0));
+}
+__device__ __forceinline__ v2i buf_ld8(__amdgpu_buffer_rsrc_t r, uint32_t off, int soff) {
+  return __builtin_bit_cast(v2i, __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, 0));
+}
+__device__ __forceinline__ int buf_ld4(__amdgpu_buffer_rsrc_t r, uint32_t off, int soff) {
+  return __builtin_bit_cast(int, __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, 0));
+}
+
+template <bool SPARSE, bool PACKED, int RB, int MT, int GRAN_N>
+__device__ __forceinline__ void dec_load(const GemmArgs& a, const DecRes& res, int64_t n0, int kb, int KB, int lr,
+                                         int g, DecOps<RB, MT>& o) {
 #pragma unroll
-  for (int j = 0; j < MT; ++j) acc[j] = (v4f){0.f, 0.f, 0.f, 0.f};
-
-  for (int kb = wave; kb < KB; kb += DEC_WAVES) {
-    const int64_t k0 = (int64_t)kb * 128;
-    // A operand (W rows n0..n0+15)
-    v4i asp;
-    v8i ad;
-    int idx = 0;
+  for (int rb = 0; rb < RB; ++rb) {
+    const int64_t nb = n0 + 16 * rb;
+    o.idx[rb] = 0;
     if (SPARSE && PACKED) {
-      // rows past N are zero padding inside the packed buffer: no predicate
-      const uint8_t* blk = a.w + ((n0 / PK_TILE) * KB + kb) * (int64_t)PK_BLOCK;
-      const int r = (int)(n0 % PK_TILE) + lr;
-      const uint4 av = *reinterpret_cast<const uint4*>(blk + pk_val_off(r, g));
-      asp = (v4i){(int)av.x, (int)av.y, (int)av.z, (int)av.w};
-      idx = *reinterpret_cast<const int*>(blk + pk_meta_off(r, g));
+      // chunk of (row block rb of this workgroup, K block kb)
+      const uint32_t c = (uint32_t)(rb * KB) * PK_CHUNK;
+      const v4i av = buf_ld16(res.rw, c + pk_val_off(lr, g), kb * PK_CHUNK);
+      o.asp[rb] = av;
+      o.idx[rb] = buf_ld4(res.rw, c + PK_META + pk_meta_word(lr, g), kb * PK_CHUNK);
     } else if (SPARSE) {
-      uint2 lo = {0u, 0u}, hi = {0u, 0u};
-      uint4 mw = {0u, 0u, 0u, 0u};
-      if (n_ok) {
-        const uint8_t* wr = a.w + n * a.ldw + k0 / 2 + sp_a_off(g);
-        lo = *reinterpret_cast<const uint2*>(wr);
-        hi = *reinterpret_cast<const uint2*>(wr + 16);
-        mw = *reinterpret_cast<const uint4*>(a.meta + n * a.ldm + k0 / 8);
-      }
-      asp = (v4i){(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y};
-      idx = sp_meta_word(mw, g);
+      const uint32_t row = (uint32_t)((16 * rb + lr) * a.ldw) + sp_a_off(g);
+      const v2i lo = buf_ld8(res.rw, row, kb * 64), hi = buf_ld8(res.rw, row + 16, kb * 64);
+      const v4i mw = buf_ld16(res.rm, (uint32_t)((16 * rb + lr) * a.ldm), kb * 16);
+      o.asp[rb] = (v4i){lo[0], lo[1], hi[0], hi[1]};
+      o.idx[rb] = sp_meta_word(make_uint4(mw[0], mw[1], mw[2], mw[3]), g);
     } else {
-      uint4 lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
-      if (n_ok) {
-        const uint8_t* wr = a.w + n * a.ldw + k0 + 32 * g;
-        lo = *reinterpret_cast<const uint4*>(wr);
-        hi = *reinterpret_cast<const uint4*>(wr + 16);
-      }
-      ad = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      const uint32_t row = (uint32_t)((16 * rb + lr) * a.ldw) + 32 * g;
+      const v4i lo = buf_ld16(res.rw, row, kb * 128), hi = buf_ld16(res.rw, row + 16, kb * 128);
+      o.ad[rb] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
-    // W scale(s) of this K block
-    float sw4[4];
+    // W scale(s) of this K block (rows past N read the last row's scale; they are never stored)
     if (GRAN_N == 128) {
-      const float v = a.sw[(n0 >> 7) * a.sw_sn + kb * a.sw_sk];
-      sw4[0] = sw4[1] = sw4[2] = sw4[3] = v;
+      const float v = a.sw[(min(nb, a.N - 1) >> 7) * a.sw_sn + kb * a.sw_sk];
+      o.sw4[rb][0] = o.sw4[rb][1] = o.sw4[rb][2] = o.sw4[rb][3] = v;
     } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int64_t ne = n0 + 4 * g + e;
-        sw4[e] = ne < a.N ? a.sw[ne * a.sw_sn + kb * a.sw_sk] : 0.f;
-      }
+      for (int e = 0; e < 4; ++e) o.sw4[rb][e] = a.sw[min(nb + 4 * g + e, a.N - 1) * a.sw_sn + kb * a.sw_sk];
     }
+  }
+#pragma unroll
+  for (int j = 0; j < MT; ++j) {
+    const int m = j * 16 + lr;   // rows past M read as zero; their scale is the last row's
+    const uint32_t xo = (uint32_t)(m * a.ldx) + 32 * g;
+    const v4i lo = buf_ld16(res.rx, xo, kb * 128), hi = buf_ld16(res.rx, xo + 16, kb * 128);
+    o.bx[j] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    o.sxv[j] = a.sx[(min((int64_t)m, a.M - 1) >> a.gm_shift) * a.sx_sm + kb * a.sx_sk];
+  }
+}
+#endif  // SG_DEVICE_PASS
+
+template <bool SPARSE, int RB, int MT>
+__device__ __forceinline__ void dec_compute(const DecOps<RB, MT>& o, v4f (&acc)[RB][MT]) {
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int j = 0; j < MT; ++j) {
-      const int64_t m = j * 16 + lr;
-      uint4 lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
-      float sxv = 0.f;
-      if (m < a.M) {
-        const uint8_t* xr = a.x + m * a.ldx + k0 + 32 * g;
-        lo = *reinterpret_cast<const uint4*>(xr);
-        hi = *reinterpret_cast<const uint4*>(xr + 16);
-        sxv = a.sx[(m >> a.gm_shift) * a.sx_sm + kb * a.sx_sk];
-      }
-      const v8i bx = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      const v4f p = SPARSE ? mma_sparse(asp, bx, idx) : mma_dense(ad, bx);
+      const v4f p = SPARSE ? mma_sparse(o.asp[rb], o.bx[j], o.idx[rb]) : mma_dense(o.ad[rb], o.bx[j]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[j][e] = fmaf(p[e] * sw4[e], sxv, acc[j][e]);
+      for (int e = 0; e < 4; ++e) acc[rb][j][e] = fmaf(p[e] * o.sw4[rb][e], o.sxv[j], acc[rb][j][e]);
     }
+}
+
+template <bool SPARSE, bool PACKED, int RB, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
+__global__ void __launch_bounds__(512) k_gemm_decode(GemmArgs a) {
+  constexpr int U = DEC_U;
+  __shared__ __attribute__((aligned(16))) float red[DEC_WAVES][RB * MT][64][4];
+#if SG_DEVICE_PASS
+  const int t = threadIdx.x, l = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int g = l >> 4, lr = l & 15;
+  const int64_t n0 = (int64_t)blockIdx.x * 16 * RB;
+  const int KB = (int)(a.K >> 7);
+  const int nt = (KB - wave + DEC_WAVES - 1) / DEC_WAVES;   // K blocks of this wave
+  const int rows = (int)min((int64_t)(16 * RB), a.N - n0);  // W rows of this workgroup that exist
+  DecRes res;
+  res.rx = rsrc(a.x, (uint32_t)(a.M * a.ldx));
+  if (SPARSE && PACKED) {
+    const int rbs = (rows + PK_ROWS - 1) / PK_ROWS;
+    res.rw = rsrc(a.w + (n0 / PK_ROWS) * KB * PK_CHUNK, (uint32_t)(rbs * KB * PK_CHUNK));
+    res.rm = res.rw;
+  } else {
+    res.rw = rsrc(a.w + n0 * a.ldw, (uint32_t)(rows * a.ldw));
+    res.rm = SPARSE ? rsrc(a.meta + n0 * a.ldm, (uint32_t)(rows * a.ldm)) : res.rw;
+  }
+
+  v4f acc[RB][MT];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int j = 0; j < MT; ++j) acc[rb][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+  DecOps<RB, MT> ops[U];
+  // (K blocks past the wave's last are loaded as its last one and not multiplied)
+  auto load_batch = [&](DecOps<RB, MT>(&o)[U], int t0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      dec_load<SPARSE, PACKED, RB, MT, GRAN_N>(a, res, n0, wave + DEC_WAVES * min(t0 + u, nt - 1), KB, lr, g, o[u]);
+  };
+  auto compute_batch = [&](const DecOps<RB, MT>(&o)[U], int t0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (t0 + u < nt) dec_compute<SPARSE, RB, MT>(o[u], acc);
+  };
+  for (int t0 = 0; t0 < nt; t0 += U) {
+    load_batch(ops, t0);
+    compute_batch(ops, t0);
   }
 
 #pragma unroll
-  for (int j = 0; j < MT; ++j)
-    *reinterpret_cast<float4*>(&red[wave][j][l][0]) = make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int j = 0; j < MT; ++j)
+      *reinterpret_cast<float4*>(&red[wave][rb * MT + j][l][0]) =
+          make_float4(acc[rb][j][0], acc[rb][j][1], acc[rb][j][2], acc[rb][j][3]);
   __syncthreads();
-  // 512 threads: thread -> (sub-tile j, lane ll); MT * 64 lanes of 4 values
-  for (int q = t; q < MT * 64; q += 512) {
-    const int j = q >> 6, ll = q & 63;
-    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  // 512 threads: thread -> (row block rb, sub-tile j, lane ll); RB * MT * 64 lanes of 4 values
+  for (int q = t; q < RB * MT * 64; q += 512) {
+    const int s = q >> 6, ll = q & 63, rb = s / MT, j = s % MT;
+    float4 v4 = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int w = 0; w < DEC_WAVES; ++w) {
-      const float4 v = *reinterpret_cast<const float4*>(&red[w][j][ll][0]);
-      s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+      const float4 v = *reinterpret_cast<const float4*>(&red[w][s][ll][0]);
+      v4.x += v.x; v4.y += v.y; v4.z += v.z; v4.w += v.w;
     }
-    const v4f out = {s.x, s.y, s.z, s.w};
-    store_quad<OUT_BF16, OUT_T>(a, (int64_t)j * 16 + (ll & 15), n0 + 4 * (ll >> 4), out);
+    const v4f out = {v4.x, v4.y, v4.z, v4.w};
+    store_quad<OUT_BF16, OUT_T>(a, (int64_t)j * 16 + (ll & 15), n0 + 16 * rb + 4 * (ll >> 4), out);
   }
+#endif  // SG_DEVICE_PASS
 }
 
 // ------------------------------------------------------------------ dispatch
@@ -789,9 +863,19 @@ static void launch_large(const GemmArgs& a, hipStream_t st) {
     k_gemm_large<SPARSE, GRAN_N, OUT_BF16, OUT_T><<<tm * tn, 256, 0, st>>>(a, tm, tn);
 }
 
+// Row blocks per workgroup: the largest of 4, 2, 1 with RB * MT <= 4 (the
+// registers of the operands) that keeps at least 224 workgroups (7/8 of the
+// CUs busy).
 template <bool SPARSE, bool PACKED, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
 static void launch_decode_mt(const GemmArgs& a, hipStream_t st) {
-  k_gemm_decode<SPARSE, PACKED, MT, GRAN_N, OUT_BF16, OUT_T><<<(unsigned)cdiv(a.N, 16), 512, 0, st>>>(a);
+  const int64_t rows16 = cdiv(a.N, 16);
+  constexpr int RB4 = MT == 1 ? 4 : 1, RB2 = MT <= 2 ? 2 : 1;
+  if (RB4 == 4 && rows16 >= 4 * 224)
+    k_gemm_decode<SPARSE, PACKED, RB4, MT, GRAN_N, OUT_BF16, OUT_T><<<(unsigned)cdiv(rows16, RB4), 512, 0, st>>>(a);
+  else if (RB2 == 2 && rows16 >= 2 * 224)
+    k_gemm_decode<SPARSE, PACKED, RB2, MT, GRAN_N, OUT_BF16, OUT_T><<<(unsigned)cdiv(rows16, RB2), 512, 0, st>>>(a);
+  else
+    k_gemm_decode<SPARSE, PACKED, 1, MT, GRAN_N, OUT_BF16, OUT_T><<<(unsigned)rows16, 512, 0, st>>>(a);
 }
 
 template <bool SPARSE, bool PACKED, int GRAN_N, bool OUT_BF16, bool OUT_T>
@@ -920,7 +1004,8 @@ extern "C" sg_status sg_fp8_sparse24_gemm_groupwise_packed(int64_t M, int64_t N,
   if (st != SG_OK) return st;
   if (!wpacked) return SG_ERR_NULL;
   if (!aligned(wpacked, 16)) return SG_ERR_ALIGN;
-  if ((K / 128) * (int64_t)PK_BLOCK > 0x7fffffffLL) return SG_ERR_SHAPE;
+  // the large-M kernel addresses a tile's 16 row blocks with 32-bit offsets
+  if ((K / 128) * (int64_t)(BN / PK_ROWS) * PK_CHUNK > 0x7fffffffLL) return SG_ERR_SHAPE;
   if (M == 0 || N == 0) return SG_OK;
   const GemmArgs a = make_args(M, N, K, xq, ldx, sx, sx_sm, sx_sk, gran_m, wpacked, 0, nullptr, 0, sw, sw_sn,
                                sw_sk, gran_n, y, y_dt, ldy);

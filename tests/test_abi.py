@@ -174,8 +174,8 @@ def test_binding_rejects_cpu_tensors():
 
 def test_packed_bytes():
     lib = sg.lib()
-    assert lib.sg_sparse24_packed_bytes(4096, 4096) == 16 * 32 * 20480
-    assert lib.sg_sparse24_packed_bytes(300, 384) == 2 * 3 * 20480
+    assert lib.sg_sparse24_packed_bytes(4096, 4096) == 256 * 32 * 1280
+    assert lib.sg_sparse24_packed_bytes(300, 384) == 19 * 3 * 1280
     assert lib.sg_sparse24_packed_bytes(0, 128) == 0
     assert lib.sg_sparse24_packed_bytes(10, 100) == -1 and lib.sg_sparse24_packed_bytes(-1, 128) == -1
 

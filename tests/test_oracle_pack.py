@@ -16,7 +16,7 @@ def test_golden_row0():
     meta = np.zeros((1, 16), np.uint8)
     meta[0] = np.arange(200, 216)
     p = oracle.pack24_gfx950(vals, meta)
-    assert p.size == 20480
+    assert p.size == 1280
     seen = 0
     for line in open(os.path.join(GOLDEN, "pack_gfx950_row0.txt")):
         line = line.split("#")[0].strip()
@@ -34,15 +34,30 @@ def test_roundtrip_and_zero_padding():
     vals = workloads.random_e4m3_codes(rng, (n, k // 2))
     meta = rng.integers(0, 256, size=(n, k // 8)).astype(np.uint8)
     p = oracle.pack24_gfx950(vals, meta)
-    assert p.size == oracle.packed_bytes(n, k) == 2 * 3 * 20480
+    assert p.size == oracle.packed_bytes(n, k) == 19 * 3 * 1280
     v2, m2 = oracle.unpack24_gfx950(p, n, k)
     assert np.array_equal(v2, vals) and np.array_equal(m2, meta)
-    # padded rows 300..511 of tile 1 hold zeros only
-    pv, pm = oracle.unpack24_gfx950(p, 512, k)
+    # padded rows 300..303 of row block 18 hold zeros only
+    pv, pm = oracle.unpack24_gfx950(p, 304, k)
     assert not pv[300:].any() and not pm[300:].any()
-    # every byte of the 256-row tiles is used exactly once by the first 512 rows
-    assert np.count_nonzero(oracle.pack24_gfx950(np.full((512, k // 2), 7, np.uint8),
-                                                 np.full((512, k // 8), 9, np.uint8))) == p.size
+    # every byte of the 16-row blocks is used exactly once by the first 304 rows
+    assert np.count_nonzero(oracle.pack24_gfx950(np.full((304, k // 2), 7, np.uint8),
+                                                 np.full((304, k // 8), 9, np.uint8))) == p.size
+
+
+def test_row_block_chunks_are_contiguous_along_k():
+    """The chunk of (row block R, K block kb) starts at (R * KB + kb) * 1280, so
+    one row block's chunks follow each other: packing a row block alone gives
+    exactly its bytes of the full buffer."""
+    rng = np.random.default_rng(43)
+    n, k = 48, 512
+    vals = workloads.random_e4m3_codes(rng, (n, k // 2))
+    meta = rng.integers(0, 256, size=(n, k // 8)).astype(np.uint8)
+    p = oracle.pack24_gfx950(vals, meta)
+    per_block = (k // 128) * 1280
+    for rb in range(3):
+        sub = oracle.pack24_gfx950(vals[16 * rb:16 * rb + 16], meta[16 * rb:16 * rb + 16])
+        assert np.array_equal(p[rb * per_block:(rb + 1) * per_block], sub)
 
 
 def test_each_lane_group_word_is_its_smfmac_index():
@@ -59,7 +74,7 @@ def test_each_lane_group_word_is_its_smfmac_index():
     for r in range(16):
         for g in range(4):
             slot = (g + 2 * ((r >> 3) & 1)) & 3
-            w = int.from_bytes(bytes(p[16384 + r * 16 + 4 * slot:16384 + r * 16 + 4 * slot + 4]), "little")
+            w = int.from_bytes(bytes(p[1024 + r * 16 + 4 * slot:1024 + r * 16 + 4 * slot + 4]), "little")
             base = 64 * (g & 1) + 16 * (g >> 1)
             groups = [base // 4 + j for j in range(4)] + [base // 4 + 8 + j for j in range(4)]
             assert [(w >> (4 * j)) & 15 for j in range(8)] == [nib[r, q] for q in groups]
