@@ -852,6 +852,192 @@ __global__ void __launch_bounds__(512) k_gemm_decode(GemmArgs a) {
 #endif  // SG_DEVICE_PASS
 }
 
+// ------------------------------------------- decode kernel, LDS-DMA streaming
+// For packed 2:4 weights with 128-row W scales and M <= 48.  Same work split
+// as k_gemm_decode, but each wave streams its K blocks into a private ring of
+// LDS slots with buffer loads that write LDS directly: per K block the RB
+// weight chunks (verbatim), the MT X slices (16 rows x 128 B, 16-byte chunks
+// swizzled by row against bank conflicts) and both scales.  A wave only waits
+// for its own loads, so the loop has no barriers, and a load into LDS needs no
+// registers while in flight (measured on MI355X: this streams faster than
+// loads into registers, which stop gaining from more loads in flight early).
+// Ring of two slots per wave (the compiler tracks the loads in flight into two
+// LDS arrays separately, so that reading one slot does not wait for the
+// other); a slot holds KPS K blocks.
+template <int RB, int MT>
+struct DmaCfg {
+  static constexpr int XOFF = RB * PK_CHUNK;                    // X slices (2 KB each)
+  static constexpr int SXOFF = XOFF + MT * 2048;                // X scales (256 B per sub-tile)
+  static constexpr int SWOFF = SXOFF + MT * 256;                // W scales (256 B)
+  static constexpr int KSZ = SWOFF + 256;                       // bytes per wave per K block
+  static constexpr int KPS = 2 * 2 * DEC_WAVES * KSZ <= 150 * 1024 ? 2 : 1;   // K blocks per slot
+  static constexpr int SLOT = KPS * KSZ;                        // bytes per wave per slot
+  static constexpr int ARR = DEC_WAVES * SLOT;                  // one ring slot of all waves
+  static constexpr int L = KPS * (2 * RB + 3 * MT + 1);         // LDS-DMA loads per slot
+  static constexpr bool FITS = 2 * DEC_WAVES * KSZ <= 160 * 1024;  // two slots of one K block
+};
+
+#if SG_DEVICE_PASS
+struct DmaOffs {
+  uint32_t x[2];    // X slice chunk source offsets (K block 0)
+  uint32_t sx[4];   // X scale source offsets per sub-tile (K block 0)
+  uint32_t sw;      // W scale source offset (K block 0)
+};
+
+// Loads of one K block into its part of a slot.  Every load writes LDS
+// directly (so that the compiler can neither merge nor drop any of them: the
+// slot's count of L loads is exact).  A K block past the wave's last is still
+// issued (so that every slot has exactly L loads in flight on every path), but
+// its weight and X loads are out of range (no memory access, zeros) and its
+// scales are those of a valid block.
+template <int RB, int MT>
+__device__ __forceinline__ void dma_issue(uint8_t* slot, const GemmArgs& a, __amdgpu_buffer_rsrc_t rw,
+                                          __amdgpu_buffer_rsrc_t rx, __amdgpu_buffer_rsrc_t rsx,
+                                          __amdgpu_buffer_rsrc_t rsw, const DmaOffs& o, int kb, int KB, int l,
+                                          bool valid) {
+  using C = DmaCfg<RB, MT>;
+  const int ws = valid ? kb * PK_CHUNK : 0x40000000, xs = valid ? kb * 128 : 0x40000000;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    uint8_t* c = slot + rb * PK_CHUNK;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)c, 16, (uint32_t)(rb * KB) * PK_CHUNK + l * 16, ws, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(c + PK_META), 4,
+                                             (uint32_t)(rb * KB) * PK_CHUNK + PK_META + l * 4, ws, 0, 0);
+  }
+#pragma unroll
+  for (int j = 0; j < MT; ++j) {
+    uint8_t* x = slot + C::XOFF + j * 2048;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)x, 16, o.x[0] + (uint32_t)(16 * j * a.ldx), xs, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(x + 1024), 16, o.x[1] + (uint32_t)(16 * j * a.ldx),
+                                             xs, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsx, (lds_void*)(slot + C::SXOFF + j * 256), 4, o.sx[j],
+                                             (int)(kb * a.sx_sk * 4), 0, 0);
+  }
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, (lds_void*)(slot + C::SWOFF), 4, o.sw, (int)(kb * a.sw_sk * 4), 0, 0);
+}
+#endif
+
+template <int RB, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
+__global__ void __launch_bounds__(512) k_gemm_decode_dma(GemmArgs a) {
+#if SG_DEVICE_PASS
+  using C = DmaCfg<RB, MT>;
+  constexpr int KPS = C::KPS;
+  static_assert(MT <= 4 && 2 * C::ARR <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(1024))) uint8_t r0[C::ARR];
+  __shared__ __attribute__((aligned(1024))) uint8_t r1[C::ARR];
+  const int t = threadIdx.x, l = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int g = l >> 4, lr = l & 15;
+  const int64_t n0 = (int64_t)blockIdx.x * 16 * RB;
+  const int KB = (int)(a.K >> 7);
+  const int nt = (KB - wave + DEC_WAVES - 1) / DEC_WAVES;    // K blocks of this wave
+  const int ns = (nt + KPS - 1) / KPS;                         // slots of this wave
+  const int rows = (int)min((int64_t)(16 * RB), a.N - n0);
+  const int rbs = (rows + PK_ROWS - 1) / PK_ROWS;
+  const __amdgpu_buffer_rsrc_t rw = rsrc(a.w + (n0 / PK_ROWS) * KB * PK_CHUNK, (uint32_t)(rbs * KB * PK_CHUNK));
+  const __amdgpu_buffer_rsrc_t rx = rsrc(a.x, (uint32_t)(a.M * a.ldx));
+  const __amdgpu_buffer_rsrc_t rsx = rsrc(a.sx, 0xffffffffu);
+  const __amdgpu_buffer_rsrc_t rsw = rsrc(a.sw, 0xffffffffu);
+  DmaOffs o;
+  // X slice: instruction i, lane l -> LDS 16-byte position p = 64 i + l: row p >> 3, chunk (p & 7) ^ (row & 7)
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int p = 64 * i + l, r = p >> 3, c = (p & 7) ^ (r & 7);
+    o.x[i] = (uint32_t)(r * a.ldx + c * 16);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t m = min((int64_t)(16 * j + (l & 15)), a.M - 1);
+    o.sx[j] = (uint32_t)(((m >> a.gm_shift) * a.sx_sm) * 4);
+  }
+  o.sw = (uint32_t)(((min(n0 + 16 * (l % RB), a.N - 1) >> 7) * a.sw_sn) * 4);
+  // lane-constant LDS offsets within a wave's slot
+  const uint32_t wslot = (uint32_t)wave * C::SLOT;
+  const uint32_t oa = wslot + pk_val_off(lr, g), om = wslot + PK_META + pk_meta_word(lr, g);
+  const uint32_t ox0 = wslot + C::XOFF + lr * 128 + (((2 * g) ^ (lr & 7)) << 4);
+  const uint32_t ox1 = wslot + C::XOFF + lr * 128 + (((2 * g + 1) ^ (lr & 7)) << 4);
+  const uint32_t osx = wslot + C::SXOFF + lr * 4, osw = wslot + C::SWOFF;
+
+  auto issue = [&](uint8_t* arr, int s) {
+#pragma unroll
+    for (int k = 0; k < KPS; ++k) {
+      const int tt = s * KPS + k;
+      dma_issue<RB, MT>(arr + wslot + k * C::KSZ, a, rw, rx, rsx, rsw, o, wave + DEC_WAVES * min(tt, nt - 1), KB, l,
+                        tt < nt);
+    }
+  };
+
+  v4f acc[RB][MT];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int j = 0; j < MT; ++j) acc[rb][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const uint8_t* sl, int s) {
+#pragma unroll
+    for (int k = 0; k < KPS; ++k) {
+      if (s * KPS + k < nt) {
+        const uint32_t kk = k * C::KSZ;
+        v8i bx[MT];
+        float sxv[MT];
+#pragma unroll
+        for (int j = 0; j < MT; ++j) {
+          const uint4 lo = lds_ld<uint4>(sl, ox0 + kk + j * 2048), hi = lds_ld<uint4>(sl, ox1 + kk + j * 2048);
+          bx[j] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+          sxv[j] = lds_ld<float>(sl, osx + kk + j * 256);
+        }
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const uint4 av = lds_ld<uint4>(sl, oa + kk + rb * PK_CHUNK);
+          const int idx = lds_ld<int>(sl, om + kk + rb * PK_CHUNK);
+          const float swv = lds_ld<float>(sl, osw + kk + rb * 4);
+          const v4i aa = {(int)av.x, (int)av.y, (int)av.z, (int)av.w};
+#pragma unroll
+          for (int j = 0; j < MT; ++j) {
+            const v4f p = mma_sparse(aa, bx[j], idx);
+            acc[rb][j] += p * (swv * sxv[j]);
+          }
+        }
+      }
+    }
+  };
+
+  // slot s lives in r0 for even s, r1 for odd s; slot s + 1 is loaded while
+  // slot s is multiplied
+  if (ns > 0) issue(r0, 0);
+  for (int s0 = 0; s0 < ns; s0 += 2) {
+    issue(r1, s0 + 1);
+    wait_vmcnt<C::L>();
+    compute(r0, s0);
+    if (s0 + 1 < ns) {
+      issue(r0, s0 + 2);
+      wait_vmcnt<C::L>();
+      compute(r1, s0 + 1);
+    }
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+  float4* red = reinterpret_cast<float4*>(r0);    // [DEC_WAVES][RB * MT][64]
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int j = 0; j < MT; ++j)
+      red[(wave * RB * MT + rb * MT + j) * 64 + l] = make_float4(acc[rb][j][0], acc[rb][j][1], acc[rb][j][2], acc[rb][j][3]);
+  __syncthreads();
+  for (int q = t; q < RB * MT * 64; q += 512) {
+    const int s = q >> 6, ll = q & 63, rb = s / MT, j = s % MT;
+    float4 v4 = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int w = 0; w < DEC_WAVES; ++w) {
+      const float4 v = red[(w * RB * MT + s) * 64 + ll];
+      v4.x += v.x; v4.y += v.y; v4.z += v.z; v4.w += v.w;
+    }
+    const v4f out = {v4.x, v4.y, v4.z, v4.w};
+    store_quad<OUT_BF16, OUT_T>(a, (int64_t)j * 16 + (ll & 15), n0 + 16 * rb + 4 * (ll >> 4), out);
+  }
+#endif
+}
+
 // ------------------------------------------------------------------ dispatch
 
 template <bool SPARSE, bool PACKED, int GRAN_N, bool OUT_BF16, bool OUT_T>
@@ -863,12 +1049,33 @@ static void launch_large(const GemmArgs& a, hipStream_t st) {
     k_gemm_large<SPARSE, GRAN_N, OUT_BF16, OUT_T><<<tm * tn, 256, 0, st>>>(a, tm, tn);
 }
 
-// Row blocks per workgroup: the largest of 4, 2, 1 with RB * MT <= 4 (the
-// registers of the operands) that keeps at least 224 workgroups (7/8 of the
-// CUs busy).
+// Launches the LDS-streaming decode kernel with RB row blocks per workgroup if
+// its ring fits LDS and the grid keeps at least 224 workgroups (7/8 of the
+// CUs busy; RB = 1 always qualifies).
+template <int RB, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
+static bool try_decode_dma(const GemmArgs& a, hipStream_t st, int64_t rows16) {
+  if constexpr (DmaCfg<RB, MT>::FITS) {
+    if (RB == 1 || rows16 >= RB * 224) {
+      k_gemm_decode_dma<RB, MT, GRAN_N, OUT_BF16, OUT_T><<<(unsigned)cdiv(rows16, RB), 512, 0, st>>>(a);
+      return true;
+    }
+  }
+  return false;
+}
+
+// Row blocks per workgroup: the largest of 4, 2, 1 that keeps at least 224
+// workgroups and whose operands fit (LDS ring of the streaming kernel, or
+// RB * MT <= 4 for the registers of k_gemm_decode).  Packed 2:4 weights with
+// 128-row W scales take the LDS-streaming kernel when one of its rings fits.
 template <bool SPARSE, bool PACKED, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
 static void launch_decode_mt(const GemmArgs& a, hipStream_t st) {
   const int64_t rows16 = cdiv(a.N, 16);
+  if constexpr (SPARSE && PACKED && GRAN_N == 128 && DmaCfg<1, MT>::FITS) {
+    if (try_decode_dma<4, MT, GRAN_N, OUT_BF16, OUT_T>(a, st, rows16) ||
+        try_decode_dma<2, MT, GRAN_N, OUT_BF16, OUT_T>(a, st, rows16) ||
+        try_decode_dma<1, MT, GRAN_N, OUT_BF16, OUT_T>(a, st, rows16))
+      return;
+  }
   constexpr int RB4 = MT == 1 ? 4 : 1, RB2 = MT <= 2 ? 2 : 1;
   if (RB4 == 4 && rows16 >= 4 * 224)
     k_gemm_decode<SPARSE, PACKED, RB4, MT, GRAN_N, OUT_BF16, OUT_T><<<(unsigned)cdiv(rows16, RB4), 512, 0, st>>>(a);

@@ -166,6 +166,14 @@ def test_packed_decode_shapes(m, n, k):
     check(True, m, n, k, seed=4, forms=("y", "yt"), packed=True)
 
 
+# Decode-sized M with N large enough that a workgroup owns 4 (M <= 16) or 2
+# (M <= 48) row blocks of 16 and the last workgroup is partly past N; K of
+# 384 leaves 5 of the 8 waves without a K block.
+@pytest.mark.parametrize("m,n", [(16, 14350), (9, 14400), (37, 7190), (30, 7200)])
+def test_packed_decode_ragged_row_blocks(m, n):
+    check(True, m, n, 384, seed=13 + m, packed=True)
+
+
 def test_packed_fp32_row_major_scales_and_equal_to_unpacked():
     d = workloads.sparse_large(seed=21, m=300, n=700, k=512)
     xq, sx, wq, meta, sw = oracle_operands(d["x"], d["w"], 1, 128, True)
