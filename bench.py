@@ -74,27 +74,6 @@ def gen_layer(seed, m, n, k, on_gpu_rng=False):
     return x, wq, meta, sw, wp
 
 
-class Timer:
-    """HIP events on the current stream around repeated launches."""
-
-    def __init__(self):
-        self.pairs = []
-
-    def __enter__(self):
-        self.s = torch.cuda.Event(enable_timing=True)
-        self.s.record()
-        return self
-
-    def __exit__(self, *a):
-        e = torch.cuda.Event(enable_timing=True)
-        e.record()
-        self.pairs.append((self.s, e))
-
-    def mean_ms(self):
-        torch.cuda.synchronize()
-        return float(np.mean([s.elapsed_time(e) for s, e in self.pairs]))
-
-
 def time_fn(fn, reps=50, warm=5):
     """Mean GPU time of one call: `reps` calls are queued back to back behind a
     short GPU sleep (so that the host's launch cost, which exceeds the run time
@@ -119,26 +98,27 @@ def headline(steps, warmup):
     xq = torch.empty((m, k), dtype=torch.uint8, device=DEV)
     sx = torch.empty((k // 128, m), dtype=torch.float32, device=DEV).t()
     y = torch.empty((m, n), dtype=torch.bfloat16, device=DEV)
-    gemm_t = Timer()
 
-    def step(i, timed):
+    def step(i):
         x, _, _, sw, wp = sets[i % ROTATE]
         sg.fp8_quant_groupwise(x, gr=1, gc=128, q=xq, s=sx)
-        if timed:
-            with gemm_t:
-                sg.fp8_sparse24_gemm_groupwise_packed(xq, sx, wp, n, sw, 1, 128, y=y)
-        else:
-            sg.fp8_sparse24_gemm_groupwise_packed(xq, sx, wp, n, sw, 1, 128, y=y)
+        sg.fp8_sparse24_gemm_groupwise_packed(xq, sx, wp, n, sw, 1, 128, y=y)
 
     for i in range(warmup):
-        step(i, False)
+        step(i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        step(i, True)
+        step(i)
     torch.cuda.synchronize()
     ms_step = (time.perf_counter() - t0) * 1e3 / steps
-    gemm_ms = gemm_t.mean_ms()
+    # The GEMM alone, launched back to back over the same rotating sets (X
+    # quantised once per set): its mean launch duration, for the roofline.
+    xqs = [sg.fp8_quant_groupwise(sets[i][0], gr=1, gc=128) for i in range(ROTATE)]
+    gemm_ms = time_fn(lambda i: sg.fp8_sparse24_gemm_groupwise_packed(
+        xqs[i % ROTATE][0], xqs[i % ROTATE][1], sets[i % ROTATE][4], n, sets[i % ROTATE][3], 1, 128, y=y),
+        reps=steps, warm=warmup)
+    del xqs
     flops = 2.0 * m * n * k
     return {"ms_per_step": ms_step, "value": flops / (ms_step * 1e-3) / 1e12, "gemm_ms": gemm_ms,
             "gemm_tflops": flops / (gemm_ms * 1e-3) / 1e12, "m": m, "n": n, "k": k}
