@@ -34,6 +34,14 @@ constexpr int PK_ROWS = 16, PK_CHUNK = 1280, PK_META = 1024, LDS_META = 16384;
 __device__ __host__ __forceinline__ int pk_val_off(int r, int g) { return r * 64 + 16 * (g ^ ((r >> 1) & 3)); }
 __device__ __host__ __forceinline__ int pk_meta_word(int r, int g) { return r * 16 + 4 * ((g + 2 * ((r >> 3) & 1)) & 3); }
 
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 template <bool OUT_BF16>
 __device__ __forceinline__ void store1(void* y, int64_t off, float v) {
   if (OUT_BF16)

@@ -15,11 +15,16 @@
 // bf16 part: v_mfma_f32_16x16x32_bf16 accumulating straight into acc (no
 // scales).
 //
-// Tile, waves and LDS staging follow the FP8 large-M kernel: 256 W rows x 128
-// X rows, 4 waves in 2 x 2, W on the matrix-core A side.  Stage s < KB1 holds
-// int4 block s (64 B per row); the following stages hold 64-wide bf16 blocks
-// (128 B per row).
-#include "gemm_common.h"
+// Workgroup tile 256 W rows (n) x 128 X rows (m), W on the matrix-core A
+// side, 8 waves in two K groups of a 2 x 2 wave grid (each wave 128 n x 64 m),
+// like the FP8 sparse kernel: operands travel HBM -> LDS with buffer loads
+// that write LDS directly, two "double stages" alternate, and group q
+// multiplies half q of a double stage.  An int4 double stage holds two
+// 128-wide K blocks (group q takes K block 2 it + q, promoted with its own
+// scales); a bf16 double stage holds 64 columns of X2 and W2 (group q takes
+// columns 32 q .. 32 q + 31).  At the end the two groups add their partial
+// tiles and the finished tile is stored in whole rows.
+#include "tile_epilogue.h"
 
 namespace sg {
 
@@ -41,100 +46,126 @@ struct MixedArgs {
   int64_t ldw2;
   void* y;
   int64_t ldy;
-  int vec_store;
+  int vec16;      // y is 16-byte aligned and a row of y is a multiple of 16 bytes
 };
 
 namespace mixed {
-constexpr int BN = 256, BM = 128;
-// stage layout (bytes): X 128 rows x 128 B | W 256 rows x 128 B | sx 128 f | sw 256 f
-// (int4 stages use the first 64 B of every row slot, i.e. a row stride of 64 B)
-constexpr int X_OFF = 0;
-constexpr int W_OFF = BM * 128;
-constexpr int SX_OFF = W_OFF + BN * 128;
-constexpr int SW_OFF = SX_OFF + BM * 4;
-constexpr int BYTES = SW_OFF + BN * 4;
+// int4 K block (one half of a double stage), bytes:
+//   X1 128 rows x 64 B, W1 256 rows x 64 B: 16-byte chunk c of row r at c ^ ((r >> 1) & 3)
+//   sx 128 floats (+ a dummy copy written by the waves that have no sx rows), sw 256 floats
+constexpr int X1_OFF = 0;
+constexpr int W1_OFF = TILE_M * 64;
+constexpr int SX_OFF = W1_OFF + TILE_N * 64;
+constexpr int SW_OFF = SX_OFF + 2 * TILE_M * 4;
+constexpr int HALF = SW_OFF + TILE_N * 4;
+// bf16 double stage (64 columns): X2 128 rows x 128 B, W2 256 rows x 128 B,
+// 16-byte chunk c of row r at c ^ (r & 7)
+constexpr int X2_OFF = 0;
+constexpr int W2_OFF = TILE_M * 128;
+// one double-stage buffer; it also holds a K group's partial tile at the end
+constexpr int BUF = 65536;
+static_assert(2 * HALF <= BUF && W2_OFF + TILE_N * 128 <= BUF, "stages fit the buffers");
 }  // namespace mixed
 
-struct MixedStaged {
-  uint4 x[4];
-  uint4 w[8];
-  float sx, sw;
+#if SG_DEVICE_PASS
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t mixed_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+typedef __attribute__((address_space(3))) void mixed_lds_void;
+
+// Per-lane source offsets, fixed for the whole K loop (the K block or the
+// column block enters through the scalar offset).  Every wave issues six
+// 1 KB loads per double stage (64 lanes x 16 B) and, for int4 stages, two
+// 256-byte scale loads.
+struct MixedPlan {
+  uint32_t io[3];       // int4: X1 slot, W1 slots (same for both halves)
+  uint32_t bo[6];       // bf16: X2 slots 0-1, W2 slots 2-5
+  uint32_t so[2], sdst[2];
+  int sk[2];            // 0: sx1, 1: sw1
 };
 
-__device__ __forceinline__ void mixed_load(const MixedArgs& a, int64_t n0, int64_t m0, int s, int KB1, int t,
-                                           MixedStaged& st) {
-  const uint4 zero = {0u, 0u, 0u, 0u};
-  if (s < KB1) {
-    // int4 block s: 64 B per row; X1 128 rows = 512 chunks, W1 256 rows = 1024 chunks
+__device__ __forceinline__ MixedPlan mixed_plan(const MixedArgs& a, int64_t n0, int64_t m0, int wave, int l) {
+  using namespace mixed;
+  MixedPlan p;
+  {   // int4: load jj = 0 fills X1 slot `wave`, jj = 1, 2 W1 slots 8 (jj - 1) + wave; 16 rows of 64 B per slot
+    const int r = 16 * wave + (l >> 2), c = (l & 3) ^ ((r >> 1) & 3);
+    p.io[0] = (uint32_t)(r * a.ldx1 + c * 16);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int i = t + 256 * j;
-      const int r = i >> 2, c = i & 3;
-      const int64_t m = m0 + r;
-      st.x[j] = m < a.M ? *reinterpret_cast<const uint4*>(a.x1 + m * a.ldx1 + (int64_t)s * 64 + c * 16) : zero;
+    for (int jj = 1; jj < 3; ++jj) {
+      const int rw = 16 * (8 * (jj - 1) + wave) + (l >> 2), cw = (l & 3) ^ ((rw >> 1) & 3);
+      p.io[jj] = (uint32_t)(rw * a.ldw1 + cw * 16);
     }
+  }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int i = t + 256 * j;
-      const int r = i >> 2, c = i & 3;
-      const int64_t n = n0 + r;
-      st.w[j] = n < a.N ? *reinterpret_cast<const uint4*>(a.w1 + n * a.ldw1 + (int64_t)s * 64 + c * 16) : zero;
-    }
-    const int64_t m = m0 + (t & 127), n = n0 + t;
-    st.sx = (t < 128 && m < a.M) ? a.sx1[m * a.sx1_sm + (int64_t)s * a.sx1_sk] : 0.f;
-    st.sw = n < a.N ? a.sw1[n * a.sw1_sn + (int64_t)s * a.sw1_sk] : 0.f;
-  } else {
-    // bf16 block b: 64 elements = 128 B per row, 16-byte chunks of 8 elements
-    const int64_t k0 = (int64_t)(s - KB1) * 64;
+  for (int j = 0; j < 6; ++j) {   // bf16: 8 rows of 128 B per slot
+    const int slot = j < 2 ? 8 * j + wave : 8 * (j - 2) + wave;
+    const int r = 8 * slot + (l >> 3), c = (l & 7) ^ (r & 7);
+    p.bo[j] = (uint32_t)(r * (j < 2 ? a.ldx2 : a.ldw2) * 2 + c * 16);
+  }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int i = t + 256 * j;
-      const int r = i >> 3, c = i & 7;
-      const int64_t m = m0 + r, k = k0 + c * 8;
-      st.x[j] = (m < a.M && k < a.K2) ? *reinterpret_cast<const uint4*>(a.x2 + m * a.ldx2 + k) : zero;
+  for (int j = 0; j < 2; ++j) {
+    const int sidx = 2 * wave + j, h = sidx >> 3, t = sidx & 7;
+    if (t < 2 || t >= 6) {
+      const int tp = t < 2 ? t : t - 6;
+      const int64_t m = min(m0 + tp * 64 + l, a.M - 1);
+      p.so[j] = (uint32_t)(m * a.sx1_sm * 4);
+      p.sdst[j] = h * HALF + SX_OFF + (t < 2 ? 0 : TILE_M * 4) + tp * 256;
+      p.sk[j] = 0;
+    } else {
+      const int64_t n = min(n0 + (t - 2) * 64 + l, a.N - 1);
+      p.so[j] = (uint32_t)(n * a.sw1_sn * 4);
+      p.sdst[j] = h * HALF + SW_OFF + (t - 2) * 256;
+      p.sk[j] = 1;
     }
+  }
+  return p;
+}
+
+struct MixedRes {
+  __amdgpu_buffer_rsrc_t x1, w1, x2, w2, sx, sw;
+};
+
+// int4 K blocks kb0, kb0 + 1 (the second clamped to the last block).
+__device__ __forceinline__ void mixed_issue_int4(uint8_t* st, const MixedPlan& p, const MixedRes& r,
+                                                 const MixedArgs& a, int kb0, int KB1, int wave) {
+  using namespace mixed;
+  const int kbh[2] = {kb0, min(kb0 + 1, KB1 - 1)};
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int i = t + 256 * j;
-      const int r = i >> 3, c = i & 7;
-      const int64_t n = n0 + r, k = k0 + c * 8;
-      st.w[j] = (n < a.N && k < a.K2) ? *reinterpret_cast<const uint4*>(a.w2 + n * a.ldw2 + k) : zero;
-    }
+  for (int h = 0; h < 2; ++h) {
+    uint8_t* hs = st + h * HALF;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r.x1, (mixed_lds_void*)(hs + X1_OFF + wave * 1024), 16, p.io[0],
+                                             kbh[h] * 64, 0, 0);
+#pragma unroll
+    for (int jj = 1; jj < 3; ++jj)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r.w1, (mixed_lds_void*)(hs + W1_OFF + (8 * (jj - 1) + wave) * 1024),
+                                               16, p.io[jj], kbh[h] * 64, 0, 0);
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int h = (2 * wave + j) >> 3;
+    if (p.sk[j] == 0)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r.sx, (mixed_lds_void*)(st + p.sdst[j]), 4, p.so[j],
+                                               (int)(kbh[h] * a.sx1_sk * 4), 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r.sw, (mixed_lds_void*)(st + p.sdst[j]), 4, p.so[j],
+                                               (int)(kbh[h] * a.sw1_sk * 4), 0, 0);
   }
 }
 
-__device__ __forceinline__ void mixed_store(uint8_t* sm, int s, int KB1, int t, const MixedStaged& st) {
+// bf16 columns 64 b .. 64 b + 63 (columns past K2 are loaded but not used).
+__device__ __forceinline__ void mixed_issue_bf16(uint8_t* st, const MixedPlan& p, const MixedRes& r, int b,
+                                                 int wave) {
   using namespace mixed;
-  if (s < KB1) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int i = t + 256 * j;
-      const int r = i >> 2, c = i & 3;
-      *reinterpret_cast<uint4*>(sm + X_OFF + r * 64 + ((c ^ ((r >> 1) & 3)) << 4)) = st.x[j];
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int i = t + 256 * j;
-      const int r = i >> 2, c = i & 3;
-      *reinterpret_cast<uint4*>(sm + W_OFF + r * 64 + ((c ^ ((r >> 1) & 3)) << 4)) = st.w[j];
-    }
-    if (t < 128) reinterpret_cast<float*>(sm + SX_OFF)[t] = st.sx;
-    reinterpret_cast<float*>(sm + SW_OFF)[t] = st.sw;
-  } else {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int i = t + 256 * j;
-      const int r = i >> 3, c = i & 7;
-      *reinterpret_cast<uint4*>(sm + X_OFF + r * 128 + ((c ^ (r & 7)) << 4)) = st.x[j];
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int i = t + 256 * j;
-      const int r = i >> 3, c = i & 7;
-      *reinterpret_cast<uint4*>(sm + W_OFF + r * 128 + ((c ^ (r & 7)) << 4)) = st.w[j];
-    }
+  for (int j = 0; j < 6; ++j) {
+    const int slot = j < 2 ? 8 * j + wave : 8 * (j - 2) + wave;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(j < 2 ? r.x2 : r.w2,
+                                             (mixed_lds_void*)(st + (j < 2 ? X2_OFF : W2_OFF) + slot * 1024), 16,
+                                             p.bo[j], b * 128, 0, 0);
   }
 }
+#endif  // SG_DEVICE_PASS
 
 // Low / high nibbles of 16 packed bytes as two int8 operand vectors (x16).
 __device__ __forceinline__ void unpack_int4(const uint4 p, v4i& lo, v4i& hi) {
@@ -144,32 +175,127 @@ __device__ __forceinline__ void unpack_int4(const uint4 p, v4i& lo, v4i& hi) {
              (int)(p.w & 0xf0f0f0f0u)};
 }
 
-__device__ __forceinline__ v8bf as_bf(uint4 u) {
-  return __builtin_bit_cast(v8bf, u);
+__device__ __forceinline__ v8bf as_bf(uint4 u) { return __builtin_bit_cast(v8bf, u); }
+
+template <typename T>
+__device__ __forceinline__ T mx_ld(const uint8_t* st, uint32_t off) {
+  return *reinterpret_cast<const T*>(st + off);
 }
 
-template <bool OUT_T>
-__global__ void __launch_bounds__(256, 1) k_mixed(MixedArgs a, int tiles_m, int tiles_n) {
+// Lane-constant LDS offsets (the swizzles depend on the row modulo 16 only,
+// and every sub-tile starts at a multiple of 16 rows).
+struct MixedLane {
+  uint32_t x1, w1, sx, sw;   // int4 half: X1 row wm*64 + lr chunk g, W1 row wn*128 + lr chunk g, scales
+  uint32_t x2, w2;           // bf16: chunk 4 q + g of X2 row wm*64 + lr / W2 row wn*128 + lr
+};
+
+__device__ __forceinline__ MixedLane mixed_lane(int wn, int wm, int g, int lr, int q) {
   using namespace mixed;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * BYTES];
+  MixedLane o;
+  const int xr = wm * 64 + lr, wr = wn * 128 + lr;
+  o.x1 = X1_OFF + xr * 64 + ((g ^ ((lr >> 1) & 3)) << 4);
+  o.w1 = W1_OFF + wr * 64 + ((g ^ ((lr >> 1) & 3)) << 4);
+  o.sx = SX_OFF + xr * 4;
+  o.sw = SW_OFF + (wn * 128 + 4 * g) * 4;
+  o.x2 = X2_OFF + xr * 128 + (((4 * q + g) ^ (lr & 7)) << 4);
+  o.w2 = W2_OFF + wr * 128 + (((4 * q + g) ^ (lr & 7)) << 4);
+  return o;
+}
 
-  const int T = tiles_m * tiles_n;
-  int b = blockIdx.x;
-  if ((T & 7) == 0) b = (b & 7) * (T >> 3) + (b >> 3);
-  const int G = 4;
-  const int group = b / (G * tiles_m);
-  const int first_n = group * G;
-  const int gsize = min(tiles_n - first_n, G);
-  const int in_g = b - group * G * tiles_m;
-  const int tn = first_n + in_g % gsize;
-  const int tm = in_g / gsize;
-  const int64_t n0 = (int64_t)tn * BN, m0 = (int64_t)tm * BM;
+__device__ __forceinline__ void promote(v4f& acc, const v4i& p, const float4& sw4, float sx) {
+  acc[0] = fmaf((float)p[0], sw4.x * sx, acc[0]);
+  acc[1] = fmaf((float)p[1], sw4.y * sx, acc[1]);
+  acc[2] = fmaf((float)p[2], sw4.z * sx, acc[2]);
+  acc[3] = fmaf((float)p[3], sw4.w * sx, acc[3]);
+}
 
-  const int t = threadIdx.x, l = t & 63, wave = t >> 6;
-  const int wn = wave & 1, wm = wave >> 1;
+// One int4 K block: two i8 MFMAs per sub-tile give 256 * sum x1 w1 exactly;
+// the partial is promoted with the block's scales.  Sub-tile row i is
+// promoted after the MFMAs of row i + 1 are issued, and the scheduling
+// barrier keeps that order (left alone, the compiler issues all 64 MFMAs
+// first and needs 128 registers for their results).
+__device__ __forceinline__ void mixed_int4_block(const uint8_t* st, v4f (&acc)[8][4], const MixedLane& o) {
+  float sxj[4];
+  v4i blo[4], bhi[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    sxj[j] = mx_ld<float>(st, o.sx + j * 64) * 0.00390625f;   // 2^-8 undoes the x16 of both operands
+    unpack_int4(mx_ld<uint4>(st, o.x1 + j * 1024), blo[j], bhi[j]);
+  }
+  uint4 anext = mx_ld<uint4>(st, o.w1);
+  float4 swnext = mx_ld<float4>(st, o.sw);
+  v4i pr[2][4];      // MFMA results of rows i (pr[i & 1]) and i - 1
+  float4 swr[2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint4 araw = anext;
+    const float4 sw4 = swnext;
+    if (i + 1 < 8) {
+      anext = mx_ld<uint4>(st, o.w1 + (i + 1) * 1024);
+      swnext = mx_ld<float4>(st, o.sw + (i + 1) * 64);
+    }
+    v4i alo, ahi;
+    unpack_int4(araw, alo, ahi);
+    swr[i & 1] = sw4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const v4i z = {0, 0, 0, 0};
+      pr[i & 1][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(alo, blo[j], z, 0, 0, 0);
+      pr[i & 1][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ahi, bhi[j], pr[i & 1][j], 0, 0, 0);
+    }
+    if (i > 0) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) promote(acc[i - 1][j], pr[(i - 1) & 1][j], swr[(i - 1) & 1], sxj[j]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) promote(acc[7][j], pr[1][j], swr[1], sxj[j]);
+}
+
+// 32 bf16 columns (lane group g holds 8 of them, the same ones for A and B).
+__device__ __forceinline__ void mixed_bf16_block(const uint8_t* st, v4f (&acc)[8][4], const MixedLane& o) {
+  uint4 bx[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) bx[j] = mx_ld<uint4>(st, o.x2 + j * 2048);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint4 av = mx_ld<uint4>(st, o.w2 + i * 2048);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(av), as_bf(bx[j]), acc[i][j], 0, 0, 0);
+  }
+}
+
+__global__ void __launch_bounds__(512) k_mixed(MixedArgs a, int tiles_m, int tiles_n) {
+#if SG_DEVICE_PASS
+  using namespace mixed;
+  __shared__ __attribute__((aligned(1024))) uint8_t db0[BUF];
+  __shared__ __attribute__((aligned(1024))) uint8_t db1[BUF];
+
+  int tn, tm;
+  tile_coords(tiles_m, tiles_n, tn, tm);
+  const int64_t n0 = (int64_t)tn * TILE_N, m0 = (int64_t)tm * TILE_M;
+
+  const int t = threadIdx.x, l = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int q = wave >> 2, w4 = wave & 3;
+  const int wn = w4 & 1, wm = w4 >> 1;
   const int g = l >> 4, lr = l & 15;
   const int KB1 = (int)(a.K1 >> 7);
-  const int NS = KB1 + (int)((a.K2 + 63) >> 6);
+  const int NIT1 = (KB1 + 1) >> 1;
+  const int NIT2 = (int)((a.K2 + 63) >> 6);
+
+  const int64_t mrows = min((int64_t)TILE_M, a.M - m0), nrows = min((int64_t)TILE_N, a.N - n0);
+  MixedRes rs;
+  rs.x1 = mixed_rsrc(a.x1 + m0 * a.ldx1, (uint32_t)(mrows * a.ldx1));
+  rs.w1 = mixed_rsrc(a.w1 + n0 * a.ldw1, (uint32_t)(nrows * a.ldw1));
+  rs.x2 = mixed_rsrc(a.K2 ? a.x2 + m0 * a.ldx2 : a.x2, a.K2 ? (uint32_t)(mrows * a.ldx2 * 2) : 0u);
+  rs.w2 = mixed_rsrc(a.K2 ? a.w2 + n0 * a.ldw2 : a.w2, a.K2 ? (uint32_t)(nrows * a.ldw2 * 2) : 0u);
+  rs.sx = mixed_rsrc(a.sx1, 0xffffffffu);
+  rs.sw = mixed_rsrc(a.sw1, 0xffffffffu);
+  const MixedPlan plan = mixed_plan(a, n0, m0, wave, l);
+  const MixedLane lo = mixed_lane(wn, wm, g, lr, q);
 
   v4f acc[8][4];
 #pragma unroll
@@ -177,79 +303,43 @@ __global__ void __launch_bounds__(256, 1) k_mixed(MixedArgs a, int tiles_m, int 
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-  MixedStaged stg;
-  mixed_load(a, n0, m0, 0, KB1, t, stg);
-  mixed_store(smem, 0, KB1, t, stg);
-  __syncthreads();
-
-  for (int s = 0; s < NS; ++s) {
-    const uint8_t* st = smem + (s & 1) * BYTES;
-    if (s + 1 < NS) mixed_load(a, n0, m0, s + 1, KB1, t, stg);
-
-    if (s < KB1) {
-      const float* sxs = reinterpret_cast<const float*>(st + SX_OFF);
-      const float* sws = reinterpret_cast<const float*>(st + SW_OFF);
-      float sxj[4];
-      v4i blo[4], bhi[4];
+  // int4 double stages it = 0 .. NIT1 - 1 (K blocks 2 it, 2 it + 1) in db0,
+  // db1, db0, ...; the last one's successor is the first bf16 stage.
+  mixed_issue_int4(db0, plan, rs, a, 0, KB1, wave);
+  for (int it0 = 0; it0 < NIT1; it0 += 2) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = wm * 64 + j * 16 + lr;
-        sxj[j] = sxs[r] * 0.00390625f;  // 2^-8 undoes the x16 of both unpacked operands
-        const uint4 p = *reinterpret_cast<const uint4*>(st + X_OFF + r * 64 + ((g ^ ((r >> 1) & 3)) << 4));
-        unpack_int4(p, blo[j], bhi[j]);
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int r = wn * 128 + i * 16 + lr;
-        const uint4 p = *reinterpret_cast<const uint4*>(st + W_OFF + r * 64 + ((g ^ ((r >> 1) & 3)) << 4));
-        v4i alo, ahi;
-        unpack_int4(p, alo, ahi);
-        const float4 sw4 = *reinterpret_cast<const float4*>(sws + wn * 128 + i * 16 + 4 * g);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const v4i z = {0, 0, 0, 0};
-          v4i pi = __builtin_amdgcn_mfma_i32_16x16x64_i8(alo, blo[j], z, 0, 0, 0);
-          pi = __builtin_amdgcn_mfma_i32_16x16x64_i8(ahi, bhi[j], pi, 0, 0, 0);
-          acc[i][j][0] = fmaf((float)pi[0], sw4.x * sxj[j], acc[i][j][0]);
-          acc[i][j][1] = fmaf((float)pi[1], sw4.y * sxj[j], acc[i][j][1]);
-          acc[i][j][2] = fmaf((float)pi[2], sw4.z * sxj[j], acc[i][j][2]);
-          acc[i][j][3] = fmaf((float)pi[3], sw4.w * sxj[j], acc[i][j][3]);
-        }
-      }
-    } else {
-      // bf16 block: lane group g holds 16 elements (32 B); the first 8 feed one
-      // MFMA and the next 8 the other, identically for both operands.
-      uint4 bx[4][2];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = wm * 64 + j * 16 + lr;
-        const uint8_t* row = st + X_OFF + r * 128;
-        bx[j][0] = *reinterpret_cast<const uint4*>(row + (((2 * g) ^ (r & 7)) << 4));
-        bx[j][1] = *reinterpret_cast<const uint4*>(row + (((2 * g + 1) ^ (r & 7)) << 4));
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int r = wn * 128 + i * 16 + lr;
-        const uint8_t* row = st + W_OFF + r * 128;
-        const uint4 a0 = *reinterpret_cast<const uint4*>(row + (((2 * g) ^ (r & 7)) << 4));
-        const uint4 a1 = *reinterpret_cast<const uint4*>(row + (((2 * g + 1) ^ (r & 7)) << 4));
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(a0), as_bf(bx[j][0]), acc[i][j], 0, 0, 0);
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(a1), as_bf(bx[j][1]), acc[i][j], 0, 0, 0);
-        }
+    for (int u = 0; u < 2; ++u) {
+      const int it = it0 + u;
+      if (it < NIT1) {
+        wait_vmcnt<0>();
+        __syncthreads();
+        if (it + 1 < NIT1) mixed_issue_int4(u == 0 ? db1 : db0, plan, rs, a, 2 * (it + 1), KB1, wave);
+        else if (NIT2 > 0) mixed_issue_bf16(u == 0 ? db1 : db0, plan, rs, 0, wave);
+        if (2 * it + q < KB1) mixed_int4_block((u == 0 ? db0 : db1) + q * HALF, acc, lo);
       }
     }
-
-    if (s + 1 < NS) mixed_store(smem + ((s + 1) & 1) * BYTES, s + 1, KB1, t, stg);
+  }
+  // bf16 stages b = 0 .. NIT2 - 1 continue the alternation (stage NIT1 + b).
+  for (int b = 0; b < NIT2; ++b) {
+    uint8_t* const cur = ((NIT1 + b) & 1) ? db1 : db0;
+    uint8_t* const nxt = ((NIT1 + b) & 1) ? db0 : db1;
+    wait_vmcnt<0>();
     __syncthreads();
+    if (b + 1 < NIT2) mixed_issue_bf16(nxt, plan, rs, b + 1, wave);
+    if ((int64_t)b * 64 + 32 * q < a.K2) mixed_bf16_block(cur, acc, lo);
   }
 
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      store_quad<true, OUT_T>(a, m0 + wm * 64 + j * 16 + lr, n0 + wn * 128 + i * 16 + 4 * g, acc[i][j]);
+  // Add the two groups' partial tiles (group 0 finishes sub-tile rows i < 4,
+  // group 1 rows i >= 4) and store the staged tile.
+  __syncthreads();
+  if (q == 0) xchg_out<4>(reinterpret_cast<float4*>(db0), acc, w4, l);
+  else xchg_out<0>(reinterpret_cast<float4*>(db1), acc, w4, l);
+  __syncthreads();
+  if (q == 0) x2_finish<0, true, false, BUF>(db1, db0, db1, acc, w4, l, wn, wm, g, lr);
+  else x2_finish<1, true, false, BUF>(db0, db0, db1, acc, w4, l, wn, wm, g, lr);
+  __syncthreads();
+  store_staged<true, false, BUF>(a, db0, db1, m0, n0, t);
+#endif  // SG_DEVICE_PASS
 }
 
 }  // namespace sg
@@ -267,6 +357,11 @@ extern "C" sg_status sg_mixed_gemm_add(int64_t M, int64_t N, int64_t K1, int64_t
   if (ldx1 < K1 / 2 || ldw1 < K1 / 2 || ldy < N) return SG_ERR_SHAPE;
   if (K2 > 0 && (ldx2 < K2 || ldw2 < K2)) return SG_ERR_SHAPE;
   if (cdiv(M, 128) * cdiv(N, 256) > 0x7fffffffLL) return SG_ERR_SHAPE;
+  // Tiles and scales are addressed with 32-bit buffer offsets.
+  if (ldx1 >= (1LL << 23) || ldw1 >= (1LL << 23) || ldx2 >= (1LL << 22) || ldw2 >= (1LL << 22)) return SG_ERR_SHAPE;
+  if (sx1_sm < 0 || sx1_sk < 0 || sw1_sn < 0 || sw1_sk < 0) return SG_ERR_SHAPE;
+  if (((M - 1) * sx1_sm + (K1 / 128 - 1) * sx1_sk) * 4 >= (1LL << 31)) return SG_ERR_SHAPE;
+  if (((N - 1) * sw1_sn + (K1 / 128 - 1) * sw1_sk) * 4 >= (1LL << 31)) return SG_ERR_SHAPE;
   if (!aligned(x1, 16) || !aligned(w1, 16) || ldx1 % 16 || ldw1 % 16 || !aligned(sx1, 4) ||
       !aligned(sw1, 4) || !aligned(y, 2))
     return SG_ERR_ALIGN;
@@ -278,9 +373,9 @@ extern "C" sg_status sg_mixed_gemm_add(int64_t M, int64_t N, int64_t K1, int64_t
   a.w1 = w1; a.ldw1 = ldw1; a.sw1 = sw1; a.sw1_sn = sw1_sn; a.sw1_sk = sw1_sk;
   a.x2 = x2; a.ldx2 = ldx2; a.w2 = w2; a.ldw2 = ldw2;
   a.y = y; a.ldy = ldy;
-  a.vec_store = (ldy % 4 == 0) && aligned(y, 8);
-  const int tm = (int)cdiv(M, mixed::BM), tn = (int)cdiv(N, mixed::BN);
+  a.vec16 = (ldy % 8 == 0) && aligned(y, 16);
+  const int tm = (int)cdiv(M, TILE_M), tn = (int)cdiv(N, TILE_N);
   clear_hip_error();
-  k_mixed<false><<<tm * tn, 256, 0, stream>>>(a, tm, tn);
+  k_mixed<<<tm * tn, 512, 0, stream>>>(a, tm, tn);
   return launch_status();
 }
