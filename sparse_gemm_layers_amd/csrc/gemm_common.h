@@ -7,6 +7,19 @@
 
 namespace sg {
 
+// LDS swizzles of operand rows: the 16-byte chunk c of row r is stored at
+// chunk position c ^ swz(r).  Operand fragments are 16 rows read with
+// ds_read_b128 (lane l reads row l % 16).  The functions below were chosen
+// with gfx950's LDS bank-conflict counter: each makes its read pattern
+// conflict-free, where the textbook c ^ (r & 7) on 128-byte rows costs four
+// extra LDS cycles per read.  They depend on r mod 16 only.
+//   swz8  - 128-byte rows, lane group g reads chunks 2 g and 2 g + 1 (fp8 operands)
+//   swz8q - 128-byte rows, lane group g reads chunk 4 q + g (bf16 operands)
+//   swz4  - 64-byte rows, lane group g reads chunk g
+__device__ __host__ __forceinline__ int swz8(int r) { return (r & 6) ^ ((r >> 3) & 1); }
+__device__ __host__ __forceinline__ int swz8q(int r) { return r & 6; }
+__device__ __host__ __forceinline__ int swz4(int r) { return (r >> 1) & 3; }
+
 // SMFMAC (v_smfmac_f32_16x16x128_fp8_fp8) A-operand layout: lane group g
 // (lanes 16 g .. 16 g + 15) takes, from a row's 64 compressed bytes of a
 // 128-wide K block, bytes [b, b + 8) and [b + 16, b + 24) with
@@ -31,7 +44,7 @@ __device__ __forceinline__ int sp_a_off(int g) { return 32 * (g & 1) + 8 * (g >>
 // tile uses the same swizzle with the tile row r (it depends on r mod 16
 // only): values at pk_val_off(r, g), index words at LDS_META + pk_meta_word(r, g).
 constexpr int PK_ROWS = 16, PK_CHUNK = 1280, PK_META = 1024, LDS_META = 16384;
-__device__ __host__ __forceinline__ int pk_val_off(int r, int g) { return r * 64 + 16 * (g ^ ((r >> 1) & 3)); }
+__device__ __host__ __forceinline__ int pk_val_off(int r, int g) { return r * 64 + 16 * (g ^ swz4(r)); }
 __device__ __host__ __forceinline__ int pk_meta_word(int r, int g) { return r * 16 + 4 * ((g + 2 * ((r >> 3) & 1)) & 3); }
 
 // s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding:

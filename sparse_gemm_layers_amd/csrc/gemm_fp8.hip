@@ -67,19 +67,16 @@ __device__ __forceinline__ v4f mma_sparse(const v4i& a, const v8i& b, int idx) {
 }
 
 
-// ============================================================ large-M kernel
-// Workgroup tile: 256 W rows (n) x 128 X rows (m), 4 waves in a 2 x 2 grid,
-// each wave 128 n x 64 m = 8 x 4 sub-tiles of 16 x 16.  One 128-wide K block
-// per pipeline stage.  Operands travel HBM -> LDS with buffer loads that
-// write LDS directly (no staging registers); NST stages are in flight, and a
-// wave waits only for the stage it is about to multiply.  Buffer resources
-// are based at the tile's first row and sized to the rows that exist, so rows
-// past M or N read as zero (the partial tiles) without any branch.
-//
-// LDS stage layout (bytes):
-//   X    : 128 rows x 128 B; 16-byte chunk c of row r stored at chunk c ^ (r & 7)
+// ================================================= large-M stage layout
+// Workgroup tile: 256 W rows (n) x 128 X rows (m).  Operands travel HBM -> LDS
+// with buffer loads that write LDS directly (no staging registers); buffer
+// resources are based at the tile's first row and sized to the rows that
+// exist, so rows past M or N read as zero (the partial tiles) without any
+// branch.  One stage holds one 128-wide K block:
+//   X    : 128 rows x 128 B; 16-byte chunk c of row r stored at chunk c ^ swz8(r)
 //   W    : dense 256 rows x 128 B (same swizzle as X), or
 //          sparse 256 rows x 64 B of values; chunk c of row r at c ^ ((r >> 1) & 3)
+//          (the packed form holds 16-row chunks of the packed layout instead)
 //   meta : sparse only, 256 rows x 16 B, unswizzled
 //   sx   : 128 floats, scale of X row r for the stage's K block (+ a copy slot)
 //   sw   : 256 floats, scale of W row r
@@ -90,7 +87,6 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 template <bool SPARSE>
 struct Stage {
-  static constexpr int NST = SPARSE ? 4 : 3;                   // pipeline depth
   static constexpr int X_OFF = 0;
   static constexpr int W_OFF = BM * 128;
   static constexpr int W_BYTES = SPARSE ? BN * 64 : BN * 128;
@@ -99,8 +95,6 @@ struct Stage {
   static constexpr int SX_OFF = M_OFF + M_BYTES;               // 2 x 128 floats (second is a dummy copy)
   static constexpr int SW_OFF = SX_OFF + 2 * BM * 4;
   static constexpr int BYTES = SW_OFF + BN * 4;
-  // buffer-load instructions per wave per stage (identical for every wave)
-  static constexpr int LOADS = 4 + (SPARSE ? 4 + 1 : 8) + 2;
 };
 
 #if SG_DEVICE_PASS
@@ -108,125 +102,39 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t b
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, (int)RSRC_WORD3);
 }
 
-// Per-thread source offsets, fixed for the whole K loop (the K block enters
-// through the scalar offset).
-template <bool SPARSE>
-struct LoadPlan {
-  uint32_t xo[4], wo[SPARSE ? 4 : 8], mo, sxo, swo;
-};
-
-template <bool SPARSE>
-__device__ __forceinline__ LoadPlan<SPARSE> make_plan(const GemmArgs& a, int64_t n0, int64_t m0, int wave, int l) {
-  LoadPlan<SPARSE> p;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {              // X: wave-load q = 4 j + wave covers 16-byte slots 64 q .. 64 q + 63
-    const int s = (4 * j + wave) * 64 + l;
-    const int r = s >> 3, c = (s & 7) ^ (r & 7);
-    p.xo[j] = (uint32_t)(r * a.ldx + c * 16);
-  }
-  if (SPARSE) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int s = (4 * j + wave) * 64 + l;
-      const int r = s >> 2, c = (s & 3) ^ ((r >> 1) & 3);
-      p.wo[j] = (uint32_t)(r * a.ldw + c * 16);
-    }
-    p.mo = (uint32_t)((wave * 64 + l) * a.ldm);
-  } else {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int s = (4 * j + wave) * 64 + l;
-      const int r = s >> 3, c = (s & 7) ^ (r & 7);
-      p.wo[j] = (uint32_t)(r * a.ldw + c * 16);
-    }
-    p.mo = 0;
-  }
-  // scales: rows past M / N are clamped to the last row (their results are never stored)
-  const int64_t m = min(m0 + (int64_t)(wave & 1) * 64 + l, a.M - 1);
-  const int64_t n = min(n0 + (int64_t)wave * 64 + l, a.N - 1);
-  p.sxo = (uint32_t)(((m >> a.gm_shift) * a.sx_sm) * 4);
-  p.swo = (uint32_t)(((n >> a.gn_shift) * a.sw_sn) * 4);
-  return p;
-}
-
-template <bool SPARSE>
-__device__ __forceinline__ void issue_stage(uint8_t* st, const LoadPlan<SPARSE>& p, __amdgpu_buffer_rsrc_t rx,
-                                            __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t rm,
-                                            __amdgpu_buffer_rsrc_t rsx, __amdgpu_buffer_rsrc_t rsw,
-                                            const GemmArgs& a, int kb, int wave) {
-  using L = Stage<SPARSE>;
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(st + L::X_OFF + (4 * j + wave) * 1024), 16, p.xo[j],
-                                             kb * 128, 0, 0);
-  if (SPARSE) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(st + L::W_OFF + (4 * j + wave) * 1024), 16, p.wo[j],
-                                               kb * 64, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rm, (lds_void*)(st + L::M_OFF + wave * 1024), 16, p.mo, kb * 16, 0, 0);
-  } else {
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(st + L::W_OFF + (4 * j + wave) * 1024), 16, p.wo[j],
-                                               kb * 128, 0, 0);
-  }
-  // waves 0,1 fill sx[0..127]; waves 2,3 load the same values into the dummy copy
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsx, (lds_void*)(st + L::SX_OFF + wave * 256), 4, p.sxo,
-                                           (int)(kb * a.sx_sk * 4), 0, 0);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, (lds_void*)(st + L::SW_OFF + wave * 256), 4, p.swo,
-                                           (int)(kb * a.sw_sk * 4), 0, 0);
-}
-
 #endif  // SG_DEVICE_PASS
 
-template <bool SPARSE>
-__device__ __forceinline__ void wait_stage(int later_stages) {
-  constexpr int L = Stage<SPARSE>::LOADS;
-  if (later_stages >= 2) wait_vmcnt<2 * L>();
-  else if (later_stages == 1) wait_vmcnt<L>();
-  else wait_vmcnt<0>();
-}
-
-// Lane-constant LDS byte offsets of the wave's operands within a stage.  The
-// swizzles only depend on the row modulo 8 (X, dense W) or on (row >> 1) & 3
-// (sparse W), and every sub-tile starts at a multiple of 16 rows, so each
-// lane's swizzled offset is fixed; sub-tiles are reached by immediate offsets.
-template <bool SPARSE>
+// Lane-constant LDS byte offsets of the wave's operands within a sparse
+// stage.  The swizzles only depend on the row modulo 16, and every sub-tile
+// starts at a multiple of 16 rows, so each lane's swizzled offset is fixed;
+// sub-tiles are reached by immediate offsets.
 struct LaneOffsets {
   uint32_t x0, x1;   // X row wm*64 + lr: the two 16-byte chunks of lane group g
-  uint32_t w0, w1;   // W row wn*128 + lr: dense 16-byte chunks / sparse 8-byte halves
+  uint32_t w0, w1;   // W row wn*128 + lr: the two 8-byte halves of the A operand
   uint32_t mt;       // metadata word pair of lane group g
   uint32_t sx;       // X scale of row wm*64 + lr
 };
 
-template <bool SPARSE>
-__device__ __forceinline__ LaneOffsets<SPARSE> lane_offsets(int wn, int wm, int g, int lr) {
-  using L = Stage<SPARSE>;
-  LaneOffsets<SPARSE> o;
+__device__ __forceinline__ LaneOffsets lane_offsets(int wn, int wm, int g, int lr) {
+  using L = Stage<true>;
+  LaneOffsets o;
   const int xr = wm * 64 + lr, wr = wn * 128 + lr;
-  o.x0 = L::X_OFF + xr * 128 + (((2 * g) ^ (lr & 7)) << 4);
-  o.x1 = L::X_OFF + xr * 128 + (((2 * g + 1) ^ (lr & 7)) << 4);
-  if (SPARSE) {
-    const int sw = (lr >> 1) & 3;
-    const int a0 = sp_a_off(g), a1 = a0 + 16;
-    o.w0 = L::W_OFF + wr * 64 + ((((a0 >> 4) ^ sw) << 4) | (a0 & 15));
-    o.w1 = L::W_OFF + wr * 64 + ((((a1 >> 4) ^ sw) << 4) | (a1 & 15));
-    o.mt = L::M_OFF + wr * 16 + 8 * (g & 1);
-  } else {
-    o.w0 = L::W_OFF + wr * 128 + (((2 * g) ^ (lr & 7)) << 4);
-    o.w1 = L::W_OFF + wr * 128 + (((2 * g + 1) ^ (lr & 7)) << 4);
-    o.mt = 0;
-  }
+  o.x0 = L::X_OFF + xr * 128 + (((2 * g) ^ swz8(lr)) << 4);
+  o.x1 = L::X_OFF + xr * 128 + (((2 * g + 1) ^ swz8(lr)) << 4);
+  const int sw = (lr >> 1) & 3;
+  const int a0 = sp_a_off(g), a1 = a0 + 16;
+  o.w0 = L::W_OFF + wr * 64 + ((((a0 >> 4) ^ sw) << 4) | (a0 & 15));
+  o.w1 = L::W_OFF + wr * 64 + ((((a1 >> 4) ^ sw) << 4) | (a1 & 15));
+  o.mt = L::M_OFF + wr * 16 + 8 * (g & 1);
   o.sx = L::SX_OFF + xr * 4;
   return o;
 }
 
 // Packed weights: the stage's W area holds the packed block verbatim, so a
 // lane's A operand is one 16-byte read and its index one 4-byte read.
-__device__ __forceinline__ LaneOffsets<true> lane_offsets_packed(int wn, int wm, int g, int lr) {
+__device__ __forceinline__ LaneOffsets lane_offsets_packed(int wn, int wm, int g, int lr) {
   using L = Stage<true>;
-  LaneOffsets<true> o = lane_offsets<true>(wn, wm, g, lr);
+  LaneOffsets o = lane_offsets(wn, wm, g, lr);
   o.w0 = L::W_OFF + pk_val_off(wn * 128 + lr, g);
   o.w1 = 0;
   o.mt = L::W_OFF + LDS_META + pk_meta_word(wn * 128 + lr, g);
@@ -238,11 +146,11 @@ __device__ __forceinline__ T lds_ld(const uint8_t* st, uint32_t off) {
   return *reinterpret_cast<const T*>(st + off);
 }
 
-// Multiplies one LDS stage into the wave's 8 x 4 sub-tiles and promotes.
-template <bool SPARSE, int GRAN_N, bool PACKED = false>
-__device__ __forceinline__ void compute_stage(const uint8_t* st, v4f (&acc)[8][4], const LaneOffsets<SPARSE>& o,
+// Multiplies one sparse LDS stage into the wave's 8 x 4 sub-tiles and promotes.
+template <int GRAN_N, bool PACKED>
+__device__ __forceinline__ void compute_stage(const uint8_t* st, v4f (&acc)[8][4], const LaneOffsets& o,
                                               int wn, int g, uint32_t msel) {
-  using L = Stage<SPARSE>;
+  using L = Stage<true>;
   float sxj[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) sxj[j] = lds_ld<float>(st, o.sx + j * 64);
@@ -266,13 +174,13 @@ __device__ __forceinline__ void compute_stage(const uint8_t* st, v4f (&acc)[8][4
     float4 swr = make_float4(0.f, 0.f, 0.f, 0.f);
     if (GRAN_N == 1) swr = lds_ld<float4>(st, L::SW_OFF + (wn * 128 + i * 16 + 4 * g) * 4);
     v4f p[4];
-    if (SPARSE && PACKED) {
+    if (PACKED) {
       const uint4 av = lds_ld<uint4>(st, o.w0 + i * 1024);
       const int idx = lds_ld<int>(st, o.mt + i * 256);
       const v4i aa = {(int)av.x, (int)av.y, (int)av.z, (int)av.w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) p[j] = mma_sparse(aa, bx[j], idx);
-    } else if (SPARSE) {
+    } else {
       const uint2 v0 = lds_ld<uint2>(st, o.w0 + i * 1024);
       const uint2 v1 = lds_ld<uint2>(st, o.w1 + i * 1024);
       const uint2 mw = lds_ld<uint2>(st, o.mt + i * 256);
@@ -280,12 +188,6 @@ __device__ __forceinline__ void compute_stage(const uint8_t* st, v4f (&acc)[8][4
       const v4i aa = {(int)v0.x, (int)v0.y, (int)v1.x, (int)v1.y};
 #pragma unroll
       for (int j = 0; j < 4; ++j) p[j] = mma_sparse(aa, bx[j], idx);
-    } else {
-      const uint4 lo = lds_ld<uint4>(st, o.w0 + i * 2048);
-      const uint4 hi = lds_ld<uint4>(st, o.w1 + i * 2048);
-      const v8i aa = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) p[j] = mma_dense(aa, bx[j]);
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -301,76 +203,9 @@ __device__ __forceinline__ void compute_stage(const uint8_t* st, v4f (&acc)[8][4
   }
 }
 
-template <bool SPARSE, int GRAN_N, bool OUT_BF16, bool OUT_T>
-__global__ void __launch_bounds__(256, 1) k_gemm_large(GemmArgs a, int tiles_m, int tiles_n) {
-#if SG_DEVICE_PASS
-  using L = Stage<SPARSE>;
-  constexpr int NST = L::NST;
-  static_assert(NST >= 3 && NST <= 4, "wait_stage handles at most two later stages");
-  // One array per stage: LDS reads of one stage then provably do not alias the
-  // buffer loads in flight into the others, so no extra wait is inserted.
-  __shared__ __attribute__((aligned(1024))) uint8_t sm0[L::BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t sm1[L::BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t sm2[L::BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t sm3[NST > 3 ? L::BYTES : 16];
-  uint8_t* const buf[4] = {sm0, sm1, sm2, sm3};
-
-  int tn, tm;
-  tile_coords(tiles_m, tiles_n, tn, tm);
-  const int64_t n0 = (int64_t)tn * BN, m0 = (int64_t)tm * BM;
-
-  const int t = threadIdx.x, l = t & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int wn = wave & 1, wm = wave >> 1;
-  const int g = l >> 4, lr = l & 15;
-  const int KB = (int)(a.K >> 7);
-
-  const int64_t mrows = min((int64_t)BM, a.M - m0), nrows = min((int64_t)BN, a.N - n0);
-  const __amdgpu_buffer_rsrc_t rx = rsrc(a.x + m0 * a.ldx, (uint32_t)(mrows * a.ldx));
-  const __amdgpu_buffer_rsrc_t rw = rsrc(a.w + n0 * a.ldw, (uint32_t)(nrows * a.ldw));
-  const __amdgpu_buffer_rsrc_t rm = rsrc(SPARSE ? a.meta + n0 * a.ldm : a.w, SPARSE ? (uint32_t)(nrows * a.ldm) : 0u);
-  const __amdgpu_buffer_rsrc_t rsx = rsrc(a.sx, 0xffffffffu);
-  const __amdgpu_buffer_rsrc_t rsw = rsrc(a.sw, 0xffffffffu);
-  const LoadPlan<SPARSE> plan = make_plan<SPARSE>(a, n0, m0, wave, l);
-  const uint32_t msel = (g >> 1) ? 0x07060302u : 0x05040100u;   // metadata halves of this lane group
-  const LaneOffsets<SPARSE> lo = lane_offsets<SPARSE>(wn, wm, g, lr);
-
-  v4f acc[8][4];
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
-
-#pragma unroll
-  for (int s = 0; s < NST - 1; ++s)
-    if (s < KB) issue_stage<SPARSE>(buf[s], plan, rx, rw, rm, rsx, rsw, a, s, wave);
-
-  for (int kb0 = 0; kb0 < KB; kb0 += NST) {
-#pragma unroll
-    for (int u = 0; u < NST; ++u) {
-      const int kb = kb0 + u;
-      if (kb < KB) {
-        wait_stage<SPARSE>(min(NST - 2, KB - 1 - kb));
-        __syncthreads();
-        if (kb + NST - 1 < KB)
-          issue_stage<SPARSE>(buf[(u + NST - 1) % NST], plan, rx, rw, rm, rsx, rsw, a, kb + NST - 1, wave);
-        compute_stage<SPARSE, GRAN_N>(buf[u], acc, lo, wn, g, msel);
-      }
-    }
-  }
-
-  // Epilogue: lane holds D[n = n0 + wn*128 + 16 i + 4 g + e][m = m0 + wm*64 + 16 j + lr].
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      store_quad<OUT_BF16, OUT_T>(a, m0 + wm * 64 + j * 16 + lr, n0 + wn * 128 + i * 16 + 4 * g, acc[i][j]);
-#endif  // SG_DEVICE_PASS
-}
-
 // ================================================ sparse kernel, 2 waves / SIMD
-// Same 256 x 128 workgroup tile and the same per-wave 128 x 64 sub-tile as
-// k_gemm_large, but 8 waves: two K groups of 4 waves.  Group q multiplies the
+// 256 x 128 workgroup tile, 8 waves: two K groups of 4 waves in a 2 x 2 grid,
+// each wave 128 n x 64 m = 8 x 4 sub-tiles of 16 x 16.  Group q multiplies the
 // K blocks kb = 2 it + q, so two waves share every SIMD and one wave's LDS,
 // barrier and matrix-core latencies hide behind the other's work.  A "double
 // stage" holds K blocks 2 it and 2 it + 1 (two copies of the single-stage
@@ -410,7 +245,7 @@ __device__ __forceinline__ PlanX2 make_plan_x2(const GemmArgs& a, int64_t n0, in
     const int slot = (8 * j + wave) & 15;      // 1 KB slot within the K block's X / W area
     {
       const int s = slot * 64 + l;
-      const int r = s >> 3, c = (s & 7) ^ (r & 7);
+      const int r = s >> 3, c = (s & 7) ^ swz8(r);
       p.xo[j] = (uint32_t)(r * a.ldx + c * 16);
     }
     if (!PACKED) {
@@ -515,7 +350,7 @@ __global__ void __launch_bounds__(512) k_gemm_sparse_x2(GemmArgs a, int tiles_m,
   const __amdgpu_buffer_rsrc_t rsw = rsrc(a.sw, 0xffffffffu);
   const PlanX2 plan = make_plan_x2<PACKED>(a, n0, m0, wave, l);
   const uint32_t msel = (g >> 1) ? 0x07060302u : 0x05040100u;
-  const LaneOffsets<true> lo = PACKED ? lane_offsets_packed(wn, wm, g, lr) : lane_offsets<true>(wn, wm, g, lr);
+  const LaneOffsets lo = PACKED ? lane_offsets_packed(wn, wm, g, lr) : lane_offsets(wn, wm, g, lr);
   const uint32_t qoff = (uint32_t)q * x2::HALF;
 
   v4f acc[8][4];
@@ -535,7 +370,7 @@ __global__ void __launch_bounds__(512) k_gemm_sparse_x2(GemmArgs a, int tiles_m,
         if (it + 1 < NIT)
           issue_double<PACKED>(u == 0 ? db1 : db0, plan, rx, rw, rm, rsx, rsw, a, 2 * (it + 1), KB, wave);
         if (2 * it + q < KB)
-          compute_stage<true, GRAN_N, PACKED>((u == 0 ? db0 : db1) + qoff, acc, lo, wn, g, msel);
+          compute_stage<GRAN_N, PACKED>((u == 0 ? db0 : db1) + qoff, acc, lo, wn, g, msel);
       }
     }
   }
@@ -556,6 +391,211 @@ __global__ void __launch_bounds__(512) k_gemm_sparse_x2(GemmArgs a, int tiles_m,
     x2_finish<1, OUT_BF16, OUT_T, x2::DBL>(db0, db0, db1, acc, w4, l, wn, wm, g, lr);
   __syncthreads();
   store_staged<OUT_BF16, OUT_T, x2::DBL>(a, db0, db1, m0, n0, t);
+#endif  // SG_DEVICE_PASS
+}
+
+// ================================================= dense kernel, 2 waves / SIMD
+// Workgroup tile 256 W rows (n) x 128 X rows (m), 8 waves in a 4 (n) x 2 (m)
+// grid, each wave 64 n x 64 m = 4 x 4 sub-tiles of 16 x 16.  One 128-wide K
+// block per stage (the single-stage layout above), three stages in LDS: while
+// all waves multiply stage kb, stages kb + 1 and kb + 2 are in flight.  Every
+// wave issues the same number of loads per stage (two 1 KB X slots, four
+// 1 KB W slots, one 256-byte scale load), so a wave waits for a stage by
+// counting its own loads.  The finished tile is staged in LDS and stored in
+// whole rows.
+namespace d8 {
+constexpr int NST = 3;
+constexpr int LOADS = 7;                       // buffer loads per wave per stage
+constexpr int BYTES = Stage<false>::BYTES;
+}  // namespace d8
+
+#if SG_DEVICE_PASS
+struct PlanD8 {
+  uint32_t xo[2], wo[4], so, sdst;
+  int sk;   // 0: sx, 1: sw
+};
+
+__device__ __forceinline__ PlanD8 make_plan_d8(const GemmArgs& a, int64_t n0, int64_t m0, int wave, int l) {
+  using L = Stage<false>;
+  PlanD8 p;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {               // X slot 8 j + wave: rows 8 slot .. 8 slot + 7
+    const int s = (8 * j + wave) * 64 + l;
+    const int r = s >> 3, c = (s & 7) ^ swz8(r);
+    p.xo[j] = (uint32_t)(r * a.ldx + c * 16);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {               // W slot 8 j + wave
+    const int s = (8 * j + wave) * 64 + l;
+    const int r = s >> 3, c = (s & 7) ^ swz8(r);
+    p.wo[j] = (uint32_t)(r * a.ldw + c * 16);
+  }
+  // waves 0, 1: sx rows 64 w ..; waves 2 - 5: sw rows 64 (w - 2) ..; waves 6, 7
+  // load sx rows again into the dummy copy.  Rows past M / N are clamped.
+  if (wave < 2 || wave >= 6) {
+    const int tp = wave < 2 ? wave : wave - 6;
+    const int64_t m = min(m0 + tp * 64 + l, a.M - 1);
+    p.so = (uint32_t)(((m >> a.gm_shift) * a.sx_sm) * 4);
+    p.sdst = L::SX_OFF + (wave < 2 ? 0 : BM * 4) + tp * 256;
+    p.sk = 0;
+  } else {
+    const int64_t n = min(n0 + (wave - 2) * 64 + l, a.N - 1);
+    p.so = (uint32_t)(((n >> a.gn_shift) * a.sw_sn) * 4);
+    p.sdst = L::SW_OFF + (wave - 2) * 256;
+    p.sk = 1;
+  }
+  return p;
+}
+
+__device__ __forceinline__ void issue_d8(uint8_t* st, const PlanD8& p, __amdgpu_buffer_rsrc_t rx,
+                                         __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t rsx,
+                                         __amdgpu_buffer_rsrc_t rsw, const GemmArgs& a, int kb, int wave) {
+  using L = Stage<false>;
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(st + L::X_OFF + (8 * j + wave) * 1024), 16, p.xo[j],
+                                             kb * 128, 0, 0);
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(st + L::W_OFF + (8 * j + wave) * 1024), 16, p.wo[j],
+                                             kb * 128, 0, 0);
+  if (p.sk == 0)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsx, (lds_void*)(st + p.sdst), 4, p.so, (int)(kb * a.sx_sk * 4), 0, 0);
+  else
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, (lds_void*)(st + p.sdst), 4, p.so, (int)(kb * a.sw_sk * 4), 0, 0);
+}
+#endif  // SG_DEVICE_PASS
+
+// Lane-constant LDS offsets: X row wm*64 + lr and W row wn*64 + lr, the two
+// 16-byte chunks of lane group g (sub-tiles are 2 KB apart), the X scale of
+// the lane's row and the W scales of the wave's rows.
+struct LaneD8 {
+  uint32_t x0, x1, w0, w1, sx, sw;
+};
+
+__device__ __forceinline__ LaneD8 lane_d8(int wn, int wm, int g, int lr) {
+  using L = Stage<false>;
+  LaneD8 o;
+  const int xr = wm * 64 + lr, wr = wn * 64 + lr;
+  o.x0 = L::X_OFF + xr * 128 + (((2 * g) ^ swz8(lr)) << 4);
+  o.x1 = L::X_OFF + xr * 128 + (((2 * g + 1) ^ swz8(lr)) << 4);
+  o.w0 = L::W_OFF + wr * 128 + (((2 * g) ^ swz8(lr)) << 4);
+  o.w1 = L::W_OFF + wr * 128 + (((2 * g + 1) ^ swz8(lr)) << 4);
+  o.sx = L::SX_OFF + xr * 4;
+  o.sw = L::SW_OFF + (wn * 64 + 4 * g) * 4;
+  return o;
+}
+
+// Multiplies one stage into the wave's 4 x 4 sub-tiles and promotes.
+template <int GRAN_N>
+__device__ __forceinline__ void compute_d8(const uint8_t* st, v4f (&acc)[4][4], const LaneD8& o, int wn) {
+  using L = Stage<false>;
+  float sxj[4];
+  v8i bx[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    sxj[j] = lds_ld<float>(st, o.sx + j * 64);
+    const uint4 lo = lds_ld<uint4>(st, o.x0 + j * 2048);
+    const uint4 hi = lds_ld<uint4>(st, o.x1 + j * 2048);
+    bx[j] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  }
+  float s128[4];
+  if (GRAN_N == 128) {
+    const float swv = lds_ld<float>(st, L::SW_OFF + wn * 256);   // the wave's 64 rows share one W scale
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s128[j] = sxj[j] * swv;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 lo = lds_ld<uint4>(st, o.w0 + i * 2048);
+    const uint4 hi = lds_ld<uint4>(st, o.w1 + i * 2048);
+    const v8i aa = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    float4 swr = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (GRAN_N == 1) swr = lds_ld<float4>(st, o.sw + i * 64);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const v4f p = mma_dense(aa, bx[j]);
+      if (GRAN_N == 128) {
+        acc[i][j] += p * s128[j];
+      } else {
+        acc[i][j][0] = fmaf(p[0] * swr.x, sxj[j], acc[i][j][0]);
+        acc[i][j][1] = fmaf(p[1] * swr.y, sxj[j], acc[i][j][1]);
+        acc[i][j][2] = fmaf(p[2] * swr.z, sxj[j], acc[i][j][2]);
+        acc[i][j][3] = fmaf(p[3] * swr.w, sxj[j], acc[i][j][3]);
+      }
+    }
+  }
+}
+
+template <int GRAN_N, bool OUT_BF16, bool OUT_T>
+__global__ void __launch_bounds__(512) k_gemm_dense8(GemmArgs a, int tiles_m, int tiles_n) {
+#if SG_DEVICE_PASS
+  using namespace d8;
+  __shared__ __attribute__((aligned(1024))) uint8_t sm0[BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t sm1[BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t sm2[BYTES];
+  uint8_t* const buf[3] = {sm0, sm1, sm2};
+
+  int tn, tm;
+  tile_coords(tiles_m, tiles_n, tn, tm);
+  const int64_t n0 = (int64_t)tn * BN, m0 = (int64_t)tm * BM;
+
+  const int t = threadIdx.x, l = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wn = wave & 3, wm = wave >> 2;
+  const int g = l >> 4, lr = l & 15;
+  const int KB = (int)(a.K >> 7);
+
+  const int64_t mrows = min((int64_t)BM, a.M - m0), nrows = min((int64_t)BN, a.N - n0);
+  const __amdgpu_buffer_rsrc_t rx = rsrc(a.x + m0 * a.ldx, (uint32_t)(mrows * a.ldx));
+  const __amdgpu_buffer_rsrc_t rw = rsrc(a.w + n0 * a.ldw, (uint32_t)(nrows * a.ldw));
+  const __amdgpu_buffer_rsrc_t rsx = rsrc(a.sx, 0xffffffffu);
+  const __amdgpu_buffer_rsrc_t rsw = rsrc(a.sw, 0xffffffffu);
+  const PlanD8 plan = make_plan_d8(a, n0, m0, wave, l);
+  const LaneD8 lo = lane_d8(wn, wm, g, lr);
+
+  v4f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int s = 0; s < NST - 1; ++s)
+    if (s < KB) issue_d8(buf[s], plan, rx, rw, rsx, rsw, a, s, wave);
+
+  for (int kb0 = 0; kb0 < KB; kb0 += NST) {
+#pragma unroll
+    for (int u = 0; u < NST; ++u) {
+      const int kb = kb0 + u;
+      if (kb < KB) {
+        if (kb + 1 < KB) wait_vmcnt<LOADS>();   // stage kb + 1 may stay in flight
+        else wait_vmcnt<0>();
+        __syncthreads();
+        if (kb + NST - 1 < KB) issue_d8(buf[(u + NST - 1) % NST], plan, rx, rw, rsx, rsw, a, kb + NST - 1, wave);
+        compute_d8<GRAN_N>(buf[u], acc, lo, wn);
+      }
+    }
+  }
+
+  if constexpr (OUT_BF16) {   // half of a bf16 tile fits one stage buffer
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+        stage_quad<OUT_BF16, OUT_T, BYTES>(sm0, sm1, wn * 64 + i * 16 + 4 * g, wm * 64 + j * 16 + lr, v);
+      }
+    __syncthreads();
+    store_staged<OUT_BF16, OUT_T, BYTES>(a, sm0, sm1, m0, n0, t);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        store_quad<OUT_BF16, OUT_T>(a, m0 + wm * 64 + j * 16 + lr, n0 + wn * 64 + i * 16 + 4 * g, acc[i][j]);
+  }
 #endif  // SG_DEVICE_PASS
 }
 
@@ -610,7 +650,7 @@ __device__ __forceinline__ void dec_load(const GemmArgs& a, const DecRes& res, i
   for (int rb = 0; rb < RB; ++rb) {
     const int64_t nb = n0 + 16 * rb;
     o.idx[rb] = 0;
-    if (SPARSE && PACKED) {
+    if (PACKED) {
       // chunk of (row block rb of this workgroup, K block kb)
       const uint32_t c = (uint32_t)(rb * KB) * PK_CHUNK;
       const v4i av = buf_ld16(res.rw, c + pk_val_off(lr, g), kb * PK_CHUNK);
@@ -817,7 +857,7 @@ __global__ void __launch_bounds__(512) k_gemm_decode_dma(GemmArgs a) {
   // X slice: instruction i, lane l -> LDS 16-byte position p = 64 i + l: row p >> 3, chunk (p & 7) ^ (row & 7)
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int p = 64 * i + l, r = p >> 3, c = (p & 7) ^ (r & 7);
+    const int p = 64 * i + l, r = p >> 3, c = (p & 7) ^ swz8(r);
     o.x[i] = (uint32_t)(r * a.ldx + c * 16);
   }
 #pragma unroll
@@ -829,8 +869,8 @@ __global__ void __launch_bounds__(512) k_gemm_decode_dma(GemmArgs a) {
   // lane-constant LDS offsets within a wave's slot
   const uint32_t wslot = (uint32_t)wave * C::SLOT;
   const uint32_t oa = wslot + pk_val_off(lr, g), om = wslot + PK_META + pk_meta_word(lr, g);
-  const uint32_t ox0 = wslot + C::XOFF + lr * 128 + (((2 * g) ^ (lr & 7)) << 4);
-  const uint32_t ox1 = wslot + C::XOFF + lr * 128 + (((2 * g + 1) ^ (lr & 7)) << 4);
+  const uint32_t ox0 = wslot + C::XOFF + lr * 128 + (((2 * g) ^ swz8(lr)) << 4);
+  const uint32_t ox1 = wslot + C::XOFF + lr * 128 + (((2 * g + 1) ^ swz8(lr)) << 4);
   const uint32_t osx = wslot + C::SXOFF + lr * 4, osw = wslot + C::SWOFF;
 
   auto issue = [&](uint8_t* arr, int s) {
@@ -921,7 +961,7 @@ static void launch_large(const GemmArgs& a, hipStream_t st) {
   if (SPARSE)
     k_gemm_sparse_x2<PACKED, GRAN_N, OUT_BF16, OUT_T><<<tm * tn, 512, 0, st>>>(a, tm, tn);
   else
-    k_gemm_large<SPARSE, GRAN_N, OUT_BF16, OUT_T><<<tm * tn, 256, 0, st>>>(a, tm, tn);
+    k_gemm_dense8<GRAN_N, OUT_BF16, OUT_T><<<tm * tn, 512, 0, st>>>(a, tm, tn);
 }
 
 // Launches the LDS-streaming decode kernel with RB row blocks per workgroup if
@@ -1046,7 +1086,7 @@ extern "C" sg_status sg_fp8_gemm_groupwise(int64_t M, int64_t N, int64_t K, cons
   sg_status st = check_common(M, N, K, xq, ldx, sx, sx_sm, sx_sk, gran_m, sw, sw_sn, sw_sk, gran_n, y, y_dt, ldy, form);
   if (st != SG_OK) return st;
   if (!wq) return SG_ERR_NULL;
-  if (ldw < K || ldw > (1LL << 24)) return SG_ERR_SHAPE;
+  if (ldw < K || ldw >= (1LL << 24)) return SG_ERR_SHAPE;
   if (!aligned(wq, 16) || ldw % 16) return SG_ERR_ALIGN;
   if (M == 0 || N == 0) return SG_OK;
   const GemmArgs a = make_args(M, N, K, xq, ldx, sx, sx_sm, sx_sk, gran_m, wq, ldw, nullptr, 0, sw, sw_sn,
@@ -1066,7 +1106,7 @@ extern "C" sg_status sg_fp8_sparse24_gemm_groupwise(int64_t M, int64_t N, int64_
   sg_status st = check_common(M, N, K, xq, ldx, sx, sx_sm, sx_sk, gran_m, sw, sw_sn, sw_sk, gran_n, y, y_dt, ldy, form);
   if (st != SG_OK) return st;
   if (!wv || !wmeta) return SG_ERR_NULL;
-  if (ldwv < K / 2 || ldwm < K / 8 || ldwv > (1LL << 24) || ldwm > (1LL << 24)) return SG_ERR_SHAPE;
+  if (ldwv < K / 2 || ldwm < K / 8 || ldwv >= (1LL << 24) || ldwm >= (1LL << 24)) return SG_ERR_SHAPE;
   if (!aligned(wv, 16) || !aligned(wmeta, 16) || ldwv % 16 || ldwm % 16) return SG_ERR_ALIGN;
   if (M == 0 || N == 0) return SG_OK;
   const GemmArgs a = make_args(M, N, K, xq, ldx, sx, sx_sm, sx_sk, gran_m, wv, ldwv, wmeta, ldwm, sw, sw_sn,

@@ -51,7 +51,7 @@ struct MixedArgs {
 
 namespace mixed {
 // int4 K block (one half of a double stage), bytes:
-//   X1 128 rows x 64 B, W1 256 rows x 64 B: 16-byte chunk c of row r at c ^ ((r >> 1) & 3)
+//   X1 128 rows x 64 B, W1 256 rows x 64 B: 16-byte chunk c of row r at c ^ swz4(r)
 //   sx 128 floats (+ a dummy copy written by the waves that have no sx rows), sw 256 floats
 constexpr int X1_OFF = 0;
 constexpr int W1_OFF = TILE_M * 64;
@@ -59,7 +59,7 @@ constexpr int SX_OFF = W1_OFF + TILE_N * 64;
 constexpr int SW_OFF = SX_OFF + 2 * TILE_M * 4;
 constexpr int HALF = SW_OFF + TILE_N * 4;
 // bf16 double stage (64 columns): X2 128 rows x 128 B, W2 256 rows x 128 B,
-// 16-byte chunk c of row r at c ^ (r & 7)
+// 16-byte chunk c of row r at c ^ swz8q(r)
 constexpr int X2_OFF = 0;
 constexpr int W2_OFF = TILE_M * 128;
 // one double-stage buffer; it also holds a K group's partial tile at the end
@@ -89,18 +89,18 @@ __device__ __forceinline__ MixedPlan mixed_plan(const MixedArgs& a, int64_t n0, 
   using namespace mixed;
   MixedPlan p;
   {   // int4: load jj = 0 fills X1 slot `wave`, jj = 1, 2 W1 slots 8 (jj - 1) + wave; 16 rows of 64 B per slot
-    const int r = 16 * wave + (l >> 2), c = (l & 3) ^ ((r >> 1) & 3);
+    const int r = 16 * wave + (l >> 2), c = (l & 3) ^ swz4(r);
     p.io[0] = (uint32_t)(r * a.ldx1 + c * 16);
 #pragma unroll
     for (int jj = 1; jj < 3; ++jj) {
-      const int rw = 16 * (8 * (jj - 1) + wave) + (l >> 2), cw = (l & 3) ^ ((rw >> 1) & 3);
+      const int rw = 16 * (8 * (jj - 1) + wave) + (l >> 2), cw = (l & 3) ^ swz4(rw);
       p.io[jj] = (uint32_t)(rw * a.ldw1 + cw * 16);
     }
   }
 #pragma unroll
   for (int j = 0; j < 6; ++j) {   // bf16: 8 rows of 128 B per slot
     const int slot = j < 2 ? 8 * j + wave : 8 * (j - 2) + wave;
-    const int r = 8 * slot + (l >> 3), c = (l & 7) ^ (r & 7);
+    const int r = 8 * slot + (l >> 3), c = (l & 7) ^ swz8q(r);
     p.bo[j] = (uint32_t)(r * (j < 2 ? a.ldx2 : a.ldw2) * 2 + c * 16);
   }
 #pragma unroll
@@ -193,12 +193,12 @@ __device__ __forceinline__ MixedLane mixed_lane(int wn, int wm, int g, int lr, i
   using namespace mixed;
   MixedLane o;
   const int xr = wm * 64 + lr, wr = wn * 128 + lr;
-  o.x1 = X1_OFF + xr * 64 + ((g ^ ((lr >> 1) & 3)) << 4);
-  o.w1 = W1_OFF + wr * 64 + ((g ^ ((lr >> 1) & 3)) << 4);
+  o.x1 = X1_OFF + xr * 64 + ((g ^ swz4(lr)) << 4);
+  o.w1 = W1_OFF + wr * 64 + ((g ^ swz4(lr)) << 4);
   o.sx = SX_OFF + xr * 4;
   o.sw = SW_OFF + (wn * 128 + 4 * g) * 4;
-  o.x2 = X2_OFF + xr * 128 + (((4 * q + g) ^ (lr & 7)) << 4);
-  o.w2 = W2_OFF + wr * 128 + (((4 * q + g) ^ (lr & 7)) << 4);
+  o.x2 = X2_OFF + xr * 128 + (((4 * q + g) ^ swz8q(lr)) << 4);
+  o.w2 = W2_OFF + wr * 128 + (((4 * q + g) ^ swz8q(lr)) << 4);
   return o;
 }
 

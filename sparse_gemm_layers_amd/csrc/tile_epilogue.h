@@ -57,10 +57,34 @@ struct OutTile {
 // the partner group's partial tile (16 float4 per lane in buffer `src`) and
 // writes the result into the staged output tile.  Lane holds
 // D[n = wn*128 + 16 i + 4 g + e][m = wm*64 + 16 j + lr].
+// Writes one lane's four results D[nl + e][ml] (e = 0..3, tile-local
+// indices) into the staged output tile.
+template <bool OUT_BF16, bool OUT_T, int BUF>
+__device__ __forceinline__ void stage_quad(uint8_t* t0, uint8_t* t1, int nl, int ml, const float (&v)[4]) {
+  using OT = OutTile<OUT_BF16, OUT_T, BUF>;
+  if (!OUT_T) {
+    uint8_t* row = (ml < OT::RPH ? t0 : t1) + (ml % OT::RPH) * OT::PITCH;
+    if (OUT_BF16) {
+      uint2 pk;
+      pk.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
+      pk.y = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
+      *reinterpret_cast<uint2*>(row + nl * 2) = pk;
+    } else {
+      *reinterpret_cast<float4*>(row + nl * 4) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      uint8_t* row = (nl + e < OT::RPH ? t0 : t1) + ((nl + e) % OT::RPH) * OT::PITCH;
+      if (OUT_BF16) *reinterpret_cast<uint16_t*>(row + ml * 2) = (uint16_t)f32_to_bf16(v[e]);
+      else *reinterpret_cast<float*>(row + ml * 4) = v[e];
+    }
+  }
+}
+
 template <int Q, bool OUT_BF16, bool OUT_T, int BUF>
 __device__ __forceinline__ void x2_finish(const uint8_t* src, uint8_t* t0, uint8_t* t1, const v4f (&acc)[8][4],
                                           int w4, int l, int wn, int wm, int g, int lr) {
-  using OT = OutTile<OUT_BF16, OUT_T, BUF>;
   float4 part[16];
 #pragma unroll
   for (int k = 0; k < 16; ++k) part[k] = reinterpret_cast<const float4*>(src)[((w4 * 16 + k) << 6) + l];
@@ -72,25 +96,7 @@ __device__ __forceinline__ void x2_finish(const uint8_t* src, uint8_t* t0, uint8
       const float4 o = part[i * 4 + j];
       const v4f av = acc[4 * Q + i][j];
       const float v[4] = {av[0] + o.x, av[1] + o.y, av[2] + o.z, av[3] + o.w};
-      const int nl = wn * 128 + (4 * Q + i) * 16 + 4 * g, ml = wm * 64 + j * 16 + lr;
-      if (!OUT_T) {
-        uint8_t* row = (ml < OT::RPH ? t0 : t1) + (ml % OT::RPH) * OT::PITCH;
-        if (OUT_BF16) {
-          uint2 pk;
-          pk.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
-          pk.y = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
-          *reinterpret_cast<uint2*>(row + nl * 2) = pk;
-        } else {
-          *reinterpret_cast<float4*>(row + nl * 4) = make_float4(v[0], v[1], v[2], v[3]);
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          uint8_t* row = (nl + e < OT::RPH ? t0 : t1) + ((nl + e) % OT::RPH) * OT::PITCH;
-          if (OUT_BF16) *reinterpret_cast<uint16_t*>(row + ml * 2) = (uint16_t)f32_to_bf16(v[e]);
-          else *reinterpret_cast<float*>(row + ml * 4) = v[e];
-        }
-      }
+      stage_quad<OUT_BF16, OUT_T, BUF>(t0, t1, wn * 128 + (4 * Q + i) * 16 + 4 * g, wm * 64 + j * 16 + lr, v);
     }
 }
 
