@@ -55,6 +55,15 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Workgroup barrier for the LDS stage rings.  __syncthreads() also fences
+// global memory, which makes the compiler wait for every load in flight,
+// including the buffer loads that are filling later stages.  Here each wave
+// first waits (vmcnt) for its own loads of the stage it is about to read;
+// this barrier then waits for the wave's LDS reads to finish (so a stage read
+// before the barrier may be refilled after it) and joins the waves.  The
+// "memory" clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 template <bool OUT_BF16>
 __device__ __forceinline__ void store1(void* y, int64_t off, float v) {
   if (OUT_BF16)

@@ -447,22 +447,44 @@ __device__ __forceinline__ PlanD8 make_plan_d8(const GemmArgs& a, int64_t n0, in
   return p;
 }
 
-__device__ __forceinline__ void issue_d8(uint8_t* st, const PlanD8& p, __amdgpu_buffer_rsrc_t rx,
-                                         __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t rsx,
-                                         __amdgpu_buffer_rsrc_t rsw, const GemmArgs& a, int kb, int wave) {
+// The dense ring issues its loads through inline assembly (the same two
+// instructions the buffer-load-to-LDS builtin produces: M0 = LDS byte address,
+// then the load).  The compiler then does not track them, so it adds no
+// waits of its own before LDS reads of other stages (its tracking of three
+// ring buffers across the unrolled loop is not precise and waited for every
+// load in flight); the explicit per-stage load counts carry the ordering.
+typedef int rsrc_v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ rsrc_v rsrc_words(const void* p, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  return (rsrc_v){(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xffffu), (int)bytes, (int)RSRC_WORD3};
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>((const lds_void*)p);
+}
+
+__device__ __forceinline__ void dma16(const rsrc_v& r, uint32_t lds, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(lds), "v"(voff), "s"(r), "s"(soff) : "memory", "m0");
+}
+
+__device__ __forceinline__ void dma4(const rsrc_v& r, uint32_t lds, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :: "s"(lds), "v"(voff), "s"(r), "s"(soff) : "memory", "m0");
+}
+
+__device__ __forceinline__ void issue_d8(uint8_t* st, const PlanD8& p, const rsrc_v& rx, const rsrc_v& rw,
+                                         const rsrc_v& rsx, const rsrc_v& rsw, const GemmArgs& a, int kb,
+                                         int wave) {
   using L = Stage<false>;
+  const uint32_t base = lds_addr(st);
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(st + L::X_OFF + (8 * j + wave) * 1024), 16, p.xo[j],
-                                             kb * 128, 0, 0);
+  for (int j = 0; j < 2; ++j) dma16(rx, base + L::X_OFF + (8 * j + wave) * 1024, p.xo[j], (uint32_t)kb * 128);
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(st + L::W_OFF + (8 * j + wave) * 1024), 16, p.wo[j],
-                                             kb * 128, 0, 0);
-  if (p.sk == 0)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsx, (lds_void*)(st + p.sdst), 4, p.so, (int)(kb * a.sx_sk * 4), 0, 0);
-  else
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, (lds_void*)(st + p.sdst), 4, p.so, (int)(kb * a.sw_sk * 4), 0, 0);
+  for (int j = 0; j < 4; ++j) dma16(rw, base + L::W_OFF + (8 * j + wave) * 1024, p.wo[j], (uint32_t)kb * 128);
+  if (p.sk == 0) dma4(rsx, base + p.sdst, p.so, (uint32_t)(kb * a.sx_sk * 4));
+  else dma4(rsw, base + p.sdst, p.so, (uint32_t)(kb * a.sw_sk * 4));
 }
 #endif  // SG_DEVICE_PASS
 
@@ -486,45 +508,96 @@ __device__ __forceinline__ LaneD8 lane_d8(int wn, int wm, int g, int lr) {
   return o;
 }
 
-// Multiplies one stage into the wave's 4 x 4 sub-tiles and promotes.
+// One stage's operands of a wave in registers: the A (W) and B (X) fragments
+// of its 4 x 4 sub-tiles and the scales.
+struct FragD8 {
+  v8i a[4], b[4];
+  float sx[4];    // X scales of the lane's rows (per-row W scales), or
+                  // sx * sw, the whole scale of sub-tile column j (128-row W scale blocks)
+  float4 sw[4];   // W scales of rows 16 i + 4 g .. + 3 (per-row W scales only)
+};
+
+__device__ __forceinline__ v8i ld_frag(const uint8_t* st, uint32_t o0, uint32_t o1) {
+  const uint4 lo = lds_ld<uint4>(st, o0);
+  const uint4 hi = lds_ld<uint4>(st, o1);
+  return (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+}
+
+// X fragments and scales of a stage.
 template <int GRAN_N>
-__device__ __forceinline__ void compute_d8(const uint8_t* st, v4f (&acc)[4][4], const LaneD8& o, int wn) {
+__device__ __forceinline__ void read_b_d8(const uint8_t* st, const LaneD8& o, int wn, FragD8& f) {
   using L = Stage<false>;
-  float sxj[4];
-  v8i bx[4];
+  const float swv = GRAN_N == 128 ? lds_ld<float>(st, L::SW_OFF + wn * 256) : 1.f;   // the wave's 64 rows share it
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    sxj[j] = lds_ld<float>(st, o.sx + j * 64);
-    const uint4 lo = lds_ld<uint4>(st, o.x0 + j * 2048);
-    const uint4 hi = lds_ld<uint4>(st, o.x1 + j * 2048);
-    bx[j] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    f.sx[j] = lds_ld<float>(st, o.sx + j * 64) * swv;
+    f.b[j] = ld_frag(st, o.x0 + j * 2048, o.x1 + j * 2048);
   }
-  float s128[4];
-  if (GRAN_N == 128) {
-    const float swv = lds_ld<float>(st, L::SW_OFF + wn * 256);   // the wave's 64 rows share one W scale
+}
+
+// W fragment (and per-row W scales) of sub-tile row i of a stage.
+template <int GRAN_N>
+__device__ __forceinline__ void read_a_d8(const uint8_t* st, const LaneD8& o, int i, FragD8& f) {
+  f.a[i] = ld_frag(st, o.w0 + i * 2048, o.w1 + i * 2048);
+  if (GRAN_N == 1) f.sw[i] = lds_ld<float4>(st, o.sw + i * 64);
+}
+
+// Promotes sub-tile row i.  The empty asm pins each result at this point:
+// otherwise the compiler sinks the promotions past the next barrier (they
+// are register-only arithmetic), keeping 64 MFMA results alive across it and
+// bunching two stages' promotions into one.
+template <int GRAN_N>
+__device__ __forceinline__ void promote_d8(v4f (&acc)[4], const v4f (&p)[4], const FragD8& f, int i) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) s128[j] = sxj[j] * swv;
+  for (int j = 0; j < 4; ++j) {
+    if (GRAN_N == 128) {
+      acc[j] += p[j] * f.sx[j];
+    } else {
+      acc[j][0] = fmaf(p[j][0] * f.sw[i].x, f.sx[j], acc[j][0]);
+      acc[j][1] = fmaf(p[j][1] * f.sw[i].y, f.sx[j], acc[j][1]);
+      acc[j][2] = fmaf(p[j][2] * f.sw[i].z, f.sx[j], acc[j][2]);
+      acc[j][3] = fmaf(p[j][3] * f.sw[i].w, f.sx[j], acc[j][3]);
+    }
+    asm volatile("" : "+v"(acc[j]));
   }
+}
+
+// Multiplies stage `cur` (in registers) into the wave's 4 x 4 sub-tiles and
+// promotes, while reading the next stage into `nxt`: its X fragments first,
+// then the W fragment of row i once row i of `cur` is multiplied, so the two
+// register sets can share the W registers.
+template <int GRAN_N>
+__device__ __forceinline__ void step_d8(const FragD8& cur, FragD8& nxt, const uint8_t* st_next, const LaneD8& o,
+                                        int wn, v4f (&acc)[4][4]) {
+  read_b_d8<GRAN_N>(st_next, o, wn, nxt);
+  v4f p[2][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint4 lo = lds_ld<uint4>(st, o.w0 + i * 2048);
-    const uint4 hi = lds_ld<uint4>(st, o.w1 + i * 2048);
-    const v8i aa = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    float4 swr = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (GRAN_N == 1) swr = lds_ld<float4>(st, o.sw + i * 64);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) p[i & 1][j] = mma_dense(cur.a[i], cur.b[j]);
+    if (i > 0) promote_d8<GRAN_N>(acc[i - 1], p[(i - 1) & 1], cur, i - 1);
+    read_a_d8<GRAN_N>(st_next, o, i, nxt);
+  }
+  promote_d8<GRAN_N>(acc[3], p[1], cur, 3);
+}
+
+// Multiplies one stage's fragments into the wave's 4 x 4 sub-tiles and promotes.
+template <int GRAN_N>
+__device__ __forceinline__ void mma_d8(const FragD8& f, v4f (&acc)[4][4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const v4f p = mma_dense(aa, bx[j]);
+      const v4f p = mma_dense(f.a[i], f.b[j]);
       if (GRAN_N == 128) {
-        acc[i][j] += p * s128[j];
+        acc[i][j] += p * f.sx[j];
       } else {
-        acc[i][j][0] = fmaf(p[0] * swr.x, sxj[j], acc[i][j][0]);
-        acc[i][j][1] = fmaf(p[1] * swr.y, sxj[j], acc[i][j][1]);
-        acc[i][j][2] = fmaf(p[2] * swr.z, sxj[j], acc[i][j][2]);
-        acc[i][j][3] = fmaf(p[3] * swr.w, sxj[j], acc[i][j][3]);
+        acc[i][j][0] = fmaf(p[0] * f.sw[i].x, f.sx[j], acc[i][j][0]);
+        acc[i][j][1] = fmaf(p[1] * f.sw[i].y, f.sx[j], acc[i][j][1]);
+        acc[i][j][2] = fmaf(p[2] * f.sw[i].z, f.sx[j], acc[i][j][2]);
+        acc[i][j][3] = fmaf(p[3] * f.sw[i].w, f.sx[j], acc[i][j][3]);
       }
     }
-  }
 }
 
 template <int GRAN_N, bool OUT_BF16, bool OUT_T>
@@ -547,10 +620,10 @@ __global__ void __launch_bounds__(512) k_gemm_dense8(GemmArgs a, int tiles_m, in
   const int KB = (int)(a.K >> 7);
 
   const int64_t mrows = min((int64_t)BM, a.M - m0), nrows = min((int64_t)BN, a.N - n0);
-  const __amdgpu_buffer_rsrc_t rx = rsrc(a.x + m0 * a.ldx, (uint32_t)(mrows * a.ldx));
-  const __amdgpu_buffer_rsrc_t rw = rsrc(a.w + n0 * a.ldw, (uint32_t)(nrows * a.ldw));
-  const __amdgpu_buffer_rsrc_t rsx = rsrc(a.sx, 0xffffffffu);
-  const __amdgpu_buffer_rsrc_t rsw = rsrc(a.sw, 0xffffffffu);
+  const rsrc_v rx = rsrc_words(a.x + m0 * a.ldx, (uint32_t)(mrows * a.ldx));
+  const rsrc_v rw = rsrc_words(a.w + n0 * a.ldw, (uint32_t)(nrows * a.ldw));
+  const rsrc_v rsx = rsrc_words(a.sx, 0xffffffffu);
+  const rsrc_v rsw = rsrc_words(a.sw, 0xffffffffu);
   const PlanD8 plan = make_plan_d8(a, n0, m0, wave, l);
   const LaneD8 lo = lane_d8(wn, wm, g, lr);
 
@@ -560,23 +633,65 @@ __global__ void __launch_bounds__(512) k_gemm_dense8(GemmArgs a, int tiles_m, in
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
 
+  if constexpr (GRAN_N == 128) {
+    // Three LDS stages and two register sets.  Step kb waits for stage
+    // kb + 1, issues stage kb + 3 into the buffer stage kb has left, reads
+    // stage kb + 1 into the spare register set and multiplies stage kb (read
+    // during the previous step), so the LDS reads of one stage overlap the
+    // MFMAs of the one before.  Stages past the last K block reload the last
+    // block (into buffers whose contents are read but not used), so every
+    // step issues one stage, each wave has exactly two stages in flight
+    // before its wait, and the loop has no branches.  The loads are not
+    // tracked by the compiler (see dma16), so the buffers rotate at run time.
 #pragma unroll
-  for (int s = 0; s < NST - 1; ++s)
-    if (s < KB) issue_d8(buf[s], plan, rx, rw, rsx, rsw, a, s, wave);
+    for (int s = 0; s < NST; ++s) issue_d8(buf[s], plan, rx, rw, rsx, rsw, a, min(s, KB - 1), wave);
+    uint8_t* b0 = sm0;   // stage kb
+    uint8_t* b1 = sm1;   // stage kb + 1
+    uint8_t* b2 = sm2;   // stage kb + 2
+    FragD8 f0, f1;
+    wait_vmcnt<2 * LOADS>();
+    lds_barrier();
+    read_b_d8<GRAN_N>(b0, lo, wn, f0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) read_a_d8<GRAN_N>(b0, lo, i, f0);
 
-  for (int kb0 = 0; kb0 < KB; kb0 += NST) {
+    auto step = [&](const FragD8& cur, FragD8& nxt, int kb) {
+      wait_vmcnt<LOADS>();   // stage kb + 1 has landed; stage kb + 2 may stay in flight
+      lds_barrier();         // every wave is done reading stage kb into registers
+      issue_d8(b0, plan, rx, rw, rsx, rsw, a, min(kb + NST, KB - 1), wave);
+      step_d8<GRAN_N>(cur, nxt, b1, lo, wn, acc);
+      uint8_t* const t = b0;
+      b0 = b1; b1 = b2; b2 = t;
+    };
+    int kb = 0;
+    for (; kb + 2 <= KB; kb += 2) {
+      step(f0, f1, kb);
+      step(f1, f0, kb + 1);
+    }
+    if (kb < KB) step(f0, f1, kb);
+  } else {
+    // Per-row W scales need more registers per stage: one register set.
+    // Step kb waits for stage kb, issues stage kb + 2 into the buffer stage
+    // kb - 1 has left, then reads and multiplies stage kb.
 #pragma unroll
-    for (int u = 0; u < NST; ++u) {
-      const int kb = kb0 + u;
-      if (kb < KB) {
-        if (kb + 1 < KB) wait_vmcnt<LOADS>();   // stage kb + 1 may stay in flight
-        else wait_vmcnt<0>();
-        __syncthreads();
-        if (kb + NST - 1 < KB) issue_d8(buf[(u + NST - 1) % NST], plan, rx, rw, rsx, rsw, a, kb + NST - 1, wave);
-        compute_d8<GRAN_N>(buf[u], acc, lo, wn);
-      }
+    for (int s = 0; s < NST - 1; ++s) issue_d8(buf[s], plan, rx, rw, rsx, rsw, a, min(s, KB - 1), wave);
+    uint8_t* bp = sm2;   // stage kb - 1
+    uint8_t* b0 = sm0;   // stage kb
+    uint8_t* b1 = sm1;   // stage kb + 1
+    FragD8 f;
+    for (int kb = 0; kb < KB; ++kb) {
+      wait_vmcnt<LOADS>();   // stage kb has landed; stage kb + 1 may stay in flight
+      lds_barrier();
+      issue_d8(bp, plan, rx, rw, rsx, rsw, a, min(kb + NST - 1, KB - 1), wave);
+      read_b_d8<GRAN_N>(b0, lo, wn, f);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) read_a_d8<GRAN_N>(b0, lo, i, f);
+      mma_d8<GRAN_N>(f, acc);
+      uint8_t* const t = bp;
+      bp = b0; b0 = b1; b1 = t;
     }
   }
+  wait_vmcnt<0>();   // no load may still be writing LDS when the tile is staged there
 
   if constexpr (OUT_BF16) {   // half of a bf16 tile fits one stage buffer
     __syncthreads();
