@@ -40,7 +40,9 @@ METRIC = "dense-equiv FP8 TFLOP/s @M=2048 N=K=4096 2:4 W; % MFMA peak; M=16 GB/s
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense FP8 MFMA
 PEAK_INT8_TOPS = 5000.0
 PEAK_HBM_GBS = 8000.0
-GEMM_SRC = os.path.join(ROOT, "sparse_gemm_layers_amd", "csrc", "gemm_fp8.hip")
+# the sources the sparse GEMM kernel is compiled from (a change voids the recorded traffic)
+GEMM_SRCS = [os.path.join(ROOT, "sparse_gemm_layers_amd", "csrc", f)
+             for f in ("gemm_fp8.hip", "gemm_common.h", "tile_epilogue.h", "common.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sparse_gemm_2048x4096x4096_traffic.txt")
 DEV = torch.device("cuda:0")
 ROTATE = 8          # input sets cycled through in the headline loop (> MALL)
@@ -222,6 +224,107 @@ def cpu_baseline(min_seconds=8.0):
                       f"{np.mean(times):.2f} s each; quantisation/pruning done beforehand, untimed)"}
 
 
+def measured_peaks():
+    """What the chip sustains, next to the published peaks: each matrix-core
+    instruction the kernels use (register operands, two waves per SIMD, eight
+    independent chains), the shader clock during those runs, and a device copy."""
+    out = {}
+    sink = torch.empty(sg._binding.PROBE_WORKGROUPS * 512, dtype=torch.float32, device=DEV)
+    clocks = torch.zeros(4 * sg._binding.PROBE_WORKGROUPS, dtype=torch.int64, device=DEV)
+    for kind, iters in (("mfma_fp8", 2000), ("smfmac_fp8", 4000), ("mfma_i8", 4000)):
+        best, ghz = None, None
+        for _ in range(3):
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            sg.probe_matrix_rate(kind, iters, sink, clocks)
+            e.record()
+            torch.cuda.synchronize()
+            ms = s.elapsed_time(e)
+            if best is None or ms < best:
+                c = clocks.cpu().numpy().reshape(-1, 4).astype(np.float64)
+                ok = (c[:, 3] - c[:, 2]) > 0
+                best = ms
+                ghz = float(np.median((c[ok, 1] - c[ok, 0]) / (c[ok, 3] - c[ok, 2])) * 0.1)
+        out[kind] = {"TFLOP/s" if kind != "mfma_i8" else "TOP/s": round(sg.probe_matrix_ops(kind, iters) / best / 1e9, 1),
+                     "shader_GHz": round(ghz, 3)}
+    nbytes = 1 << 30
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device=DEV).fill_(1.0)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    ms = time_fn(lambda i: b.copy_(a), reps=10, warm=2)
+    out["device_copy_1GiB"] = {"GB/s": round(2 * nbytes / ms / 1e6, 1)}
+    del a, b
+    return out
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in GEMM_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
+def pmc_kib_per_dispatch(run_dir, counter, kernel_substr):
+    """Mean value of one counter per dispatch of the kernels whose name
+    contains kernel_substr, from a rocprofv3 --pmc database (KiB for the
+    FETCH_SIZE / WRITE_SIZE derived counters)."""
+    import glob
+    import sqlite3
+    db = sorted(glob.glob(os.path.join(run_dir, "**", "*_results.db"), recursive=True))[0]
+    cur = sqlite3.connect(db).cursor()
+    rows = cur.execute(
+        "select d.id, sum(p.value) from rocpd_pmc_event p join rocpd_kernel_dispatch d on p.event_id = d.event_id "
+        "join rocpd_info_kernel_symbol s on d.kernel_id = s.id join rocpd_info_pmc i on p.pmc_id = i.id "
+        "where i.name = ? and s.kernel_name like ? group by d.id", (counter, f"%{kernel_substr}%")).fetchall()
+    return float(np.mean([v for _, v in rows]))
+
+
+def write_traffic_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
+    """Writes the traffic file of the sparse GEMM from four counter runs (see
+    its header for the commands): HBM bytes per launch, each counter scaled by
+    what it reads for a plain device copy of known size."""
+    kern = "k_gemm_sparse_x2"
+    g_f = pmc_kib_per_dispatch(fetch_dir, "FETCH_SIZE", kern)
+    g_w = pmc_kib_per_dispatch(write_dir, "WRITE_SIZE", kern)
+    # the device-to-device copy (the HIP runtime's blit kernel behind tensor.copy_)
+    c_f = pmc_kib_per_dispatch(copy_fetch_dir, "FETCH_SIZE", "copyBuffer")
+    c_w = pmc_kib_per_dispatch(copy_write_dir, "WRITE_SIZE", "copyBuffer")
+    each_way_kib = (512 << 20) / 1024
+    rs, ws = each_way_kib / c_f, each_way_kib / c_w
+    rd, wr = g_f * 1024 * rs, g_w * 1024 * ws
+    m, n, k = 2048, 4096, 4096
+    cmd = "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {c} -d <repo>/gpurun_out/prof/{d} -o run -- python -u <repo>/bench.py {a}"
+    lines = [
+        "# HBM traffic of the 2:4 sparse FP8 GEMM, 2048x4096x4096, packed weight, Y form, bf16 output",
+        "# kernel: sg::k_gemm_sparse_x2<true, 128, true, false> (one launch = the whole GEMM)",
+        "# commands (from the repository root on an MI355X; one counter per run):",
+        "#   " + cmd.format(c="FETCH_SIZE", d="FETCH_SIZE", a="--only gemm --steps 20 --warmup 5"),
+        "#   " + cmd.format(c="WRITE_SIZE", d="WRITE_SIZE", a="--only gemm --steps 20 --warmup 5"),
+        "# calibration (a plain 512 MiB device copy, same two counters):",
+        "#   " + cmd.format(c="FETCH_SIZE", d="copy_FETCH_SIZE", a="--copy-calibration"),
+        "#   " + cmd.format(c="WRITE_SIZE", d="copy_WRITE_SIZE", a="--copy-calibration"),
+        "# this file: python bench.py --traffic-summary gpurun_out/prof/{FETCH_SIZE,WRITE_SIZE,copy_FETCH_SIZE,"
+        "copy_WRITE_SIZE}",
+        "# counters are mean KiB per dispatch over the run's dispatches of the kernel",
+        f"gemm_FETCH_SIZE_KiB: {g_f:.1f}",
+        f"gemm_WRITE_SIZE_KiB: {g_w:.1f}",
+        f"copy_FETCH_SIZE_KiB: {c_f:.1f}",
+        f"copy_WRITE_SIZE_KiB: {c_w:.1f}",
+        f"copy_bytes_each_way_KiB: {each_way_kib:.0f}",
+        f"read_scale: {rs:.5f}",
+        f"write_scale: {ws:.5f}",
+        f"hbm_read_bytes_per_launch: {rd:.0f}",
+        f"hbm_write_bytes_per_launch: {wr:.0f}",
+        f"hbm_bytes_per_launch: {rd + wr:.0f}",
+        f"algorithmic_bytes_per_launch: {sparse_bytes(m, n, k)}",
+        "# reads are well above the algorithmic input bytes: each of the 8 XCDs' L2 fetches the X",
+        "# row panels and W tiles its 32 workgroups use (4 n-tiles x 8 m-tiles per XCD)",
+        f"kernel_source_sha256: {kernel_source_hash()}",
+    ]
+    open(TRAFFIC_FILE, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def traffic_from_profile():
     """HBM bytes per launch of the sparse GEMM from the committed counter
     summary, only if it was taken on the current kernel source."""
@@ -232,8 +335,7 @@ def traffic_from_profile():
         if ":" in line and not line.startswith("#"):
             a, b = line.split(":", 1)
             kv[a.strip()] = b.strip()
-    src = hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()
-    if kv.get("kernel_source_sha256") != src:
+    if kv.get("kernel_source_sha256") != kernel_source_hash():
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -257,8 +359,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--only", choices=["gemm"], default=None,
-                    help="run only the headline loop (for counter collection)")
+    ap.add_argument("--only", choices=["gemm", "rows"], default=None,
+                    help="run only the headline loop, or only the per-row kernels (for counter collection)")
+    ap.add_argument("--traffic-summary", nargs=4, metavar="DIR", default=None,
+                    help="write the sparse GEMM traffic file from FETCH_SIZE, WRITE_SIZE and the two copy "
+                         "calibration counter runs")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -270,7 +375,13 @@ def main():
     if args.copy_calibration:
         copy_calibration()
         return
+    if args.traffic_summary:
+        write_traffic_summary(*args.traffic_summary)
+        return
     sg.lib()
+    if args.only == "rows":
+        print(json.dumps({"rows": rows_report()}))
+        return
     h = headline(args.steps, args.warmup)
     if args.only == "gemm":
         print(json.dumps({"headline": h}))
@@ -303,6 +414,7 @@ def main():
             "kernel": "k_gemm_sparse_x2<packed> (2:4 FP8 GEMM, Y form)", "avg_launch_ms": round(h["gemm_ms"], 5),
         },
         "rows": {k: {kk: round(vv, 5) for kk, vv in v.items()} for k, v in rows.items()},
+        "measured_peaks": measured_peaks(),
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline()

@@ -2,7 +2,7 @@
 linear-layer GEMMs for AMD Instinct MI355X (gfx950).
 
 A thin Python binding over the C ABI of ``libsg.so`` (declared in
-``include/sg.h``).  The functions only marshal arguments: PyTorch supplies
+``include/sg.h``; the measurement helpers in ``include/sg_probe.h``).  The functions only marshal arguments: PyTorch supplies
 device memory and the current HIP stream; every step runs in the library's
 HIP kernels.  There is no CPU fallback: if ``libsg.so`` is missing or the
 tensors are not on a GPU, the call raises.
@@ -20,11 +20,13 @@ from ._binding import (
     sparse24_pack_gfx950,
     fp8_sparse24_gemm_groupwise_packed,
     mixed_gemm_add,
+    probe_matrix_ops,
+    probe_matrix_rate,
 )
 
 __all__ = [
     "SgError", "lib", "fp8_quant_groupwise", "int4_quant_groupwise",
     "sparse24_prune_compress", "fp8_gemm_groupwise", "fp8_sparse24_gemm_groupwise",
     "sparse24_packed_bytes", "sparse24_pack_gfx950", "fp8_sparse24_gemm_groupwise_packed",
-    "mixed_gemm_add",
+    "mixed_gemm_add", "probe_matrix_ops", "probe_matrix_rate",
 ]

@@ -37,6 +37,8 @@ _SIGS = {
                                                _i64, _i64, _int, _ptr, _int, _i64, _int, _ptr], _int),
     "sg_mixed_gemm_add": ([_i64, _i64, _i64, _i64, _ptr, _i64, _ptr, _i64, _i64, _ptr, _i64, _ptr, _i64, _i64,
                            _ptr, _i64, _ptr, _i64, _ptr, _i64, _ptr], _int),
+    "sg_probe_matrix_ops": ([_int, _int], _i64),
+    "sg_probe_matrix_rate": ([_int, _int, _ptr, _ptr, _ptr], _int),
 }
 
 _lib = None
@@ -251,3 +253,26 @@ def mixed_gemm_add(x1, sx1, w1, sw1, x2, w2, y=None):
                                  _p(y), _row_stride(y), _stream(x1))
     _check(st, "sg_mixed_gemm_add")
     return y
+
+
+# ------------------------------------------------------------ measurement helpers
+
+PROBE_WORKGROUPS = 1024
+PROBE_KINDS = {"mfma_fp8": 0, "smfmac_fp8": 1, "mfma_i8": 2}
+
+
+def probe_matrix_ops(kind, iters):
+    """Dense-equivalent operations of one probe_matrix_rate launch."""
+    return lib().sg_probe_matrix_ops(PROBE_KINDS[kind], iters)
+
+
+def probe_matrix_rate(kind, iters, sink, clocks):
+    """Enqueues one matrix-core rate probe (sg_probe.h).  sink: float32 device
+    tensor of PROBE_WORKGROUPS * 512 elements; clocks: int64 device tensor of
+    4 * PROBE_WORKGROUPS elements (shader clock and real-time counter at the
+    start and end of each workgroup's first wave)."""
+    for t, n, nm in ((sink, PROBE_WORKGROUPS * 512, "sink"), (clocks, 4 * PROBE_WORKGROUPS, "clocks")):
+        if not t.is_cuda or t.numel() < n or not t.is_contiguous():
+            raise SgError(f"{nm} must be a contiguous device tensor of at least {n} elements")
+    st = lib().sg_probe_matrix_rate(PROBE_KINDS[kind], iters, _p(sink), _p(clocks), _stream(sink))
+    _check(st, "sg_probe_matrix_rate")

@@ -14,7 +14,7 @@ import sparse_gemm_layers_amd as sg
 from sparse_gemm_layers_amd import _binding as B
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "sg.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("sg.h", "sg_probe.h")]
 
 OK, NULL, SHAPE, UNSUP, ALIGN, HIP = range(6)
 P = ctypes.c_void_p(0x100000)          # 16-byte aligned fake address
@@ -26,9 +26,13 @@ no_gpu = pytest.mark.skipif(torch.cuda.is_available(), reason="fake-pointer chec
 
 
 def declared_functions():
-    src = open(HEADER).read()
+    src = "".join(open(h).read() for h in HEADERS)
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"\b(sg_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_include_holds_only_the_known_headers():
+    assert sorted(os.listdir(os.path.join(ROOT, "include"))) == ["sg.h", "sg_probe.h"]
 
 
 def test_header_declares_the_entry_points():
@@ -36,7 +40,7 @@ def test_header_declares_the_entry_points():
         "sg_abi_version", "sg_status_str", "sg_fp8_quant_groupwise", "sg_int4_quant_groupwise",
         "sg_sparse24_prune_compress", "sg_fp8_gemm_groupwise", "sg_fp8_sparse24_gemm_groupwise",
         "sg_mixed_gemm_add", "sg_sparse24_packed_bytes", "sg_sparse24_pack_gfx950",
-        "sg_fp8_sparse24_gemm_groupwise_packed"])
+        "sg_fp8_sparse24_gemm_groupwise_packed", "sg_probe_matrix_ops", "sg_probe_matrix_rate"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -201,3 +205,22 @@ def test_packed_gemm_validation(kw, code):
     assert sg.lib().sg_fp8_sparse24_gemm_groupwise_packed(a["M"], a["N"], a["K"], a["x"], a["ldx"], a["sx"], 1, 64,
                                                           1, a["w"], a["sw"], 2, 1, 128, a["y"], 1, 256, 0,
                                                           None) == code
+
+
+@no_gpu
+def test_probe_rejects_bad_arguments_on_the_host():
+    lib = sg.lib()
+    assert lib.sg_probe_matrix_rate(0, 10, None, P, None) == NULL
+    assert lib.sg_probe_matrix_rate(0, 10, P, None, None) == NULL
+    assert lib.sg_probe_matrix_rate(3, 10, P, P2, None) == UNSUP
+    assert lib.sg_probe_matrix_rate(-1, 10, P, P2, None) == UNSUP
+    assert lib.sg_probe_matrix_rate(0, 0, P, P2, None) == SHAPE
+
+
+def test_probe_operation_counts():
+    lib = sg.lib()
+    # 1024 workgroups x 8 waves x 8 instructions per round
+    assert lib.sg_probe_matrix_ops(0, 1) == 2 * 16 * 16 * 128 * 8 * 8 * 1024
+    assert lib.sg_probe_matrix_ops(1, 3) == 3 * 2 * 16 * 16 * 128 * 8 * 8 * 1024
+    assert lib.sg_probe_matrix_ops(2, 1) == 2 * 16 * 16 * 64 * 8 * 8 * 1024
+    assert lib.sg_probe_matrix_ops(5, 1) == -1 and lib.sg_probe_matrix_ops(0, 0) == -1
