@@ -28,22 +28,24 @@ exact rational brute force, or identities the pages state).  None is
 
 from .e4m3 import E4M3_MAX, e4m3_decode, e4m3_encode
 from .bf16 import bf16_decode
-from .quant import fp8_quant_groupwise, int4_quant_groupwise, int4_decode
+from .quant import fp8_quant_groupwise, int4_quant_groupwise, int4_decode, int8_quant_groupwise
 from .sparse24 import prune24, compress24, decompress24, prune_compress24
 from .pack import pack24_gfx950, unpack24_gfx950, packed_bytes
 from .gemm import (
     expand_scales,
     fp8_gemm_groupwise,
     fp8_sparse24_gemm_groupwise,
+    int8_gemm_groupwise,
+    int8_sparse24_gemm_groupwise,
     mixed_gemm_add,
     within_tolerance,
 )
 
 __all__ = [
     "E4M3_MAX", "e4m3_decode", "e4m3_encode", "bf16_decode",
-    "fp8_quant_groupwise", "int4_quant_groupwise", "int4_decode",
+    "fp8_quant_groupwise", "int4_quant_groupwise", "int4_decode", "int8_quant_groupwise",
     "prune24", "compress24", "decompress24", "prune_compress24",
     "pack24_gfx950", "unpack24_gfx950", "packed_bytes",
     "expand_scales", "fp8_gemm_groupwise", "fp8_sparse24_gemm_groupwise",
-    "mixed_gemm_add", "within_tolerance",
+    "int8_gemm_groupwise", "int8_sparse24_gemm_groupwise", "mixed_gemm_add", "within_tolerance",
 ]

@@ -36,6 +36,10 @@ Y = X1 W1^T + X2 W2^T with X1, W1 quantised to 4 bit):
     y = sum_kb sx1[m, kb] * sw1[n, kb] * sum_{k in kb} int4(x1) int4(w1)
         + sum_{k < K2} bf16(x2[m, k]) * bf16(w2[n, k])
 
+int8 x int8 with the same groupwise scales (the other 2:4 kernel torchao PR
+#3258 names, jcaip's comment): the same sum with int8 codes; every 128-term
+partial is an integer below 2^21, exact in fp64.
+
 Tolerance (the accepted error of a GPU result g against the oracle y):
     |g - y| <= 1e-2 |y| + 1e-3 T,
     T[m, n] = sum_kb s(m, n, kb) * sum_{k in kb} |dec x * dec w|  (+ sum |x2 w2|).
@@ -94,6 +98,29 @@ def fp8_sparse24_gemm_groupwise(xq, sx, gm: int, wv, wmeta, sw, gn: int, bound: 
     wv [N, K/2] and metadata wmeta [N, K/8]."""
     wq = decompress24(np.asarray(wv, dtype=np.uint8), wmeta)
     return fp8_gemm_groupwise(xq, sx, gm, wq, sw, gn, bound=bound)
+
+
+def int8_gemm_groupwise(xq, sx, gm: int, wq, sw, gn: int, bound: bool = False):
+    """xq [M, K] int8 codes, sx fp32 [ceil(M/gm), K/128]; wq [N, K] int8 codes,
+    sw fp32 [ceil(N/gn), K/128].  Returns y fp64 [M, N] (and T if bound)."""
+    xd = np.asarray(xq, dtype=np.int8).astype(np.float64)
+    wd = np.asarray(wq, dtype=np.int8).astype(np.float64)
+    m, k = xd.shape
+    n = wd.shape[0]
+    assert gm in (1, 128) and gn in (1, 128)
+    sxe, swe = expand_scales(sx, gm, m), expand_scales(sw, gn, n)
+    assert sxe.shape == (m, k // KBLK) and swe.shape == (n, k // KBLK)
+    y = _scaled_kblock_sum(xd, sxe, wd, swe, absolute=False)
+    if not bound:
+        return y
+    return y, _scaled_kblock_sum(xd, sxe, wd, swe, absolute=True)
+
+
+def int8_sparse24_gemm_groupwise(xq, sx, gm: int, wv, wmeta, sw, gn: int, bound: bool = False):
+    """``int8_gemm_groupwise`` with W given as 2:4 compressed int8 codes
+    wv [N, K/2] and metadata wmeta [N, K/8]."""
+    wq = decompress24(np.asarray(wv, dtype=np.int8).view(np.uint8), wmeta).view(np.int8)
+    return int8_gemm_groupwise(xq, sx, gm, wq, sw, gn, bound=bound)
 
 
 def mixed_gemm_add(x1p, sx1, w1p, sw1, x2, w2, bound: bool = False):

@@ -23,6 +23,14 @@ scheme; the reading used here is symmetric per (row, 128-column group):
 s = fl32(amax / 7) (1 when amax == 0), q = clamp(rint_even(fl32(v / s)), -7, 7),
 two's-complement nibbles packed two per byte, element 2j in the low nibble
 of byte j.
+
+int8 (``int8_quant_groupwise``), for the int8 x int8 2:4-sparse GEMM that
+torchao PR #3258 "Introduce new W8A8-FP-CSR quantization API" names beside the
+fp8 one (jcaip: the only kernels are int8 x int8 2:4 sparse and fp8 x fp8 2:4
+sparse).  The page fixes no int8 scheme; the reading used here keeps the FP8
+path's groupwise blocks (1 or 128 rows x 64 or 128 columns) and uses the
+symmetric int8 grid: s = fl32(amax / 127) (1 when amax == 0),
+q = clamp(rint_even(fl32(v / s)), -127, 127), stored as int8.
 """
 
 import numpy as np
@@ -69,6 +77,18 @@ def int4_quant_groupwise(x, gc: int = 128):
     nib = (qi & 0xF).astype(np.uint8)
     packed = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
     return packed, s
+
+
+def int8_quant_groupwise(x, gr: int, gc: int):
+    """x: fp32 [rows, cols].  Returns (codes int8 [rows, cols],
+    scales fp32 [ceil(rows/gr), ceil(cols/gc)], row-major)."""
+    x32 = np.asarray(x, dtype=np.float32)
+    rows, cols = x32.shape
+    amax = _block_amax(x32, gr, gc)
+    s = np.where(amax > 0, amax / np.float32(127.0), np.float32(1.0)).astype(np.float32)
+    q = (x32 / _expand(s, gr, gc, rows, cols)).astype(np.float32)   # fp32 IEEE divide
+    codes = np.clip(np.rint(q), -127, 127).astype(np.int8)            # rint: ties to even
+    return codes, s
 
 
 def int4_decode(packed) -> np.ndarray:

@@ -137,3 +137,49 @@ def test_scale_granularity_ignored_is_caught(monkeypatch):
         return out
     monkeypatch.setattr(gemm_mod, "expand_scales", no_repeat)
     _fails(t_gemm.test_identity_dequantises_weight)
+
+
+import test_oracle_int8 as t_int8  # noqa: E402
+
+
+def test_int8_ties_away_from_zero_is_caught(monkeypatch):
+    def quant(x, gr, gc):
+        x32 = np.asarray(x, np.float32)
+        rows, cols = x32.shape
+        amax = quant_mod._block_amax(x32, gr, gc)
+        s = np.where(amax > 0, amax / np.float32(127), np.float32(1)).astype(np.float32)
+        q = (x32 / quant_mod._expand(s, gr, gc, rows, cols)).astype(np.float32)
+        r = np.sign(q) * np.floor(np.abs(q) + 0.5)                       # ties away from zero
+        return np.clip(r, -127, 127).astype(np.int8), s
+    monkeypatch.setattr(oracle, "int8_quant_groupwise", quant)
+    _fails(t_int8.test_int8_ties_round_to_even)
+
+
+def test_int8_scale_by_128_is_caught(monkeypatch):
+    def quant(x, gr, gc):
+        x32 = np.asarray(x, np.float32)
+        rows, cols = x32.shape
+        amax = quant_mod._block_amax(x32, gr, gc)
+        s = np.where(amax > 0, amax / np.float32(128), np.float32(1)).astype(np.float32)
+        q = (x32 / quant_mod._expand(s, gr, gc, rows, cols)).astype(np.float32)
+        return np.clip(np.rint(q), -127, 127).astype(np.int8), s
+    monkeypatch.setattr(oracle, "int8_quant_groupwise", quant)
+    _fails(t_int8.test_int8_power_of_two_roundtrip_is_exact)
+
+
+def test_int8_shifted_kblock_scale_is_caught(monkeypatch):
+    orig = gemm_mod.int8_gemm_groupwise
+
+    def gemm(xq, sx, gm, wq, sw, gn, bound=False):
+        return orig(xq, np.roll(np.asarray(sx), 1, axis=1), gm, wq, sw, gn, bound=bound)
+    monkeypatch.setattr(oracle, "int8_gemm_groupwise", gemm)
+    _fails(t_int8.test_int8_exact_rational_brute_force, 4, 2, 256, 1, 128)
+
+
+def test_int8_dropped_sign_is_caught(monkeypatch):
+    orig = gemm_mod.int8_gemm_groupwise
+
+    def gemm(xq, sx, gm, wq, sw, gn, bound=False):
+        return orig(np.abs(np.asarray(xq, np.int8).astype(np.int64)).astype(np.int8), sx, gm, wq, sw, gn, bound=bound)
+    monkeypatch.setattr(oracle, "int8_gemm_groupwise", gemm)
+    _fails(t_int8.test_int8_unit_scales_match_int64_matmul)

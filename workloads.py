@@ -91,6 +91,11 @@ def random_e4m3_codes(gen, shape) -> np.ndarray:
     return c.astype(np.uint8)
 
 
+def random_int8_codes(gen, shape) -> np.ndarray:
+    """Uniform random symmetric int8 codes in [-127, 127]."""
+    return gen.integers(-127, 128, size=shape, dtype=np.int64).astype(np.int8)
+
+
 def random_scales(gen, shape) -> np.ndarray:
     """Positive fp32 scales spread over a few binades."""
     return np.exp2(gen.uniform(-12.0, 2.0, size=shape)).astype(np.float32)
