@@ -187,6 +187,34 @@ def rows_report():
             out[f"decode_M{dm}_N{dn}_K{dk}_{form}"] = {"ms": ms, "GB/s": b / ms / 1e6,
                                                      "frac_hbm": b / ms / 1e6 / PEAK_HBM_GBS}
         del wsets
+    # next row: int8 x int8 2:4 GEMM, packed weight, 2048x4096x4096 and the M=16 decode shape
+    d = workloads.sparse_large(seed=3, m=m, n=n, k=k)
+    wv8, mt8 = sg.sparse24_prune_compress(torch.from_numpy(d["w"]).to(DEV))
+    wq8, sw8 = sg.int8_quant_groupwise(wv8, gr=128, gc=64)
+    wp8 = sg.sparse24_pack_gfx950(wq8, mt8)
+    xq8, sx8 = sg.int8_quant_groupwise(torch.from_numpy(d["x"]).to(DEV))
+    y = torch.empty((m, n), dtype=torch.bfloat16, device=DEV)
+    ms = time_fn(lambda i: sg.int8_sparse24_gemm_groupwise_packed(xq8, sx8, wp8, n, sw8, 1, 128, y=y))
+    out["next_int8_sparse_gemm_packed_2048x4096x4096_y"] = {
+        "ms": ms, "TOP/s": flops / ms / 1e9, "frac_int8_peak": flops / ms / 1e9 / PEAK_INT8_TOPS}
+    del wv8, mt8, wq8, wp8
+    dm, dn, dk = 16, 14336, 4096
+    wsets = []
+    for i in range(ROTATE_DECODE):
+        g = torch.Generator(device=DEV)
+        g.manual_seed(3000 + i)
+        wr = torch.randn((dn, dk), generator=g, device=DEV) * 0.02
+        v, mt = sg.sparse24_prune_compress(wr)
+        q8, s8 = sg.int8_quant_groupwise(v, gr=128, gc=64)
+        wsets.append((s8, sg.sparse24_pack_gfx950(q8, mt)))
+        del wr, v, mt, q8
+    xq16, sx16 = sg.int8_quant_groupwise(torch.from_numpy(workloads.decode(seed=4, m=dm, n=8, k=dk)["x"]).to(DEV))
+    y = torch.empty((dm, dn), dtype=torch.bfloat16, device=DEV)
+    ms = time_fn(lambda i: sg.int8_sparse24_gemm_groupwise_packed(
+        xq16, sx16, wsets[i % ROTATE_DECODE][1], dn, wsets[i % ROTATE_DECODE][0], 1, 128, y=y), reps=64, warm=16)
+    b = sparse_bytes(dm, dn, dk)
+    out[f"next_int8_decode_M{dm}_N{dn}_K{dk}_y"] = {"ms": ms, "GB/s": b / ms / 1e6, "frac_hbm": b / ms / 1e6 / PEAK_HBM_GBS}
+    del wsets
     # a7: fused int4 + bf16 add at L=2048, D1=4096, D2=64, D=4096
     dd = workloads.mixed_add(seed=5)
     x1, sx1 = sg.int4_quant_groupwise(torch.from_numpy(dd["x1"]).to(DEV))

@@ -227,15 +227,59 @@ sg_status sg_fp8_sparse24_gemm_groupwise_packed(int64_t M, int64_t N, int64_t K,
  *   w1 : [N, K1/2] packed int4, ld ldw1; sw1 (n, kb) at sw1[n * sw1_sn + kb * sw1_sk].
  *   x2 : [M, K2] bf16 bits, ld ldx2.   w2: [N, K2] bf16 bits, ld ldw2.
  *   y  : [M, N] bf16 (round to nearest even), ld ldy.
- * Requires K1 % 128 == 0, K1 > 0, K2 % 32 == 0, K2 >= 0; ldx1, ldw1 >= K1/2 and
- * multiples of 16; ldx2, ldw2 >= K2 with rows a multiple of 16 bytes; x1, w1, x2,
- * w2 16-byte aligned (x2, w2 may be NULL when K2 == 0); y 2-byte aligned.
+ * Requires K1 % 128 == 0, K1 > 0, K2 % 32 == 0, K2 >= 0; ldx1, ldw1 >= K1/2,
+ * multiples of 16 and below 2^23; ldx2, ldw2 >= K2, below 2^22, with rows a
+ * multiple of 16 bytes; x1, w1, x2, w2 16-byte aligned (x2, w2 may be NULL when
+ * K2 == 0); y 2-byte aligned; the scale arrays' byte extents below 2^31.
  */
 sg_status sg_mixed_gemm_add(int64_t M, int64_t N, int64_t K1, int64_t K2, const uint8_t* x1,
                             int64_t ldx1, const float* sx1, int64_t sx1_sm, int64_t sx1_sk,
                             const uint8_t* w1, int64_t ldw1, const float* sw1, int64_t sw1_sn,
                             int64_t sw1_sk, const uint16_t* x2, int64_t ldx2, const uint16_t* w2,
                             int64_t ldw2, uint16_t* y, int64_t ldy, hipStream_t stream);
+
+/*
+ * int8 x int8 2:4-sparse GEMM ([T3258], jcaip: the existing 2:4 kernels are
+ * int8 x int8 and fp8 x fp8).  The page fixes no int8 scheme; this one keeps
+ * the FP8 path's groupwise blocks and uses the symmetric int8 grid.
+ *
+ * sg_int8_quant_groupwise -- as sg_fp8_quant_groupwise (same arguments, blocks,
+ * layouts, requirements and errors) with int8 codes:
+ *   s = fl32(amax / 127) (1 when amax == 0); q = clamp(rint_even(fl32(v / s)), -127, 127).
+ */
+sg_status sg_int8_quant_groupwise(const void* x, sg_dtype x_dt, int64_t rows, int64_t cols,
+                                  int64_t ldx, int gr, int gc, int8_t* q, int64_t ldq, float* s,
+                                  int64_t s_stride_r, int64_t s_stride_c, hipStream_t stream);
+
+/*
+ * sg_int8_sparse24_gemm_groupwise -- as sg_fp8_sparse24_gemm_groupwise (same
+ * arguments, scale modes, output forms, requirements and errors) with int8
+ * codes for X and for the compressed W values (W pruned with
+ * sg_sparse24_prune_compress, then quantised with sg_int8_quant_groupwise at
+ * gr = 128, gc = 64):
+ *   y[m, n] = sum_kb sx[m / gran_m, kb] * sw[n / gran_n, kb] * P[m, n, kb],
+ *   P = the exact integer sum over the K block of x * w (int32 on the matrix core).
+ */
+sg_status sg_int8_sparse24_gemm_groupwise(int64_t M, int64_t N, int64_t K, const int8_t* xq,
+                                          int64_t ldx, const float* sx, int64_t sx_sm,
+                                          int64_t sx_sk, int gran_m, const int8_t* wv,
+                                          int64_t ldwv, const uint8_t* wmeta, int64_t ldwm,
+                                          const float* sw, int64_t sw_sn, int64_t sw_sk,
+                                          int gran_n, void* y, sg_dtype y_dt, int64_t ldy,
+                                          sg_form form, hipStream_t stream);
+
+/*
+ * sg_int8_sparse24_gemm_groupwise_packed -- the same with the weight in the
+ * packed form of sg_sparse24_pack_gfx950 (which moves bytes and so packs int8
+ * codes as it packs e4m3 codes); arguments as
+ * sg_fp8_sparse24_gemm_groupwise_packed.
+ */
+sg_status sg_int8_sparse24_gemm_groupwise_packed(int64_t M, int64_t N, int64_t K, const int8_t* xq,
+                                                 int64_t ldx, const float* sx, int64_t sx_sm,
+                                                 int64_t sx_sk, int gran_m, const uint8_t* wpacked,
+                                                 const float* sw, int64_t sw_sn, int64_t sw_sk,
+                                                 int gran_n, void* y, sg_dtype y_dt, int64_t ldy,
+                                                 sg_form form, hipStream_t stream);
 
 #ifdef __cplusplus
 }

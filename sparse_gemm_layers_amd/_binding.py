@@ -37,6 +37,11 @@ _SIGS = {
                                                _i64, _i64, _int, _ptr, _int, _i64, _int, _ptr], _int),
     "sg_mixed_gemm_add": ([_i64, _i64, _i64, _i64, _ptr, _i64, _ptr, _i64, _i64, _ptr, _i64, _ptr, _i64, _i64,
                            _ptr, _i64, _ptr, _i64, _ptr, _i64, _ptr], _int),
+    "sg_int8_quant_groupwise": ([_ptr, _int, _i64, _i64, _i64, _int, _int, _ptr, _i64, _ptr, _i64, _i64, _ptr], _int),
+    "sg_int8_sparse24_gemm_groupwise": ([_i64, _i64, _i64, _ptr, _i64, _ptr, _i64, _i64, _int, _ptr, _i64, _ptr,
+                                         _i64, _ptr, _i64, _i64, _int, _ptr, _int, _i64, _int, _ptr], _int),
+    "sg_int8_sparse24_gemm_groupwise_packed": ([_i64, _i64, _i64, _ptr, _i64, _ptr, _i64, _i64, _int, _ptr, _ptr,
+                                                _i64, _i64, _int, _ptr, _int, _i64, _int, _ptr], _int),
     "sg_probe_matrix_ops": ([_int, _int], _i64),
     "sg_probe_matrix_rate": ([_int, _int, _ptr, _ptr, _ptr], _int),
 }
@@ -114,6 +119,22 @@ def fp8_quant_groupwise(x, gr: int = 1, gc: int = 128, q=None, s=None):
     st = lib().sg_fp8_quant_groupwise(_p(x), _dtype_code(x, "x"), rows, cols, _row_stride(x), gr, gc,
                                       _p(q), _row_stride(q), _p(s), s.stride(0), s.stride(1), _stream(x))
     _check(st, "sg_fp8_quant_groupwise")
+    return q, s
+
+
+def int8_quant_groupwise(x, gr: int = 1, gc: int = 128, q=None, s=None):
+    """x [rows, cols] float32/bfloat16 -> (codes int8 [rows, cols], scales fp32
+    [ceil(rows/gr), cols/gc]).  One scale per gr x gc block: amax / 127."""
+    _gpu2d(x, "x")
+    rows, cols = x.shape
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.int8, device=x.device)
+    if s is None:
+        s = _scales(-(-rows // gr), cols // gc if gc else 0, x.device)
+    _gpu2d(q, "q")
+    st = lib().sg_int8_quant_groupwise(_p(x), _dtype_code(x, "x"), rows, cols, _row_stride(x), gr, gc,
+                                       _p(q), _row_stride(q), _p(s), s.stride(0), s.stride(1), _stream(x))
+    _check(st, "sg_int8_quant_groupwise")
     return q, s
 
 
@@ -226,6 +247,41 @@ def fp8_sparse24_gemm_groupwise_packed(xq, sx, wpacked, n: int, sw, gran_m: int 
                                                      sw.stride(1), gran_n, _p(y), ydt, _row_stride(y), f,
                                                      _stream(xq))
     _check(st, "sg_fp8_sparse24_gemm_groupwise_packed")
+    return y
+
+
+def int8_sparse24_gemm_groupwise(xq, sx, wv, wmeta, sw, gran_m: int = 1, gran_n: int = 128,
+                                 out_dtype=torch.bfloat16, form: str = "y", y=None):
+    """The 2:4-sparse GEMM with int8 codes: xq int8 [M, K], wv int8 [N, K/2],
+    metadata wmeta uint8 [N, K/8]; scales as for the FP8 GEMM."""
+    _gpu2d(xq, "xq")
+    _gpu2d(wv, "wv")
+    _gpu2d(wmeta, "wmeta")
+    M, K = xq.shape
+    N = wv.shape[0]
+    y, f, ydt = _out(y, M, N, out_dtype, form, xq.device)
+    st = lib().sg_int8_sparse24_gemm_groupwise(M, N, K, _p(xq), _row_stride(xq), _p(sx), sx.stride(0),
+                                               sx.stride(1), gran_m, _p(wv), _row_stride(wv), _p(wmeta),
+                                               _row_stride(wmeta), _p(sw), sw.stride(0), sw.stride(1), gran_n,
+                                               _p(y), ydt, _row_stride(y), f, _stream(xq))
+    _check(st, "sg_int8_sparse24_gemm_groupwise")
+    return y
+
+
+def int8_sparse24_gemm_groupwise_packed(xq, sx, wpacked, n: int, sw, gran_m: int = 1, gran_n: int = 128,
+                                        out_dtype=torch.bfloat16, form: str = "y", y=None):
+    """2:4-sparse int8 GEMM with the weight in the gfx950 packed form (N rows;
+    sparse24_pack_gfx950 packs int8 codes as it packs e4m3 codes)."""
+    _gpu2d(xq, "xq")
+    M, K = xq.shape
+    if not wpacked.is_cuda or wpacked.numel() < sparse24_packed_bytes(n, K):
+        raise SgError("wpacked too small or not on the GPU")
+    y, f, ydt = _out(y, M, n, out_dtype, form, xq.device)
+    st = lib().sg_int8_sparse24_gemm_groupwise_packed(M, n, K, _p(xq), _row_stride(xq), _p(sx), sx.stride(0),
+                                                      sx.stride(1), gran_m, _p(wpacked), _p(sw), sw.stride(0),
+                                                      sw.stride(1), gran_n, _p(y), ydt, _row_stride(y), f,
+                                                      _stream(xq))
+    _check(st, "sg_int8_sparse24_gemm_groupwise_packed")
     return y
 
 

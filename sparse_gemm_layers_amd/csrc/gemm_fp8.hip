@@ -61,9 +61,19 @@ __device__ __forceinline__ v4f mma_dense(const v8i& a, const v8i& b) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 0, 0, 0, 0, 0, 0);
 }
 
+// The partial of one 16 x 16 x 128 block of a 2:4-sparse A (W) and dense B
+// (X), from zero: e4m3 operands (fp32 result), or int8 operands (the exact
+// int32 sum, converted to fp32 exactly: |P| <= 64 * 127^2 < 2^24).
+template <bool I8>
 __device__ __forceinline__ v4f mma_sparse(const v4i& a, const v8i& b, int idx) {
-  v4f p = {0.f, 0.f, 0.f, 0.f};
-  return __builtin_amdgcn_smfmac_f32_16x16x128_fp8_fp8(a, b, p, idx, 0, 0);
+  if constexpr (I8) {
+    const v4i z = {0, 0, 0, 0};
+    const v4i p = __builtin_amdgcn_smfmac_i32_16x16x128_i8(a, b, z, idx, 0, 0);
+    return (v4f){(float)p[0], (float)p[1], (float)p[2], (float)p[3]};
+  } else {
+    v4f p = {0.f, 0.f, 0.f, 0.f};
+    return __builtin_amdgcn_smfmac_f32_16x16x128_fp8_fp8(a, b, p, idx, 0, 0);
+  }
 }
 
 
@@ -147,7 +157,7 @@ __device__ __forceinline__ T lds_ld(const uint8_t* st, uint32_t off) {
 }
 
 // Multiplies one sparse LDS stage into the wave's 8 x 4 sub-tiles and promotes.
-template <int GRAN_N, bool PACKED>
+template <int GRAN_N, bool PACKED, bool I8>
 __device__ __forceinline__ void compute_stage(const uint8_t* st, v4f (&acc)[8][4], const LaneOffsets& o,
                                               int wn, int g, uint32_t msel) {
   using L = Stage<true>;
@@ -179,7 +189,7 @@ __device__ __forceinline__ void compute_stage(const uint8_t* st, v4f (&acc)[8][4
       const int idx = lds_ld<int>(st, o.mt + i * 256);
       const v4i aa = {(int)av.x, (int)av.y, (int)av.z, (int)av.w};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) p[j] = mma_sparse(aa, bx[j], idx);
+      for (int j = 0; j < 4; ++j) p[j] = mma_sparse<I8>(aa, bx[j], idx);
     } else {
       const uint2 v0 = lds_ld<uint2>(st, o.w0 + i * 1024);
       const uint2 v1 = lds_ld<uint2>(st, o.w1 + i * 1024);
@@ -187,7 +197,7 @@ __device__ __forceinline__ void compute_stage(const uint8_t* st, v4f (&acc)[8][4
       const int idx = (int)__builtin_amdgcn_perm(mw.y, mw.x, msel);
       const v4i aa = {(int)v0.x, (int)v0.y, (int)v1.x, (int)v1.y};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) p[j] = mma_sparse(aa, bx[j], idx);
+      for (int j = 0; j < 4; ++j) p[j] = mma_sparse<I8>(aa, bx[j], idx);
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -319,7 +329,7 @@ __device__ __forceinline__ void issue_double(uint8_t* st, const PlanX2& p, __amd
 }
 #endif  // SG_DEVICE_PASS
 
-template <bool PACKED, int GRAN_N, bool OUT_BF16, bool OUT_T>
+template <bool I8, bool PACKED, int GRAN_N, bool OUT_BF16, bool OUT_T>
 __global__ void __launch_bounds__(512) k_gemm_sparse_x2(GemmArgs a, int tiles_m, int tiles_n) {
 #if SG_DEVICE_PASS
   __shared__ __attribute__((aligned(1024))) uint8_t db0[x2::DBL];
@@ -370,7 +380,7 @@ __global__ void __launch_bounds__(512) k_gemm_sparse_x2(GemmArgs a, int tiles_m,
         if (it + 1 < NIT)
           issue_double<PACKED>(u == 0 ? db1 : db0, plan, rx, rw, rm, rsx, rsw, a, 2 * (it + 1), KB, wave);
         if (2 * it + q < KB)
-          compute_stage<GRAN_N, PACKED>((u == 0 ? db0 : db1) + qoff, acc, lo, wn, g, msel);
+          compute_stage<GRAN_N, PACKED, I8>((u == 0 ? db0 : db1) + qoff, acc, lo, wn, g, msel);
       }
     }
   }
@@ -802,19 +812,19 @@ __device__ __forceinline__ void dec_load(const GemmArgs& a, const DecRes& res, i
 }
 #endif  // SG_DEVICE_PASS
 
-template <bool SPARSE, int RB, int MT>
+template <bool SPARSE, bool I8, int RB, int MT>
 __device__ __forceinline__ void dec_compute(const DecOps<RB, MT>& o, v4f (&acc)[RB][MT]) {
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int j = 0; j < MT; ++j) {
-      const v4f p = SPARSE ? mma_sparse(o.asp[rb], o.bx[j], o.idx[rb]) : mma_dense(o.ad[rb], o.bx[j]);
+      const v4f p = SPARSE ? mma_sparse<I8>(o.asp[rb], o.bx[j], o.idx[rb]) : mma_dense(o.ad[rb], o.bx[j]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[rb][j][e] = fmaf(p[e] * o.sw4[rb][e], o.sxv[j], acc[rb][j][e]);
     }
 }
 
-template <bool SPARSE, bool PACKED, int RB, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
+template <bool SPARSE, bool I8, bool PACKED, int RB, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
 __global__ void __launch_bounds__(512) k_gemm_decode(GemmArgs a) {
   constexpr int U = DEC_U;
   __shared__ __attribute__((aligned(16))) float red[DEC_WAVES][RB * MT][64][4];
@@ -853,7 +863,7 @@ __global__ void __launch_bounds__(512) k_gemm_decode(GemmArgs a) {
   auto compute_batch = [&](const DecOps<RB, MT>(&o)[U], int t0) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      if (t0 + u < nt) dec_compute<SPARSE, RB, MT>(o[u], acc);
+      if (t0 + u < nt) dec_compute<SPARSE, I8, RB, MT>(o[u], acc);
   };
   for (int t0 = 0; t0 < nt; t0 += U) {
     load_batch(ops, t0);
@@ -947,7 +957,7 @@ __device__ __forceinline__ void dma_issue(uint8_t* slot, const GemmArgs& a, __am
 }
 #endif
 
-template <int RB, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
+template <bool I8, int RB, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
 __global__ void __launch_bounds__(512) k_gemm_decode_dma(GemmArgs a) {
 #if SG_DEVICE_PASS
   using C = DmaCfg<RB, MT>;
@@ -1024,7 +1034,7 @@ __global__ void __launch_bounds__(512) k_gemm_decode_dma(GemmArgs a) {
           const v4i aa = {(int)av.x, (int)av.y, (int)av.z, (int)av.w};
 #pragma unroll
           for (int j = 0; j < MT; ++j) {
-            const v4f p = mma_sparse(aa, bx[j], idx);
+            const v4f p = mma_sparse<I8>(aa, bx[j], idx);
             acc[rb][j] += p * (swv * sxv[j]);
           }
         }
@@ -1070,11 +1080,11 @@ __global__ void __launch_bounds__(512) k_gemm_decode_dma(GemmArgs a) {
 
 // ------------------------------------------------------------------ dispatch
 
-template <bool SPARSE, bool PACKED, int GRAN_N, bool OUT_BF16, bool OUT_T>
+template <bool SPARSE, bool I8, bool PACKED, int GRAN_N, bool OUT_BF16, bool OUT_T>
 static void launch_large(const GemmArgs& a, hipStream_t st) {
   const int tm = (int)cdiv(a.M, BM), tn = (int)cdiv(a.N, BN);
   if (SPARSE)
-    k_gemm_sparse_x2<PACKED, GRAN_N, OUT_BF16, OUT_T><<<tm * tn, 512, 0, st>>>(a, tm, tn);
+    k_gemm_sparse_x2<I8, PACKED, GRAN_N, OUT_BF16, OUT_T><<<tm * tn, 512, 0, st>>>(a, tm, tn);
   else
     k_gemm_dense8<GRAN_N, OUT_BF16, OUT_T><<<tm * tn, 512, 0, st>>>(a, tm, tn);
 }
@@ -1082,11 +1092,11 @@ static void launch_large(const GemmArgs& a, hipStream_t st) {
 // Launches the LDS-streaming decode kernel with RB row blocks per workgroup if
 // its ring fits LDS and the grid keeps at least 224 workgroups (7/8 of the
 // CUs busy; RB = 1 always qualifies).
-template <int RB, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
+template <bool I8, int RB, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
 static bool try_decode_dma(const GemmArgs& a, hipStream_t st, int64_t rows16) {
   if constexpr (DmaCfg<RB, MT>::FITS) {
     if (RB == 1 || rows16 >= RB * 224) {
-      k_gemm_decode_dma<RB, MT, GRAN_N, OUT_BF16, OUT_T><<<(unsigned)cdiv(rows16, RB), 512, 0, st>>>(a);
+      k_gemm_decode_dma<I8, RB, MT, GRAN_N, OUT_BF16, OUT_T><<<(unsigned)cdiv(rows16, RB), 512, 0, st>>>(a);
       return true;
     }
   }
@@ -1097,55 +1107,55 @@ static bool try_decode_dma(const GemmArgs& a, hipStream_t st, int64_t rows16) {
 // workgroups and whose operands fit (LDS ring of the streaming kernel, or
 // RB * MT <= 4 for the registers of k_gemm_decode).  Packed 2:4 weights with
 // 128-row W scales take the LDS-streaming kernel when one of its rings fits.
-template <bool SPARSE, bool PACKED, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
+template <bool SPARSE, bool I8, bool PACKED, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
 static void launch_decode_mt(const GemmArgs& a, hipStream_t st) {
   const int64_t rows16 = cdiv(a.N, 16);
   if constexpr (SPARSE && PACKED && GRAN_N == 128 && DmaCfg<1, MT>::FITS) {
-    if (try_decode_dma<4, MT, GRAN_N, OUT_BF16, OUT_T>(a, st, rows16) ||
-        try_decode_dma<2, MT, GRAN_N, OUT_BF16, OUT_T>(a, st, rows16) ||
-        try_decode_dma<1, MT, GRAN_N, OUT_BF16, OUT_T>(a, st, rows16))
+    if (try_decode_dma<I8, 4, MT, GRAN_N, OUT_BF16, OUT_T>(a, st, rows16) ||
+        try_decode_dma<I8, 2, MT, GRAN_N, OUT_BF16, OUT_T>(a, st, rows16) ||
+        try_decode_dma<I8, 1, MT, GRAN_N, OUT_BF16, OUT_T>(a, st, rows16))
       return;
   }
   constexpr int RB4 = MT == 1 ? 4 : 1, RB2 = MT <= 2 ? 2 : 1;
   if (RB4 == 4 && rows16 >= 4 * 224)
-    k_gemm_decode<SPARSE, PACKED, RB4, MT, GRAN_N, OUT_BF16, OUT_T><<<(unsigned)cdiv(rows16, RB4), 512, 0, st>>>(a);
+    k_gemm_decode<SPARSE, I8, PACKED, RB4, MT, GRAN_N, OUT_BF16, OUT_T><<<(unsigned)cdiv(rows16, RB4), 512, 0, st>>>(a);
   else if (RB2 == 2 && rows16 >= 2 * 224)
-    k_gemm_decode<SPARSE, PACKED, RB2, MT, GRAN_N, OUT_BF16, OUT_T><<<(unsigned)cdiv(rows16, RB2), 512, 0, st>>>(a);
+    k_gemm_decode<SPARSE, I8, PACKED, RB2, MT, GRAN_N, OUT_BF16, OUT_T><<<(unsigned)cdiv(rows16, RB2), 512, 0, st>>>(a);
   else
-    k_gemm_decode<SPARSE, PACKED, 1, MT, GRAN_N, OUT_BF16, OUT_T><<<(unsigned)rows16, 512, 0, st>>>(a);
+    k_gemm_decode<SPARSE, I8, PACKED, 1, MT, GRAN_N, OUT_BF16, OUT_T><<<(unsigned)rows16, 512, 0, st>>>(a);
 }
 
-template <bool SPARSE, bool PACKED, int GRAN_N, bool OUT_BF16, bool OUT_T>
+template <bool SPARSE, bool I8, bool PACKED, int GRAN_N, bool OUT_BF16, bool OUT_T>
 static void launch_shape(const GemmArgs& a, hipStream_t st) {
   if (a.M <= 16)
-    launch_decode_mt<SPARSE, PACKED, 1, GRAN_N, OUT_BF16, OUT_T>(a, st);
+    launch_decode_mt<SPARSE, I8, PACKED, 1, GRAN_N, OUT_BF16, OUT_T>(a, st);
   else if (a.M <= 32)
-    launch_decode_mt<SPARSE, PACKED, 2, GRAN_N, OUT_BF16, OUT_T>(a, st);
+    launch_decode_mt<SPARSE, I8, PACKED, 2, GRAN_N, OUT_BF16, OUT_T>(a, st);
   else if (a.M <= 48)
-    launch_decode_mt<SPARSE, PACKED, 3, GRAN_N, OUT_BF16, OUT_T>(a, st);
+    launch_decode_mt<SPARSE, I8, PACKED, 3, GRAN_N, OUT_BF16, OUT_T>(a, st);
   else if (a.M <= 64)
-    launch_decode_mt<SPARSE, PACKED, 4, GRAN_N, OUT_BF16, OUT_T>(a, st);
+    launch_decode_mt<SPARSE, I8, PACKED, 4, GRAN_N, OUT_BF16, OUT_T>(a, st);
   else
-    launch_large<SPARSE, PACKED, GRAN_N, OUT_BF16, OUT_T>(a, st);
+    launch_large<SPARSE, I8, PACKED, GRAN_N, OUT_BF16, OUT_T>(a, st);
 }
 
-template <bool SPARSE, bool PACKED>
+template <bool SPARSE, bool PACKED, bool I8 = false>
 static void launch_gemm(const GemmArgs& a, int gran_n, bool bf16, bool yt, hipStream_t st) {
   if (gran_n == 128) {
     if (bf16) {
-      if (yt) launch_shape<SPARSE, PACKED, 128, true, true>(a, st);
-      else launch_shape<SPARSE, PACKED, 128, true, false>(a, st);
+      if (yt) launch_shape<SPARSE, I8, PACKED, 128, true, true>(a, st);
+      else launch_shape<SPARSE, I8, PACKED, 128, true, false>(a, st);
     } else {
-      if (yt) launch_shape<SPARSE, PACKED, 128, false, true>(a, st);
-      else launch_shape<SPARSE, PACKED, 128, false, false>(a, st);
+      if (yt) launch_shape<SPARSE, I8, PACKED, 128, false, true>(a, st);
+      else launch_shape<SPARSE, I8, PACKED, 128, false, false>(a, st);
     }
   } else {
     if (bf16) {
-      if (yt) launch_shape<SPARSE, PACKED, 1, true, true>(a, st);
-      else launch_shape<SPARSE, PACKED, 1, true, false>(a, st);
+      if (yt) launch_shape<SPARSE, I8, PACKED, 1, true, true>(a, st);
+      else launch_shape<SPARSE, I8, PACKED, 1, true, false>(a, st);
     } else {
-      if (yt) launch_shape<SPARSE, PACKED, 1, false, true>(a, st);
-      else launch_shape<SPARSE, PACKED, 1, false, false>(a, st);
+      if (yt) launch_shape<SPARSE, I8, PACKED, 1, false, true>(a, st);
+      else launch_shape<SPARSE, I8, PACKED, 1, false, false>(a, st);
     }
   }
 }
@@ -1211,13 +1221,13 @@ extern "C" sg_status sg_fp8_gemm_groupwise(int64_t M, int64_t N, int64_t K, cons
   return launch_status();
 }
 
-extern "C" sg_status sg_fp8_sparse24_gemm_groupwise(int64_t M, int64_t N, int64_t K, const uint8_t* xq,
-                                                    int64_t ldx, const float* sx, int64_t sx_sm,
-                                                    int64_t sx_sk, int gran_m, const uint8_t* wv,
-                                                    int64_t ldwv, const uint8_t* wmeta, int64_t ldwm,
-                                                    const float* sw, int64_t sw_sn, int64_t sw_sk,
-                                                    int gran_n, void* y, sg_dtype y_dt, int64_t ldy,
-                                                    sg_form form, hipStream_t stream) {
+// The 2:4 GEMM entry points: FP8 (e4m3) or int8 codes, canonical (values +
+// metadata) or gfx950-packed weights.
+template <bool I8>
+static sg_status sparse24_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* xq, int64_t ldx, const float* sx,
+                               int64_t sx_sm, int64_t sx_sk, int gran_m, const uint8_t* wv, int64_t ldwv,
+                               const uint8_t* wmeta, int64_t ldwm, const float* sw, int64_t sw_sn, int64_t sw_sk,
+                               int gran_n, void* y, sg_dtype y_dt, int64_t ldy, sg_form form, hipStream_t stream) {
   sg_status st = check_common(M, N, K, xq, ldx, sx, sx_sm, sx_sk, gran_m, sw, sw_sn, sw_sk, gran_n, y, y_dt, ldy, form);
   if (st != SG_OK) return st;
   if (!wv || !wmeta) return SG_ERR_NULL;
@@ -1227,16 +1237,16 @@ extern "C" sg_status sg_fp8_sparse24_gemm_groupwise(int64_t M, int64_t N, int64_
   const GemmArgs a = make_args(M, N, K, xq, ldx, sx, sx_sm, sx_sk, gran_m, wv, ldwv, wmeta, ldwm, sw, sw_sn,
                                sw_sk, gran_n, y, y_dt, ldy);
   clear_hip_error();
-  launch_gemm<true, false>(a, gran_n, y_dt == SG_BF16, form == SG_OUT_YT, stream);
+  launch_gemm<true, false, I8>(a, gran_n, y_dt == SG_BF16, form == SG_OUT_YT, stream);
   return launch_status();
 }
 
-extern "C" sg_status sg_fp8_sparse24_gemm_groupwise_packed(int64_t M, int64_t N, int64_t K, const uint8_t* xq,
-                                                           int64_t ldx, const float* sx, int64_t sx_sm,
-                                                           int64_t sx_sk, int gran_m, const uint8_t* wpacked,
-                                                           const float* sw, int64_t sw_sn, int64_t sw_sk,
-                                                           int gran_n, void* y, sg_dtype y_dt, int64_t ldy,
-                                                           sg_form form, hipStream_t stream) {
+template <bool I8>
+static sg_status sparse24_gemm_packed(int64_t M, int64_t N, int64_t K, const uint8_t* xq, int64_t ldx,
+                                      const float* sx, int64_t sx_sm, int64_t sx_sk, int gran_m,
+                                      const uint8_t* wpacked, const float* sw, int64_t sw_sn, int64_t sw_sk,
+                                      int gran_n, void* y, sg_dtype y_dt, int64_t ldy, sg_form form,
+                                      hipStream_t stream) {
   sg_status st = check_common(M, N, K, xq, ldx, sx, sx_sm, sx_sk, gran_m, sw, sw_sn, sw_sk, gran_n, y, y_dt, ldy, form);
   if (st != SG_OK) return st;
   if (!wpacked) return SG_ERR_NULL;
@@ -1247,6 +1257,49 @@ extern "C" sg_status sg_fp8_sparse24_gemm_groupwise_packed(int64_t M, int64_t N,
   const GemmArgs a = make_args(M, N, K, xq, ldx, sx, sx_sm, sx_sk, gran_m, wpacked, 0, nullptr, 0, sw, sw_sn,
                                sw_sk, gran_n, y, y_dt, ldy);
   clear_hip_error();
-  launch_gemm<true, true>(a, gran_n, y_dt == SG_BF16, form == SG_OUT_YT, stream);
+  launch_gemm<true, true, I8>(a, gran_n, y_dt == SG_BF16, form == SG_OUT_YT, stream);
   return launch_status();
+}
+
+extern "C" sg_status sg_fp8_sparse24_gemm_groupwise(int64_t M, int64_t N, int64_t K, const uint8_t* xq,
+                                                    int64_t ldx, const float* sx, int64_t sx_sm,
+                                                    int64_t sx_sk, int gran_m, const uint8_t* wv,
+                                                    int64_t ldwv, const uint8_t* wmeta, int64_t ldwm,
+                                                    const float* sw, int64_t sw_sn, int64_t sw_sk,
+                                                    int gran_n, void* y, sg_dtype y_dt, int64_t ldy,
+                                                    sg_form form, hipStream_t stream) {
+  return sparse24_gemm<false>(M, N, K, xq, ldx, sx, sx_sm, sx_sk, gran_m, wv, ldwv, wmeta, ldwm, sw, sw_sn, sw_sk,
+                              gran_n, y, y_dt, ldy, form, stream);
+}
+
+extern "C" sg_status sg_fp8_sparse24_gemm_groupwise_packed(int64_t M, int64_t N, int64_t K, const uint8_t* xq,
+                                                           int64_t ldx, const float* sx, int64_t sx_sm,
+                                                           int64_t sx_sk, int gran_m, const uint8_t* wpacked,
+                                                           const float* sw, int64_t sw_sn, int64_t sw_sk,
+                                                           int gran_n, void* y, sg_dtype y_dt, int64_t ldy,
+                                                           sg_form form, hipStream_t stream) {
+  return sparse24_gemm_packed<false>(M, N, K, xq, ldx, sx, sx_sm, sx_sk, gran_m, wpacked, sw, sw_sn, sw_sk, gran_n,
+                                     y, y_dt, ldy, form, stream);
+}
+
+extern "C" sg_status sg_int8_sparse24_gemm_groupwise(int64_t M, int64_t N, int64_t K, const int8_t* xq,
+                                                     int64_t ldx, const float* sx, int64_t sx_sm,
+                                                     int64_t sx_sk, int gran_m, const int8_t* wv,
+                                                     int64_t ldwv, const uint8_t* wmeta, int64_t ldwm,
+                                                     const float* sw, int64_t sw_sn, int64_t sw_sk,
+                                                     int gran_n, void* y, sg_dtype y_dt, int64_t ldy,
+                                                     sg_form form, hipStream_t stream) {
+  return sparse24_gemm<true>(M, N, K, reinterpret_cast<const uint8_t*>(xq), ldx, sx, sx_sm, sx_sk, gran_m,
+                             reinterpret_cast<const uint8_t*>(wv), ldwv, wmeta, ldwm, sw, sw_sn, sw_sk, gran_n, y,
+                             y_dt, ldy, form, stream);
+}
+
+extern "C" sg_status sg_int8_sparse24_gemm_groupwise_packed(int64_t M, int64_t N, int64_t K, const int8_t* xq,
+                                                            int64_t ldx, const float* sx, int64_t sx_sm,
+                                                            int64_t sx_sk, int gran_m, const uint8_t* wpacked,
+                                                            const float* sw, int64_t sw_sn, int64_t sw_sk,
+                                                            int gran_n, void* y, sg_dtype y_dt, int64_t ldy,
+                                                            sg_form form, hipStream_t stream) {
+  return sparse24_gemm_packed<true>(M, N, K, reinterpret_cast<const uint8_t*>(xq), ldx, sx, sx_sm, sx_sk, gran_m,
+                                    wpacked, sw, sw_sn, sw_sk, gran_n, y, y_dt, ldy, form, stream);
 }

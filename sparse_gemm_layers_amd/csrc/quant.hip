@@ -1,5 +1,5 @@
-// Groupwise quantisers: fp32/bf16 -> e4m3 codes + one fp32 scale per block
-// (1 x gc or 128 x gc), and fp32/bf16 -> packed int4 + one scale per
+// Groupwise quantisers: fp32/bf16 -> e4m3 or int8 codes + one fp32 scale per
+// block (1 x gc or 128 x gc), and fp32/bf16 -> packed int4 + one scale per
 // (row, 128 columns).  Both are HBM-bound streaming kernels: every input
 // byte is read once with 16- or 8-byte loads, codes are written once with
 // 4- or 2-byte stores per lane, scales once per block.
@@ -8,15 +8,25 @@
 // Groupwise scaling along M for FP8 gemm" (hwu36's comment on the
 // ScaleGranularityM/N modes) and torchao PR #3258 "Introduce new W8A8-FP-CSR
 // quantization API" (jcaip's review: positive scales, all-zero input allowed,
-// scale then cast to float8_e4m3fn).
+// scale then cast to float8_e4m3fn).  int8 (for the int8 x int8 2:4 GEMM the
+// same torchao page names): s = amax / 127, codes rint-even clamped to +-127.
 #include "common.h"
 
 namespace sg {
 
+enum QuantMode { Q_FP8 = 0, Q_INT4 = 1, Q_INT8 = 2 };
+
+// int8 code of v / sc as a byte (two's complement), rounding half to even.
+__device__ __forceinline__ uint32_t int8_encode(float v, float sc) {
+  float t = __builtin_rintf(v / sc);                             // IEEE divide, half to even
+  t = fminf(fmaxf(t, -127.0f), 127.0f);
+  return (uint32_t)(int)t & 0xffu;
+}
+
 // ------------------------------------------------------------------ 1 x GC
 // LPB = GC/4 lanes share one block, 4 consecutive elements per lane; a wave
 // covers 64/LPB blocks per iteration of a grid-stride loop.
-template <typename TIn, int GC, bool INT4>
+template <typename TIn, int GC, int MODE>
 __global__ void __launch_bounds__(256) k_quant_rowblock(const TIn* __restrict__ x, int64_t rows,
                                                         int64_t cols, int64_t ldx,
                                                         uint8_t* __restrict__ q, int64_t ldq,
@@ -40,11 +50,12 @@ __global__ void __launch_bounds__(256) k_quant_rowblock(const TIn* __restrict__ 
     if (valid) load4(x + r * ldx + cb * GC + li * 4, v);
     float a = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
     a = group_max<LPB>(a);
-    if (!INT4) {
-      const float sc = a > 0.f ? a / 448.0f : 1.0f;             // IEEE divide
+    if (MODE == Q_FP8 || MODE == Q_INT8) {
+      const float sc = a > 0.f ? a / (MODE == Q_FP8 ? 448.0f : 127.0f) : 1.0f;   // IEEE divide
       uint32_t packed = 0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) packed |= e4m3_encode(v[i] / sc) << (8 * i);
+      for (int i = 0; i < 4; ++i)
+        packed |= (MODE == Q_FP8 ? e4m3_encode(v[i] / sc) : int8_encode(v[i], sc)) << (8 * i);
       if (valid) {
         *reinterpret_cast<uint32_t*>(q + r * ldq + cb * GC + li * 4) = packed;
         if (li == 0) s[r * ssr + cb * ssc] = sc;
@@ -70,7 +81,7 @@ __global__ void __launch_bounds__(256) k_quant_rowblock(const TIn* __restrict__ 
 // One 256-thread workgroup per block.  LPR = GC/4 lanes cover one row of the
 // block; each thread keeps its STEPS x 4 inputs in registers between the amax
 // reduction and the encode, so the block is read from HBM once.
-template <typename TIn, int GC>
+template <typename TIn, int GC, int MODE>
 __global__ void __launch_bounds__(256) k_quant_block128(const TIn* __restrict__ x, int64_t rows,
                                                         int64_t ldx, uint8_t* __restrict__ q,
                                                         int64_t ldq, float* __restrict__ s,
@@ -98,36 +109,36 @@ __global__ void __launch_bounds__(256) k_quant_block128(const TIn* __restrict__ 
   if ((t & 63) == 0) red[t >> 6] = a;
   __syncthreads();
   a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const float sc = a > 0.f ? a / 448.0f : 1.0f;
+  const float sc = a > 0.f ? a / (MODE == Q_FP8 ? 448.0f : 127.0f) : 1.0f;
 #pragma unroll
   for (int st = 0; st < STEPS; ++st) {
     const int64_t r = rb * 128 + st * RPS + lr;
     uint32_t packed = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) packed |= e4m3_encode(v[st][i] / sc) << (8 * i);
+    for (int i = 0; i < 4; ++i)
+      packed |= (MODE == Q_FP8 ? e4m3_encode(v[st][i] / sc) : int8_encode(v[st][i], sc)) << (8 * i);
     if (r < rows) *reinterpret_cast<uint32_t*>(q + r * ldq + cb * GC + li * 4) = packed;
   }
   if (t == 0) s[rb * ssr + cb * ssc] = sc;
 }
 
-template <typename TIn>
-static void launch_fp8_quant(const TIn* x, int64_t rows, int64_t cols, int64_t ldx, int gr, int gc,
-                             uint8_t* q, int64_t ldq, float* s, int64_t ssr, int64_t ssc,
-                             hipStream_t st) {
+template <typename TIn, int MODE>
+static void launch_quant(const TIn* x, int64_t rows, int64_t cols, int64_t ldx, int gr, int gc,
+                         uint8_t* q, int64_t ldq, float* s, int64_t ssr, int64_t ssc, hipStream_t st) {
   if (gr == 1) {
     const int64_t blocks = rows * (cols / gc);
     const int per_wg = 4 * (64 / (gc / 4));
     const unsigned g = grid_for(blocks, per_wg);
     if (gc == 128)
-      k_quant_rowblock<TIn, 128, false><<<g, 256, 0, st>>>(x, rows, cols, ldx, q, ldq, s, ssr, ssc);
+      k_quant_rowblock<TIn, 128, MODE><<<g, 256, 0, st>>>(x, rows, cols, ldx, q, ldq, s, ssr, ssc);
     else
-      k_quant_rowblock<TIn, 64, false><<<g, 256, 0, st>>>(x, rows, cols, ldx, q, ldq, s, ssr, ssc);
+      k_quant_rowblock<TIn, 64, MODE><<<g, 256, 0, st>>>(x, rows, cols, ldx, q, ldq, s, ssr, ssc);
   } else {
     const dim3 grid((unsigned)(cols / gc), (unsigned)cdiv(rows, 128));
     if (gc == 128)
-      k_quant_block128<TIn, 128><<<grid, 256, 0, st>>>(x, rows, ldx, q, ldq, s, ssr, ssc);
+      k_quant_block128<TIn, 128, MODE><<<grid, 256, 0, st>>>(x, rows, ldx, q, ldq, s, ssr, ssc);
     else
-      k_quant_block128<TIn, 64><<<grid, 256, 0, st>>>(x, rows, ldx, q, ldq, s, ssr, ssc);
+      k_quant_block128<TIn, 64, MODE><<<grid, 256, 0, st>>>(x, rows, ldx, q, ldq, s, ssr, ssc);
   }
 }
 
@@ -135,10 +146,10 @@ static void launch_fp8_quant(const TIn* x, int64_t rows, int64_t cols, int64_t l
 
 using namespace sg;
 
-extern "C" sg_status sg_fp8_quant_groupwise(const void* x, sg_dtype x_dt, int64_t rows,
-                                            int64_t cols, int64_t ldx, int gr, int gc, uint8_t* q,
-                                            int64_t ldq, float* s, int64_t s_stride_r,
-                                            int64_t s_stride_c, hipStream_t stream) {
+template <int MODE>
+static sg_status quant_groupwise(const void* x, sg_dtype x_dt, int64_t rows, int64_t cols, int64_t ldx, int gr,
+                                 int gc, uint8_t* q, int64_t ldq, float* s, int64_t s_stride_r, int64_t s_stride_c,
+                                 hipStream_t stream) {
   if (!x || !q || !s) return SG_ERR_NULL;
   if (x_dt != SG_F32 && x_dt != SG_BF16) return SG_ERR_UNSUPPORTED;
   if ((gr != 1 && gr != 128) || (gc != 128 && gc != 64)) return SG_ERR_UNSUPPORTED;
@@ -150,11 +161,26 @@ extern "C" sg_status sg_fp8_quant_groupwise(const void* x, sg_dtype x_dt, int64_
   if (rows == 0) return SG_OK;
   clear_hip_error();
   if (x_dt == SG_F32)
-    launch_fp8_quant((const float*)x, rows, cols, ldx, gr, gc, q, ldq, s, s_stride_r, s_stride_c, stream);
+    launch_quant<float, MODE>((const float*)x, rows, cols, ldx, gr, gc, q, ldq, s, s_stride_r, s_stride_c, stream);
   else
-    launch_fp8_quant((const uint16_t*)x, rows, cols, ldx, gr, gc, q, ldq, s, s_stride_r, s_stride_c,
-                     stream);
+    launch_quant<uint16_t, MODE>((const uint16_t*)x, rows, cols, ldx, gr, gc, q, ldq, s, s_stride_r, s_stride_c,
+                                 stream);
   return launch_status();
+}
+
+extern "C" sg_status sg_fp8_quant_groupwise(const void* x, sg_dtype x_dt, int64_t rows,
+                                            int64_t cols, int64_t ldx, int gr, int gc, uint8_t* q,
+                                            int64_t ldq, float* s, int64_t s_stride_r,
+                                            int64_t s_stride_c, hipStream_t stream) {
+  return quant_groupwise<Q_FP8>(x, x_dt, rows, cols, ldx, gr, gc, q, ldq, s, s_stride_r, s_stride_c, stream);
+}
+
+extern "C" sg_status sg_int8_quant_groupwise(const void* x, sg_dtype x_dt, int64_t rows,
+                                             int64_t cols, int64_t ldx, int gr, int gc, int8_t* q,
+                                             int64_t ldq, float* s, int64_t s_stride_r,
+                                             int64_t s_stride_c, hipStream_t stream) {
+  return quant_groupwise<Q_INT8>(x, x_dt, rows, cols, ldx, gr, gc, reinterpret_cast<uint8_t*>(q), ldq, s,
+                                 s_stride_r, s_stride_c, stream);
 }
 
 extern "C" sg_status sg_int4_quant_groupwise(const void* x, sg_dtype x_dt, int64_t rows,
@@ -172,10 +198,10 @@ extern "C" sg_status sg_int4_quant_groupwise(const void* x, sg_dtype x_dt, int64
   const int64_t blocks = rows * (cols / 128);
   const unsigned g = grid_for(blocks, 8);
   if (x_dt == SG_F32)
-    k_quant_rowblock<float, 128, true><<<g, 256, 0, stream>>>((const float*)x, rows, cols, ldx, q, ldq, s,
+    k_quant_rowblock<float, 128, Q_INT4><<<g, 256, 0, stream>>>((const float*)x, rows, cols, ldx, q, ldq, s,
                                                              s_stride_r, s_stride_c);
   else
-    k_quant_rowblock<uint16_t, 128, true><<<g, 256, 0, stream>>>((const uint16_t*)x, rows, cols, ldx, q,
+    k_quant_rowblock<uint16_t, 128, Q_INT4><<<g, 256, 0, stream>>>((const uint16_t*)x, rows, cols, ldx, q,
                                                                 ldq, s, s_stride_r, s_stride_c);
   return launch_status();
 }

@@ -40,7 +40,8 @@ def test_header_declares_the_entry_points():
         "sg_abi_version", "sg_status_str", "sg_fp8_quant_groupwise", "sg_int4_quant_groupwise",
         "sg_sparse24_prune_compress", "sg_fp8_gemm_groupwise", "sg_fp8_sparse24_gemm_groupwise",
         "sg_mixed_gemm_add", "sg_sparse24_packed_bytes", "sg_sparse24_pack_gfx950",
-        "sg_fp8_sparse24_gemm_groupwise_packed", "sg_probe_matrix_ops", "sg_probe_matrix_rate"])
+        "sg_fp8_sparse24_gemm_groupwise_packed", "sg_probe_matrix_ops", "sg_probe_matrix_rate",
+        "sg_int8_quant_groupwise", "sg_int8_sparse24_gemm_groupwise", "sg_int8_sparse24_gemm_groupwise_packed"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -76,6 +77,19 @@ def quant(**kw):
 ])
 def test_fp8_quant_validation(kw, code):
     assert quant(**kw) == code
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), NULL), (dict(q=None), NULL), (dict(dt=2), UNSUP), (dict(gr=2), UNSUP), (dict(gc=32), UNSUP),
+    (dict(cols=200), SHAPE), (dict(ldq=100), SHAPE), (dict(x=ODD), ALIGN), (dict(ldq=264), ALIGN),
+    (dict(rows=0), OK),
+])
+def test_int8_quant_validation(kw, code):
+    a = dict(x=P, dt=0, rows=4, cols=256, ldx=256, gr=1, gc=128, q=P2, ldq=256, s=P3, ssr=1, ssc=4)
+    a.update(kw)
+    assert sg.lib().sg_int8_quant_groupwise(a["x"], a["dt"], a["rows"], a["cols"], a["ldx"], a["gr"], a["gc"],
+                                            a["q"], a["ldq"], a["s"], a["ssr"], a["ssc"], None) == code
 
 
 def int4q(**kw):
@@ -149,6 +163,20 @@ def test_dense_gemm_validation(kw, code):
     (dict(ldm=40), ALIGN)])
 def test_sparse_gemm_validation(kw, code):
     assert gemm(True, **kw) == code
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,code", GEMM_CASES + [
+    (dict(meta=None), NULL), (dict(ldw=64), SHAPE), (dict(ldm=16), SHAPE), (dict(meta=ODD), ALIGN)])
+def test_int8_sparse_gemm_validation(kw, code):
+    a = dict(M=64, N=256, K=256, x=P, ldx=256, sx=P3, sxm=1, sxk=64, gm=1, w=P2, meta=P3, ldm=32,
+             sw=P3, swn=2, swk=1, gn=128, y=P, ydt=1, ldy=256, form=0)
+    a.update(kw)
+    ldw = a["ldw"] if "ldw" in kw else a["K"] // 2
+    assert sg.lib().sg_int8_sparse24_gemm_groupwise(a["M"], a["N"], a["K"], a["x"], a["ldx"], a["sx"], a["sxm"],
+                                                    a["sxk"], a["gm"], a["w"], ldw, a["meta"], a["ldm"], a["sw"],
+                                                    a["swn"], a["swk"], a["gn"], a["y"], a["ydt"], a["ldy"],
+                                                    a["form"], None) == code
 
 
 def mixed(**kw):
