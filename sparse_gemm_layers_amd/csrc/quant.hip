@@ -14,7 +14,7 @@
 
 namespace sg {
 
-enum QuantMode { Q_FP8 = 0, Q_INT4 = 1, Q_INT8 = 2 };
+enum QuantMode { Q_FP8 = 0, Q_INT8 = 2 };
 
 // int8 code of v / sc as a byte (two's complement), rounding half to even.
 __device__ __forceinline__ uint32_t int8_encode(float v, float sc) {
@@ -23,15 +23,14 @@ __device__ __forceinline__ uint32_t int8_encode(float v, float sc) {
   return (uint32_t)(int)t & 0xffu;
 }
 
-// ------------------------------------------------------------------ 1 x GC
-// LPB = GC/4 lanes share one block, 4 consecutive elements per lane; a wave
-// covers 64/LPB blocks per iteration of a grid-stride loop.
-template <typename TIn, int GC, int MODE>
-__global__ void __launch_bounds__(256) k_quant_rowblock(const TIn* __restrict__ x, int64_t rows,
-                                                        int64_t cols, int64_t ldx,
-                                                        uint8_t* __restrict__ q, int64_t ldq,
-                                                        float* __restrict__ s, int64_t ssr,
-                                                        int64_t ssc) {
+// ------------------------------------------------------------------ int4, 1 x 128
+// LPB = GC/4 lanes share one block, 4 consecutive elements per lane (two
+// codes per byte: 2-byte stores); a wave covers 64/LPB blocks per iteration
+// of a grid-stride loop.
+template <typename TIn, int GC>
+__global__ void __launch_bounds__(256) k_quant_int4(const TIn* __restrict__ x, int64_t rows, int64_t cols,
+                                                    int64_t ldx, uint8_t* __restrict__ q, int64_t ldq,
+                                                    float* __restrict__ s, int64_t ssr, int64_t ssc) {
   constexpr int LPB = GC / 4;
   constexpr int BPW = 64 / LPB;
   const int64_t nbc = cols / GC;
@@ -50,29 +49,71 @@ __global__ void __launch_bounds__(256) k_quant_rowblock(const TIn* __restrict__ 
     if (valid) load4(x + r * ldx + cb * GC + li * 4, v);
     float a = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
     a = group_max<LPB>(a);
-    if (MODE == Q_FP8 || MODE == Q_INT8) {
-      const float sc = a > 0.f ? a / (MODE == Q_FP8 ? 448.0f : 127.0f) : 1.0f;   // IEEE divide
-      uint32_t packed = 0;
+    const float sc = a > 0.f ? a / 7.0f : 1.0f;
+    uint32_t packed = 0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        packed |= (MODE == Q_FP8 ? e4m3_encode(v[i] / sc) : int8_encode(v[i], sc)) << (8 * i);
-      if (valid) {
-        *reinterpret_cast<uint32_t*>(q + r * ldq + cb * GC + li * 4) = packed;
-        if (li == 0) s[r * ssr + cb * ssc] = sc;
-      }
-    } else {
-      const float sc = a > 0.f ? a / 7.0f : 1.0f;
-      uint32_t packed = 0;
+    for (int i = 0; i < 4; ++i) {
+      float t = __builtin_rintf(v[i] / sc);                    // half to even
+      t = fminf(fmaxf(t, -7.0f), 7.0f);
+      packed |= ((uint32_t)(int)t & 0xfu) << (4 * i);
+    }
+    if (valid) {
+      *reinterpret_cast<uint16_t*>(q + r * ldq + cb * (GC / 2) + li * 2) = (uint16_t)packed;
+      if (li == 0) s[r * ssr + cb * ssc] = sc;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ 1 x GC, 16 per lane
+// FP8 / int8 codes with one scale per (row, GC columns): each lane owns 16
+// consecutive elements (four 16-byte fp32 loads or two bf16 loads in flight,
+// one 16-byte code store), GC/16 lanes share a block, a wave covers
+// 64 / (GC/16) blocks per iteration of a grid-stride loop.
+template <typename TIn, int GC, int MODE>
+__global__ void __launch_bounds__(256) k_quant_row16(const TIn* __restrict__ x, int64_t rows, int64_t cols,
+                                                     int64_t ldx, uint8_t* __restrict__ q, int64_t ldq,
+                                                     float* __restrict__ s, int64_t ssr, int64_t ssc) {
+  static_assert(MODE == Q_FP8 || MODE == Q_INT8, "byte codes only");
+  constexpr int LPB = GC / 16;
+  constexpr int BPW = 64 / LPB;
+  const int64_t nbc = cols / GC;
+  const int64_t nblk = rows * nbc;
+  const int lane = threadIdx.x & 63;
+  const int sub = lane / LPB, li = lane % LPB;
+  const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+  for (int64_t b0 = wave * BPW; b0 < nblk; b0 += nwaves * BPW) {
+    const int64_t b = b0 + sub;
+    const bool valid = b < nblk;
+    const int64_t r = valid ? b / nbc : 0;
+    const int64_t cb = valid ? b % nbc : 0;
+    float v[16];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float t = __builtin_rintf(v[i] / sc);                    // half to even
-        t = fminf(fmaxf(t, -7.0f), 7.0f);
-        packed |= ((uint32_t)(int)t & 0xfu) << (4 * i);
+    for (int i = 0; i < 16; ++i) v[i] = 0.f;
+    if (valid) {
+      const TIn* src = x + r * ldx + cb * GC + li * 16;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) load4(src + 4 * i, v + 4 * i);
+    }
+    float a = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(v[i]));
+    a = group_max<LPB>(a);
+    const float sc = a > 0.f ? a / (MODE == Q_FP8 ? 448.0f : 127.0f) : 1.0f;   // IEEE divide
+    uint32_t w[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const float* t = v + 4 * d;
+      if (MODE == Q_FP8) {
+        w[d] = e4m3_pack4(t[0] / sc, t[1] / sc, t[2] / sc, t[3] / sc);   // IEEE divides
+      } else {
+        w[d] = int8_encode(t[0], sc) | (int8_encode(t[1], sc) << 8) | (int8_encode(t[2], sc) << 16) |
+               (int8_encode(t[3], sc) << 24);
       }
-      if (valid) {
-        *reinterpret_cast<uint16_t*>(q + r * ldq + cb * (GC / 2) + li * 2) = (uint16_t)packed;
-        if (li == 0) s[r * ssr + cb * ssc] = sc;
-      }
+    }
+    if (valid) {
+      *reinterpret_cast<uint4*>(q + r * ldq + cb * GC + li * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+      if (li == 0) s[r * ssr + cb * ssc] = sc;
     }
   }
 }
@@ -113,10 +154,11 @@ __global__ void __launch_bounds__(256) k_quant_block128(const TIn* __restrict__ 
 #pragma unroll
   for (int st = 0; st < STEPS; ++st) {
     const int64_t r = rb * 128 + st * RPS + lr;
-    uint32_t packed = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      packed |= (MODE == Q_FP8 ? e4m3_encode(v[st][i] / sc) : int8_encode(v[st][i], sc)) << (8 * i);
+    const float* t = v[st];
+    const uint32_t packed =
+        MODE == Q_FP8 ? e4m3_pack4(t[0] / sc, t[1] / sc, t[2] / sc, t[3] / sc)
+                      : (int8_encode(t[0], sc) | (int8_encode(t[1], sc) << 8) | (int8_encode(t[2], sc) << 16) |
+                         (int8_encode(t[3], sc) << 24));
     if (r < rows) *reinterpret_cast<uint32_t*>(q + r * ldq + cb * GC + li * 4) = packed;
   }
   if (t == 0) s[rb * ssr + cb * ssc] = sc;
@@ -127,12 +169,12 @@ static void launch_quant(const TIn* x, int64_t rows, int64_t cols, int64_t ldx, 
                          uint8_t* q, int64_t ldq, float* s, int64_t ssr, int64_t ssc, hipStream_t st) {
   if (gr == 1) {
     const int64_t blocks = rows * (cols / gc);
-    const int per_wg = 4 * (64 / (gc / 4));
+    const int per_wg = 4 * (64 / (gc / 16));
     const unsigned g = grid_for(blocks, per_wg);
     if (gc == 128)
-      k_quant_rowblock<TIn, 128, MODE><<<g, 256, 0, st>>>(x, rows, cols, ldx, q, ldq, s, ssr, ssc);
+      k_quant_row16<TIn, 128, MODE><<<g, 256, 0, st>>>(x, rows, cols, ldx, q, ldq, s, ssr, ssc);
     else
-      k_quant_rowblock<TIn, 64, MODE><<<g, 256, 0, st>>>(x, rows, cols, ldx, q, ldq, s, ssr, ssc);
+      k_quant_row16<TIn, 64, MODE><<<g, 256, 0, st>>>(x, rows, cols, ldx, q, ldq, s, ssr, ssc);
   } else {
     const dim3 grid((unsigned)(cols / gc), (unsigned)cdiv(rows, 128));
     if (gc == 128)
@@ -198,10 +240,10 @@ extern "C" sg_status sg_int4_quant_groupwise(const void* x, sg_dtype x_dt, int64
   const int64_t blocks = rows * (cols / 128);
   const unsigned g = grid_for(blocks, 8);
   if (x_dt == SG_F32)
-    k_quant_rowblock<float, 128, Q_INT4><<<g, 256, 0, stream>>>((const float*)x, rows, cols, ldx, q, ldq, s,
+    k_quant_int4<float, 128><<<g, 256, 0, stream>>>((const float*)x, rows, cols, ldx, q, ldq, s,
                                                              s_stride_r, s_stride_c);
   else
-    k_quant_rowblock<uint16_t, 128, Q_INT4><<<g, 256, 0, stream>>>((const uint16_t*)x, rows, cols, ldx, q,
+    k_quant_int4<uint16_t, 128><<<g, 256, 0, stream>>>((const uint16_t*)x, rows, cols, ldx, q,
                                                                 ldq, s, s_stride_r, s_stride_c);
   return launch_status();
 }
