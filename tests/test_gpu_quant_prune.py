@@ -61,6 +61,26 @@ def test_fp8_encoder_on_every_midpoint_and_neighbour():
     assert np.array_equal(q.cpu().numpy(), oracle.e4m3_encode(x))
 
 
+def test_fp8_quant_saturates_a_quotient_just_above_448():
+    """For some block maxima a, fl32(a / fl32(a / 448)) is 448.00003, just above
+    the largest e4m3 value: the code must saturate to 0x7E (448), as the oracle's
+    encoder does, not become NaN."""
+    rng = np.random.default_rng(11)
+    a = (rng.uniform(1, 2, 200_000) * np.exp2(rng.integers(-20, 20, 200_000))).astype(np.float32)
+    over = a[(a / (a / np.float32(448)).astype(np.float32)).astype(np.float32) > np.float32(448)][:256]
+    assert len(over) == 256
+    x = np.zeros((256, 128), np.float32)
+    x[:, 0] = over
+    x[:, 1] = -over
+    x[:, 2:] = over[:, None] * rng.uniform(-1, 1, (256, 126)).astype(np.float32)
+    q, s = sg.fp8_quant_groupwise(up(x), gr=1, gc=128)
+    torch.cuda.synchronize()
+    rq, rs = oracle.fp8_quant_groupwise(x, 1, 128)
+    qc = q.cpu().numpy()
+    assert np.all(qc[:, 0] == 0x7E) and np.all(qc[:, 1] == 0xFE)
+    assert np.array_equal(qc, rq) and np.array_equal(s.cpu().numpy(), rs)
+
+
 def test_fp8_quant_all_zero_and_scale_layouts():
     x = np.zeros((5, 384), np.float32)
     x[2, 130:140] = -3.5
