@@ -37,6 +37,9 @@ from .gemm import (
     fp8_sparse24_gemm_groupwise,
     int8_gemm_groupwise,
     int8_sparse24_gemm_groupwise,
+    fp8_gemm_rowwise,
+    fp8_sparse24_gemm_rowwise,
+    int8_sparse24_gemm_rowwise,
     mixed_gemm_add,
     within_tolerance,
 )
@@ -47,5 +50,6 @@ __all__ = [
     "prune24", "compress24", "decompress24", "prune_compress24",
     "pack24_gfx950", "unpack24_gfx950", "packed_bytes",
     "expand_scales", "fp8_gemm_groupwise", "fp8_sparse24_gemm_groupwise",
-    "int8_gemm_groupwise", "int8_sparse24_gemm_groupwise", "mixed_gemm_add", "within_tolerance",
+    "int8_gemm_groupwise", "int8_sparse24_gemm_groupwise", "fp8_gemm_rowwise",
+    "fp8_sparse24_gemm_rowwise", "int8_sparse24_gemm_rowwise", "mixed_gemm_add", "within_tolerance",
 ]

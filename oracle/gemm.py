@@ -40,6 +40,16 @@ int8 x int8 with the same groupwise scales (the other 2:4 kernel torchao PR
 #3258 names, jcaip's comment): the same sum with int8 codes; every 128-term
 partial is an integer below 2^21, exact in fp64.
 
+Scales constant along K (rowwise: one scale per X row and per W row;
+tensorwise: one per tensor).  The weight quantisation code quoted in torchao
+PR #3258 expands one scale per weight row across all of that row's columns,
+and jcaip's review asks for the kernels that fuse the scale multiplication
+into the GEMM.  With s independent of kb the promotion sum factors,
+    y[m, n] = sx[m] * sw[n] * sum_k dec(xq[m, k]) * dec(wq[n, k]),
+so the scale can be applied once, after the whole K sum.  The full-K sum is
+still exact in fp64 (integer multiples of 2^-18 below 2^(17.6 + log2 K) <
+2^53 quanta for K < 2^17).
+
 Tolerance (the accepted error of a GPU result g against the oracle y):
     |g - y| <= 1e-2 |y| + 1e-3 T,
     T[m, n] = sum_kb s(m, n, kb) * sum_{k in kb} |dec x * dec w|  (+ sum |x2 w2|).
@@ -121,6 +131,45 @@ def int8_sparse24_gemm_groupwise(xq, sx, gm: int, wv, wmeta, sw, gn: int, bound:
     wv [N, K/2] and metadata wmeta [N, K/8]."""
     wq = decompress24(np.asarray(wv, dtype=np.int8).view(np.uint8), wmeta).view(np.int8)
     return int8_gemm_groupwise(xq, sx, gm, wq, sw, gn, bound=bound)
+
+
+def _row_scales(s, rows: int) -> np.ndarray:
+    """One fp32 scale per row ([rows]) or one for the tensor ([1]) -> fp64 [rows]."""
+    s = np.asarray(s, dtype=np.float32).reshape(-1)
+    assert s.shape[0] in (1, rows)
+    return np.broadcast_to(s, (rows,)).astype(np.float64)
+
+
+def _rowwise(xd, sx, wd, sw, bound: bool):
+    m, k = xd.shape
+    n = wd.shape[0]
+    assert wd.shape[1] == k and k % KBLK == 0 and k < (1 << 17)
+    s = np.outer(_row_scales(sx, m), _row_scales(sw, n))   # exact fp32 x fp32 products
+    y = s * (xd @ wd.T)                                     # exact full-K sum, one rounding
+    if not bound:
+        return y
+    return y, s * (np.abs(xd) @ np.abs(wd).T)
+
+
+def fp8_gemm_rowwise(xq, sx, wq, sw, bound: bool = False):
+    """xq [M, K] e4m3 codes with sx fp32 [M] (rowwise) or [1] (tensorwise);
+    wq [N, K] codes with sw fp32 [N] or [1].  y = sx[m] sw[n] sum_k x w, fp64."""
+    xd = e4m3_decode(np.asarray(xq, dtype=np.uint8))
+    wd = e4m3_decode(np.asarray(wq, dtype=np.uint8))
+    return _rowwise(xd, sx, wd, sw, bound)
+
+
+def fp8_sparse24_gemm_rowwise(xq, sx, wv, wmeta, sw, bound: bool = False):
+    """``fp8_gemm_rowwise`` with W as 2:4 compressed codes wv [N, K/2] + wmeta [N, K/8]."""
+    wq = decompress24(np.asarray(wv, dtype=np.uint8), wmeta)
+    return fp8_gemm_rowwise(xq, sx, wq, sw, bound=bound)
+
+
+def int8_sparse24_gemm_rowwise(xq, sx, wv, wmeta, sw, bound: bool = False):
+    """Rowwise / tensorwise scales with int8 codes and a 2:4 compressed int8 W."""
+    wq = decompress24(np.asarray(wv, dtype=np.int8).view(np.uint8), wmeta).view(np.int8)
+    xd = np.asarray(xq, dtype=np.int8).astype(np.float64)
+    return _rowwise(xd, sx, wq.astype(np.float64), sw, bound)
 
 
 def mixed_gemm_add(x1p, sx1, w1p, sw1, x2, w2, bound: bool = False):

@@ -13,7 +13,11 @@ import oracle.sparse24 as sp_mod
 import test_oracle_e4m3 as t_e4m3
 import test_oracle_gemm as t_gemm
 import test_oracle_quant as t_quant
+import test_oracle_rowwise as t_row
 import test_oracle_sparse24 as t_sp
+
+
+_ROWWISE = gemm_mod._rowwise
 
 
 def _fails(fn, *args):
@@ -183,3 +187,32 @@ def test_int8_dropped_sign_is_caught(monkeypatch):
         return orig(np.abs(np.asarray(xq, np.int8).astype(np.int64)).astype(np.int8), sx, gm, wq, sw, gn, bound=bound)
     monkeypatch.setattr(oracle, "int8_gemm_groupwise", gemm)
     _fails(t_int8.test_int8_unit_scales_match_int64_matmul)
+
+
+def test_rowwise_dropped_w_scale_is_caught(monkeypatch):
+    def rowwise(xd, sx, wd, sw, bound):
+        return _ROWWISE(xd, sx, wd, np.ones_like(np.asarray(sw, np.float32)), bound)
+    monkeypatch.setattr(gemm_mod, "_rowwise", rowwise)
+    _fails(t_row.test_rowwise_matches_exact_rationals, 3, 2, 128, False, False)
+
+
+def test_rowwise_scale_of_wrong_row_is_caught(monkeypatch):
+    def rowwise(xd, sx, wd, sw, bound):
+        return _ROWWISE(xd, np.roll(np.broadcast_to(np.asarray(sx, np.float32), (xd.shape[0],)), 1), wd, sw, bound)
+    monkeypatch.setattr(gemm_mod, "_rowwise", rowwise)
+    _fails(t_row.test_rowwise_matches_exact_rationals, 3, 2, 128, False, False)
+
+
+def test_rowwise_first_kblock_only_is_caught(monkeypatch):
+    def rowwise(xd, sx, wd, sw, bound):
+        return _ROWWISE(xd[:, :128], sx, wd[:, :128], sw, bound)
+    monkeypatch.setattr(gemm_mod, "_rowwise", rowwise)
+    _fails(t_row.test_rowwise_unit_scales_integer_codes_match_int64)
+
+
+def test_rowwise_bound_without_abs_is_caught(monkeypatch):
+    def rowwise(xd, sx, wd, sw, bound):
+        y = _ROWWISE(xd, sx, wd, sw, False)
+        return (y, y) if bound else y
+    monkeypatch.setattr(gemm_mod, "_rowwise", rowwise)
+    _fails(t_row.test_rowwise_bound_dominates_and_is_tight_for_nonnegative_codes)
