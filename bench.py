@@ -76,6 +76,11 @@ def gen_layer(seed, m, n, k, on_gpu_rng=False):
     return x, wq, meta, sw, wp
 
 
+def k_constant(s, rows, k):
+    """Scales s [rows] repeated over every 128-wide K block (K-block stride 0)."""
+    return s[:, None].expand(rows, k // 128)
+
+
 def time_fn(fn, reps=50, warm=5):
     """Mean GPU time of one call: `reps` calls are queued back to back behind a
     short GPU sleep (so that the host's launch cost, which exceeds the run time
@@ -172,7 +177,8 @@ def rows_report():
     ms = time_fn(lambda i: sg.fp8_gemm_groupwise(xdq, sxd, wdq, swd, 1, 128, y=y))
     out["a4_dense_gemm_2048x4096x4096"] = {"ms": ms, "TFLOP/s": flops / ms / 1e9,
                                            "frac_fp8_peak": flops / ms / 1e9 / PEAK_FP8_TFLOPS}
-    del xd, wd, xdq, wdq
+    wq_dense = wdq
+    del xd, wd, xdq
     # decode shapes, rotating weight copies so the 256 MB MALL cannot serve repeats
     for (dm, dn, dk) in workloads.DECODE_SHAPES:
         wsets = [gen_layer(2000 + i, 8, dn, dk, on_gpu_rng=True)[3:] for i in range(ROTATE_DECODE)]
@@ -215,6 +221,32 @@ def rows_report():
     b = sparse_bytes(dm, dn, dk)
     out[f"next_int8_decode_M{dm}_N{dn}_K{dk}_y"] = {"ms": ms, "GB/s": b / ms / 1e6, "frac_hbm": b / ms / 1e6 / PEAK_HBM_GBS}
     del wsets
+    # next row: scales constant along K (rowwise), applied once after the K
+    # loop, 2048x4096x4096 packed 2:4 and dense; and the batched ("L" mode)
+    # 2:4 GEMM, 8 problems of 256x4096x4096 with distinct packed weights
+    sxr = k_constant(sx[:, 0].contiguous(), m, k)
+    swr = k_constant(sw[:, 0].repeat_interleave(128)[:n].contiguous(), n, k)
+    y = torch.empty((m, n), dtype=torch.bfloat16, device=DEV)
+    ms = time_fn(lambda i: sg.fp8_sparse24_gemm_groupwise_packed(xq, sxr, wp, n, swr, 1, 1, y=y))
+    out["next_rowwise_sparse_gemm_packed_2048x4096x4096_y"] = {
+        "ms": ms, "TFLOP/s": flops / ms / 1e9, "frac_fp8_peak": flops / ms / 1e9 / PEAK_FP8_TFLOPS}
+    ms = time_fn(lambda i: sg.fp8_gemm_groupwise(xq, sxr, wq_dense, swr, 1, 1, y=y))
+    out["next_rowwise_dense_gemm_2048x4096x4096"] = {
+        "ms": ms, "TFLOP/s": flops / ms / 1e9, "frac_fp8_peak": flops / ms / 1e9 / PEAK_FP8_TFLOPS}
+    del wq_dense
+    L, bm = 8, 256
+    bsets = [gen_layer(4000 + i, 8, n, k, on_gpu_rng=True) for i in range(L)]
+    wpb = torch.stack([b_[4] for b_ in bsets])
+    swb = torch.stack([b_[3] for b_ in bsets])
+    del bsets
+    xb = xq[:L * bm].view(L, bm, k)
+    sxb = torch.empty((L, k // 128, bm), dtype=torch.float32, device=DEV).transpose(1, 2)
+    sxb.copy_(sx[:L * bm].view(L, bm, k // 128))
+    yb = torch.empty((L, bm, n), dtype=torch.bfloat16, device=DEV)
+    ms = time_fn(lambda i: sg.fp8_sparse24_gemm_groupwise_packed_batched(xb, sxb, wpb, n, swb, 1, 128, y=yb))
+    out[f"next_batched_sparse_gemm_packed_L{L}_{bm}x{n}x{k}_y"] = {
+        "ms": ms, "TFLOP/s": flops / ms / 1e9, "frac_fp8_peak": flops / ms / 1e9 / PEAK_FP8_TFLOPS}
+    del wpb, swb, yb
     # a7: fused int4 + bf16 add at L=2048, D1=4096, D2=64, D=4096
     dd = workloads.mixed_add(seed=5)
     x1, sx1 = sg.int4_quant_groupwise(torch.from_numpy(dd["x1"]).to(DEV))

@@ -140,6 +140,15 @@ sg_status sg_sparse24_prune_compress(const void* w, sg_dtype dt, int64_t rows, i
  * ldx, ldw multiples of 16; ldy >= N (SG_OUT_Y) or >= M (SG_OUT_YT); y aligned to
  * its element size.  M and N need not be multiples of any tile (the partial M
  * and N tiles of [P2095] are predicated).
+ * Scales constant along K (sx_sk == 0 and sw_sk == 0): rowwise scales (gran 1,
+ * one per X row and per W row) or tensorwise ones (also sx_sm == 0, sw_sn ==
+ * 0), as in [T3258] (its quoted weight quantisation expands one scale per
+ * weight row over the whole row; jcaip's review asks for kernels that fuse
+ * the scale multiplication).  Then y = sx * sw * sum_k x w, and for M > 64
+ * the kernels add all of K in the matrix core's fp32 accumulator and apply
+ * the scale product once, after the K loop (the same result within rounding;
+ * the int8 GEMMs keep an exact int32 sum while K <= 131072).  This holds for
+ * every GEMM entry point below.
  */
 sg_status sg_fp8_gemm_groupwise(int64_t M, int64_t N, int64_t K, const uint8_t* xq, int64_t ldx,
                                 const float* sx, int64_t sx_sm, int64_t sx_sk, int gran_m,
@@ -280,6 +289,45 @@ sg_status sg_int8_sparse24_gemm_groupwise_packed(int64_t M, int64_t N, int64_t K
                                                  const float* sw, int64_t sw_sn, int64_t sw_sk,
                                                  int gran_n, void* y, sg_dtype y_dt, int64_t ldy,
                                                  sg_form form, hipStream_t stream);
+
+/*
+ * Batched ("L" mode) forms: L problems of one shape (M, N, K), problem z
+ * reading and writing its operands at these offsets from problem 0's:
+ *   xq + z * x_bs, wq / wv / wpacked + z * (w_bs / wv_bs / wp_bs), wmeta +
+ *   z * wm_bs (bytes); sx + z * sx_bs, sw + z * sw_bs (floats); y + z * y_bs
+ *   (elements of y_dt).
+ * [P2095] PR description: the scale layout (M / ScaleGranularityM, K_TILES, L)
+ * carries the batch L as its outermost mode.  Every problem follows its
+ * single-problem entry point; L == 1 with zero strides is that call.
+ * Requires in addition 0 <= L <= 65535 (L == 0: SG_OK, nothing enqueued),
+ * every batch stride >= 0, and x_bs, w_bs / wv_bs / wp_bs, wm_bs multiples of 16
+ * (SG_ERR_ALIGN otherwise).  Outputs of different problems must not overlap;
+ * inputs may (a zero weight stride shares one weight among the problems).
+ */
+sg_status sg_fp8_gemm_groupwise_batched(int64_t L, int64_t M, int64_t N, int64_t K, const uint8_t* xq,
+                                        int64_t ldx, int64_t x_bs, const float* sx, int64_t sx_sm,
+                                        int64_t sx_sk, int64_t sx_bs, int gran_m, const uint8_t* wq,
+                                        int64_t ldw, int64_t w_bs, const float* sw, int64_t sw_sn,
+                                        int64_t sw_sk, int64_t sw_bs, int gran_n, void* y, sg_dtype y_dt,
+                                        int64_t ldy, int64_t y_bs, sg_form form, hipStream_t stream);
+
+sg_status sg_fp8_sparse24_gemm_groupwise_batched(int64_t L, int64_t M, int64_t N, int64_t K, const uint8_t* xq,
+                                                 int64_t ldx, int64_t x_bs, const float* sx, int64_t sx_sm,
+                                                 int64_t sx_sk, int64_t sx_bs, int gran_m, const uint8_t* wv,
+                                                 int64_t ldwv, int64_t wv_bs, const uint8_t* wmeta,
+                                                 int64_t ldwm, int64_t wm_bs, const float* sw, int64_t sw_sn,
+                                                 int64_t sw_sk, int64_t sw_bs, int gran_n, void* y,
+                                                 sg_dtype y_dt, int64_t ldy, int64_t y_bs, sg_form form,
+                                                 hipStream_t stream);
+
+sg_status sg_fp8_sparse24_gemm_groupwise_packed_batched(int64_t L, int64_t M, int64_t N, int64_t K,
+                                                        const uint8_t* xq, int64_t ldx, int64_t x_bs,
+                                                        const float* sx, int64_t sx_sm, int64_t sx_sk,
+                                                        int64_t sx_bs, int gran_m, const uint8_t* wpacked,
+                                                        int64_t wp_bs, const float* sw, int64_t sw_sn,
+                                                        int64_t sw_sk, int64_t sw_bs, int gran_n, void* y,
+                                                        sg_dtype y_dt, int64_t ldy, int64_t y_bs, sg_form form,
+                                                        hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -25,6 +25,10 @@ from ._binding import (
     int8_sparse24_gemm_groupwise_packed,
     probe_matrix_ops,
     probe_matrix_rate,
+    k_constant_scales,
+    fp8_gemm_groupwise_batched,
+    fp8_sparse24_gemm_groupwise_batched,
+    fp8_sparse24_gemm_groupwise_packed_batched,
 )
 
 __all__ = [
@@ -32,5 +36,7 @@ __all__ = [
     "sparse24_prune_compress", "fp8_gemm_groupwise", "fp8_sparse24_gemm_groupwise",
     "sparse24_packed_bytes", "sparse24_pack_gfx950", "fp8_sparse24_gemm_groupwise_packed",
     "mixed_gemm_add", "int8_quant_groupwise", "int8_sparse24_gemm_groupwise",
-    "int8_sparse24_gemm_groupwise_packed", "probe_matrix_ops", "probe_matrix_rate",
+    "int8_sparse24_gemm_groupwise_packed", "probe_matrix_ops", "probe_matrix_rate", "k_constant_scales",
+    "fp8_gemm_groupwise_batched", "fp8_sparse24_gemm_groupwise_batched",
+    "fp8_sparse24_gemm_groupwise_packed_batched",
 ]

@@ -42,6 +42,15 @@ _SIGS = {
                                          _i64, _ptr, _i64, _i64, _int, _ptr, _int, _i64, _int, _ptr], _int),
     "sg_int8_sparse24_gemm_groupwise_packed": ([_i64, _i64, _i64, _ptr, _i64, _ptr, _i64, _i64, _int, _ptr, _ptr,
                                                 _i64, _i64, _int, _ptr, _int, _i64, _int, _ptr], _int),
+    "sg_fp8_gemm_groupwise_batched": ([_i64, _i64, _i64, _i64, _ptr, _i64, _i64, _ptr, _i64, _i64, _i64, _int,
+                                       _ptr, _i64, _i64, _ptr, _i64, _i64, _i64, _int, _ptr, _int, _i64, _i64,
+                                       _int, _ptr], _int),
+    "sg_fp8_sparse24_gemm_groupwise_batched": ([_i64, _i64, _i64, _i64, _ptr, _i64, _i64, _ptr, _i64, _i64, _i64,
+                                                _int, _ptr, _i64, _i64, _ptr, _i64, _i64, _ptr, _i64, _i64, _i64,
+                                                _int, _ptr, _int, _i64, _i64, _int, _ptr], _int),
+    "sg_fp8_sparse24_gemm_groupwise_packed_batched": ([_i64, _i64, _i64, _i64, _ptr, _i64, _i64, _ptr, _i64, _i64,
+                                                       _i64, _int, _ptr, _i64, _ptr, _i64, _i64, _i64, _int, _ptr,
+                                                       _int, _i64, _i64, _int, _ptr], _int),
     "sg_probe_matrix_ops": ([_int, _int], _i64),
     "sg_probe_matrix_rate": ([_int, _int, _ptr, _ptr, _ptr], _int),
 }
@@ -208,6 +217,109 @@ def fp8_sparse24_gemm_groupwise(xq, sx, wv, wmeta, sw, gran_m: int = 1, gran_n: 
                                               _row_stride(wmeta), _p(sw), sw.stride(0), sw.stride(1), gran_n,
                                               _p(y), ydt, _row_stride(y), f, _stream(xq))
     _check(st, "sg_fp8_sparse24_gemm_groupwise")
+    return y
+
+
+def k_constant_scales(s, rows: int, k: int):
+    """A [rows, K/128] view of rowwise scales s [rows] (or tensorwise s [1]) that
+    repeats them over every K block (K-block stride 0), the layout the GEMM entry
+    points take for scales constant along K (pass gran 1)."""
+    if not isinstance(s, torch.Tensor) or s.dim() != 1 or s.shape[0] not in (1, rows):
+        raise SgError("scales must be 1-D with one entry per row, or one entry")
+    return s[:, None].expand(rows, k // 128)
+
+
+def _gpu3d(t, name):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise SgError(f"{name} must be a GPU tensor")
+    if t.dim() != 3 or (t.shape[2] > 1 and t.stride(2) != 1):
+        raise SgError(f"{name} must be 3-D [L, rows, cols] with unit column stride")
+    return t
+
+
+def _bstride(t):
+    """Batch stride of a 3-D operand, 0 for a 2-D operand shared by every problem."""
+    return 0 if t.dim() == 2 or t.shape[0] == 1 else t.stride(0)
+
+
+def _mat(t, name):
+    """(rows, row stride) of a [L, rows, cols] or shared [rows, cols] operand."""
+    if t.dim() == 2:
+        _gpu2d(t, name)
+        return t.shape[0], _row_stride(t)
+    _gpu3d(t, name)
+    return t.shape[1], (t.stride(1) if t.shape[1] > 1 else max(t.shape[2], 1))
+
+
+def _sc(t):
+    """(row stride, K-block stride, batch stride) of [L, rows, KB] or shared [rows, KB] scales."""
+    if t.dim() == 2:
+        return t.stride(0), t.stride(1), 0
+    return t.stride(1), t.stride(2), _bstride(t)
+
+
+def _out_batched(y, L, M, N, out_dtype, form, device):
+    yt = form in ("yt", SG_OUT_YT)
+    if y is None:
+        y = torch.empty((L, N, M) if yt else (L, M, N), dtype=out_dtype, device=device)
+    _gpu3d(y, "y")
+    return y, (SG_OUT_YT if yt else SG_OUT_Y), _dtype_code(y, "y")
+
+
+def fp8_gemm_groupwise_batched(xq, sx, wq, sw, gran_m: int = 1, gran_n: int = 128, out_dtype=torch.bfloat16,
+                               form: str = "y", y=None):
+    """L independent GEMMs: xq uint8 [L, M, K], sx [L, ceil(M/gran_m), K/128];
+    wq uint8 [L, N, K] and sw [L, ., K/128], or 2-D to share one weight.  Returns
+    y [L, M, N] ("y") or [L, N, M] ("yt")."""
+    _gpu3d(xq, "xq")
+    L, M, K = xq.shape
+    N, ldw = _mat(wq, "wq")
+    y, f, ydt = _out_batched(y, L, M, N, out_dtype, form, xq.device)
+    sxm, sxk, sxb = _sc(sx)
+    swn, swk, swb = _sc(sw)
+    st = lib().sg_fp8_gemm_groupwise_batched(L, M, N, K, _p(xq), _mat(xq, "xq")[1], _bstride(xq), _p(sx), sxm, sxk,
+                                             sxb, gran_m, _p(wq), ldw, _bstride(wq), _p(sw), swn, swk, swb, gran_n,
+                                             _p(y), ydt, _mat(y, "y")[1], _bstride(y), f, _stream(xq))
+    _check(st, "sg_fp8_gemm_groupwise_batched")
+    return y
+
+
+def fp8_sparse24_gemm_groupwise_batched(xq, sx, wv, wmeta, sw, gran_m: int = 1, gran_n: int = 128,
+                                        out_dtype=torch.bfloat16, form: str = "y", y=None):
+    """Batched 2:4 GEMM: wv [L, N, K/2] and wmeta [L, N, K/8] (or 2-D, shared)."""
+    _gpu3d(xq, "xq")
+    L, M, K = xq.shape
+    N, ldwv = _mat(wv, "wv")
+    _, ldwm = _mat(wmeta, "wmeta")
+    y, f, ydt = _out_batched(y, L, M, N, out_dtype, form, xq.device)
+    sxm, sxk, sxb = _sc(sx)
+    swn, swk, swb = _sc(sw)
+    st = lib().sg_fp8_sparse24_gemm_groupwise_batched(
+        L, M, N, K, _p(xq), _mat(xq, "xq")[1], _bstride(xq), _p(sx), sxm, sxk, sxb, gran_m, _p(wv), ldwv,
+        _bstride(wv), _p(wmeta), ldwm, _bstride(wmeta), _p(sw), swn, swk, swb, gran_n, _p(y), ydt,
+        _mat(y, "y")[1], _bstride(y), f, _stream(xq))
+    _check(st, "sg_fp8_sparse24_gemm_groupwise_batched")
+    return y
+
+
+def fp8_sparse24_gemm_groupwise_packed_batched(xq, sx, wpacked, n: int, sw, gran_m: int = 1, gran_n: int = 128,
+                                               out_dtype=torch.bfloat16, form: str = "y", y=None):
+    """Batched 2:4 GEMM with packed weights: wpacked uint8 [L, bytes] (one packed
+    weight per problem) or 1-D (shared)."""
+    _gpu3d(xq, "xq")
+    L, M, K = xq.shape
+    need = sparse24_packed_bytes(n, K)
+    if not isinstance(wpacked, torch.Tensor) or not wpacked.is_cuda or wpacked.dim() not in (1, 2) \
+            or wpacked.shape[-1] < need or wpacked.stride(-1) != 1:
+        raise SgError("wpacked must be a GPU tensor [L, bytes] or [bytes] holding a packed weight")
+    wpb = 0 if wpacked.dim() == 1 or wpacked.shape[0] == 1 else wpacked.stride(0)
+    y, f, ydt = _out_batched(y, L, M, n, out_dtype, form, xq.device)
+    sxm, sxk, sxb = _sc(sx)
+    swn, swk, swb = _sc(sw)
+    st = lib().sg_fp8_sparse24_gemm_groupwise_packed_batched(
+        L, M, n, K, _p(xq), _mat(xq, "xq")[1], _bstride(xq), _p(sx), sxm, sxk, sxb, gran_m, _p(wpacked), wpb,
+        _p(sw), swn, swk, swb, gran_n, _p(y), ydt, _mat(y, "y")[1], _bstride(y), f, _stream(xq))
+    _check(st, "sg_fp8_sparse24_gemm_groupwise_packed_batched")
     return y
 
 

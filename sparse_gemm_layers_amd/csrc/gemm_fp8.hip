@@ -52,13 +52,45 @@ struct GemmArgs {
   int64_t ldy;
   int vec_store;  // Y-form: 4 consecutive n may be stored as one vector
   int vec16;      // y is 16-byte aligned and a row of y is a multiple of 16 bytes
+  // Batched problems (grid z = problem index): problem z's operands start this
+  // far after problem 0's, in bytes for x, w, meta and y, in floats for the
+  // scales; all zero for a single problem.
+  int64_t bx, bw, bm, bsx, bsw, by;
+  int L;
 };
+
+#if SG_DEVICE_PASS
+__device__ __forceinline__ void to_batch(GemmArgs& a) {
+  const int64_t z = blockIdx.z;
+  a.x += z * a.bx;
+  a.w += z * a.bw;
+  a.meta += z * a.bm;
+  a.sx += z * a.bsx;
+  a.sw += z * a.bsw;
+  a.y = static_cast<uint8_t*>(a.y) + z * a.by;
+}
+#endif
 
 // ------------------------------------------------------------------ helpers
 
 __device__ __forceinline__ v4f mma_dense(const v8i& a, const v8i& b) {
   const v4f z = {0.f, 0.f, 0.f, 0.f};
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 0, 0, 0, 0, 0, 0);
+}
+
+// Accumulating forms, for scales constant along K: the K blocks' products
+// add up in the matrix core's fp32 C operand (the int8 form keeps an exact
+// int32 sum in the same registers).
+__device__ __forceinline__ v4f mma_dense_acc(const v8i& a, const v8i& b, const v4f& c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+template <bool I8>
+__device__ __forceinline__ v4f mma_sparse_acc(const v4i& a, const v8i& b, const v4f& c, int idx) {
+  if constexpr (I8)
+    return __builtin_bit_cast(v4f, __builtin_amdgcn_smfmac_i32_16x16x128_i8(a, b, __builtin_bit_cast(v4i, c), idx, 0, 0));
+  else
+    return __builtin_amdgcn_smfmac_f32_16x16x128_fp8_fp8(a, b, c, idx, 0, 0);
 }
 
 // The partial of one 16 x 16 x 128 block of a 2:4-sparse A (W) and dense B
@@ -156,14 +188,18 @@ __device__ __forceinline__ T lds_ld(const uint8_t* st, uint32_t off) {
   return *reinterpret_cast<const T*>(st + off);
 }
 
-// Multiplies one sparse LDS stage into the wave's 8 x 4 sub-tiles and promotes.
+// Multiplies one sparse LDS stage into the wave's 8 x 4 sub-tiles and
+// promotes (GRAN_N = 128 or 1: 128-row or per-row W scales of the K block),
+// or accumulates in the matrix core (GRAN_N = 0: scales constant along K,
+// applied after the K loop).
 template <int GRAN_N, bool PACKED, bool I8>
 __device__ __forceinline__ void compute_stage(const uint8_t* st, v4f (&acc)[8][4], const LaneOffsets& o,
                                               int wn, int g, uint32_t msel) {
   using L = Stage<true>;
+  constexpr bool ROWS = GRAN_N == 0;
   float sxj[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) sxj[j] = lds_ld<float>(st, o.sx + j * 64);
+  for (int j = 0; j < 4; ++j) sxj[j] = ROWS ? 1.f : lds_ld<float>(st, o.sx + j * 64);
 
   v8i bx[4];
 #pragma unroll
@@ -189,7 +225,10 @@ __device__ __forceinline__ void compute_stage(const uint8_t* st, v4f (&acc)[8][4
       const int idx = lds_ld<int>(st, o.mt + i * 256);
       const v4i aa = {(int)av.x, (int)av.y, (int)av.z, (int)av.w};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) p[j] = mma_sparse<I8>(aa, bx[j], idx);
+      for (int j = 0; j < 4; ++j) {
+        if (ROWS) acc[i][j] = mma_sparse_acc<I8>(aa, bx[j], acc[i][j], idx);
+        else p[j] = mma_sparse<I8>(aa, bx[j], idx);
+      }
     } else {
       const uint2 v0 = lds_ld<uint2>(st, o.w0 + i * 1024);
       const uint2 v1 = lds_ld<uint2>(st, o.w1 + i * 1024);
@@ -197,8 +236,12 @@ __device__ __forceinline__ void compute_stage(const uint8_t* st, v4f (&acc)[8][4
       const int idx = (int)__builtin_amdgcn_perm(mw.y, mw.x, msel);
       const v4i aa = {(int)v0.x, (int)v0.y, (int)v1.x, (int)v1.y};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) p[j] = mma_sparse<I8>(aa, bx[j], idx);
+      for (int j = 0; j < 4; ++j) {
+        if (ROWS) acc[i][j] = mma_sparse_acc<I8>(aa, bx[j], acc[i][j], idx);
+        else p[j] = mma_sparse<I8>(aa, bx[j], idx);
+      }
     }
+    if (ROWS) continue;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       if (GRAN_N == 128) {
@@ -210,6 +253,31 @@ __device__ __forceinline__ void compute_stage(const uint8_t* st, v4f (&acc)[8][4
         acc[i][j][3] = fmaf(p[j][3] * swr.w, sxj[j], acc[i][j][3]);
       }
     }
+  }
+}
+
+// Scales constant along K: multiplies the wave's RI x 4 sub-tiles by
+// sx (X row of the lane's column) * sw (W rows 16 i + 4 g .. + 3), read from
+// a landed stage (every stage holds the same scales).  int8 sums are
+// converted from their exact int32 first.
+template <bool I8, int RI>
+__device__ __forceinline__ void rows_scale(const uint8_t* st, v4f (&acc)[RI][4], uint32_t sx_off, uint32_t sw_off) {
+  float sxj[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) sxj[j] = lds_ld<float>(st, sx_off + j * 64);
+#pragma unroll
+  for (int i = 0; i < RI; ++i) {
+    const float4 w = lds_ld<float4>(st, sw_off + i * 64);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v4f v = acc[i][j];
+      if (I8) {
+        const v4i q = __builtin_bit_cast(v4i, v);
+        v = (v4f){(float)q[0], (float)q[1], (float)q[2], (float)q[3]};
+      }
+      acc[i][j] = (v4f){v[0] * (w.x * sxj[j]), v[1] * (w.y * sxj[j]), v[2] * (w.z * sxj[j]), v[3] * (w.w * sxj[j])};
+    }
+    asm volatile("" ::: "memory");   // one row's W scales live at a time (all 128 results are)
   }
 }
 
@@ -334,6 +402,7 @@ __global__ void __launch_bounds__(512) k_gemm_sparse_x2(GemmArgs a, int tiles_m,
 #if SG_DEVICE_PASS
   __shared__ __attribute__((aligned(1024))) uint8_t db0[x2::DBL];
   __shared__ __attribute__((aligned(1024))) uint8_t db1[x2::DBL];
+  to_batch(a);
 
   int tn, tm;
   tile_coords(tiles_m, tiles_n, tn, tm);
@@ -395,10 +464,21 @@ __global__ void __launch_bounds__(512) k_gemm_sparse_x2(GemmArgs a, int tiles_m,
     xchg_out<0>(reinterpret_cast<float4*>(db1), acc, w4, l);
   }
   __syncthreads();
+  // Scales constant along K: the second half of the last double stage holds
+  // them (a landed K block, or the copy of the last one), above the bytes the
+  // exchange and the staged tile use.
+  constexpr int SCALE = GRAN_N == 0 ? (I8 ? 2 : 1) : 0;
+  static_assert(x2::HALF + Stage<true>::SX_OFF >= 65536 &&
+                x2::HALF + Stage<true>::SX_OFF >= OutTile<OUT_BF16, OUT_T, x2::DBL>::RPH *
+                                                       OutTile<OUT_BF16, OUT_T, x2::DBL>::PITCH,
+                "scales must survive the exchange and the staged tile");
+  const uint8_t* const sst = ((NIT - 1) & 1 ? db1 : db0) + x2::HALF;
+  const float* const sxp = reinterpret_cast<const float*>(sst + Stage<true>::SX_OFF) + wm * 64 + lr;
+  const float* const swp = reinterpret_cast<const float*>(sst + Stage<true>::SW_OFF) + wn * 128 + 4 * g;
   if (q == 0)
-    x2_finish<0, OUT_BF16, OUT_T, x2::DBL>(db1, db0, db1, acc, w4, l, wn, wm, g, lr);
+    x2_finish<0, OUT_BF16, OUT_T, x2::DBL, SCALE>(db1, db0, db1, acc, w4, l, wn, wm, g, lr, sxp, swp);
   else
-    x2_finish<1, OUT_BF16, OUT_T, x2::DBL>(db0, db0, db1, acc, w4, l, wn, wm, g, lr);
+    x2_finish<1, OUT_BF16, OUT_T, x2::DBL, SCALE>(db0, db0, db1, acc, w4, l, wn, wm, g, lr, sxp, swp);
   __syncthreads();
   store_staged<OUT_BF16, OUT_T, x2::DBL>(a, db0, db1, m0, n0, t);
 #endif  // SG_DEVICE_PASS
@@ -540,7 +620,7 @@ __device__ __forceinline__ void read_b_d8(const uint8_t* st, const LaneD8& o, in
   const float swv = GRAN_N == 128 ? lds_ld<float>(st, L::SW_OFF + wn * 256) : 1.f;   // the wave's 64 rows share it
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    f.sx[j] = lds_ld<float>(st, o.sx + j * 64) * swv;
+    if (GRAN_N != 0) f.sx[j] = lds_ld<float>(st, o.sx + j * 64) * swv;
     f.b[j] = ld_frag(st, o.x0 + j * 2048, o.x1 + j * 2048);
   }
 }
@@ -573,9 +653,10 @@ __device__ __forceinline__ void promote_d8(v4f (&acc)[4], const v4f (&p)[4], con
 }
 
 // Multiplies stage `cur` (in registers) into the wave's 4 x 4 sub-tiles and
-// promotes, while reading the next stage into `nxt`: its X fragments first,
-// then the W fragment of row i once row i of `cur` is multiplied, so the two
-// register sets can share the W registers.
+// promotes (or, with scales constant along K, GRAN_N = 0, accumulates in the
+// matrix core), while reading the next stage into `nxt`: its X fragments
+// first, then the W fragment of row i once row i of `cur` is multiplied, so
+// the two register sets can share the W registers.
 template <int GRAN_N>
 __device__ __forceinline__ void step_d8(const FragD8& cur, FragD8& nxt, const uint8_t* st_next, const LaneD8& o,
                                         int wn, v4f (&acc)[4][4]) {
@@ -584,11 +665,14 @@ __device__ __forceinline__ void step_d8(const FragD8& cur, FragD8& nxt, const ui
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) p[i & 1][j] = mma_dense(cur.a[i], cur.b[j]);
-    if (i > 0) promote_d8<GRAN_N>(acc[i - 1], p[(i - 1) & 1], cur, i - 1);
+    for (int j = 0; j < 4; ++j) {
+      if (GRAN_N == 0) acc[i][j] = mma_dense_acc(cur.a[i], cur.b[j], acc[i][j]);
+      else p[i & 1][j] = mma_dense(cur.a[i], cur.b[j]);
+    }
+    if (GRAN_N != 0 && i > 0) promote_d8<GRAN_N>(acc[i - 1], p[(i - 1) & 1], cur, i - 1);
     read_a_d8<GRAN_N>(st_next, o, i, nxt);
   }
-  promote_d8<GRAN_N>(acc[3], p[1], cur, 3);
+  if (GRAN_N != 0) promote_d8<GRAN_N>(acc[3], p[1], cur, 3);
 }
 
 // Multiplies one stage's fragments into the wave's 4 x 4 sub-tiles and promotes.
@@ -618,6 +702,7 @@ __global__ void __launch_bounds__(512) k_gemm_dense8(GemmArgs a, int tiles_m, in
   __shared__ __attribute__((aligned(1024))) uint8_t sm1[BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t sm2[BYTES];
   uint8_t* const buf[3] = {sm0, sm1, sm2};
+  to_batch(a);
 
   int tn, tm;
   tile_coords(tiles_m, tiles_n, tn, tm);
@@ -643,7 +728,7 @@ __global__ void __launch_bounds__(512) k_gemm_dense8(GemmArgs a, int tiles_m, in
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-  if constexpr (GRAN_N == 128) {
+  if constexpr (GRAN_N == 128 || GRAN_N == 0) {
     // Three LDS stages and two register sets.  Step kb waits for stage
     // kb + 1, issues stage kb + 3 into the buffer stage kb has left, reads
     // stage kb + 1 into the spare register set and multiplies stage kb (read
@@ -702,6 +787,10 @@ __global__ void __launch_bounds__(512) k_gemm_dense8(GemmArgs a, int tiles_m, in
     }
   }
   wait_vmcnt<0>();   // no load may still be writing LDS when the tile is staged there
+  if constexpr (GRAN_N == 0) {   // every wave's loads of the stages have landed
+    lds_barrier();
+    rows_scale<false, 4>(sm2, acc, lo.sx, lo.sw);
+  }
 
   if constexpr (OUT_BF16) {   // half of a bf16 tile fits one stage buffer
     __syncthreads();
@@ -829,6 +918,7 @@ __global__ void __launch_bounds__(512) k_gemm_decode(GemmArgs a) {
   constexpr int U = DEC_U;
   __shared__ __attribute__((aligned(16))) float red[DEC_WAVES][RB * MT][64][4];
 #if SG_DEVICE_PASS
+  to_batch(a);
   const int t = threadIdx.x, l = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int g = l >> 4, lr = l & 15;
@@ -965,6 +1055,7 @@ __global__ void __launch_bounds__(512) k_gemm_decode_dma(GemmArgs a) {
   static_assert(MT <= 4 && 2 * C::ARR <= 160 * 1024, "LDS");
   __shared__ __attribute__((aligned(1024))) uint8_t r0[C::ARR];
   __shared__ __attribute__((aligned(1024))) uint8_t r1[C::ARR];
+  to_batch(a);
   const int t = threadIdx.x, l = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int g = l >> 4, lr = l & 15;
@@ -1083,10 +1174,15 @@ __global__ void __launch_bounds__(512) k_gemm_decode_dma(GemmArgs a) {
 template <bool SPARSE, bool I8, bool PACKED, int GRAN_N, bool OUT_BF16, bool OUT_T>
 static void launch_large(const GemmArgs& a, hipStream_t st) {
   const int tm = (int)cdiv(a.M, BM), tn = (int)cdiv(a.N, BN);
+  const dim3 grid((unsigned)(tm * tn), 1, (unsigned)a.L);
   if (SPARSE)
-    k_gemm_sparse_x2<I8, PACKED, GRAN_N, OUT_BF16, OUT_T><<<tm * tn, 512, 0, st>>>(a, tm, tn);
+    k_gemm_sparse_x2<I8, PACKED, GRAN_N, OUT_BF16, OUT_T><<<grid, 512, 0, st>>>(a, tm, tn);
   else
-    k_gemm_dense8<GRAN_N, OUT_BF16, OUT_T><<<tm * tn, 512, 0, st>>>(a, tm, tn);
+    k_gemm_dense8<GRAN_N, OUT_BF16, OUT_T><<<grid, 512, 0, st>>>(a, tm, tn);
+}
+
+static dim3 dec_grid(const GemmArgs& a, int64_t rows16, int rb) {
+  return dim3((unsigned)cdiv(rows16, rb), 1, (unsigned)a.L);
 }
 
 // Launches the LDS-streaming decode kernel with RB row blocks per workgroup if
@@ -1096,7 +1192,7 @@ template <bool I8, int RB, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
 static bool try_decode_dma(const GemmArgs& a, hipStream_t st, int64_t rows16) {
   if constexpr (DmaCfg<RB, MT>::FITS) {
     if (RB == 1 || rows16 >= RB * 224) {
-      k_gemm_decode_dma<I8, RB, MT, GRAN_N, OUT_BF16, OUT_T><<<(unsigned)cdiv(rows16, RB), 512, 0, st>>>(a);
+      k_gemm_decode_dma<I8, RB, MT, GRAN_N, OUT_BF16, OUT_T><<<dec_grid(a, rows16, RB), 512, 0, st>>>(a);
       return true;
     }
   }
@@ -1118,11 +1214,11 @@ static void launch_decode_mt(const GemmArgs& a, hipStream_t st) {
   }
   constexpr int RB4 = MT == 1 ? 4 : 1, RB2 = MT <= 2 ? 2 : 1;
   if (RB4 == 4 && rows16 >= 4 * 224)
-    k_gemm_decode<SPARSE, I8, PACKED, RB4, MT, GRAN_N, OUT_BF16, OUT_T><<<(unsigned)cdiv(rows16, RB4), 512, 0, st>>>(a);
+    k_gemm_decode<SPARSE, I8, PACKED, RB4, MT, GRAN_N, OUT_BF16, OUT_T><<<dec_grid(a, rows16, RB4), 512, 0, st>>>(a);
   else if (RB2 == 2 && rows16 >= 2 * 224)
-    k_gemm_decode<SPARSE, I8, PACKED, RB2, MT, GRAN_N, OUT_BF16, OUT_T><<<(unsigned)cdiv(rows16, RB2), 512, 0, st>>>(a);
+    k_gemm_decode<SPARSE, I8, PACKED, RB2, MT, GRAN_N, OUT_BF16, OUT_T><<<dec_grid(a, rows16, RB2), 512, 0, st>>>(a);
   else
-    k_gemm_decode<SPARSE, I8, PACKED, 1, MT, GRAN_N, OUT_BF16, OUT_T><<<(unsigned)rows16, 512, 0, st>>>(a);
+    k_gemm_decode<SPARSE, I8, PACKED, 1, MT, GRAN_N, OUT_BF16, OUT_T><<<dec_grid(a, rows16, 1), 512, 0, st>>>(a);
 }
 
 template <bool SPARSE, bool I8, bool PACKED, int GRAN_N, bool OUT_BF16, bool OUT_T>
@@ -1139,9 +1235,23 @@ static void launch_shape(const GemmArgs& a, hipStream_t st) {
     launch_large<SPARSE, I8, PACKED, GRAN_N, OUT_BF16, OUT_T>(a, st);
 }
 
+// Scales constant along K (both K-block strides 0) take the large-M kernels'
+// accumulate-then-scale form (GRAN_N = 0); decode-sized M keeps the
+// per-block kernels, which read the repeated scales (it streams the weight
+// and does not wait on the promotion).  int8 sums stay exact in int32 while
+// K * 127^2 < 2^31.
 template <bool SPARSE, bool PACKED, bool I8 = false>
 static void launch_gemm(const GemmArgs& a, int gran_n, bool bf16, bool yt, hipStream_t st) {
-  if (gran_n == 128) {
+  const bool rows = a.sx_sk == 0 && a.sw_sk == 0 && a.M > 64 && (!I8 || a.K <= (1LL << 17));
+  if (rows) {
+    if (bf16) {
+      if (yt) launch_large<SPARSE, I8, PACKED, 0, true, true>(a, st);
+      else launch_large<SPARSE, I8, PACKED, 0, true, false>(a, st);
+    } else {
+      if (yt) launch_large<SPARSE, I8, PACKED, 0, false, true>(a, st);
+      else launch_large<SPARSE, I8, PACKED, 0, false, false>(a, st);
+    }
+  } else if (gran_n == 128) {
     if (bf16) {
       if (yt) launch_shape<SPARSE, I8, PACKED, 128, true, true>(a, st);
       else launch_shape<SPARSE, I8, PACKED, 128, true, false>(a, st);
@@ -1181,10 +1291,23 @@ static sg_status check_common(int64_t M, int64_t N, int64_t K, const uint8_t* xq
   return SG_OK;
 }
 
+// Batched problems: count and per-operand batch strides (bytes for the codes
+// and metadata, floats for the scales, elements for y).
+struct Batch {
+  int64_t L = 1, bx = 0, bw = 0, bm = 0, bsx = 0, bsw = 0, by = 0;
+};
+
+static sg_status check_batch(const Batch& b) {
+  if (b.L < 0 || b.L > 65535) return SG_ERR_SHAPE;
+  if (b.bx < 0 || b.bw < 0 || b.bm < 0 || b.bsx < 0 || b.bsw < 0 || b.by < 0) return SG_ERR_SHAPE;
+  if (b.bx % 16 || b.bw % 16 || b.bm % 16) return SG_ERR_ALIGN;
+  return SG_OK;
+}
+
 static GemmArgs make_args(int64_t M, int64_t N, int64_t K, const uint8_t* xq, int64_t ldx,
                           const float* sx, int64_t sx_sm, int64_t sx_sk, int gran_m, const uint8_t* w,
                           int64_t ldw, const uint8_t* meta, int64_t ldm, const float* sw, int64_t sw_sn,
-                          int64_t sw_sk, int gran_n, void* y, sg_dtype y_dt, int64_t ldy) {
+                          int64_t sw_sk, int gran_n, void* y, sg_dtype y_dt, int64_t ldy, const Batch& b) {
   GemmArgs a;
   a.M = M; a.N = N; a.K = K;
   a.x = xq; a.ldx = ldx;
@@ -1192,9 +1315,12 @@ static GemmArgs make_args(int64_t M, int64_t N, int64_t K, const uint8_t* xq, in
   a.w = w; a.ldw = ldw; a.meta = meta; a.ldm = ldm;
   a.sw = sw; a.sw_sn = sw_sn; a.sw_sk = sw_sk; a.gn_shift = gran_n == 128 ? 7 : 0;
   a.y = y; a.ldy = ldy;
-  const size_t vb = 4 * dtype_size(y_dt);
-  a.vec_store = (ldy % 4 == 0) && aligned(y, vb);
-  a.vec16 = ((ldy * (int64_t)dtype_size(y_dt)) % 16 == 0) && aligned(y, 16);
+  const int64_t es = (int64_t)dtype_size(y_dt);
+  const size_t vb = 4 * es;
+  a.vec_store = (ldy % 4 == 0) && aligned(y, vb) && (b.by * es) % (int64_t)vb == 0;
+  a.vec16 = ((ldy * es) % 16 == 0) && aligned(y, 16) && (b.by * es) % 16 == 0;
+  a.bx = b.bx; a.bw = b.bw; a.bm = b.bm; a.bsx = b.bsx; a.bsw = b.bsw; a.by = b.by * es;
+  a.L = (int)b.L;
   return a;
 }
 
@@ -1202,23 +1328,45 @@ static GemmArgs make_args(int64_t M, int64_t N, int64_t K, const uint8_t* xq, in
 
 using namespace sg;
 
+static sg_status dense_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* xq, int64_t ldx, const float* sx,
+                            int64_t sx_sm, int64_t sx_sk, int gran_m, const uint8_t* wq, int64_t ldw,
+                            const float* sw, int64_t sw_sn, int64_t sw_sk, int gran_n, void* y, sg_dtype y_dt,
+                            int64_t ldy, sg_form form, const Batch& b, hipStream_t stream) {
+  sg_status st = check_common(M, N, K, xq, ldx, sx, sx_sm, sx_sk, gran_m, sw, sw_sn, sw_sk, gran_n, y, y_dt, ldy, form);
+  if (st != SG_OK) return st;
+  if ((st = check_batch(b)) != SG_OK) return st;
+  if (!wq) return SG_ERR_NULL;
+  if (ldw < K || ldw >= (1LL << 24)) return SG_ERR_SHAPE;
+  if (!aligned(wq, 16) || ldw % 16) return SG_ERR_ALIGN;
+  if (M == 0 || N == 0 || b.L == 0) return SG_OK;
+  const GemmArgs a = make_args(M, N, K, xq, ldx, sx, sx_sm, sx_sk, gran_m, wq, ldw, nullptr, 0, sw, sw_sn,
+                               sw_sk, gran_n, y, y_dt, ldy, b);
+  clear_hip_error();
+  launch_gemm<false, false>(a, gran_n, y_dt == SG_BF16, form == SG_OUT_YT, stream);
+  return launch_status();
+}
+
 extern "C" sg_status sg_fp8_gemm_groupwise(int64_t M, int64_t N, int64_t K, const uint8_t* xq,
                                            int64_t ldx, const float* sx, int64_t sx_sm,
                                            int64_t sx_sk, int gran_m, const uint8_t* wq,
                                            int64_t ldw, const float* sw, int64_t sw_sn,
                                            int64_t sw_sk, int gran_n, void* y, sg_dtype y_dt,
                                            int64_t ldy, sg_form form, hipStream_t stream) {
-  sg_status st = check_common(M, N, K, xq, ldx, sx, sx_sm, sx_sk, gran_m, sw, sw_sn, sw_sk, gran_n, y, y_dt, ldy, form);
-  if (st != SG_OK) return st;
-  if (!wq) return SG_ERR_NULL;
-  if (ldw < K || ldw >= (1LL << 24)) return SG_ERR_SHAPE;
-  if (!aligned(wq, 16) || ldw % 16) return SG_ERR_ALIGN;
-  if (M == 0 || N == 0) return SG_OK;
-  const GemmArgs a = make_args(M, N, K, xq, ldx, sx, sx_sm, sx_sk, gran_m, wq, ldw, nullptr, 0, sw, sw_sn,
-                               sw_sk, gran_n, y, y_dt, ldy);
-  clear_hip_error();
-  launch_gemm<false, false>(a, gran_n, y_dt == SG_BF16, form == SG_OUT_YT, stream);
-  return launch_status();
+  return dense_gemm(M, N, K, xq, ldx, sx, sx_sm, sx_sk, gran_m, wq, ldw, sw, sw_sn, sw_sk, gran_n, y, y_dt, ldy,
+                    form, Batch{}, stream);
+}
+
+extern "C" sg_status sg_fp8_gemm_groupwise_batched(int64_t L, int64_t M, int64_t N, int64_t K, const uint8_t* xq,
+                                                   int64_t ldx, int64_t x_bs, const float* sx, int64_t sx_sm,
+                                                   int64_t sx_sk, int64_t sx_bs, int gran_m, const uint8_t* wq,
+                                                   int64_t ldw, int64_t w_bs, const float* sw, int64_t sw_sn,
+                                                   int64_t sw_sk, int64_t sw_bs, int gran_n, void* y,
+                                                   sg_dtype y_dt, int64_t ldy, int64_t y_bs, sg_form form,
+                                                   hipStream_t stream) {
+  Batch b;
+  b.L = L; b.bx = x_bs; b.bw = w_bs; b.bsx = sx_bs; b.bsw = sw_bs; b.by = y_bs;
+  return dense_gemm(M, N, K, xq, ldx, sx, sx_sm, sx_sk, gran_m, wq, ldw, sw, sw_sn, sw_sk, gran_n, y, y_dt, ldy,
+                    form, b, stream);
 }
 
 // The 2:4 GEMM entry points: FP8 (e4m3) or int8 codes, canonical (values +
@@ -1227,15 +1375,17 @@ template <bool I8>
 static sg_status sparse24_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* xq, int64_t ldx, const float* sx,
                                int64_t sx_sm, int64_t sx_sk, int gran_m, const uint8_t* wv, int64_t ldwv,
                                const uint8_t* wmeta, int64_t ldwm, const float* sw, int64_t sw_sn, int64_t sw_sk,
-                               int gran_n, void* y, sg_dtype y_dt, int64_t ldy, sg_form form, hipStream_t stream) {
+                               int gran_n, void* y, sg_dtype y_dt, int64_t ldy, sg_form form, const Batch& b,
+                               hipStream_t stream) {
   sg_status st = check_common(M, N, K, xq, ldx, sx, sx_sm, sx_sk, gran_m, sw, sw_sn, sw_sk, gran_n, y, y_dt, ldy, form);
   if (st != SG_OK) return st;
+  if ((st = check_batch(b)) != SG_OK) return st;
   if (!wv || !wmeta) return SG_ERR_NULL;
   if (ldwv < K / 2 || ldwm < K / 8 || ldwv >= (1LL << 24) || ldwm >= (1LL << 24)) return SG_ERR_SHAPE;
   if (!aligned(wv, 16) || !aligned(wmeta, 16) || ldwv % 16 || ldwm % 16) return SG_ERR_ALIGN;
-  if (M == 0 || N == 0) return SG_OK;
+  if (M == 0 || N == 0 || b.L == 0) return SG_OK;
   const GemmArgs a = make_args(M, N, K, xq, ldx, sx, sx_sm, sx_sk, gran_m, wv, ldwv, wmeta, ldwm, sw, sw_sn,
-                               sw_sk, gran_n, y, y_dt, ldy);
+                               sw_sk, gran_n, y, y_dt, ldy, b);
   clear_hip_error();
   launch_gemm<true, false, I8>(a, gran_n, y_dt == SG_BF16, form == SG_OUT_YT, stream);
   return launch_status();
@@ -1246,16 +1396,17 @@ static sg_status sparse24_gemm_packed(int64_t M, int64_t N, int64_t K, const uin
                                       const float* sx, int64_t sx_sm, int64_t sx_sk, int gran_m,
                                       const uint8_t* wpacked, const float* sw, int64_t sw_sn, int64_t sw_sk,
                                       int gran_n, void* y, sg_dtype y_dt, int64_t ldy, sg_form form,
-                                      hipStream_t stream) {
+                                      const Batch& b, hipStream_t stream) {
   sg_status st = check_common(M, N, K, xq, ldx, sx, sx_sm, sx_sk, gran_m, sw, sw_sn, sw_sk, gran_n, y, y_dt, ldy, form);
   if (st != SG_OK) return st;
+  if ((st = check_batch(b)) != SG_OK) return st;
   if (!wpacked) return SG_ERR_NULL;
   if (!aligned(wpacked, 16)) return SG_ERR_ALIGN;
   // the large-M kernel addresses a tile's 16 row blocks with 32-bit offsets
   if ((K / 128) * (int64_t)(BN / PK_ROWS) * PK_CHUNK > 0x7fffffffLL) return SG_ERR_SHAPE;
-  if (M == 0 || N == 0) return SG_OK;
+  if (M == 0 || N == 0 || b.L == 0) return SG_OK;
   const GemmArgs a = make_args(M, N, K, xq, ldx, sx, sx_sm, sx_sk, gran_m, wpacked, 0, nullptr, 0, sw, sw_sn,
-                               sw_sk, gran_n, y, y_dt, ldy);
+                               sw_sk, gran_n, y, y_dt, ldy, b);
   clear_hip_error();
   launch_gemm<true, true, I8>(a, gran_n, y_dt == SG_BF16, form == SG_OUT_YT, stream);
   return launch_status();
@@ -1269,7 +1420,7 @@ extern "C" sg_status sg_fp8_sparse24_gemm_groupwise(int64_t M, int64_t N, int64_
                                                     int gran_n, void* y, sg_dtype y_dt, int64_t ldy,
                                                     sg_form form, hipStream_t stream) {
   return sparse24_gemm<false>(M, N, K, xq, ldx, sx, sx_sm, sx_sk, gran_m, wv, ldwv, wmeta, ldwm, sw, sw_sn, sw_sk,
-                              gran_n, y, y_dt, ldy, form, stream);
+                              gran_n, y, y_dt, ldy, form, Batch{}, stream);
 }
 
 extern "C" sg_status sg_fp8_sparse24_gemm_groupwise_packed(int64_t M, int64_t N, int64_t K, const uint8_t* xq,
@@ -1279,7 +1430,7 @@ extern "C" sg_status sg_fp8_sparse24_gemm_groupwise_packed(int64_t M, int64_t N,
                                                            int gran_n, void* y, sg_dtype y_dt, int64_t ldy,
                                                            sg_form form, hipStream_t stream) {
   return sparse24_gemm_packed<false>(M, N, K, xq, ldx, sx, sx_sm, sx_sk, gran_m, wpacked, sw, sw_sn, sw_sk, gran_n,
-                                     y, y_dt, ldy, form, stream);
+                                     y, y_dt, ldy, form, Batch{}, stream);
 }
 
 extern "C" sg_status sg_int8_sparse24_gemm_groupwise(int64_t M, int64_t N, int64_t K, const int8_t* xq,
@@ -1291,7 +1442,7 @@ extern "C" sg_status sg_int8_sparse24_gemm_groupwise(int64_t M, int64_t N, int64
                                                      sg_form form, hipStream_t stream) {
   return sparse24_gemm<true>(M, N, K, reinterpret_cast<const uint8_t*>(xq), ldx, sx, sx_sm, sx_sk, gran_m,
                              reinterpret_cast<const uint8_t*>(wv), ldwv, wmeta, ldwm, sw, sw_sn, sw_sk, gran_n, y,
-                             y_dt, ldy, form, stream);
+                             y_dt, ldy, form, Batch{}, stream);
 }
 
 extern "C" sg_status sg_int8_sparse24_gemm_groupwise_packed(int64_t M, int64_t N, int64_t K, const int8_t* xq,
@@ -1301,5 +1452,30 @@ extern "C" sg_status sg_int8_sparse24_gemm_groupwise_packed(int64_t M, int64_t N
                                                             int gran_n, void* y, sg_dtype y_dt, int64_t ldy,
                                                             sg_form form, hipStream_t stream) {
   return sparse24_gemm_packed<true>(M, N, K, reinterpret_cast<const uint8_t*>(xq), ldx, sx, sx_sm, sx_sk, gran_m,
-                                    wpacked, sw, sw_sn, sw_sk, gran_n, y, y_dt, ldy, form, stream);
+                                    wpacked, sw, sw_sn, sw_sk, gran_n, y, y_dt, ldy, form, Batch{}, stream);
+}
+
+// Batched 2:4 GEMMs ("L" mode): L problems of one shape, each operand at its
+// own batch stride.
+extern "C" sg_status sg_fp8_sparse24_gemm_groupwise_batched(
+    int64_t L, int64_t M, int64_t N, int64_t K, const uint8_t* xq, int64_t ldx, int64_t x_bs, const float* sx,
+    int64_t sx_sm, int64_t sx_sk, int64_t sx_bs, int gran_m, const uint8_t* wv, int64_t ldwv, int64_t wv_bs,
+    const uint8_t* wmeta, int64_t ldwm, int64_t wm_bs, const float* sw, int64_t sw_sn, int64_t sw_sk,
+    int64_t sw_bs, int gran_n, void* y, sg_dtype y_dt, int64_t ldy, int64_t y_bs, sg_form form,
+    hipStream_t stream) {
+  Batch b;
+  b.L = L; b.bx = x_bs; b.bw = wv_bs; b.bm = wm_bs; b.bsx = sx_bs; b.bsw = sw_bs; b.by = y_bs;
+  return sparse24_gemm<false>(M, N, K, xq, ldx, sx, sx_sm, sx_sk, gran_m, wv, ldwv, wmeta, ldwm, sw, sw_sn, sw_sk,
+                              gran_n, y, y_dt, ldy, form, b, stream);
+}
+
+extern "C" sg_status sg_fp8_sparse24_gemm_groupwise_packed_batched(
+    int64_t L, int64_t M, int64_t N, int64_t K, const uint8_t* xq, int64_t ldx, int64_t x_bs, const float* sx,
+    int64_t sx_sm, int64_t sx_sk, int64_t sx_bs, int gran_m, const uint8_t* wpacked, int64_t wp_bs,
+    const float* sw, int64_t sw_sn, int64_t sw_sk, int64_t sw_bs, int gran_n, void* y, sg_dtype y_dt,
+    int64_t ldy, int64_t y_bs, sg_form form, hipStream_t stream) {
+  Batch b;
+  b.L = L; b.bx = x_bs; b.bw = wp_bs; b.bsx = sx_bs; b.bsw = sw_bs; b.by = y_bs;
+  return sparse24_gemm_packed<false>(M, N, K, xq, ldx, sx, sx_sm, sx_sk, gran_m, wpacked, sw, sw_sn, sw_sk, gran_n,
+                                     y, y_dt, ldy, form, b, stream);
 }

@@ -82,22 +82,43 @@ __device__ __forceinline__ void stage_quad(uint8_t* t0, uint8_t* t1, int nl, int
   }
 }
 
-template <int Q, bool OUT_BF16, bool OUT_T, int BUF>
+// SCALE = 0: the sums are final.  SCALE = 1 (fp32 sums) or 2 (exact int32
+// sums, added as integers): scales constant along K are applied here, once:
+// sxp[16 j] is the X scale of the lane's column in sub-tile column j and
+// swp[16 i' + e] the W scale of row 16 i' + e (i' = 4 Q + i) of the wave's
+// rows; both live in LDS that the exchange and the staged tile leave alone.
+template <int Q, bool OUT_BF16, bool OUT_T, int BUF, int SCALE = 0>
 __device__ __forceinline__ void x2_finish(const uint8_t* src, uint8_t* t0, uint8_t* t1, const v4f (&acc)[8][4],
-                                          int w4, int l, int wn, int wm, int g, int lr) {
+                                          int w4, int l, int wn, int wm, int g, int lr,
+                                          const float* sxp = nullptr, const float* swp = nullptr) {
   float4 part[16];
 #pragma unroll
   for (int k = 0; k < 16; ++k) part[k] = reinterpret_cast<const float4*>(src)[((w4 * 16 + k) << 6) + l];
   __syncthreads();   // every wave has its partner's partials: the buffers may be overwritten
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 4; ++i) {
+    float4 sw = make_float4(1.f, 1.f, 1.f, 1.f);
+    if (SCALE) sw = *reinterpret_cast<const float4*>(swp + (4 * Q + i) * 16);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const float4 o = part[i * 4 + j];
       const v4f av = acc[4 * Q + i][j];
-      const float v[4] = {av[0] + o.x, av[1] + o.y, av[2] + o.z, av[3] + o.w};
+      float v[4];
+      if (SCALE == 2) {
+        const v4i ai = __builtin_bit_cast(v4i, av);
+        const int4 oi = __builtin_bit_cast(int4, o);
+        v[0] = (float)(ai[0] + oi.x); v[1] = (float)(ai[1] + oi.y);
+        v[2] = (float)(ai[2] + oi.z); v[3] = (float)(ai[3] + oi.w);
+      } else {
+        v[0] = av[0] + o.x; v[1] = av[1] + o.y; v[2] = av[2] + o.z; v[3] = av[3] + o.w;
+      }
+      if (SCALE) {
+        const float sx = sxp[16 * j];
+        v[0] *= sw.x * sx; v[1] *= sw.y * sx; v[2] *= sw.z * sx; v[3] *= sw.w * sx;
+      }
       stage_quad<OUT_BF16, OUT_T, BUF>(t0, t1, wn * 128 + (4 * Q + i) * 16 + 4 * g, wm * 64 + j * 16 + lr, v);
     }
+  }
 }
 
 // Stores the staged tile: 16-byte chunks of whole rows, non-temporal (the

@@ -41,7 +41,9 @@ def test_header_declares_the_entry_points():
         "sg_sparse24_prune_compress", "sg_fp8_gemm_groupwise", "sg_fp8_sparse24_gemm_groupwise",
         "sg_mixed_gemm_add", "sg_sparse24_packed_bytes", "sg_sparse24_pack_gfx950",
         "sg_fp8_sparse24_gemm_groupwise_packed", "sg_probe_matrix_ops", "sg_probe_matrix_rate",
-        "sg_int8_quant_groupwise", "sg_int8_sparse24_gemm_groupwise", "sg_int8_sparse24_gemm_groupwise_packed"])
+        "sg_int8_quant_groupwise", "sg_int8_sparse24_gemm_groupwise", "sg_int8_sparse24_gemm_groupwise_packed",
+        "sg_fp8_gemm_groupwise_batched", "sg_fp8_sparse24_gemm_groupwise_batched",
+        "sg_fp8_sparse24_gemm_groupwise_packed_batched"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -252,3 +254,57 @@ def test_probe_operation_counts():
     assert lib.sg_probe_matrix_ops(1, 3) == 3 * 2 * 16 * 16 * 128 * 8 * 8 * 1024
     assert lib.sg_probe_matrix_ops(2, 1) == 2 * 16 * 16 * 64 * 8 * 8 * 1024
     assert lib.sg_probe_matrix_ops(5, 1) == -1 and lib.sg_probe_matrix_ops(0, 0) == -1
+
+
+def batched(kind, **kw):
+    a = dict(L=3, M=64, N=256, K=256, x=P, ldx=256, xb=64 * 256, sx=P3, sxm=1, sxk=64, sxb=64 * 2, gm=1, w=P2,
+             ldw=256, wb=256 * 256, meta=P3, ldm=32, mb=256 * 32, sw=P3, swn=2, swk=1, swb=4, gn=128, y=P, ydt=1,
+             ldy=256, yb=64 * 256, form=0)
+    a.update(kw)
+    lib = sg.lib()
+    if kind == "dense":
+        return lib.sg_fp8_gemm_groupwise_batched(
+            a["L"], a["M"], a["N"], a["K"], a["x"], a["ldx"], a["xb"], a["sx"], a["sxm"], a["sxk"], a["sxb"], a["gm"],
+            a["w"], a["ldw"], a["wb"], a["sw"], a["swn"], a["swk"], a["swb"], a["gn"], a["y"], a["ydt"], a["ldy"],
+            a["yb"], a["form"], None)
+    if kind == "sparse":
+        ldw = a["ldw"] if "ldw" in kw else a["K"] // 2
+        return lib.sg_fp8_sparse24_gemm_groupwise_batched(
+            a["L"], a["M"], a["N"], a["K"], a["x"], a["ldx"], a["xb"], a["sx"], a["sxm"], a["sxk"], a["sxb"], a["gm"],
+            a["w"], ldw, a["wb"], a["meta"], a["ldm"], a["mb"], a["sw"], a["swn"], a["swk"], a["swb"], a["gn"],
+            a["y"], a["ydt"], a["ldy"], a["yb"], a["form"], None)
+    return lib.sg_fp8_sparse24_gemm_groupwise_packed_batched(
+        a["L"], a["M"], a["N"], a["K"], a["x"], a["ldx"], a["xb"], a["sx"], a["sxm"], a["sxk"], a["sxb"], a["gm"],
+        a["w"], a["wb"], a["sw"], a["swn"], a["swk"], a["swb"], a["gn"], a["y"], a["ydt"], a["ldy"], a["yb"],
+        a["form"], None)
+
+
+BATCH_CASES = [
+    (dict(L=-1), SHAPE), (dict(L=65536), SHAPE), (dict(xb=-16), SHAPE), (dict(sxb=-1), SHAPE),
+    (dict(swb=-1), SHAPE), (dict(yb=-1), SHAPE), (dict(wb=-16), SHAPE),
+    (dict(xb=8), ALIGN), (dict(wb=24), ALIGN),
+    (dict(L=0), OK), (dict(M=0), OK),
+    (dict(x=None), NULL), (dict(w=None), NULL), (dict(K=200), SHAPE), (dict(gm=64), UNSUP),
+]
+
+
+@no_gpu
+@pytest.mark.parametrize("kind", ["dense", "sparse", "packed"])
+@pytest.mark.parametrize("kw,code", BATCH_CASES)
+def test_batched_gemm_validation(kind, kw, code):
+    assert batched(kind, **kw) == code
+
+
+@no_gpu
+def test_batched_sparse_metadata_stride_must_be_aligned():
+    assert batched("sparse", mb=8) == ALIGN and batched("sparse", meta=None) == NULL
+
+
+def test_k_constant_scale_views():
+    s = torch.arange(5, dtype=torch.float32)
+    v = sg.k_constant_scales(s, 5, 512)
+    assert v.shape == (5, 4) and v.stride() == (1, 0) and torch.equal(v[:, 3], s)
+    t = sg.k_constant_scales(torch.ones(1), 7, 256)
+    assert t.shape == (7, 2) and t.stride() == (0, 0)
+    with pytest.raises(sg.SgError):
+        sg.k_constant_scales(torch.ones(3), 5, 128)

@@ -1,0 +1,205 @@
+"""GPU parity of scales constant along K (rowwise / tensorwise, applied once
+after the K loop in the large-M kernels) and of the batched ("L" mode) GEMMs,
+against the oracle: ragged shapes, both output forms, fp32 and bf16 outputs,
+dense / canonical 2:4 / packed 2:4 weights, FP8 and int8 codes, the decode
+sizes (which keep the per-block kernels), and the full 2048 x 4096 x 4096
+size on sampled outputs."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_gemm_layers_amd as sg
+import workloads
+from gpu_helpers import DEV, assert_within_tolerance, down, say, up, up_scales
+
+pytestmark = pytest.mark.gpu
+
+
+def rowwise_operands(m, n, k, seed, tensor=False, int8=False, sparse=True):
+    """Codes with one scale per row over the whole row (the oracle's quantiser
+    with one block per row), or one per tensor (one block for the tensor)."""
+    d = workloads.sparse_large(seed=seed, m=m, n=n, k=k)
+    quant = oracle.int8_quant_groupwise if int8 else oracle.fp8_quant_groupwise
+    xq, sx = quant(d["x"], m if tensor else 1, k)
+    if sparse:
+        wv32, meta = oracle.prune_compress24(d["w"])
+        wq, sw = quant(wv32, n if tensor else 1, k // 2)
+    else:
+        wq, sw = quant(d["w"], n if tensor else 1, k)
+        meta = None
+    return xq, sx[:, 0].copy(), wq, meta, sw[:, 0].copy()
+
+
+def run_rowwise(kind, xq, sx, wq, meta, sw, n, k, out_dtype, form, int8=False):
+    m = xq.shape[0]
+    sxt = sg.k_constant_scales(up(sx), m, k)
+    swt = sg.k_constant_scales(up(sw), n, k)
+    if kind == "dense":
+        return sg.fp8_gemm_groupwise(up(xq), sxt, up(wq), swt, 1, 1, out_dtype=out_dtype, form=form)
+    if kind == "sparse":
+        f = sg.int8_sparse24_gemm_groupwise if int8 else sg.fp8_sparse24_gemm_groupwise
+        return f(up(xq), sxt, up(wq), up(meta), swt, 1, 1, out_dtype=out_dtype, form=form)
+    wp = sg.sparse24_pack_gfx950(up(wq), up(meta))
+    f = sg.int8_sparse24_gemm_groupwise_packed if int8 else sg.fp8_sparse24_gemm_groupwise_packed
+    return f(up(xq), sxt, wp, n, swt, 1, 1, out_dtype=out_dtype, form=form)
+
+
+def check_rowwise(kind, m, n, k, seed, tensor=False, int8=False, out_dtype=torch.bfloat16, forms=("y", "yt")):
+    say(f"rowwise {kind} M={m} N={n} K={k} tensor={tensor} int8={int8} {out_dtype} seed={seed}")
+    xq, sx, wq, meta, sw = rowwise_operands(m, n, k, seed, tensor, int8, sparse=kind != "dense")
+    if kind == "dense":
+        ref, bound = oracle.fp8_gemm_rowwise(xq, sx, wq, sw, bound=True)
+    elif int8:
+        ref, bound = oracle.int8_sparse24_gemm_rowwise(xq, sx, wq, meta, sw, bound=True)
+    else:
+        ref, bound = oracle.fp8_sparse24_gemm_rowwise(xq, sx, wq, meta, sw, bound=True)
+    outs = {}
+    for form in forms:
+        got = down(run_rowwise(kind, xq, sx, wq, meta, sw, n, k, out_dtype, form, int8))
+        got = got.T if form == "yt" else got
+        assert got.shape == (m, n)
+        assert_within_tolerance(got.astype(np.float64), ref, bound, f"form={form}")
+        outs[form] = got
+    if len(outs) == 2:
+        assert np.array_equal(outs["y"], outs["yt"])
+
+
+# M > 64 takes the accumulate-then-scale kernels; partial M and N tiles, K
+# blocks of either parity (the last double stage half full), and M <= 64
+# (the per-block decode kernels reading repeated scales).
+SHAPES = [(65, 256, 128), (128, 256, 256), (200, 300, 384), (129, 513, 640), (300, 1000, 896),
+          (16, 256, 256), (37, 300, 384)]
+
+
+@pytest.mark.parametrize("kind", ["packed", "sparse", "dense"])
+@pytest.mark.parametrize("m,n,k", SHAPES)
+def test_rowwise_ragged(kind, m, n, k):
+    check_rowwise(kind, m, n, k, seed=m + n + k)
+
+
+@pytest.mark.parametrize("kind", ["packed", "dense"])
+@pytest.mark.parametrize("m", [16, 200])
+def test_tensorwise(kind, m):
+    check_rowwise(kind, m, 384, 512, seed=31 + m, tensor=True)
+
+
+@pytest.mark.parametrize("kind", ["packed", "sparse"])
+@pytest.mark.parametrize("m,n,k", [(65, 256, 128), (200, 300, 384), (300, 700, 1024), (37, 512, 256)])
+def test_int8_rowwise_exact_sums(kind, m, n, k):
+    check_rowwise(kind, m, n, k, seed=7 * m + n, int8=True)
+
+
+@pytest.mark.parametrize("kind", ["packed", "dense"])
+def test_rowwise_fp32_output(kind):
+    check_rowwise(kind, 150, 260, 384, seed=41, out_dtype=torch.float32)
+
+
+def test_rowwise_128_row_blocks_constant_along_k():
+    """gran 128 with K-block stride 0: one scale per 128 rows for all of K."""
+    m, n, k = 200, 384, 512
+    say(f"rowwise gran 128 M={m} N={n} K={k}")
+    d = workloads.sparse_large(seed=43, m=m, n=n, k=k)
+    xq, sx = oracle.fp8_quant_groupwise(d["x"], 128, k)
+    wv32, meta = oracle.prune_compress24(d["w"])
+    wq, sw = oracle.fp8_quant_groupwise(wv32, 128, k // 2)
+    kb = k // 128
+    sxe, swe = np.repeat(sx, kb, axis=1), np.repeat(sw, kb, axis=1)
+    ref, bound = oracle.fp8_sparse24_gemm_groupwise(xq, sxe, 128, wq, meta, swe, 128, bound=True)
+    sxt = up(sx[:, 0].copy())[:, None].expand(sx.shape[0], kb)
+    swt = up(sw[:, 0].copy())[:, None].expand(sw.shape[0], kb)
+    wp = sg.sparse24_pack_gfx950(up(wq), up(meta))
+    got = down(sg.fp8_sparse24_gemm_groupwise_packed(up(xq), sxt, wp, n, swt, 128, 128))
+    assert_within_tolerance(got, ref, bound, "gran 128")
+
+
+def test_rowwise_full_size_sampled():
+    """2048 x 4096 x 4096 packed 2:4, rowwise scales, in the launch the benchmark
+    times; 4096 sampled outputs against the oracle, computed one by one."""
+    m, n, k = 2048, 4096, 4096
+    say(f"rowwise full size M={m} N={n} K={k}")
+    xq, sx, wq, meta, sw = rowwise_operands(m, n, k, seed=44)
+    got = down(run_rowwise("packed", xq, sx, wq, meta, sw, n, k, torch.bfloat16, "y"))
+    rng = np.random.default_rng(45)
+    rows = np.concatenate([[0, m - 1], rng.integers(0, m, 62)])
+    cols = np.concatenate([[0, n - 1], rng.integers(0, n, 62)])
+    wd = oracle.decompress24(wq[cols], meta[cols])
+    ref, bound = oracle.fp8_gemm_rowwise(xq[rows], sx[rows], wd, sw[cols], bound=True)
+    assert_within_tolerance(got[np.ix_(rows, cols)], ref, bound, "full size sample")
+
+
+# --------------------------------------------------------------- batched
+
+def batched_operands(L, m, n, k, seed, gm=1, gn=128):
+    xs, sxs, wqs, metas, sws = [], [], [], [], []
+    for z in range(L):
+        d = workloads.sparse_large(seed=seed + z, m=m, n=n, k=k)
+        xq, sx = oracle.fp8_quant_groupwise(d["x"], gm, 128)
+        wv32, meta = oracle.prune_compress24(d["w"])
+        wq, sw = oracle.fp8_quant_groupwise(wv32, gn, 64)
+        xs.append(xq); sxs.append(sx); wqs.append(wq); metas.append(meta); sws.append(sw)
+    return [np.stack(a) for a in (xs, sxs, wqs, metas, sws)]
+
+
+def up_scales3(s):
+    """[L, rows, KB] oracle scales -> device [L, rows, KB] view, each problem M-major."""
+    return torch.from_numpy(np.ascontiguousarray(np.swapaxes(s, 1, 2))).to(DEV).transpose(1, 2)
+
+
+@pytest.mark.parametrize("kind", ["packed", "sparse", "dense"])
+@pytest.mark.parametrize("L,m,n,k,form", [(3, 200, 300, 384, "y"), (2, 16, 512, 256, "y"), (4, 129, 256, 256, "yt"),
+                                          (1, 70, 260, 128, "y")])
+def test_batched(kind, L, m, n, k, form):
+    say(f"batched {kind} L={L} M={m} N={n} K={k} form={form}")
+    xq, sx, wq, meta, sw = batched_operands(L, m, n, k, seed=50 + L + m)
+    if kind == "dense":
+        wd = np.stack([oracle.decompress24(wq[z], meta[z]) for z in range(L)])
+        y = sg.fp8_gemm_groupwise_batched(up(xq), up_scales3(sx), up(wd), up_scales3(sw), 1, 128, form=form)
+    elif kind == "sparse":
+        y = sg.fp8_sparse24_gemm_groupwise_batched(up(xq), up_scales3(sx), up(wq), up(meta), up_scales3(sw), 1, 128,
+                                                   form=form)
+    else:
+        wp = torch.stack([sg.sparse24_pack_gfx950(up(wq[z]), up(meta[z])) for z in range(L)])
+        y = sg.fp8_sparse24_gemm_groupwise_packed_batched(up(xq), up_scales3(sx), wp, n, up_scales3(sw), 1, 128,
+                                                          form=form)
+    got = down(y)
+    for z in range(L):
+        ref, bound = oracle.fp8_sparse24_gemm_groupwise(xq[z], sx[z], 1, wq[z], meta[z], sw[z], 128, bound=True)
+        gz = got[z].T if form == "yt" else got[z]
+        assert_within_tolerance(gz, ref, bound, f"problem {z}")
+
+
+@pytest.mark.parametrize("m", [16, 200])
+def test_batched_shared_weight_and_rowwise(m):
+    """One packed weight for every problem (batch stride 0), rowwise scales."""
+    L, n, k = 3, 384, 512
+    say(f"batched shared weight rowwise L={L} M={m} N={n} K={k}")
+    d = [workloads.sparse_large(seed=60 + z, m=m, n=n, k=k) for z in range(L)]
+    wv32, meta = oracle.prune_compress24(d[0]["w"])
+    wq, sw = oracle.fp8_quant_groupwise(wv32, 1, k // 2)
+    xs = [oracle.fp8_quant_groupwise(dz["x"], 1, k) for dz in d]
+    xq = np.stack([a for a, _ in xs])
+    sx = np.stack([s[:, 0] for _, s in xs])                        # [L, M]
+    sxt = up(sx)[:, :, None].expand(L, m, k // 128)
+    swt = sg.k_constant_scales(up(sw[:, 0].copy()), n, k)
+    wp = sg.sparse24_pack_gfx950(up(wq), up(meta))
+    got = down(sg.fp8_sparse24_gemm_groupwise_packed_batched(up(xq), sxt, wp, n, swt, 1, 1))
+    for z in range(L):
+        ref, bound = oracle.fp8_sparse24_gemm_rowwise(xq[z], sx[z], wq, meta, sw[:, 0], bound=True)
+        assert_within_tolerance(got[z], ref, bound, f"problem {z}")
+
+
+def test_batched_output_leaves_other_memory_alone():
+    """Problem z writes only its own slice of a padded output."""
+    L, m, n, k = 3, 100, 260, 256
+    say(f"batched padded output L={L} M={m} N={n} K={k}")
+    xq, sx, wq, meta, sw = batched_operands(L, m, n, k, seed=70)
+    ybuf = torch.full((L, m + 3, n + 8), 5.0, dtype=torch.bfloat16, device=DEV)
+    wp = torch.stack([sg.sparse24_pack_gfx950(up(wq[z]), up(meta[z])) for z in range(L)])
+    sg.fp8_sparse24_gemm_groupwise_packed_batched(up(xq), up_scales3(sx), wp, n, up_scales3(sw), 1, 128,
+                                                  y=ybuf[:, :m, :n])
+    yb = down(ybuf)
+    assert np.all(yb[:, m:, :] == 5.0) and np.all(yb[:, :, n:] == 5.0)
+    for z in range(L):
+        ref, bound = oracle.fp8_sparse24_gemm_groupwise(xq[z], sx[z], 1, wq[z], meta[z], sw[z], 128, bound=True)
+        assert_within_tolerance(yb[z, :m, :n], ref, bound, f"problem {z}")
