@@ -50,6 +50,11 @@ so the scale can be applied once, after the whole K sum.  The full-K sum is
 still exact in fp64 (integer multiples of 2^-18 below 2^(17.6 + log2 K) <
 2^53 quanta for K < 2^17).
 
+Bias epilogue: the sparse FP8 linear implementation torchao PR #3258's review
+points to takes a bias argument; a linear layer adds it to every row of the
+output, y[m, n] + bias[n], after the scales.  In the tolerance the bias is one
+more term of the abs-sum with scale 1 (like the bf16 part of the fused add).
+
 Tolerance (the accepted error of a GPU result g against the oracle y):
     |g - y| <= 1e-2 |y| + 1e-3 T,
     T[m, n] = sum_kb s(m, n, kb) * sum_{k in kb} |dec x * dec w|  (+ sum |x2 w2|).
@@ -170,6 +175,14 @@ def int8_sparse24_gemm_rowwise(xq, sx, wv, wmeta, sw, bound: bool = False):
     wq = decompress24(np.asarray(wv, dtype=np.int8).view(np.uint8), wmeta).view(np.int8)
     xd = np.asarray(xq, dtype=np.int8).astype(np.float64)
     return _rowwise(xd, sx, wq.astype(np.float64), sw, bound)
+
+
+def add_bias(y, bound, bias):
+    """The bias epilogue: y [M, N] fp64 (and its bound T) plus bias fp32 [N]
+    on every row; returns (y + bias, T + |bias|)."""
+    b = np.asarray(bias, dtype=np.float32).astype(np.float64).reshape(1, -1)
+    assert b.shape[1] == y.shape[1]
+    return y + b, bound + np.abs(b)
 
 
 def mixed_gemm_add(x1p, sx1, w1p, sw1, x2, w2, bound: bool = False):

@@ -216,3 +216,11 @@ def test_rowwise_bound_without_abs_is_caught(monkeypatch):
         return (y, y) if bound else y
     monkeypatch.setattr(gemm_mod, "_rowwise", rowwise)
     _fails(t_row.test_rowwise_bound_dominates_and_is_tight_for_nonnegative_codes)
+
+
+def test_bias_on_rows_instead_of_columns_is_caught(monkeypatch):
+    def add_bias(y, bound, bias):
+        b = np.asarray(bias, np.float64)
+        return y + np.resize(b, y.shape[0])[:, None], bound + np.abs(np.resize(b, y.shape[0]))[:, None]
+    monkeypatch.setattr(oracle, "add_bias", add_bias)
+    _fails(t_row.test_bias_adds_per_output_column_exactly_on_integers)

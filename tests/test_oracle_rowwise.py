@@ -114,3 +114,26 @@ def test_rowwise_bound_dominates_and_is_tight_for_nonnegative_codes():
     xp, wp = xq & 0x7F, wq & 0x7F
     yp, tp = oracle.fp8_gemm_rowwise(xp, sx, wp, sw, bound=True)
     assert np.array_equal(yp, tp)
+
+
+def test_bias_on_zero_product_is_the_bias_exactly():
+    rng = np.random.default_rng(19)
+    xq = np.zeros((5, 128), np.uint8)
+    wq = _codes(rng, (7, 128))
+    bias = (rng.standard_normal(7) * 10).astype(np.float32)
+    y, t = oracle.fp8_gemm_rowwise(xq, _scales(rng, 5), wq, _scales(rng, 7), bound=True)
+    yb, tb = oracle.add_bias(y, t, bias)
+    assert np.array_equal(yb, np.broadcast_to(bias.astype(np.float64), (5, 7)))
+    assert np.array_equal(tb, np.abs(yb))
+
+
+def test_bias_adds_per_output_column_exactly_on_integers():
+    rng = np.random.default_rng(20)
+    xi = rng.integers(-8, 9, size=(4, 256))
+    wi = rng.integers(-8, 9, size=(6, 256))
+    bias = rng.integers(-1000, 1000, size=6).astype(np.float32)
+    xq, wq = oracle.e4m3_encode(xi.astype(np.float32)), oracle.e4m3_encode(wi.astype(np.float32))
+    y, t = oracle.fp8_gemm_rowwise(xq, np.ones(1, np.float32), wq, np.ones(1, np.float32), bound=True)
+    yb, tb = oracle.add_bias(y, t, bias)
+    assert np.array_equal(yb, (xi @ wi.T + bias.astype(np.int64)[None, :]).astype(np.float64))
+    assert np.array_equal(tb, (np.abs(xi) @ np.abs(wi).T + np.abs(bias).astype(np.int64)[None, :]).astype(np.float64))
