@@ -299,6 +299,10 @@ sg_status sg_int8_sparse24_gemm_groupwise_packed(int64_t M, int64_t N, int64_t K
  * [P2095] PR description: the scale layout (M / ScaleGranularityM, K_TILES, L)
  * carries the batch L as its outermost mode.  Every problem follows its
  * single-problem entry point; L == 1 with zero strides is that call.
+ * bias (may be NULL: no bias): fp32 [N] per problem, at bias + z * bias_bs,
+ * 4-byte aligned; bias[n] is added to output row n of every column after the
+ * scales and before the output rounding (the `bias` argument of the sparse
+ * FP8 linear that jcaip's review in [T3258] points to).
  * Requires in addition 0 <= L <= 65535 (L == 0: SG_OK, nothing enqueued),
  * every batch stride >= 0, and x_bs, w_bs / wv_bs / wp_bs, wm_bs multiples of 16
  * (SG_ERR_ALIGN otherwise).  Outputs of different problems must not overlap;
@@ -308,24 +312,26 @@ sg_status sg_fp8_gemm_groupwise_batched(int64_t L, int64_t M, int64_t N, int64_t
                                         int64_t ldx, int64_t x_bs, const float* sx, int64_t sx_sm,
                                         int64_t sx_sk, int64_t sx_bs, int gran_m, const uint8_t* wq,
                                         int64_t ldw, int64_t w_bs, const float* sw, int64_t sw_sn,
-                                        int64_t sw_sk, int64_t sw_bs, int gran_n, void* y, sg_dtype y_dt,
-                                        int64_t ldy, int64_t y_bs, sg_form form, hipStream_t stream);
+                                        int64_t sw_sk, int64_t sw_bs, int gran_n, const float* bias,
+                                        int64_t bias_bs, void* y, sg_dtype y_dt, int64_t ldy, int64_t y_bs,
+                                        sg_form form, hipStream_t stream);
 
 sg_status sg_fp8_sparse24_gemm_groupwise_batched(int64_t L, int64_t M, int64_t N, int64_t K, const uint8_t* xq,
                                                  int64_t ldx, int64_t x_bs, const float* sx, int64_t sx_sm,
                                                  int64_t sx_sk, int64_t sx_bs, int gran_m, const uint8_t* wv,
                                                  int64_t ldwv, int64_t wv_bs, const uint8_t* wmeta,
                                                  int64_t ldwm, int64_t wm_bs, const float* sw, int64_t sw_sn,
-                                                 int64_t sw_sk, int64_t sw_bs, int gran_n, void* y,
-                                                 sg_dtype y_dt, int64_t ldy, int64_t y_bs, sg_form form,
-                                                 hipStream_t stream);
+                                                 int64_t sw_sk, int64_t sw_bs, int gran_n, const float* bias,
+                                                 int64_t bias_bs, void* y, sg_dtype y_dt, int64_t ldy,
+                                                 int64_t y_bs, sg_form form, hipStream_t stream);
 
 sg_status sg_fp8_sparse24_gemm_groupwise_packed_batched(int64_t L, int64_t M, int64_t N, int64_t K,
                                                         const uint8_t* xq, int64_t ldx, int64_t x_bs,
                                                         const float* sx, int64_t sx_sm, int64_t sx_sk,
                                                         int64_t sx_bs, int gran_m, const uint8_t* wpacked,
                                                         int64_t wp_bs, const float* sw, int64_t sw_sn,
-                                                        int64_t sw_sk, int64_t sw_bs, int gran_n, void* y,
+                                                        int64_t sw_sk, int64_t sw_bs, int gran_n,
+                                                        const float* bias, int64_t bias_bs, void* y,
                                                         sg_dtype y_dt, int64_t ldy, int64_t y_bs, sg_form form,
                                                         hipStream_t stream);
 

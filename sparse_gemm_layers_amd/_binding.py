@@ -43,14 +43,14 @@ _SIGS = {
     "sg_int8_sparse24_gemm_groupwise_packed": ([_i64, _i64, _i64, _ptr, _i64, _ptr, _i64, _i64, _int, _ptr, _ptr,
                                                 _i64, _i64, _int, _ptr, _int, _i64, _int, _ptr], _int),
     "sg_fp8_gemm_groupwise_batched": ([_i64, _i64, _i64, _i64, _ptr, _i64, _i64, _ptr, _i64, _i64, _i64, _int,
-                                       _ptr, _i64, _i64, _ptr, _i64, _i64, _i64, _int, _ptr, _int, _i64, _i64,
-                                       _int, _ptr], _int),
+                                       _ptr, _i64, _i64, _ptr, _i64, _i64, _i64, _int, _ptr, _i64, _ptr, _int,
+                                       _i64, _i64, _int, _ptr], _int),
     "sg_fp8_sparse24_gemm_groupwise_batched": ([_i64, _i64, _i64, _i64, _ptr, _i64, _i64, _ptr, _i64, _i64, _i64,
                                                 _int, _ptr, _i64, _i64, _ptr, _i64, _i64, _ptr, _i64, _i64, _i64,
-                                                _int, _ptr, _int, _i64, _i64, _int, _ptr], _int),
+                                                _int, _ptr, _i64, _ptr, _int, _i64, _i64, _int, _ptr], _int),
     "sg_fp8_sparse24_gemm_groupwise_packed_batched": ([_i64, _i64, _i64, _i64, _ptr, _i64, _i64, _ptr, _i64, _i64,
                                                        _i64, _int, _ptr, _i64, _ptr, _i64, _i64, _i64, _int, _ptr,
-                                                       _int, _i64, _i64, _int, _ptr], _int),
+                                                       _i64, _ptr, _int, _i64, _i64, _int, _ptr], _int),
     "sg_probe_matrix_ops": ([_int, _int], _i64),
     "sg_probe_matrix_rate": ([_int, _int, _ptr, _ptr, _ptr], _int),
 }
@@ -266,8 +266,18 @@ def _out_batched(y, L, M, N, out_dtype, form, device):
     return y, (SG_OUT_YT if yt else SG_OUT_Y), _dtype_code(y, "y")
 
 
+def _bias(bias, N):
+    """(pointer, batch stride) of an optional fp32 bias [L, N] or shared [N]."""
+    if bias is None:
+        return None, 0
+    if not isinstance(bias, torch.Tensor) or not bias.is_cuda or bias.dtype != torch.float32 \
+            or bias.dim() not in (1, 2) or bias.shape[-1] != N or (N > 1 and bias.stride(-1) != 1):
+        raise SgError("bias must be a float32 GPU tensor [L, N] or [N]")
+    return _p(bias), (0 if bias.dim() == 1 or bias.shape[0] == 1 else bias.stride(0))
+
+
 def fp8_gemm_groupwise_batched(xq, sx, wq, sw, gran_m: int = 1, gran_n: int = 128, out_dtype=torch.bfloat16,
-                               form: str = "y", y=None):
+                               form: str = "y", y=None, bias=None):
     """L independent GEMMs: xq uint8 [L, M, K], sx [L, ceil(M/gran_m), K/128];
     wq uint8 [L, N, K] and sw [L, ., K/128], or 2-D to share one weight.  Returns
     y [L, M, N] ("y") or [L, N, M] ("yt")."""
@@ -277,15 +287,16 @@ def fp8_gemm_groupwise_batched(xq, sx, wq, sw, gran_m: int = 1, gran_n: int = 12
     y, f, ydt = _out_batched(y, L, M, N, out_dtype, form, xq.device)
     sxm, sxk, sxb = _sc(sx)
     swn, swk, swb = _sc(sw)
+    bp, bb = _bias(bias, N)
     st = lib().sg_fp8_gemm_groupwise_batched(L, M, N, K, _p(xq), _mat(xq, "xq")[1], _bstride(xq), _p(sx), sxm, sxk,
                                              sxb, gran_m, _p(wq), ldw, _bstride(wq), _p(sw), swn, swk, swb, gran_n,
-                                             _p(y), ydt, _mat(y, "y")[1], _bstride(y), f, _stream(xq))
+                                             bp, bb, _p(y), ydt, _mat(y, "y")[1], _bstride(y), f, _stream(xq))
     _check(st, "sg_fp8_gemm_groupwise_batched")
     return y
 
 
 def fp8_sparse24_gemm_groupwise_batched(xq, sx, wv, wmeta, sw, gran_m: int = 1, gran_n: int = 128,
-                                        out_dtype=torch.bfloat16, form: str = "y", y=None):
+                                        out_dtype=torch.bfloat16, form: str = "y", y=None, bias=None):
     """Batched 2:4 GEMM: wv [L, N, K/2] and wmeta [L, N, K/8] (or 2-D, shared)."""
     _gpu3d(xq, "xq")
     L, M, K = xq.shape
@@ -294,16 +305,17 @@ def fp8_sparse24_gemm_groupwise_batched(xq, sx, wv, wmeta, sw, gran_m: int = 1, 
     y, f, ydt = _out_batched(y, L, M, N, out_dtype, form, xq.device)
     sxm, sxk, sxb = _sc(sx)
     swn, swk, swb = _sc(sw)
+    bp, bb = _bias(bias, N)
     st = lib().sg_fp8_sparse24_gemm_groupwise_batched(
         L, M, N, K, _p(xq), _mat(xq, "xq")[1], _bstride(xq), _p(sx), sxm, sxk, sxb, gran_m, _p(wv), ldwv,
-        _bstride(wv), _p(wmeta), ldwm, _bstride(wmeta), _p(sw), swn, swk, swb, gran_n, _p(y), ydt,
+        _bstride(wv), _p(wmeta), ldwm, _bstride(wmeta), _p(sw), swn, swk, swb, gran_n, bp, bb, _p(y), ydt,
         _mat(y, "y")[1], _bstride(y), f, _stream(xq))
     _check(st, "sg_fp8_sparse24_gemm_groupwise_batched")
     return y
 
 
 def fp8_sparse24_gemm_groupwise_packed_batched(xq, sx, wpacked, n: int, sw, gran_m: int = 1, gran_n: int = 128,
-                                               out_dtype=torch.bfloat16, form: str = "y", y=None):
+                                               out_dtype=torch.bfloat16, form: str = "y", y=None, bias=None):
     """Batched 2:4 GEMM with packed weights: wpacked uint8 [L, bytes] (one packed
     weight per problem) or 1-D (shared)."""
     _gpu3d(xq, "xq")
@@ -316,9 +328,10 @@ def fp8_sparse24_gemm_groupwise_packed_batched(xq, sx, wpacked, n: int, sw, gran
     y, f, ydt = _out_batched(y, L, M, n, out_dtype, form, xq.device)
     sxm, sxk, sxb = _sc(sx)
     swn, swk, swb = _sc(sw)
+    bp, bb = _bias(bias, n)
     st = lib().sg_fp8_sparse24_gemm_groupwise_packed_batched(
         L, M, n, K, _p(xq), _mat(xq, "xq")[1], _bstride(xq), _p(sx), sxm, sxk, sxb, gran_m, _p(wpacked), wpb,
-        _p(sw), swn, swk, swb, gran_n, _p(y), ydt, _mat(y, "y")[1], _bstride(y), f, _stream(xq))
+        _p(sw), swn, swk, swb, gran_n, bp, bb, _p(y), ydt, _mat(y, "y")[1], _bstride(y), f, _stream(xq))
     _check(st, "sg_fp8_sparse24_gemm_groupwise_packed_batched")
     return y
 

@@ -57,6 +57,10 @@ struct GemmArgs {
   // scales; all zero for a single problem.
   int64_t bx, bw, bm, bsx, bsw, by;
   int L;
+  // Optional bias (NULL: none): bias[n] is added to every output row after
+  // the scales; problem z's bias starts bbs floats after problem 0's.
+  const float* bias;
+  int64_t bbs;
 };
 
 #if SG_DEVICE_PASS
@@ -68,6 +72,17 @@ __device__ __forceinline__ void to_batch(GemmArgs& a) {
   a.sx += z * a.bsx;
   a.sw += z * a.bsw;
   a.y = static_cast<uint8_t*>(a.y) + z * a.by;
+  if (a.bias) a.bias += z * a.bbs;
+}
+
+// v (output rows n .. n + 3 of one column) plus the bias; rows past N read
+// bias[N - 1] (they are not stored).
+__device__ __forceinline__ v4f with_bias(const GemmArgs& a, int64_t n, v4f v) {
+  if (a.bias) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] += a.bias[min(n + e, a.N - 1)];
+  }
+  return v;
 }
 #endif
 
@@ -475,10 +490,12 @@ __global__ void __launch_bounds__(512) k_gemm_sparse_x2(GemmArgs a, int tiles_m,
   const uint8_t* const sst = ((NIT - 1) & 1 ? db1 : db0) + x2::HALF;
   const float* const sxp = reinterpret_cast<const float*>(sst + Stage<true>::SX_OFF) + wm * 64 + lr;
   const float* const swp = reinterpret_cast<const float*>(sst + Stage<true>::SW_OFF) + wn * 128 + 4 * g;
+  const float* const bias = a.bias ? a.bias + n0 : nullptr;
+  const int nlim = (int)nrows;
   if (q == 0)
-    x2_finish<0, OUT_BF16, OUT_T, x2::DBL, SCALE>(db1, db0, db1, acc, w4, l, wn, wm, g, lr, sxp, swp);
+    x2_finish<0, OUT_BF16, OUT_T, x2::DBL, SCALE>(db1, db0, db1, acc, w4, l, wn, wm, g, lr, sxp, swp, bias, nlim);
   else
-    x2_finish<1, OUT_BF16, OUT_T, x2::DBL, SCALE>(db0, db0, db1, acc, w4, l, wn, wm, g, lr, sxp, swp);
+    x2_finish<1, OUT_BF16, OUT_T, x2::DBL, SCALE>(db0, db0, db1, acc, w4, l, wn, wm, g, lr, sxp, swp, bias, nlim);
   __syncthreads();
   store_staged<OUT_BF16, OUT_T, x2::DBL>(a, db0, db1, m0, n0, t);
 #endif  // SG_DEVICE_PASS
@@ -798,7 +815,8 @@ __global__ void __launch_bounds__(512) k_gemm_dense8(GemmArgs a, int tiles_m, in
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+        const v4f b = with_bias(a, n0 + wn * 64 + i * 16 + 4 * g, acc[i][j]);
+        const float v[4] = {b[0], b[1], b[2], b[3]};
         stage_quad<OUT_BF16, OUT_T, BYTES>(sm0, sm1, wn * 64 + i * 16 + 4 * g, wm * 64 + j * 16 + lr, v);
       }
     __syncthreads();
@@ -808,7 +826,8 @@ __global__ void __launch_bounds__(512) k_gemm_dense8(GemmArgs a, int tiles_m, in
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        store_quad<OUT_BF16, OUT_T>(a, m0 + wm * 64 + j * 16 + lr, n0 + wn * 64 + i * 16 + 4 * g, acc[i][j]);
+        store_quad<OUT_BF16, OUT_T>(a, m0 + wm * 64 + j * 16 + lr, n0 + wn * 64 + i * 16 + 4 * g,
+                                    with_bias(a, n0 + wn * 64 + i * 16 + 4 * g, acc[i][j]));
   }
 #endif  // SG_DEVICE_PASS
 }
@@ -977,7 +996,8 @@ __global__ void __launch_bounds__(512) k_gemm_decode(GemmArgs a) {
       v4.x += v.x; v4.y += v.y; v4.z += v.z; v4.w += v.w;
     }
     const v4f out = {v4.x, v4.y, v4.z, v4.w};
-    store_quad<OUT_BF16, OUT_T>(a, (int64_t)j * 16 + (ll & 15), n0 + 16 * rb + 4 * (ll >> 4), out);
+    store_quad<OUT_BF16, OUT_T>(a, (int64_t)j * 16 + (ll & 15), n0 + 16 * rb + 4 * (ll >> 4),
+                                with_bias(a, n0 + 16 * rb + 4 * (ll >> 4), out));
   }
 #endif  // SG_DEVICE_PASS
 }
@@ -1164,7 +1184,8 @@ __global__ void __launch_bounds__(512) k_gemm_decode_dma(GemmArgs a) {
       v4.x += v.x; v4.y += v.y; v4.z += v.z; v4.w += v.w;
     }
     const v4f out = {v4.x, v4.y, v4.z, v4.w};
-    store_quad<OUT_BF16, OUT_T>(a, (int64_t)j * 16 + (ll & 15), n0 + 16 * rb + 4 * (ll >> 4), out);
+    store_quad<OUT_BF16, OUT_T>(a, (int64_t)j * 16 + (ll & 15), n0 + 16 * rb + 4 * (ll >> 4),
+                                with_bias(a, n0 + 16 * rb + 4 * (ll >> 4), out));
   }
 #endif
 }
@@ -1295,12 +1316,15 @@ static sg_status check_common(int64_t M, int64_t N, int64_t K, const uint8_t* xq
 // and metadata, floats for the scales, elements for y).
 struct Batch {
   int64_t L = 1, bx = 0, bw = 0, bm = 0, bsx = 0, bsw = 0, by = 0;
+  const float* bias = nullptr;   // optional per-output-row bias [N] per problem
+  int64_t bbs = 0;
 };
 
 static sg_status check_batch(const Batch& b) {
   if (b.L < 0 || b.L > 65535) return SG_ERR_SHAPE;
   if (b.bx < 0 || b.bw < 0 || b.bm < 0 || b.bsx < 0 || b.bsw < 0 || b.by < 0) return SG_ERR_SHAPE;
-  if (b.bx % 16 || b.bw % 16 || b.bm % 16) return SG_ERR_ALIGN;
+  if (b.bbs < 0) return SG_ERR_SHAPE;
+  if (b.bx % 16 || b.bw % 16 || b.bm % 16 || !aligned(b.bias, 4)) return SG_ERR_ALIGN;
   return SG_OK;
 }
 
@@ -1321,6 +1345,8 @@ static GemmArgs make_args(int64_t M, int64_t N, int64_t K, const uint8_t* xq, in
   a.vec16 = ((ldy * es) % 16 == 0) && aligned(y, 16) && (b.by * es) % 16 == 0;
   a.bx = b.bx; a.bw = b.bw; a.bm = b.bm; a.bsx = b.bsx; a.bsw = b.bsw; a.by = b.by * es;
   a.L = (int)b.L;
+  a.bias = b.bias;
+  a.bbs = b.bbs;
   return a;
 }
 
@@ -1360,11 +1386,12 @@ extern "C" sg_status sg_fp8_gemm_groupwise_batched(int64_t L, int64_t M, int64_t
                                                    int64_t ldx, int64_t x_bs, const float* sx, int64_t sx_sm,
                                                    int64_t sx_sk, int64_t sx_bs, int gran_m, const uint8_t* wq,
                                                    int64_t ldw, int64_t w_bs, const float* sw, int64_t sw_sn,
-                                                   int64_t sw_sk, int64_t sw_bs, int gran_n, void* y,
-                                                   sg_dtype y_dt, int64_t ldy, int64_t y_bs, sg_form form,
-                                                   hipStream_t stream) {
+                                                   int64_t sw_sk, int64_t sw_bs, int gran_n, const float* bias,
+                                                   int64_t bias_bs, void* y, sg_dtype y_dt, int64_t ldy,
+                                                   int64_t y_bs, sg_form form, hipStream_t stream) {
   Batch b;
   b.L = L; b.bx = x_bs; b.bw = w_bs; b.bsx = sx_bs; b.bsw = sw_bs; b.by = y_bs;
+  b.bias = bias; b.bbs = bias_bs;
   return dense_gemm(M, N, K, xq, ldx, sx, sx_sm, sx_sk, gran_m, wq, ldw, sw, sw_sn, sw_sk, gran_n, y, y_dt, ldy,
                     form, b, stream);
 }
@@ -1461,10 +1488,11 @@ extern "C" sg_status sg_fp8_sparse24_gemm_groupwise_batched(
     int64_t L, int64_t M, int64_t N, int64_t K, const uint8_t* xq, int64_t ldx, int64_t x_bs, const float* sx,
     int64_t sx_sm, int64_t sx_sk, int64_t sx_bs, int gran_m, const uint8_t* wv, int64_t ldwv, int64_t wv_bs,
     const uint8_t* wmeta, int64_t ldwm, int64_t wm_bs, const float* sw, int64_t sw_sn, int64_t sw_sk,
-    int64_t sw_bs, int gran_n, void* y, sg_dtype y_dt, int64_t ldy, int64_t y_bs, sg_form form,
-    hipStream_t stream) {
+    int64_t sw_bs, int gran_n, const float* bias, int64_t bias_bs, void* y, sg_dtype y_dt, int64_t ldy,
+    int64_t y_bs, sg_form form, hipStream_t stream) {
   Batch b;
   b.L = L; b.bx = x_bs; b.bw = wv_bs; b.bm = wm_bs; b.bsx = sx_bs; b.bsw = sw_bs; b.by = y_bs;
+  b.bias = bias; b.bbs = bias_bs;
   return sparse24_gemm<false>(M, N, K, xq, ldx, sx, sx_sm, sx_sk, gran_m, wv, ldwv, wmeta, ldwm, sw, sw_sn, sw_sk,
                               gran_n, y, y_dt, ldy, form, b, stream);
 }
@@ -1472,10 +1500,11 @@ extern "C" sg_status sg_fp8_sparse24_gemm_groupwise_batched(
 extern "C" sg_status sg_fp8_sparse24_gemm_groupwise_packed_batched(
     int64_t L, int64_t M, int64_t N, int64_t K, const uint8_t* xq, int64_t ldx, int64_t x_bs, const float* sx,
     int64_t sx_sm, int64_t sx_sk, int64_t sx_bs, int gran_m, const uint8_t* wpacked, int64_t wp_bs,
-    const float* sw, int64_t sw_sn, int64_t sw_sk, int64_t sw_bs, int gran_n, void* y, sg_dtype y_dt,
-    int64_t ldy, int64_t y_bs, sg_form form, hipStream_t stream) {
+    const float* sw, int64_t sw_sn, int64_t sw_sk, int64_t sw_bs, int gran_n, const float* bias,
+    int64_t bias_bs, void* y, sg_dtype y_dt, int64_t ldy, int64_t y_bs, sg_form form, hipStream_t stream) {
   Batch b;
   b.L = L; b.bx = x_bs; b.bw = wp_bs; b.bsx = sx_bs; b.bsw = sw_bs; b.by = y_bs;
+  b.bias = bias; b.bbs = bias_bs;
   return sparse24_gemm_packed<false>(M, N, K, xq, ldx, sx, sx_sm, sx_sk, gran_m, wpacked, sw, sw_sn, sw_sk, gran_n,
                                      y, y_dt, ldy, form, b, stream);
 }

@@ -87,10 +87,13 @@ __device__ __forceinline__ void stage_quad(uint8_t* t0, uint8_t* t1, int nl, int
 // sxp[16 j] is the X scale of the lane's column in sub-tile column j and
 // swp[16 i' + e] the W scale of row 16 i' + e (i' = 4 Q + i) of the wave's
 // rows; both live in LDS that the exchange and the staged tile leave alone.
+// bias (NULL: none) points at the tile's first row's bias; tile rows at or
+// past nlim read bias[nlim - 1] (they are not stored).
 template <int Q, bool OUT_BF16, bool OUT_T, int BUF, int SCALE = 0>
 __device__ __forceinline__ void x2_finish(const uint8_t* src, uint8_t* t0, uint8_t* t1, const v4f (&acc)[8][4],
                                           int w4, int l, int wn, int wm, int g, int lr,
-                                          const float* sxp = nullptr, const float* swp = nullptr) {
+                                          const float* sxp = nullptr, const float* swp = nullptr,
+                                          const float* bias = nullptr, int nlim = 0) {
   float4 part[16];
 #pragma unroll
   for (int k = 0; k < 16; ++k) part[k] = reinterpret_cast<const float4*>(src)[((w4 * 16 + k) << 6) + l];
@@ -99,6 +102,12 @@ __device__ __forceinline__ void x2_finish(const uint8_t* src, uint8_t* t0, uint8
   for (int i = 0; i < 4; ++i) {
     float4 sw = make_float4(1.f, 1.f, 1.f, 1.f);
     if (SCALE) sw = *reinterpret_cast<const float4*>(swp + (4 * Q + i) * 16);
+    const int nl = wn * 128 + (4 * Q + i) * 16 + 4 * g;
+    float bv[4] = {0.f, 0.f, 0.f, 0.f};
+    if (bias) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) bv[e] = bias[min(nl + e, nlim - 1)];
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const float4 o = part[i * 4 + j];
@@ -116,7 +125,8 @@ __device__ __forceinline__ void x2_finish(const uint8_t* src, uint8_t* t0, uint8
         const float sx = sxp[16 * j];
         v[0] *= sw.x * sx; v[1] *= sw.y * sx; v[2] *= sw.z * sx; v[3] *= sw.w * sx;
       }
-      stage_quad<OUT_BF16, OUT_T, BUF>(t0, t1, wn * 128 + (4 * Q + i) * 16 + 4 * g, wm * 64 + j * 16 + lr, v);
+      v[0] += bv[0]; v[1] += bv[1]; v[2] += bv[2]; v[3] += bv[3];
+      stage_quad<OUT_BF16, OUT_T, BUF>(t0, t1, nl, wm * 64 + j * 16 + lr, v);
     }
   }
 }

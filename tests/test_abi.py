@@ -258,25 +258,25 @@ def test_probe_operation_counts():
 
 def batched(kind, **kw):
     a = dict(L=3, M=64, N=256, K=256, x=P, ldx=256, xb=64 * 256, sx=P3, sxm=1, sxk=64, sxb=64 * 2, gm=1, w=P2,
-             ldw=256, wb=256 * 256, meta=P3, ldm=32, mb=256 * 32, sw=P3, swn=2, swk=1, swb=4, gn=128, y=P, ydt=1,
-             ldy=256, yb=64 * 256, form=0)
+             ldw=256, wb=256 * 256, meta=P3, ldm=32, mb=256 * 32, sw=P3, swn=2, swk=1, swb=4, gn=128, bias=None,
+             bb=0, y=P, ydt=1, ldy=256, yb=64 * 256, form=0)
     a.update(kw)
     lib = sg.lib()
     if kind == "dense":
         return lib.sg_fp8_gemm_groupwise_batched(
             a["L"], a["M"], a["N"], a["K"], a["x"], a["ldx"], a["xb"], a["sx"], a["sxm"], a["sxk"], a["sxb"], a["gm"],
-            a["w"], a["ldw"], a["wb"], a["sw"], a["swn"], a["swk"], a["swb"], a["gn"], a["y"], a["ydt"], a["ldy"],
-            a["yb"], a["form"], None)
+            a["w"], a["ldw"], a["wb"], a["sw"], a["swn"], a["swk"], a["swb"], a["gn"], a["bias"], a["bb"], a["y"],
+            a["ydt"], a["ldy"], a["yb"], a["form"], None)
     if kind == "sparse":
         ldw = a["ldw"] if "ldw" in kw else a["K"] // 2
         return lib.sg_fp8_sparse24_gemm_groupwise_batched(
             a["L"], a["M"], a["N"], a["K"], a["x"], a["ldx"], a["xb"], a["sx"], a["sxm"], a["sxk"], a["sxb"], a["gm"],
             a["w"], ldw, a["wb"], a["meta"], a["ldm"], a["mb"], a["sw"], a["swn"], a["swk"], a["swb"], a["gn"],
-            a["y"], a["ydt"], a["ldy"], a["yb"], a["form"], None)
+            a["bias"], a["bb"], a["y"], a["ydt"], a["ldy"], a["yb"], a["form"], None)
     return lib.sg_fp8_sparse24_gemm_groupwise_packed_batched(
         a["L"], a["M"], a["N"], a["K"], a["x"], a["ldx"], a["xb"], a["sx"], a["sxm"], a["sxk"], a["sxb"], a["gm"],
-        a["w"], a["wb"], a["sw"], a["swn"], a["swk"], a["swb"], a["gn"], a["y"], a["ydt"], a["ldy"], a["yb"],
-        a["form"], None)
+        a["w"], a["wb"], a["sw"], a["swn"], a["swk"], a["swb"], a["gn"], a["bias"], a["bb"], a["y"], a["ydt"],
+        a["ldy"], a["yb"], a["form"], None)
 
 
 BATCH_CASES = [
@@ -285,6 +285,7 @@ BATCH_CASES = [
     (dict(xb=8), ALIGN), (dict(wb=24), ALIGN),
     (dict(L=0), OK), (dict(M=0), OK),
     (dict(x=None), NULL), (dict(w=None), NULL), (dict(K=200), SHAPE), (dict(gm=64), UNSUP),
+    (dict(bias=P2, bb=-1), SHAPE), (dict(bias=ctypes.c_void_p(0x200002)), ALIGN),
 ]
 
 

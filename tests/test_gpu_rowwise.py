@@ -11,7 +11,7 @@ import torch
 import oracle
 import sparse_gemm_layers_amd as sg
 import workloads
-from gpu_helpers import DEV, assert_within_tolerance, down, say, up, up_scales
+from gpu_helpers import DEV, assert_within_tolerance, down, say, up
 
 pytestmark = pytest.mark.gpu
 
@@ -203,3 +203,61 @@ def test_batched_output_leaves_other_memory_alone():
     for z in range(L):
         ref, bound = oracle.fp8_sparse24_gemm_groupwise(xq[z], sx[z], 1, wq[z], meta[z], sw[z], 128, bound=True)
         assert_within_tolerance(yb[z, :m, :n], ref, bound, f"problem {z}")
+
+
+# --------------------------------------------------------------- bias
+
+@pytest.mark.parametrize("kind", ["packed", "sparse", "dense"])
+@pytest.mark.parametrize("L,m,n,k,form,out", [(2, 200, 300, 384, "y", torch.bfloat16),
+                                              (1, 16, 520, 256, "yt", torch.bfloat16),
+                                              (2, 129, 256, 128, "yt", torch.float32),
+                                              (3, 37, 260, 384, "y", torch.float32)])
+def test_bias(kind, L, m, n, k, form, out):
+    say(f"bias {kind} L={L} M={m} N={n} K={k} form={form} {out}")
+    xq, sx, wq, meta, sw = batched_operands(L, m, n, k, seed=80 + m + n)
+    bias = (np.random.default_rng(81 + n).standard_normal((L, n)) * 0.5).astype(np.float32)
+    bt = up(bias)
+    if kind == "dense":
+        wd = np.stack([oracle.decompress24(wq[z], meta[z]) for z in range(L)])
+        y = sg.fp8_gemm_groupwise_batched(up(xq), up_scales3(sx), up(wd), up_scales3(sw), 1, 128, out_dtype=out,
+                                          form=form, bias=bt)
+    elif kind == "sparse":
+        y = sg.fp8_sparse24_gemm_groupwise_batched(up(xq), up_scales3(sx), up(wq), up(meta), up_scales3(sw), 1, 128,
+                                                   out_dtype=out, form=form, bias=bt)
+    else:
+        wp = torch.stack([sg.sparse24_pack_gfx950(up(wq[z]), up(meta[z])) for z in range(L)])
+        y = sg.fp8_sparse24_gemm_groupwise_packed_batched(up(xq), up_scales3(sx), wp, n, up_scales3(sw), 1, 128,
+                                                          out_dtype=out, form=form, bias=bt)
+    got = down(y)
+    for z in range(L):
+        ref, bound = oracle.fp8_sparse24_gemm_groupwise(xq[z], sx[z], 1, wq[z], meta[z], sw[z], 128, bound=True)
+        ref, bound = oracle.add_bias(ref, bound, bias[z])
+        gz = got[z].T if form == "yt" else got[z]
+        assert_within_tolerance(gz.astype(np.float64), ref, bound, f"problem {z}")
+
+
+@pytest.mark.parametrize("kind", ["packed", "dense"])
+@pytest.mark.parametrize("m", [16, 300])
+def test_rowwise_with_shared_bias(kind, m):
+    """Scales constant along K (accumulate-then-scale for M > 64) plus one bias
+    shared by the batch."""
+    L, n, k = 2, 392, 512
+    say(f"rowwise + shared bias {kind} L={L} M={m} N={n} K={k}")
+    ops = [rowwise_operands(m, n, k, seed=90 + z, sparse=kind != "dense") for z in range(L)]
+    bias = (np.random.default_rng(91).standard_normal(n) * 2).astype(np.float32)
+    xq = np.stack([o[0] for o in ops])
+    sxt = up(np.stack([o[1] for o in ops]))[:, :, None].expand(L, m, k // 128)
+    swt = up(np.stack([o[4] for o in ops]))[:, :, None].expand(L, n, k // 128)
+    if kind == "dense":
+        y = sg.fp8_gemm_groupwise_batched(up(xq), sxt, up(np.stack([o[2] for o in ops])), swt, 1, 1, bias=up(bias))
+    else:
+        wp = torch.stack([sg.sparse24_pack_gfx950(up(o[2]), up(o[3])) for o in ops])
+        y = sg.fp8_sparse24_gemm_groupwise_packed_batched(up(xq), sxt, wp, n, swt, 1, 1, bias=up(bias))
+    got = down(y)
+    for z, (xqz, sxz, wqz, metaz, swz) in enumerate(ops):
+        if kind == "dense":
+            ref, bound = oracle.fp8_gemm_rowwise(xqz, sxz, wqz, swz, bound=True)
+        else:
+            ref, bound = oracle.fp8_sparse24_gemm_rowwise(xqz, sxz, wqz, metaz, swz, bound=True)
+        ref, bound = oracle.add_bias(ref, bound, bias)
+        assert_within_tolerance(got[z], ref, bound, f"problem {z}")
