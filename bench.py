@@ -224,6 +224,15 @@ def rows_report():
     # next row: scales constant along K (rowwise), applied once after the K
     # loop, 2048x4096x4096 packed 2:4 and dense; and the batched ("L" mode)
     # 2:4 GEMM, 8 problems of 256x4096x4096 with distinct packed weights
+    xqr = torch.empty((m, k), dtype=torch.uint8, device=DEV)
+    sxq = torch.empty((1, m), dtype=torch.float32, device=DEV).t()
+    ms = time_fn(lambda i: sg.fp8_quant_groupwise(x, gr=1, gc=k, q=xqr, s=sxq))
+    b = m * k * 4 + m * k + 4 * m
+    out["next_rowwise_quant_x_2048x4096"] = {"ms": ms, "GB/s": b / ms / 1e6}
+    st = torch.empty((1, 1), dtype=torch.float32, device=DEV)
+    ms = time_fn(lambda i: sg.fp8_quant_groupwise(x, gr=m, gc=k, q=xqr, s=st))
+    out["next_tensorwise_quant_x_2048x4096"] = {"ms": ms, "GB/s": (m * k * 4 + m * k + 4) / ms / 1e6}
+    del xqr
     sxr = k_constant(sx[:, 0].contiguous(), m, k)
     swr = k_constant(sw[:, 0].repeat_interleave(128)[:n].contiguous(), n, k)
     y = torch.empty((m, n), dtype=torch.bfloat16, device=DEV)

@@ -80,6 +80,10 @@ int sg_abi_version(void);
  *   x   : [rows, cols], dtype x_dt (SG_F32 or SG_BF16), leading dim ldx.
  *   gr  : 1 or 128.   gc: 128 or 64 (64 serves the compressed 2:4 values, whose
  *         128 x 64 blocks are the 128 x 128 blocks of the dense weight).
+ *         Or one block per row (gr = 1, gc = cols) or one for the tensor
+ *         (gr = rows, gc = cols), with cols a multiple of 16: the rowwise and
+ *         tensorwise scales that the GEMMs take as scales constant along K
+ *         ([T3258]: its quoted weight quantisation keeps one scale per row).
  *   q   : [rows, cols] e4m3 codes (uint8), leading dim ldq (bytes).
  *   s   : block (rb, cb) at s[rb * s_stride_r + cb * s_stride_c],
  *         rb < ceil(rows / gr), cb < cols / gc.

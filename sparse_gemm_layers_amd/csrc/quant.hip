@@ -164,10 +164,101 @@ __global__ void __launch_bounds__(256) k_quant_block128(const TIn* __restrict__ 
   if (t == 0) s[rb * ssr + cb * ssc] = sc;
 }
 
+// ------------------------------------------------------------------ whole rows, whole tensor
+// Scales constant along K: one scale per row (gc = cols) or one for the whole
+// tensor (gr = rows, gc = cols).  Rows: one 256-thread workgroup per row, 16
+// consecutive elements per thread and step; the first pass takes the row's
+// amax, the second reads the row again (from L2) and encodes it.  Tensor: the
+// amax comes first from k_amax_tensor (amax_in), and the encode pass reads it.
+template <typename TIn>
+__device__ __forceinline__ void load16(const TIn* p, float (&v)[16]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) load4(p + 4 * i, v + 4 * i);
+}
+
+template <typename TIn, int MODE>
+__global__ void __launch_bounds__(256) k_quant_rowwide(const TIn* __restrict__ x, int64_t cols, int64_t ldx,
+                                                       uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ s,
+                                                       int64_t ssr, const float* __restrict__ amax_in) {
+  __shared__ float red[4];
+  const int64_t r = blockIdx.x;
+  const int t = threadIdx.x;
+  const TIn* xr = x + r * ldx;
+  float a;
+  if (amax_in) {
+    a = *amax_in;
+  } else {
+    a = 0.f;
+    for (int64_t c = (int64_t)t * 16; c < cols; c += 256 * 16) {
+      float v[16];
+      load16(xr + c, v);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(v[i]));
+    }
+    a = group_max<64>(a);
+    if ((t & 63) == 0) red[t >> 6] = a;
+    __syncthreads();
+    a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  }
+  const float sc = a > 0.f ? a / (MODE == Q_FP8 ? 448.0f : 127.0f) : 1.0f;   // IEEE divide
+  for (int64_t c = (int64_t)t * 16; c < cols; c += 256 * 16) {
+    float v[16];
+    load16(xr + c, v);
+    uint32_t w[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const float* e = v + 4 * d;
+      w[d] = MODE == Q_FP8 ? e4m3_pack4(e[0] / sc, e[1] / sc, e[2] / sc, e[3] / sc)
+                           : (int8_encode(e[0], sc) | (int8_encode(e[1], sc) << 8) |
+                              (int8_encode(e[2], sc) << 16) | (int8_encode(e[3], sc) << 24));
+    }
+    *reinterpret_cast<uint4*>(q + r * ldq + c) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+  if (t == 0 && !amax_in) s[r * ssr] = sc;
+}
+
+// amax of the whole tensor into *slot (cleared first by k_fill1): each wave
+// reduces its grid-stride share, one atomic max per wave on the value's bits
+// (non-negative floats order like their bit patterns).
+template <typename TIn>
+__global__ void __launch_bounds__(256) k_amax_tensor(const TIn* __restrict__ x, int64_t rows, int64_t cols,
+                                                     int64_t ldx, float* __restrict__ slot) {
+  const int64_t per_row = cols / 16, items = rows * per_row;
+  float a = 0.f;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < items; i += (int64_t)gridDim.x * 256) {
+    const int64_t r = i / per_row, c = (i % per_row) * 16;
+    float v[16];
+    load16(x + r * ldx + c, v);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) a = fmaxf(a, fabsf(v[k]));
+  }
+  a = group_max<64>(a);
+  if ((threadIdx.x & 63) == 0) atomicMax(reinterpret_cast<unsigned int*>(slot), __float_as_uint(a));
+}
+
+__global__ void k_fill1(float* p, float v) { *p = v; }
+
+// The tensor's scale from its amax (in place).
+template <int MODE>
+__global__ void k_tensor_scale(float* s) {
+  const float a = *s;
+  *s = a > 0.f ? a / (MODE == Q_FP8 ? 448.0f : 127.0f) : 1.0f;
+}
+
 template <typename TIn, int MODE>
 static void launch_quant(const TIn* x, int64_t rows, int64_t cols, int64_t ldx, int gr, int gc,
                          uint8_t* q, int64_t ldq, float* s, int64_t ssr, int64_t ssc, hipStream_t st) {
-  if (gr == 1) {
+  if ((gr != 1 && gr != 128) || (gc != 64 && gc != 128)) {
+    // gc == cols: whole rows (gr == 1) or the whole tensor (gr == rows)
+    if (gr == 1) {
+      k_quant_rowwide<TIn, MODE><<<(unsigned)rows, 256, 0, st>>>(x, cols, ldx, q, ldq, s, ssr, nullptr);
+    } else {
+      k_fill1<<<1, 1, 0, st>>>(s, 0.f);
+      k_amax_tensor<TIn><<<grid_for(rows * (cols / 16), 256, 2048), 256, 0, st>>>(x, rows, cols, ldx, s);
+      k_quant_rowwide<TIn, MODE><<<(unsigned)rows, 256, 0, st>>>(x, cols, ldx, q, ldq, nullptr, 0, s);
+      k_tensor_scale<MODE><<<1, 1, 0, st>>>(s);
+    }
+  } else if (gr == 1) {
     const int64_t blocks = rows * (cols / gc);
     const int per_wg = 4 * (64 / (gc / 16));
     const unsigned g = grid_for(blocks, per_wg);
@@ -194,9 +285,14 @@ static sg_status quant_groupwise(const void* x, sg_dtype x_dt, int64_t rows, int
                                  hipStream_t stream) {
   if (!x || !q || !s) return SG_ERR_NULL;
   if (x_dt != SG_F32 && x_dt != SG_BF16) return SG_ERR_UNSUPPORTED;
-  if ((gr != 1 && gr != 128) || (gc != 128 && gc != 64)) return SG_ERR_UNSUPPORTED;
+  // 1 x {64, 128}, 128 x {64, 128}, one group per row (gr = 1, gc = cols) or
+  // one for the tensor (gr = rows, gc = cols; cols a multiple of 16)
+  const bool blocks = (gr == 1 || gr == 128) && (gc == 128 || gc == 64);
+  const bool whole = gc == cols && (gr == 1 || gr == rows) && cols % 16 == 0 && cols > 0;
+  if (!blocks && !whole) return SG_ERR_UNSUPPORTED;
   if (rows < 0 || cols <= 0 || cols % gc != 0 || ldx < cols || ldq < cols) return SG_ERR_SHAPE;
-  if (cdiv(rows, gr) > 65535 && gr == 128) return SG_ERR_SHAPE;
+  if (gr == 128 && cdiv(rows, gr) > 65535) return SG_ERR_SHAPE;
+  if (!blocks && rows >= (1LL << 24)) return SG_ERR_SHAPE;   // one 256-thread workgroup per row
   if (!aligned(x, 16) || !aligned(q, 16) || !aligned(s, 4) || (ldx * (int64_t)dtype_size(x_dt)) % 16 ||
       ldq % 16)
     return SG_ERR_ALIGN;

@@ -76,6 +76,9 @@ def quant(**kw):
     (dict(cols=200), SHAPE), (dict(cols=0), SHAPE), (dict(rows=-1), SHAPE), (dict(ldx=128), SHAPE),
     (dict(ldq=100), SHAPE), (dict(x=ODD), ALIGN), (dict(ldx=258), ALIGN), (dict(ldq=264), ALIGN),
     (dict(rows=0), OK),
+    (dict(gc=256, rows=0), OK), (dict(gr=0, gc=256, rows=0), OK), (dict(gr=3, gc=256), UNSUP),
+    (dict(cols=200, gc=200, ldx=208, ldq=208, rows=0), UNSUP), (dict(gr=4, gc=256, ldq=100), SHAPE),
+    (dict(gc=128, cols=256, gr=4), UNSUP),
 ])
 def test_fp8_quant_validation(kw, code):
     assert quant(**kw) == code

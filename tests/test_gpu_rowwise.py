@@ -261,3 +261,55 @@ def test_rowwise_with_shared_bias(kind, m):
             ref, bound = oracle.fp8_sparse24_gemm_rowwise(xqz, sxz, wqz, metaz, swz, bound=True)
         ref, bound = oracle.add_bias(ref, bound, bias)
         assert_within_tolerance(got[z], ref, bound, f"problem {z}")
+
+
+# --------------------------------------------------------------- rowwise / tensorwise quantiser
+
+@pytest.mark.parametrize("int8", [False, True])
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("whole,rows,cols", [("rows", 37, 4096), ("rows", 2, 14336), ("rows", 300, 384),
+                                             ("rows", 1, 16), ("tensor", 300, 128), ("tensor", 64, 512),
+                                             ("tensor", 1, 256), ("tensor", 129, 4096)])
+def test_whole_row_and_tensor_quant_bit_exact(whole, rows, cols, bf16, int8):
+    say(f"quant whole={whole} {rows}x{cols} bf16={bf16} int8={int8}")
+    x = workloads.sparse_large(seed=rows + cols, m=rows, n=8, k=cols)["x"]
+    if rows > 3:
+        x[3] = 0.0                                               # an all-zero row
+    xt = up(x)
+    if bf16:
+        xt = xt.to(torch.bfloat16)
+        x = xt.float().cpu().numpy()
+    gr = 1 if whole == "rows" else rows
+    f = sg.int8_quant_groupwise if int8 else sg.fp8_quant_groupwise
+    q, s = f(xt, gr=gr, gc=cols)
+    rq, rs = (oracle.int8_quant_groupwise if int8 else oracle.fp8_quant_groupwise)(x, gr, cols)
+    assert np.array_equal(down(q), rq)
+    assert np.array_equal(down(s), rs)
+
+
+def test_all_zero_tensor_gets_unit_scale():
+    say("quant tensor all zero")
+    q, s = sg.fp8_quant_groupwise(torch.zeros((40, 256), device=DEV), gr=40, gc=256)
+    assert np.array_equal(down(s), np.ones((1, 1), np.float32)) and not down(q).any()
+
+
+@pytest.mark.parametrize("m", [16, 300])
+def test_rowwise_end_to_end_on_the_gpu(m):
+    """GPU rowwise quantisation of X and of the pruned W, then the packed 2:4
+    GEMM with those scales constant along K, against the oracle's chain."""
+    n, k = 512, 1024
+    say(f"rowwise end to end M={m} N={n} K={k}")
+    d = workloads.sparse_large(seed=95 + m, m=m, n=n, k=k)
+    wv32, meta = sg.sparse24_prune_compress(up(d["w"]))
+    wq, sw = sg.fp8_quant_groupwise(wv32, gr=1, gc=k // 2)
+    xq, sx = sg.fp8_quant_groupwise(up(d["x"]), gr=1, gc=k)
+    wp = sg.sparse24_pack_gfx950(wq, meta)
+    y = down(sg.fp8_sparse24_gemm_groupwise_packed(xq, sg.k_constant_scales(sx[:, 0], m, k), wp, n,
+                                                   sg.k_constant_scales(sw[:, 0], n, k), 1, 1))
+    oxq, osx = oracle.fp8_quant_groupwise(d["x"], 1, k)
+    ov32, ometa = oracle.prune_compress24(d["w"])
+    owq, osw = oracle.fp8_quant_groupwise(ov32, 1, k // 2)
+    assert np.array_equal(down(xq), oxq) and np.array_equal(down(sx), osx)
+    assert np.array_equal(down(wq), owq) and np.array_equal(down(sw), osw)
+    ref, bound = oracle.fp8_sparse24_gemm_rowwise(oxq, osx[:, 0], owq, ometa, osw[:, 0], bound=True)
+    assert_within_tolerance(y, ref, bound, "end to end")

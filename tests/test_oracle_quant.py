@@ -142,3 +142,21 @@ def test_divide_not_reciprocal_on_a_tie():
     assert codes[0, 0] == 0x7E and codes[0, 1] == 0x3E
     tc, _ = _torch_quant(x, 1, 128)
     assert tc[0, 1] == 0x3E
+
+
+@pytest.mark.parametrize("whole", ["rows", "tensor"])
+def test_whole_row_and_tensor_groups_roundtrip_and_reach_448(whole):
+    """One group per row (gr = 1, gc = cols) or per tensor (gr = rows): a power-
+    of-two multiple of e4m3 values whose group maximum is 448 * 2^j comes back
+    code for code with scale 2^j, and the group maximum's code is +-448."""
+    rng = np.random.default_rng(77)
+    rows, cols = 6, 384
+    codes = rng.integers(0, 0x7F, size=(rows, cols)).astype(np.uint8) | (rng.integers(0, 2, size=(rows, cols)) << 7).astype(np.uint8)
+    codes[np.arange(rows), rng.integers(0, cols, rows)] = 0x7E          # 448 in every row
+    j = rng.integers(-12, 12, size=(rows, 1)) if whole == "rows" else np.full((rows, 1), 5)
+    v = (oracle.e4m3_decode(codes) * np.exp2(j)).astype(np.float32)
+    gr = 1 if whole == "rows" else rows
+    q, s = oracle.fp8_quant_groupwise(v, gr, cols)
+    assert s.shape == ((rows, 1) if whole == "rows" else (1, 1))
+    assert np.array_equal(s.reshape(-1), np.exp2(j[:, 0] if whole == "rows" else j[:1, 0]).astype(np.float32))
+    assert np.array_equal(q, codes)
