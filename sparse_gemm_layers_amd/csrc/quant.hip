@@ -217,12 +217,14 @@ __global__ void __launch_bounds__(256) k_quant_rowwide(const TIn* __restrict__ x
   if (t == 0 && !amax_in) s[r * ssr] = sc;
 }
 
-// amax of the whole tensor into *slot (cleared first by k_fill1): each wave
-// reduces its grid-stride share, one atomic max per wave on the value's bits
-// (non-negative floats order like their bit patterns).
+// amax of the whole tensor into *slot (cleared first by k_fill1): each
+// workgroup reduces its grid-stride share, then one atomic max per workgroup
+// on the value's bits (non-negative floats order like their bit patterns);
+// the grid is kept small so that few atomics meet at the one address.
 template <typename TIn>
 __global__ void __launch_bounds__(256) k_amax_tensor(const TIn* __restrict__ x, int64_t rows, int64_t cols,
                                                      int64_t ldx, float* __restrict__ slot) {
+  __shared__ float red[4];
   const int64_t per_row = cols / 16, items = rows * per_row;
   float a = 0.f;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < items; i += (int64_t)gridDim.x * 256) {
@@ -233,7 +235,10 @@ __global__ void __launch_bounds__(256) k_amax_tensor(const TIn* __restrict__ x, 
     for (int k = 0; k < 16; ++k) a = fmaxf(a, fabsf(v[k]));
   }
   a = group_max<64>(a);
-  if ((threadIdx.x & 63) == 0) atomicMax(reinterpret_cast<unsigned int*>(slot), __float_as_uint(a));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    atomicMax(reinterpret_cast<unsigned int*>(slot), __float_as_uint(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]))));
 }
 
 __global__ void k_fill1(float* p, float v) { *p = v; }
@@ -254,7 +259,7 @@ static void launch_quant(const TIn* x, int64_t rows, int64_t cols, int64_t ldx, 
       k_quant_rowwide<TIn, MODE><<<(unsigned)rows, 256, 0, st>>>(x, cols, ldx, q, ldq, s, ssr, nullptr);
     } else {
       k_fill1<<<1, 1, 0, st>>>(s, 0.f);
-      k_amax_tensor<TIn><<<grid_for(rows * (cols / 16), 256, 2048), 256, 0, st>>>(x, rows, cols, ldx, s);
+      k_amax_tensor<TIn><<<grid_for(rows * (cols / 16), 256, 512), 256, 0, st>>>(x, rows, cols, ldx, s);
       k_quant_rowwide<TIn, MODE><<<(unsigned)rows, 256, 0, st>>>(x, cols, ldx, q, ldq, nullptr, 0, s);
       k_tensor_scale<MODE><<<1, 1, 0, st>>>(s);
     }
