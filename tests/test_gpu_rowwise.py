@@ -313,3 +313,33 @@ def test_rowwise_end_to_end_on_the_gpu(m):
     assert np.array_equal(down(wq), owq) and np.array_equal(down(sw), osw)
     ref, bound = oracle.fp8_sparse24_gemm_rowwise(oxq, osx[:, 0], owq, ometa, osw[:, 0], bound=True)
     assert_within_tolerance(y, ref, bound, "end to end")
+
+
+def test_batched_full_size_sampled():
+    """The benchmark's batched launch: 8 problems of 256 x 4096 x 4096, each
+    with its own packed 2:4 weight; sampled outputs of every problem against
+    the oracle, computed one by one."""
+    L, m, n, k = 8, 256, 4096, 4096
+    say(f"batched full size L={L} M={m} N={n} K={k}")
+    xq, sx, wq, meta, sw = batched_operands(L, m, n, k, seed=100)
+    wp = torch.stack([sg.sparse24_pack_gfx950(up(wq[z]), up(meta[z])) for z in range(L)])
+    got = down(sg.fp8_sparse24_gemm_groupwise_packed_batched(up(xq), up_scales3(sx), wp, n, up_scales3(sw), 1, 128))
+    rng = np.random.default_rng(101)
+    for z in range(L):
+        rows = np.concatenate([[0, m - 1], rng.integers(0, m, 14)])
+        cols = np.concatenate([[0, n - 1], rng.integers(0, n, 30)])
+        ref, bound = oracle.fp8_sparse24_gemm_groupwise(xq[z][rows], sx[z][rows], 1, wq[z][cols], meta[z][cols],
+                                                         sw[z][cols // 128], 1, bound=True)
+        assert_within_tolerance(got[z][np.ix_(rows, cols)], ref, bound, f"problem {z}")
+
+
+@pytest.mark.parametrize("whole", ["rows", "tensor"])
+def test_whole_row_and_tensor_quant_full_size(whole):
+    """The benchmark's 2048 x 4096 activation, bit-exact."""
+    m, k = 2048, 4096
+    say(f"quant full size whole={whole}")
+    x = workloads.sparse_large(seed=3, m=m, n=8, k=k)["x"]
+    gr = 1 if whole == "rows" else m
+    q, s = sg.fp8_quant_groupwise(up(x), gr=gr, gc=k)
+    rq, rs = oracle.fp8_quant_groupwise(x, gr, k)
+    assert np.array_equal(down(q), rq) and np.array_equal(down(s), rs)
