@@ -255,6 +255,11 @@ def rows_report():
     ms = time_fn(lambda i: sg.fp8_sparse24_gemm_groupwise_packed_batched(xb, sxb, wpb, n, swb, 1, 128, y=yb))
     out[f"next_batched_sparse_gemm_packed_L{L}_{bm}x{n}x{k}_y"] = {
         "ms": ms, "TFLOP/s": flops / ms / 1e9, "frac_fp8_peak": flops / ms / 1e9 / PEAK_FP8_TFLOPS}
+    # grouped: 8 groups of different M (summing to 2048 rows), one packed weight each
+    sizes = [400, 120, 310, 256, 64, 380, 218, 300]
+    ms = time_fn(lambda i: sg.fp8_sparse24_gemm_groupwise_packed_grouped(xq, sx, sizes, wpb, n, swb, 128, y=y))
+    out[f"next_grouped_sparse_gemm_packed_G8_ragged{m}x{n}x{k}_y"] = {
+        "ms": ms, "TFLOP/s": flops / ms / 1e9, "frac_fp8_peak": flops / ms / 1e9 / PEAK_FP8_TFLOPS}
     del wpb, swb, yb
     # a7: fused int4 + bf16 add at L=2048, D1=4096, D2=64, D=4096
     dd = workloads.mixed_add(seed=5)

@@ -339,6 +339,29 @@ sg_status sg_fp8_sparse24_gemm_groupwise_packed_batched(int64_t L, int64_t M, in
                                                         sg_dtype y_dt, int64_t ldy, int64_t y_bs, sg_form form,
                                                         hipStream_t stream);
 
+/*
+ * sg_fp8_sparse24_gemm_groupwise_packed_grouped -- G problems that share N and
+ * K but not M (e.g. tokens routed to experts): group g multiplies rows
+ * row_off[g] .. row_off[g] + m_sizes[g] - 1 of X (row_off = prefix sums of
+ * m_sizes) with its own packed weight wpacked + g * wp_bs (bytes), W scales
+ * sw + g * sw_bs (floats) and bias + g * bias_bs, and writes the same rows of Y
+ * (SG_OUT_Y) or columns of Y^T (SG_OUT_YT).  X scales are per X row (gran_m 1):
+ * row r's scale of K block kb at sx[r * sx_sm + kb * sx_sk].  Every group follows
+ * sg_fp8_sparse24_gemm_groupwise_packed (scales constant along K included); one
+ * launch covers every group's 128-row tiles ([P2095] PR description: the L mode
+ * of the scale layout; this form lets L's problems differ in M).
+ *   m_sizes : HOST array of G entries >= 0 (0: an empty group).
+ * Requires 0 <= G <= 64, sum(m_sizes) as M and all requirements of the packed
+ * entry point and of the batched forms' strides; bias may be NULL.
+ */
+sg_status sg_fp8_sparse24_gemm_groupwise_packed_grouped(int64_t G, const int64_t* m_sizes, int64_t N, int64_t K,
+                                                        const uint8_t* xq, int64_t ldx, const float* sx,
+                                                        int64_t sx_sm, int64_t sx_sk, const uint8_t* wpacked,
+                                                        int64_t wp_bs, const float* sw, int64_t sw_sn,
+                                                        int64_t sw_sk, int64_t sw_bs, int gran_n, const float* bias,
+                                                        int64_t bias_bs, void* y, sg_dtype y_dt, int64_t ldy,
+                                                        sg_form form, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

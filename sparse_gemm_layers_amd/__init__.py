@@ -29,6 +29,7 @@ from ._binding import (
     fp8_gemm_groupwise_batched,
     fp8_sparse24_gemm_groupwise_batched,
     fp8_sparse24_gemm_groupwise_packed_batched,
+    fp8_sparse24_gemm_groupwise_packed_grouped,
 )
 
 __all__ = [
@@ -38,5 +39,5 @@ __all__ = [
     "mixed_gemm_add", "int8_quant_groupwise", "int8_sparse24_gemm_groupwise",
     "int8_sparse24_gemm_groupwise_packed", "probe_matrix_ops", "probe_matrix_rate", "k_constant_scales",
     "fp8_gemm_groupwise_batched", "fp8_sparse24_gemm_groupwise_batched",
-    "fp8_sparse24_gemm_groupwise_packed_batched",
+    "fp8_sparse24_gemm_groupwise_packed_batched", "fp8_sparse24_gemm_groupwise_packed_grouped",
 ]

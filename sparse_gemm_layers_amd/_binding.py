@@ -51,6 +51,9 @@ _SIGS = {
     "sg_fp8_sparse24_gemm_groupwise_packed_batched": ([_i64, _i64, _i64, _i64, _ptr, _i64, _i64, _ptr, _i64, _i64,
                                                        _i64, _int, _ptr, _i64, _ptr, _i64, _i64, _i64, _int, _ptr,
                                                        _i64, _ptr, _int, _i64, _i64, _int, _ptr], _int),
+    "sg_fp8_sparse24_gemm_groupwise_packed_grouped": ([_i64, _ptr, _i64, _i64, _ptr, _i64, _ptr, _i64, _i64, _ptr,
+                                                       _i64, _ptr, _i64, _i64, _i64, _int, _ptr, _i64, _ptr, _int,
+                                                       _i64, _int, _ptr], _int),
     "sg_probe_matrix_ops": ([_int, _int], _i64),
     "sg_probe_matrix_rate": ([_int, _int, _ptr, _ptr, _ptr], _int),
 }
@@ -333,6 +336,36 @@ def fp8_sparse24_gemm_groupwise_packed_batched(xq, sx, wpacked, n: int, sw, gran
         L, M, n, K, _p(xq), _mat(xq, "xq")[1], _bstride(xq), _p(sx), sxm, sxk, sxb, gran_m, _p(wpacked), wpb,
         _p(sw), swn, swk, swb, gran_n, bp, bb, _p(y), ydt, _mat(y, "y")[1], _bstride(y), f, _stream(xq))
     _check(st, "sg_fp8_sparse24_gemm_groupwise_packed_batched")
+    return y
+
+
+def fp8_sparse24_gemm_groupwise_packed_grouped(xq, sx, m_sizes, wpacked, n: int, sw, gran_n: int = 128,
+                                               out_dtype=torch.bfloat16, form: str = "y", y=None, bias=None):
+    """Grouped 2:4 GEMM: xq uint8 [sum(m_sizes), K] with the groups' rows one
+    after another, sx [sum(m_sizes), K/128] (one scale row per X row), one packed
+    weight per group wpacked [G, bytes] and its scales sw [G, ., K/128] (or 2-D /
+    1-D to share); returns y [sum, N] ("y") or [N, sum] ("yt")."""
+    sizes = [int(v) for v in m_sizes]
+    if not isinstance(xq, torch.Tensor) or not xq.is_cuda or xq.dim() != 2 or sum(sizes) != xq.shape[0]:
+        raise SgError("xq must be a 2-D GPU tensor whose rows m_sizes sums to")
+    if xq.shape[0] == 0 or n == 0:     # nothing to compute (and empty tensors carry no device address)
+        return _out(y, xq.shape[0], n, out_dtype, form, xq.device)[0]
+    _gpu2d(xq, "xq")
+    M, K = xq.shape
+    G = len(sizes)
+    need = sparse24_packed_bytes(n, K)
+    if not isinstance(wpacked, torch.Tensor) or not wpacked.is_cuda or wpacked.dim() not in (1, 2) \
+            or wpacked.shape[-1] < need or wpacked.stride(-1) != 1:
+        raise SgError("wpacked must be a GPU tensor [G, bytes] or [bytes] holding a packed weight")
+    wpb = 0 if wpacked.dim() == 1 or wpacked.shape[0] == 1 else wpacked.stride(0)
+    y, f, ydt = _out(y, M, n, out_dtype, form, xq.device)
+    swn, swk, swb = _sc(sw)
+    bp, bb = _bias(bias, n)
+    arr = (ctypes.c_int64 * max(G, 1))(*sizes)
+    st = lib().sg_fp8_sparse24_gemm_groupwise_packed_grouped(
+        G, ctypes.cast(arr, ctypes.c_void_p), n, K, _p(xq), _row_stride(xq), _p(sx), sx.stride(0), sx.stride(1),
+        _p(wpacked), wpb, _p(sw), swn, swk, swb, gran_n, bp, bb, _p(y), ydt, _row_stride(y), f, _stream(xq))
+    _check(st, "sg_fp8_sparse24_gemm_groupwise_packed_grouped")
     return y
 
 

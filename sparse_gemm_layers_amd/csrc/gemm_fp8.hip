@@ -412,15 +412,12 @@ __device__ __forceinline__ void issue_double(uint8_t* st, const PlanX2& p, __amd
 }
 #endif  // SG_DEVICE_PASS
 
-template <bool I8, bool PACKED, int GRAN_N, bool OUT_BF16, bool OUT_T>
-__global__ void __launch_bounds__(512) k_gemm_sparse_x2(GemmArgs a, int tiles_m, int tiles_n) {
 #if SG_DEVICE_PASS
+// One 256 x 128 output tile (n tile tn, m tile tm) of problem `a`.
+template <bool I8, bool PACKED, int GRAN_N, bool OUT_BF16, bool OUT_T>
+__device__ __forceinline__ void x2_tile(const GemmArgs& a, int tn, int tm) {
   __shared__ __attribute__((aligned(1024))) uint8_t db0[x2::DBL];
   __shared__ __attribute__((aligned(1024))) uint8_t db1[x2::DBL];
-  to_batch(a);
-
-  int tn, tm;
-  tile_coords(tiles_m, tiles_n, tn, tm);
   const int64_t n0 = (int64_t)tn * BN, m0 = (int64_t)tm * BM;
 
   const int t = threadIdx.x, l = t & 63;
@@ -498,6 +495,48 @@ __global__ void __launch_bounds__(512) k_gemm_sparse_x2(GemmArgs a, int tiles_m,
     x2_finish<1, OUT_BF16, OUT_T, x2::DBL, SCALE>(db0, db0, db1, acc, w4, l, wn, wm, g, lr, sxp, swp, bias, nlim);
   __syncthreads();
   store_staged<OUT_BF16, OUT_T, x2::DBL>(a, db0, db1, m0, n0, t);
+}
+#endif  // SG_DEVICE_PASS
+
+template <bool I8, bool PACKED, int GRAN_N, bool OUT_BF16, bool OUT_T>
+__global__ void __launch_bounds__(512) k_gemm_sparse_x2(GemmArgs a, int tiles_m, int tiles_n) {
+#if SG_DEVICE_PASS
+  to_batch(a);
+  int tn, tm;
+  tile_coords(tiles_m, tiles_n, tn, tm);
+  x2_tile<I8, PACKED, GRAN_N, OUT_BF16, OUT_T>(a, tn, tm);
+#endif  // SG_DEVICE_PASS
+}
+
+// Grouped problems (different M per group, one packed weight per group): the
+// groups' rows follow each other in X, in the scales of X and in Y; group g
+// owns the m tiles of rows row_off[g] .. row_off[g + 1] - 1, numbered from
+// tile_start[g] (tiles_n n tiles per m tile).
+constexpr int MAX_GROUPS = 64;
+struct GroupTable {
+  int G, tiles_n;
+  int tile_start[MAX_GROUPS + 1];
+  int64_t row_off[MAX_GROUPS + 1];
+};
+
+template <bool I8, bool PACKED, int GRAN_N, bool OUT_BF16, bool OUT_T>
+__global__ void __launch_bounds__(512) k_gemm_sparse_x2_grouped(GemmArgs a, GroupTable gt) {
+#if SG_DEVICE_PASS
+  const int b = xcd_order(blockIdx.x, gt.tile_start[gt.G]);
+  int g = 0;
+  while (g + 1 < gt.G && gt.tile_start[g + 1] <= b) ++g;   // uniform; empty groups are skipped
+  const int tiles_m = (gt.tile_start[g + 1] - gt.tile_start[g]) / gt.tiles_n;
+  int tn, tm;
+  tile_of(b - gt.tile_start[g], tiles_m, gt.tiles_n, tn, tm);
+  const int64_t r0 = gt.row_off[g];
+  a.M = gt.row_off[g + 1] - r0;
+  a.x += r0 * a.ldx;
+  a.sx += r0 * a.sx_sm;
+  a.y = static_cast<uint8_t*>(a.y) + (OUT_T ? r0 : r0 * a.ldy) * (OUT_BF16 ? 2 : 4);
+  a.w += g * a.bw;
+  a.sw += g * a.bsw;
+  if (a.bias) a.bias += g * a.bbs;
+  x2_tile<I8, PACKED, GRAN_N, OUT_BF16, OUT_T>(a, tn, tm);
 #endif  // SG_DEVICE_PASS
 }
 
@@ -1507,4 +1546,69 @@ extern "C" sg_status sg_fp8_sparse24_gemm_groupwise_packed_batched(
   b.bias = bias; b.bbs = bias_bs;
   return sparse24_gemm_packed<false>(M, N, K, xq, ldx, sx, sx_sm, sx_sk, gran_m, wpacked, sw, sw_sn, sw_sk, gran_n,
                                      y, y_dt, ldy, form, b, stream);
+}
+
+// Grouped 2:4 GEMM (one launch over every group's tiles; see GroupTable).
+template <int GRAN_N, bool OUT_BF16, bool OUT_T>
+static void launch_grouped(const GemmArgs& a, const GroupTable& gt, hipStream_t st) {
+  k_gemm_sparse_x2_grouped<false, true, GRAN_N, OUT_BF16, OUT_T>
+      <<<(unsigned)gt.tile_start[gt.G], 512, 0, st>>>(a, gt);
+}
+
+template <int GRAN_N>
+static void launch_grouped_form(const GemmArgs& a, const GroupTable& gt, bool bf16, bool yt, hipStream_t st) {
+  if (bf16) {
+    if (yt) launch_grouped<GRAN_N, true, true>(a, gt, st);
+    else launch_grouped<GRAN_N, true, false>(a, gt, st);
+  } else {
+    if (yt) launch_grouped<GRAN_N, false, true>(a, gt, st);
+    else launch_grouped<GRAN_N, false, false>(a, gt, st);
+  }
+}
+
+extern "C" sg_status sg_fp8_sparse24_gemm_groupwise_packed_grouped(
+    int64_t G, const int64_t* m_sizes, int64_t N, int64_t K, const uint8_t* xq, int64_t ldx, const float* sx,
+    int64_t sx_sm, int64_t sx_sk, const uint8_t* wpacked, int64_t wp_bs, const float* sw, int64_t sw_sn,
+    int64_t sw_sk, int64_t sw_bs, int gran_n, const float* bias, int64_t bias_bs, void* y, sg_dtype y_dt,
+    int64_t ldy, sg_form form, hipStream_t stream) {
+  if (G < 0 || G > MAX_GROUPS) return SG_ERR_SHAPE;
+  if (G > 0 && !m_sizes) return SG_ERR_NULL;
+  GroupTable gt;
+  gt.G = (int)G;
+  gt.row_off[0] = 0;
+  for (int g = 0; g < G; ++g) {
+    if (m_sizes[g] < 0) return SG_ERR_SHAPE;
+    gt.row_off[g + 1] = gt.row_off[g] + m_sizes[g];
+  }
+  const int64_t M = gt.row_off[G];
+  sg_status st = check_common(M, N, K, xq, ldx, sx, sx_sm, sx_sk, 1, sw, sw_sn, sw_sk, gran_n, y, y_dt, ldy, form);
+  if (st != SG_OK) return st;
+  Batch b;
+  b.bw = wp_bs; b.bsw = sw_bs; b.bias = bias; b.bbs = bias_bs;
+  if ((st = check_batch(b)) != SG_OK) return st;
+  if (!wpacked) return SG_ERR_NULL;
+  if (!aligned(wpacked, 16)) return SG_ERR_ALIGN;
+  if ((K / 128) * (int64_t)(BN / PK_ROWS) * PK_CHUNK > 0x7fffffffLL) return SG_ERR_SHAPE;
+  const int64_t tiles_n = cdiv(N, BN);
+  gt.tiles_n = (int)tiles_n;
+  gt.tile_start[0] = 0;
+  for (int g = 0; g < G; ++g) {
+    const int64_t t = gt.tile_start[g] + cdiv(m_sizes[g], BM) * tiles_n;
+    if (t > 0x7fffffffLL) return SG_ERR_SHAPE;
+    gt.tile_start[g + 1] = (int)t;
+  }
+  if (G == 0 || gt.tile_start[G] == 0 || N == 0) return SG_OK;
+  GemmArgs a = make_args(M, N, K, xq, ldx, sx, sx_sm, sx_sk, 1, wpacked, 0, nullptr, 0, sw, sw_sn, sw_sk, gran_n,
+                         y, y_dt, ldy, b);
+  // Y^T: a group's columns start at its row offset, so 16-byte stores need
+  // every offset to keep 16-byte alignment.
+  if (form == SG_OUT_YT)
+    for (int g = 0; g < G; ++g)
+      if ((gt.row_off[g] * (int64_t)dtype_size(y_dt)) % 16) a.vec16 = 0;
+  clear_hip_error();
+  const bool bf16 = y_dt == SG_BF16, yt = form == SG_OUT_YT;
+  if (sx_sk == 0 && sw_sk == 0) launch_grouped_form<0>(a, gt, bf16, yt, stream);
+  else if (gran_n == 128) launch_grouped_form<128>(a, gt, bf16, yt, stream);
+  else launch_grouped_form<1>(a, gt, bf16, yt, stream);
+  return launch_status();
 }

@@ -12,10 +12,12 @@ constexpr int TILE_N = 256, TILE_M = 128;
 // Workgroups go to the 8 XCDs round-robin.  Renumber so that each XCD owns a
 // contiguous range of tile ids, then walk tiles in groups of 4 n-tiles so that
 // the tiles resident on one XCD share W rows and X rows in its L2.
-__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tn, int& tm) {
-  const int T = tiles_m * tiles_n;
-  int b = blockIdx.x;
-  if ((T & 7) == 0) b = (b & 7) * (T >> 3) + (b >> 3);
+__device__ __forceinline__ int xcd_order(int b, int T) {
+  return (T & 7) == 0 ? (b & 7) * (T >> 3) + (b >> 3) : b;
+}
+
+// Tile b (in the XCD order) of a tiles_m x tiles_n grid.
+__device__ __forceinline__ void tile_of(int b, int tiles_m, int tiles_n, int& tn, int& tm) {
   const int G = 4;
   const int group = b / (G * tiles_m);
   const int first_n = group * G;
@@ -23,6 +25,10 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tn, i
   const int in_g = b - group * G * tiles_m;
   tn = first_n + in_g % gsize;
   tm = in_g / gsize;
+}
+
+__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tn, int& tm) {
+  tile_of(xcd_order(blockIdx.x, tiles_m * tiles_n), tiles_m, tiles_n, tn, tm);
 }
 
 // Partial-tile exchange between the two K groups (rows I0 .. I0+3 of the

@@ -43,7 +43,7 @@ def test_header_declares_the_entry_points():
         "sg_fp8_sparse24_gemm_groupwise_packed", "sg_probe_matrix_ops", "sg_probe_matrix_rate",
         "sg_int8_quant_groupwise", "sg_int8_sparse24_gemm_groupwise", "sg_int8_sparse24_gemm_groupwise_packed",
         "sg_fp8_gemm_groupwise_batched", "sg_fp8_sparse24_gemm_groupwise_batched",
-        "sg_fp8_sparse24_gemm_groupwise_packed_batched"])
+        "sg_fp8_sparse24_gemm_groupwise_packed_batched", "sg_fp8_sparse24_gemm_groupwise_packed_grouped"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -312,3 +312,27 @@ def test_k_constant_scale_views():
     assert t.shape == (7, 2) and t.stride() == (0, 0)
     with pytest.raises(sg.SgError):
         sg.k_constant_scales(torch.ones(3), 5, 128)
+
+
+def grouped(sizes, **kw):
+    a = dict(N=256, K=256, x=P, ldx=256, sx=P3, sxm=1, sxk=512, w=P2, wb=16 * 2 * 1280, sw=P3, swn=2, swk=1, swb=4,
+             gn=128, bias=None, bb=0, y=P, ydt=1, ldy=256, form=0)
+    a.update(kw)
+    arr = (ctypes.c_int64 * max(len(sizes), 1))(*sizes)
+    G = a.pop("G", len(sizes))
+    return sg.lib().sg_fp8_sparse24_gemm_groupwise_packed_grouped(
+        G, ctypes.cast(arr, ctypes.c_void_p) if a.get("nosizes") is None else None, a["N"], a["K"], a["x"],
+        a["ldx"], a["sx"], a["sxm"], a["sxk"], a["w"], a["wb"], a["sw"], a["swn"], a["swk"], a["swb"], a["gn"],
+        a["bias"], a["bb"], a["y"], a["ydt"], a["ldy"], a["form"], None)
+
+
+@no_gpu
+@pytest.mark.parametrize("sizes,kw,code", [
+    ([10, -1], {}, SHAPE), ([1] * 65, {}, SHAPE), ([5], dict(G=-1), SHAPE), ([5], dict(nosizes=1), NULL),
+    ([0, 0, 0], {}, OK), ([], {}, OK), ([5, 7], dict(x=None), NULL), ([5, 7], dict(w=None), NULL),
+    ([5, 7], dict(w=ODD), ALIGN), ([5, 7], dict(wb=8), ALIGN), ([5, 7], dict(swb=-1), SHAPE),
+    ([5, 7], dict(K=200), SHAPE), ([5, 7], dict(gn=3), UNSUP), ([5, 7], dict(bb=-2, bias=P2), SHAPE),
+    ([5, 7], dict(N=0), OK),
+])
+def test_grouped_gemm_validation(sizes, kw, code):
+    assert grouped(sizes, **kw) == code

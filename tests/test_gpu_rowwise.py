@@ -343,3 +343,76 @@ def test_whole_row_and_tensor_quant_full_size(whole):
     q, s = sg.fp8_quant_groupwise(up(x), gr=gr, gc=k)
     rq, rs = oracle.fp8_quant_groupwise(x, gr, k)
     assert np.array_equal(down(q), rq) and np.array_equal(down(s), rs)
+
+
+# --------------------------------------------------------------- grouped (ragged M)
+
+def grouped_operands(sizes, n, k, seed, gn=128):
+    """X rows of all groups one after another (1 x 128 scales), one pruned,
+    quantised, packed weight per group."""
+    m = sum(sizes)
+    d = workloads.sparse_large(seed=seed, m=max(m, 1), n=8, k=k)
+    xq, sx = oracle.fp8_quant_groupwise(d["x"][:m], 1, 128)
+    ws = []
+    for g in range(len(sizes)):
+        w = workloads.sparse_large(seed=seed + 1 + g, m=1, n=n, k=k)["w"]
+        wv32, meta = oracle.prune_compress24(w)
+        wq, sw = oracle.fp8_quant_groupwise(wv32, gn, 64)
+        ws.append((wq, meta, sw))
+    return xq, sx, ws
+
+
+@pytest.mark.parametrize("sizes,form,out,gn", [([300, 0, 1, 128, 129, 64], "y", torch.bfloat16, 128),
+                                               ([5, 7, 300], "yt", torch.bfloat16, 128),
+                                               ([200, 72], "yt", torch.float32, 1),
+                                               ([16], "y", torch.float32, 128),
+                                               ([0, 0], "y", torch.bfloat16, 128)])
+def test_grouped(sizes, form, out, gn):
+    n, k = 384, 512
+    say(f"grouped sizes={sizes} N={n} K={k} form={form} {out} gn={gn}")
+    xq, sx, ws = grouped_operands(sizes, n, k, seed=110 + len(sizes), gn=gn)
+    wp = torch.stack([sg.sparse24_pack_gfx950(up(wq), up(meta)) for wq, meta, _ in ws])
+    sw = torch.stack([up_m_major(s) for _, _, s in ws])
+    bias = (np.random.default_rng(111).standard_normal((len(sizes), n))).astype(np.float32)
+    got = down(sg.fp8_sparse24_gemm_groupwise_packed_grouped(up(xq), up_m_major(sx), sizes, wp, n, sw, gn,
+                                                             out_dtype=out, form=form, bias=up(bias)))
+    got = got.T if form == "yt" else got
+    assert got.shape == (sum(sizes), n)
+    r = 0
+    for g, mg in enumerate(sizes):
+        if mg:
+            wq, meta, swg = ws[g]
+            ref, bound = oracle.fp8_sparse24_gemm_groupwise(xq[r:r + mg], sx[r:r + mg], 1, wq, meta, swg, gn,
+                                                             bound=True)
+            ref, bound = oracle.add_bias(ref, bound, bias[g])
+            assert_within_tolerance(got[r:r + mg].astype(np.float64), ref, bound, f"group {g}")
+        r += mg
+
+
+def test_grouped_rowwise_scales():
+    sizes, n, k = [130, 3, 257], 512, 640
+    say(f"grouped rowwise sizes={sizes} N={n} K={k}")
+    m = sum(sizes)
+    d = workloads.sparse_large(seed=120, m=m, n=8, k=k)
+    xq, sx = oracle.fp8_quant_groupwise(d["x"], 1, k)
+    ops = []
+    for g in range(len(sizes)):
+        w = workloads.sparse_large(seed=121 + g, m=1, n=n, k=k)["w"]
+        wv32, meta = oracle.prune_compress24(w)
+        wq, sw = oracle.fp8_quant_groupwise(wv32, 1, k // 2)
+        ops.append((wq, meta, sw[:, 0].copy()))
+    wp = torch.stack([sg.sparse24_pack_gfx950(up(wq), up(meta)) for wq, meta, _ in ops])
+    swt = up(np.stack([s for _, _, s in ops]))[:, :, None].expand(len(sizes), n, k // 128)
+    sxt = sg.k_constant_scales(up(sx[:, 0].copy()), m, k)
+    got = down(sg.fp8_sparse24_gemm_groupwise_packed_grouped(up(xq), sxt, sizes, wp, n, swt, 1))
+    r = 0
+    for g, mg in enumerate(sizes):
+        wq, meta, swg = ops[g]
+        ref, bound = oracle.fp8_sparse24_gemm_rowwise(xq[r:r + mg], sx[r:r + mg, 0], wq, meta, swg, bound=True)
+        assert_within_tolerance(got[r:r + mg], ref, bound, f"group {g}")
+        r += mg
+
+
+def up_m_major(s):
+    """[rows, KB] scales -> device view stored M-major."""
+    return torch.from_numpy(np.ascontiguousarray(s.T)).to(DEV).t()
