@@ -41,6 +41,7 @@ from .gemm import (
     fp8_sparse24_gemm_rowwise,
     int8_sparse24_gemm_rowwise,
     add_bias,
+    w8a16_sparse24_gemm_groupwise,
     mixed_gemm_add,
     within_tolerance,
 )
@@ -52,5 +53,5 @@ __all__ = [
     "pack24_gfx950", "unpack24_gfx950", "packed_bytes",
     "expand_scales", "fp8_gemm_groupwise", "fp8_sparse24_gemm_groupwise",
     "int8_gemm_groupwise", "int8_sparse24_gemm_groupwise", "fp8_gemm_rowwise",
-    "fp8_sparse24_gemm_rowwise", "int8_sparse24_gemm_rowwise", "add_bias", "mixed_gemm_add", "within_tolerance",
+    "fp8_sparse24_gemm_rowwise", "int8_sparse24_gemm_rowwise", "add_bias", "w8a16_sparse24_gemm_groupwise", "mixed_gemm_add", "within_tolerance",
 ]

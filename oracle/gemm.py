@@ -50,6 +50,14 @@ so the scale can be applied once, after the whole K sum.  The full-K sum is
 still exact in fp64 (integer multiples of 2^-18 below 2^(17.6 + log2 K) <
 2^53 quanta for K < 2^17).
 
+Weight-only 2:4 GEMM (W8A16): bf16 activations, unquantised, times a 2:4
+weight of 8-bit codes (e4m3 or int8) with groupwise scales.  torchao PR
+#3258's review (jcaip) says weight-only sparsity configs for int8 and float8
+have no mixed-dtype kernel to run on; this is that operation:
+    y[m, n] = sum_kb sw[n // gN, kb] * sum_{k in kb} bf16(x[m, k]) * dec(wq[n, k])
+Every product is exact in fp64 (8 x 8 significant bits); the K-block sums are
+exact up to fp64 rounding (relative 2^-53 of the block's abs-sum).
+
 Bias epilogue: the sparse FP8 linear implementation torchao PR #3258's review
 points to takes a bias argument; a linear layer adds it to every row of the
 output, y[m, n] + bias[n], after the scales.  In the tolerance the bias is one
@@ -175,6 +183,24 @@ def int8_sparse24_gemm_rowwise(xq, sx, wv, wmeta, sw, bound: bool = False):
     wq = decompress24(np.asarray(wv, dtype=np.int8).view(np.uint8), wmeta).view(np.int8)
     xd = np.asarray(xq, dtype=np.int8).astype(np.float64)
     return _rowwise(xd, sx, wq.astype(np.float64), sw, bound)
+
+
+def w8a16_sparse24_gemm_groupwise(x_bits, wv, wmeta, sw, gn: int, codes: str = "e4m3", bound: bool = False):
+    """x_bits bf16 bits [M, K]; wv [N, K/2] 2:4 compressed codes (e4m3 bytes, or
+    int8) with metadata wmeta [N, K/8] and scales sw [ceil(N/gn), K/128]."""
+    assert codes in ("e4m3", "int8") and gn in (1, 128)
+    xd = bf16_decode(x_bits)
+    wq = decompress24(np.asarray(wv).view(np.uint8), wmeta)
+    wd = e4m3_decode(wq) if codes == "e4m3" else wq.view(np.int8).astype(np.float64)
+    m, k = xd.shape
+    n = wd.shape[0]
+    swe = expand_scales(sw, gn, n)
+    assert swe.shape == (n, k // KBLK) and wd.shape[1] == k
+    ones = np.ones((m, k // KBLK), dtype=np.float64)
+    y = _scaled_kblock_sum(xd, ones, wd, swe, absolute=False)
+    if not bound:
+        return y
+    return y, _scaled_kblock_sum(xd, ones, wd, swe, absolute=True)
 
 
 def add_bias(y, bound, bias):

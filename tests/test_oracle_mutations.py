@@ -224,3 +224,28 @@ def test_bias_on_rows_instead_of_columns_is_caught(monkeypatch):
         return y + np.resize(b, y.shape[0])[:, None], bound + np.abs(np.resize(b, y.shape[0]))[:, None]
     monkeypatch.setattr(oracle, "add_bias", add_bias)
     _fails(t_row.test_bias_adds_per_output_column_exactly_on_integers)
+
+
+import test_oracle_w8a16 as t_w8  # noqa: E402
+
+
+def test_w8a16_scale_of_wrong_kblock_is_caught(monkeypatch):
+    orig = gemm_mod.w8a16_sparse24_gemm_groupwise
+
+    def gemm(x_bits, wv, wmeta, sw, gn, codes="e4m3", bound=False):
+        return orig(x_bits, wv, wmeta, np.roll(np.asarray(sw), 1, axis=1), gn, codes, bound)
+    monkeypatch.setattr(oracle, "w8a16_sparse24_gemm_groupwise", gemm)
+    _fails(t_w8.test_w8a16_matches_exact_rationals, False, 128)
+
+
+def test_w8a16_int8_read_unsigned_is_caught(monkeypatch):
+    orig = gemm_mod.w8a16_sparse24_gemm_groupwise
+
+    def gemm(x_bits, wv, wmeta, sw, gn, codes="e4m3", bound=False):
+        if codes == "int8":
+            wq = oracle.decompress24(np.asarray(wv).view(np.uint8), wmeta).astype(np.float64)
+            y = oracle.bf16_decode(x_bits) @ wq.T * np.float64(np.asarray(sw).reshape(-1)[0])
+            return (y, np.abs(y)) if bound else y
+        return orig(x_bits, wv, wmeta, sw, gn, codes, bound)
+    monkeypatch.setattr(oracle, "w8a16_sparse24_gemm_groupwise", gemm)
+    _fails(t_w8.test_w8a16_integer_activations_int8_codes_unit_scales)
