@@ -39,6 +39,7 @@ import workloads  # noqa: E402
 METRIC = "dense-equiv FP8 TFLOP/s @M=2048 N=K=4096 2:4 W; % MFMA peak; M=16 GB/s"
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense FP8 MFMA
 PEAK_INT8_TOPS = 5000.0
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 # the sources the sparse GEMM kernel is compiled from (a change voids the recorded traffic)
 GEMM_SRCS = [os.path.join(ROOT, "sparse_gemm_layers_amd", "csrc", f)
@@ -261,6 +262,37 @@ def rows_report():
     out[f"next_grouped_sparse_gemm_packed_G8_ragged{m}x{n}x{k}_y"] = {
         "ms": ms, "TFLOP/s": flops / ms / 1e9, "frac_fp8_peak": flops / ms / 1e9 / PEAK_FP8_TFLOPS}
     del wpb, swb, yb
+    # next row: weight-only 2:4 (bf16 activations x e4m3 / int8 2:4 codes) at
+    # the decode shapes (rotating weight copies) and at 2048x4096x4096
+    dn, dk = 14336, 4096
+    for codes in ("e4m3", "int8"):
+        qf = sg.int8_quant_groupwise if codes == "int8" else sg.fp8_quant_groupwise
+        wsets = []
+        for i in range(ROTATE_DECODE):
+            g = torch.Generator(device=DEV)
+            g.manual_seed(5000 + i)
+            v, mt = sg.sparse24_prune_compress(torch.randn((dn, dk), generator=g, device=DEV) * 0.02)
+            q, s8 = qf(v, gr=128, gc=64)
+            wsets.append((q, mt, s8))
+            del v
+        for dm in (16, 37):
+            xb = torch.from_numpy(workloads.decode(seed=4, m=dm, n=8, k=dk)["x"]).to(DEV).to(torch.bfloat16)
+            y = torch.empty((dm, dn), dtype=torch.bfloat16, device=DEV)
+            ms = time_fn(lambda i: sg.w8a16_sparse24_gemm_groupwise(
+                xb, wsets[i % ROTATE_DECODE][0], wsets[i % ROTATE_DECODE][1], wsets[i % ROTATE_DECODE][2], 128, y=y),
+                reps=64, warm=16)
+            b = dn * dk // 2 + dn * dk // 8 + 4 * (dn // 128) * (dk // 128) + dm * dk * 2 + dm * dn * 2
+            out[f"next_w8a16_{codes}_decode_M{dm}_N{dn}_K{dk}_y"] = {"ms": ms, "GB/s": b / ms / 1e6,
+                                                                   "frac_hbm": b / ms / 1e6 / PEAK_HBM_GBS}
+        del wsets
+    xb = x.to(torch.bfloat16)
+    wv8, mt8 = sg.sparse24_prune_compress(torch.from_numpy(workloads.sparse_large(seed=3, m=8, n=n, k=k)["w"]).to(DEV))
+    wq8, sw8 = sg.fp8_quant_groupwise(wv8, gr=128, gc=64)
+    y = torch.empty((m, n), dtype=torch.bfloat16, device=DEV)
+    ms = time_fn(lambda i: sg.w8a16_sparse24_gemm_groupwise(xb, wq8, mt8, sw8, 128, y=y), reps=10, warm=2)
+    out["next_w8a16_e4m3_gemm_2048x4096x4096_y"] = {"ms": ms, "TFLOP/s": flops / ms / 1e9,
+                                                    "frac_bf16_peak": flops / ms / 1e9 / PEAK_BF16_TFLOPS}
+    del xb, wv8, mt8, wq8
     # a7: fused int4 + bf16 add at L=2048, D1=4096, D2=64, D=4096
     dd = workloads.mixed_add(seed=5)
     x1, sx1 = sg.int4_quant_groupwise(torch.from_numpy(dd["x1"]).to(DEV))

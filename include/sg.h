@@ -50,7 +50,7 @@ typedef enum {
   SG_ERR_HIP = 5          /* the HIP runtime reported an error at launch         */
 } sg_status;
 
-typedef enum { SG_F32 = 0, SG_BF16 = 1, SG_E4M3 = 2 } sg_dtype;
+typedef enum { SG_F32 = 0, SG_BF16 = 1, SG_E4M3 = 2, SG_I8 = 3 } sg_dtype;
 
 /* Output form of the GEMMs.  Both compute the same numbers.
  *   SG_OUT_Y : Y   [M, N] row-major, element (m, n) at y[m * ldy + n]
@@ -338,6 +338,31 @@ sg_status sg_fp8_sparse24_gemm_groupwise_packed_batched(int64_t L, int64_t M, in
                                                         const float* bias, int64_t bias_bs, void* y,
                                                         sg_dtype y_dt, int64_t ldy, int64_t y_bs, sg_form form,
                                                         hipStream_t stream);
+
+/*
+ * sg_w8a16_sparse24_gemm_groupwise -- weight-only 2:4 GEMM: bf16 activations
+ * (not quantised) times a 2:4 weight of 8-bit codes with groupwise scales.
+ * [T3258] jcaip's review (weight-only sparsity configs for int8 and float8
+ * have no mixed-dtype kernel); [P2095] hwu36's comment (scale blocks):
+ *   y[m, n] = sum_kb sw[n/gran_n, kb] * sum_{k in kb} x[m, k] * dec(w[n, k])  (+ bias[n])
+ *   x     : [M, K] bf16 bits, leading dim ldx (elements).
+ *   wv    : [N, K/2] codes, w_dt = SG_E4M3 or SG_I8, as produced by
+ *           sg_sparse24_prune_compress then sg_fp8_quant_groupwise or
+ *           sg_int8_quant_groupwise at gr = 128 (or 1), gc = 64; ld ldwv (bytes).
+ *   wmeta : [N, K/8] metadata, ld ldwm.   sw, gran_n: as sg_fp8_gemm_groupwise.
+ *   bias  : [N] fp32 or NULL.   y, y_dt, ldy, form: as sg_fp8_gemm_groupwise.
+ * The codes are widened to bf16 (exactly) in registers and multiplied on the
+ * dense bf16 matrix core; shaped for decode sizes (a workgroup streams its
+ * weight rows once per 64 rows of X).
+ * Requires K % 128 == 0, ldx >= K, ldwv >= K/2, ldwm >= K/8, ldx, ldwv, ldwm <
+ * 2^24, ceil(M/16) <= 65535; x, wv 16-byte aligned, ldx * 2 and ldwv multiples
+ * of 16, wmeta 16-byte aligned and ldwm a multiple of 16.
+ */
+sg_status sg_w8a16_sparse24_gemm_groupwise(int64_t M, int64_t N, int64_t K, const uint16_t* x, int64_t ldx,
+                                           const uint8_t* wv, int64_t ldwv, const uint8_t* wmeta, int64_t ldwm,
+                                           sg_dtype w_dt, const float* sw, int64_t sw_sn, int64_t sw_sk, int gran_n,
+                                           const float* bias, void* y, sg_dtype y_dt, int64_t ldy, sg_form form,
+                                           hipStream_t stream);
 
 /*
  * sg_fp8_sparse24_gemm_groupwise_packed_grouped -- G problems that share N and

@@ -14,7 +14,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsg.so")
 
-SG_F32, SG_BF16, SG_E4M3 = 0, 1, 2
+SG_F32, SG_BF16, SG_E4M3, SG_I8 = 0, 1, 2, 3
 SG_OUT_Y, SG_OUT_YT = 0, 1
 
 _i64 = ctypes.c_int64
@@ -54,6 +54,8 @@ _SIGS = {
     "sg_fp8_sparse24_gemm_groupwise_packed_grouped": ([_i64, _ptr, _i64, _i64, _ptr, _i64, _ptr, _i64, _i64, _ptr,
                                                        _i64, _ptr, _i64, _i64, _i64, _int, _ptr, _i64, _ptr, _int,
                                                        _i64, _int, _ptr], _int),
+    "sg_w8a16_sparse24_gemm_groupwise": ([_i64, _i64, _i64, _ptr, _i64, _ptr, _i64, _ptr, _i64, _int, _ptr, _i64,
+                                          _i64, _int, _ptr, _ptr, _int, _i64, _int, _ptr], _int),
     "sg_probe_matrix_ops": ([_int, _int], _i64),
     "sg_probe_matrix_rate": ([_int, _int, _ptr, _ptr, _ptr], _int),
 }
@@ -366,6 +368,33 @@ def fp8_sparse24_gemm_groupwise_packed_grouped(xq, sx, m_sizes, wpacked, n: int,
         G, ctypes.cast(arr, ctypes.c_void_p), n, K, _p(xq), _row_stride(xq), _p(sx), sx.stride(0), sx.stride(1),
         _p(wpacked), wpb, _p(sw), swn, swk, swb, gran_n, bp, bb, _p(y), ydt, _row_stride(y), f, _stream(xq))
     _check(st, "sg_fp8_sparse24_gemm_groupwise_packed_grouped")
+    return y
+
+
+def w8a16_sparse24_gemm_groupwise(x, wv, wmeta, sw, gran_n: int = 128, out_dtype=torch.bfloat16, form: str = "y",
+                                   y=None, bias=None):
+    """Weight-only 2:4 GEMM: x bfloat16 [M, K] (not quantised) times 2:4 codes
+    wv [N, K/2] (uint8: e4m3, int8: int8) with metadata wmeta [N, K/8] and W
+    scales sw [ceil(N/gran_n), K/128]."""
+    _gpu2d(x, "x")
+    _gpu2d(wv, "wv")
+    _gpu2d(wmeta, "wmeta")
+    if x.dtype != torch.bfloat16:
+        raise SgError("x must be bfloat16")
+    if wv.dtype == torch.uint8:
+        wdt = SG_E4M3
+    elif wv.dtype == torch.int8:
+        wdt = SG_I8
+    else:
+        raise SgError("wv must be uint8 (e4m3 codes) or int8")
+    M, K = x.shape
+    N = wv.shape[0]
+    y, f, ydt = _out(y, M, N, out_dtype, form, x.device)
+    bp, _ = _bias(bias, N)
+    st = lib().sg_w8a16_sparse24_gemm_groupwise(M, N, K, _p(x), _row_stride(x), _p(wv), _row_stride(wv), _p(wmeta),
+                                                _row_stride(wmeta), wdt, _p(sw), sw.stride(0), sw.stride(1), gran_n,
+                                                bp, _p(y), ydt, _row_stride(y), f, _stream(x))
+    _check(st, "sg_w8a16_sparse24_gemm_groupwise")
     return y
 
 

@@ -1,0 +1,304 @@
+// Weight-only 2:4 GEMM (W8A16): Y = X . W^T with X in bf16 (unquantised) and
+// W as 2:4-compressed 8-bit codes (e4m3 or int8) with groupwise scales.
+//
+// torchao PR #3258 "Introduce new W8A8-FP-CSR quantization API": jcaip's
+// review says weight-only sparsity configs for int8 and float8 have no
+// mixed-dtype kernel to run on; CUTLASS PR #2095 "Improvements for: Groupwise
+// scaling along M for FP8 gemm" (hwu36's comment) fixes the scale blocks:
+//   y[m, n] = sum_kb sw[n / gran_n, kb] * sum_{k in kb} x[m, k] * dec(w[n, k]).
+//
+// gfx950 has no matrix instruction that mixes 8-bit and bf16 operands, so the
+// codes are widened to bf16 in registers (exact for both code types) and
+// multiplied on the sparse bf16 matrix core (v_smfmac_f32_16x16x64_bf16),
+// which reads the 2:4 metadata itself.  Its operand layout, measured on
+// MI355X with one-hot operands: per 64-wide K slice, B lane (group g', column
+// c) holds 16 values, virtual k = 16 g' + e; A lane group g holds the
+// compressed pairs of the virtual groups of 4 {b, b+1, b+4, b+5},
+// b = 8 (g & 1) + 2 (g >> 1), and nibble p of its index word (bits 4p..4p+3)
+// places pair p inside its group.  The instruction sums over its K in any
+// order, so virtual groups may stand for any aligned groups of the weight as
+// long as A and B agree: here A lane group g of instruction h (K slice
+// 64 h .. 64 h + 63 of a 128-wide K block) takes the four consecutive groups
+// 16 h + 4 g .. + 3, i.e. 8 contiguous code bytes and 16 contiguous metadata
+// bits (the index word as stored), and B lane group g' then holds
+// x[k = 64 h + 8 g' .. + 7] and x[k = 64 h + 32 + 8 g' .. + 7].
+//
+// The kernel is shaped for the decode sizes where weight-only quantisation is
+// used (M <= 64 per workgroup): a workgroup owns RB blocks of 16 W rows and MT
+// sub-tiles of 16 X rows, its 8 waves split the K blocks, read their operands
+// straight from global memory and add their partial tiles through LDS; the
+// weight is streamed from HBM once per 64 X rows.
+#include "tile_epilogue.h"
+#include "sg.h"
+
+namespace sg {
+
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v16bf __attribute__((ext_vector_type(16)));
+
+struct W8Args {
+  int64_t M, N, K;
+  const uint16_t* x;     // bf16 [M, K]
+  int64_t ldx;           // elements
+  const uint8_t* w;      // codes [N, K/2]
+  int64_t ldw;
+  const uint8_t* meta;   // [N, K/8]
+  int64_t ldm;
+  const float* sw;
+  int64_t sw_sn, sw_sk;
+  int gn_shift;
+  const float* bias;     // [N] or NULL
+  void* y;
+  int64_t ldy;
+  int vec_store;
+};
+
+constexpr int W8_WAVES = 8, W8_U = 2;
+
+#if SG_DEVICE_PASS
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t w8_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ v4i w8_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off, int soff) {
+  return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0));
+}
+__device__ __forceinline__ int w8_ld4(__amdgpu_buffer_rsrc_t r, uint32_t off, int soff) {
+  return __builtin_bit_cast(int, __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, 0));
+}
+
+// bf16 bits of the two codes in the low (HI = false) or high half of w,
+// first code in the low 16 bits.  Both conversions are exact.
+template <bool I8, bool HI>
+__device__ __forceinline__ uint32_t bf16_pair(uint32_t w) {
+  float f0, f1;
+  if constexpr (I8) {
+    f0 = (float)(int)(int8_t)(w >> (HI ? 16 : 0));
+    f1 = (float)(int)(int8_t)(w >> (HI ? 24 : 8));
+  } else {
+    const auto f = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
+    f0 = f[0];
+    f1 = f[1];
+  }
+  return (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xffff0000u);
+}
+
+__device__ __forceinline__ v2i w8_ld8(__amdgpu_buffer_rsrc_t r, uint32_t off, int soff) {
+  return __builtin_bit_cast(v2i, __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, 0));
+}
+
+// bf16 A operand (8 values) of 8 consecutive code bytes (two dwords).
+template <bool I8>
+__device__ __forceinline__ v4i widen8(int w0, int w1) {
+  return (v4i){(int)bf16_pair<I8, false>((uint32_t)w0), (int)bf16_pair<I8, true>((uint32_t)w0),
+               (int)bf16_pair<I8, false>((uint32_t)w1), (int)bf16_pair<I8, true>((uint32_t)w1)};
+}
+
+template <int RB, int MT>
+struct W8Ops {
+  v4i cw[RB];       // code bytes of W row n0 + 16 rb + lr: 8 for K slice 0, 8 for slice 1
+  v4i mw[RB];       // the row's 16 metadata bytes of the K block
+  v4i bx[MT][4];    // X row m0 + 16 j + lr: k = 8 g + 32 q .. + 7 for q = 0..3
+  float sw4[RB][4];
+};
+
+template <int RB, int MT, int GRAN_N>
+__device__ __forceinline__ void w8_load(const W8Args& a, __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t rm,
+                                        __amdgpu_buffer_rsrc_t rx, int64_t n0, int kb, int lr, int g,
+                                        W8Ops<RB, MT>& o) {
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const uint32_t r = (uint32_t)(16 * rb + lr);
+    const v2i c0 = w8_ld8(rw, r * (uint32_t)a.ldw + 8 * g, kb * 64);
+    const v2i c1 = w8_ld8(rw, r * (uint32_t)a.ldw + 32 + 8 * g, kb * 64);
+    o.cw[rb] = (v4i){c0[0], c0[1], c1[0], c1[1]};
+    o.mw[rb] = w8_ld16(rm, r * (uint32_t)a.ldm, kb * 16);
+    const int64_t nb = n0 + 16 * rb;   // rows past N read the last row's scale (never stored)
+    if (GRAN_N == 128) {
+      const float v = a.sw[(min(nb, a.N - 1) >> 7) * a.sw_sn + kb * a.sw_sk];
+      o.sw4[rb][0] = o.sw4[rb][1] = o.sw4[rb][2] = o.sw4[rb][3] = v;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o.sw4[rb][e] = a.sw[min(nb + 4 * g + e, a.N - 1) * a.sw_sn + kb * a.sw_sk];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < MT; ++j) {
+    const uint32_t xo = (uint32_t)((16 * j + lr) * a.ldx * 2) + 16 * g;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o.bx[j][q] = w8_ld16(rx, xo + 64 * q, kb * 256);
+  }
+}
+
+// 16-bit index word of metadata halfword hw of a row's 16 bytes.
+__device__ __forceinline__ int meta_half(const v4i& m, int hw) {
+  const uint32_t d = (uint32_t)((hw >> 1) == 0 ? m[0] : (hw >> 1) == 1 ? m[1] : (hw >> 1) == 2 ? m[2] : m[3]);
+  return (int)((d >> (16 * (hw & 1))) & 0xffffu);
+}
+
+template <bool I8, int RB, int MT>
+__device__ __forceinline__ void w8_compute(const W8Ops<RB, MT>& o, int g, v4f (&acc)[RB][MT]) {
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const v4i a0 = widen8<I8>(o.cw[rb][0], o.cw[rb][1]);
+    const v4i a1 = widen8<I8>(o.cw[rb][2], o.cw[rb][3]);
+    const int i0 = meta_half(o.mw[rb], g), i1 = meta_half(o.mw[rb], g + 4);
+#pragma unroll
+    for (int j = 0; j < MT; ++j) {
+      const v8i b0 = {o.bx[j][0][0], o.bx[j][0][1], o.bx[j][0][2], o.bx[j][0][3],
+                      o.bx[j][1][0], o.bx[j][1][1], o.bx[j][1][2], o.bx[j][1][3]};
+      const v8i b1 = {o.bx[j][2][0], o.bx[j][2][1], o.bx[j][2][2], o.bx[j][2][3],
+                      o.bx[j][3][0], o.bx[j][3][1], o.bx[j][3][2], o.bx[j][3][3]};
+      v4f p = {0.f, 0.f, 0.f, 0.f};
+      p = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(v8bf, a0), __builtin_bit_cast(v16bf, b0), p,
+                                                    i0, 0, 0);
+      p = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(v8bf, a1), __builtin_bit_cast(v16bf, b1), p,
+                                                    i1, 0, 0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[rb][j][e] = fmaf(p[e], o.sw4[rb][e], acc[rb][j][e]);
+    }
+  }
+}
+#endif  // SG_DEVICE_PASS
+
+template <bool I8, int RB, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
+__global__ void __launch_bounds__(512) k_gemm_w8a16(W8Args a) {
+  constexpr int U = W8_U;
+  __shared__ __attribute__((aligned(16))) float red[W8_WAVES][RB * MT][64][4];
+#if SG_DEVICE_PASS
+  const int t = threadIdx.x, l = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int g = l >> 4, lr = l & 15;
+  const int KB = (int)(a.K >> 7);
+  const int64_t n0 = (int64_t)blockIdx.x * (16 * RB);
+  const int64_t m0 = (int64_t)blockIdx.y * (16 * MT);
+  const int64_t wrows = min((int64_t)(16 * RB), a.N - n0), xrows = min((int64_t)(16 * MT), a.M - m0);
+  // rows past N or M read as zero
+  const __amdgpu_buffer_rsrc_t rw = w8_rsrc(a.w + n0 * a.ldw, (uint32_t)(wrows * a.ldw));
+  const __amdgpu_buffer_rsrc_t rm = w8_rsrc(a.meta + n0 * a.ldm, (uint32_t)(wrows * a.ldm));
+  const __amdgpu_buffer_rsrc_t rx = w8_rsrc(a.x + m0 * a.ldx, (uint32_t)(xrows * a.ldx * 2));
+
+  v4f acc[RB][MT];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int j = 0; j < MT; ++j) acc[rb][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+  // wave w multiplies K blocks w, w + 8, ...; U of them loaded before they are multiplied
+  const int nt = (KB - wave + W8_WAVES - 1) / W8_WAVES;
+  W8Ops<RB, MT> ops[U];
+  for (int t0 = 0; t0 < nt; t0 += U) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      w8_load<RB, MT, GRAN_N>(a, rw, rm, rx, n0, wave + W8_WAVES * min(t0 + u, nt - 1), lr, g, ops[u]);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (t0 + u < nt) w8_compute<I8, RB, MT>(ops[u], g, acc);
+  }
+
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int j = 0; j < MT; ++j)
+      *reinterpret_cast<float4*>(&red[wave][rb * MT + j][l][0]) =
+          make_float4(acc[rb][j][0], acc[rb][j][1], acc[rb][j][2], acc[rb][j][3]);
+  __syncthreads();
+  for (int q = t; q < RB * MT * 64; q += 512) {
+    const int s = q >> 6, ll = q & 63, rb = s / MT, j = s % MT;
+    float4 v4 = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int w = 0; w < W8_WAVES; ++w) {
+      const float4 v = *reinterpret_cast<const float4*>(&red[w][s][ll][0]);
+      v4.x += v.x; v4.y += v.y; v4.z += v.z; v4.w += v.w;
+    }
+    const int64_t n = n0 + 16 * rb + 4 * (ll >> 4);
+    v4f out = {v4.x, v4.y, v4.z, v4.w};
+    if (a.bias) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) out[e] += a.bias[min(n + e, a.N - 1)];
+    }
+    store_quad<OUT_BF16, OUT_T>(a, m0 + (int64_t)j * 16 + (ll & 15), n, out);
+  }
+#endif  // SG_DEVICE_PASS
+}
+
+// Row blocks per workgroup: the largest of 4 (2 for MT > 2), 2, 1 that keeps
+// at least 224 workgroups.  Every workgroup reads its X rows in full, so
+// fewer, taller workgroups read X fewer times (measured at M = 37 and 64:
+// 1.7x faster than one row block per workgroup).
+template <bool I8, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
+static void launch_w8_mt(const W8Args& a, hipStream_t st) {
+  const int64_t rows16 = cdiv(a.N, 16);
+  const unsigned gy = (unsigned)cdiv(a.M, 16 * MT);
+  constexpr int RB4 = MT <= 2 ? 4 : 2, RB2 = 2;
+  if (RB4 == 4 && rows16 * gy >= 4 * 224)
+    k_gemm_w8a16<I8, RB4, MT, GRAN_N, OUT_BF16, OUT_T><<<dim3((unsigned)cdiv(rows16, RB4), gy), 512, 0, st>>>(a);
+  else if (RB2 == 2 && rows16 * gy >= 2 * 224)
+    k_gemm_w8a16<I8, RB2, MT, GRAN_N, OUT_BF16, OUT_T><<<dim3((unsigned)cdiv(rows16, RB2), gy), 512, 0, st>>>(a);
+  else
+    k_gemm_w8a16<I8, 1, MT, GRAN_N, OUT_BF16, OUT_T><<<dim3((unsigned)rows16, gy), 512, 0, st>>>(a);
+}
+
+template <bool I8, int GRAN_N, bool OUT_BF16, bool OUT_T>
+static void launch_w8_shape(const W8Args& a, hipStream_t st) {
+  if (a.M <= 16) launch_w8_mt<I8, 1, GRAN_N, OUT_BF16, OUT_T>(a, st);
+  else if (a.M <= 32) launch_w8_mt<I8, 2, GRAN_N, OUT_BF16, OUT_T>(a, st);
+  else if (a.M <= 48) launch_w8_mt<I8, 3, GRAN_N, OUT_BF16, OUT_T>(a, st);
+  else launch_w8_mt<I8, 4, GRAN_N, OUT_BF16, OUT_T>(a, st);
+}
+
+template <bool I8, int GRAN_N>
+static void launch_w8_form(const W8Args& a, bool bf16, bool yt, hipStream_t st) {
+  if (bf16) {
+    if (yt) launch_w8_shape<I8, GRAN_N, true, true>(a, st);
+    else launch_w8_shape<I8, GRAN_N, true, false>(a, st);
+  } else {
+    if (yt) launch_w8_shape<I8, GRAN_N, false, true>(a, st);
+    else launch_w8_shape<I8, GRAN_N, false, false>(a, st);
+  }
+}
+
+}  // namespace sg
+
+using namespace sg;
+
+extern "C" sg_status sg_w8a16_sparse24_gemm_groupwise(int64_t M, int64_t N, int64_t K, const uint16_t* x,
+                                                      int64_t ldx, const uint8_t* wv, int64_t ldwv,
+                                                      const uint8_t* wmeta, int64_t ldwm, sg_dtype w_dt,
+                                                      const float* sw, int64_t sw_sn, int64_t sw_sk, int gran_n,
+                                                      const float* bias, void* y, sg_dtype y_dt, int64_t ldy,
+                                                      sg_form form, hipStream_t stream) {
+  if (!x || !wv || !wmeta || !sw || !y) return SG_ERR_NULL;
+  if (w_dt != SG_E4M3 && w_dt != SG_I8) return SG_ERR_UNSUPPORTED;
+  if (gran_n != 1 && gran_n != 128) return SG_ERR_UNSUPPORTED;
+  if (y_dt != SG_F32 && y_dt != SG_BF16) return SG_ERR_UNSUPPORTED;
+  if (form != SG_OUT_Y && form != SG_OUT_YT) return SG_ERR_UNSUPPORTED;
+  if (M < 0 || N < 0 || K <= 0 || K % 128 != 0 || ldx < K || ldwv < K / 2 || ldwm < K / 8) return SG_ERR_SHAPE;
+  if (ldy < (form == SG_OUT_Y ? N : M)) return SG_ERR_SHAPE;
+  // 32-bit buffer offsets: 64 rows of each operand per workgroup
+  if (ldx >= (1LL << 24) || ldwv >= (1LL << 24) || ldwm >= (1LL << 24) || sw_sn < 0 || sw_sk < 0) return SG_ERR_SHAPE;
+  if (((cdiv(N, gran_n) - 1) * sw_sn + (K / 128 - 1) * sw_sk) * 4 >= (1LL << 31)) return SG_ERR_SHAPE;
+  if (cdiv(N, 16) > 0x7fffffffLL || cdiv(M, 16) > 65535) return SG_ERR_SHAPE;
+  if (!aligned(x, 16) || (ldx * 2) % 16 || !aligned(wv, 16) || ldwv % 16 || !aligned(wmeta, 16) || ldwm % 16 ||
+      !aligned(sw, 4) || !aligned(bias, 4) || !aligned(y, dtype_size(y_dt)))
+    return SG_ERR_ALIGN;
+  if (M == 0 || N == 0) return SG_OK;
+  W8Args a;
+  a.M = M; a.N = N; a.K = K;
+  a.x = x; a.ldx = ldx;
+  a.w = wv; a.ldw = ldwv; a.meta = wmeta; a.ldm = ldwm;
+  a.sw = sw; a.sw_sn = sw_sn; a.sw_sk = sw_sk; a.gn_shift = gran_n == 128 ? 7 : 0;
+  a.bias = bias;
+  a.y = y; a.ldy = ldy;
+  a.vec_store = (ldy % 4 == 0) && aligned(y, 4 * dtype_size(y_dt));
+  clear_hip_error();
+  const bool bf16 = y_dt == SG_BF16, yt = form == SG_OUT_YT;
+  if (w_dt == SG_I8) {
+    if (gran_n == 128) launch_w8_form<true, 128>(a, bf16, yt, stream);
+    else launch_w8_form<true, 1>(a, bf16, yt, stream);
+  } else {
+    if (gran_n == 128) launch_w8_form<false, 128>(a, bf16, yt, stream);
+    else launch_w8_form<false, 1>(a, bf16, yt, stream);
+  }
+  return launch_status();
+}

@@ -43,7 +43,8 @@ def test_header_declares_the_entry_points():
         "sg_fp8_sparse24_gemm_groupwise_packed", "sg_probe_matrix_ops", "sg_probe_matrix_rate",
         "sg_int8_quant_groupwise", "sg_int8_sparse24_gemm_groupwise", "sg_int8_sparse24_gemm_groupwise_packed",
         "sg_fp8_gemm_groupwise_batched", "sg_fp8_sparse24_gemm_groupwise_batched",
-        "sg_fp8_sparse24_gemm_groupwise_packed_batched", "sg_fp8_sparse24_gemm_groupwise_packed_grouped"])
+        "sg_fp8_sparse24_gemm_groupwise_packed_batched", "sg_fp8_sparse24_gemm_groupwise_packed_grouped",
+        "sg_w8a16_sparse24_gemm_groupwise"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -336,3 +337,25 @@ def grouped(sizes, **kw):
 ])
 def test_grouped_gemm_validation(sizes, kw, code):
     assert grouped(sizes, **kw) == code
+
+
+def w8a16(**kw):
+    a = dict(M=16, N=256, K=256, x=P, ldx=256, w=P2, ldw=128, meta=P3, ldm=32, wdt=2, sw=P3, swn=2, swk=1, gn=128,
+             bias=None, y=P, ydt=1, ldy=256, form=0)
+    a.update(kw)
+    return sg.lib().sg_w8a16_sparse24_gemm_groupwise(a["M"], a["N"], a["K"], a["x"], a["ldx"], a["w"], a["ldw"],
+                                                     a["meta"], a["ldm"], a["wdt"], a["sw"], a["swn"], a["swk"], a["gn"],
+                                                     a["bias"], a["y"], a["ydt"], a["ldy"], a["form"], None)
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), NULL), (dict(w=None), NULL), (dict(meta=None), NULL), (dict(sw=None), NULL), (dict(y=None), NULL),
+    (dict(wdt=0), UNSUP), (dict(wdt=1), UNSUP), (dict(gn=64), UNSUP), (dict(ydt=2), UNSUP), (dict(form=3), UNSUP),
+    (dict(K=200), SHAPE), (dict(ldx=128), SHAPE), (dict(ldw=64), SHAPE), (dict(ldm=16), SHAPE), (dict(ldy=100), SHAPE),
+    (dict(M=65535 * 16 + 1), SHAPE), (dict(swk=-1), SHAPE),
+    (dict(x=ODD), ALIGN), (dict(ldx=260), ALIGN), (dict(ldw=136), ALIGN), (dict(ldm=34), ALIGN), (dict(ldm=36), ALIGN),
+    (dict(bias=ctypes.c_void_p(0x100002)), ALIGN), (dict(M=0), OK), (dict(N=0), OK), (dict(wdt=3, M=0), OK),
+])
+def test_w8a16_validation(kw, code):
+    assert w8a16(**kw) == code

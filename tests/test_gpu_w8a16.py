@@ -1,0 +1,91 @@
+"""GPU parity of the weight-only 2:4 GEMM (bf16 activations x e4m3 / int8 2:4
+codes, groupwise weight scales) against the oracle: random codes over each
+code type's whole finite range, ragged shapes, both scale granularities, both
+output forms, fp32 and bf16 outputs, bias, and the M=16 decode shape."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_gemm_layers_amd as sg
+import workloads
+from gpu_helpers import DEV, assert_within_tolerance, down, say, up
+
+pytestmark = pytest.mark.gpu
+
+
+def operands(m, n, k, gn, int8, seed):
+    rng = np.random.default_rng(seed)
+    x = torch.from_numpy(workloads.sparse_large(seed=seed, m=m, n=8, k=k)["x"]).to(DEV).to(torch.bfloat16)
+    keep, _ = oracle.prune24(rng.standard_normal((n, k)).astype(np.float32))
+    if int8:
+        c = rng.integers(-127, 128, size=(n, k)).astype(np.int8)
+    else:
+        c = rng.integers(0, 256, size=(n, k)).astype(np.uint8)
+        c[(c & 0x7F) == 0x7F] ^= 1                              # every finite e4m3 code, no NaN
+    wv, meta = oracle.compress24(c, keep)
+    sw = (rng.uniform(0.5, 2.0, size=(-(-n // gn), k // 128)) * 2.0 ** -6).astype(np.float32)
+    return x, wv, meta, sw
+
+
+def check(m, n, k, gn=128, int8=False, out=torch.bfloat16, forms=("y", "yt"), bias=False, seed=0):
+    say(f"w8a16 M={m} N={n} K={k} gn={gn} int8={int8} {out} bias={bias} seed={seed}")
+    x, wv, meta, sw = operands(m, n, k, gn, int8, seed)
+    xbits = x.view(torch.int16).cpu().numpy().view(np.uint16)
+    ref, bound = oracle.w8a16_sparse24_gemm_groupwise(xbits, wv, meta, sw, gn, "int8" if int8 else "e4m3", bound=True)
+    b = None
+    if bias:
+        bnp = np.random.default_rng(seed + 1).standard_normal(n).astype(np.float32)
+        ref, bound = oracle.add_bias(ref, bound, bnp)
+        b = up(bnp)
+    outs = {}
+    for form in forms:
+        y = sg.w8a16_sparse24_gemm_groupwise(x, up(wv), up(meta), up(sw), gn, out_dtype=out, form=form, bias=b)
+        got = down(y)
+        got = got.T if form == "yt" else got
+        assert got.shape == (m, n)
+        assert_within_tolerance(got.astype(np.float64), ref, bound, f"form={form}")
+        outs[form] = got
+    if len(outs) == 2:
+        assert np.array_equal(outs["y"], outs["yt"])
+
+
+SHAPES = [(1, 256, 128), (16, 512, 256), (17, 300, 384), (37, 1000, 512), (64, 260, 256), (65, 256, 256),
+          (200, 384, 640)]
+
+
+@pytest.mark.parametrize("int8", [False, True])
+@pytest.mark.parametrize("m,n,k", SHAPES)
+def test_w8a16_ragged(m, n, k, int8):
+    check(m, n, k, int8=int8, seed=m + n + k + int8)
+
+
+@pytest.mark.parametrize("int8", [False, True])
+@pytest.mark.parametrize("gn", [1, 128])
+def test_w8a16_scales_fp32_bias(gn, int8):
+    check(37, 300, 384, gn=gn, int8=int8, out=torch.float32, bias=True, seed=7 + gn)
+
+
+@pytest.mark.parametrize("int8", [False, True])
+def test_w8a16_decode_full_size(int8):
+    """M = 16, N = 14336, K = 4096 (the benchmark's shape), every output."""
+    check(16, 14336, 4096, int8=int8, forms=("y",), seed=21 + int8)
+
+
+def test_w8a16_from_the_gpu_weight_pipeline():
+    """GPU prune + compress + int8 / e4m3 quantisation of a weight, then the
+    weight-only GEMM, against the oracle's chain."""
+    m, n, k = 16, 512, 1024
+    say(f"w8a16 pipeline M={m} N={n} K={k}")
+    d = workloads.sparse_large(seed=30, m=m, n=n, k=k)
+    x = up(d["x"]).to(torch.bfloat16)
+    xbits = x.view(torch.int16).cpu().numpy().view(np.uint16)
+    v32, meta = sg.sparse24_prune_compress(up(d["w"]))
+    ov32, ometa = oracle.prune_compress24(d["w"])
+    for int8 in (False, True):
+        q, s = (sg.int8_quant_groupwise if int8 else sg.fp8_quant_groupwise)(v32, gr=128, gc=64)
+        oq, os_ = (oracle.int8_quant_groupwise if int8 else oracle.fp8_quant_groupwise)(ov32, 128, 64)
+        got = down(sg.w8a16_sparse24_gemm_groupwise(x, q, meta, s, 128))
+        ref, bound = oracle.w8a16_sparse24_gemm_groupwise(xbits, oq, ometa, os_, 128, "int8" if int8 else "e4m3",
+                                                          bound=True)
+        assert_within_tolerance(got, ref, bound, f"int8={int8}")
