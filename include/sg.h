@@ -63,7 +63,8 @@ typedef enum { SG_OUT_Y = 0, SG_OUT_YT = 1 } sg_form;
 /* Human-readable name of a status code (static string, never NULL). */
 const char* sg_status_str(sg_status s);
 
-/* Version of this ABI; bumped on any incompatible change. */
+/* Version of this ABI; bumped on any incompatible change (2: the int4
+ * quantiser takes its group width). */
 int sg_abi_version(void);
 
 /*
@@ -96,18 +97,21 @@ sg_status sg_fp8_quant_groupwise(const void* x, sg_dtype x_dt, int64_t rows, int
 
 /*
  * sg_int4_quant_groupwise -- symmetric int4 codes with one fp32 scale per
- * (row, 128-column group), the input format of sg_mixed_gemm_add ([I2058]
- * hyx1999: X1 and W1 are quantised to 4 bit; the page fixes no scheme).
+ * (row, gc-column group), the input format of sg_mixed_gemm_add (gc = 128;
+ * [I2058] hyx1999: X1 and W1 are quantised to 4 bit; the page fixes no
+ * scheme) and, over 2:4-compressed values (gc = 64 = one 128-wide K block),
+ * of sg_w4a16_sparse24_gemm_groupwise.
  *   s = amax / 7 in fp32 (1 if amax == 0);  q = clamp(rint(x / s), -7, 7),
  *   rint = round half to even, IEEE fp32 divide.
  *   Packed two's-complement nibbles: element 2j in the low nibble of byte j.
  *   x : [rows, cols] (SG_F32 or SG_BF16), ld ldx.  q: [rows, cols/2] bytes, ld ldq.
- *   s : (r, cb) at s[r * s_stride_r + cb * s_stride_c], cb < cols / 128.
- * Requires cols % 128 == 0; x 16-byte aligned, ldx * sizeof(x_dt) % 16 == 0;
+ *   gc: 128 or 64.
+ *   s : (r, cb) at s[r * s_stride_r + cb * s_stride_c], cb < cols / gc.
+ * Requires cols % gc == 0; x 16-byte aligned, ldx * sizeof(x_dt) % 16 == 0;
  * q 4-byte aligned, ldq % 4 == 0, ldq >= cols / 2.
  */
 sg_status sg_int4_quant_groupwise(const void* x, sg_dtype x_dt, int64_t rows, int64_t cols,
-                                  int64_t ldx, uint8_t* q, int64_t ldq, float* s,
+                                  int64_t ldx, int gc, uint8_t* q, int64_t ldq, float* s,
                                   int64_t s_stride_r, int64_t s_stride_c, hipStream_t stream);
 
 /*

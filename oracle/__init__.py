@@ -42,6 +42,7 @@ from .gemm import (
     int8_sparse24_gemm_rowwise,
     add_bias,
     w8a16_sparse24_gemm_groupwise,
+    w4a16_sparse24_gemm_groupwise,
     mixed_gemm_add,
     within_tolerance,
 )
@@ -53,5 +54,6 @@ __all__ = [
     "pack24_gfx950", "unpack24_gfx950", "packed_bytes",
     "expand_scales", "fp8_gemm_groupwise", "fp8_sparse24_gemm_groupwise",
     "int8_gemm_groupwise", "int8_sparse24_gemm_groupwise", "fp8_gemm_rowwise",
-    "fp8_sparse24_gemm_rowwise", "int8_sparse24_gemm_rowwise", "add_bias", "w8a16_sparse24_gemm_groupwise", "mixed_gemm_add", "within_tolerance",
+    "fp8_sparse24_gemm_rowwise", "int8_sparse24_gemm_rowwise", "add_bias", "w8a16_sparse24_gemm_groupwise",
+    "w4a16_sparse24_gemm_groupwise", "mixed_gemm_add", "within_tolerance",
 ]

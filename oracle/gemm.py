@@ -58,6 +58,10 @@ have no mixed-dtype kernel to run on; this is that operation:
 Every product is exact in fp64 (8 x 8 significant bits); the K-block sums are
 exact up to fp64 rounding (relative 2^-53 of the block's abs-sum).
 
+W4A16 is the same with 4-bit codes: the 2:4-compressed values quantised to
+int4 (one scale per row and 128-wide K block, i.e. per 64 compressed values),
+packed two per byte, element 2j in the low nibble of byte j.
+
 Bias epilogue: the sparse FP8 linear implementation torchao PR #3258's review
 points to takes a bias argument; a linear layer adds it to every row of the
 output, y[m, n] + bias[n], after the scales.  In the tolerance the bias is one
@@ -201,6 +205,13 @@ def w8a16_sparse24_gemm_groupwise(x_bits, wv, wmeta, sw, gn: int, codes: str = "
     if not bound:
         return y
     return y, _scaled_kblock_sum(xd, ones, wd, swe, absolute=True)
+
+
+def w4a16_sparse24_gemm_groupwise(x_bits, wv4, wmeta, sw, bound: bool = False):
+    """x_bits bf16 bits [M, K]; wv4 packed int4 [N, K/4] (the 2:4-compressed
+    values, two per byte); wmeta [N, K/8]; sw fp32 [N, K/128] (one per row and K block)."""
+    codes = int4_decode(wv4).astype(np.int8)                       # [N, K/2]
+    return w8a16_sparse24_gemm_groupwise(x_bits, codes, wmeta, sw, 1, "int8", bound=bound)
 
 
 def add_bias(y, bound, bias):

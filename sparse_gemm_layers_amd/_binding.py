@@ -25,7 +25,7 @@ _SIGS = {
     "sg_status_str": ([_int], ctypes.c_char_p),
     "sg_abi_version": ([], _int),
     "sg_fp8_quant_groupwise": ([_ptr, _int, _i64, _i64, _i64, _int, _int, _ptr, _i64, _ptr, _i64, _i64, _ptr], _int),
-    "sg_int4_quant_groupwise": ([_ptr, _int, _i64, _i64, _i64, _ptr, _i64, _ptr, _i64, _i64, _ptr], _int),
+    "sg_int4_quant_groupwise": ([_ptr, _int, _i64, _i64, _i64, _int, _ptr, _i64, _ptr, _i64, _i64, _ptr], _int),
     "sg_sparse24_prune_compress": ([_ptr, _int, _i64, _i64, _i64, _ptr, _i64, _ptr, _i64, _ptr], _int),
     "sg_fp8_gemm_groupwise": ([_i64, _i64, _i64, _ptr, _i64, _ptr, _i64, _i64, _int, _ptr, _i64, _ptr, _i64, _i64,
                                _int, _ptr, _int, _i64, _int, _ptr], _int),
@@ -152,16 +152,16 @@ def int8_quant_groupwise(x, gr: int = 1, gc: int = 128, q=None, s=None):
     return q, s
 
 
-def int4_quant_groupwise(x, q=None, s=None):
-    """x [rows, cols] -> (packed int4 uint8 [rows, cols/2], scales fp32 [rows, cols/128])."""
+def int4_quant_groupwise(x, gc: int = 128, q=None, s=None):
+    """x [rows, cols] -> (packed int4 uint8 [rows, cols/2], scales fp32 [rows, cols/gc]); gc 128 or 64."""
     _gpu2d(x, "x")
     rows, cols = x.shape
     if q is None:
         q = torch.empty((rows, cols // 2), dtype=torch.uint8, device=x.device)
     if s is None:
-        s = _scales(rows, cols // 128, x.device)
+        s = _scales(rows, cols // gc, x.device)
     _gpu2d(q, "q")
-    st = lib().sg_int4_quant_groupwise(_p(x), _dtype_code(x, "x"), rows, cols, _row_stride(x), _p(q),
+    st = lib().sg_int4_quant_groupwise(_p(x), _dtype_code(x, "x"), rows, cols, _row_stride(x), gc, _p(q),
                                        _row_stride(q), _p(s), s.stride(0), s.stride(1), _stream(x))
     _check(st, "sg_int4_quant_groupwise")
     return q, s

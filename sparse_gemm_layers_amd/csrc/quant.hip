@@ -327,24 +327,34 @@ extern "C" sg_status sg_int8_quant_groupwise(const void* x, sg_dtype x_dt, int64
 }
 
 extern "C" sg_status sg_int4_quant_groupwise(const void* x, sg_dtype x_dt, int64_t rows,
-                                             int64_t cols, int64_t ldx, uint8_t* q, int64_t ldq,
+                                             int64_t cols, int64_t ldx, int gc, uint8_t* q, int64_t ldq,
                                              float* s, int64_t s_stride_r, int64_t s_stride_c,
                                              hipStream_t stream) {
   if (!x || !q || !s) return SG_ERR_NULL;
   if (x_dt != SG_F32 && x_dt != SG_BF16) return SG_ERR_UNSUPPORTED;
-  if (rows < 0 || cols <= 0 || cols % 128 != 0 || ldx < cols || ldq < cols / 2) return SG_ERR_SHAPE;
+  if (gc != 128 && gc != 64) return SG_ERR_UNSUPPORTED;
+  if (rows < 0 || cols <= 0 || cols % gc != 0 || ldx < cols || ldq < cols / 2) return SG_ERR_SHAPE;
   if (!aligned(x, 16) || !aligned(q, 4) || !aligned(s, 4) || (ldx * (int64_t)dtype_size(x_dt)) % 16 ||
       ldq % 4)
     return SG_ERR_ALIGN;
   if (rows == 0) return SG_OK;
   clear_hip_error();
-  const int64_t blocks = rows * (cols / 128);
-  const unsigned g = grid_for(blocks, 8);
-  if (x_dt == SG_F32)
-    k_quant_int4<float, 128><<<g, 256, 0, stream>>>((const float*)x, rows, cols, ldx, q, ldq, s,
-                                                             s_stride_r, s_stride_c);
-  else
-    k_quant_int4<uint16_t, 128><<<g, 256, 0, stream>>>((const uint16_t*)x, rows, cols, ldx, q,
-                                                                ldq, s, s_stride_r, s_stride_c);
+  const int64_t blocks = rows * (cols / gc);
+  const unsigned g = grid_for(blocks, 4 * (64 / (gc / 4)));
+  if (x_dt == SG_F32) {
+    if (gc == 128)
+      k_quant_int4<float, 128><<<g, 256, 0, stream>>>((const float*)x, rows, cols, ldx, q, ldq, s, s_stride_r,
+                                                       s_stride_c);
+    else
+      k_quant_int4<float, 64><<<g, 256, 0, stream>>>((const float*)x, rows, cols, ldx, q, ldq, s, s_stride_r,
+                                                      s_stride_c);
+  } else {
+    if (gc == 128)
+      k_quant_int4<uint16_t, 128><<<g, 256, 0, stream>>>((const uint16_t*)x, rows, cols, ldx, q, ldq, s,
+                                                          s_stride_r, s_stride_c);
+    else
+      k_quant_int4<uint16_t, 64><<<g, 256, 0, stream>>>((const uint16_t*)x, rows, cols, ldx, q, ldq, s,
+                                                         s_stride_r, s_stride_c);
+  }
   return launch_status();
 }

@@ -56,7 +56,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     lib = sg.lib()
-    assert lib.sg_abi_version() == 1
+    assert lib.sg_abi_version() == 2
     for code, word in [(OK, b"SG_OK"), (NULL, b"SG_ERR_NULL"), (SHAPE, b"SG_ERR_SHAPE"),
                        (UNSUP, b"SG_ERR_UNSUPPORTED"), (ALIGN, b"SG_ERR_ALIGN"), (HIP, b"SG_ERR_HIP")]:
         assert lib.sg_status_str(code).startswith(word)
@@ -99,16 +99,18 @@ def test_int8_quant_validation(kw, code):
 
 
 def int4q(**kw):
-    a = dict(x=P, dt=1, rows=4, cols=256, ldx=256, q=P2, ldq=128, s=P3, ssr=2, ssc=1)
+    a = dict(x=P, dt=1, rows=4, cols=256, ldx=256, gc=128, q=P2, ldq=128, s=P3, ssr=2, ssc=1)
     a.update(kw)
-    return sg.lib().sg_int4_quant_groupwise(a["x"], a["dt"], a["rows"], a["cols"], a["ldx"], a["q"], a["ldq"],
-                                            a["s"], a["ssr"], a["ssc"], None)
+    return sg.lib().sg_int4_quant_groupwise(a["x"], a["dt"], a["rows"], a["cols"], a["ldx"], a["gc"], a["q"],
+                                            a["ldq"], a["s"], a["ssr"], a["ssc"], None)
 
 
 @no_gpu
 @pytest.mark.parametrize("kw,code", [
     (dict(q=None), NULL), (dict(dt=2), UNSUP), (dict(cols=64), SHAPE), (dict(ldq=64), SHAPE),
     (dict(ldq=130), ALIGN), (dict(x=ODD), ALIGN), (dict(rows=0), OK),
+    (dict(gc=32), UNSUP), (dict(gc=64, cols=200, ldx=208, ldq=104), SHAPE),
+    (dict(gc=64, cols=320, ldx=320, ldq=160, rows=0), OK),
 ])
 def test_int4_quant_validation(kw, code):
     assert int4q(**kw) == code

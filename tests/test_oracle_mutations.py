@@ -249,3 +249,13 @@ def test_w8a16_int8_read_unsigned_is_caught(monkeypatch):
         return orig(x_bits, wv, wmeta, sw, gn, codes, bound)
     monkeypatch.setattr(oracle, "w8a16_sparse24_gemm_groupwise", gemm)
     _fails(t_w8.test_w8a16_integer_activations_int8_codes_unit_scales)
+
+
+def test_w4a16_nibbles_swapped_is_caught(monkeypatch):
+    def w4(x_bits, wv4, wmeta, sw, bound=False):
+        b = np.asarray(wv4, np.uint8)
+        swapped = ((b >> 4) | (b << 4)).astype(np.uint8)
+        codes = oracle.int4_decode(swapped).astype(np.int8)
+        return oracle.w8a16_sparse24_gemm_groupwise(x_bits, codes, wmeta, sw, 1, "int8", bound=bound)
+    monkeypatch.setattr(oracle, "w4a16_sparse24_gemm_groupwise", w4)
+    _fails(t_w8.test_w4a16_matches_exact_rationals)

@@ -73,3 +73,29 @@ def test_w8a16_equals_fp8_gemm_on_e4m3_activations():
     ones = np.ones((7, 512 // 128), np.float32)
     yf, tf = oracle.fp8_sparse24_gemm_groupwise(xq, ones, 1, wq, meta, sw, 128, bound=True)
     assert np.array_equal(y, yf) and np.array_equal(t, tf)
+
+
+def test_w4a16_matches_exact_rationals():
+    """The int4 path from its packed bytes: nibble order, sign, decompression
+    and per-row scales against exact rationals written out here."""
+    rng = np.random.default_rng(31)
+    m, n, k = 2, 3, 256
+    x = bf16_bits(rng.standard_normal((m, k)))
+    q = rng.integers(-7, 8, size=(n, k))
+    keep, _ = oracle.prune24(rng.standard_normal((n, k)).astype(np.float32))
+    qv, meta = oracle.compress24(q.astype(np.int8), keep)             # [n, k/2] values
+    nib = (qv.astype(np.int64) & 0xF).astype(np.uint8)
+    packed = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)   # element 2j low nibble
+    sw = (rng.uniform(0.5, 2, size=(n, k // 128)) * 2.0 ** -3).astype(np.float32)
+    y = oracle.w4a16_sparse24_gemm_groupwise(x, packed, meta, sw)
+    xd = oracle.bf16_decode(x)
+    qd = np.where(keep, q, 0)
+    for i in range(m):
+        for j in range(n):
+            exact = Fraction(0)
+            for kb in range(k // 128):
+                part = sum(Fraction(float(xd[i, kk])) * int(qd[j, kk]) for kk in range(kb * 128, kb * 128 + 128))
+                exact += Fraction(float(sw[j, kb])) * part
+            absum = sum(Fraction(float(sw[j, kk // 128])) * abs(Fraction(float(xd[i, kk]))) * abs(int(qd[j, kk]))
+                        for kk in range(k))
+            assert abs(Fraction(float(y[i, j])) - exact) <= absum * Fraction(1, 2 ** 46)
