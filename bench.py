@@ -285,6 +285,24 @@ def rows_report():
             out[f"next_w8a16_{codes}_decode_M{dm}_N{dn}_K{dk}_y"] = {"ms": ms, "GB/s": b / ms / 1e6,
                                                                    "frac_hbm": b / ms / 1e6 / PEAK_HBM_GBS}
         del wsets
+    wsets = []
+    for i in range(ROTATE_DECODE):
+        g = torch.Generator(device=DEV)
+        g.manual_seed(6000 + i)
+        v, mt = sg.sparse24_prune_compress(torch.randn((dn, dk), generator=g, device=DEV) * 0.02)
+        q4, s4 = sg.int4_quant_groupwise(v, gc=64)
+        wsets.append((q4, mt, s4))
+        del v
+    for dm in (16, 37):
+        xb = torch.from_numpy(workloads.decode(seed=4, m=dm, n=8, k=dk)["x"]).to(DEV).to(torch.bfloat16)
+        y = torch.empty((dm, dn), dtype=torch.bfloat16, device=DEV)
+        ms = time_fn(lambda i: sg.w4a16_sparse24_gemm_groupwise(
+            xb, wsets[i % ROTATE_DECODE][0], wsets[i % ROTATE_DECODE][1], wsets[i % ROTATE_DECODE][2], y=y),
+            reps=64, warm=16)
+        b = dn * dk // 4 + dn * dk // 8 + 4 * dn * (dk // 128) + dm * dk * 2 + dm * dn * 2
+        out[f"next_w4a16_decode_M{dm}_N{dn}_K{dk}_y"] = {"ms": ms, "GB/s": b / ms / 1e6,
+                                                        "frac_hbm": b / ms / 1e6 / PEAK_HBM_GBS}
+    del wsets
     xb = x.to(torch.bfloat16)
     wv8, mt8 = sg.sparse24_prune_compress(torch.from_numpy(workloads.sparse_large(seed=3, m=8, n=n, k=k)["w"]).to(DEV))
     wq8, sw8 = sg.fp8_quant_groupwise(wv8, gr=128, gc=64)

@@ -369,6 +369,19 @@ sg_status sg_w8a16_sparse24_gemm_groupwise(int64_t M, int64_t N, int64_t K, cons
                                            hipStream_t stream);
 
 /*
+ * sg_w4a16_sparse24_gemm_groupwise -- the same with int4 weight codes: the
+ * 2:4-compressed values quantised by sg_int4_quant_groupwise with gc = 64 (one
+ * scale per row and 128-wide K block), two per byte.
+ *   wv4 : [N, K/4] packed int4, element 2j in the low nibble of byte j; ld ldwv4 (bytes).
+ *   sw  : (n, kb) at sw[n * sw_sn + kb * sw_sk].   Other arguments as the W8A16 GEMM.
+ * Requires ldwv4 >= K/4, wv4 16-byte aligned and ldwv4 a multiple of 16.
+ */
+sg_status sg_w4a16_sparse24_gemm_groupwise(int64_t M, int64_t N, int64_t K, const uint16_t* x, int64_t ldx,
+                                           const uint8_t* wv4, int64_t ldwv4, const uint8_t* wmeta, int64_t ldwm,
+                                           const float* sw, int64_t sw_sn, int64_t sw_sk, const float* bias,
+                                           void* y, sg_dtype y_dt, int64_t ldy, sg_form form, hipStream_t stream);
+
+/*
  * sg_fp8_sparse24_gemm_groupwise_packed_grouped -- G problems that share N and
  * K but not M (e.g. tokens routed to experts): group g multiplies rows
  * row_off[g] .. row_off[g] + m_sizes[g] - 1 of X (row_off = prefix sums of

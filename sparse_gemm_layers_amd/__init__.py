@@ -31,6 +31,7 @@ from ._binding import (
     fp8_sparse24_gemm_groupwise_packed_batched,
     fp8_sparse24_gemm_groupwise_packed_grouped,
     w8a16_sparse24_gemm_groupwise,
+    w4a16_sparse24_gemm_groupwise,
 )
 
 __all__ = [
@@ -41,5 +42,5 @@ __all__ = [
     "int8_sparse24_gemm_groupwise_packed", "probe_matrix_ops", "probe_matrix_rate", "k_constant_scales",
     "fp8_gemm_groupwise_batched", "fp8_sparse24_gemm_groupwise_batched",
     "fp8_sparse24_gemm_groupwise_packed_batched", "fp8_sparse24_gemm_groupwise_packed_grouped",
-    "w8a16_sparse24_gemm_groupwise",
+    "w8a16_sparse24_gemm_groupwise", "w4a16_sparse24_gemm_groupwise",
 ]

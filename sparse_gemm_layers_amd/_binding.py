@@ -56,6 +56,8 @@ _SIGS = {
                                                        _i64, _int, _ptr], _int),
     "sg_w8a16_sparse24_gemm_groupwise": ([_i64, _i64, _i64, _ptr, _i64, _ptr, _i64, _ptr, _i64, _int, _ptr, _i64,
                                           _i64, _int, _ptr, _ptr, _int, _i64, _int, _ptr], _int),
+    "sg_w4a16_sparse24_gemm_groupwise": ([_i64, _i64, _i64, _ptr, _i64, _ptr, _i64, _ptr, _i64, _ptr, _i64, _i64,
+                                          _ptr, _ptr, _int, _i64, _int, _ptr], _int),
     "sg_probe_matrix_ops": ([_int, _int], _i64),
     "sg_probe_matrix_rate": ([_int, _int, _ptr, _ptr, _ptr], _int),
 }
@@ -395,6 +397,27 @@ def w8a16_sparse24_gemm_groupwise(x, wv, wmeta, sw, gran_n: int = 128, out_dtype
                                                 _row_stride(wmeta), wdt, _p(sw), sw.stride(0), sw.stride(1), gran_n,
                                                 bp, _p(y), ydt, _row_stride(y), f, _stream(x))
     _check(st, "sg_w8a16_sparse24_gemm_groupwise")
+    return y
+
+
+def w4a16_sparse24_gemm_groupwise(x, wv4, wmeta, sw, out_dtype=torch.bfloat16, form: str = "y", y=None,
+                                   bias=None):
+    """Weight-only 2:4 GEMM with int4 codes: x bfloat16 [M, K]; wv4 uint8 [N, K/4]
+    (2:4-compressed values quantised with int4_quant_groupwise(gc=64)); wmeta
+    uint8 [N, K/8]; sw fp32 [N, K/128]."""
+    _gpu2d(x, "x")
+    _gpu2d(wv4, "wv4")
+    _gpu2d(wmeta, "wmeta")
+    if x.dtype != torch.bfloat16 or wv4.dtype != torch.uint8:
+        raise SgError("x must be bfloat16 and wv4 uint8")
+    M, K = x.shape
+    N = wv4.shape[0]
+    y, f, ydt = _out(y, M, N, out_dtype, form, x.device)
+    bp, _ = _bias(bias, N)
+    st = lib().sg_w4a16_sparse24_gemm_groupwise(M, N, K, _p(x), _row_stride(x), _p(wv4), _row_stride(wv4), _p(wmeta),
+                                                _row_stride(wmeta), _p(sw), sw.stride(0), sw.stride(1), bp, _p(y), ydt,
+                                                _row_stride(y), f, _stream(x))
+    _check(st, "sg_w4a16_sparse24_gemm_groupwise")
     return y
 
 

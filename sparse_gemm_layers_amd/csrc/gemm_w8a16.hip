@@ -1,5 +1,6 @@
-// Weight-only 2:4 GEMM (W8A16): Y = X . W^T with X in bf16 (unquantised) and
-// W as 2:4-compressed 8-bit codes (e4m3 or int8) with groupwise scales.
+// Weight-only 2:4 GEMMs (W8A16 and W4A16): Y = X . W^T with X in bf16
+// (unquantised) and W as 2:4-compressed 8-bit codes (e4m3 or int8) or int4
+// codes (two per byte) with groupwise scales.
 //
 // torchao PR #3258 "Introduce new W8A8-FP-CSR quantization API": jcaip's
 // review says weight-only sparsity configs for int8 and float8 have no
@@ -54,6 +55,7 @@ struct W8Args {
 };
 
 constexpr int W8_WAVES = 8, W8_U = 2;
+enum W8Codes { C_E4M3 = 0, C_I8 = 1, C_I4 = 2 };
 
 #if SG_DEVICE_PASS
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t w8_rsrc(const void* p, uint32_t bytes) {
@@ -87,11 +89,25 @@ __device__ __forceinline__ v2i w8_ld8(__amdgpu_buffer_rsrc_t r, uint32_t off, in
   return __builtin_bit_cast(v2i, __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, 0));
 }
 
-// bf16 A operand (8 values) of 8 consecutive code bytes (two dwords).
-template <bool I8>
+// bf16 A operand (8 values) of 8 consecutive codes: two dwords of bytes, or
+// (int4) the 8 nibbles of w0, element 2j in the low nibble of byte j.
+template <int CODES>
 __device__ __forceinline__ v4i widen8(int w0, int w1) {
-  return (v4i){(int)bf16_pair<I8, false>((uint32_t)w0), (int)bf16_pair<I8, true>((uint32_t)w0),
-               (int)bf16_pair<I8, false>((uint32_t)w1), (int)bf16_pair<I8, true>((uint32_t)w1)};
+  if constexpr (CODES == C_I4) {
+    uint32_t d[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      // the builtin's result type is unsigned: convert it as the signed value it holds
+      const float f0 = (float)(int)__builtin_amdgcn_sbfe(w0, 8 * q, 4);
+      const float f1 = (float)(int)__builtin_amdgcn_sbfe(w0, 8 * q + 4, 4);
+      d[q] = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xffff0000u);
+    }
+    return (v4i){(int)d[0], (int)d[1], (int)d[2], (int)d[3]};
+  } else {
+    constexpr bool I8 = CODES == C_I8;
+    return (v4i){(int)bf16_pair<I8, false>((uint32_t)w0), (int)bf16_pair<I8, true>((uint32_t)w0),
+                 (int)bf16_pair<I8, false>((uint32_t)w1), (int)bf16_pair<I8, true>((uint32_t)w1)};
+  }
 }
 
 template <int RB, int MT>
@@ -102,16 +118,22 @@ struct W8Ops {
   float sw4[RB][4];
 };
 
-template <int RB, int MT, int GRAN_N>
+template <int CODES, int RB, int MT, int GRAN_N>
 __device__ __forceinline__ void w8_load(const W8Args& a, __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t rm,
                                         __amdgpu_buffer_rsrc_t rx, int64_t n0, int kb, int lr, int g,
                                         W8Ops<RB, MT>& o) {
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const uint32_t r = (uint32_t)(16 * rb + lr);
-    const v2i c0 = w8_ld8(rw, r * (uint32_t)a.ldw + 8 * g, kb * 64);
-    const v2i c1 = w8_ld8(rw, r * (uint32_t)a.ldw + 32 + 8 * g, kb * 64);
-    o.cw[rb] = (v4i){c0[0], c0[1], c1[0], c1[1]};
+    if constexpr (CODES == C_I4) {   // 32 bytes per row and K block: 4 per lane and K slice
+      const int c0 = w8_ld4(rw, r * (uint32_t)a.ldw + 4 * g, kb * 32);
+      const int c1 = w8_ld4(rw, r * (uint32_t)a.ldw + 16 + 4 * g, kb * 32);
+      o.cw[rb] = (v4i){c0, 0, c1, 0};
+    } else {
+      const v2i c0 = w8_ld8(rw, r * (uint32_t)a.ldw + 8 * g, kb * 64);
+      const v2i c1 = w8_ld8(rw, r * (uint32_t)a.ldw + 32 + 8 * g, kb * 64);
+      o.cw[rb] = (v4i){c0[0], c0[1], c1[0], c1[1]};
+    }
     o.mw[rb] = w8_ld16(rm, r * (uint32_t)a.ldm, kb * 16);
     const int64_t nb = n0 + 16 * rb;   // rows past N read the last row's scale (never stored)
     if (GRAN_N == 128) {
@@ -136,12 +158,12 @@ __device__ __forceinline__ int meta_half(const v4i& m, int hw) {
   return (int)((d >> (16 * (hw & 1))) & 0xffffu);
 }
 
-template <bool I8, int RB, int MT>
+template <int CODES, int RB, int MT>
 __device__ __forceinline__ void w8_compute(const W8Ops<RB, MT>& o, int g, v4f (&acc)[RB][MT]) {
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    const v4i a0 = widen8<I8>(o.cw[rb][0], o.cw[rb][1]);
-    const v4i a1 = widen8<I8>(o.cw[rb][2], o.cw[rb][3]);
+    const v4i a0 = widen8<CODES>(o.cw[rb][0], o.cw[rb][1]);
+    const v4i a1 = widen8<CODES>(o.cw[rb][2], o.cw[rb][3]);
     const int i0 = meta_half(o.mw[rb], g), i1 = meta_half(o.mw[rb], g + 4);
 #pragma unroll
     for (int j = 0; j < MT; ++j) {
@@ -161,7 +183,7 @@ __device__ __forceinline__ void w8_compute(const W8Ops<RB, MT>& o, int g, v4f (&
 }
 #endif  // SG_DEVICE_PASS
 
-template <bool I8, int RB, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
+template <int CODES, int RB, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
 __global__ void __launch_bounds__(512) k_gemm_w8a16(W8Args a) {
   constexpr int U = W8_U;
   __shared__ __attribute__((aligned(16))) float red[W8_WAVES][RB * MT][64][4];
@@ -190,10 +212,10 @@ __global__ void __launch_bounds__(512) k_gemm_w8a16(W8Args a) {
   for (int t0 = 0; t0 < nt; t0 += U) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      w8_load<RB, MT, GRAN_N>(a, rw, rm, rx, n0, wave + W8_WAVES * min(t0 + u, nt - 1), lr, g, ops[u]);
+      w8_load<CODES, RB, MT, GRAN_N>(a, rw, rm, rx, n0, wave + W8_WAVES * min(t0 + u, nt - 1), lr, g, ops[u]);
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      if (t0 + u < nt) w8_compute<I8, RB, MT>(ops[u], g, acc);
+      if (t0 + u < nt) w8_compute<CODES, RB, MT>(ops[u], g, acc);
   }
 
 #pragma unroll
@@ -226,35 +248,35 @@ __global__ void __launch_bounds__(512) k_gemm_w8a16(W8Args a) {
 // at least 224 workgroups.  Every workgroup reads its X rows in full, so
 // fewer, taller workgroups read X fewer times (measured at M = 37 and 64:
 // 1.7x faster than one row block per workgroup).
-template <bool I8, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
+template <int CODES, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
 static void launch_w8_mt(const W8Args& a, hipStream_t st) {
   const int64_t rows16 = cdiv(a.N, 16);
   const unsigned gy = (unsigned)cdiv(a.M, 16 * MT);
   constexpr int RB4 = MT <= 2 ? 4 : 2, RB2 = 2;
   if (RB4 == 4 && rows16 * gy >= 4 * 224)
-    k_gemm_w8a16<I8, RB4, MT, GRAN_N, OUT_BF16, OUT_T><<<dim3((unsigned)cdiv(rows16, RB4), gy), 512, 0, st>>>(a);
+    k_gemm_w8a16<CODES, RB4, MT, GRAN_N, OUT_BF16, OUT_T><<<dim3((unsigned)cdiv(rows16, RB4), gy), 512, 0, st>>>(a);
   else if (RB2 == 2 && rows16 * gy >= 2 * 224)
-    k_gemm_w8a16<I8, RB2, MT, GRAN_N, OUT_BF16, OUT_T><<<dim3((unsigned)cdiv(rows16, RB2), gy), 512, 0, st>>>(a);
+    k_gemm_w8a16<CODES, RB2, MT, GRAN_N, OUT_BF16, OUT_T><<<dim3((unsigned)cdiv(rows16, RB2), gy), 512, 0, st>>>(a);
   else
-    k_gemm_w8a16<I8, 1, MT, GRAN_N, OUT_BF16, OUT_T><<<dim3((unsigned)rows16, gy), 512, 0, st>>>(a);
+    k_gemm_w8a16<CODES, 1, MT, GRAN_N, OUT_BF16, OUT_T><<<dim3((unsigned)rows16, gy), 512, 0, st>>>(a);
 }
 
-template <bool I8, int GRAN_N, bool OUT_BF16, bool OUT_T>
+template <int CODES, int GRAN_N, bool OUT_BF16, bool OUT_T>
 static void launch_w8_shape(const W8Args& a, hipStream_t st) {
-  if (a.M <= 16) launch_w8_mt<I8, 1, GRAN_N, OUT_BF16, OUT_T>(a, st);
-  else if (a.M <= 32) launch_w8_mt<I8, 2, GRAN_N, OUT_BF16, OUT_T>(a, st);
-  else if (a.M <= 48) launch_w8_mt<I8, 3, GRAN_N, OUT_BF16, OUT_T>(a, st);
-  else launch_w8_mt<I8, 4, GRAN_N, OUT_BF16, OUT_T>(a, st);
+  if (a.M <= 16) launch_w8_mt<CODES, 1, GRAN_N, OUT_BF16, OUT_T>(a, st);
+  else if (a.M <= 32) launch_w8_mt<CODES, 2, GRAN_N, OUT_BF16, OUT_T>(a, st);
+  else if (a.M <= 48) launch_w8_mt<CODES, 3, GRAN_N, OUT_BF16, OUT_T>(a, st);
+  else launch_w8_mt<CODES, 4, GRAN_N, OUT_BF16, OUT_T>(a, st);
 }
 
-template <bool I8, int GRAN_N>
+template <int CODES, int GRAN_N>
 static void launch_w8_form(const W8Args& a, bool bf16, bool yt, hipStream_t st) {
   if (bf16) {
-    if (yt) launch_w8_shape<I8, GRAN_N, true, true>(a, st);
-    else launch_w8_shape<I8, GRAN_N, true, false>(a, st);
+    if (yt) launch_w8_shape<CODES, GRAN_N, true, true>(a, st);
+    else launch_w8_shape<CODES, GRAN_N, true, false>(a, st);
   } else {
-    if (yt) launch_w8_shape<I8, GRAN_N, false, true>(a, st);
-    else launch_w8_shape<I8, GRAN_N, false, false>(a, st);
+    if (yt) launch_w8_shape<CODES, GRAN_N, false, true>(a, st);
+    else launch_w8_shape<CODES, GRAN_N, false, false>(a, st);
   }
 }
 
@@ -294,11 +316,41 @@ extern "C" sg_status sg_w8a16_sparse24_gemm_groupwise(int64_t M, int64_t N, int6
   clear_hip_error();
   const bool bf16 = y_dt == SG_BF16, yt = form == SG_OUT_YT;
   if (w_dt == SG_I8) {
-    if (gran_n == 128) launch_w8_form<true, 128>(a, bf16, yt, stream);
-    else launch_w8_form<true, 1>(a, bf16, yt, stream);
+    if (gran_n == 128) launch_w8_form<C_I8, 128>(a, bf16, yt, stream);
+    else launch_w8_form<C_I8, 1>(a, bf16, yt, stream);
   } else {
-    if (gran_n == 128) launch_w8_form<false, 128>(a, bf16, yt, stream);
-    else launch_w8_form<false, 1>(a, bf16, yt, stream);
+    if (gran_n == 128) launch_w8_form<C_E4M3, 128>(a, bf16, yt, stream);
+    else launch_w8_form<C_E4M3, 1>(a, bf16, yt, stream);
   }
+  return launch_status();
+}
+
+extern "C" sg_status sg_w4a16_sparse24_gemm_groupwise(int64_t M, int64_t N, int64_t K, const uint16_t* x,
+                                                      int64_t ldx, const uint8_t* wv4, int64_t ldwv4,
+                                                      const uint8_t* wmeta, int64_t ldwm, const float* sw,
+                                                      int64_t sw_sn, int64_t sw_sk, const float* bias, void* y,
+                                                      sg_dtype y_dt, int64_t ldy, sg_form form, hipStream_t stream) {
+  if (!x || !wv4 || !wmeta || !sw || !y) return SG_ERR_NULL;
+  if (y_dt != SG_F32 && y_dt != SG_BF16) return SG_ERR_UNSUPPORTED;
+  if (form != SG_OUT_Y && form != SG_OUT_YT) return SG_ERR_UNSUPPORTED;
+  if (M < 0 || N < 0 || K <= 0 || K % 128 != 0 || ldx < K || ldwv4 < K / 4 || ldwm < K / 8) return SG_ERR_SHAPE;
+  if (ldy < (form == SG_OUT_Y ? N : M)) return SG_ERR_SHAPE;
+  if (ldx >= (1LL << 24) || ldwv4 >= (1LL << 24) || ldwm >= (1LL << 24) || sw_sn < 0 || sw_sk < 0) return SG_ERR_SHAPE;
+  if (((N - 1) * sw_sn + (K / 128 - 1) * sw_sk) * 4 >= (1LL << 31)) return SG_ERR_SHAPE;
+  if (cdiv(N, 16) > 0x7fffffffLL || cdiv(M, 16) > 65535) return SG_ERR_SHAPE;
+  if (!aligned(x, 16) || (ldx * 2) % 16 || !aligned(wv4, 16) || ldwv4 % 16 || !aligned(wmeta, 16) || ldwm % 16 ||
+      !aligned(sw, 4) || !aligned(bias, 4) || !aligned(y, dtype_size(y_dt)))
+    return SG_ERR_ALIGN;
+  if (M == 0 || N == 0) return SG_OK;
+  W8Args a;
+  a.M = M; a.N = N; a.K = K;
+  a.x = x; a.ldx = ldx;
+  a.w = wv4; a.ldw = ldwv4; a.meta = wmeta; a.ldm = ldwm;
+  a.sw = sw; a.sw_sn = sw_sn; a.sw_sk = sw_sk; a.gn_shift = 0;
+  a.bias = bias;
+  a.y = y; a.ldy = ldy;
+  a.vec_store = (ldy % 4 == 0) && aligned(y, 4 * dtype_size(y_dt));
+  clear_hip_error();
+  launch_w8_form<C_I4, 1>(a, y_dt == SG_BF16, form == SG_OUT_YT, stream);
   return launch_status();
 }

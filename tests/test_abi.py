@@ -44,7 +44,7 @@ def test_header_declares_the_entry_points():
         "sg_int8_quant_groupwise", "sg_int8_sparse24_gemm_groupwise", "sg_int8_sparse24_gemm_groupwise_packed",
         "sg_fp8_gemm_groupwise_batched", "sg_fp8_sparse24_gemm_groupwise_batched",
         "sg_fp8_sparse24_gemm_groupwise_packed_batched", "sg_fp8_sparse24_gemm_groupwise_packed_grouped",
-        "sg_w8a16_sparse24_gemm_groupwise"])
+        "sg_w8a16_sparse24_gemm_groupwise", "sg_w4a16_sparse24_gemm_groupwise"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -361,3 +361,22 @@ def w8a16(**kw):
 ])
 def test_w8a16_validation(kw, code):
     assert w8a16(**kw) == code
+
+
+def w4a16(**kw):
+    a = dict(M=16, N=256, K=256, x=P, ldx=256, w=P2, ldw=64, meta=P3, ldm=32, sw=P3, swn=2, swk=1, bias=None,
+             y=P, ydt=1, ldy=256, form=0)
+    a.update(kw)
+    return sg.lib().sg_w4a16_sparse24_gemm_groupwise(a["M"], a["N"], a["K"], a["x"], a["ldx"], a["w"], a["ldw"],
+                                                     a["meta"], a["ldm"], a["sw"], a["swn"], a["swk"], a["bias"],
+                                                     a["y"], a["ydt"], a["ldy"], a["form"], None)
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), NULL), (dict(w=None), NULL), (dict(meta=None), NULL), (dict(sw=None), NULL),
+    (dict(ydt=2), UNSUP), (dict(form=2), UNSUP), (dict(K=200), SHAPE), (dict(ldw=32), SHAPE), (dict(ldm=16), SHAPE),
+    (dict(swn=-1), SHAPE), (dict(ldw=72), ALIGN), (dict(w=ODD), ALIGN), (dict(M=0), OK), (dict(N=0), OK),
+])
+def test_w4a16_validation(kw, code):
+    assert w4a16(**kw) == code

@@ -89,3 +89,59 @@ def test_w8a16_from_the_gpu_weight_pipeline():
         ref, bound = oracle.w8a16_sparse24_gemm_groupwise(xbits, oq, ometa, os_, 128, "int8" if int8 else "e4m3",
                                                           bound=True)
         assert_within_tolerance(got, ref, bound, f"int8={int8}")
+
+
+# --------------------------------------------------------------- W4A16
+
+def check_w4(m, n, k, out=torch.bfloat16, forms=("y", "yt"), bias=False, seed=0):
+    say(f"w4a16 M={m} N={n} K={k} {out} bias={bias} seed={seed}")
+    d = workloads.sparse_large(seed=seed, m=m, n=n, k=k)
+    x = up(d["x"]).to(torch.bfloat16)
+    xbits = x.view(torch.int16).cpu().numpy().view(np.uint16)
+    v32, meta = oracle.prune_compress24(d["w"])
+    q4, s4 = oracle.int4_quant_groupwise(v32, 64)
+    ref, bound = oracle.w4a16_sparse24_gemm_groupwise(xbits, q4, meta, s4, bound=True)
+    b = None
+    if bias:
+        bnp = np.random.default_rng(seed + 1).standard_normal(n).astype(np.float32) * 0.1
+        ref, bound = oracle.add_bias(ref, bound, bnp)
+        b = up(bnp)
+    outs = {}
+    for form in forms:
+        got = down(sg.w4a16_sparse24_gemm_groupwise(x, up(q4), up(meta), up(s4), out_dtype=out, form=form, bias=b))
+        got = got.T if form == "yt" else got
+        assert_within_tolerance(got.astype(np.float64), ref, bound, f"form={form}")
+        outs[form] = got
+    if len(outs) == 2:
+        assert np.array_equal(outs["y"], outs["yt"])
+
+
+@pytest.mark.parametrize("m,n,k", SHAPES)
+def test_w4a16_ragged(m, n, k):
+    check_w4(m, n, k, seed=40 + m + n)
+
+
+def test_w4a16_fp32_bias():
+    check_w4(37, 300, 384, out=torch.float32, bias=True, seed=41)
+
+
+def test_w4a16_decode_full_size():
+    check_w4(16, 14336, 4096, forms=("y",), seed=42)
+
+
+def test_w4a16_from_the_gpu_weight_pipeline():
+    """GPU prune + compress + int4 quantisation (64 compressed values per
+    scale), bit-exact against the oracle's, then the GEMM."""
+    m, n, k = 16, 512, 1024
+    say(f"w4a16 pipeline M={m} N={n} K={k}")
+    d = workloads.sparse_large(seed=43, m=m, n=n, k=k)
+    x = up(d["x"]).to(torch.bfloat16)
+    v32, meta = sg.sparse24_prune_compress(up(d["w"]))
+    q4, s4 = sg.int4_quant_groupwise(v32, gc=64)
+    ov32, ometa = oracle.prune_compress24(d["w"])
+    oq4, os4 = oracle.int4_quant_groupwise(ov32, 64)
+    assert np.array_equal(down(q4), oq4) and np.array_equal(down(s4), os4)
+    got = down(sg.w4a16_sparse24_gemm_groupwise(x, q4, meta, s4))
+    ref, bound = oracle.w4a16_sparse24_gemm_groupwise(x.view(torch.int16).cpu().numpy().view(np.uint16), oq4, ometa,
+                                                      os4, bound=True)
+    assert_within_tolerance(got, ref, bound, "pipeline")
