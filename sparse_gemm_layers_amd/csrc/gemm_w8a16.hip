@@ -244,6 +244,179 @@ __global__ void __launch_bounds__(512) k_gemm_w8a16(W8Args a) {
 #endif  // SG_DEVICE_PASS
 }
 
+// ------------------------------------------------------- M <= 16: LDS streaming
+// The same arithmetic with every operand streamed into a private LDS ring of
+// each wave by buffer loads that write LDS directly (no registers in flight,
+// no barriers in the loop): per K block the RB row blocks' codes and metadata,
+// X's 16 rows (bf16, 16-byte chunks XOR-swizzled by row) and the W scales.
+// Two slots per wave; each wave waits only for its own loads, counted exactly.
+template <int CODES, int RB>
+struct W8Dma {
+  static constexpr int CB = CODES == C_I4 ? 512 : 1024;   // code bytes of 16 rows per K block
+  static constexpr int MOFF = RB * CB;                       // metadata, 256 B per row block
+  static constexpr int XOFF = MOFF + RB * 256;               // X: 16 rows x 256 B
+  static constexpr int SWOFF = XOFF + 4096;                  // W scales, 256 B
+  static constexpr int KSZ = SWOFF + 256;                    // bytes per wave per K block
+  static constexpr int ARR = W8_WAVES * KSZ;                 // one slot of every wave
+  static constexpr int L = RB * (CODES == C_I4 ? 2 : 1) + RB + 4 + 1;   // loads per K block
+  static constexpr bool FITS = 2 * ARR <= 160 * 1024;
+};
+
+typedef __attribute__((address_space(3))) void w8_lds_t;
+
+#if SG_DEVICE_PASS
+__device__ __forceinline__ int xswz(int r) { return r & 7; }
+
+template <typename T>
+__device__ __forceinline__ T w8_lds(const uint8_t* base, uint32_t off) {
+  return *reinterpret_cast<const T*>(base + off);
+}
+
+template <int CODES, int RB, int GRAN_N>
+__device__ __forceinline__ void w8_dma_issue(uint8_t* sl, const W8Args& a, __amdgpu_buffer_rsrc_t rw,
+                                             __amdgpu_buffer_rsrc_t rm, __amdgpu_buffer_rsrc_t rx,
+                                             __amdgpu_buffer_rsrc_t rsw, int64_t n0, int kb, int l, bool valid) {
+  using D = W8Dma<CODES, RB>;
+  constexpr int KBB = CODES == C_I4 ? 32 : 64;      // code bytes per row per K block
+  const int far = 0x40000000;                        // out of range: no access, zeros
+  const int ws = valid ? kb * KBB : far, ms = valid ? kb * 16 : far, xs = valid ? kb * 256 : far;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    if constexpr (CODES == C_I4) {
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rw, (w8_lds_t*)(sl + rb * D::CB + e * 256), 4,
+            (uint32_t)((16 * rb + 8 * e + (l >> 3)) * a.ldw + 4 * (l & 7)), ws, 0, 0);
+    } else {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (w8_lds_t*)(sl + rb * D::CB), 16,
+                                               (uint32_t)((16 * rb + (l >> 2)) * a.ldw + 16 * (l & 3)), ws, 0, 0);
+    }
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rm, (w8_lds_t*)(sl + D::MOFF + rb * 256), 4,
+                                             (uint32_t)((16 * rb + (l >> 2)) * a.ldm + 4 * (l & 3)), ms, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int p = 64 * i + l, r = p >> 4, c = (p & 15) ^ xswz(r);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (w8_lds_t*)(sl + D::XOFF + i * 1024), 16,
+                                             (uint32_t)(r * a.ldx * 2 + c * 16), xs, 0, 0);
+  }
+  // W scales of this K block: lane rb < RB (128-row blocks) or lane = row (per row)
+  const int64_t n = GRAN_N == 128 ? (min(n0 + 16 * (l % RB), a.N - 1) >> 7) : min(n0 + l, a.N - 1);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, (w8_lds_t*)(sl + D::SWOFF), 4, (uint32_t)(n * a.sw_sn * 4),
+                                           (int)(kb * a.sw_sk * 4), 0, 0);
+}
+#endif  // SG_DEVICE_PASS
+
+template <int CODES, int RB, int GRAN_N, bool OUT_BF16, bool OUT_T>
+__global__ void __launch_bounds__(512) k_gemm_w8a16_dma(W8Args a) {
+#if SG_DEVICE_PASS
+  using D = W8Dma<CODES, RB>;
+  static_assert(D::FITS, "LDS");
+  __shared__ __attribute__((aligned(1024))) uint8_t r0[D::ARR];
+  __shared__ __attribute__((aligned(1024))) uint8_t r1[D::ARR];
+  const int t = threadIdx.x, l = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int g = l >> 4, lr = l & 15;
+  const int KB = (int)(a.K >> 7);
+  const int64_t n0 = (int64_t)blockIdx.x * (16 * RB);
+  const int64_t wrows = min((int64_t)(16 * RB), a.N - n0);
+  const __amdgpu_buffer_rsrc_t rw = w8_rsrc(a.w + n0 * a.ldw, (uint32_t)(wrows * a.ldw));
+  const __amdgpu_buffer_rsrc_t rm = w8_rsrc(a.meta + n0 * a.ldm, (uint32_t)(wrows * a.ldm));
+  const __amdgpu_buffer_rsrc_t rx = w8_rsrc(a.x, (uint32_t)(a.M * a.ldx * 2));   // rows past M read zero
+  const __amdgpu_buffer_rsrc_t rsw = w8_rsrc(a.sw, 0xffffffffu);
+  const int nt = (KB - wave + W8_WAVES - 1) / W8_WAVES;
+  const uint32_t wslot = (uint32_t)wave * D::KSZ;
+
+  v4f acc[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) acc[rb] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+  auto issue = [&](uint8_t* arr, int tt) {
+    w8_dma_issue<CODES, RB, GRAN_N>(arr + wslot, a, rw, rm, rx, rsw, n0, wave + W8_WAVES * min(tt, nt - 1), l,
+                                    tt < nt);
+  };
+  auto compute = [&](const uint8_t* arr) {
+    const uint8_t* sl = arr + wslot;
+    v8i b[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint4 lo = w8_lds<uint4>(sl, D::XOFF + lr * 256 + (((g + 8 * h) ^ xswz(lr)) << 4));
+      const uint4 hi = w8_lds<uint4>(sl, D::XOFF + lr * 256 + (((g + 8 * h + 4) ^ xswz(lr)) << 4));
+      b[h] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      v4i cw;
+      if constexpr (CODES == C_I4) {
+        cw = (v4i){w8_lds<int>(sl, rb * D::CB + lr * 32 + 4 * g), 0, w8_lds<int>(sl, rb * D::CB + lr * 32 + 16 + 4 * g), 0};
+      } else {
+        const uint2 c0 = w8_lds<uint2>(sl, rb * D::CB + lr * 64 + 8 * g);
+        const uint2 c1 = w8_lds<uint2>(sl, rb * D::CB + lr * 64 + 32 + 8 * g);
+        cw = (v4i){(int)c0.x, (int)c0.y, (int)c1.x, (int)c1.y};
+      }
+      const uint4 m = w8_lds<uint4>(sl, D::MOFF + rb * 256 + lr * 16);
+      const v4i mv = {(int)m.x, (int)m.y, (int)m.z, (int)m.w};
+      const v4i a0 = widen8<CODES>(cw[0], cw[1]);
+      const v4i a1 = widen8<CODES>(cw[2], cw[3]);
+      v4f p = {0.f, 0.f, 0.f, 0.f};
+      p = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(v8bf, a0), __builtin_bit_cast(v16bf, b[0]), p,
+                                                    meta_half(mv, g), 0, 0);
+      p = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(v8bf, a1), __builtin_bit_cast(v16bf, b[1]), p,
+                                                    meta_half(mv, g + 4), 0, 0);
+      float4 sw;
+      if (GRAN_N == 128) {
+        const float v = w8_lds<float>(sl, D::SWOFF + rb * 4);
+        sw = make_float4(v, v, v, v);
+      } else {
+        sw = w8_lds<float4>(sl, D::SWOFF + (16 * rb + 4 * g) * 4);
+      }
+      acc[rb][0] = fmaf(p[0], sw.x, acc[rb][0]);
+      acc[rb][1] = fmaf(p[1], sw.y, acc[rb][1]);
+      acc[rb][2] = fmaf(p[2], sw.z, acc[rb][2]);
+      acc[rb][3] = fmaf(p[3], sw.w, acc[rb][3]);
+    }
+  };
+
+  // K block t of this wave lives in r0 for even t, r1 for odd t; block t + 1
+  // is loaded while block t is multiplied
+  if (nt > 0) issue(r0, 0);
+  for (int t0 = 0; t0 < nt; t0 += 2) {
+    issue(r1, t0 + 1);
+    wait_vmcnt<D::L>();
+    compute(r0);
+    if (t0 + 1 < nt) {
+      issue(r0, t0 + 2);
+      wait_vmcnt<D::L>();
+      compute(r1);
+    }
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+  float4* red = reinterpret_cast<float4*>(r0);    // [W8_WAVES][RB][64]
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+    red[(wave * RB + rb) * 64 + l] = make_float4(acc[rb][0], acc[rb][1], acc[rb][2], acc[rb][3]);
+  __syncthreads();
+  for (int q = t; q < RB * 64; q += 512) {
+    const int rb = q >> 6, ll = q & 63;
+    float4 v4 = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int w = 0; w < W8_WAVES; ++w) {
+      const float4 v = red[(w * RB + rb) * 64 + ll];
+      v4.x += v.x; v4.y += v.y; v4.z += v.z; v4.w += v.w;
+    }
+    const int64_t n = n0 + 16 * rb + 4 * (ll >> 4);
+    v4f out = {v4.x, v4.y, v4.z, v4.w};
+    if (a.bias) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) out[e] += a.bias[min(n + e, a.N - 1)];
+    }
+    store_quad<OUT_BF16, OUT_T>(a, (int64_t)(ll & 15), n, out);
+  }
+#endif  // SG_DEVICE_PASS
+}
+
 // Row blocks per workgroup: the largest of 4 (2 for MT > 2), 2, 1 that keeps
 // at least 224 workgroups.  Every workgroup reads its X rows in full, so
 // fewer, taller workgroups read X fewer times (measured at M = 37 and 64:
@@ -252,6 +425,15 @@ template <int CODES, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
 static void launch_w8_mt(const W8Args& a, hipStream_t st) {
   const int64_t rows16 = cdiv(a.N, 16);
   const unsigned gy = (unsigned)cdiv(a.M, 16 * MT);
+  if constexpr (MT == 1) {   // LDS streaming: 4 row blocks per workgroup while >= 224 workgroups remain
+    if (rows16 >= 4 * 224)
+      k_gemm_w8a16_dma<CODES, 4, GRAN_N, OUT_BF16, OUT_T><<<(unsigned)cdiv(rows16, 4), 512, 0, st>>>(a);
+    else if (rows16 >= 2 * 224)
+      k_gemm_w8a16_dma<CODES, 2, GRAN_N, OUT_BF16, OUT_T><<<(unsigned)cdiv(rows16, 2), 512, 0, st>>>(a);
+    else
+      k_gemm_w8a16_dma<CODES, 1, GRAN_N, OUT_BF16, OUT_T><<<(unsigned)rows16, 512, 0, st>>>(a);
+    return;
+  }
   constexpr int RB4 = MT <= 2 ? 4 : 2, RB2 = 2;
   if (RB4 == 4 && rows16 * gy >= 4 * 224)
     k_gemm_w8a16<CODES, RB4, MT, GRAN_N, OUT_BF16, OUT_T><<<dim3((unsigned)cdiv(rows16, RB4), gy), 512, 0, st>>>(a);
