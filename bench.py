@@ -261,7 +261,18 @@ def rows_report():
     ms = time_fn(lambda i: sg.fp8_sparse24_gemm_groupwise_packed_grouped(xq, sx, sizes, wpb, n, swb, 128, y=y))
     out[f"next_grouped_sparse_gemm_packed_G8_ragged{m}x{n}x{k}_y"] = {
         "ms": ms, "TFLOP/s": flops / ms / 1e9, "frac_fp8_peak": flops / ms / 1e9 / PEAK_FP8_TFLOPS}
-    del wpb, swb, yb
+    # grouped decode (MoE): 8 experts of at most 16 tokens each; 4 copies of
+    # the 8 packed weights (4 x 84 MB) so the 256 MB MALL cannot serve repeats
+    sizes = [3, 9, 16, 1, 12, 5, 16, 2]
+    gm = sum(sizes)
+    wrot = [wpb] + [wpb.clone() for _ in range(3)]
+    yg = torch.empty((gm, n), dtype=torch.bfloat16, device=DEV)
+    ms = time_fn(lambda i: sg.fp8_sparse24_gemm_groupwise_packed_grouped(
+        xq[:gm], sx[:gm], sizes, wrot[i % 4], n, swb, 128, y=yg), reps=64, warm=16)
+    b = sum(sparse_bytes(mg, n, k) for mg in sizes if mg)
+    out[f"next_grouped_decode_G8_M{gm}_N{n}_K{k}_y"] = {"ms": ms, "GB/s": b / ms / 1e6,
+                                                       "frac_hbm": b / ms / 1e6 / PEAK_HBM_GBS}
+    del wpb, swb, yb, wrot, yg
     # next row: weight-only 2:4 (bf16 activations x e4m3 / int8 2:4 codes) at
     # the decode shapes (rotating weight copies) and at 2048x4096x4096
     dn, dk = 14336, 4096

@@ -1106,15 +1106,14 @@ __device__ __forceinline__ void dma_issue(uint8_t* slot, const GemmArgs& a, __am
 }
 #endif
 
-template <bool I8, int RB, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
-__global__ void __launch_bounds__(512) k_gemm_decode_dma(GemmArgs a) {
 #if SG_DEVICE_PASS
+template <bool I8, int RB, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
+__device__ __forceinline__ void decode_dma_body(const GemmArgs& a) {
   using C = DmaCfg<RB, MT>;
   constexpr int KPS = C::KPS;
   static_assert(MT <= 4 && 2 * C::ARR <= 160 * 1024, "LDS");
   __shared__ __attribute__((aligned(1024))) uint8_t r0[C::ARR];
   __shared__ __attribute__((aligned(1024))) uint8_t r1[C::ARR];
-  to_batch(a);
   const int t = threadIdx.x, l = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int g = l >> 4, lr = l & 15;
@@ -1226,6 +1225,35 @@ __global__ void __launch_bounds__(512) k_gemm_decode_dma(GemmArgs a) {
     store_quad<OUT_BF16, OUT_T>(a, (int64_t)j * 16 + (ll & 15), n0 + 16 * rb + 4 * (ll >> 4),
                                 with_bias(a, n0 + 16 * rb + 4 * (ll >> 4), out));
   }
+}
+#endif  // SG_DEVICE_PASS
+
+template <bool I8, int RB, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
+__global__ void __launch_bounds__(512) k_gemm_decode_dma(GemmArgs a) {
+#if SG_DEVICE_PASS
+  to_batch(a);
+  decode_dma_body<I8, RB, MT, GRAN_N, OUT_BF16, OUT_T>(a);
+#endif
+}
+
+// Grouped problems of at most 16 MT rows each (grid y = group): group g's X
+// rows, X scales (one row each), Y rows (columns of Y^T), packed weight, W
+// scales and bias, as in k_gemm_sparse_x2_grouped.  An empty group's
+// workgroups return at once.
+template <bool I8, int RB, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
+__global__ void __launch_bounds__(512) k_gemm_decode_dma_grouped(GemmArgs a, GroupTable gt) {
+#if SG_DEVICE_PASS
+  const int g = blockIdx.y;
+  const int64_t r0 = gt.row_off[g];
+  a.M = gt.row_off[g + 1] - r0;
+  if (a.M == 0) return;
+  a.x += r0 * a.ldx;
+  a.sx += r0 * a.sx_sm;
+  a.y = static_cast<uint8_t*>(a.y) + (OUT_T ? r0 : r0 * a.ldy) * (OUT_BF16 ? 2 : 4);
+  a.w += g * a.bw;
+  a.sw += g * a.bsw;
+  if (a.bias) a.bias += g * a.bbs;
+  decode_dma_body<I8, RB, MT, GRAN_N, OUT_BF16, OUT_T>(a);
 #endif
 }
 
@@ -1566,6 +1594,35 @@ static void launch_grouped_form(const GemmArgs& a, const GroupTable& gt, bool bf
   }
 }
 
+// Decode-sized groups: RB row blocks per workgroup, the largest of 4, 2, 1
+// whose ring fits LDS and that keeps at least 224 workgroups over all groups.
+template <int RB, int MT, bool OUT_BF16, bool OUT_T>
+static bool try_grouped_decode(const GemmArgs& a, const GroupTable& gt, hipStream_t st, int64_t rows16) {
+  if constexpr (DmaCfg<RB, MT>::FITS) {
+    if (RB == 1 || cdiv(rows16, RB) * gt.G >= 224) {
+      k_gemm_decode_dma_grouped<false, RB, MT, 128, OUT_BF16, OUT_T>
+          <<<dim3((unsigned)cdiv(rows16, RB), (unsigned)gt.G), 512, 0, st>>>(a, gt);
+      return true;
+    }
+  }
+  return false;
+}
+
+template <int MT, bool OUT_BF16, bool OUT_T>
+static void launch_grouped_decode_mt(const GemmArgs& a, const GroupTable& gt, hipStream_t st) {
+  const int64_t rows16 = cdiv(a.N, 16);
+  (void)(try_grouped_decode<4, MT, OUT_BF16, OUT_T>(a, gt, st, rows16) ||
+         try_grouped_decode<2, MT, OUT_BF16, OUT_T>(a, gt, st, rows16) ||
+         try_grouped_decode<1, MT, OUT_BF16, OUT_T>(a, gt, st, rows16));
+}
+
+template <bool OUT_BF16, bool OUT_T>
+static void launch_grouped_decode(const GemmArgs& a, const GroupTable& gt, int64_t mmax, hipStream_t st) {
+  if (mmax <= 16) launch_grouped_decode_mt<1, OUT_BF16, OUT_T>(a, gt, st);
+  else if (mmax <= 32) launch_grouped_decode_mt<2, OUT_BF16, OUT_T>(a, gt, st);
+  else launch_grouped_decode_mt<3, OUT_BF16, OUT_T>(a, gt, st);
+}
+
 extern "C" sg_status sg_fp8_sparse24_gemm_groupwise_packed_grouped(
     int64_t G, const int64_t* m_sizes, int64_t N, int64_t K, const uint8_t* xq, int64_t ldx, const float* sx,
     int64_t sx_sm, int64_t sx_sk, const uint8_t* wpacked, int64_t wp_bs, const float* sw, int64_t sw_sn,
@@ -1607,8 +1664,22 @@ extern "C" sg_status sg_fp8_sparse24_gemm_groupwise_packed_grouped(
       if ((gt.row_off[g] * (int64_t)dtype_size(y_dt)) % 16) a.vec16 = 0;
   clear_hip_error();
   const bool bf16 = y_dt == SG_BF16, yt = form == SG_OUT_YT;
-  if (sx_sk == 0 && sw_sk == 0) launch_grouped_form<0>(a, gt, bf16, yt, stream);
-  else if (gran_n == 128) launch_grouped_form<128>(a, gt, bf16, yt, stream);
-  else launch_grouped_form<1>(a, gt, bf16, yt, stream);
+  int64_t mmax = 0;
+  for (int g = 0; g < G; ++g) mmax = std::max(mmax, m_sizes[g]);
+  if (gran_n == 128 && mmax <= 48) {   // decode-sized groups: the LDS-streaming decode kernel
+    if (bf16) {
+      if (yt) launch_grouped_decode<true, true>(a, gt, mmax, stream);
+      else launch_grouped_decode<true, false>(a, gt, mmax, stream);
+    } else {
+      if (yt) launch_grouped_decode<false, true>(a, gt, mmax, stream);
+      else launch_grouped_decode<false, false>(a, gt, mmax, stream);
+    }
+  } else if (sx_sk == 0 && sw_sk == 0) {
+    launch_grouped_form<0>(a, gt, bf16, yt, stream);
+  } else if (gran_n == 128) {
+    launch_grouped_form<128>(a, gt, bf16, yt, stream);
+  } else {
+    launch_grouped_form<1>(a, gt, bf16, yt, stream);
+  }
   return launch_status();
 }

@@ -366,7 +366,12 @@ def grouped_operands(sizes, n, k, seed, gn=128):
                                                ([5, 7, 300], "yt", torch.bfloat16, 128),
                                                ([200, 72], "yt", torch.float32, 1),
                                                ([16], "y", torch.float32, 128),
-                                               ([0, 0], "y", torch.bfloat16, 128)])
+                                               ([0, 0], "y", torch.bfloat16, 128),
+                                               # every group <= 48 rows: the decode-sized grouped kernel
+                                               ([1, 0, 17, 48, 33], "yt", torch.bfloat16, 128),
+                                               ([16, 16, 3, 9], "y", torch.float32, 128),
+                                               ([20, 32], "y", torch.bfloat16, 128),
+                                               ([7, 40], "yt", torch.float32, 128)])
 def test_grouped(sizes, form, out, gn):
     n, k = 384, 512
     say(f"grouped sizes={sizes} N={n} K={k} form={form} {out} gn={gn}")
@@ -385,6 +390,28 @@ def test_grouped(sizes, form, out, gn):
             ref, bound = oracle.fp8_sparse24_gemm_groupwise(xq[r:r + mg], sx[r:r + mg], 1, wq, meta, swg, gn,
                                                              bound=True)
             ref, bound = oracle.add_bias(ref, bound, bias[g])
+            assert_within_tolerance(got[r:r + mg].astype(np.float64), ref, bound, f"group {g}")
+        r += mg
+
+
+@pytest.mark.parametrize("sizes,form", [([5, 16, 1, 12, 0, 16, 7, 2], "y"), ([3, 9], "yt")])
+def test_grouped_decode_wide(sizes, form):
+    """MoE decode: many small groups over a wide weight (four row blocks per
+    workgroup for the 8-group case, one for the 2-group case)."""
+    n, k = 4096, 1024
+    say(f"grouped decode sizes={sizes} N={n} K={k} form={form}")
+    xq, sx, ws = grouped_operands(sizes, n, k, seed=130 + len(sizes))
+    wp = torch.stack([sg.sparse24_pack_gfx950(up(wq), up(meta)) for wq, meta, _ in ws])
+    sw = torch.stack([up_m_major(s) for _, _, s in ws])
+    got = down(sg.fp8_sparse24_gemm_groupwise_packed_grouped(up(xq), up_m_major(sx), sizes, wp, n, sw, 128,
+                                                             out_dtype=torch.bfloat16, form=form))
+    got = got.T if form == "yt" else got
+    r = 0
+    for g, mg in enumerate(sizes):
+        if mg:
+            wq, meta, swg = ws[g]
+            ref, bound = oracle.fp8_sparse24_gemm_groupwise(xq[r:r + mg], sx[r:r + mg], 1, wq, meta, swg, 128,
+                                                             bound=True)
             assert_within_tolerance(got[r:r + mg].astype(np.float64), ref, bound, f"group {g}")
         r += mg
 
