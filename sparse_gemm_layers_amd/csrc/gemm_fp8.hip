@@ -1077,15 +1077,20 @@ struct DmaOffs {
 // directly (so that the compiler can neither merge nor drop any of them: the
 // slot's count of L loads is exact).  A K block past the wave's last is still
 // issued (so that every slot has exactly L loads in flight on every path), but
-// its weight and X loads are out of range (no memory access, zeros) and its
-// scales are those of a valid block.
+// its weight and X loads go through descriptors of zero records, out of range
+// for every offset (no memory access, zeros), and its scales are those of a
+// valid block.
 template <int RB, int MT>
 __device__ __forceinline__ void dma_issue(uint8_t* slot, const GemmArgs& a, __amdgpu_buffer_rsrc_t rw,
                                           __amdgpu_buffer_rsrc_t rx, __amdgpu_buffer_rsrc_t rsx,
                                           __amdgpu_buffer_rsrc_t rsw, const DmaOffs& o, int kb, int KB, int l,
                                           bool valid) {
   using C = DmaCfg<RB, MT>;
-  const int ws = valid ? kb * PK_CHUNK : 0x40000000, xs = valid ? kb * 128 : 0x40000000;
+  const int ws = valid ? kb * PK_CHUNK : 0, xs = valid ? kb * 128 : 0;
+  if (!valid) {
+    rw = rsrc(a.w, 0);
+    rx = rsrc(a.x, 0);
+  }
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     uint8_t* c = slot + rb * PK_CHUNK;

@@ -244,21 +244,25 @@ __global__ void __launch_bounds__(512) k_gemm_w8a16(W8Args a) {
 #endif  // SG_DEVICE_PASS
 }
 
-// ------------------------------------------------------- M <= 16: LDS streaming
-// The same arithmetic with every operand streamed into a private LDS ring of
-// each wave by buffer loads that write LDS directly (no registers in flight,
-// no barriers in the loop): per K block the RB row blocks' codes and metadata,
-// X's 16 rows (bf16, 16-byte chunks XOR-swizzled by row) and the W scales.
-// Two slots per wave; each wave waits only for its own loads, counted exactly.
-template <int CODES, int RB>
+// ------------------------------------------------------- M <= 48: LDS streaming
+// The same arithmetic with the weight streamed into a private LDS ring of each
+// wave by buffer loads that write LDS directly (no registers in flight, no
+// barriers in the loop): per K block the RB row blocks' codes and metadata and
+// the W scales.  X (bf16) takes 4 KB per 16 rows and K block: for one 16-row
+// sub-tile it rides in the ring too (16-byte chunks XOR-swizzled by row); for
+// two or three it would overflow LDS, so each wave loads its X fragments into
+// registers with the same K block's loads (from L2: every workgroup reads all
+// of X).  Two slots per wave; each wave waits only for its own loads, counted
+// exactly (loads return in order, whether to LDS or to registers).
+template <int CODES, int RB, int MT>
 struct W8Dma {
   static constexpr int CB = CODES == C_I4 ? 512 : 1024;   // code bytes of 16 rows per K block
   static constexpr int MOFF = RB * CB;                       // metadata, 256 B per row block
-  static constexpr int XOFF = MOFF + RB * 256;               // X: 16 rows x 256 B
-  static constexpr int SWOFF = XOFF + 4096;                  // W scales, 256 B
+  static constexpr int XOFF = MOFF + RB * 256;               // X (one sub-tile): 16 rows x 256 B
+  static constexpr int SWOFF = XOFF + (MT == 1 ? 4096 : 0);  // W scales, 256 B
   static constexpr int KSZ = SWOFF + 256;                    // bytes per wave per K block
   static constexpr int ARR = W8_WAVES * KSZ;                 // one slot of every wave
-  static constexpr int L = RB * (CODES == C_I4 ? 2 : 1) + RB + 4 + 1;   // loads per K block
+  static constexpr int L = RB * (CODES == C_I4 ? 2 : 1) + RB + 4 * MT + 1;   // loads per K block
   static constexpr bool FITS = 2 * ARR <= 160 * 1024;
 };
 
@@ -272,14 +276,28 @@ __device__ __forceinline__ T w8_lds(const uint8_t* base, uint32_t off) {
   return *reinterpret_cast<const T*>(base + off);
 }
 
-template <int CODES, int RB, int GRAN_N>
+// X fragments of lane (g, lr) for MT sub-tiles: row 16 j + lr, 16-byte chunks
+// g, g + 4, g + 8, g + 12 of the K block's 256 bytes
+template <int MT>
+struct W8X {
+  v4i c[MT][4];
+};
+
+template <int CODES, int RB, int MT, int GRAN_N>
 __device__ __forceinline__ void w8_dma_issue(uint8_t* sl, const W8Args& a, __amdgpu_buffer_rsrc_t rw,
                                              __amdgpu_buffer_rsrc_t rm, __amdgpu_buffer_rsrc_t rx,
-                                             __amdgpu_buffer_rsrc_t rsw, int64_t n0, int kb, int l, bool valid) {
-  using D = W8Dma<CODES, RB>;
+                                             __amdgpu_buffer_rsrc_t rsw, int64_t n0, int kb, int l, bool valid,
+                                             W8X<MT>& xr) {
+  using D = W8Dma<CODES, RB, MT>;
   constexpr int KBB = CODES == C_I4 ? 32 : 64;      // code bytes per row per K block
-  const int far = 0x40000000;                        // out of range: no access, zeros
-  const int ws = valid ? kb * KBB : far, ms = valid ? kb * 16 : far, xs = valid ? kb * 256 : far;
+  // a K block past the wave's last reads through descriptors of zero records,
+  // out of range for every offset: no memory access, zeros
+  const int ws = valid ? kb * KBB : 0, ms = valid ? kb * 16 : 0, xs = valid ? kb * 256 : 0;
+  if (!valid) {
+    rw = w8_rsrc(a.w, 0);
+    rm = w8_rsrc(a.meta, 0);
+    rx = w8_rsrc(a.x, 0);
+  }
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     if constexpr (CODES == C_I4) {
@@ -295,11 +313,20 @@ __device__ __forceinline__ void w8_dma_issue(uint8_t* sl, const W8Args& a, __amd
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rm, (w8_lds_t*)(sl + D::MOFF + rb * 256), 4,
                                              (uint32_t)((16 * rb + (l >> 2)) * a.ldm + 4 * (l & 3)), ms, 0, 0);
   }
+  if constexpr (MT == 1) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int p = 64 * i + l, r = p >> 4, c = (p & 15) ^ xswz(r);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (w8_lds_t*)(sl + D::XOFF + i * 1024), 16,
-                                             (uint32_t)(r * a.ldx * 2 + c * 16), xs, 0, 0);
+    for (int i = 0; i < 4; ++i) {
+      const int p = 64 * i + l, r = p >> 4, c = (p & 15) ^ xswz(r);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (w8_lds_t*)(sl + D::XOFF + i * 1024), 16,
+                                               (uint32_t)(r * a.ldx * 2 + c * 16), xs, 0, 0);
+    }
+  } else {
+    const int g = l >> 4, lr = l & 15;
+#pragma unroll
+    for (int j = 0; j < MT; ++j)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        xr.c[j][c] = w8_ld16(rx, (uint32_t)((16 * j + lr) * a.ldx * 2 + (g + 4 * c) * 16), xs);
   }
   // W scales of this K block: lane rb < RB (128-row blocks) or lane = row (per row)
   const int64_t n = GRAN_N == 128 ? (min(n0 + 16 * (l % RB), a.N - 1) >> 7) : min(n0 + l, a.N - 1);
@@ -308,11 +335,11 @@ __device__ __forceinline__ void w8_dma_issue(uint8_t* sl, const W8Args& a, __amd
 }
 #endif  // SG_DEVICE_PASS
 
-template <int CODES, int RB, int GRAN_N, bool OUT_BF16, bool OUT_T>
+template <int CODES, int RB, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
 __global__ void __launch_bounds__(512) k_gemm_w8a16_dma(W8Args a) {
 #if SG_DEVICE_PASS
-  using D = W8Dma<CODES, RB>;
-  static_assert(D::FITS, "LDS");
+  using D = W8Dma<CODES, RB, MT>;
+  static_assert(D::FITS && 4 * RB * 64 * 16 <= D::ARR, "LDS");
   __shared__ __attribute__((aligned(1024))) uint8_t r0[D::ARR];
   __shared__ __attribute__((aligned(1024))) uint8_t r1[D::ARR];
   const int t = threadIdx.x, l = t & 63;
@@ -328,22 +355,35 @@ __global__ void __launch_bounds__(512) k_gemm_w8a16_dma(W8Args a) {
   const int nt = (KB - wave + W8_WAVES - 1) / W8_WAVES;
   const uint32_t wslot = (uint32_t)wave * D::KSZ;
 
-  v4f acc[RB];
+  v4f acc[RB][MT];
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) acc[rb] = (v4f){0.f, 0.f, 0.f, 0.f};
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int j = 0; j < MT; ++j) acc[rb][j] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-  auto issue = [&](uint8_t* arr, int tt) {
-    w8_dma_issue<CODES, RB, GRAN_N>(arr + wslot, a, rw, rm, rx, rsw, n0, wave + W8_WAVES * min(tt, nt - 1), l,
-                                    tt < nt);
+  auto issue = [&](uint8_t* arr, W8X<MT>& xr, int tt) {
+    w8_dma_issue<CODES, RB, MT, GRAN_N>(arr + wslot, a, rw, rm, rx, rsw, n0, wave + W8_WAVES * min(tt, nt - 1), l,
+                                        tt < nt, xr);
   };
-  auto compute = [&](const uint8_t* arr) {
+  auto compute = [&](const uint8_t* arr, const W8X<MT>& xr) {
     const uint8_t* sl = arr + wslot;
-    v8i b[2];
+    v8i b[MT][2];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const uint4 lo = w8_lds<uint4>(sl, D::XOFF + lr * 256 + (((g + 8 * h) ^ xswz(lr)) << 4));
-      const uint4 hi = w8_lds<uint4>(sl, D::XOFF + lr * 256 + (((g + 8 * h + 4) ^ xswz(lr)) << 4));
-      b[h] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    for (int j = 0; j < MT; ++j) {
+      if constexpr (MT == 1) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint4 lo = w8_lds<uint4>(sl, D::XOFF + lr * 256 + (((g + 8 * h) ^ xswz(lr)) << 4));
+          const uint4 hi = w8_lds<uint4>(sl, D::XOFF + lr * 256 + (((g + 8 * h + 4) ^ xswz(lr)) << 4));
+          b[j][h] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        }
+      } else {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const v4i lo = xr.c[j][2 * h], hi = xr.c[j][2 * h + 1];
+          b[j][h] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
+      }
     }
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -359,11 +399,7 @@ __global__ void __launch_bounds__(512) k_gemm_w8a16_dma(W8Args a) {
       const v4i mv = {(int)m.x, (int)m.y, (int)m.z, (int)m.w};
       const v4i a0 = widen8<CODES>(cw[0], cw[1]);
       const v4i a1 = widen8<CODES>(cw[2], cw[3]);
-      v4f p = {0.f, 0.f, 0.f, 0.f};
-      p = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(v8bf, a0), __builtin_bit_cast(v16bf, b[0]), p,
-                                                    meta_half(mv, g), 0, 0);
-      p = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(v8bf, a1), __builtin_bit_cast(v16bf, b[1]), p,
-                                                    meta_half(mv, g + 4), 0, 0);
+      const int i0 = meta_half(mv, g), i1 = meta_half(mv, g + 4);
       float4 sw;
       if (GRAN_N == 128) {
         const float v = w8_lds<float>(sl, D::SWOFF + rb * 4);
@@ -371,50 +407,78 @@ __global__ void __launch_bounds__(512) k_gemm_w8a16_dma(W8Args a) {
       } else {
         sw = w8_lds<float4>(sl, D::SWOFF + (16 * rb + 4 * g) * 4);
       }
-      acc[rb][0] = fmaf(p[0], sw.x, acc[rb][0]);
-      acc[rb][1] = fmaf(p[1], sw.y, acc[rb][1]);
-      acc[rb][2] = fmaf(p[2], sw.z, acc[rb][2]);
-      acc[rb][3] = fmaf(p[3], sw.w, acc[rb][3]);
+#pragma unroll
+      for (int j = 0; j < MT; ++j) {
+        v4f p = {0.f, 0.f, 0.f, 0.f};
+        p = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(v8bf, a0), __builtin_bit_cast(v16bf, b[j][0]),
+                                                      p, i0, 0, 0);
+        p = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(v8bf, a1), __builtin_bit_cast(v16bf, b[j][1]),
+                                                      p, i1, 0, 0);
+        acc[rb][j][0] = fmaf(p[0], sw.x, acc[rb][j][0]);
+        acc[rb][j][1] = fmaf(p[1], sw.y, acc[rb][j][1]);
+        acc[rb][j][2] = fmaf(p[2], sw.z, acc[rb][j][2]);
+        acc[rb][j][3] = fmaf(p[3], sw.w, acc[rb][j][3]);
+      }
     }
   };
 
-  // K block t of this wave lives in r0 for even t, r1 for odd t; block t + 1
-  // is loaded while block t is multiplied
-  if (nt > 0) issue(r0, 0);
+  // K block t of this wave lives in r0 / xa for even t, r1 / xb for odd t;
+  // block t + 1 is loaded while block t is multiplied
+  W8X<MT> xa, xb;
+  if (nt > 0) issue(r0, xa, 0);
   for (int t0 = 0; t0 < nt; t0 += 2) {
-    issue(r1, t0 + 1);
+    issue(r1, xb, t0 + 1);
     wait_vmcnt<D::L>();
-    compute(r0);
+    compute(r0, xa);
     if (t0 + 1 < nt) {
-      issue(r0, t0 + 2);
+      issue(r0, xa, t0 + 2);
       wait_vmcnt<D::L>();
-      compute(r1);
+      compute(r1, xb);
     }
   }
   wait_vmcnt<0>();
-  __syncthreads();
-  float4* red = reinterpret_cast<float4*>(r0);    // [W8_WAVES][RB][64]
+  // waves 0-3 hand their partial tiles over in r0, waves 4-7 in r1, one
+  // sub-tile column j at a time: [4][RB][64] float4 each
+  float4* const mine = reinterpret_cast<float4*>(wave < 4 ? r0 : r1) + (wave & 3) * RB * 64;
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
-    red[(wave * RB + rb) * 64 + l] = make_float4(acc[rb][0], acc[rb][1], acc[rb][2], acc[rb][3]);
-  __syncthreads();
-  for (int q = t; q < RB * 64; q += 512) {
-    const int rb = q >> 6, ll = q & 63;
-    float4 v4 = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j = 0; j < MT; ++j) {
+    __syncthreads();
 #pragma unroll
-    for (int w = 0; w < W8_WAVES; ++w) {
-      const float4 v = red[(w * RB + rb) * 64 + ll];
-      v4.x += v.x; v4.y += v.y; v4.z += v.z; v4.w += v.w;
+    for (int rb = 0; rb < RB; ++rb)
+      mine[rb * 64 + l] = make_float4(acc[rb][j][0], acc[rb][j][1], acc[rb][j][2], acc[rb][j][3]);
+    __syncthreads();
+    for (int q = t; q < RB * 64; q += 512) {
+      const int rb = q >> 6, ll = q & 63;
+      float4 v4 = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int w = 0; w < W8_WAVES; ++w) {
+        const float4 v = reinterpret_cast<const float4*>(w < 4 ? r0 : r1)[((w & 3) * RB + rb) * 64 + ll];
+        v4.x += v.x; v4.y += v.y; v4.z += v.z; v4.w += v.w;
+      }
+      const int64_t n = n0 + 16 * rb + 4 * (ll >> 4);
+      v4f out = {v4.x, v4.y, v4.z, v4.w};
+      if (a.bias) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[e] += a.bias[min(n + e, a.N - 1)];
+      }
+      store_quad<OUT_BF16, OUT_T>(a, (int64_t)(16 * j + (ll & 15)), n, out);
     }
-    const int64_t n = n0 + 16 * rb + 4 * (ll >> 4);
-    v4f out = {v4.x, v4.y, v4.z, v4.w};
-    if (a.bias) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) out[e] += a.bias[min(n + e, a.N - 1)];
-    }
-    store_quad<OUT_BF16, OUT_T>(a, (int64_t)(ll & 15), n, out);
   }
 #endif  // SG_DEVICE_PASS
+}
+
+// Launches the LDS-streaming kernel with RB row blocks per workgroup if its
+// ring fits LDS and the grid keeps at least 224 workgroups (RB = 1 always
+// qualifies).
+template <int CODES, int RB, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
+static bool try_w8_dma(const W8Args& a, hipStream_t st, int64_t rows16) {
+  if constexpr (W8Dma<CODES, RB, MT>::FITS) {
+    if (RB == 1 || rows16 >= RB * 224) {
+      k_gemm_w8a16_dma<CODES, RB, MT, GRAN_N, OUT_BF16, OUT_T><<<(unsigned)cdiv(rows16, RB), 512, 0, st>>>(a);
+      return true;
+    }
+  }
+  return false;
 }
 
 // Row blocks per workgroup: the largest of 4 (2 for MT > 2), 2, 1 that keeps
@@ -425,14 +489,11 @@ template <int CODES, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
 static void launch_w8_mt(const W8Args& a, hipStream_t st) {
   const int64_t rows16 = cdiv(a.N, 16);
   const unsigned gy = (unsigned)cdiv(a.M, 16 * MT);
-  if constexpr (MT == 1) {   // LDS streaming: 4 row blocks per workgroup while >= 224 workgroups remain
-    if (rows16 >= 4 * 224)
-      k_gemm_w8a16_dma<CODES, 4, GRAN_N, OUT_BF16, OUT_T><<<(unsigned)cdiv(rows16, 4), 512, 0, st>>>(a);
-    else if (rows16 >= 2 * 224)
-      k_gemm_w8a16_dma<CODES, 2, GRAN_N, OUT_BF16, OUT_T><<<(unsigned)cdiv(rows16, 2), 512, 0, st>>>(a);
-    else
-      k_gemm_w8a16_dma<CODES, 1, GRAN_N, OUT_BF16, OUT_T><<<(unsigned)rows16, 512, 0, st>>>(a);
-    return;
+  if constexpr (MT <= 3) {   // LDS streaming, one workgroup per RB row blocks and all of M
+    if (try_w8_dma<CODES, 4, MT, GRAN_N, OUT_BF16, OUT_T>(a, st, rows16) ||
+        try_w8_dma<CODES, 2, MT, GRAN_N, OUT_BF16, OUT_T>(a, st, rows16) ||
+        try_w8_dma<CODES, 1, MT, GRAN_N, OUT_BF16, OUT_T>(a, st, rows16))
+      return;
   }
   constexpr int RB4 = MT <= 2 ? 4 : 2, RB2 = 2;
   if (RB4 == 4 && rows16 * gy >= 4 * 224)

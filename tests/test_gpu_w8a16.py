@@ -72,6 +72,18 @@ def test_w8a16_decode_full_size(int8):
     check(16, 14336, 4096, int8=int8, forms=("y",), seed=21 + int8)
 
 
+@pytest.mark.parametrize("int8", [False, True])
+def test_w8a16_decode_m37_full_size(int8):
+    """M = 37 (three 16-row sub-tiles, X in registers), N = 14336, K = 4096:
+    four row blocks per workgroup."""
+    check(37, 14336, 4096, int8=int8, forms=("y",), seed=23 + int8)
+
+
+def test_w8a16_two_row_blocks_ragged_last():
+    """M = 32, N = 7208: two row blocks per workgroup, the last one partial."""
+    check(32, 7208, 512, out=torch.float32, bias=True, seed=25)
+
+
 def test_w8a16_from_the_gpu_weight_pipeline():
     """GPU prune + compress + int8 / e4m3 quantisation of a weight, then the
     weight-only GEMM, against the oracle's chain."""
@@ -127,6 +139,10 @@ def test_w4a16_fp32_bias():
 
 def test_w4a16_decode_full_size():
     check_w4(16, 14336, 4096, forms=("y",), seed=42)
+
+
+def test_w4a16_decode_m37_full_size():
+    check_w4(37, 14336, 4096, forms=("y",), seed=43)
 
 
 def test_w4a16_from_the_gpu_weight_pipeline():
