@@ -1042,21 +1042,28 @@ __global__ void __launch_bounds__(512) k_gemm_decode(GemmArgs a) {
 }
 
 // ------------------------------------------- decode kernel, LDS-DMA streaming
-// For packed 2:4 weights with 128-row W scales and M <= 48.  Same work split
+// For packed 2:4 weights with 128-row W scales and M <= 64.  Same work split
 // as k_gemm_decode, but each wave streams its K blocks into a private ring of
 // LDS slots with buffer loads that write LDS directly: per K block the RB
-// weight chunks (verbatim), the MT X slices (16 rows x 128 B, 16-byte chunks
-// swizzled by row against bank conflicts) and both scales.  A wave only waits
+// weight chunks (verbatim), the X slice when M <= 16 (16 rows x 128 B, 16-byte
+// chunks swizzled by row against bank conflicts) and both scales.  A wave only waits
 // for its own loads, so the loop has no barriers, and a load into LDS needs no
 // registers while in flight (measured on MI355X: this streams faster than
 // loads into registers, which stop gaining from more loads in flight early).
 // Ring of two slots per wave (the compiler tracks the loads in flight into two
 // LDS arrays separately, so that reading one slot does not wait for the
-// other); a slot holds KPS K blocks.
+// other); a slot holds KPS K blocks.  With two or more 16-row sub-tiles the X
+// slices would crowd 4 row blocks of weight out of the ring (2 KB per sub-tile
+// and K block against 1.25 KB per row block): there each wave loads its X
+// fragments into registers with the same K block's loads (loads return in
+// order, so the per-slot count still covers them).  With fewer row blocks X
+// outweighs the weight, and the ring streams it better than register loads
+// (measured at M = 37, N = 4096, K = 14336: 16.8 against 23.0 us).
 template <int RB, int MT>
 struct DmaCfg {
-  static constexpr int XOFF = RB * PK_CHUNK;                    // X slices (2 KB each)
-  static constexpr int SXOFF = XOFF + MT * 2048;                // X scales (256 B per sub-tile)
+  static constexpr bool XR = MT >= 2 && RB == 4;                // X fragments in registers
+  static constexpr int XOFF = RB * PK_CHUNK;                    // X slices (2 KB each) unless XR
+  static constexpr int SXOFF = XOFF + (XR ? 0 : MT * 2048);     // X scales (256 B per sub-tile)
   static constexpr int SWOFF = SXOFF + MT * 256;                // W scales (256 B)
   static constexpr int KSZ = SWOFF + 256;                       // bytes per wave per K block
   static constexpr int KPS = 2 * 2 * DEC_WAVES * KSZ <= 150 * 1024 ? 2 : 1;   // K blocks per slot
@@ -1084,7 +1091,7 @@ template <int RB, int MT>
 __device__ __forceinline__ void dma_issue(uint8_t* slot, const GemmArgs& a, __amdgpu_buffer_rsrc_t rw,
                                           __amdgpu_buffer_rsrc_t rx, __amdgpu_buffer_rsrc_t rsx,
                                           __amdgpu_buffer_rsrc_t rsw, const DmaOffs& o, int kb, int KB, int l,
-                                          bool valid) {
+                                          bool valid, v8i (&xr)[MT]) {
   using C = DmaCfg<RB, MT>;
   const int ws = valid ? kb * PK_CHUNK : 0, xs = valid ? kb * 128 : 0;
   if (!valid) {
@@ -1100,10 +1107,17 @@ __device__ __forceinline__ void dma_issue(uint8_t* slot, const GemmArgs& a, __am
   }
 #pragma unroll
   for (int j = 0; j < MT; ++j) {
-    uint8_t* x = slot + C::XOFF + j * 2048;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)x, 16, o.x[0] + (uint32_t)(16 * j * a.ldx), xs, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(x + 1024), 16, o.x[1] + (uint32_t)(16 * j * a.ldx),
-                                             xs, 0, 0);
+    if constexpr (C::XR) {   // row 16 j + (l & 15), bytes 32 (l >> 4) .. + 31 of the K block
+      const uint32_t xo = (uint32_t)((16 * j + (l & 15)) * a.ldx) + 32 * (l >> 4);
+      const v4i lo = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rx, xo, xs, 0));
+      const v4i hi = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rx, xo + 16, xs, 0));
+      xr[j] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    } else {
+      uint8_t* x = slot + C::XOFF + j * 2048;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)x, 16, o.x[0] + (uint32_t)(16 * j * a.ldx), xs, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(x + 1024), 16, o.x[1] + (uint32_t)(16 * j * a.ldx),
+                                               xs, 0, 0);
+    }
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsx, (lds_void*)(slot + C::SXOFF + j * 256), 4, o.sx[j],
                                              (int)(kb * a.sx_sk * 4), 0, 0);
   }
@@ -1152,12 +1166,14 @@ __device__ __forceinline__ void decode_dma_body(const GemmArgs& a) {
   const uint32_t ox1 = wslot + C::XOFF + lr * 128 + (((2 * g + 1) ^ swz8(lr)) << 4);
   const uint32_t osx = wslot + C::SXOFF + lr * 4, osw = wslot + C::SWOFF;
 
-  auto issue = [&](uint8_t* arr, int s) {
+  // X fragments of the K blocks of the slot in r0 / r1 (registers when XR)
+  v8i xa[KPS][MT], xb[KPS][MT];
+  auto issue = [&](uint8_t* arr, v8i (&xr)[KPS][MT], int s) {
 #pragma unroll
     for (int k = 0; k < KPS; ++k) {
       const int tt = s * KPS + k;
       dma_issue<RB, MT>(arr + wslot + k * C::KSZ, a, rw, rx, rsx, rsw, o, wave + DEC_WAVES * min(tt, nt - 1), KB, l,
-                        tt < nt);
+                        tt < nt, xr[k]);
     }
   };
 
@@ -1167,7 +1183,7 @@ __device__ __forceinline__ void decode_dma_body(const GemmArgs& a) {
 #pragma unroll
     for (int j = 0; j < MT; ++j) acc[rb][j] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](const uint8_t* sl, int s) {
+  auto compute = [&](const uint8_t* sl, const v8i (&xr)[KPS][MT], int s) {
 #pragma unroll
     for (int k = 0; k < KPS; ++k) {
       if (s * KPS + k < nt) {
@@ -1176,8 +1192,12 @@ __device__ __forceinline__ void decode_dma_body(const GemmArgs& a) {
         float sxv[MT];
 #pragma unroll
         for (int j = 0; j < MT; ++j) {
-          const uint4 lo = lds_ld<uint4>(sl, ox0 + kk + j * 2048), hi = lds_ld<uint4>(sl, ox1 + kk + j * 2048);
-          bx[j] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+          if constexpr (C::XR) {
+            bx[j] = xr[k][j];
+          } else {
+            const uint4 lo = lds_ld<uint4>(sl, ox0 + kk + j * 2048), hi = lds_ld<uint4>(sl, ox1 + kk + j * 2048);
+            bx[j] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+          }
           sxv[j] = lds_ld<float>(sl, osx + kk + j * 256);
         }
 #pragma unroll
@@ -1198,37 +1218,65 @@ __device__ __forceinline__ void decode_dma_body(const GemmArgs& a) {
 
   // slot s lives in r0 for even s, r1 for odd s; slot s + 1 is loaded while
   // slot s is multiplied
-  if (ns > 0) issue(r0, 0);
+  if (ns > 0) issue(r0, xa, 0);
   for (int s0 = 0; s0 < ns; s0 += 2) {
-    issue(r1, s0 + 1);
+    issue(r1, xb, s0 + 1);
     wait_vmcnt<C::L>();
-    compute(r0, s0);
+    compute(r0, xa, s0);
     if (s0 + 1 < ns) {
-      issue(r0, s0 + 2);
+      issue(r0, xa, s0 + 2);
       wait_vmcnt<C::L>();
-      compute(r1, s0 + 1);
+      compute(r1, xb, s0 + 1);
     }
   }
   wait_vmcnt<0>();
-  __syncthreads();
-  float4* red = reinterpret_cast<float4*>(r0);    // [DEC_WAVES][RB * MT][64]
+  if constexpr (DEC_WAVES * RB * MT * 64 * 16 <= C::ARR) {   // all partial tiles at once, in r0
+    __syncthreads();
+    float4* red = reinterpret_cast<float4*>(r0);    // [DEC_WAVES][RB * MT][64]
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-    for (int j = 0; j < MT; ++j)
-      red[(wave * RB * MT + rb * MT + j) * 64 + l] = make_float4(acc[rb][j][0], acc[rb][j][1], acc[rb][j][2], acc[rb][j][3]);
-  __syncthreads();
-  for (int q = t; q < RB * MT * 64; q += 512) {
-    const int s = q >> 6, ll = q & 63, rb = s / MT, j = s % MT;
-    float4 v4 = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int j = 0; j < MT; ++j)
+        red[(wave * RB * MT + rb * MT + j) * 64 + l] =
+            make_float4(acc[rb][j][0], acc[rb][j][1], acc[rb][j][2], acc[rb][j][3]);
+    __syncthreads();
+    for (int q = t; q < RB * MT * 64; q += 512) {
+      const int s = q >> 6, ll = q & 63, rb = s / MT, j = s % MT;
+      float4 v4 = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int w = 0; w < DEC_WAVES; ++w) {
-      const float4 v = red[(w * RB * MT + s) * 64 + ll];
-      v4.x += v.x; v4.y += v.y; v4.z += v.z; v4.w += v.w;
+      for (int w = 0; w < DEC_WAVES; ++w) {
+        const float4 v = red[(w * RB * MT + s) * 64 + ll];
+        v4.x += v.x; v4.y += v.y; v4.z += v.z; v4.w += v.w;
+      }
+      const v4f out = {v4.x, v4.y, v4.z, v4.w};
+      store_quad<OUT_BF16, OUT_T>(a, (int64_t)j * 16 + (ll & 15), n0 + 16 * rb + 4 * (ll >> 4),
+                                  with_bias(a, n0 + 16 * rb + 4 * (ll >> 4), out));
     }
-    const v4f out = {v4.x, v4.y, v4.z, v4.w};
-    store_quad<OUT_BF16, OUT_T>(a, (int64_t)j * 16 + (ll & 15), n0 + 16 * rb + 4 * (ll >> 4),
-                                with_bias(a, n0 + 16 * rb + 4 * (ll >> 4), out));
+    return;
+  }
+  // otherwise waves 0-3 hand their partial tiles over in r0, waves 4-7 in r1,
+  // one sub-tile column j at a time: [4][RB][64] float4 each
+  static_assert(4 * RB * 64 * 16 <= C::ARR, "LDS");
+  float4* const mine = reinterpret_cast<float4*>(wave < 4 ? r0 : r1) + (wave & 3) * RB * 64;
+#pragma unroll
+  for (int j = 0; j < MT; ++j) {
+    __syncthreads();
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+      mine[rb * 64 + l] = make_float4(acc[rb][j][0], acc[rb][j][1], acc[rb][j][2], acc[rb][j][3]);
+    __syncthreads();
+    for (int q = t; q < RB * 64; q += 512) {
+      const int rb = q >> 6, ll = q & 63;
+      float4 v4 = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int w = 0; w < DEC_WAVES; ++w) {
+        const float4 v = reinterpret_cast<const float4*>(w < 4 ? r0 : r1)[((w & 3) * RB + rb) * 64 + ll];
+        v4.x += v.x; v4.y += v.y; v4.z += v.z; v4.w += v.w;
+      }
+      const v4f out = {v4.x, v4.y, v4.z, v4.w};
+      store_quad<OUT_BF16, OUT_T>(a, (int64_t)j * 16 + (ll & 15), n0 + 16 * rb + 4 * (ll >> 4),
+                                  with_bias(a, n0 + 16 * rb + 4 * (ll >> 4), out));
+    }
   }
 }
 #endif  // SG_DEVICE_PASS
@@ -1299,7 +1347,7 @@ static bool try_decode_dma(const GemmArgs& a, hipStream_t st, int64_t rows16) {
 template <bool SPARSE, bool I8, bool PACKED, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
 static void launch_decode_mt(const GemmArgs& a, hipStream_t st) {
   const int64_t rows16 = cdiv(a.N, 16);
-  if constexpr (SPARSE && PACKED && GRAN_N == 128 && DmaCfg<1, MT>::FITS) {
+  if constexpr (SPARSE && PACKED && GRAN_N == 128) {
     if (try_decode_dma<I8, 4, MT, GRAN_N, OUT_BF16, OUT_T>(a, st, rows16) ||
         try_decode_dma<I8, 2, MT, GRAN_N, OUT_BF16, OUT_T>(a, st, rows16) ||
         try_decode_dma<I8, 1, MT, GRAN_N, OUT_BF16, OUT_T>(a, st, rows16))
@@ -1613,19 +1661,21 @@ static bool try_grouped_decode(const GemmArgs& a, const GroupTable& gt, hipStrea
   return false;
 }
 
+// False when no ring fits (nothing launched).
 template <int MT, bool OUT_BF16, bool OUT_T>
-static void launch_grouped_decode_mt(const GemmArgs& a, const GroupTable& gt, hipStream_t st) {
+static bool launch_grouped_decode_mt(const GemmArgs& a, const GroupTable& gt, hipStream_t st) {
   const int64_t rows16 = cdiv(a.N, 16);
-  (void)(try_grouped_decode<4, MT, OUT_BF16, OUT_T>(a, gt, st, rows16) ||
+  return try_grouped_decode<4, MT, OUT_BF16, OUT_T>(a, gt, st, rows16) ||
          try_grouped_decode<2, MT, OUT_BF16, OUT_T>(a, gt, st, rows16) ||
-         try_grouped_decode<1, MT, OUT_BF16, OUT_T>(a, gt, st, rows16));
+         try_grouped_decode<1, MT, OUT_BF16, OUT_T>(a, gt, st, rows16);
 }
 
 template <bool OUT_BF16, bool OUT_T>
-static void launch_grouped_decode(const GemmArgs& a, const GroupTable& gt, int64_t mmax, hipStream_t st) {
-  if (mmax <= 16) launch_grouped_decode_mt<1, OUT_BF16, OUT_T>(a, gt, st);
-  else if (mmax <= 32) launch_grouped_decode_mt<2, OUT_BF16, OUT_T>(a, gt, st);
-  else launch_grouped_decode_mt<3, OUT_BF16, OUT_T>(a, gt, st);
+static bool launch_grouped_decode(const GemmArgs& a, const GroupTable& gt, int64_t mmax, hipStream_t st) {
+  if (mmax <= 16) return launch_grouped_decode_mt<1, OUT_BF16, OUT_T>(a, gt, st);
+  if (mmax <= 32) return launch_grouped_decode_mt<2, OUT_BF16, OUT_T>(a, gt, st);
+  if (mmax <= 48) return launch_grouped_decode_mt<3, OUT_BF16, OUT_T>(a, gt, st);
+  return launch_grouped_decode_mt<4, OUT_BF16, OUT_T>(a, gt, st);
 }
 
 extern "C" sg_status sg_fp8_sparse24_gemm_groupwise_packed_grouped(
@@ -1671,20 +1721,18 @@ extern "C" sg_status sg_fp8_sparse24_gemm_groupwise_packed_grouped(
   const bool bf16 = y_dt == SG_BF16, yt = form == SG_OUT_YT;
   int64_t mmax = 0;
   for (int g = 0; g < G; ++g) mmax = std::max(mmax, m_sizes[g]);
-  if (gran_n == 128 && mmax <= 48) {   // decode-sized groups: the LDS-streaming decode kernel
-    if (bf16) {
-      if (yt) launch_grouped_decode<true, true>(a, gt, mmax, stream);
-      else launch_grouped_decode<true, false>(a, gt, mmax, stream);
-    } else {
-      if (yt) launch_grouped_decode<false, true>(a, gt, mmax, stream);
-      else launch_grouped_decode<false, false>(a, gt, mmax, stream);
-    }
-  } else if (sx_sk == 0 && sw_sk == 0) {
-    launch_grouped_form<0>(a, gt, bf16, yt, stream);
-  } else if (gran_n == 128) {
-    launch_grouped_form<128>(a, gt, bf16, yt, stream);
-  } else {
-    launch_grouped_form<1>(a, gt, bf16, yt, stream);
+  // decode-sized groups: the LDS-streaming decode kernel where one of its rings fits
+  bool done = false;
+  if (gran_n == 128 && mmax <= 64) {
+    if (bf16) done = yt ? launch_grouped_decode<true, true>(a, gt, mmax, stream)
+                        : launch_grouped_decode<true, false>(a, gt, mmax, stream);
+    else done = yt ? launch_grouped_decode<false, true>(a, gt, mmax, stream)
+                   : launch_grouped_decode<false, false>(a, gt, mmax, stream);
+  }
+  if (!done) {
+    if (sx_sk == 0 && sw_sk == 0) launch_grouped_form<0>(a, gt, bf16, yt, stream);
+    else if (gran_n == 128) launch_grouped_form<128>(a, gt, bf16, yt, stream);
+    else launch_grouped_form<1>(a, gt, bf16, yt, stream);
   }
   return launch_status();
 }

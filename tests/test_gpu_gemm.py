@@ -166,10 +166,11 @@ def test_packed_decode_shapes(m, n, k):
     check(True, m, n, k, seed=4, forms=("y", "yt"), packed=True)
 
 
-# Decode-sized M with N large enough that a workgroup owns 4 (M <= 16) or 2
-# (M <= 48) row blocks of 16 and the last workgroup is partly past N; K of
-# 384 leaves 5 of the 8 waves without a K block.
-@pytest.mark.parametrize("m,n", [(16, 14350), (9, 14400), (37, 7190), (30, 7200)])
+# Decode-sized M with N large enough that a workgroup owns 4 or 2 row blocks
+# of 16 and the last workgroup is partly past N (M > 16: X in registers, up to
+# four 16-row sub-tiles); K of 384 leaves 5 of the 8 waves without a K block.
+@pytest.mark.parametrize("m,n", [(16, 14350), (9, 14400), (37, 7190), (30, 7200), (37, 14350), (64, 14350),
+                                 (50, 7200), (17, 14336)])
 def test_packed_decode_ragged_row_blocks(m, n):
     check(True, m, n, 384, seed=13 + m, packed=True)
 

@@ -371,7 +371,8 @@ def grouped_operands(sizes, n, k, seed, gn=128):
                                                ([1, 0, 17, 48, 33], "yt", torch.bfloat16, 128),
                                                ([16, 16, 3, 9], "y", torch.float32, 128),
                                                ([20, 32], "y", torch.bfloat16, 128),
-                                               ([7, 40], "yt", torch.float32, 128)])
+                                               ([7, 40], "yt", torch.float32, 128),
+                                               ([64, 0, 49, 3], "y", torch.bfloat16, 128)])
 def test_grouped(sizes, form, out, gn):
     n, k = 384, 512
     say(f"grouped sizes={sizes} N={n} K={k} form={form} {out} gn={gn}")
@@ -394,10 +395,11 @@ def test_grouped(sizes, form, out, gn):
         r += mg
 
 
-@pytest.mark.parametrize("sizes,form", [([5, 16, 1, 12, 0, 16, 7, 2], "y"), ([3, 9], "yt")])
+@pytest.mark.parametrize("sizes,form", [([5, 16, 1, 12, 0, 16, 7, 2], "y"), ([3, 9], "yt"),
+                                        ([64, 33, 0, 20, 64, 1, 40, 9], "yt")])
 def test_grouped_decode_wide(sizes, form):
     """MoE decode: many small groups over a wide weight (four row blocks per
-    workgroup for the 8-group case, one for the 2-group case)."""
+    workgroup for the 8-group and the 64-row cases, one for the 2-group case)."""
     n, k = 4096, 1024
     say(f"grouped decode sizes={sizes} N={n} K={k} form={form}")
     xq, sx, ws = grouped_operands(sizes, n, k, seed=130 + len(sizes))
