@@ -194,6 +194,20 @@ def rows_report():
             out[f"decode_M{dm}_N{dn}_K{dk}_{form}"] = {"ms": ms, "GB/s": b / ms / 1e6,
                                                      "frac_hbm": b / ms / 1e6 / PEAK_HBM_GBS}
         del wsets
+    # one GPU's share of an 8-way tensor-parallel layer (column-parallel
+    # up-projection N = 14336 / 8, bf16 out; row-parallel down-projection
+    # K = 14336 / 8, fp32 partial out), 64 weight copies (> 256 MB MALL)
+    for (dm, dn, dk, odt) in ((16, 1792, 4096, torch.bfloat16), (16, 4096, 1792, torch.float32)):
+        wsets = [gen_layer(2500 + i, 8, dn, dk, on_gpu_rng=True)[3:] for i in range(64)]
+        xdd = torch.from_numpy(workloads.decode(seed=4, m=dm, n=8, k=dk)["x"]).to(DEV)
+        xq4, sx4 = sg.fp8_quant_groupwise(xdd)
+        y = torch.empty((dm, dn), dtype=odt, device=DEV)
+        ms = time_fn(lambda i: sg.fp8_sparse24_gemm_groupwise_packed(
+            xq4, sx4, wsets[i % 64][1], dn, wsets[i % 64][0], 1, 128, y=y), reps=128, warm=64)
+        b = sparse_bytes(dm, dn, dk, out_bytes=2 if odt == torch.bfloat16 else 4)
+        out[f"tp8_share_decode_M{dm}_N{dn}_K{dk}_y"] = {"ms": ms, "GB/s": b / ms / 1e6,
+                                                       "frac_hbm": b / ms / 1e6 / PEAK_HBM_GBS}
+        del wsets
     # next row: int8 x int8 2:4 GEMM, packed weight, 2048x4096x4096 and the M=16 decode shape
     d = workloads.sparse_large(seed=3, m=m, n=n, k=k)
     wv8, mt8 = sg.sparse24_prune_compress(torch.from_numpy(d["w"]).to(DEV))

@@ -175,6 +175,16 @@ def test_packed_decode_ragged_row_blocks(m, n):
     check(True, m, n, 384, seed=13 + m, packed=True)
 
 
+# One GPU's share of an 8-way tensor-parallel decode layer: the column-parallel
+# up-projection (N = 14336 / 8 rows of W) and the row-parallel
+# down-projection's partial product (K = 14336 / 8), fp32 as an all-reduce
+# would sum it before the bf16 rounding.
+@pytest.mark.parametrize("m,n,k,out", [(16, 1792, 4096, torch.bfloat16), (16, 4096, 1792, torch.float32),
+                                       (37, 1792, 4096, torch.bfloat16)])
+def test_packed_tensor_parallel_share_shapes(m, n, k, out):
+    check(True, m, n, k, out_dtype=out, seed=5 + m, packed=True)
+
+
 def test_packed_fp32_row_major_scales_and_equal_to_unpacked():
     d = workloads.sparse_large(seed=21, m=300, n=700, k=512)
     xq, sx, wq, meta, sw = oracle_operands(d["x"], d["w"], 1, 128, True)
