@@ -481,6 +481,196 @@ static bool try_w8_dma(const W8Args& a, hipStream_t st, int64_t rows16) {
   return false;
 }
 
+// --------------------------------------------------------------- large M
+// Workgroup tile 256 W rows (n) x 128 X rows (m), 8 waves in a 4 (n) x 2 (m)
+// grid, each wave 64 x 64 = 4 x 4 sub-tiles, so every X fragment a wave reads
+// serves four W row blocks and every widened W fragment four X sub-tiles.
+// One 128-wide K block per LDS stage, two stages: all waves multiply stage kb
+// while stage kb + 1 streams in through buffer loads that write LDS; one
+// barrier per K block.  Stage layout (bytes; swizzles keep the fragment reads
+// free of bank conflicts):
+//   X    : 128 rows x 256 B (bf16); 16-byte chunk c of row r at chunk c ^ (r & 15)
+//   W    : 256 rows x 64 B of codes (int4: 32 B); 16-byte unit u of row r at
+//          u ^ ((r >> 2) & 3) (int4: u ^ ((r >> 3) & 1))
+//   meta : 256 rows x 16 B
+//   sw   : 256 floats, the scale of each W row for the K block (its 128-row
+//          block's with 128-row scales); rows past N read row N - 1's
+namespace w8t {
+constexpr int BN = 256, BM = 128;
+constexpr int MIN_TILES = 192;   // below this the decode-shaped kernel keeps more CUs busy
+template <int CODES>
+struct Lay {
+  static constexpr int WROW = CODES == C_I4 ? 32 : 64;
+  static constexpr int X_OFF = 0;
+  static constexpr int W_OFF = BM * 256;
+  static constexpr int M_OFF = W_OFF + BN * WROW;
+  static constexpr int S_OFF = M_OFF + BN * 16;
+  static constexpr int BYTES = S_OFF + BN * 4;
+};
+}  // namespace w8t
+
+#if SG_DEVICE_PASS
+template <int CODES, int GRAN_N>
+__device__ __forceinline__ void w8t_issue(uint8_t* st, const W8Args& a, __amdgpu_buffer_rsrc_t rx,
+                                          __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t rm,
+                                          __amdgpu_buffer_rsrc_t rsw, int64_t n0, int kb, int wave, int l) {
+  using L = w8t::Lay<CODES>;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {   // X: 2048 units of 16 B, unit p at LDS 16 p
+    const int s = 8 * i + wave, p = 64 * s + l, r = p >> 4, c = (p & 15) ^ (r & 15);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (w8_lds_t*)(st + L::X_OFF + s * 1024), 16,
+                                             (uint32_t)(r * a.ldx * 2 + c * 16), kb * 256, 0, 0);
+  }
+  if constexpr (CODES == C_I4) {   // 512 units: row p >> 1, stored unit p & 1
+    const int p = 64 * wave + l, r = p >> 1, u = (p & 1) ^ ((r >> 3) & 1);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (w8_lds_t*)(st + L::W_OFF + wave * 1024), 16,
+                                             (uint32_t)(r * a.ldw + u * 16), kb * 32, 0, 0);
+  } else {                         // 1024 units: row p >> 2, stored unit p & 3
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int s = 8 * i + wave, p = 64 * s + l, r = p >> 2, u = (p & 3) ^ ((r >> 2) & 3);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (w8_lds_t*)(st + L::W_OFF + s * 1024), 16,
+                                               (uint32_t)(r * a.ldw + u * 16), kb * 64, 0, 0);
+    }
+  }
+  if (wave < 4) {   // metadata: row 64 wave + l
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rm, (w8_lds_t*)(st + L::M_OFF + wave * 1024), 16,
+                                             (uint32_t)((64 * wave + l) * a.ldm), kb * 16, 0, 0);
+  } else {          // W scales: row 64 (wave - 4) + l
+    const int64_t n = min(n0 + 64 * (wave - 4) + l, a.N - 1);
+    const int64_t row = GRAN_N == 128 ? (n >> 7) : n;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, (w8_lds_t*)(st + L::S_OFF + (wave - 4) * 256), 4,
+                                             (uint32_t)(row * a.sw_sn * 4), (int)(kb * a.sw_sk * 4), 0, 0);
+  }
+}
+
+// Multiplies one stage into the wave's 4 x 4 sub-tiles and promotes each
+// K block's partial with its W scale.
+template <int CODES, int GRAN_N>
+__device__ __forceinline__ void w8t_compute(const uint8_t* st, int wn, int wm, int g, int lr, v4f (&acc)[4][4]) {
+  using L = w8t::Lay<CODES>;
+  v8i b0[4], b1[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {   // X row wm * 64 + 16 j + lr: chunks g, g + 4 | g + 8, g + 12
+    const uint32_t row = L::X_OFF + (uint32_t)(wm * 64 + 16 * j + lr) * 256;
+    const uint4 c0 = w8_lds<uint4>(st, row + (((g) ^ lr) << 4));
+    const uint4 c1 = w8_lds<uint4>(st, row + (((g + 4) ^ lr) << 4));
+    const uint4 c2 = w8_lds<uint4>(st, row + (((g + 8) ^ lr) << 4));
+    const uint4 c3 = w8_lds<uint4>(st, row + (((g + 12) ^ lr) << 4));
+    b0[j] = (v8i){(int)c0.x, (int)c0.y, (int)c0.z, (int)c0.w, (int)c1.x, (int)c1.y, (int)c1.z, (int)c1.w};
+    b1[j] = (v8i){(int)c2.x, (int)c2.y, (int)c2.z, (int)c2.w, (int)c3.x, (int)c3.y, (int)c3.z, (int)c3.w};
+  }
+  const float swv = GRAN_N == 128 ? w8_lds<float>(st, L::S_OFF + wn * 256) : 1.f;   // the wave's 64 rows share it
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = wn * 64 + 16 * i + lr;   // W row in the tile
+    v4i cw;
+    if constexpr (CODES == C_I4) {
+      const int f = (lr >> 3) & 1;
+      cw = (v4i){w8_lds<int>(st, L::W_OFF + r * 32 + (f << 4) + 4 * g), 0,
+                 w8_lds<int>(st, L::W_OFF + r * 32 + ((1 ^ f) << 4) + 4 * g), 0};
+    } else {
+      const int f = (lr >> 2) & 3;
+      const uint2 c0 = w8_lds<uint2>(st, L::W_OFF + r * 64 + (((g >> 1) ^ f) << 4) + 8 * (g & 1));
+      const uint2 c1 = w8_lds<uint2>(st, L::W_OFF + r * 64 + (((2 + (g >> 1)) ^ f) << 4) + 8 * (g & 1));
+      cw = (v4i){(int)c0.x, (int)c0.y, (int)c1.x, (int)c1.y};
+    }
+    const uint4 m = w8_lds<uint4>(st, L::M_OFF + r * 16);
+    const v4i mv = {(int)m.x, (int)m.y, (int)m.z, (int)m.w};
+    const v4i a0 = widen8<CODES>(cw[0], cw[1]);
+    const v4i a1 = widen8<CODES>(cw[2], cw[3]);
+    const int i0 = meta_half(mv, g), i1 = meta_half(mv, g + 4);
+    float4 sw;
+    if (GRAN_N == 128) sw = make_float4(swv, swv, swv, swv);
+    else sw = w8_lds<float4>(st, L::S_OFF + (wn * 64 + 16 * i + 4 * g) * 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v4f p = {0.f, 0.f, 0.f, 0.f};
+      p = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(v8bf, a0), __builtin_bit_cast(v16bf, b0[j]),
+                                                    p, i0, 0, 0);
+      p = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(v8bf, a1), __builtin_bit_cast(v16bf, b1[j]),
+                                                    p, i1, 0, 0);
+      acc[i][j][0] = fmaf(p[0], sw.x, acc[i][j][0]);
+      acc[i][j][1] = fmaf(p[1], sw.y, acc[i][j][1]);
+      acc[i][j][2] = fmaf(p[2], sw.z, acc[i][j][2]);
+      acc[i][j][3] = fmaf(p[3], sw.w, acc[i][j][3]);
+    }
+  }
+}
+#endif  // SG_DEVICE_PASS
+
+template <int CODES, int GRAN_N, bool OUT_BF16, bool OUT_T>
+__global__ void __launch_bounds__(512) k_gemm_w8a16_tile(W8Args a, int tiles_m, int tiles_n) {
+#if SG_DEVICE_PASS
+  using L = w8t::Lay<CODES>;
+  __shared__ __attribute__((aligned(1024))) uint8_t s0[L::BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t s1[L::BYTES];
+  int tn, tm;
+  tile_coords(tiles_m, tiles_n, tn, tm);
+  const int64_t n0 = (int64_t)tn * w8t::BN, m0 = (int64_t)tm * w8t::BM;
+  const int t = threadIdx.x, l = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wn = wave & 3, wm = wave >> 2;
+  const int g = l >> 4, lr = l & 15;
+  const int KB = (int)(a.K >> 7);
+  // rows past M or N read as zero (resources sized to the rows that exist)
+  const int64_t mrows = min((int64_t)w8t::BM, a.M - m0), nrows = min((int64_t)w8t::BN, a.N - n0);
+  const __amdgpu_buffer_rsrc_t rx = w8_rsrc(a.x + m0 * a.ldx, (uint32_t)(mrows * a.ldx * 2));
+  const __amdgpu_buffer_rsrc_t rw = w8_rsrc(a.w + n0 * a.ldw, (uint32_t)(nrows * a.ldw));
+  const __amdgpu_buffer_rsrc_t rm = w8_rsrc(a.meta + n0 * a.ldm, (uint32_t)(nrows * a.ldm));
+  const __amdgpu_buffer_rsrc_t rsw = w8_rsrc(a.sw, 0xffffffffu);
+
+  v4f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+  // K block kb lives in s0 for even kb, s1 for odd kb; a wave's only loads in
+  // flight at each wait are the next stage's, and the barrier after it also
+  // tells every wave that the stage it is about to overwrite has been read
+  w8t_issue<CODES, GRAN_N>(s0, a, rx, rw, rm, rsw, n0, 0, wave, l);
+  wait_vmcnt<0>();
+  __syncthreads();
+  for (int kb = 0; kb < KB; kb += 2) {
+    if (kb + 1 < KB) w8t_issue<CODES, GRAN_N>(s1, a, rx, rw, rm, rsw, n0, kb + 1, wave, l);
+    w8t_compute<CODES, GRAN_N>(s0, wn, wm, g, lr, acc);
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (kb + 1 < KB) {
+      if (kb + 2 < KB) w8t_issue<CODES, GRAN_N>(s0, a, rx, rw, rm, rsw, n0, kb + 2, wave, l);
+      w8t_compute<CODES, GRAN_N>(s1, wn, wm, g, lr, acc);
+      wait_vmcnt<0>();
+      __syncthreads();
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t n = n0 + wn * 64 + 16 * i + 4 * g;
+      v4f out = acc[i][j];
+      if (a.bias) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[e] += a.bias[min(n + e, a.N - 1)];
+      }
+      store_quad<OUT_BF16, OUT_T>(a, m0 + wm * 64 + 16 * j + lr, n, out);
+    }
+#endif  // SG_DEVICE_PASS
+}
+
+// The large-M tile kernel when its tiles fill most of the chip and its 32-bit
+// per-tile buffer offsets hold.
+template <int CODES, int GRAN_N, bool OUT_BF16, bool OUT_T>
+static bool try_w8_tile(const W8Args& a, hipStream_t st) {
+  const int64_t tm = cdiv(a.M, w8t::BM), tn = cdiv(a.N, w8t::BN);
+  if (tm * tn < w8t::MIN_TILES || tm * tn > 0x7fffffffLL || a.ldx >= (1LL << 22) || a.ldw >= (1LL << 23) ||
+      a.ldm >= (1LL << 23))
+    return false;
+  k_gemm_w8a16_tile<CODES, GRAN_N, OUT_BF16, OUT_T><<<(unsigned)(tm * tn), 512, 0, st>>>(a, (int)tm, (int)tn);
+  return true;
+}
+
 // Row blocks per workgroup: the largest of 4 (2 for MT > 2), 2, 1 that keeps
 // at least 224 workgroups.  Every workgroup reads its X rows in full, so
 // fewer, taller workgroups read X fewer times (measured at M = 37 and 64:
@@ -506,6 +696,7 @@ static void launch_w8_mt(const W8Args& a, hipStream_t st) {
 
 template <int CODES, int GRAN_N, bool OUT_BF16, bool OUT_T>
 static void launch_w8_shape(const W8Args& a, hipStream_t st) {
+  if (a.M > 64 && try_w8_tile<CODES, GRAN_N, OUT_BF16, OUT_T>(a, st)) return;
   if (a.M <= 16) launch_w8_mt<CODES, 1, GRAN_N, OUT_BF16, OUT_T>(a, st);
   else if (a.M <= 32) launch_w8_mt<CODES, 2, GRAN_N, OUT_BF16, OUT_T>(a, st);
   else if (a.M <= 48) launch_w8_mt<CODES, 3, GRAN_N, OUT_BF16, OUT_T>(a, st);

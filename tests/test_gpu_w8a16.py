@@ -84,6 +84,32 @@ def test_w8a16_two_row_blocks_ragged_last():
     check(32, 7208, 512, out=torch.float32, bias=True, seed=25)
 
 
+# Large M: the 256 x 128 tile kernel (taken from 192 tiles on), with the last
+# tiles partly past M and N.
+@pytest.mark.parametrize("int8", [False, True])
+def test_w8a16_large_m_tiles(int8):
+    check(1000, 12300, 256, int8=int8, seed=60 + int8)
+
+
+def test_w8a16_large_m_per_row_scales_fp32_bias_single_k_block():
+    check(300, 24580, 128, gn=1, out=torch.float32, bias=True, seed=62)
+
+
+@pytest.mark.parametrize("int8", [False, True])
+def test_w8a16_large_m_full_size_sampled_rows(int8):
+    """2048 x 4096 x 4096 (the benchmark's shape) on the tile kernel; the
+    oracle computes a sample of rows from every kind of tile position."""
+    m, n, k = 2048, 4096, 4096
+    say(f"w8a16 full size M={m} N={n} K={k} int8={int8}")
+    x, wv, meta, sw = operands(m, n, k, 128, int8, seed=64 + int8)
+    got = down(sg.w8a16_sparse24_gemm_groupwise(x, up(wv), up(meta), up(sw), 128))
+    rows = np.array([0, 1, 63, 64, 127, 128, 1000, 1919, 2047])
+    xbits = x.view(torch.int16).cpu().numpy().view(np.uint16)[rows]
+    ref, bound = oracle.w8a16_sparse24_gemm_groupwise(xbits, wv, meta, sw, 128, "int8" if int8 else "e4m3",
+                                                      bound=True)
+    assert_within_tolerance(got[rows].astype(np.float64), ref, bound, "sampled rows")
+
+
 def test_w8a16_from_the_gpu_weight_pipeline():
     """GPU prune + compress + int8 / e4m3 quantisation of a weight, then the
     weight-only GEMM, against the oracle's chain."""
@@ -143,6 +169,10 @@ def test_w4a16_decode_full_size():
 
 def test_w4a16_decode_m37_full_size():
     check_w4(37, 14336, 4096, forms=("y",), seed=43)
+
+
+def test_w4a16_large_m_tiles():
+    check_w4(1000, 12300, 256, seed=63)
 
 
 def test_w4a16_from_the_gpu_weight_pipeline():
