@@ -70,19 +70,18 @@ __device__ __forceinline__ int w8_ld4(__amdgpu_buffer_rsrc_t r, uint32_t off, in
 }
 
 // bf16 bits of the two codes in the low (HI = false) or high half of w,
-// first code in the low 16 bits.  Both conversions are exact.
+// first code in the low 16 bits.  Both conversions are exact: e4m3 goes
+// through gfx950's scaled fp8 -> bf16 pair conversion with scale 1 (every
+// e4m3 value, subnormals included, is a bf16 value).
 template <bool I8, bool HI>
 __device__ __forceinline__ uint32_t bf16_pair(uint32_t w) {
-  float f0, f1;
   if constexpr (I8) {
-    f0 = (float)(int)(int8_t)(w >> (HI ? 16 : 0));
-    f1 = (float)(int)(int8_t)(w >> (HI ? 24 : 8));
+    const float f0 = (float)(int)(int8_t)(w >> (HI ? 16 : 0));
+    const float f1 = (float)(int)(int8_t)(w >> (HI ? 24 : 8));
+    return (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xffff0000u);
   } else {
-    const auto f = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
-    f0 = f[0];
-    f1 = f[1];
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
   }
-  return (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xffff0000u);
 }
 
 __device__ __forceinline__ v2i w8_ld8(__amdgpu_buffer_rsrc_t r, uint32_t off, int soff) {
@@ -395,11 +394,11 @@ __global__ void __launch_bounds__(512) k_gemm_w8a16_dma(W8Args a) {
         const uint2 c1 = w8_lds<uint2>(sl, rb * D::CB + lr * 64 + 32 + 8 * g);
         cw = (v4i){(int)c0.x, (int)c0.y, (int)c1.x, (int)c1.y};
       }
-      const uint4 m = w8_lds<uint4>(sl, D::MOFF + rb * 256 + lr * 16);
-      const v4i mv = {(int)m.x, (int)m.y, (int)m.z, (int)m.w};
+      // index words: halfwords g and g + 4 of the row's 16 metadata bytes
+      const int i0 = w8_lds<uint16_t>(sl, D::MOFF + rb * 256 + lr * 16 + 2 * g);
+      const int i1 = w8_lds<uint16_t>(sl, D::MOFF + rb * 256 + lr * 16 + 8 + 2 * g);
       const v4i a0 = widen8<CODES>(cw[0], cw[1]);
       const v4i a1 = widen8<CODES>(cw[2], cw[3]);
-      const int i0 = meta_half(mv, g), i1 = meta_half(mv, g + 4);
       float4 sw;
       if (GRAN_N == 128) {
         const float v = w8_lds<float>(sl, D::SWOFF + rb * 4);
@@ -575,11 +574,11 @@ __device__ __forceinline__ void w8t_compute(const uint8_t* st, int wn, int wm, i
       const uint2 c1 = w8_lds<uint2>(st, L::W_OFF + r * 64 + (((2 + (g >> 1)) ^ f) << 4) + 8 * (g & 1));
       cw = (v4i){(int)c0.x, (int)c0.y, (int)c1.x, (int)c1.y};
     }
-    const uint4 m = w8_lds<uint4>(st, L::M_OFF + r * 16);
-    const v4i mv = {(int)m.x, (int)m.y, (int)m.z, (int)m.w};
+    // index words: halfwords g and g + 4 of the row's 16 metadata bytes
+    const int i0 = w8_lds<uint16_t>(st, L::M_OFF + r * 16 + 2 * g);
+    const int i1 = w8_lds<uint16_t>(st, L::M_OFF + r * 16 + 8 + 2 * g);
     const v4i a0 = widen8<CODES>(cw[0], cw[1]);
     const v4i a1 = widen8<CODES>(cw[2], cw[3]);
-    const int i0 = meta_half(mv, g), i1 = meta_half(mv, g + 4);
     float4 sw;
     if (GRAN_N == 128) sw = make_float4(swv, swv, swv, swv);
     else sw = w8_lds<float4>(st, L::S_OFF + (wn * 64 + 16 * i + 4 * g) * 4);
