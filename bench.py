@@ -335,7 +335,15 @@ def rows_report():
     ms = time_fn(lambda i: sg.w8a16_sparse24_gemm_groupwise(xb, wq8, mt8, sw8, 128, y=y), reps=10, warm=2)
     out["next_w8a16_e4m3_gemm_2048x4096x4096_y"] = {"ms": ms, "TFLOP/s": flops / ms / 1e9,
                                                     "frac_bf16_peak": flops / ms / 1e9 / PEAK_BF16_TFLOPS}
-    del xb, wv8, mt8, wq8
+    wq8, sw8 = sg.int8_quant_groupwise(wv8, gr=128, gc=64)
+    ms = time_fn(lambda i: sg.w8a16_sparse24_gemm_groupwise(xb, wq8, mt8, sw8, 128, y=y), reps=10, warm=2)
+    out["next_w8a16_int8_gemm_2048x4096x4096_y"] = {"ms": ms, "TFLOP/s": flops / ms / 1e9,
+                                                    "frac_bf16_peak": flops / ms / 1e9 / PEAK_BF16_TFLOPS}
+    q4, s4 = sg.int4_quant_groupwise(wv8, gc=64)
+    ms = time_fn(lambda i: sg.w4a16_sparse24_gemm_groupwise(xb, q4, mt8, s4, y=y), reps=10, warm=2)
+    out["next_w4a16_gemm_2048x4096x4096_y"] = {"ms": ms, "TFLOP/s": flops / ms / 1e9,
+                                               "frac_bf16_peak": flops / ms / 1e9 / PEAK_BF16_TFLOPS}
+    del xb, wv8, mt8, wq8, q4, s4
     # a7: fused int4 + bf16 add at L=2048, D1=4096, D2=64, D=4096
     dd = workloads.mixed_add(seed=5)
     x1, sx1 = sg.int4_quant_groupwise(torch.from_numpy(dd["x1"]).to(DEV))

@@ -78,7 +78,8 @@ __device__ __forceinline__ uint32_t bf16_pair(uint32_t w) {
   if constexpr (I8) {
     const float f0 = (float)(int)(int8_t)(w >> (HI ? 16 : 0));
     const float f1 = (float)(int)(int8_t)(w >> (HI ? 24 : 8));
-    return (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xffff0000u);
+    // high halves of f0 (low 16 bits) and f1 (high 16 bits)
+    return __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
   } else {
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
   }
@@ -99,7 +100,7 @@ __device__ __forceinline__ v4i widen8(int w0, int w1) {
       // the builtin's result type is unsigned: convert it as the signed value it holds
       const float f0 = (float)(int)__builtin_amdgcn_sbfe(w0, 8 * q, 4);
       const float f1 = (float)(int)__builtin_amdgcn_sbfe(w0, 8 * q + 4, 4);
-      d[q] = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xffff0000u);
+      d[q] = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
     }
     return (v4i){(int)d[0], (int)d[1], (int)d[2], (int)d[3]};
   } else {
