@@ -525,8 +525,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build runs every kernel on a single MI355X "
-              "and has no multi-GPU path (see how it would shard in the design notes). Use --gpus 1.",
+        print("bench.py measures one GPU only: the library runs every kernel on a single MI355X "
+              "and has no multi-GPU path. Use --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:

@@ -17,7 +17,7 @@ of the source pages it follows; the pages are
   w4a4 + w16a16?" (CUTLASS issue #2058),
 * "Introduce new W8A8-FP-CSR quantization API" (torchao PR #3258).
 
-``pack.py`` additionally defines this build's gfx950 packed weight layout (a
+``pack.py`` additionally defines the library's own gfx950 packed weight layout (a
 byte permutation of the compressed values and metadata).
 
 Parity status: every public function here is pinned by a ``-m "not gpu"`` test
