@@ -30,6 +30,8 @@
 //          of the row's 16 metadata bytes (nibble order unchanged).
 //          B column l%16, k = 32 g + byte.
 //   result: lane l holds D[4 g + i][l % 16], i = 0..3.
+#include <atomic>
+
 #include "tile_epilogue.h"
 
 namespace sg {
@@ -509,14 +511,16 @@ __global__ void __launch_bounds__(512) k_gemm_sparse_x2(GemmArgs a, int tiles_m,
 }
 
 // Grouped problems (different M per group, one packed weight per group): the
-// groups' rows follow each other in X, in the scales of X and in Y; group g
-// owns the m tiles of rows row_off[g] .. row_off[g + 1] - 1, numbered from
+// groups' rows follow each other in X, in the scales of X and in Y; a launch
+// covers rows row_off[g] .. row_end[g] - 1 of group g (all of them, or the
+// part its kernel takes), the large-M kernel as m tiles numbered from
 // tile_start[g] (tiles_n n tiles per m tile).
 constexpr int MAX_GROUPS = 64;
 struct GroupTable {
   int G, tiles_n;
   int tile_start[MAX_GROUPS + 1];
   int64_t row_off[MAX_GROUPS + 1];
+  int64_t row_end[MAX_GROUPS];
 };
 
 template <bool I8, bool PACKED, int GRAN_N, bool OUT_BF16, bool OUT_T>
@@ -529,7 +533,7 @@ __global__ void __launch_bounds__(512) k_gemm_sparse_x2_grouped(GemmArgs a, Grou
   int tn, tm;
   tile_of(b - gt.tile_start[g], tiles_m, gt.tiles_n, tn, tm);
   const int64_t r0 = gt.row_off[g];
-  a.M = gt.row_off[g + 1] - r0;
+  a.M = gt.row_end[g] - r0;
   a.x += r0 * a.ldx;
   a.sx += r0 * a.sx_sm;
   a.y = static_cast<uint8_t*>(a.y) + (OUT_T ? r0 : r0 * a.ldy) * (OUT_BF16 ? 2 : 4);
@@ -973,9 +977,9 @@ __device__ __forceinline__ void dec_compute(const DecOps<RB, MT>& o, v4f (&acc)[
 
 template <bool SPARSE, bool I8, bool PACKED, int RB, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
 __global__ void __launch_bounds__(512) k_gemm_decode(GemmArgs a) {
+#if SG_DEVICE_PASS
   constexpr int U = DEC_U;
   __shared__ __attribute__((aligned(16))) float red[DEC_WAVES][RB * MT][64][4];
-#if SG_DEVICE_PASS
   to_batch(a);
   const int t = threadIdx.x, l = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -1298,7 +1302,7 @@ __global__ void __launch_bounds__(512) k_gemm_decode_dma_grouped(GemmArgs a, Gro
 #if SG_DEVICE_PASS
   const int g = blockIdx.y;
   const int64_t r0 = gt.row_off[g];
-  a.M = gt.row_off[g + 1] - r0;
+  a.M = gt.row_end[g] - r0;
   if (a.M == 0) return;
   a.x += r0 * a.ldx;
   a.sx += r0 * a.sx_sm;
@@ -1678,6 +1682,27 @@ static bool launch_grouped_decode(const GemmArgs& a, const GroupTable& gt, int64
   return launch_grouped_decode_mt<4, OUT_BF16, OUT_T>(a, gt, st);
 }
 
+// Compute units of the current device (cached per device).
+static int cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+// Whether the grouped decode kernel has a ring for groups of up to mmax rows
+// (16-row sub-tiles up to 3 always fit with one row block per workgroup; 4
+// need four row blocks and enough workgroups).
+static bool grouped_decode_fits(int64_t mmax, int64_t N, int G) {
+  if (mmax <= 48) return true;
+  return mmax <= 64 && cdiv(cdiv(N, 16), 4) * G >= 224;
+}
+
 extern "C" sg_status sg_fp8_sparse24_gemm_groupwise_packed_grouped(
     int64_t G, const int64_t* m_sizes, int64_t N, int64_t K, const uint8_t* xq, int64_t ldx, const float* sx,
     int64_t sx_sm, int64_t sx_sk, const uint8_t* wpacked, int64_t wp_bs, const float* sw, int64_t sw_sn,
@@ -1691,6 +1716,7 @@ extern "C" sg_status sg_fp8_sparse24_gemm_groupwise_packed_grouped(
   for (int g = 0; g < G; ++g) {
     if (m_sizes[g] < 0) return SG_ERR_SHAPE;
     gt.row_off[g + 1] = gt.row_off[g] + m_sizes[g];
+    gt.row_end[g] = gt.row_off[g + 1];
   }
   const int64_t M = gt.row_off[G];
   sg_status st = check_common(M, N, K, xq, ldx, sx, sx_sm, sx_sk, 1, sw, sw_sn, sw_sk, gran_n, y, y_dt, ldy, form);
@@ -1730,9 +1756,35 @@ extern "C" sg_status sg_fp8_sparse24_gemm_groupwise_packed_grouped(
                    : launch_grouped_decode<false, false>(a, gt, mmax, stream);
   }
   if (!done) {
-    if (sx_sk == 0 && sw_sk == 0) launch_grouped_form<0>(a, gt, bf16, yt, stream);
-    else if (gran_n == 128) launch_grouped_form<128>(a, gt, bf16, yt, stream);
-    else launch_grouped_form<1>(a, gt, bf16, yt, stream);
+    // Tails: a group's last rows past a multiple of 128, when there are at
+    // most 64 of them, cost the large-M kernel a whole K loop per tile.  When
+    // leaving them out saves the tiles a round over the CUs, they take the
+    // grouped decode kernel in a second launch instead (streaming their
+    // group's weight once more).
+    GroupTable gh = gt, gtail = gt;
+    int64_t tail_max = 0;
+    gh.tile_start[0] = 0;
+    for (int g = 0; g < G; ++g) {
+      const int64_t r = m_sizes[g] % BM, tail = (r > 0 && r <= 64) ? r : 0;
+      tail_max = std::max(tail_max, tail);
+      gh.row_end[g] = gt.row_off[g + 1] - tail;
+      gh.tile_start[g + 1] = gh.tile_start[g] + (int)(cdiv(gh.row_end[g] - gt.row_off[g], BM) * tiles_n);
+      gtail.row_off[g] = gt.row_off[g + 1] - tail;
+    }
+    const int cus = cu_count();
+    const bool split = gran_n == 128 && tail_max > 0 && gh.tile_start[G] > 0 &&
+                       cdiv(gh.tile_start[G], cus) < cdiv(gt.tile_start[G], cus) &&
+                       grouped_decode_fits(tail_max, N, (int)G);
+    const GroupTable& tiles = split ? gh : gt;
+    if (sx_sk == 0 && sw_sk == 0) launch_grouped_form<0>(a, tiles, bf16, yt, stream);
+    else if (gran_n == 128) launch_grouped_form<128>(a, tiles, bf16, yt, stream);
+    else launch_grouped_form<1>(a, tiles, bf16, yt, stream);
+    if (split) {
+      if (bf16) (void)(yt ? launch_grouped_decode<true, true>(a, gtail, tail_max, stream)
+                          : launch_grouped_decode<true, false>(a, gtail, tail_max, stream));
+      else (void)(yt ? launch_grouped_decode<false, true>(a, gtail, tail_max, stream)
+                     : launch_grouped_decode<false, false>(a, gtail, tail_max, stream));
+    }
   }
   return launch_status();
 }

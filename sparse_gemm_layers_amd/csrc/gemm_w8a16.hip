@@ -185,9 +185,9 @@ __device__ __forceinline__ void w8_compute(const W8Ops<RB, MT>& o, int g, v4f (&
 
 template <int CODES, int RB, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
 __global__ void __launch_bounds__(512) k_gemm_w8a16(W8Args a) {
+#if SG_DEVICE_PASS
   constexpr int U = W8_U;
   __shared__ __attribute__((aligned(16))) float red[W8_WAVES][RB * MT][64][4];
-#if SG_DEVICE_PASS
   const int t = threadIdx.x, l = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int g = l >> 4, lr = l & 15;

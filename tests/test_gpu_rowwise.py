@@ -418,6 +418,33 @@ def test_grouped_decode_wide(sizes, form):
         r += mg
 
 
+# Ragged groups whose large tiles would need a second round over the CUs:
+# each group's last <= 64 rows take the grouped decode kernel instead (tails
+# of 44 / 40 rows: three sub-tiles; tails of 64 rows: four).
+@pytest.mark.parametrize("sizes,form,out", [([300] * 6 + [40], "y", torch.bfloat16),
+                                            ([320] * 7 + [64], "yt", torch.float32),
+                                            ([0, 300, 1, 300, 300, 300, 300, 300, 44], "y", torch.bfloat16)])
+def test_grouped_tails_on_the_decode_kernel(sizes, form, out):
+    n, k = 4096, 256
+    say(f"grouped tails sizes={sizes} N={n} K={k} form={form} {out}")
+    xq, sx, ws = grouped_operands(sizes, n, k, seed=140 + len(sizes))
+    wp = torch.stack([sg.sparse24_pack_gfx950(up(wq), up(meta)) for wq, meta, _ in ws])
+    sw = torch.stack([up_m_major(s) for _, _, s in ws])
+    bias = (np.random.default_rng(141).standard_normal((len(sizes), n))).astype(np.float32)
+    got = down(sg.fp8_sparse24_gemm_groupwise_packed_grouped(up(xq), up_m_major(sx), sizes, wp, n, sw, 128,
+                                                             out_dtype=out, form=form, bias=up(bias)))
+    got = got.T if form == "yt" else got
+    r = 0
+    for g, mg in enumerate(sizes):
+        if mg:
+            wq, meta, swg = ws[g]
+            ref, bound = oracle.fp8_sparse24_gemm_groupwise(xq[r:r + mg], sx[r:r + mg], 1, wq, meta, swg, 128,
+                                                             bound=True)
+            ref, bound = oracle.add_bias(ref, bound, bias[g])
+            assert_within_tolerance(got[r:r + mg].astype(np.float64), ref, bound, f"group {g}")
+        r += mg
+
+
 def test_grouped_rowwise_scales():
     sizes, n, k = [130, 3, 257], 512, 640
     say(f"grouped rowwise sizes={sizes} N={n} K={k}")
