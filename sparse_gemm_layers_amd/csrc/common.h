@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "sg.h"
 
 // Device-only code (buffer resources and the kernel bodies that use them) is
@@ -87,6 +89,19 @@ inline void clear_hip_error() { (void)hipGetLastError(); }
 inline sg_status launch_status() { return hipGetLastError() == hipSuccess ? SG_OK : SG_ERR_HIP; }
 
 // Workgroup count for grid-stride loops: enough to fill 256 CUs several times.
+// Compute units of the current device (queried once per device).
+inline int cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 inline unsigned grid_for(int64_t items, int per_group, unsigned cap = 4096) {
   const int64_t g = cdiv(items, per_group);
   return (unsigned)(g < 1 ? 1 : (g > cap ? cap : g));

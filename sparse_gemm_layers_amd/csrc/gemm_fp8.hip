@@ -30,8 +30,6 @@
 //          of the row's 16 metadata bytes (nibble order unchanged).
 //          B column l%16, k = 32 g + byte.
 //   result: lane l holds D[4 g + i][l % 16], i = 0..3.
-#include <atomic>
-
 #include "tile_epilogue.h"
 
 namespace sg {
@@ -1680,19 +1678,6 @@ static bool launch_grouped_decode(const GemmArgs& a, const GroupTable& gt, int64
   if (mmax <= 32) return launch_grouped_decode_mt<2, OUT_BF16, OUT_T>(a, gt, st);
   if (mmax <= 48) return launch_grouped_decode_mt<3, OUT_BF16, OUT_T>(a, gt, st);
   return launch_grouped_decode_mt<4, OUT_BF16, OUT_T>(a, gt, st);
-}
-
-// Compute units of the current device (cached per device).
-static int cu_count() {
-  static std::atomic<int> cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  int n = cache[dev].load(std::memory_order_relaxed);
-  if (n == 0) {
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cache[dev].store(n, std::memory_order_relaxed);
-  }
-  return n;
 }
 
 // Whether the grouped decode kernel has a ring for groups of up to mmax rows

@@ -497,7 +497,6 @@ static bool try_w8_dma(const W8Args& a, hipStream_t st, int64_t rows16) {
 //          block's with 128-row scales); rows past N read row N - 1's
 namespace w8t {
 constexpr int BN = 256, BM = 128;
-constexpr int MIN_TILES = 192;   // below this the decode-shaped kernel keeps more CUs busy
 template <int CODES>
 struct Lay {
   static constexpr int WROW = CODES == C_I4 ? 32 : 64;
@@ -659,14 +658,20 @@ __global__ void __launch_bounds__(512) k_gemm_w8a16_tile(W8Args a, int tiles_m, 
 #endif  // SG_DEVICE_PASS
 }
 
-// The large-M tile kernel when its tiles fill most of the chip and its 32-bit
-// per-tile buffer offsets hold.
+// The large-M tile kernel when it is the faster of the two and its 32-bit
+// per-tile buffer offsets hold.  Measured on MI355X at K = 4096 (e4m3 codes):
+// the tile kernel takes about 48 us per round of tiles over the CUs whatever
+// M is, the decode-shaped kernel about 10.8 us per 64 rows of M and 4096 of N
+// (N = 4096: 24 us at M = 128, 44 us at 256, 66 us at 384; the tile kernel
+// 44-51 us for all three), so the tile kernel wins once
+// ceil(M / 64) * N / 4096 exceeds 4.5 rounds.
 template <int CODES, int GRAN_N, bool OUT_BF16, bool OUT_T>
 static bool try_w8_tile(const W8Args& a, hipStream_t st) {
   const int64_t tm = cdiv(a.M, w8t::BM), tn = cdiv(a.N, w8t::BN);
-  if (tm * tn < w8t::MIN_TILES || tm * tn > 0x7fffffffLL || a.ldx >= (1LL << 22) || a.ldw >= (1LL << 23) ||
-      a.ldm >= (1LL << 23))
+  if (tm * tn > 0x7fffffffLL || a.ldx >= (1LL << 22) || a.ldw >= (1LL << 23) || a.ldm >= (1LL << 23))
     return false;
+  const int64_t rounds = cdiv(tm * tn, cu_count());
+  if (2 * cdiv(a.M, 64) * a.N < 9 * 4096 * rounds) return false;
   k_gemm_w8a16_tile<CODES, GRAN_N, OUT_BF16, OUT_T><<<(unsigned)(tm * tn), 512, 0, st>>>(a, (int)tm, (int)tn);
   return true;
 }

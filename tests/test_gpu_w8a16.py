@@ -91,6 +91,11 @@ def test_w8a16_large_m_tiles(int8):
     check(1000, 12300, 256, int8=int8, seed=60 + int8)
 
 
+def test_w8a16_mid_m_on_the_tile_kernel():
+    """M = 130 over a wide weight: two m tiles, the second 2 rows tall."""
+    check(130, 14336, 256, seed=66)
+
+
 def test_w8a16_large_m_per_row_scales_fp32_bias_single_k_block():
     check(300, 24580, 128, gn=1, out=torch.float32, bias=True, seed=62)
 
