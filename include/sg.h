@@ -355,9 +355,10 @@ sg_status sg_fp8_sparse24_gemm_groupwise_packed_batched(int64_t L, int64_t M, in
  *           sg_int8_quant_groupwise at gr = 128 (or 1), gc = 64; ld ldwv (bytes).
  *   wmeta : [N, K/8] metadata, ld ldwm.   sw, gran_n: as sg_fp8_gemm_groupwise.
  *   bias  : [N] fp32 or NULL.   y, y_dt, ldy, form: as sg_fp8_gemm_groupwise.
- * The codes are widened to bf16 (exactly) in registers and multiplied on the
- * dense bf16 matrix core; shaped for decode sizes (a workgroup streams its
- * weight rows once per 64 rows of X).
+ * The codes are widened to bf16 (exactly) in registers and multiplied with the
+ * sparse bf16 matrix-core instruction, which reads the metadata as stored.
+ * Decode-sized M streams the weight once per call; large M runs on 256 x 128
+ * output tiles staged in LDS (the faster of the two is picked per shape).
  * Requires K % 128 == 0, ldx >= K, ldwv >= K/2, ldwm >= K/8, ldx, ldwv, ldwm <
  * 2^24, ceil(M/16) <= 65535; x, wv 16-byte aligned, ldx * 2 and ldwv multiples
  * of 16, wmeta 16-byte aligned and ldwm a multiple of 16.
