@@ -445,6 +445,26 @@ def test_grouped_tails_on_the_decode_kernel(sizes, form, out):
         r += mg
 
 
+def test_grouped_maximum_group_count():
+    """64 groups (the most one call takes), ragged sizes with empty groups."""
+    sizes = [int(v) for v in np.random.default_rng(150).integers(0, 300, size=64)]
+    sizes[5] = sizes[40] = 0
+    n, k = 768, 128   # 303 large tiles (two rounds over 256 CUs), 201 with the tails split off
+    say(f"grouped G=64 M={sum(sizes)} N={n} K={k}")
+    xq, sx, ws = grouped_operands(sizes, n, k, seed=151)
+    wp = torch.stack([sg.sparse24_pack_gfx950(up(wq), up(meta)) for wq, meta, _ in ws])
+    sw = torch.stack([up_m_major(s) for _, _, s in ws])
+    got = down(sg.fp8_sparse24_gemm_groupwise_packed_grouped(up(xq), up_m_major(sx), sizes, wp, n, sw, 128))
+    r = 0
+    for g, mg in enumerate(sizes):
+        if mg:
+            wq, meta, swg = ws[g]
+            ref, bound = oracle.fp8_sparse24_gemm_groupwise(xq[r:r + mg], sx[r:r + mg], 1, wq, meta, swg, 128,
+                                                             bound=True)
+            assert_within_tolerance(got[r:r + mg].astype(np.float64), ref, bound, f"group {g}")
+        r += mg
+
+
 def test_grouped_rowwise_scales():
     sizes, n, k = [130, 3, 257], 512, 640
     say(f"grouped rowwise sizes={sizes} N={n} K={k}")
