@@ -185,6 +185,13 @@ def test_packed_tensor_parallel_share_shapes(m, n, k, out):
     check(True, m, n, k, out_dtype=out, seed=5 + m, packed=True)
 
 
+# Long K: many iterations of the large-M kernel's double-stage loop (odd count
+# of K-block pairs) and 32 K blocks per wave in the decode ring.
+@pytest.mark.parametrize("m,n,k", [(256, 512, 16384), (200, 300, 16256), (16, 1024, 32768), (37, 600, 24576)])
+def test_packed_long_k(m, n, k):
+    check(True, m, n, k, out_dtype=torch.float32, forms=("y",), seed=7 + m, packed=True)
+
+
 def test_packed_fp32_row_major_scales_and_equal_to_unpacked():
     d = workloads.sparse_large(seed=21, m=300, n=700, k=512)
     xq, sx, wq, meta, sw = oracle_operands(d["x"], d["w"], 1, 128, True)

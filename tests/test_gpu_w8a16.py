@@ -96,6 +96,19 @@ def test_w8a16_mid_m_on_the_tile_kernel():
     check(130, 14336, 256, seed=66)
 
 
+def test_w8a16_long_k_tile_kernel():
+    """K = 8192 (64 K blocks) through the tile kernel's two-stage loop, M = 512,
+    N = 4096; the oracle computes a sample of rows."""
+    m, n, k = 512, 4096, 8192
+    say(f"w8a16 long K M={m} N={n} K={k}")
+    x, wv, meta, sw = operands(m, n, k, 128, False, seed=67)
+    got = down(sg.w8a16_sparse24_gemm_groupwise(x, up(wv), up(meta), up(sw), 128))
+    rows = np.array([0, 77, 128, 300, 511])
+    xbits = x.view(torch.int16).cpu().numpy().view(np.uint16)[rows]
+    ref, bound = oracle.w8a16_sparse24_gemm_groupwise(xbits, wv, meta, sw, 128, "e4m3", bound=True)
+    assert_within_tolerance(got[rows].astype(np.float64), ref, bound, "sampled rows")
+
+
 def test_w8a16_large_m_per_row_scales_fp32_bias_single_k_block():
     check(300, 24580, 128, gn=1, out=torch.float32, bias=True, seed=62)
 
