@@ -415,9 +415,8 @@ __device__ __forceinline__ void issue_double(uint8_t* st, const PlanX2& p, __amd
 #if SG_DEVICE_PASS
 // One 256 x 128 output tile (n tile tn, m tile tm) of problem `a`.
 template <bool I8, bool PACKED, int GRAN_N, bool OUT_BF16, bool OUT_T>
-__device__ __forceinline__ void x2_tile(const GemmArgs& a, int tn, int tm) {
-  __shared__ __attribute__((aligned(1024))) uint8_t db0[x2::DBL];
-  __shared__ __attribute__((aligned(1024))) uint8_t db1[x2::DBL];
+// db0, db1: the kernel's two double-stage LDS arrays (x2::DBL bytes each).
+__device__ __forceinline__ void x2_tile(const GemmArgs& a, int tn, int tm, uint8_t* db0, uint8_t* db1) {
   const int64_t n0 = (int64_t)tn * BN, m0 = (int64_t)tm * BM;
 
   const int t = threadIdx.x, l = t & 63;
@@ -504,7 +503,9 @@ __global__ void __launch_bounds__(512) k_gemm_sparse_x2(GemmArgs a, int tiles_m,
   to_batch(a);
   int tn, tm;
   tile_coords(tiles_m, tiles_n, tn, tm);
-  x2_tile<I8, PACKED, GRAN_N, OUT_BF16, OUT_T>(a, tn, tm);
+  __shared__ __attribute__((aligned(1024))) uint8_t db0[x2::DBL];
+  __shared__ __attribute__((aligned(1024))) uint8_t db1[x2::DBL];
+  x2_tile<I8, PACKED, GRAN_N, OUT_BF16, OUT_T>(a, tn, tm, db0, db1);
 #endif  // SG_DEVICE_PASS
 }
 
@@ -521,15 +522,12 @@ struct GroupTable {
   int64_t row_end[MAX_GROUPS];
 };
 
-template <bool I8, bool PACKED, int GRAN_N, bool OUT_BF16, bool OUT_T>
-__global__ void __launch_bounds__(512) k_gemm_sparse_x2_grouped(GemmArgs a, GroupTable gt) {
 #if SG_DEVICE_PASS
-  const int b = xcd_order(blockIdx.x, gt.tile_start[gt.G]);
-  int g = 0;
-  while (g + 1 < gt.G && gt.tile_start[g + 1] <= b) ++g;   // uniform; empty groups are skipped
-  const int tiles_m = (gt.tile_start[g + 1] - gt.tile_start[g]) / gt.tiles_n;
-  int tn, tm;
-  tile_of(b - gt.tile_start[g], tiles_m, gt.tiles_n, tn, tm);
+// Points a at group g's part of a grouped problem: rows row_off[g] ..
+// row_end[g] - 1 of X, its scales and Y (columns of Y^T), the group's packed
+// weight, W scales and bias.
+template <bool OUT_BF16, bool OUT_T>
+__device__ __forceinline__ void group_args(GemmArgs& a, const GroupTable& gt, int g) {
   const int64_t r0 = gt.row_off[g];
   a.M = gt.row_end[g] - r0;
   a.x += r0 * a.ldx;
@@ -538,7 +536,28 @@ __global__ void __launch_bounds__(512) k_gemm_sparse_x2_grouped(GemmArgs a, Grou
   a.w += g * a.bw;
   a.sw += g * a.bsw;
   if (a.bias) a.bias += g * a.bbs;
-  x2_tile<I8, PACKED, GRAN_N, OUT_BF16, OUT_T>(a, tn, tm);
+}
+
+// Large tile b (in the XCD order over T tiles) of a grouped problem.
+template <bool I8, bool PACKED, int GRAN_N, bool OUT_BF16, bool OUT_T>
+__device__ __forceinline__ void x2_grouped_tile(GemmArgs a, const GroupTable& gt, int T, uint8_t* db0, uint8_t* db1) {
+  const int b = xcd_order(blockIdx.x, T);
+  int g = 0;
+  while (g + 1 < gt.G && gt.tile_start[g + 1] <= b) ++g;   // uniform; empty groups are skipped
+  const int tiles_m = (gt.tile_start[g + 1] - gt.tile_start[g]) / gt.tiles_n;
+  int tn, tm;
+  tile_of(b - gt.tile_start[g], tiles_m, gt.tiles_n, tn, tm);
+  group_args<OUT_BF16, OUT_T>(a, gt, g);
+  x2_tile<I8, PACKED, GRAN_N, OUT_BF16, OUT_T>(a, tn, tm, db0, db1);
+}
+#endif  // SG_DEVICE_PASS
+
+template <bool I8, bool PACKED, int GRAN_N, bool OUT_BF16, bool OUT_T>
+__global__ void __launch_bounds__(512) k_gemm_sparse_x2_grouped(GemmArgs a, GroupTable gt) {
+#if SG_DEVICE_PASS
+  __shared__ __attribute__((aligned(1024))) uint8_t db0[x2::DBL];
+  __shared__ __attribute__((aligned(1024))) uint8_t db1[x2::DBL];
+  x2_grouped_tile<I8, PACKED, GRAN_N, OUT_BF16, OUT_T>(a, gt, gt.tile_start[gt.G], db0, db1);
 #endif  // SG_DEVICE_PASS
 }
 
@@ -1128,17 +1147,17 @@ __device__ __forceinline__ void dma_issue(uint8_t* slot, const GemmArgs& a, __am
 #endif
 
 #if SG_DEVICE_PASS
+// r0, r1: two LDS arrays of at least DmaCfg<RB, MT>::ARR bytes (the ring's
+// slots); bx: the workgroup's block of RB row blocks.
 template <bool I8, int RB, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
-__device__ __forceinline__ void decode_dma_body(const GemmArgs& a) {
+__device__ __forceinline__ void decode_dma_body(const GemmArgs& a, uint8_t* r0, uint8_t* r1, int bx) {
   using C = DmaCfg<RB, MT>;
   constexpr int KPS = C::KPS;
   static_assert(MT <= 4 && 2 * C::ARR <= 160 * 1024, "LDS");
-  __shared__ __attribute__((aligned(1024))) uint8_t r0[C::ARR];
-  __shared__ __attribute__((aligned(1024))) uint8_t r1[C::ARR];
   const int t = threadIdx.x, l = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int g = l >> 4, lr = l & 15;
-  const int64_t n0 = (int64_t)blockIdx.x * 16 * RB;
+  const int64_t n0 = (int64_t)bx * 16 * RB;
   const int KB = (int)(a.K >> 7);
   const int nt = (KB - wave + DEC_WAVES - 1) / DEC_WAVES;    // K blocks of this wave
   const int ns = (nt + KPS - 1) / KPS;                         // slots of this wave
@@ -1287,7 +1306,9 @@ template <bool I8, int RB, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
 __global__ void __launch_bounds__(512) k_gemm_decode_dma(GemmArgs a) {
 #if SG_DEVICE_PASS
   to_batch(a);
-  decode_dma_body<I8, RB, MT, GRAN_N, OUT_BF16, OUT_T>(a);
+  __shared__ __attribute__((aligned(1024))) uint8_t r0[DmaCfg<RB, MT>::ARR];
+  __shared__ __attribute__((aligned(1024))) uint8_t r1[DmaCfg<RB, MT>::ARR];
+  decode_dma_body<I8, RB, MT, GRAN_N, OUT_BF16, OUT_T>(a, r0, r1, blockIdx.x);
 #endif
 }
 
@@ -1298,17 +1319,35 @@ __global__ void __launch_bounds__(512) k_gemm_decode_dma(GemmArgs a) {
 template <bool I8, int RB, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
 __global__ void __launch_bounds__(512) k_gemm_decode_dma_grouped(GemmArgs a, GroupTable gt) {
 #if SG_DEVICE_PASS
-  const int g = blockIdx.y;
-  const int64_t r0 = gt.row_off[g];
-  a.M = gt.row_end[g] - r0;
+  group_args<OUT_BF16, OUT_T>(a, gt, blockIdx.y);
   if (a.M == 0) return;
-  a.x += r0 * a.ldx;
-  a.sx += r0 * a.sx_sm;
-  a.y = static_cast<uint8_t*>(a.y) + (OUT_T ? r0 : r0 * a.ldy) * (OUT_BF16 ? 2 : 4);
-  a.w += g * a.bw;
-  a.sw += g * a.bsw;
-  if (a.bias) a.bias += g * a.bbs;
-  decode_dma_body<I8, RB, MT, GRAN_N, OUT_BF16, OUT_T>(a);
+  __shared__ __attribute__((aligned(1024))) uint8_t r0[DmaCfg<RB, MT>::ARR];
+  __shared__ __attribute__((aligned(1024))) uint8_t r1[DmaCfg<RB, MT>::ARR];
+  decode_dma_body<I8, RB, MT, GRAN_N, OUT_BF16, OUT_T>(a, r0, r1, blockIdx.x);
+#endif
+}
+
+// Grouped problem with tails (group tables gt for the large tiles, gtail for
+// each group's last <= 64 rows): workgroups 0 .. T - 1 run the large tiles,
+// the rest each run one block of 4 row blocks of one group's tail with the
+// LDS-streaming decode body (tail_gx of them per group).  The tiles are
+// dispatched first, so the tails run on the CUs the tiles leave idle and
+// after them, in the same launch; both bodies use the same two LDS arrays.
+template <int GRAN_N, bool OUT_BF16, bool OUT_T>
+__global__ void __launch_bounds__(512) k_gemm_grouped_tails(GemmArgs a, GroupTable gt, GroupTable gtail, int T,
+                                                             int tail_gx) {
+#if SG_DEVICE_PASS
+  static_assert(DmaCfg<4, 4>::ARR <= x2::DBL, "the decode ring fits the tile's LDS arrays");
+  __shared__ __attribute__((aligned(1024))) uint8_t s0[x2::DBL];
+  __shared__ __attribute__((aligned(1024))) uint8_t s1[x2::DBL];
+  if ((int)blockIdx.x < T) {
+    x2_grouped_tile<false, true, GRAN_N, OUT_BF16, OUT_T>(a, gt, T, s0, s1);
+  } else {
+    const int d = (int)blockIdx.x - T;
+    group_args<OUT_BF16, OUT_T>(a, gtail, d / tail_gx);
+    if (a.M == 0) return;
+    decode_dma_body<false, 4, 4, 128, OUT_BF16, OUT_T>(a, s0, s1, d % tail_gx);
+  }
 #endif
 }
 
@@ -1680,12 +1719,20 @@ static bool launch_grouped_decode(const GemmArgs& a, const GroupTable& gt, int64
   return launch_grouped_decode_mt<4, OUT_BF16, OUT_T>(a, gt, st);
 }
 
-// Whether the grouped decode kernel has a ring for groups of up to mmax rows
-// (16-row sub-tiles up to 3 always fit with one row block per workgroup; 4
-// need four row blocks and enough workgroups).
-static bool grouped_decode_fits(int64_t mmax, int64_t N, int G) {
-  if (mmax <= 48) return true;
-  return mmax <= 64 && cdiv(cdiv(N, 16), 4) * G >= 224;
+// Large tiles and tails in one launch (k_gemm_grouped_tails).
+template <int GRAN_N>
+static void launch_grouped_tails(const GemmArgs& a, const GroupTable& gt, const GroupTable& gtail, bool bf16,
+                                 bool yt, hipStream_t st) {
+  const int T = gt.tile_start[gt.G];
+  const int tail_gx = (int)cdiv(cdiv(a.N, 16), 4);
+  const unsigned blocks = (unsigned)(T + (int64_t)tail_gx * gt.G);
+  if (bf16) {
+    if (yt) k_gemm_grouped_tails<GRAN_N, true, true><<<blocks, 512, 0, st>>>(a, gt, gtail, T, tail_gx);
+    else k_gemm_grouped_tails<GRAN_N, true, false><<<blocks, 512, 0, st>>>(a, gt, gtail, T, tail_gx);
+  } else {
+    if (yt) k_gemm_grouped_tails<GRAN_N, false, true><<<blocks, 512, 0, st>>>(a, gt, gtail, T, tail_gx);
+    else k_gemm_grouped_tails<GRAN_N, false, false><<<blocks, 512, 0, st>>>(a, gt, gtail, T, tail_gx);
+  }
 }
 
 extern "C" sg_status sg_fp8_sparse24_gemm_groupwise_packed_grouped(
@@ -1743,9 +1790,9 @@ extern "C" sg_status sg_fp8_sparse24_gemm_groupwise_packed_grouped(
   if (!done) {
     // Tails: a group's last rows past a multiple of 128, when there are at
     // most 64 of them, cost the large-M kernel a whole K loop per tile.  When
-    // leaving them out saves the tiles a round over the CUs, they take the
-    // grouped decode kernel in a second launch instead (streaming their
-    // group's weight once more).
+    // leaving them out saves the tiles a round over the CUs, the same launch
+    // runs them with the LDS-streaming decode body instead (streaming their
+    // group's weight once more), on the CUs the tiles leave idle.
     GroupTable gh = gt, gtail = gt;
     int64_t tail_max = 0;
     gh.tile_start[0] = 0;
@@ -1758,17 +1805,16 @@ extern "C" sg_status sg_fp8_sparse24_gemm_groupwise_packed_grouped(
     }
     const int cus = cu_count();
     const bool split = gran_n == 128 && tail_max > 0 && gh.tile_start[G] > 0 &&
-                       cdiv(gh.tile_start[G], cus) < cdiv(gt.tile_start[G], cus) &&
-                       grouped_decode_fits(tail_max, N, (int)G);
-    const GroupTable& tiles = split ? gh : gt;
-    if (sx_sk == 0 && sw_sk == 0) launch_grouped_form<0>(a, tiles, bf16, yt, stream);
-    else if (gran_n == 128) launch_grouped_form<128>(a, tiles, bf16, yt, stream);
-    else launch_grouped_form<1>(a, tiles, bf16, yt, stream);
+                       cdiv(gh.tile_start[G], cus) < cdiv(gt.tile_start[G], cus);
     if (split) {
-      if (bf16) (void)(yt ? launch_grouped_decode<true, true>(a, gtail, tail_max, stream)
-                          : launch_grouped_decode<true, false>(a, gtail, tail_max, stream));
-      else (void)(yt ? launch_grouped_decode<false, true>(a, gtail, tail_max, stream)
-                     : launch_grouped_decode<false, false>(a, gtail, tail_max, stream));
+      if (sx_sk == 0 && sw_sk == 0) launch_grouped_tails<0>(a, gh, gtail, bf16, yt, stream);
+      else launch_grouped_tails<128>(a, gh, gtail, bf16, yt, stream);
+    } else if (sx_sk == 0 && sw_sk == 0) {
+      launch_grouped_form<0>(a, gt, bf16, yt, stream);
+    } else if (gran_n == 128) {
+      launch_grouped_form<128>(a, gt, bf16, yt, stream);
+    } else {
+      launch_grouped_form<1>(a, gt, bf16, yt, stream);
     }
   }
   return launch_status();
