@@ -37,6 +37,44 @@ def test_fp8_quant_matches_oracle(gr, gc, rows, cols, dist, dtype):
     assert np.array_equal(q.cpu().numpy(), oq)
 
 
+def _extreme_rows(rows, cols, seed):
+    """Row groups at the ends of the fp32 range: subnormal magnitudes (the scale
+    itself subnormal), magnitudes near the fp32 maximum, exact powers of two,
+    zeros, and blocks of mixed extremes."""
+    rng = np.random.default_rng(seed)
+    u = rng.uniform(-1.0, 1.0, size=(rows, cols))
+    kind = np.arange(rows) % 5
+    x = np.where(kind[:, None] == 0, u * 1e-40, 0.0)
+    x = np.where(kind[:, None] == 1, u * 3.0e38, x)
+    x = np.where(kind[:, None] == 2, np.sign(u) * np.exp2(rng.integers(-149, 127, size=(rows, cols))), x)
+    mixed = np.where(rng.integers(0, 2, size=(rows, cols)) == 1, u * 1e-38, u * 1e30)
+    x = np.where(kind[:, None] == 4, mixed, x)
+    return x.astype(np.float32)
+
+
+@pytest.mark.parametrize("gr,gc,rows", [(1, 128, 10), (1, 64, 10), (128, 64, 256), (1, 512, 10), (10, 512, 10)])
+def test_fp8_and_int8_quant_at_the_ends_of_the_fp32_range(gr, gc, rows):
+    x = _extreme_rows(rows, 512, seed=300 + gr + gc)
+    say(f"extreme quant gr={gr} gc={gc} rows={rows}")
+    for fn, ofn in ((sg.fp8_quant_groupwise, oracle.fp8_quant_groupwise),
+                    (sg.int8_quant_groupwise, oracle.int8_quant_groupwise)):
+        q, s = fn(up(x), gr=gr, gc=gc)
+        oq, os_ = ofn(x, gr, gc)
+        torch.cuda.synchronize()
+        assert np.array_equal(s.cpu().numpy().view(np.uint32), os_.view(np.uint32)), fn.__name__
+        assert np.array_equal(q.cpu().numpy(), oq), fn.__name__
+
+
+@pytest.mark.parametrize("gc", [128, 64])
+def test_int4_quant_at_the_ends_of_the_fp32_range(gc):
+    x = _extreme_rows(10, 512, seed=310 + gc)
+    q, s = sg.int4_quant_groupwise(up(x), gc=gc)
+    oq, os_ = oracle.int4_quant_groupwise(x, gc)
+    torch.cuda.synchronize()
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), os_.view(np.uint32))
+    assert np.array_equal(q.cpu().numpy(), oq)
+
+
 def test_fp8_encoder_on_every_midpoint_and_neighbour():
     """Blocks whose amax is 448 have scale 1, so the codes are the encoder's
     output for the raw values: every e4m3 midpoint, its fp32 neighbours, every
