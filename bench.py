@@ -42,8 +42,10 @@ PEAK_INT8_TOPS = 5000.0
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 # the sources the sparse GEMM kernel is compiled from (a change voids the recorded traffic)
+# the sparse GEMM's sources and the build script (its compile flags shape the kernel too)
 GEMM_SRCS = [os.path.join(ROOT, "sparse_gemm_layers_amd", "csrc", f)
-             for f in ("gemm_fp8.hip", "gemm_common.h", "tile_epilogue.h", "common.h")]
+             for f in ("gemm_fp8.hip", "gemm_common.h", "tile_epilogue.h", "common.h")] + \
+            [os.path.join(ROOT, "sparse_gemm_layers_amd", "build.py")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sparse_gemm_2048x4096x4096_traffic.txt")
 DEV = torch.device("cuda:0")
 ROTATE = 8          # input sets cycled through in the headline loop (> MALL)

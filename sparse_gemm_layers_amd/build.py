@@ -30,9 +30,16 @@ CFLAGS = [
 ]
 
 
+# Per-source extra flags.  The FP8 GEMM / decode kernels schedule better with
+# the ILP-maximising machine scheduler (decode 1-4% faster on MI355X, the
+# large-M kernels unchanged); the quantisers and the weight-only kernels were
+# slower with it, so the library as a whole keeps the default.
+SRC_FLAGS = {"gemm_fp8.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *SRC_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     err = "\n".join(line for line in r.stderr.splitlines() if "packed-fp32-ops" not in line)
     if r.returncode != 0:
