@@ -24,11 +24,12 @@
 // bits (the index word as stored), and B lane group g' then holds
 // x[k = 64 h + 8 g' .. + 7] and x[k = 64 h + 32 + 8 g' .. + 7].
 //
-// The kernel is shaped for the decode sizes where weight-only quantisation is
-// used (M <= 64 per workgroup): a workgroup owns RB blocks of 16 W rows and MT
-// sub-tiles of 16 X rows, its 8 waves split the K blocks, read their operands
-// straight from global memory and add their partial tiles through LDS; the
-// weight is streamed from HBM once per 64 X rows.
+// Three kernels share that arithmetic.  At decode sizes a workgroup owns RB
+// blocks of 16 W rows and all (M <= 48, k_gemm_w8a16_dma: the weight streamed
+// through per-wave LDS rings) or 64 (k_gemm_w8a16: operands loaded straight
+// into registers) X rows; its 8 waves split the K blocks and add their
+// partial tiles through LDS.  Large M (k_gemm_w8a16_tile) uses 256 x 128
+// output tiles staged in LDS; the host picks it where it is the cheaper.
 #include "tile_epilogue.h"
 #include "sg.h"
 
