@@ -30,6 +30,8 @@
 //          of the row's 16 metadata bytes (nibble order unchanged).
 //          B column l%16, k = 32 g + byte.
 //   result: lane l holds D[4 g + i][l % 16], i = 0..3.
+#include <type_traits>
+
 #include "tile_epilogue.h"
 
 namespace sg {
@@ -271,6 +273,128 @@ __device__ __forceinline__ void compute_stage(const uint8_t* st, v4f (&acc)[8][4
   }
 }
 
+// The same stage with the promotion folded into the accumulator (128-row W
+// scale blocks, FP8 codes).  The accumulator of sub-tile column j is kept in
+// units of the current K block's scale product c_j = sx[m, kb] * sw[kb]: per
+// K block it is rescaled by c_prev / c_j (one multiply per element) and the
+// SMFMAC adds the block's products into it directly, so no partial has to be
+// cleared first.  On gfx950 the sparse instruction does not overlap VALU work,
+// and clearing the partials costs as much as the multiplies, so this form
+// needs about a third less VALU time per promoted unit.  The true sum is
+// acc * c_last.  Callers use it only when every scale product the wave meets
+// is a positive normal number within a factor 2^60 of the others (see
+// scales_tame), so the rescaled sums stay far inside the fp32 range.
+template <bool PACKED>
+__device__ __forceinline__ void compute_stage_scaled(const uint8_t* st, v4f (&acc)[8][4], const LaneOffsets& o,
+                                                     int wn, int g, uint32_t msel, float (&cprev)[4]) {
+  using L = Stage<true>;
+  const float swv = lds_ld<float>(st, L::SW_OFF + wn * 512);
+  float r[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float c = lds_ld<float>(st, o.sx + j * 64) * swv;
+    r[j] = cprev[j] * __builtin_amdgcn_rcpf(c);
+    cprev[j] = c;
+  }
+  v8i bx[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint4 lo = lds_ld<uint4>(st, o.x0 + j * 2048);
+    const uint4 hi = lds_ld<uint4>(st, o.x1 + j * 2048);
+    bx[j] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    v4i aa;
+    int idx;
+    if (PACKED) {
+      const uint4 av = lds_ld<uint4>(st, o.w0 + i * 1024);
+      idx = lds_ld<int>(st, o.mt + i * 256);
+      aa = (v4i){(int)av.x, (int)av.y, (int)av.z, (int)av.w};
+    } else {
+      const uint2 v0 = lds_ld<uint2>(st, o.w0 + i * 1024);
+      const uint2 v1 = lds_ld<uint2>(st, o.w1 + i * 1024);
+      const uint2 mw = lds_ld<uint2>(st, o.mt + i * 256);
+      idx = (int)__builtin_amdgcn_perm(mw.y, mw.x, msel);
+      aa = (v4i){(int)v0.x, (int)v0.y, (int)v1.x, (int)v1.y};
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = mma_sparse_acc<false>(aa, bx[j], acc[i][j] * r[j], idx);
+  }
+}
+
+#if SG_DEVICE_PASS
+// Whether every scale product c = sx[m, kb] * sw[n-block, kb] of the K blocks
+// kb = k0, k0 + 2, ... that a wave of the large-M kernels multiplies is a
+// positive normal fp32 number, all within a factor 2^60 of each other, for
+// the wave's X rows (lane l checks rows mw0 + l + 64 r, r < NR, clamped to
+// M - 1 as the stage loads are) and its W row block (row nw0, clamped to
+// N - 1).  Then the rescaled accumulator of the promotion stays below
+// 2^60 * 32 * 2^24 in magnitude and its terms above 2^-78: no overflow, no
+// subnormals.  issue() loads the scales of the first 16 K blocks, tame()
+// waits for them, reads any further K blocks (16 at a time) and returns the
+// wave-uniform answer; loads issued between the two (the first stage's)
+// travel with the scan's.
+template <int NR>
+struct ScaleScan {
+  static constexpr int CH = 16;
+  float xs[NR][CH], ws[CH];
+  const float* sxp[NR];
+  const float* swp;
+  int k0, KB;
+
+  __device__ __forceinline__ void load(const GemmArgs& a, int c0) {
+#pragma unroll
+    for (int t = 0; t < CH; ++t) {
+      const int kb = min(c0 + 2 * t, KB - 1 - ((KB - 1 - k0) & 1));   // past the end: the last block of this parity
+#pragma unroll
+      for (int r = 0; r < NR; ++r) xs[r][t] = sxp[r][kb * a.sx_sk];
+      ws[t] = swp[kb * a.sw_sk];
+    }
+    __builtin_amdgcn_sched_barrier(0);   // all loads of the batch before any use
+  }
+
+  __device__ __forceinline__ void issue(const GemmArgs& a, int64_t mw0, int64_t nw0, int k0_, int KB_, int l) {
+    k0 = k0_;
+    KB = KB_;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) sxp[r] = a.sx + (min(mw0 + l + 64 * r, a.M - 1) >> a.gm_shift) * a.sx_sm;
+    swp = a.sw + (min(nw0, a.N - 1) >> a.gn_shift) * a.sw_sn;
+    load(a, k0);
+  }
+
+  __device__ __forceinline__ void reduce(int& emin, int& emax) const {
+#pragma unroll
+    for (int t = 0; t < CH; ++t)
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        const int e = __float_as_int(xs[r][t] * ws[t]) >> 23;   // biased exponent; negative for a negative product
+        emin = min(emin, e);
+        emax = max(emax, e);
+      }
+  }
+
+  __device__ __forceinline__ bool tame(const GemmArgs& a) {
+    __builtin_amdgcn_sched_barrier(0);   // nothing of the check moves above the loads issued since issue()
+    int emin = 255, emax = 0;
+    reduce(emin, emax);   // the first batch, outside the loop: its wait counts only the loads issued since
+    for (int c0 = k0 + 2 * CH; c0 < KB; c0 += 2 * CH) {
+      load(a, c0);
+      reduce(emin, emax);
+    }
+    const bool ok = emin >= 1 && emax <= 254 && emax - emin <= 60;
+    return __builtin_amdgcn_ballot_w64(!ok) == 0;
+  }
+};
+
+template <int NR>
+__device__ __forceinline__ bool scales_tame(const GemmArgs& a, int64_t mw0, int64_t nw0, int k0, int KB, int l) {
+  ScaleScan<NR> s;
+  s.issue(a, mw0, nw0, k0, KB, l);
+  return s.tame(a);
+}
+#endif  // SG_DEVICE_PASS
+
 // Scales constant along K: multiplies the wave's RI x 4 sub-tiles by
 // sx (X row of the lane's column) * sw (W rows 16 i + 4 g .. + 3), read from
 // a landed stage (every stage holds the same scales).  int8 sums are
@@ -450,19 +574,44 @@ __device__ __forceinline__ void x2_tile(const GemmArgs& a, int tn, int tm, uint8
     for (int j = 0; j < 4; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
 
   issue_double<PACKED>(db0, plan, rx, rw, rm, rsx, rsw, a, 0, KB, wave);
-  for (int it0 = 0; it0 < NIT; it0 += 2) {
+  // The K loop: group q multiplies K block 2 it + q of double stage it.
+  // SCALED: the rescaled-accumulator promotion (compute_stage_scaled).
+  auto kloop = [&](auto scaled_tag) {
+    constexpr bool SCALED = decltype(scaled_tag)::value;
+    float cprev[4] = {0.f, 0.f, 0.f, 0.f};   // scale product of the last K block multiplied (0: none yet)
+    for (int it0 = 0; it0 < NIT; it0 += 2) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int it = it0 + u;
-      if (it < NIT) {
-        wait_vmcnt<0>();
-        __syncthreads();
-        if (it + 1 < NIT)
-          issue_double<PACKED>(u == 0 ? db1 : db0, plan, rx, rw, rm, rsx, rsw, a, 2 * (it + 1), KB, wave);
-        if (2 * it + q < KB)
-          compute_stage<GRAN_N, PACKED, I8>((u == 0 ? db0 : db1) + qoff, acc, lo, wn, g, msel);
+      for (int u = 0; u < 2; ++u) {
+        const int it = it0 + u;
+        if (it < NIT) {
+          wait_vmcnt<0>();
+          __syncthreads();
+          if (it + 1 < NIT)
+            issue_double<PACKED>(u == 0 ? db1 : db0, plan, rx, rw, rm, rsx, rsw, a, 2 * (it + 1), KB, wave);
+          if (2 * it + q < KB) {
+            if constexpr (SCALED)
+              compute_stage_scaled<PACKED>((u == 0 ? db0 : db1) + qoff, acc, lo, wn, g, msel, cprev);
+            else
+              compute_stage<GRAN_N, PACKED, I8>((u == 0 ? db0 : db1) + qoff, acc, lo, wn, g, msel);
+          }
+        }
       }
     }
+    if constexpr (SCALED) {   // back to true values: acc * c_last
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] *= cprev[j];
+    }
+  };
+  // FP8 codes with 128-row W scale blocks take the rescaled-accumulator
+  // promotion where the wave's scale products allow it (a wave-uniform
+  // choice), else the zero-and-FMA promotion.
+  if constexpr (GRAN_N == 128 && !I8) {
+    if (scales_tame<1>(a, m0 + wm * 64, n0 + wn * 128, q, KB, l)) kloop(std::true_type{});
+    else kloop(std::false_type{});
+  } else {
+    kloop(std::false_type{});
   }
 
   // Add the two groups' partial tiles: group 0 finishes sub-tile rows i < 4,
@@ -506,6 +655,317 @@ __global__ void __launch_bounds__(512) k_gemm_sparse_x2(GemmArgs a, int tiles_m,
   __shared__ __attribute__((aligned(1024))) uint8_t db0[x2::DBL];
   __shared__ __attribute__((aligned(1024))) uint8_t db1[x2::DBL];
   x2_tile<I8, PACKED, GRAN_N, OUT_BF16, OUT_T>(a, tn, tm, db0, db1);
+#endif  // SG_DEVICE_PASS
+}
+
+// ============================= large-M 2:4 kernel, weight in registers
+// Packed weights, FP8 codes.  Workgroup tile 256 W rows (n) x 128 X rows (m),
+// 8 waves: two K groups of four.  Wave (q, wn) owns W rows 64 wn .. 64 wn + 63
+// (four 16-row blocks) and all 128 X rows (eight 16-column sub-tiles) and
+// multiplies the K blocks kb = q (mod 2).  No other wave needs its W rows, so
+// it loads them from the packed weight straight into registers: a lane's
+// 16-byte A operand and 4-byte index word of one row block are one dwordx4
+// and one dword load, coalesced over the wave, issued one period (two K
+// blocks) ahead.  X, which the four waves of a group share, goes through LDS:
+// two arrays of four K blocks (per K block 16 KB of codes with 16-byte chunks
+// swizzled by row, the 128 X scales and the 256 W-row scales), filled by
+// buffer loads that write LDS.  While one array is multiplied the other
+// one's loads are in flight, and one barrier per four K blocks joins the
+// waves.  Against the 2 x 2 wave grid of k_gemm_sparse_x2 this halves the
+// bytes written into LDS per K block and doubles the time an LDS load has
+// to land.  At the end the two groups add their partial tiles through LDS
+// (group q finishes sub-tile columns 4 q .. 4 q + 3) and the finished tile is
+// staged for whole-row stores.
+namespace wr {
+constexpr int KPA = 4;                       // K blocks per LDS array
+constexpr int XB = BM * 128;                 // X codes of one K block
+constexpr int SX_OFF = XB;                   // 128 X scales
+constexpr int SW_OFF = XB + BM * 4;          // 256 W-row scales
+constexpr int SPARE_OFF = SW_OFF + BN * 4;   // spare slot for the scale loads of waves 6, 7
+constexpr int KBYTES = SPARE_OFF + BM * 4;   // one K block
+constexpr int ARR = KPA * KBYTES;            // one array
+constexpr int NW = 8;                        // register loads per wave per K block
+}  // namespace wr
+
+#if SG_DEVICE_PASS
+// A wave's W operands of one K block: row block rb = 4 wn + i, i = 0..3.
+struct WrRegs {
+  v4i v[4];
+  int idx[4];
+};
+
+// Loads row block 4 wn + i of K block kb (clamped to the last block) into
+// registers: two buffer loads.
+__device__ __forceinline__ void wr_load_w1(WrRegs& w, int i, __amdgpu_buffer_rsrc_t rw, uint32_t voff_v,
+                                           uint32_t voff_m, int wn, int kb, int KB) {
+  const int so = ((4 * wn + i) * KB + min(kb, KB - 1)) * PK_CHUNK;
+  w.v[i] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rw, voff_v, so, 0));
+  w.idx[i] = __builtin_bit_cast(int, __builtin_amdgcn_raw_buffer_load_b32(rw, voff_m, so, 0));
+}
+
+// All four row blocks (exactly wr::NW loads).
+__device__ __forceinline__ void wr_load_w(WrRegs& w, __amdgpu_buffer_rsrc_t rw, uint32_t voff_v, uint32_t voff_m,
+                                          int wn, int kb, int KB) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) wr_load_w1(w, i, rw, voff_v, voff_m, wn, kb, KB);
+}
+
+// Issues the LDS loads of K blocks 4 P .. 4 P + 3 into an array: every wave
+// two 1 KB slices of X codes per K block and one scale load (waves 0, 1: X
+// scales; waves 2 .. 5: W-row scales; waves 6, 7: the X scales again, into a
+// spare slot), so that every wave issues the same number of loads on every
+// path (the compiler's and this kernel's load counting rely on it).  K
+// blocks at or past KB go through descriptors of zero records: no memory
+// access, zeros written.
+struct WrPlan {
+  uint32_t xo[2];   // X slice source offsets (K block 0)
+  uint32_t so;      // scale source offset (K block 0), bytes
+  uint32_t sdst;    // scale destination within a K block
+  bool sw;          // the scale is a W-row scale (else an X scale)
+};
+
+__device__ __forceinline__ WrPlan wr_plan(const GemmArgs& a, int64_t n0, int64_t m0, int wave, int l) {
+  WrPlan p;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int s = (8 * j + wave) * 64 + l;            // 16-byte position in the K block's X area
+    const int r = s >> 3, c = (s & 7) ^ swz8(r);
+    p.xo[j] = (uint32_t)(r * a.ldx + c * 16);
+  }
+  if (wave >= 2 && wave < 6) {
+    const int64_t n = min(n0 + (wave - 2) * 64 + l, a.N - 1);
+    p.so = (uint32_t)(((n >> a.gn_shift) * a.sw_sn) * 4);
+    p.sdst = wr::SW_OFF + (wave - 2) * 256;
+    p.sw = true;
+  } else {
+    const int h = wave & 1;
+    const int64_t m = min(m0 + h * 64 + l, a.M - 1);
+    p.so = (uint32_t)(((m >> a.gm_shift) * a.sx_sm) * 4);
+    p.sdst = (wave < 2 ? wr::SX_OFF : wr::SPARE_OFF) + h * 256;
+    p.sw = false;
+  }
+  return p;
+}
+
+// The loads of K block 4 P + k (three per wave).
+__device__ __forceinline__ void wr_issue_x1(uint8_t* arr, const WrPlan& p, __amdgpu_buffer_rsrc_t rx,
+                                            __amdgpu_buffer_rsrc_t rs, int64_t s_sk, int P, int k, int KB, int wave) {
+  const __amdgpu_buffer_rsrc_t none = rsrc(nullptr, 0);
+  const int kb = wr::KPA * P + k;
+  const bool ok = kb < KB;
+  const int kbc = ok ? kb : 0;
+  uint8_t* st = arr + k * wr::KBYTES;
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ok ? rx : none, (lds_void*)(st + (8 * j + wave) * 1024), 16, p.xo[j],
+                                             kbc * 128, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(ok ? rs : none, (lds_void*)(st + p.sdst), 4, p.so, (int)(kbc * s_sk * 4),
+                                           0, 0);
+}
+
+__device__ __forceinline__ void wr_issue_x(uint8_t* arr, const WrPlan& p, __amdgpu_buffer_rsrc_t rx,
+                                           __amdgpu_buffer_rsrc_t rs, int64_t s_sk, int P, int KB, int wave) {
+#pragma unroll
+  for (int k = 0; k < wr::KPA; ++k) wr_issue_x1(arr, p, rx, rs, s_sk, P, k, KB, wave);
+}
+
+// Multiplies one K block (stage st of an array, W operands w) into the
+// wave's 4 x 8 sub-tiles; issue(j) is called before sub-tile column j.  SCALED: the rescaled-accumulator promotion of
+// compute_stage_scaled; else GRAN_N = 128 promotes each partial from zero,
+// and GRAN_N = 0 accumulates in the matrix core (scales applied at the end).
+template <int GRAN_N, bool SCALED, typename Issue>
+__device__ __forceinline__ void wr_compute(const uint8_t* st, const WrRegs& w, v4f (&acc)[4][8], uint32_t x0,
+                                           uint32_t x1, uint32_t sxo, int wn, float (&cprev)[8], Issue&& issue) {
+  float swv = 1.f;
+  if (GRAN_N == 128) swv = lds_ld<float>(st, wr::SW_OFF + wn * 256);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    issue(j);   // a share of the loads for later K blocks, spread over the multiplies
+    const uint4 lo = lds_ld<uint4>(st, x0 + j * 2048);
+    const uint4 hi = lds_ld<uint4>(st, x1 + j * 2048);
+    const v8i bx = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    if constexpr (GRAN_N == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i][j] = mma_sparse_acc<false>(w.v[i], bx, acc[i][j], w.idx[i]);
+    } else {
+      const float c = lds_ld<float>(st, sxo + j * 64) * swv;
+      if constexpr (SCALED) {
+        const float r = cprev[j] * __builtin_amdgcn_rcpf(c);
+        cprev[j] = c;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i][j] = mma_sparse_acc<false>(w.v[i], bx, acc[i][j] * r, w.idx[i]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i][j] += mma_sparse<false>(w.v[i], bx, w.idx[i]) * c;
+      }
+    }
+  }
+}
+
+// Group Q's half of the epilogue: adds the partner group's partials of
+// sub-tile columns 4 Q .. 4 Q + 3 (in buffer src), applies scales constant
+// along K (GRAN_N = 0) and the bias, and stages the values in t0 / t1.
+template <int Q, int GRAN_N, bool OUT_BF16, bool OUT_T>
+__device__ __forceinline__ void wr_finish(const GemmArgs& a, const uint8_t* src, uint8_t* t0, uint8_t* t1,
+                                          const v4f (&acc)[4][8], int wn, int l, int64_t m0, int64_t n0) {
+  const int g = l >> 4, lr = l & 15;
+  float4 part[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) part[k] = reinterpret_cast<const float4*>(src)[((wn * 16 + k) << 6) + l];
+  float sxj[4] = {1.f, 1.f, 1.f, 1.f};
+  if constexpr (GRAN_N == 0) {
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+      sxj[jj] = a.sx[(min(m0 + 16 * (4 * Q + jj) + lr, a.M - 1) >> a.gm_shift) * a.sx_sm];
+  }
+  __syncthreads();   // every wave holds its partner's partials: the buffers may be overwritten
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int nl = wn * 64 + 16 * i + 4 * g;
+    float sw[4] = {1.f, 1.f, 1.f, 1.f}, bv[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int64_t n = min(n0 + nl + e, a.N - 1);
+      if (GRAN_N == 0) sw[e] = a.sw[(n >> a.gn_shift) * a.sw_sn];
+      if (a.bias) bv[e] = a.bias[n];
+    }
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const float4 o = part[i * 4 + jj];
+      const v4f av = acc[i][4 * Q + jj];
+      float v[4] = {av[0] + o.x, av[1] + o.y, av[2] + o.z, av[3] + o.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = v[e] * (sw[e] * sxj[jj]) + bv[e];
+      stage_quad<OUT_BF16, OUT_T, wr::ARR>(t0, t1, nl, 16 * (4 * Q + jj) + lr, v);
+    }
+  }
+}
+
+// Sends sub-tile columns 4 (1 - Q) .. of the wave's partials to the partner group.
+template <int Q>
+__device__ __forceinline__ void wr_send(float4* dst, const v4f (&acc)[4][8], int wn, int l) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const v4f v = acc[i][4 * (1 - Q) + jj];
+      dst[((wn * 16 + i * 4 + jj) << 6) + l] = make_float4(v[0], v[1], v[2], v[3]);
+    }
+}
+
+template <int GRAN_N, bool OUT_BF16, bool OUT_T>
+__device__ __forceinline__ void wr_tile(const GemmArgs& a, int tn, int tm, uint8_t* arr0, uint8_t* arr1) {
+  const int64_t n0 = (int64_t)tn * BN, m0 = (int64_t)tm * BM;
+  const int t = threadIdx.x, l = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int q = wave >> 2, wn = wave & 3;
+  const int g = l >> 4, lr = l & 15;
+  const int KB = (int)(a.K >> 7);
+  const int NP = (KB + wr::KPA - 1) / wr::KPA;
+
+  const int64_t mrows = min((int64_t)BM, a.M - m0);
+  const __amdgpu_buffer_rsrc_t rx = rsrc(a.x + m0 * a.ldx, (uint32_t)(mrows * a.ldx));
+  const int64_t tile_rbs = min((int64_t)(BN / PK_ROWS), (a.N + PK_ROWS - 1) / PK_ROWS - (int64_t)tn * (BN / PK_ROWS));
+  const __amdgpu_buffer_rsrc_t rw =
+      rsrc(a.w + (int64_t)tn * (BN / PK_ROWS) * KB * PK_CHUNK, (uint32_t)(tile_rbs * KB * PK_CHUNK));
+  const WrPlan plan = wr_plan(a, n0, m0, wave, l);
+  const __amdgpu_buffer_rsrc_t rs = plan.sw ? rsrc(a.sw, 0xffffffffu) : rsrc(a.sx, 0xffffffffu);
+  const int64_t s_sk = plan.sw ? a.sw_sk : a.sx_sk;
+  const uint32_t voff_v = (uint32_t)pk_val_off(lr, g), voff_m = (uint32_t)(PK_META + pk_meta_word(lr, g));
+  const uint32_t x0 = lr * 128 + (((2 * g) ^ swz8(lr)) << 4), x1 = lr * 128 + (((2 * g + 1) ^ swz8(lr)) << 4);
+  const uint32_t sxo = wr::SX_OFF + lr * 4;
+
+  v4f acc[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+  // W operands: wa / wc for the first K block of even / odd super-periods,
+  // wb for the second.  A wave's loads complete in issue order, so every W
+  // load is issued where nothing it must not wait for lies ahead of it: at a
+  // super-period's start (after waiting for its X array and W) come the W of
+  // its second K block (the only loads in flight then), the next X array,
+  // and the W of the next super-period's first K block (needed with that
+  // array).
+  WrRegs wa, wb, wc;
+  wr_issue_x(arr0, plan, rx, rs, s_sk, 0, KB, wave);
+  wr_load_w(wa, rw, voff_v, voff_m, wn, q, KB);
+
+  // Super-period P: K blocks 4 P .. 4 P + 3 in array P % 2; this wave
+  // multiplies 4 P + q and 4 P + 2 + q.  At its start all but the last
+  // wr::NW loads of the wave (the W of 4 P + q... issued after the array)
+  // have landed when the array has.
+  auto kloop = [&](auto scaled_tag) {
+    constexpr bool SCALED = decltype(scaled_tag)::value;
+    float cprev[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    // The loads are spread over the multiplies (issued all at once, a wave
+    // stalls until the memory pipeline has taken them): during the first K
+    // block the W of the second (columns 0 .. 3) and the next array (columns
+    // 4 .. 7, one K block each), during the second the W of the next
+    // super-period's first K block (columns 0 .. 3).
+    auto period = [&](uint8_t* cur, uint8_t* nxt, WrRegs& w0, WrRegs& w0next, int P) {
+      wait_vmcnt<0>();
+      lds_barrier();
+      auto issue0 = [&](int j) {
+        if (j < 4) wr_load_w1(wb, j, rw, voff_v, voff_m, wn, 4 * P + 2 + q, KB);
+        else wr_issue_x1(nxt, plan, rx, rs, s_sk, P + 1, j - 4, KB, wave);   // past the last K block: zeros
+      };
+      auto issue1 = [&](int j) {
+        if (j < 4) wr_load_w1(w0next, j, rw, voff_v, voff_m, wn, 4 * (P + 1) + q, KB);
+      };
+      if (4 * P + q < KB) {
+        wr_compute<GRAN_N, SCALED>(cur + q * wr::KBYTES, w0, acc, x0, x1, sxo, wn, cprev, issue0);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) issue0(j);
+      }
+      if (4 * P + 2 + q < KB) {
+        wr_compute<GRAN_N, SCALED>(cur + (2 + q) * wr::KBYTES, wb, acc, x0, x1, sxo, wn, cprev, issue1);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) issue1(j);
+      }
+    };
+    for (int P = 0; P < NP; P += 2) {
+      period(arr0, arr1, wa, wc, P);
+      if (P + 1 < NP) period(arr1, arr0, wc, wa, P + 1);
+    }
+    if constexpr (SCALED) {   // back to true values: acc * c_last
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] *= cprev[j];
+    }
+  };
+  if constexpr (GRAN_N == 128) {
+    if (scales_tame<2>(a, m0, n0 + wn * 64, q, KB, l)) kloop(std::true_type{});
+    else kloop(std::false_type{});
+  } else {
+    kloop(std::false_type{});
+  }
+
+  wait_vmcnt<0>();   // the last (unused) W loads
+  __syncthreads();   // every wave is done with both arrays
+  if (q == 0) wr_send<0>(reinterpret_cast<float4*>(arr1), acc, wn, l);
+  else wr_send<1>(reinterpret_cast<float4*>(arr0), acc, wn, l);
+  __syncthreads();
+  if (q == 0) wr_finish<0, GRAN_N, OUT_BF16, OUT_T>(a, arr0, arr0, arr1, acc, wn, l, m0, n0);
+  else wr_finish<1, GRAN_N, OUT_BF16, OUT_T>(a, arr1, arr0, arr1, acc, wn, l, m0, n0);
+  __syncthreads();
+  store_staged<OUT_BF16, OUT_T, wr::ARR>(a, arr0, arr1, m0, n0, t);
+}
+#endif  // SG_DEVICE_PASS
+
+template <int GRAN_N, bool OUT_BF16, bool OUT_T>
+__global__ void __launch_bounds__(512) k_gemm_sparse_wr(GemmArgs a, int tiles_m, int tiles_n) {
+#if SG_DEVICE_PASS
+  to_batch(a);
+  int tn, tm;
+  tile_coords(tiles_m, tiles_n, tn, tm);
+  __shared__ __attribute__((aligned(1024))) uint8_t arr0[wr::ARR];
+  __shared__ __attribute__((aligned(1024))) uint8_t arr1[wr::ARR];
+  wr_tile<GRAN_N, OUT_BF16, OUT_T>(a, tn, tm, arr0, arr1);
 #endif  // SG_DEVICE_PASS
 }
 
@@ -1357,7 +1817,9 @@ template <bool SPARSE, bool I8, bool PACKED, int GRAN_N, bool OUT_BF16, bool OUT
 static void launch_large(const GemmArgs& a, hipStream_t st) {
   const int tm = (int)cdiv(a.M, BM), tn = (int)cdiv(a.N, BN);
   const dim3 grid((unsigned)(tm * tn), 1, (unsigned)a.L);
-  if (SPARSE)
+  if constexpr (SPARSE && PACKED && !I8 && (GRAN_N == 128 || GRAN_N == 0))
+    k_gemm_sparse_wr<GRAN_N, OUT_BF16, OUT_T><<<grid, 512, 0, st>>>(a, tm, tn);
+  else if (SPARSE)
     k_gemm_sparse_x2<I8, PACKED, GRAN_N, OUT_BF16, OUT_T><<<grid, 512, 0, st>>>(a, tm, tn);
   else
     k_gemm_dense8<GRAN_N, OUT_BF16, OUT_T><<<grid, 512, 0, st>>>(a, tm, tn);

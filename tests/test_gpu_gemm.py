@@ -213,3 +213,48 @@ def test_packed_end_to_end_gpu_prep_chain():
     oxq, osx, owq, ometa, osw = oracle_operands(d["x"], d["w"], 1, 128, True)
     ref, bound = oracle.fp8_sparse24_gemm_groupwise(oxq, osx, 1, owq, ometa, osw, 128, bound=True)
     assert_within_tolerance(y, ref, bound, "packed end-to-end")
+
+
+# --- promotion with wide or unusual scale products ---------------------------
+# The large-M kernel keeps each wave's accumulators in units of the current K
+# block's scale product when every product the wave meets is a positive
+# normal number within a factor 2^60 of the others, and otherwise promotes
+# each block's partial from zero.  These cases put both forms in one launch.
+
+def scale_case(kind, seed, m=300, n=512, k=2048):
+    d = workloads.sparse_large(seed=seed, m=m, n=n, k=k)
+    xq, _, wq, meta, _ = oracle_operands(d["x"], d["w"], 1, 128, True)
+    g = workloads.generators(seed, 2)
+    kb = k // 128
+    sx = np.exp2(g[0].uniform(-20, 20, size=(m, kb))).astype(np.float32)
+    sw = np.exp2(g[1].uniform(-2, 2, size=(-(-n // 128), kb))).astype(np.float32)
+    if kind == "extreme_x_rows":       # rows 0..63 and 200..215: products 2^80 apart across K blocks
+        sx[0:64, 0::4] = np.float32(2.0 ** -40)
+        sx[0:64, 2::4] = np.float32(2.0 ** 40)
+        sx[200:216, 3] = np.float32(2.0 ** 70)
+    elif kind == "extreme_w_block":    # W rows 128..255: a 2^90 spread
+        sw[1, :] = np.float32(2.0 ** -45)
+        sw[1, 5] = np.float32(2.0 ** 45)
+    elif kind == "zero_and_negative":  # zero, negative and subnormal products in some rows' blocks
+        sx[10:20, 4] = 0.0
+        sx[70:90, 2] = -sx[70:90, 2]
+        sx[150:160, 7] = np.float32(1e-39)
+    elif kind == "edge_of_window":     # products exactly 2^60 apart: still the rescaled form
+        sx[:, :] = np.float32(1.0)
+        sw[:, :] = np.float32(1.0)
+        sx[0:64, 0] = np.float32(2.0 ** -30)
+        sx[0:64, 2] = np.float32(2.0 ** 30)
+    return xq, sx, wq, meta, sw
+
+
+@pytest.mark.parametrize("kind", ["wide", "extreme_x_rows", "extreme_w_block", "zero_and_negative", "edge_of_window"])
+@pytest.mark.parametrize("packed", [False, True])
+def test_scale_products_wide_and_unusual(kind, packed):
+    say(f"scale case {kind} packed={packed}")
+    xq, sx, wq, meta, sw = scale_case(kind, seed=31)
+    ref = oracle.fp8_sparse24_gemm_groupwise(xq, sx, 1, wq, meta, sw, 128)
+    # T with the magnitudes of the scale products (negative scales flip signs only)
+    _, bound = oracle.fp8_sparse24_gemm_groupwise(xq, np.abs(sx), 1, wq, meta, np.abs(sw), 128, bound=True)
+    for form in ("y", "yt"):
+        got = down(run_gemm(True, xq, sx, 1, wq, meta, sw, 128, torch.float32, form, packed=packed))
+        assert_within_tolerance((got.T if form == "yt" else got).astype(np.float64), ref, bound, f"{kind} {form}")

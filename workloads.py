@@ -99,3 +99,44 @@ def random_int8_codes(gen, shape) -> np.ndarray:
 def random_scales(gen, shape) -> np.ndarray:
     """Positive fp32 scales spread over a few binades."""
     return np.exp2(gen.uniform(-12.0, 2.0, size=shape)).astype(np.float32)
+
+
+def small_ints(gen, shape, vmax: int) -> np.ndarray:
+    """Integer-valued fp32 in [-vmax, vmax] (every such value is an exact e4m3,
+    int8 and bf16 number for vmax <= 16)."""
+    return gen.integers(-vmax, vmax + 1, size=shape).astype(np.float32)
+
+
+def two_of_four_ints(gen, shape, vmax: int) -> np.ndarray:
+    """Integer-valued fp32 [rows, k] with exactly two nonzero entries, each in
+    +-[1, vmax], at random positions of every aligned group of four along k."""
+    rows, k = shape
+    g = k // 4
+    # positions: a random pair out of the 6 pairs of a group of four
+    pairs = np.array([(0, 1), (0, 2), (0, 3), (1, 2), (1, 3), (2, 3)])
+    pick = pairs[gen.integers(0, 6, size=(rows, g))]                       # [rows, g, 2]
+    mag = gen.integers(1, vmax + 1, size=(rows, g, 2))
+    sign = np.where(gen.random((rows, g, 2)) < 0.5, -1, 1)
+    out = np.zeros((rows, g, 4), dtype=np.float32)
+    r_idx = np.arange(rows)[:, None, None]
+    g_idx = np.arange(g)[None, :, None]
+    out[r_idx, g_idx, pick] = (mag * sign).astype(np.float32)
+    return out.reshape(rows, k)
+
+
+def pow2_scales(gen, shape, emin: int, emax: int) -> np.ndarray:
+    """fp32 powers of two 2^e, e uniform in [emin, emax]."""
+    return np.exp2(gen.integers(emin, emax + 1, size=shape)).astype(np.float32)
+
+
+def exact_ints(seed: int, m: int, n: int, k: int, vmax: int = 3, emin: int = -1, emax: int = 1,
+               x_scale_rows: int = None, w_scale_rows: int = None):
+    """Operands whose GEMM is exact in fp32: integer-valued X [m, k] in
+    [-vmax, vmax], W [n, k] with two integer nonzeros per group of four, and
+    power-of-two scales for X [x_scale_rows, k/128] and W [w_scale_rows, k/128]
+    (defaults: one per X row, one per 128 W rows)."""
+    gx, gw, gsx, gsw = generators(seed, 4)
+    xs = m if x_scale_rows is None else x_scale_rows
+    ws = -(-n // 128) if w_scale_rows is None else w_scale_rows
+    return {"x": small_ints(gx, (m, k), vmax), "w": two_of_four_ints(gw, (n, k), vmax),
+            "sx": pow2_scales(gsx, (xs, k // 128), emin, emax), "sw": pow2_scales(gsw, (ws, k // 128), emin, emax)}
