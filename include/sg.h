@@ -26,10 +26,17 @@
  *   - Arguments are validated on the host BEFORE any HIP call; an invalid call
  *     returns an error status and enqueues nothing.  A launch failure reported
  *     by the HIP runtime returns SG_ERR_HIP.
- *   - An empty problem (rows == 0, or M == 0 or N == 0) is valid: SG_OK, nothing
- *     is enqueued.
- *   - Inputs must be finite; the results for NaN or infinite inputs are
- *     unspecified (but every access stays within the described buffers).
+ *   - Every size argument (rows, cols, M, N, K, L, G) must be at least 1: a
+ *     zero or negative size is SG_ERR_SHAPE and enqueues nothing.  The pages
+ *     describe no empty problem; a caller with nothing to do makes no call.
+ *     (Only single groups of the grouped GEMM may be empty.)  The mixed GEMM's
+ *     K2 may be 0.
+ *   - Non-finite inputs (the pages say nothing of them) follow IEEE arithmetic
+ *     through the documented formulas: a quantiser block holding a NaN gets a
+ *     NaN scale and one holding an infinity an infinite scale; e4m3 encoding
+ *     saturates infinities to +-448 and gives every NaN the code 0x7F; an int8
+ *     or int4 code of a NaN is 0; bf16 outputs keep NaN as NaN; pruning ranks
+ *     NaN above every number.  Every access stays within the described buffers.
  */
 #ifndef SPARSE_GEMM_LAYERS_AMD_SG_H
 #define SPARSE_GEMM_LAYERS_AMD_SG_H
@@ -41,16 +48,21 @@
 extern "C" {
 #endif
 
-typedef enum {
+/* Status, dtype and output-form codes are plain 32-bit ints with named
+ * values, so that any int a caller passes is a valid argument (an unknown
+ * value is rejected with SG_ERR_UNSUPPORTED, never undefined behaviour). */
+typedef int32_t sg_status;
+enum {
   SG_OK = 0,
   SG_ERR_NULL = 1,        /* a required pointer is NULL                          */
   SG_ERR_SHAPE = 2,       /* a size or leading dimension is out of range         */
   SG_ERR_UNSUPPORTED = 3, /* granularity, dtype or output form not supported     */
   SG_ERR_ALIGN = 4,       /* a pointer or leading dimension is misaligned        */
   SG_ERR_HIP = 5          /* the HIP runtime reported an error at launch         */
-} sg_status;
+};
 
-typedef enum { SG_F32 = 0, SG_BF16 = 1, SG_E4M3 = 2, SG_I8 = 3 } sg_dtype;
+typedef int32_t sg_dtype;
+enum { SG_F32 = 0, SG_BF16 = 1, SG_E4M3 = 2, SG_I8 = 3 };
 
 /* Output form of the GEMMs.  Both compute the same numbers.
  *   SG_OUT_Y : Y   [M, N] row-major, element (m, n) at y[m * ldy + n]
@@ -58,13 +70,14 @@ typedef enum { SG_F32 = 0, SG_BF16 = 1, SG_E4M3 = 2, SG_I8 = 3 } sg_dtype;
  * SG_OUT_YT is the swap+transpose form C^T = B^T . A^T of [I2029] (klevzoff's
  * answer: swap the operands and flip the layout of C/D), which puts the sparse
  * weight on the left. */
-typedef enum { SG_OUT_Y = 0, SG_OUT_YT = 1 } sg_form;
+typedef int32_t sg_form;
+enum { SG_OUT_Y = 0, SG_OUT_YT = 1 };
 
-/* Human-readable name of a status code (static string, never NULL). */
+/* Human-readable name of a status code (static string, never NULL; any value). */
 const char* sg_status_str(sg_status s);
 
 /* Version of this ABI; bumped on any incompatible change (2: the int4
- * quantiser takes its group width). */
+ * quantiser takes its group width; 3: empty problems are SG_ERR_SHAPE). */
 int sg_abi_version(void);
 
 /*
@@ -75,7 +88,8 @@ int sg_abi_version(void);
  * float8_e4m3fn).
  *
  * For each block of gr rows x gc columns (the last row block may be partial):
- *   amax = max |x|;  s = amax / 448 in fp32 (s = 1 if amax == 0);
+ *   amax = max |x|;  s = amax / 448 in fp32 (s = 1 if amax == 0; NaN if the
+ *          block holds a NaN);
  *   q    = e4m3(x / s): IEEE fp32 divide, round to nearest even, saturate at
  *          +-448, a negative value that rounds to zero gives -0 (0x80).
  *   x   : [rows, cols], dtype x_dt (SG_F32 or SG_BF16), leading dim ldx.
@@ -120,10 +134,12 @@ sg_status sg_int4_quant_groupwise(const void* x, sg_dtype x_dt, int64_t rows, in
  * along a row, the two smallest |w| are dropped; store only the specified
  * values and the sparsity metadata.  [I2029] klevzoff: the sparse operand is
  * passed as values + metadata E.
- *   Kept: the two largest |w| of each group; equal magnitudes -> lower index.
+ *   Kept: the two largest |w| of each group; equal magnitudes -> lower index
+ *   (+0 and -0 are equal); NaN ranks above every number, NaNs are equal.
  *   vals[r, 2g + j] = w[r, 4g + i_j] with i_0 < i_1 (bits copied unchanged);
  *   meta[r, b]      = nib(2b) | nib(2b + 1) << 4,  nib(g) = i_0 | i_1 << 2.
- *   w    : [rows, k], dtype dt (SG_F32 or SG_BF16), leading dim ldw.
+ *   w    : [rows, k], dtype dt (SG_F32, SG_BF16, or SG_E4M3 codes: a weight
+ *          already quantised, whose codes' magnitudes are ranked), leading dim ldw.
  *   vals : [rows, k/2], same dtype, leading dim ldv.
  *   meta : [rows, k/8] bytes, leading dim ldm.
  * Requires k % 8 == 0, ldw >= k, ldv >= k/2, ldm >= k/8; w and vals 16-byte
@@ -144,7 +160,7 @@ sg_status sg_sparse24_prune_compress(const void* w, sg_dtype dt, int64_t rows, i
  *   wq : [N, K] e4m3, ld ldw.   sw: (n/gran_n, kb) at sw[(n/gran_n)*sw_sn + kb*sw_sk].
  *   gran_m, gran_n : 1 or 128.
  *   y  : SG_F32 or SG_BF16 (round to nearest even) in the layout `form` selects.
- * Requires K % 128 == 0, K > 0, M, N >= 0, ldx, ldw >= K; xq, wq 16-byte aligned,
+ * Requires K % 128 == 0, K > 0, M, N >= 1, ldx, ldw >= K; xq, wq 16-byte aligned,
  * ldx, ldw multiples of 16; ldy >= N (SG_OUT_Y) or >= M (SG_OUT_YT); y aligned to
  * its element size.  M and N need not be multiples of any tile (the partial M
  * and N tiles of [P2095] are predicated).
@@ -311,7 +327,7 @@ sg_status sg_int8_sparse24_gemm_groupwise_packed(int64_t M, int64_t N, int64_t K
  * 4-byte aligned; bias[n] is added to output row n of every column after the
  * scales and before the output rounding (the `bias` argument of the sparse
  * FP8 linear that jcaip's review in [T3258] points to).
- * Requires in addition 0 <= L <= 65535 (L == 0: SG_OK, nothing enqueued),
+ * Requires in addition 1 <= L <= 65535,
  * every batch stride >= 0, and x_bs, w_bs / wv_bs / wp_bs, wm_bs multiples of 16
  * (SG_ERR_ALIGN otherwise).  Outputs of different problems must not overlap;
  * inputs may (a zero weight stride shares one weight among the problems).
@@ -394,7 +410,7 @@ sg_status sg_w4a16_sparse24_gemm_groupwise(int64_t M, int64_t N, int64_t K, cons
  * launch covers every group's 128-row tiles ([P2095] PR description: the L mode
  * of the scale layout; this form lets L's problems differ in M).
  *   m_sizes : HOST array of G entries >= 0 (0: an empty group).
- * Requires 0 <= G <= 64, sum(m_sizes) as M and all requirements of the packed
+ * Requires 1 <= G <= 64, sum(m_sizes) >= 1 as M and all requirements of the packed
  * entry point and of the batched forms' strides; bias may be NULL.
  */
 sg_status sg_fp8_sparse24_gemm_groupwise_packed_grouped(int64_t G, const int64_t* m_sizes, int64_t N, int64_t K,

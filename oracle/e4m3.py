@@ -15,9 +15,10 @@ e = (c>>3)&15, mantissa m = c&7:
     otherwise          -> (-1)^s * (1 + m/8) * 2^(e-7)
 
 Encode: round |v| to the nearest finite E4M3 magnitude, ties to the code with
-an even mantissa LSB, saturate magnitudes above 448 to 448, and keep the sign
-bit of v (so a negative value that rounds to zero gives 0x80, -0).  NaN input
-gives 0x7F with v's sign bit.
+an even mantissa LSB, saturate magnitudes above 448 to 448 (infinities
+included), and keep the sign bit of v (so a negative value that rounds to zero
+gives 0x80, -0).  Every NaN input gives 0x7F: the format has a NaN code for each
+sign, the pages fix no NaN handling, and the reading here is one canonical code.
 """
 
 import numpy as np
@@ -65,6 +66,5 @@ def e4m3_encode(v) -> np.ndarray:
     # On a tie between codes lo and lo+1 pick the even one.
     code = np.where(tie & (code % 2 == 1), code + 1, code)
     code = np.minimum(code, 0x7E)                        # saturate to 448
-    nan = np.isnan(a)
-    code = np.where(nan, 0x7F, code)
-    return (code.astype(np.uint8) | sign).astype(np.uint8)
+    code = (code.astype(np.uint8) | sign).astype(np.uint8)
+    return np.where(np.isnan(a), np.uint8(0x7F), code).astype(np.uint8)

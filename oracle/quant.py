@@ -16,6 +16,12 @@ FP8 (``fp8_quant_groupwise``), following
 Per block:  amax = max |v|;  s = fl32(amax / 448)  (or s = 1 when amax == 0);
 code = e4m3_encode(fl32(v / s)) with IEEE fp32 correctly rounded divides.
 
+Non-finite inputs (the pages say nothing of them; the reading here lets IEEE
+arithmetic run through the same formulas): amax is NaN when the block holds a
+NaN (a maximum that ignored NaN would hide it) and +inf when it holds an
+infinity, so s is NaN or +inf; codes are still the encoder applied to v / s,
+where e4m3 gives 0x7F for NaN and the integer grids give 0.
+
 int4 (``int4_quant_groupwise``), for CUTLASS issue #2058 "[QST] How to
 implement a fused mixed precision matrix multiplication such as w4a4 +
 w16a16?" (hyx1999: X1 and W1 are quantised to 4 bit).  The page fixes no
@@ -39,13 +45,20 @@ from .e4m3 import E4M3_MAX, e4m3_encode
 
 
 def _block_amax(x32: np.ndarray, gr: int, gc: int) -> np.ndarray:
-    """max |v| over each gr x gc block; edge blocks are partial (padding with
-    zeros does not change a maximum of absolute values)."""
+    """max |v| over each gr x gc block, NaN if the block holds one (numpy's max
+    propagates NaN); edge blocks are partial (padding with zeros does not
+    change a maximum of absolute values)."""
     rows, cols = x32.shape
     rb, cb = -(-rows // gr), -(-cols // gc)
     a = np.zeros((rb * gr, cb * gc), dtype=np.float32)
     a[:rows, :cols] = np.abs(x32)
     return a.reshape(rb, gr, cb, gc).max(axis=(1, 3))
+
+
+def _int_codes(q: np.ndarray, qmax: int) -> np.ndarray:
+    """clamp(rint_even(q), -qmax, qmax) as int64 (an infinite q clamps); NaN -> 0."""
+    nan = np.isnan(q)
+    return np.where(nan, 0, np.clip(np.rint(np.where(nan, 0, q)), -qmax, qmax)).astype(np.int64)
 
 
 def _expand(s: np.ndarray, gr: int, gc: int, rows: int, cols: int) -> np.ndarray:
@@ -58,8 +71,9 @@ def fp8_quant_groupwise(x, gr: int, gc: int):
     x32 = np.asarray(x, dtype=np.float32)
     rows, cols = x32.shape
     amax = _block_amax(x32, gr, gc)
-    s = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
-    q = (x32 / _expand(s, gr, gc, rows, cols)).astype(np.float32)   # fp32 IEEE divide
+    s = np.where(amax == 0, np.float32(1.0), amax / np.float32(E4M3_MAX)).astype(np.float32)
+    with np.errstate(invalid="ignore"):                              # inf / inf -> NaN
+        q = (x32 / _expand(s, gr, gc, rows, cols)).astype(np.float32)   # fp32 IEEE divide
     codes = e4m3_encode(q)
     return codes, s
 
@@ -71,9 +85,10 @@ def int4_quant_groupwise(x, gc: int = 128):
     rows, cols = x32.shape
     assert cols % 2 == 0
     amax = _block_amax(x32, 1, gc)
-    s = np.where(amax > 0, amax / np.float32(7.0), np.float32(1.0)).astype(np.float32)
-    q = (x32 / _expand(s, 1, gc, rows, cols)).astype(np.float32)
-    qi = np.clip(np.rint(q), -7, 7).astype(np.int64)                 # rint: ties to even
+    s = np.where(amax == 0, np.float32(1.0), amax / np.float32(7.0)).astype(np.float32)
+    with np.errstate(invalid="ignore"):
+        q = (x32 / _expand(s, 1, gc, rows, cols)).astype(np.float32)
+    qi = _int_codes(q, 7)
     nib = (qi & 0xF).astype(np.uint8)
     packed = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
     return packed, s
@@ -85,9 +100,10 @@ def int8_quant_groupwise(x, gr: int, gc: int):
     x32 = np.asarray(x, dtype=np.float32)
     rows, cols = x32.shape
     amax = _block_amax(x32, gr, gc)
-    s = np.where(amax > 0, amax / np.float32(127.0), np.float32(1.0)).astype(np.float32)
-    q = (x32 / _expand(s, gr, gc, rows, cols)).astype(np.float32)   # fp32 IEEE divide
-    codes = np.clip(np.rint(q), -127, 127).astype(np.int8)            # rint: ties to even
+    s = np.where(amax == 0, np.float32(1.0), amax / np.float32(127.0)).astype(np.float32)
+    with np.errstate(invalid="ignore"):
+        q = (x32 / _expand(s, gr, gc, rows, cols)).astype(np.float32)   # fp32 IEEE divide
+    codes = _int_codes(q, 127).astype(np.int8)
     return codes, s
 
 

@@ -8,7 +8,13 @@ jcaip's review comments on the pruning code: the weight is viewed in groups of
 |w|) are set to zero and the other two survive.  The pages do not say how equal
 magnitudes are ordered; the reading here is that the larger magnitude wins
 and, between equal magnitudes, the lower index wins (+0 and -0 are equal).
-Pruned entries become +0.0; survivors keep their bits.
+Nor do they say where NaN goes; the reading here ranks NaN above every number
+(a NaN weight is never silently dropped) with all NaNs equal.  Pruned entries
+become zero (+0.0, or code 0x00); survivors keep their bits.
+
+Weights may be fp32, bf16 bit patterns (uint16) or e4m3 codes (uint8, a weight
+quantised before pruning, as the FP8 path of that PR can take it): the codes
+are decoded to their values and ranked by magnitude like any other weight.
 
 Storage follows the same review ("store the specified values and the sparse
 metadata", not a dense copy) and the operand triple of CUTLASS issue #2029
@@ -21,12 +27,18 @@ pages fix no metadata bit layout; the layout used here is:
 
 import numpy as np
 
+from .e4m3 import e4m3_decode
 
-def _magnitude(w) -> np.ndarray:
+
+def _values(w) -> np.ndarray:
+    """The weights' values in fp64 (exact for all three formats)."""
     w = np.asarray(w)
-    if w.dtype == np.uint16:            # bf16 bits
-        return np.abs((w.astype(np.uint32) << 16).view(np.float32)).astype(np.float64)
-    return np.abs(np.asarray(w, dtype=np.float32).astype(np.float64))
+    with np.errstate(invalid="ignore"):  # signalling-NaN patterns widen to NaN
+        if w.dtype == np.uint16:         # bf16 bits
+            return (w.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        if w.dtype == np.uint8:          # e4m3 codes
+            return e4m3_decode(w)
+        return np.asarray(w, dtype=np.float32).astype(np.float64)
 
 
 def prune24(w):
@@ -35,10 +47,12 @@ def prune24(w):
     w = np.asarray(w)
     rows, k = w.shape
     assert k % 4 == 0
-    mag = _magnitude(w).reshape(rows, k // 4, 4)
-    # Rank each group by (-|w|, index): a stable sort on -|w| keeps index order
-    # among equal magnitudes; the first two of that order survive.
-    order = np.argsort(-mag, axis=-1, kind="stable")
+    v = _values(w).reshape(rows, k // 4, 4)
+    nan = np.isnan(v)
+    mag = np.where(nan, 0.0, np.abs(v))
+    # Rank each group by (NaN first, then -|w|, then index): lexsort is stable,
+    # so equal keys keep index order; the first two of that order survive.
+    order = np.lexsort((-mag, ~nan), axis=-1)
     keep = np.zeros((rows, k // 4, 4), dtype=bool)
     np.put_along_axis(keep, order[..., :2], True, axis=-1)
     keep = keep.reshape(rows, k)

@@ -12,7 +12,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libsg.so")
+# SG_LIBRARY selects another build of the same library (the host-sanitizer
+# build of the CPU-only ABI tests); by default the in-tree libsg.so.
+LIB_PATH = os.environ.get("SG_LIBRARY") or os.path.join(_HERE, "libsg.so")
 
 SG_F32, SG_BF16, SG_E4M3, SG_I8 = 0, 1, 2, 3
 SG_OUT_Y, SG_OUT_YT = 0, 1
@@ -113,6 +115,56 @@ def _dtype_code(t, name):
     raise SgError(f"{name}: dtype {t.dtype} not supported (float32 or bfloat16)")
 
 
+_NAMES = {torch.float32: "float32", torch.bfloat16: "bfloat16", torch.uint8: "uint8", torch.int8: "int8",
+          torch.int16: "int16", torch.uint16: "uint16"}
+
+
+def _want(t, name, dtypes, shape, device):
+    """t must be a GPU tensor on `device` with one of `dtypes` and exactly
+    `shape` (None entries: any size)."""
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise SgError(f"{name} must be a GPU tensor")
+    if t.device != device:
+        raise SgError(f"{name} is on {t.device}, the operands on {device}")
+    if t.dtype not in dtypes:
+        raise SgError(f"{name}: dtype {t.dtype} not supported ({' or '.join(_NAMES[d] for d in dtypes)})")
+    if t.dim() != len(shape) or any(w is not None and w != h for w, h in zip(shape, t.shape)):
+        want = ", ".join("*" if w is None else str(w) for w in shape)
+        raise SgError(f"{name} must have shape [{want}], got {list(t.shape)}")
+    return t
+
+
+def _want_scales(s, name, rows, kb, device, batch=None):
+    """fp32 GPU scales [rows, kb] (any strides), or [L, rows, kb] / a shared
+    [rows, kb] when batch = L; rows may be larger than needed."""
+    if not isinstance(s, torch.Tensor) or not s.is_cuda or s.dtype != torch.float32:
+        raise SgError(f"{name} must be a float32 GPU tensor")
+    if s.device != device:
+        raise SgError(f"{name} is on {s.device}, the operands on {device}")
+    if batch is not None and s.dim() == 3:
+        if s.shape[0] not in (1, batch):
+            raise SgError(f"{name} holds {s.shape[0]} problems, not {batch}")
+        s2 = s.shape[1:]
+    elif s.dim() == 2:
+        s2 = s.shape
+    else:
+        raise SgError(f"{name} must be 2-D [rows, K/128]" + (" or 3-D [L, rows, K/128]" if batch else ""))
+    if s2[0] < rows or s2[1] < kb:
+        raise SgError(f"{name} must cover [{rows}, {kb}] scales, got {list(s.shape)}")
+    return s
+
+
+def _positive(**sizes):
+    for k, v in sizes.items():
+        if v <= 0:
+            raise SgError(f"{k} must be at least 1, got {v}")
+
+
+_CODES = (torch.uint8,)
+_I8 = (torch.int8,)
+_FB = (torch.float32, torch.bfloat16)
+
+
 def _row_stride(t):
     return t.stride(0) if t.shape[0] > 1 else max(t.shape[1], 1)
 
@@ -127,11 +179,13 @@ def fp8_quant_groupwise(x, gr: int = 1, gc: int = 128, q=None, s=None):
     [ceil(rows/gr), cols/gc]).  One scale per gr x gc block: amax / 448."""
     _gpu2d(x, "x")
     rows, cols = x.shape
+    _positive(rows=rows, cols=cols, gr=gr, gc=gc)
     if q is None:
         q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
     if s is None:
-        s = _scales(-(-rows // gr), cols // gc if gc else 0, x.device)
-    _gpu2d(q, "q")
+        s = _scales(-(-rows // gr), cols // gc, x.device)
+    _gpu2d(_want(q, "q", _CODES, (rows, cols), x.device), "q")
+    _want_scales(s, "s", -(-rows // gr), cols // gc, x.device)
     st = lib().sg_fp8_quant_groupwise(_p(x), _dtype_code(x, "x"), rows, cols, _row_stride(x), gr, gc,
                                       _p(q), _row_stride(q), _p(s), s.stride(0), s.stride(1), _stream(x))
     _check(st, "sg_fp8_quant_groupwise")
@@ -143,11 +197,13 @@ def int8_quant_groupwise(x, gr: int = 1, gc: int = 128, q=None, s=None):
     [ceil(rows/gr), cols/gc]).  One scale per gr x gc block: amax / 127."""
     _gpu2d(x, "x")
     rows, cols = x.shape
+    _positive(rows=rows, cols=cols, gr=gr, gc=gc)
     if q is None:
         q = torch.empty((rows, cols), dtype=torch.int8, device=x.device)
     if s is None:
-        s = _scales(-(-rows // gr), cols // gc if gc else 0, x.device)
-    _gpu2d(q, "q")
+        s = _scales(-(-rows // gr), cols // gc, x.device)
+    _gpu2d(_want(q, "q", _I8, (rows, cols), x.device), "q")
+    _want_scales(s, "s", -(-rows // gr), cols // gc, x.device)
     st = lib().sg_int8_quant_groupwise(_p(x), _dtype_code(x, "x"), rows, cols, _row_stride(x), gr, gc,
                                        _p(q), _row_stride(q), _p(s), s.stride(0), s.stride(1), _stream(x))
     _check(st, "sg_int8_quant_groupwise")
@@ -158,11 +214,13 @@ def int4_quant_groupwise(x, gc: int = 128, q=None, s=None):
     """x [rows, cols] -> (packed int4 uint8 [rows, cols/2], scales fp32 [rows, cols/gc]); gc 128 or 64."""
     _gpu2d(x, "x")
     rows, cols = x.shape
+    _positive(rows=rows, cols=cols, gc=gc)
     if q is None:
         q = torch.empty((rows, cols // 2), dtype=torch.uint8, device=x.device)
     if s is None:
         s = _scales(rows, cols // gc, x.device)
-    _gpu2d(q, "q")
+    _gpu2d(_want(q, "q", _CODES, (rows, cols // 2), x.device), "q")
+    _want_scales(s, "s", rows, cols // gc, x.device)
     st = lib().sg_int4_quant_groupwise(_p(x), _dtype_code(x, "x"), rows, cols, _row_stride(x), gc, _p(q),
                                        _row_stride(q), _p(s), s.stride(0), s.stride(1), _stream(x))
     _check(st, "sg_int4_quant_groupwise")
@@ -170,27 +228,45 @@ def int4_quant_groupwise(x, gc: int = 128, q=None, s=None):
 
 
 def sparse24_prune_compress(w, vals=None, meta=None):
-    """w [rows, k] float32/bfloat16 -> (values [rows, k/2] same dtype, metadata uint8 [rows, k/8])."""
+    """w [rows, k] float32, bfloat16 or uint8 (e4m3 codes) -> (values [rows, k/2]
+    same dtype, metadata uint8 [rows, k/8])."""
     _gpu2d(w, "w")
     rows, k = w.shape
+    _positive(rows=rows, k=k)
+    dt = SG_E4M3 if w.dtype == torch.uint8 else _dtype_code(w, "w")
     if vals is None:
         vals = torch.empty((rows, k // 2), dtype=w.dtype, device=w.device)
     if meta is None:
         meta = torch.empty((rows, k // 8), dtype=torch.uint8, device=w.device)
-    _gpu2d(vals, "vals")
-    _gpu2d(meta, "meta")
-    st = lib().sg_sparse24_prune_compress(_p(w), _dtype_code(w, "w"), rows, k, _row_stride(w), _p(vals),
+    _gpu2d(_want(vals, "vals", (w.dtype,), (rows, k // 2), w.device), "vals")
+    _gpu2d(_want(meta, "meta", _CODES, (rows, k // 8), w.device), "meta")
+    st = lib().sg_sparse24_prune_compress(_p(w), dt, rows, k, _row_stride(w), _p(vals),
                                           _row_stride(vals), _p(meta), _row_stride(meta), _stream(w))
     _check(st, "sg_sparse24_prune_compress")
     return vals, meta
 
 
 def _out(y, M, N, out_dtype, form, device):
+    if form not in ("y", "yt", SG_OUT_Y, SG_OUT_YT):
+        raise SgError(f"form must be 'y' or 'yt', got {form!r}")
     yt = form in ("yt", SG_OUT_YT)
     if y is None:
         y = torch.empty((N, M) if yt else (M, N), dtype=out_dtype, device=device)
-    _gpu2d(y, "y")
+    _gpu2d(_want(y, "y", _FB, (N, M) if yt else (M, N), device), "y")
     return y, (SG_OUT_YT if yt else SG_OUT_Y), _dtype_code(y, "y")
+
+
+def _gemm_operands(xq, x_dtypes, M, N, K, sx, gran_m, sw, gran_n):
+    """Shape and dtype checks shared by the single-problem GEMMs."""
+    _positive(M=M, N=N, K=K)
+    if K % 128:
+        raise SgError(f"K must be a multiple of 128, got {K}")
+    _want(xq, "xq", x_dtypes, (M, K), xq.device)
+    if gran_m not in (1, 128) or gran_n not in (1, 128):
+        raise SgError("gran_m and gran_n must be 1 or 128")
+    _want_scales(sx, "sx", -(-M // gran_m), K // 128, xq.device)
+    if sw is not None:
+        _want_scales(sw, "sw", -(-N // gran_n), K // 128, xq.device)
 
 
 def fp8_gemm_groupwise(xq, sx, wq, sw, gran_m: int = 1, gran_n: int = 128, out_dtype=torch.bfloat16,
@@ -201,6 +277,8 @@ def fp8_gemm_groupwise(xq, sx, wq, sw, gran_m: int = 1, gran_n: int = 128, out_d
     _gpu2d(wq, "wq")
     M, K = xq.shape
     N = wq.shape[0]
+    _gemm_operands(xq, _CODES, M, N, K, sx, gran_m, sw, gran_n)
+    _want(wq, "wq", _CODES, (N, K), xq.device)
     y, f, ydt = _out(y, M, N, out_dtype, form, xq.device)
     st = lib().sg_fp8_gemm_groupwise(M, N, K, _p(xq), _row_stride(xq), _p(sx), sx.stride(0), sx.stride(1),
                                      gran_m, _p(wq), _row_stride(wq), _p(sw), sw.stride(0), sw.stride(1),
@@ -218,6 +296,9 @@ def fp8_sparse24_gemm_groupwise(xq, sx, wv, wmeta, sw, gran_m: int = 1, gran_n: 
     _gpu2d(wmeta, "wmeta")
     M, K = xq.shape
     N = wv.shape[0]
+    _gemm_operands(xq, _CODES, M, N, K, sx, gran_m, sw, gran_n)
+    _want(wv, "wv", _CODES, (N, K // 2), xq.device)
+    _want(wmeta, "wmeta", _CODES, (N, K // 8), xq.device)
     y, f, ydt = _out(y, M, N, out_dtype, form, xq.device)
     st = lib().sg_fp8_sparse24_gemm_groupwise(M, N, K, _p(xq), _row_stride(xq), _p(sx), sx.stride(0),
                                               sx.stride(1), gran_m, _p(wv), _row_stride(wv), _p(wmeta),
@@ -266,11 +347,36 @@ def _sc(t):
 
 
 def _out_batched(y, L, M, N, out_dtype, form, device):
+    if form not in ("y", "yt", SG_OUT_Y, SG_OUT_YT):
+        raise SgError(f"form must be 'y' or 'yt', got {form!r}")
     yt = form in ("yt", SG_OUT_YT)
     if y is None:
         y = torch.empty((L, N, M) if yt else (L, M, N), dtype=out_dtype, device=device)
-    _gpu3d(y, "y")
+    _gpu3d(_want(y, "y", _FB, (L, N, M) if yt else (L, M, N), device), "y")
     return y, (SG_OUT_YT if yt else SG_OUT_Y), _dtype_code(y, "y")
+
+
+def _want_shared(t, name, dtypes, L, rows, cols, device):
+    """[L, rows, cols] (one per problem; L may be 1) or [rows, cols] (shared)."""
+    if isinstance(t, torch.Tensor) and t.dim() == 3:
+        _want(t, name, dtypes, (None, rows, cols), device)
+        if t.shape[0] not in (1, L):
+            raise SgError(f"{name} holds {t.shape[0]} problems, not {L}")
+        return t
+    return _want(t, name, dtypes, (rows, cols), device)
+
+
+def _batched_operands(xq, x_dtypes, sx, gran_m, sw, gran_n):
+    _gpu3d(xq, "xq")
+    L, M, K = xq.shape
+    _positive(L=L, M=M, K=K)
+    if K % 128:
+        raise SgError(f"K must be a multiple of 128, got {K}")
+    _want(xq, "xq", x_dtypes, (L, M, K), xq.device)
+    if gran_m not in (1, 128) or gran_n not in (1, 128):
+        raise SgError("gran_m and gran_n must be 1 or 128")
+    _want_scales(sx, "sx", -(-M // gran_m), K // 128, xq.device, batch=L)
+    return L, M, K
 
 
 def _bias(bias, N):
@@ -288,9 +394,11 @@ def fp8_gemm_groupwise_batched(xq, sx, wq, sw, gran_m: int = 1, gran_n: int = 12
     """L independent GEMMs: xq uint8 [L, M, K], sx [L, ceil(M/gran_m), K/128];
     wq uint8 [L, N, K] and sw [L, ., K/128], or 2-D to share one weight.  Returns
     y [L, M, N] ("y") or [L, N, M] ("yt")."""
-    _gpu3d(xq, "xq")
-    L, M, K = xq.shape
+    L, M, K = _batched_operands(xq, _CODES, sx, gran_m, sw, gran_n)
     N, ldw = _mat(wq, "wq")
+    _positive(N=N)
+    _want_shared(wq, "wq", _CODES, L, N, K, xq.device)
+    _want_scales(sw, "sw", -(-N // gran_n), K // 128, xq.device, batch=L)
     y, f, ydt = _out_batched(y, L, M, N, out_dtype, form, xq.device)
     sxm, sxk, sxb = _sc(sx)
     swn, swk, swb = _sc(sw)
@@ -305,10 +413,13 @@ def fp8_gemm_groupwise_batched(xq, sx, wq, sw, gran_m: int = 1, gran_n: int = 12
 def fp8_sparse24_gemm_groupwise_batched(xq, sx, wv, wmeta, sw, gran_m: int = 1, gran_n: int = 128,
                                         out_dtype=torch.bfloat16, form: str = "y", y=None, bias=None):
     """Batched 2:4 GEMM: wv [L, N, K/2] and wmeta [L, N, K/8] (or 2-D, shared)."""
-    _gpu3d(xq, "xq")
-    L, M, K = xq.shape
+    L, M, K = _batched_operands(xq, _CODES, sx, gran_m, sw, gran_n)
     N, ldwv = _mat(wv, "wv")
     _, ldwm = _mat(wmeta, "wmeta")
+    _positive(N=N)
+    _want_shared(wv, "wv", _CODES, L, N, K // 2, xq.device)
+    _want_shared(wmeta, "wmeta", _CODES, L, N, K // 8, xq.device)
+    _want_scales(sw, "sw", -(-N // gran_n), K // 128, xq.device, batch=L)
     y, f, ydt = _out_batched(y, L, M, N, out_dtype, form, xq.device)
     sxm, sxk, sxb = _sc(sx)
     swn, swk, swb = _sc(sw)
@@ -325,12 +436,10 @@ def fp8_sparse24_gemm_groupwise_packed_batched(xq, sx, wpacked, n: int, sw, gran
                                                out_dtype=torch.bfloat16, form: str = "y", y=None, bias=None):
     """Batched 2:4 GEMM with packed weights: wpacked uint8 [L, bytes] (one packed
     weight per problem) or 1-D (shared)."""
-    _gpu3d(xq, "xq")
-    L, M, K = xq.shape
-    need = sparse24_packed_bytes(n, K)
-    if not isinstance(wpacked, torch.Tensor) or not wpacked.is_cuda or wpacked.dim() not in (1, 2) \
-            or wpacked.shape[-1] < need or wpacked.stride(-1) != 1:
-        raise SgError("wpacked must be a GPU tensor [L, bytes] or [bytes] holding a packed weight")
+    L, M, K = _batched_operands(xq, _CODES, sx, gran_m, sw, gran_n)
+    _positive(N=n)
+    _want_packed(wpacked, n, K, xq.device, batch=L)
+    _want_scales(sw, "sw", -(-n // gran_n), K // 128, xq.device, batch=L)
     wpb = 0 if wpacked.dim() == 1 or wpacked.shape[0] == 1 else wpacked.stride(0)
     y, f, ydt = _out_batched(y, L, M, n, out_dtype, form, xq.device)
     sxm, sxk, sxb = _sc(sx)
@@ -352,15 +461,14 @@ def fp8_sparse24_gemm_groupwise_packed_grouped(xq, sx, m_sizes, wpacked, n: int,
     sizes = [int(v) for v in m_sizes]
     if not isinstance(xq, torch.Tensor) or not xq.is_cuda or xq.dim() != 2 or sum(sizes) != xq.shape[0]:
         raise SgError("xq must be a 2-D GPU tensor whose rows m_sizes sums to")
-    if xq.shape[0] == 0 or n == 0:     # nothing to compute (and empty tensors carry no device address)
-        return _out(y, xq.shape[0], n, out_dtype, form, xq.device)[0]
+    if any(v < 0 for v in sizes):
+        raise SgError("m_sizes must be non-negative")
     _gpu2d(xq, "xq")
     M, K = xq.shape
     G = len(sizes)
-    need = sparse24_packed_bytes(n, K)
-    if not isinstance(wpacked, torch.Tensor) or not wpacked.is_cuda or wpacked.dim() not in (1, 2) \
-            or wpacked.shape[-1] < need or wpacked.stride(-1) != 1:
-        raise SgError("wpacked must be a GPU tensor [G, bytes] or [bytes] holding a packed weight")
+    _gemm_operands(xq, _CODES, M, n, K, sx, 1, None, gran_n)
+    _want_scales(sw, "sw", -(-n // gran_n), K // 128, xq.device, batch=G)
+    _want_packed(wpacked, n, K, xq.device, batch=G)
     wpb = 0 if wpacked.dim() == 1 or wpacked.shape[0] == 1 else wpacked.stride(0)
     y, f, ydt = _out(y, M, n, out_dtype, form, xq.device)
     swn, swk, swb = _sc(sw)
@@ -391,6 +499,12 @@ def w8a16_sparse24_gemm_groupwise(x, wv, wmeta, sw, gran_n: int = 128, out_dtype
         raise SgError("wv must be uint8 (e4m3 codes) or int8")
     M, K = x.shape
     N = wv.shape[0]
+    _positive(M=M, N=N, K=K)
+    if K % 128 or gran_n not in (1, 128):
+        raise SgError("K must be a multiple of 128 and gran_n 1 or 128")
+    _want(wv, "wv", (wv.dtype,), (N, K // 2), x.device)
+    _want(wmeta, "wmeta", _CODES, (N, K // 8), x.device)
+    _want_scales(sw, "sw", -(-N // gran_n), K // 128, x.device)
     y, f, ydt = _out(y, M, N, out_dtype, form, x.device)
     bp, _ = _bias(bias, N)
     st = lib().sg_w8a16_sparse24_gemm_groupwise(M, N, K, _p(x), _row_stride(x), _p(wv), _row_stride(wv), _p(wmeta),
@@ -412,6 +526,12 @@ def w4a16_sparse24_gemm_groupwise(x, wv4, wmeta, sw, out_dtype=torch.bfloat16, f
         raise SgError("x must be bfloat16 and wv4 uint8")
     M, K = x.shape
     N = wv4.shape[0]
+    _positive(M=M, N=N, K=K)
+    if K % 128:
+        raise SgError(f"K must be a multiple of 128, got {K}")
+    _want(wv4, "wv4", _CODES, (N, K // 4), x.device)
+    _want(wmeta, "wmeta", _CODES, (N, K // 8), x.device)
+    _want_scales(sw, "sw", N, K // 128, x.device)
     y, f, ydt = _out(y, M, N, out_dtype, form, x.device)
     bp, _ = _bias(bias, N)
     st = lib().sg_w4a16_sparse24_gemm_groupwise(M, N, K, _p(x), _row_stride(x), _p(wv4), _row_stride(wv4), _p(wmeta),
@@ -425,6 +545,24 @@ def sparse24_packed_bytes(n: int, k: int) -> int:
     return int(lib().sg_sparse24_packed_bytes(n, k))
 
 
+def _want_packed(wpacked, n, k, device, batch=None):
+    """A contiguous uint8 GPU buffer holding one packed weight ([bytes]), or one
+    per problem ([L, bytes], when batch = L)."""
+    need = sparse24_packed_bytes(n, k)
+    if need < 0:
+        raise SgError(f"no packed form for N = {n}, K = {k}")
+    if not isinstance(wpacked, torch.Tensor) or not wpacked.is_cuda or wpacked.dtype != torch.uint8 \
+            or wpacked.dim() not in ((1, 2) if batch else (1,)) or wpacked.shape[-1] < need \
+            or wpacked.stride(-1) != 1:
+        raise SgError(f"wpacked must be a uint8 GPU tensor [{'L, ' if batch else ''}bytes] of at least "
+                      f"{need} bytes per packed weight")
+    if wpacked.device != device:
+        raise SgError(f"wpacked is on {wpacked.device}, the operands on {device}")
+    if batch and wpacked.dim() == 2 and wpacked.shape[0] not in (1, batch):
+        raise SgError(f"wpacked holds {wpacked.shape[0]} weights, not {batch}")
+    return wpacked
+
+
 def sparse24_pack_gfx950(wv, wmeta, packed=None):
     """Compressed codes wv uint8 [N, K/2] + metadata uint8 [N, K/8] -> the gfx950
     packed weight (uint8, sparse24_packed_bytes(N, K) bytes)."""
@@ -433,11 +571,12 @@ def sparse24_pack_gfx950(wv, wmeta, packed=None):
     n, k = wv.shape[0], wv.shape[1] * 2
     nbytes = sparse24_packed_bytes(n, k)
     if nbytes < 0:
-        raise SgError("sparse24_pack_gfx950: K must be a positive multiple of 128")
+        raise SgError("sparse24_pack_gfx950: N must be at least 1 and K a positive multiple of 128")
+    _want(wv, "wv", (torch.uint8, torch.int8), (n, k // 2), wv.device)
+    _want(wmeta, "wmeta", _CODES, (n, k // 8), wv.device)
     if packed is None:
         packed = torch.empty(nbytes, dtype=torch.uint8, device=wv.device)
-    if packed.numel() < nbytes or not packed.is_cuda:
-        raise SgError("packed buffer too small or not on the GPU")
+    _want_packed(packed, n, k, wv.device)
     st = lib().sg_sparse24_pack_gfx950(_p(wv), _row_stride(wv), _p(wmeta), _row_stride(wmeta), n, k, _p(packed),
                                        _stream(wv))
     _check(st, "sg_sparse24_pack_gfx950")
@@ -449,8 +588,8 @@ def fp8_sparse24_gemm_groupwise_packed(xq, sx, wpacked, n: int, sw, gran_m: int 
     """2:4-sparse FP8 GEMM with the weight in the gfx950 packed form (N rows)."""
     _gpu2d(xq, "xq")
     M, K = xq.shape
-    if not wpacked.is_cuda or wpacked.numel() < sparse24_packed_bytes(n, K):
-        raise SgError("wpacked too small or not on the GPU")
+    _gemm_operands(xq, _CODES, M, n, K, sx, gran_m, sw, gran_n)
+    _want_packed(wpacked, n, K, xq.device)
     y, f, ydt = _out(y, M, n, out_dtype, form, xq.device)
     st = lib().sg_fp8_sparse24_gemm_groupwise_packed(M, n, K, _p(xq), _row_stride(xq), _p(sx), sx.stride(0),
                                                      sx.stride(1), gran_m, _p(wpacked), _p(sw), sw.stride(0),
@@ -469,6 +608,9 @@ def int8_sparse24_gemm_groupwise(xq, sx, wv, wmeta, sw, gran_m: int = 1, gran_n:
     _gpu2d(wmeta, "wmeta")
     M, K = xq.shape
     N = wv.shape[0]
+    _gemm_operands(xq, _I8, M, N, K, sx, gran_m, sw, gran_n)
+    _want(wv, "wv", _I8, (N, K // 2), xq.device)
+    _want(wmeta, "wmeta", _CODES, (N, K // 8), xq.device)
     y, f, ydt = _out(y, M, N, out_dtype, form, xq.device)
     st = lib().sg_int8_sparse24_gemm_groupwise(M, N, K, _p(xq), _row_stride(xq), _p(sx), sx.stride(0),
                                                sx.stride(1), gran_m, _p(wv), _row_stride(wv), _p(wmeta),
@@ -484,8 +626,8 @@ def int8_sparse24_gemm_groupwise_packed(xq, sx, wpacked, n: int, sw, gran_m: int
     sparse24_pack_gfx950 packs int8 codes as it packs e4m3 codes)."""
     _gpu2d(xq, "xq")
     M, K = xq.shape
-    if not wpacked.is_cuda or wpacked.numel() < sparse24_packed_bytes(n, K):
-        raise SgError("wpacked too small or not on the GPU")
+    _gemm_operands(xq, _I8, M, n, K, sx, gran_m, sw, gran_n)
+    _want_packed(wpacked, n, K, xq.device)
     y, f, ydt = _out(y, M, n, out_dtype, form, xq.device)
     st = lib().sg_int8_sparse24_gemm_groupwise_packed(M, n, K, _p(xq), _row_stride(xq), _p(sx), sx.stride(0),
                                                       sx.stride(1), gran_m, _p(wpacked), _p(sw), sw.stride(0),
@@ -503,15 +645,23 @@ def mixed_gemm_add(x1, sx1, w1, sw1, x2, w2, y=None):
     M, K1 = x1.shape[0], x1.shape[1] * 2
     N = w1.shape[0]
     K2 = x2.shape[1] if x2 is not None else 0
+    _positive(M=M, N=N, K1=K1)
+    if K1 % 128:
+        raise SgError(f"K1 must be a multiple of 128, got {K1}")
+    dev = x1.device
+    _want(x1, "x1", _CODES, (M, K1 // 2), dev)
+    _want(w1, "w1", _CODES, (N, K1 // 2), dev)
+    _want_scales(sx1, "sx1", M, K1 // 128, dev)
+    _want_scales(sw1, "sw1", N, K1 // 128, dev)
     if K2:
         _gpu2d(x2, "x2")
         _gpu2d(w2, "w2")
-        for t, nm in ((x2, "x2"), (w2, "w2")):
-            if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
-                raise SgError(f"{nm} must hold bf16 values")
+        bf = (torch.bfloat16, torch.int16, torch.uint16)
+        _want(x2, "x2", bf, (M, K2), dev)
+        _want(w2, "w2", bf, (N, K2), dev)
     if y is None:
-        y = torch.empty((M, N), dtype=torch.bfloat16, device=x1.device)
-    _gpu2d(y, "y")
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    _gpu2d(_want(y, "y", (torch.bfloat16,), (M, N), dev), "y")
     st = lib().sg_mixed_gemm_add(M, N, K1, K2, _p(x1), _row_stride(x1), _p(sx1), sx1.stride(0), sx1.stride(1),
                                  _p(w1), _row_stride(w1), _p(sw1), sw1.stride(0), sw1.stride(1),
                                  _p(x2) if K2 else None, _row_stride(x2) if K2 else 0,

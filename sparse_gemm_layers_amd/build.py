@@ -3,6 +3,13 @@
 Usage: python -m sparse_gemm_layers_amd.build   (or __graft_entry__.build()).
 Every .hip file under csrc/ is compiled to an object in parallel, then linked
 into sparse_gemm_layers_amd/libsg.so.
+
+python -m sparse_gemm_layers_amd.build --host-sanitizers builds a second copy,
+_build/san/libsg_hostsan.so, whose HOST code (argument checks, launch set-up)
+is instrumented with AddressSanitizer and UndefinedBehaviorSanitizer; device
+code is built as usual and not instrumented.  Load it with the sanitizer
+runtime preloaded (HOST_SANITIZER_RUNTIME) and SG_LIBRARY pointing at it; the
+CPU-only ABI tests run that way (tests/test_abi_sanitized.py).
 """
 import concurrent.futures
 import glob
@@ -37,9 +44,26 @@ CFLAGS = [
 SRC_FLAGS = {"gemm_fp8.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CFLAGS, *SRC_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
+# Host-only sanitizers: each -fsanitize= applies to the host pass alone.
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+             "-Xarch_host", "-g"]
+SAN_DIR = os.path.join(BUILD, "san")
+SAN_LIB = os.path.join(SAN_DIR, "libsg_hostsan.so")
+
+
+def host_sanitizer_runtime() -> str:
+    """Path of the shared AddressSanitizer runtime that must be preloaded into an
+    uninstrumented process (python) before it loads the sanitized library."""
+    r = subprocess.run([HIPCC, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    return r.stdout.strip()
+
+
+def _compile(src: str, sanitize: bool = False) -> str:
+    out_dir = SAN_DIR if sanitize else BUILD
+    obj = os.path.join(out_dir, os.path.basename(src) + ".o")
+    extra = SAN_FLAGS + ["-O1"] if sanitize else SRC_FLAGS.get(os.path.basename(src), [])
+    cmd = [HIPCC, *CFLAGS, *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     err = "\n".join(line for line in r.stderr.splitlines() if "packed-fp32-ops" not in line)
     if r.returncode != 0:
@@ -49,21 +73,27 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+def sources():
+    return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+
+
+def build(verbose: bool = True, sanitize: bool = False) -> str:
+    out_dir, lib = (SAN_DIR, SAN_LIB) if sanitize else (BUILD, LIB)
+    os.makedirs(out_dir, exist_ok=True)
+    srcs = sources()
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+        objs = list(ex.map(lambda f: _compile(f, sanitize), srcs))
+    tmp = lib + ".tmp"
+    link_extra = ["-shared-libsan", *SAN_FLAGS] if sanitize else []
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *link_extra, "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB} from {len(srcs)} sources")
-    return LIB
+        print(f"built {lib} from {len(srcs)} sources")
+    return lib
 
 
 if __name__ == "__main__":
-    build()
+    build(sanitize="--host-sanitizers" in sys.argv[1:])

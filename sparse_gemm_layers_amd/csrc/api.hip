@@ -13,4 +13,4 @@ extern "C" const char* sg_status_str(sg_status s) {
   return "unknown sg_status";
 }
 
-extern "C" int sg_abi_version(void) { return 2; }
+extern "C" int sg_abi_version(void) { return 3; }

@@ -28,28 +28,46 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 // ---------------------------------------------------------------- encoders
 
 // fp32 -> OCP e4m3 ("e4m3fn") codes of four values, packed little-endian in
-// a dword: round to nearest, ties to even, saturate at +-448, keep the sign (a
-// negative value that rounds to zero gives 0x80).  The values are clamped to
-// +-448 first because the conversion instruction turns overflow into NaN.
-// Over every finite fp32 input this gives the same code as an integer-only
-// round-to-nearest-even encoder (checked exhaustively on MI355X, all 2^32 bit
-// patterns); NaN and infinite inputs are unspecified.
+// a dword: round to nearest, ties to even, saturate at +-448 (infinities
+// included), keep the sign (a negative value that rounds to zero gives 0x80),
+// and give every NaN the one code 0x7F.  The values are clamped to +-448 first
+// because the conversion instruction turns overflow into NaN; the clamp would
+// turn NaN into -448, so NaN lanes are patched afterwards.  Over every finite
+// fp32 input the codes equal those of an integer-only round-to-nearest-even
+// encoder (checked exhaustively on MI355X, all 2^32 bit patterns).
 __device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d) {
   const auto cl = [](float v) { return fminf(fmaxf(v, -448.0f), 448.0f); };
   int w = __builtin_amdgcn_cvt_pk_fp8_f32(cl(a), cl(b), 0, false);
   w = __builtin_amdgcn_cvt_pk_fp8_f32(cl(c), cl(d), w, true);
-  return (uint32_t)w;
+  const uint32_t nan = (a != a ? 0xffu : 0u) | (b != b ? 0xff00u : 0u) | (c != c ? 0xff0000u : 0u) |
+                       (d != d ? 0xff000000u : 0u);
+  return ((uint32_t)w & ~nan) | (0x7f7f7f7fu & nan);
+}
+
+// |v| folded into a running block maximum a (a >= 0).  Non-negative floats
+// order like their bit patterns and every NaN pattern lies above +inf, so the
+// maximum is taken on the bits: a block holding a NaN gets a NaN maximum
+// (fmaxf would drop it).
+__device__ __forceinline__ float amax_fold(float a, float v) {
+  return __uint_as_float(max(__float_as_uint(a), __float_as_uint(v) & 0x7fffffffu));
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float((uint32_t)b << 16);
 }
 
-// fp32 -> bf16 bits, round to nearest even (finite inputs).
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16 bits of two values (a in the low half): round to nearest even,
+// NaN stays NaN (one v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b) {
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
+
+// fp32 -> bf16 bits of one value, as above.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) { return f32x2_to_bf16x2(f, 0.0f) & 0xffffu; }
 
 // ---------------------------------------------------------------- loads
 
@@ -66,13 +84,20 @@ __device__ __forceinline__ void load4(const uint16_t* p, float v[4]) {
   v[3] = __uint_as_float(t.y & 0xffff0000u);
 }
 
-// Max over groups of `width` consecutive lanes (width a power of two <= 64).
+// Max of non-negative values (NaN patterns included, see amax_fold) over
+// groups of `width` consecutive lanes (width a power of two <= 64).
 template <int WIDTH>
 __device__ __forceinline__ float group_max(float a) {
+  uint32_t u = __float_as_uint(a);
 #pragma unroll
-  for (int o = WIDTH / 2; o >= 1; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, 64));
-  return a;
+  for (int o = WIDTH / 2; o >= 1; o >>= 1) u = max(u, (uint32_t)__shfl_xor((int)u, o, 64));
+  return __uint_as_float(u);
 }
+
+// Scale of a block from its maximum magnitude a: a / qmax (an IEEE divide),
+// 1 for an all-zero block; a NaN maximum gives a NaN scale and an infinite
+// one an infinite scale.
+__device__ __forceinline__ float block_scale(float a, float qmax) { return a == 0.0f ? 1.0f : a / qmax; }
 
 // ---------------------------------------------------------------- host checks
 

@@ -85,8 +85,8 @@ __device__ __forceinline__ void store_quad(const Args& a, int64_t m, int64_t n, 
     if (a.vec_store && n + 3 < a.N) {
       if (OUT_BF16) {
         uint2 p;
-        p.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
-        p.y = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
+        p.x = f32x2_to_bf16x2(v[0], v[1]);
+        p.y = f32x2_to_bf16x2(v[2], v[3]);
         *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.y) + off) = p;
       } else {
         *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.y) + off) = make_float4(v[0], v[1], v[2], v[3]);

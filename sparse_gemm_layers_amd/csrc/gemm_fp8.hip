@@ -684,7 +684,6 @@ constexpr int SW_OFF = XB + BM * 4;          // 256 W-row scales
 constexpr int SPARE_OFF = SW_OFF + BN * 4;   // spare slot for the scale loads of waves 6, 7
 constexpr int KBYTES = SPARE_OFF + BM * 4;   // one K block
 constexpr int ARR = KPA * KBYTES;            // one array
-constexpr int NW = 8;                        // register loads per wave per K block
 }  // namespace wr
 
 #if SG_DEVICE_PASS
@@ -1923,7 +1922,7 @@ static sg_status check_common(int64_t M, int64_t N, int64_t K, const uint8_t* xq
   if ((gran_m != 1 && gran_m != 128) || (gran_n != 1 && gran_n != 128)) return SG_ERR_UNSUPPORTED;
   if (y_dt != SG_F32 && y_dt != SG_BF16) return SG_ERR_UNSUPPORTED;
   if (form != SG_OUT_Y && form != SG_OUT_YT) return SG_ERR_UNSUPPORTED;
-  if (M < 0 || N < 0 || K <= 0 || K % 128 != 0 || ldx < K) return SG_ERR_SHAPE;
+  if (M <= 0 || N <= 0 || K <= 0 || K % 128 != 0 || ldx < K) return SG_ERR_SHAPE;
   if (ldy < (form == SG_OUT_Y ? N : M)) return SG_ERR_SHAPE;
   if (cdiv(M, 128) * cdiv(N, 256) > 0x7fffffffLL || cdiv(N, 16) > 0x7fffffffLL) return SG_ERR_SHAPE;
   // The large-M kernel addresses tiles and scales with 32-bit buffer offsets.
@@ -1944,7 +1943,7 @@ struct Batch {
 };
 
 static sg_status check_batch(const Batch& b) {
-  if (b.L < 0 || b.L > 65535) return SG_ERR_SHAPE;
+  if (b.L <= 0 || b.L > 65535) return SG_ERR_SHAPE;
   if (b.bx < 0 || b.bw < 0 || b.bm < 0 || b.bsx < 0 || b.bsw < 0 || b.by < 0) return SG_ERR_SHAPE;
   if (b.bbs < 0) return SG_ERR_SHAPE;
   if (b.bx % 16 || b.bw % 16 || b.bm % 16 || !aligned(b.bias, 4)) return SG_ERR_ALIGN;
@@ -1987,7 +1986,6 @@ static sg_status dense_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* xq, 
   if (!wq) return SG_ERR_NULL;
   if (ldw < K || ldw >= (1LL << 24)) return SG_ERR_SHAPE;
   if (!aligned(wq, 16) || ldw % 16) return SG_ERR_ALIGN;
-  if (M == 0 || N == 0 || b.L == 0) return SG_OK;
   const GemmArgs a = make_args(M, N, K, xq, ldx, sx, sx_sm, sx_sk, gran_m, wq, ldw, nullptr, 0, sw, sw_sn,
                                sw_sk, gran_n, y, y_dt, ldy, b);
   clear_hip_error();
@@ -2033,7 +2031,6 @@ static sg_status sparse24_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* x
   if (!wv || !wmeta) return SG_ERR_NULL;
   if (ldwv < K / 2 || ldwm < K / 8 || ldwv >= (1LL << 24) || ldwm >= (1LL << 24)) return SG_ERR_SHAPE;
   if (!aligned(wv, 16) || !aligned(wmeta, 16) || ldwv % 16 || ldwm % 16) return SG_ERR_ALIGN;
-  if (M == 0 || N == 0 || b.L == 0) return SG_OK;
   const GemmArgs a = make_args(M, N, K, xq, ldx, sx, sx_sm, sx_sk, gran_m, wv, ldwv, wmeta, ldwm, sw, sw_sn,
                                sw_sk, gran_n, y, y_dt, ldy, b);
   clear_hip_error();
@@ -2054,7 +2051,6 @@ static sg_status sparse24_gemm_packed(int64_t M, int64_t N, int64_t K, const uin
   if (!aligned(wpacked, 16)) return SG_ERR_ALIGN;
   // the large-M kernel addresses a tile's 16 row blocks with 32-bit offsets
   if ((K / 128) * (int64_t)(BN / PK_ROWS) * PK_CHUNK > 0x7fffffffLL) return SG_ERR_SHAPE;
-  if (M == 0 || N == 0 || b.L == 0) return SG_OK;
   const GemmArgs a = make_args(M, N, K, xq, ldx, sx, sx_sm, sx_sk, gran_m, wpacked, 0, nullptr, 0, sw, sw_sn,
                                sw_sk, gran_n, y, y_dt, ldy, b);
   clear_hip_error();
@@ -2202,8 +2198,8 @@ extern "C" sg_status sg_fp8_sparse24_gemm_groupwise_packed_grouped(
     int64_t sx_sm, int64_t sx_sk, const uint8_t* wpacked, int64_t wp_bs, const float* sw, int64_t sw_sn,
     int64_t sw_sk, int64_t sw_bs, int gran_n, const float* bias, int64_t bias_bs, void* y, sg_dtype y_dt,
     int64_t ldy, sg_form form, hipStream_t stream) {
-  if (G < 0 || G > MAX_GROUPS) return SG_ERR_SHAPE;
-  if (G > 0 && !m_sizes) return SG_ERR_NULL;
+  if (G <= 0 || G > MAX_GROUPS) return SG_ERR_SHAPE;
+  if (!m_sizes) return SG_ERR_NULL;
   GroupTable gt;
   gt.G = (int)G;
   gt.row_off[0] = 0;
@@ -2229,7 +2225,6 @@ extern "C" sg_status sg_fp8_sparse24_gemm_groupwise_packed_grouped(
     if (t > 0x7fffffffLL) return SG_ERR_SHAPE;
     gt.tile_start[g + 1] = (int)t;
   }
-  if (G == 0 || gt.tile_start[G] == 0 || N == 0) return SG_OK;
   GemmArgs a = make_args(M, N, K, xq, ldx, sx, sx_sm, sx_sk, 1, wpacked, 0, nullptr, 0, sw, sw_sn, sw_sk, gran_n,
                          y, y_dt, ldy, b);
   // Y^T: a group's columns start at its row offset, so 16-byte stores need

@@ -735,7 +735,7 @@ extern "C" sg_status sg_w8a16_sparse24_gemm_groupwise(int64_t M, int64_t N, int6
   if (gran_n != 1 && gran_n != 128) return SG_ERR_UNSUPPORTED;
   if (y_dt != SG_F32 && y_dt != SG_BF16) return SG_ERR_UNSUPPORTED;
   if (form != SG_OUT_Y && form != SG_OUT_YT) return SG_ERR_UNSUPPORTED;
-  if (M < 0 || N < 0 || K <= 0 || K % 128 != 0 || ldx < K || ldwv < K / 2 || ldwm < K / 8) return SG_ERR_SHAPE;
+  if (M <= 0 || N <= 0 || K <= 0 || K % 128 != 0 || ldx < K || ldwv < K / 2 || ldwm < K / 8) return SG_ERR_SHAPE;
   if (ldy < (form == SG_OUT_Y ? N : M)) return SG_ERR_SHAPE;
   // 32-bit buffer offsets: 64 rows of each operand per workgroup
   if (ldx >= (1LL << 24) || ldwv >= (1LL << 24) || ldwm >= (1LL << 24) || sw_sn < 0 || sw_sk < 0) return SG_ERR_SHAPE;
@@ -744,7 +744,6 @@ extern "C" sg_status sg_w8a16_sparse24_gemm_groupwise(int64_t M, int64_t N, int6
   if (!aligned(x, 16) || (ldx * 2) % 16 || !aligned(wv, 16) || ldwv % 16 || !aligned(wmeta, 16) || ldwm % 16 ||
       !aligned(sw, 4) || !aligned(bias, 4) || !aligned(y, dtype_size(y_dt)))
     return SG_ERR_ALIGN;
-  if (M == 0 || N == 0) return SG_OK;
   W8Args a;
   a.M = M; a.N = N; a.K = K;
   a.x = x; a.ldx = ldx;
@@ -773,7 +772,7 @@ extern "C" sg_status sg_w4a16_sparse24_gemm_groupwise(int64_t M, int64_t N, int6
   if (!x || !wv4 || !wmeta || !sw || !y) return SG_ERR_NULL;
   if (y_dt != SG_F32 && y_dt != SG_BF16) return SG_ERR_UNSUPPORTED;
   if (form != SG_OUT_Y && form != SG_OUT_YT) return SG_ERR_UNSUPPORTED;
-  if (M < 0 || N < 0 || K <= 0 || K % 128 != 0 || ldx < K || ldwv4 < K / 4 || ldwm < K / 8) return SG_ERR_SHAPE;
+  if (M <= 0 || N <= 0 || K <= 0 || K % 128 != 0 || ldx < K || ldwv4 < K / 4 || ldwm < K / 8) return SG_ERR_SHAPE;
   if (ldy < (form == SG_OUT_Y ? N : M)) return SG_ERR_SHAPE;
   if (ldx >= (1LL << 24) || ldwv4 >= (1LL << 24) || ldwm >= (1LL << 24) || sw_sn < 0 || sw_sk < 0) return SG_ERR_SHAPE;
   if (((N - 1) * sw_sn + (K / 128 - 1) * sw_sk) * 4 >= (1LL << 31)) return SG_ERR_SHAPE;
@@ -781,7 +780,6 @@ extern "C" sg_status sg_w4a16_sparse24_gemm_groupwise(int64_t M, int64_t N, int6
   if (!aligned(x, 16) || (ldx * 2) % 16 || !aligned(wv4, 16) || ldwv4 % 16 || !aligned(wmeta, 16) || ldwm % 16 ||
       !aligned(sw, 4) || !aligned(bias, 4) || !aligned(y, dtype_size(y_dt)))
     return SG_ERR_ALIGN;
-  if (M == 0 || N == 0) return SG_OK;
   W8Args a;
   a.M = M; a.N = N; a.K = K;
   a.x = x; a.ldx = ldx;

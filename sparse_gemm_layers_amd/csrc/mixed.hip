@@ -353,7 +353,7 @@ extern "C" sg_status sg_mixed_gemm_add(int64_t M, int64_t N, int64_t K1, int64_t
                                        int64_t ldw2, uint16_t* y, int64_t ldy, hipStream_t stream) {
   if (!x1 || !sx1 || !w1 || !sw1 || !y) return SG_ERR_NULL;
   if (K2 > 0 && (!x2 || !w2)) return SG_ERR_NULL;
-  if (M < 0 || N < 0 || K1 <= 0 || K1 % 128 != 0 || K2 < 0 || K2 % 32 != 0) return SG_ERR_SHAPE;
+  if (M <= 0 || N <= 0 || K1 <= 0 || K1 % 128 != 0 || K2 < 0 || K2 % 32 != 0) return SG_ERR_SHAPE;
   if (ldx1 < K1 / 2 || ldw1 < K1 / 2 || ldy < N) return SG_ERR_SHAPE;
   if (K2 > 0 && (ldx2 < K2 || ldw2 < K2)) return SG_ERR_SHAPE;
   if (cdiv(M, 128) * cdiv(N, 256) > 0x7fffffffLL) return SG_ERR_SHAPE;
@@ -366,7 +366,6 @@ extern "C" sg_status sg_mixed_gemm_add(int64_t M, int64_t N, int64_t K1, int64_t
       !aligned(sw1, 4) || !aligned(y, 2))
     return SG_ERR_ALIGN;
   if (K2 > 0 && (!aligned(x2, 16) || !aligned(w2, 16) || ldx2 % 8 || ldw2 % 8)) return SG_ERR_ALIGN;
-  if (M == 0 || N == 0) return SG_OK;
   MixedArgs a;
   a.M = M; a.N = N; a.K1 = K1; a.K2 = K2;
   a.x1 = x1; a.ldx1 = ldx1; a.sx1 = sx1; a.sx1_sm = sx1_sm; a.sx1_sk = sx1_sk;

@@ -46,17 +46,16 @@ __global__ void __launch_bounds__(256) k_pack24(const uint8_t* __restrict__ wv, 
 using namespace sg;
 
 extern "C" int64_t sg_sparse24_packed_bytes(int64_t N, int64_t K) {
-  if (N < 0 || K <= 0 || K % 128 != 0) return -1;
+  if (N <= 0 || K <= 0 || K % 128 != 0) return -1;
   return cdiv(N, PK_ROWS) * (K / 128) * PK_CHUNK;
 }
 
 extern "C" sg_status sg_sparse24_pack_gfx950(const uint8_t* wv, int64_t ldwv, const uint8_t* wmeta, int64_t ldwm,
                                              int64_t N, int64_t K, uint8_t* packed, hipStream_t stream) {
   if (!wv || !wmeta || !packed) return SG_ERR_NULL;
-  if (N < 0 || K <= 0 || K % 128 != 0 || ldwv < K / 2 || ldwm < K / 8) return SG_ERR_SHAPE;
+  if (N <= 0 || K <= 0 || K % 128 != 0 || ldwv < K / 2 || ldwm < K / 8) return SG_ERR_SHAPE;
   if (!aligned(wv, 16) || !aligned(wmeta, 16) || !aligned(packed, 16) || ldwv % 16 || ldwm % 16)
     return SG_ERR_ALIGN;
-  if (N == 0) return SG_OK;
   const int64_t total = cdiv(N, PK_ROWS) * PK_ROWS * (K / 128);
   clear_hip_error();
   k_pack24<<<grid_for(total, 256), 256, 0, stream>>>(wv, ldwv, wmeta, ldwm, N, (int)(K / 128), total, packed);

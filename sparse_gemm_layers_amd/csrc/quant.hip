@@ -10,18 +10,26 @@
 // quantization API" (jcaip's review: positive scales, all-zero input allowed,
 // scale then cast to float8_e4m3fn).  int8 (for the int8 x int8 2:4 GEMM the
 // same torchao page names): s = amax / 127, codes rint-even clamped to +-127.
+//
+// Non-finite inputs (the pages say nothing of them): a block holding a NaN
+// gets a NaN scale, a block holding an infinity (and no NaN) an infinite
+// scale; codes are still the encoder applied to v / s, so finite values of
+// such a block give zero codes and NaN quotients give 0x7F (e4m3) or 0 (int).
 #include "common.h"
 
 namespace sg {
 
 enum QuantMode { Q_FP8 = 0, Q_INT8 = 2 };
 
-// int8 code of v / sc as a byte (two's complement), rounding half to even.
-__device__ __forceinline__ uint32_t int8_encode(float v, float sc) {
-  float t = __builtin_rintf(v / sc);                             // IEEE divide, half to even
-  t = fminf(fmaxf(t, -127.0f), 127.0f);
-  return (uint32_t)(int)t & 0xffu;
+// Integer code of v / sc, rounded half to even and clamped to +-qmax (an
+// infinite quotient saturates); a NaN quotient gives code 0.
+__device__ __forceinline__ int int_code(float v, float sc, float qmax) {
+  const float t = __builtin_rintf(v / sc);                       // IEEE divide, half to even
+  return t != t ? 0 : (int)fminf(fmaxf(t, -qmax), qmax);
 }
+
+// int8 code of v / sc as a byte (two's complement).
+__device__ __forceinline__ uint32_t int8_encode(float v, float sc) { return (uint32_t)int_code(v, sc, 127.0f) & 0xffu; }
 
 // ------------------------------------------------------------------ int4, 1 x 128
 // LPB = GC/4 lanes share one block, 4 consecutive elements per lane (two
@@ -47,16 +55,14 @@ __global__ void __launch_bounds__(256) k_quant_int4(const TIn* __restrict__ x, i
     const int64_t cb = valid ? b % nbc : 0;
     float v[4] = {0.f, 0.f, 0.f, 0.f};
     if (valid) load4(x + r * ldx + cb * GC + li * 4, v);
-    float a = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+    float a = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a = amax_fold(a, v[i]);
     a = group_max<LPB>(a);
-    const float sc = a > 0.f ? a / 7.0f : 1.0f;
+    const float sc = block_scale(a, 7.0f);
     uint32_t packed = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float t = __builtin_rintf(v[i] / sc);                    // half to even
-      t = fminf(fmaxf(t, -7.0f), 7.0f);
-      packed |= ((uint32_t)(int)t & 0xfu) << (4 * i);
-    }
+    for (int i = 0; i < 4; ++i) packed |= ((uint32_t)int_code(v[i], sc, 7.0f) & 0xfu) << (4 * i);
     if (valid) {
       *reinterpret_cast<uint16_t*>(q + r * ldq + cb * (GC / 2) + li * 2) = (uint16_t)packed;
       if (li == 0) s[r * ssr + cb * ssc] = sc;
@@ -97,9 +103,9 @@ __global__ void __launch_bounds__(256) k_quant_row16(const TIn* __restrict__ x, 
     }
     float a = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(v[i]));
+    for (int i = 0; i < 16; ++i) a = amax_fold(a, v[i]);
     a = group_max<LPB>(a);
-    const float sc = a > 0.f ? a / (MODE == Q_FP8 ? 448.0f : 127.0f) : 1.0f;   // IEEE divide
+    const float sc = block_scale(a, MODE == Q_FP8 ? 448.0f : 127.0f);
     uint32_t w[4];
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
@@ -144,13 +150,14 @@ __global__ void __launch_bounds__(256) k_quant_block128(const TIn* __restrict__ 
     } else {
       v[st][0] = v[st][1] = v[st][2] = v[st][3] = 0.f;
     }
-    a = fmaxf(a, fmaxf(fmaxf(fabsf(v[st][0]), fabsf(v[st][1])), fmaxf(fabsf(v[st][2]), fabsf(v[st][3]))));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a = amax_fold(a, v[st][i]);
   }
   a = group_max<64>(a);
   if ((t & 63) == 0) red[t >> 6] = a;
   __syncthreads();
-  a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const float sc = a > 0.f ? a / (MODE == Q_FP8 ? 448.0f : 127.0f) : 1.0f;
+  a = amax_fold(amax_fold(amax_fold(red[0], red[1]), red[2]), red[3]);
+  const float sc = block_scale(a, MODE == Q_FP8 ? 448.0f : 127.0f);
 #pragma unroll
   for (int st = 0; st < STEPS; ++st) {
     const int64_t r = rb * 128 + st * RPS + lr;
@@ -193,14 +200,14 @@ __global__ void __launch_bounds__(256) k_quant_rowwide(const TIn* __restrict__ x
       float v[16];
       load16(xr + c, v);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(v[i]));
+      for (int i = 0; i < 16; ++i) a = amax_fold(a, v[i]);
     }
     a = group_max<64>(a);
     if ((t & 63) == 0) red[t >> 6] = a;
     __syncthreads();
-    a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    a = amax_fold(amax_fold(amax_fold(red[0], red[1]), red[2]), red[3]);
   }
-  const float sc = a > 0.f ? a / (MODE == Q_FP8 ? 448.0f : 127.0f) : 1.0f;   // IEEE divide
+  const float sc = block_scale(a, MODE == Q_FP8 ? 448.0f : 127.0f);
   for (int64_t c = (int64_t)t * 16; c < cols; c += 256 * 16) {
     float v[16];
     load16(xr + c, v);
@@ -232,13 +239,14 @@ __global__ void __launch_bounds__(256) k_amax_tensor(const TIn* __restrict__ x, 
     float v[16];
     load16(x + r * ldx + c, v);
 #pragma unroll
-    for (int k = 0; k < 16; ++k) a = fmaxf(a, fabsf(v[k]));
+    for (int k = 0; k < 16; ++k) a = amax_fold(a, v[k]);
   }
   a = group_max<64>(a);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
   __syncthreads();
   if (threadIdx.x == 0)
-    atomicMax(reinterpret_cast<unsigned int*>(slot), __float_as_uint(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]))));
+    atomicMax(reinterpret_cast<unsigned int*>(slot),
+              __float_as_uint(amax_fold(amax_fold(amax_fold(red[0], red[1]), red[2]), red[3])));
 }
 
 __global__ void k_fill1(float* p, float v) { *p = v; }
@@ -247,7 +255,7 @@ __global__ void k_fill1(float* p, float v) { *p = v; }
 template <int MODE>
 __global__ void k_tensor_scale(float* s) {
   const float a = *s;
-  *s = a > 0.f ? a / (MODE == Q_FP8 ? 448.0f : 127.0f) : 1.0f;
+  *s = block_scale(a, MODE == Q_FP8 ? 448.0f : 127.0f);
 }
 
 template <typename TIn, int MODE>
@@ -295,13 +303,12 @@ static sg_status quant_groupwise(const void* x, sg_dtype x_dt, int64_t rows, int
   const bool blocks = (gr == 1 || gr == 128) && (gc == 128 || gc == 64);
   const bool whole = gc == cols && (gr == 1 || gr == rows) && cols % 16 == 0 && cols > 0;
   if (!blocks && !whole) return SG_ERR_UNSUPPORTED;
-  if (rows < 0 || cols <= 0 || cols % gc != 0 || ldx < cols || ldq < cols) return SG_ERR_SHAPE;
+  if (rows <= 0 || cols <= 0 || cols % gc != 0 || ldx < cols || ldq < cols) return SG_ERR_SHAPE;
   if (gr == 128 && cdiv(rows, gr) > 65535) return SG_ERR_SHAPE;
   if (!blocks && rows >= (1LL << 24)) return SG_ERR_SHAPE;   // one 256-thread workgroup per row
   if (!aligned(x, 16) || !aligned(q, 16) || !aligned(s, 4) || (ldx * (int64_t)dtype_size(x_dt)) % 16 ||
       ldq % 16)
     return SG_ERR_ALIGN;
-  if (rows == 0) return SG_OK;
   clear_hip_error();
   if (x_dt == SG_F32)
     launch_quant<float, MODE>((const float*)x, rows, cols, ldx, gr, gc, q, ldq, s, s_stride_r, s_stride_c, stream);
@@ -333,11 +340,10 @@ extern "C" sg_status sg_int4_quant_groupwise(const void* x, sg_dtype x_dt, int64
   if (!x || !q || !s) return SG_ERR_NULL;
   if (x_dt != SG_F32 && x_dt != SG_BF16) return SG_ERR_UNSUPPORTED;
   if (gc != 128 && gc != 64) return SG_ERR_UNSUPPORTED;
-  if (rows < 0 || cols <= 0 || cols % gc != 0 || ldx < cols || ldq < cols / 2) return SG_ERR_SHAPE;
+  if (rows <= 0 || cols <= 0 || cols % gc != 0 || ldx < cols || ldq < cols / 2) return SG_ERR_SHAPE;
   if (!aligned(x, 16) || !aligned(q, 4) || !aligned(s, 4) || (ldx * (int64_t)dtype_size(x_dt)) % 16 ||
       ldq % 4)
     return SG_ERR_ALIGN;
-  if (rows == 0) return SG_OK;
   clear_hip_error();
   const int64_t blocks = rows * (cols / gc);
   const unsigned g = grid_for(blocks, 4 * (64 / (gc / 4)));

@@ -72,8 +72,8 @@ __device__ __forceinline__ void stage_quad(uint8_t* t0, uint8_t* t1, int nl, int
     uint8_t* row = (ml < OT::RPH ? t0 : t1) + (ml % OT::RPH) * OT::PITCH;
     if (OUT_BF16) {
       uint2 pk;
-      pk.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
-      pk.y = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
+      pk.x = f32x2_to_bf16x2(v[0], v[1]);
+      pk.y = f32x2_to_bf16x2(v[2], v[3]);
       *reinterpret_cast<uint2*>(row + nl * 2) = pk;
     } else {
       *reinterpret_cast<float4*>(row + nl * 4) = make_float4(v[0], v[1], v[2], v[3]);

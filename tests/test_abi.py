@@ -56,7 +56,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     lib = sg.lib()
-    assert lib.sg_abi_version() == 2
+    assert lib.sg_abi_version() == 3
     for code, word in [(OK, b"SG_OK"), (NULL, b"SG_ERR_NULL"), (SHAPE, b"SG_ERR_SHAPE"),
                        (UNSUP, b"SG_ERR_UNSUPPORTED"), (ALIGN, b"SG_ERR_ALIGN"), (HIP, b"SG_ERR_HIP")]:
         assert lib.sg_status_str(code).startswith(word)
@@ -76,8 +76,8 @@ def quant(**kw):
     (dict(dt=2), UNSUP), (dict(dt=7), UNSUP), (dict(gr=2), UNSUP), (dict(gc=32), UNSUP),
     (dict(cols=200), SHAPE), (dict(cols=0), SHAPE), (dict(rows=-1), SHAPE), (dict(ldx=128), SHAPE),
     (dict(ldq=100), SHAPE), (dict(x=ODD), ALIGN), (dict(ldx=258), ALIGN), (dict(ldq=264), ALIGN),
-    (dict(rows=0), OK),
-    (dict(gc=256, rows=0), OK), (dict(gr=0, gc=256, rows=0), OK), (dict(gr=3, gc=256), UNSUP),
+    (dict(rows=0), SHAPE),
+    (dict(gc=256, rows=0), SHAPE), (dict(gr=0, gc=256, rows=0), SHAPE), (dict(gr=3, gc=256), UNSUP),
     (dict(cols=200, gc=200, ldx=208, ldq=208, rows=0), UNSUP), (dict(gr=4, gc=256, ldq=100), SHAPE),
     (dict(gc=128, cols=256, gr=4), UNSUP),
 ])
@@ -89,7 +89,7 @@ def test_fp8_quant_validation(kw, code):
 @pytest.mark.parametrize("kw,code", [
     (dict(x=None), NULL), (dict(q=None), NULL), (dict(dt=2), UNSUP), (dict(gr=2), UNSUP), (dict(gc=32), UNSUP),
     (dict(cols=200), SHAPE), (dict(ldq=100), SHAPE), (dict(x=ODD), ALIGN), (dict(ldq=264), ALIGN),
-    (dict(rows=0), OK),
+    (dict(rows=0), SHAPE), (dict(rows=-3), SHAPE),
 ])
 def test_int8_quant_validation(kw, code):
     a = dict(x=P, dt=0, rows=4, cols=256, ldx=256, gr=1, gc=128, q=P2, ldq=256, s=P3, ssr=1, ssc=4)
@@ -108,9 +108,9 @@ def int4q(**kw):
 @no_gpu
 @pytest.mark.parametrize("kw,code", [
     (dict(q=None), NULL), (dict(dt=2), UNSUP), (dict(cols=64), SHAPE), (dict(ldq=64), SHAPE),
-    (dict(ldq=130), ALIGN), (dict(x=ODD), ALIGN), (dict(rows=0), OK),
+    (dict(ldq=130), ALIGN), (dict(x=ODD), ALIGN), (dict(rows=0), SHAPE),
     (dict(gc=32), UNSUP), (dict(gc=64, cols=200, ldx=208, ldq=104), SHAPE),
-    (dict(gc=64, cols=320, ldx=320, ldq=160, rows=0), OK),
+    (dict(gc=64, cols=320, ldx=320, ldq=160, rows=0), SHAPE),
 ])
 def test_int4_quant_validation(kw, code):
     assert int4q(**kw) == code
@@ -125,9 +125,13 @@ def prune(**kw):
 
 @no_gpu
 @pytest.mark.parametrize("kw,code", [
-    (dict(w=None), NULL), (dict(v=None), NULL), (dict(m=None), NULL), (dict(dt=2), UNSUP),
+    (dict(w=None), NULL), (dict(v=None), NULL), (dict(m=None), NULL), (dict(dt=3), UNSUP), (dict(dt=9), UNSUP),
     (dict(k=12), SHAPE), (dict(k=0), SHAPE), (dict(ldw=32), SHAPE), (dict(ldv=16), SHAPE), (dict(ldm=4), SHAPE),
-    (dict(v=ODD), ALIGN), (dict(ldw=66), ALIGN), (dict(ldv=34), ALIGN), (dict(rows=0), OK),
+    (dict(v=ODD), ALIGN), (dict(ldw=66), ALIGN), (dict(ldv=34), ALIGN), (dict(rows=0), SHAPE),
+    (dict(rows=-1), SHAPE),
+    # e4m3 codes (dt 2): byte rows, 16-byte aligned leading dimension
+    (dict(dt=2, rows=0), SHAPE), (dict(dt=2, ldw=72), ALIGN), (dict(dt=2, ldv=34), ALIGN),
+    (dict(dt=2, ldm=4), SHAPE), (dict(dt=2, w=None), NULL),
 ])
 def test_prune_validation(kw, code):
     assert prune(**kw) == code
@@ -155,7 +159,7 @@ GEMM_CASES = [
     (dict(K=0), SHAPE), (dict(K=200), SHAPE), (dict(M=-1), SHAPE), (dict(ldx=128), SHAPE),
     (dict(ldy=100), SHAPE), (dict(form=1, ldy=32), SHAPE),
     (dict(x=ODD), ALIGN), (dict(ldx=264), ALIGN), (dict(y=ctypes.c_void_p(0x100001)), ALIGN),
-    (dict(M=0), OK), (dict(N=0), OK),
+    (dict(M=0), SHAPE), (dict(N=0), SHAPE), (dict(N=-5), SHAPE),
 ]
 
 
@@ -198,9 +202,9 @@ def mixed(**kw):
 
 @no_gpu
 @pytest.mark.parametrize("kw,code", [
-    (dict(x1=None), NULL), (dict(x2=None), NULL), (dict(K2=0, x2=None, w2=None, M=0), OK),
+    (dict(x1=None), NULL), (dict(x2=None), NULL), (dict(K2=0, x2=None, w2=None, M=0), SHAPE),
     (dict(K1=100), SHAPE), (dict(K2=48), SHAPE), (dict(ldx1=64), SHAPE), (dict(ldx2=32), SHAPE),
-    (dict(ldy=100), SHAPE), (dict(x1=ODD), ALIGN), (dict(ldw2=68), ALIGN), (dict(N=0), OK),
+    (dict(ldy=100), SHAPE), (dict(x1=ODD), ALIGN), (dict(ldw2=68), ALIGN), (dict(N=0), SHAPE),
 ])
 def test_mixed_validation(kw, code):
     assert mixed(**kw) == code
@@ -216,14 +220,14 @@ def test_packed_bytes():
     lib = sg.lib()
     assert lib.sg_sparse24_packed_bytes(4096, 4096) == 256 * 32 * 1280
     assert lib.sg_sparse24_packed_bytes(300, 384) == 19 * 3 * 1280
-    assert lib.sg_sparse24_packed_bytes(0, 128) == 0
+    assert lib.sg_sparse24_packed_bytes(0, 128) == -1
     assert lib.sg_sparse24_packed_bytes(10, 100) == -1 and lib.sg_sparse24_packed_bytes(-1, 128) == -1
 
 
 @no_gpu
 @pytest.mark.parametrize("kw,code", [
     (dict(wv=None), NULL), (dict(packed=None), NULL), (dict(K=100), SHAPE), (dict(ldwv=32), SHAPE),
-    (dict(ldwm=24), ALIGN), (dict(packed=ODD), ALIGN), (dict(N=0), OK),
+    (dict(ldwm=24), ALIGN), (dict(packed=ODD), ALIGN), (dict(N=0), SHAPE),
 ])
 def test_pack_validation(kw, code):
     a = dict(wv=P, ldwv=64, meta=P2, ldwm=16, N=8, K=128, packed=P3)
@@ -234,7 +238,7 @@ def test_pack_validation(kw, code):
 
 @no_gpu
 @pytest.mark.parametrize("kw,code", [(dict(w=None), NULL), (dict(w=ODD), ALIGN), (dict(K=200), SHAPE),
-                                     (dict(M=0), OK)])
+                                     (dict(M=0), SHAPE)])
 def test_packed_gemm_validation(kw, code):
     a = dict(M=64, N=256, K=256, x=P, ldx=256, sx=P3, w=P2, sw=P3, y=P)
     a.update(kw)
@@ -289,7 +293,7 @@ BATCH_CASES = [
     (dict(L=-1), SHAPE), (dict(L=65536), SHAPE), (dict(xb=-16), SHAPE), (dict(sxb=-1), SHAPE),
     (dict(swb=-1), SHAPE), (dict(yb=-1), SHAPE), (dict(wb=-16), SHAPE),
     (dict(xb=8), ALIGN), (dict(wb=24), ALIGN),
-    (dict(L=0), OK), (dict(M=0), OK),
+    (dict(L=0), SHAPE), (dict(M=0), SHAPE), (dict(N=0), SHAPE),
     (dict(x=None), NULL), (dict(w=None), NULL), (dict(K=200), SHAPE), (dict(gm=64), UNSUP),
     (dict(bias=P2, bb=-1), SHAPE), (dict(bias=ctypes.c_void_p(0x200002)), ALIGN),
 ]
@@ -332,10 +336,10 @@ def grouped(sizes, **kw):
 @no_gpu
 @pytest.mark.parametrize("sizes,kw,code", [
     ([10, -1], {}, SHAPE), ([1] * 65, {}, SHAPE), ([5], dict(G=-1), SHAPE), ([5], dict(nosizes=1), NULL),
-    ([0, 0, 0], {}, OK), ([], {}, OK), ([5, 7], dict(x=None), NULL), ([5, 7], dict(w=None), NULL),
+    ([0, 0, 0], {}, SHAPE), ([], {}, SHAPE), ([5, 7], dict(x=None), NULL), ([5, 7], dict(w=None), NULL),
     ([5, 7], dict(w=ODD), ALIGN), ([5, 7], dict(wb=8), ALIGN), ([5, 7], dict(swb=-1), SHAPE),
     ([5, 7], dict(K=200), SHAPE), ([5, 7], dict(gn=3), UNSUP), ([5, 7], dict(bb=-2, bias=P2), SHAPE),
-    ([5, 7], dict(N=0), OK),
+    ([5, 7], dict(N=0), SHAPE),
 ])
 def test_grouped_gemm_validation(sizes, kw, code):
     assert grouped(sizes, **kw) == code
@@ -357,7 +361,7 @@ def w8a16(**kw):
     (dict(K=200), SHAPE), (dict(ldx=128), SHAPE), (dict(ldw=64), SHAPE), (dict(ldm=16), SHAPE), (dict(ldy=100), SHAPE),
     (dict(M=65535 * 16 + 1), SHAPE), (dict(swk=-1), SHAPE),
     (dict(x=ODD), ALIGN), (dict(ldx=260), ALIGN), (dict(ldw=136), ALIGN), (dict(ldm=34), ALIGN), (dict(ldm=36), ALIGN),
-    (dict(bias=ctypes.c_void_p(0x100002)), ALIGN), (dict(M=0), OK), (dict(N=0), OK), (dict(wdt=3, M=0), OK),
+    (dict(bias=ctypes.c_void_p(0x100002)), ALIGN), (dict(M=0), SHAPE), (dict(N=0), SHAPE), (dict(wdt=3, M=0), SHAPE),
 ])
 def test_w8a16_validation(kw, code):
     assert w8a16(**kw) == code
@@ -376,7 +380,7 @@ def w4a16(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(x=None), NULL), (dict(w=None), NULL), (dict(meta=None), NULL), (dict(sw=None), NULL),
     (dict(ydt=2), UNSUP), (dict(form=2), UNSUP), (dict(K=200), SHAPE), (dict(ldw=32), SHAPE), (dict(ldm=16), SHAPE),
-    (dict(swn=-1), SHAPE), (dict(ldw=72), ALIGN), (dict(w=ODD), ALIGN), (dict(M=0), OK), (dict(N=0), OK),
+    (dict(swn=-1), SHAPE), (dict(ldw=72), ALIGN), (dict(w=ODD), ALIGN), (dict(M=0), SHAPE), (dict(N=0), SHAPE),
 ])
 def test_w4a16_validation(kw, code):
     assert w4a16(**kw) == code

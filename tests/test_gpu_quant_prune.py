@@ -222,3 +222,122 @@ def test_pack_strided_inputs():
     mb[:, :64] = up(meta)
     packed = sg.sparse24_pack_gfx950(vb[:, :256], mb[:, :64])
     assert np.array_equal(packed.cpu().numpy(), oracle.pack24_gfx950(vals, meta))
+
+
+def _nan_aware_equal(got: np.ndarray, want: np.ndarray) -> bool:
+    """Equal bit patterns, except that any NaN matches any NaN."""
+    gn, wn = np.isnan(got), np.isnan(want)
+    return np.array_equal(gn, wn) and np.array_equal(got[~gn].view(np.uint32), want[~wn].view(np.uint32))
+
+
+def _nonfinite_x(rows, cols, seed):
+    """Normal values with NaN and +-inf planted in some 1 x 64 blocks (and so in
+    the 128-wide and 128-row blocks around them)."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((rows, cols)).astype(np.float32)
+    for r, c, v in [(0, 3, np.nan), (1, 70, -np.inf), (2, 130, np.inf), (2, 131, np.nan), (5, 200, -np.nan),
+                    (rows - 1, cols - 1, np.inf)]:
+        x[r % rows, c % cols] = v
+    return x
+
+
+@pytest.mark.parametrize("gr,gc", [(1, 128), (1, 64), (128, 128), (128, 64)])
+@pytest.mark.parametrize("mode", ["fp8", "int8"])
+def test_quant_nan_and_inf_blocks(gr, gc, mode):
+    """A block holding a NaN gets a NaN scale, one holding an infinity an
+    infinite scale; codes are the encoder applied to v / s (e4m3: 0x7F for NaN;
+    int8: 0)."""
+    x = _nonfinite_x(260, 384, 7)
+    say(f"{mode} quant non-finite gr={gr} gc={gc}")
+    if mode == "fp8":
+        q, s = sg.fp8_quant_groupwise(up(x), gr=gr, gc=gc)
+        oq, os_ = oracle.fp8_quant_groupwise(x, gr, gc)
+    else:
+        q, s = sg.int8_quant_groupwise(up(x), gr=gr, gc=gc)
+        oq, os_ = oracle.int8_quant_groupwise(x, gr, gc)
+    torch.cuda.synchronize()
+    assert np.isnan(os_).any() and np.isinf(os_).any()
+    assert _nan_aware_equal(s.cpu().numpy(), os_)
+    assert np.array_equal(q.cpu().numpy(), oq)
+
+
+@pytest.mark.parametrize("whole", ["rows", "tensor"])
+def test_quant_nan_and_inf_scales_constant_along_k(whole):
+    x = _nonfinite_x(6, 256, 8)
+    if whole == "tensor":      # one scale: an infinity alone (no NaN) gives s = inf
+        x = np.where(np.isnan(x), np.float32(1.0), x)
+    gr = 1 if whole == "rows" else 6
+    q, s = sg.fp8_quant_groupwise(up(x), gr=gr, gc=256)
+    oq, os_ = oracle.fp8_quant_groupwise(x, gr, 256)
+    torch.cuda.synchronize()
+    assert _nan_aware_equal(s.cpu().numpy(), os_)
+    assert np.array_equal(q.cpu().numpy(), oq)
+
+
+def test_int4_quant_nan_and_inf_blocks():
+    x = _nonfinite_x(9, 384, 9)
+    q, s = sg.int4_quant_groupwise(up(x))
+    oq, os_ = oracle.int4_quant_groupwise(x, 128)
+    torch.cuda.synchronize()
+    assert _nan_aware_equal(s.cpu().numpy(), os_)
+    assert np.array_equal(q.cpu().numpy(), oq)
+
+
+def _bf16_bits(f32):
+    """Upper halves of fp32 values that bf16 represents exactly."""
+    return (np.ascontiguousarray(f32, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_prune_nan_and_inf_every_group(dtype):
+    """Every group over {+-0, +-1, +-inf, +-NaN}^4 (4096 groups), plus NaNs with
+    other payloads: NaN outranks infinity, NaNs tie, bits copied unchanged."""
+    import itertools
+    alphabet = np.array([0.0, -0.0, 1.0, -1.0, np.inf, -np.inf, np.nan, -np.nan], np.float32)
+    groups = alphabet[np.array(list(itertools.product(range(8), repeat=4)))].reshape(512, 32)
+    odd = np.array([0x7F800001, 0xFFFFFFFF, 0x7FC00001, 0x00000001] * 8, np.uint32).view(np.float32)
+    w = np.concatenate([groups, odd[None, :]])
+    if dtype == "bf16":
+        w = _bf16_bits(w)
+        w[-1, ::4] = 0x7F81          # a bf16 NaN with the smallest payload
+    v, m = sg.sparse24_prune_compress(up(w))
+    ov, om = oracle.prune_compress24(w)
+    torch.cuda.synchronize()
+    assert np.array_equal(m.cpu().numpy(), om)
+    got = v.cpu().view(torch.int16).numpy().view(np.uint16) if dtype == "bf16" else v.cpu().numpy().view(np.uint32)
+    assert np.array_equal(got, ov.view(np.uint16) if dtype == "bf16" else ov.view(np.uint32))
+
+
+@pytest.mark.parametrize("rows,k", [(128, 256), (333, 528), (4096, 4096), (1, 16), (14336, 4096)])
+def test_prune_e4m3_codes_match_oracle(rows, k):
+    """Already-quantised weights: e4m3 codes ranked by the magnitude they
+    encode (NaN codes 0x7F / 0xFF above 448, -0 equal to +0)."""
+    say(f"prune e4m3 {rows}x{k}")
+    rng = np.random.default_rng(rows + k)
+    c = rng.integers(0, 256, size=(rows, k)).astype(np.uint8)
+    special = rng.random((rows, k)) < 0.2
+    c[special] = rng.choice(np.array([0x00, 0x80, 0x7F, 0xFF, 0x7E, 0xFE, 0x01, 0x81], np.uint8),
+                            size=int(special.sum()))
+    v, m = sg.sparse24_prune_compress(up(c))
+    ov, om = oracle.prune_compress24(c)
+    torch.cuda.synchronize()
+    assert v.dtype == torch.uint8
+    assert np.array_equal(m.cpu().numpy(), om)
+    assert np.array_equal(v.cpu().numpy(), ov)
+
+
+def test_prune_e4m3_then_pack_feeds_the_sparse_gemm():
+    """Quantise W to e4m3 codes, prune the codes, pack them: the sparse GEMM on
+    that weight matches the oracle's GEMM on the oracle's pruned codes."""
+    d = workloads.sparse_large(seed=17, m=96, n=256, k=512)
+    xq, sx = oracle.fp8_quant_groupwise(d["x"], 1, 128)
+    wq, sw = oracle.fp8_quant_groupwise(d["w"], 128, 128)
+    v, m = sg.sparse24_prune_compress(up(wq))
+    ov, om = oracle.prune_compress24(wq)
+    torch.cuda.synchronize()
+    assert np.array_equal(v.cpu().numpy(), ov) and np.array_equal(m.cpu().numpy(), om)
+    from gpu_helpers import up_scales, down, assert_within_tolerance
+    y = down(sg.fp8_sparse24_gemm_groupwise(up(xq), up_scales(sx), v, m, up_scales(sw), 1, 128,
+                                            out_dtype=torch.float32))
+    ref, bound = oracle.fp8_sparse24_gemm_groupwise(xq, sx, 1, ov, om, sw, 128, bound=True)
+    assert_within_tolerance(y.astype(np.float64), ref, bound, "GEMM on pruned e4m3 codes")

@@ -366,7 +366,6 @@ def grouped_operands(sizes, n, k, seed, gn=128):
                                                ([5, 7, 300], "yt", torch.bfloat16, 128),
                                                ([200, 72], "yt", torch.float32, 1),
                                                ([16], "y", torch.float32, 128),
-                                               ([0, 0], "y", torch.bfloat16, 128),
                                                # every group <= 48 rows: the decode-sized grouped kernel
                                                ([1, 0, 17, 48, 33], "yt", torch.bfloat16, 128),
                                                ([16, 16, 3, 9], "y", torch.float32, 128),

@@ -94,5 +94,11 @@ def test_encode_saturates_and_keeps_sign_of_zero():
 
 @pytest.mark.parametrize("v", [np.nan, -np.nan])
 def test_encode_nan(v):
+    """Every NaN, whatever its sign, gets the one code 0x7F."""
     code = oracle.e4m3_encode(np.array([v], dtype=np.float32))[0]
-    assert code & 0x7F == 0x7F
+    assert code == 0x7F
+
+
+def test_encode_infinities_saturate():
+    v = np.array([np.inf, -np.inf], dtype=np.float32)
+    assert list(oracle.e4m3_encode(v)) == [0x7E, 0xFE]

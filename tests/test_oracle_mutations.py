@@ -71,7 +71,7 @@ def test_keeping_smallest_is_caught(monkeypatch):
     def prune(w):
         w = np.asarray(w)
         rows, k = w.shape
-        mag = sp_mod._magnitude(w).reshape(rows, k // 4, 4)
+        mag = np.abs(sp_mod._values(w)).reshape(rows, k // 4, 4)
         order = np.argsort(mag, axis=-1, kind="stable")
         keep = np.zeros((rows, k // 4, 4), bool)
         np.put_along_axis(keep, order[..., :2], True, axis=-1)
@@ -85,7 +85,7 @@ def test_tie_to_higher_index_is_caught(monkeypatch):
     def prune(w):
         w = np.asarray(w)
         rows, k = w.shape
-        mag = sp_mod._magnitude(w).reshape(rows, k // 4, 4)[..., ::-1]
+        mag = np.abs(sp_mod._values(w)).reshape(rows, k // 4, 4)[..., ::-1]
         order = 3 - np.argsort(-mag, axis=-1, kind="stable")
         keep = np.zeros((rows, k // 4, 4), bool)
         np.put_along_axis(keep, order[..., :2], True, axis=-1)
@@ -259,3 +259,29 @@ def test_w4a16_nibbles_swapped_is_caught(monkeypatch):
         return oracle.w8a16_sparse24_gemm_groupwise(x_bits, codes, wmeta, sw, 1, "int8", bound=bound)
     monkeypatch.setattr(oracle, "w4a16_sparse24_gemm_groupwise", w4)
     _fails(t_w8.test_w4a16_matches_exact_rationals)
+
+
+def test_nan_ranked_as_zero_is_caught(monkeypatch):
+    """A pruner that ranks |w| with NaN treated as the smallest magnitude (what
+    an fmax-style comparison does) drops NaN weights."""
+    def prune(w):
+        w = np.asarray(w)
+        rows, k = w.shape
+        mag = np.nan_to_num(np.abs(sp_mod._values(w)), nan=-1.0).reshape(rows, k // 4, 4)
+        order = np.argsort(-mag, axis=-1, kind="stable")
+        keep = np.zeros((rows, k // 4, 4), bool)
+        np.put_along_axis(keep, order[..., :2], True, axis=-1)
+        keep = keep.reshape(rows, k)
+        return keep, np.where(keep, w, np.zeros((), w.dtype)).astype(w.dtype)
+    monkeypatch.setattr(oracle, "prune24", prune)
+    _fails(t_sp.test_prune_brute_force_nonfinite)
+
+
+def test_amax_that_skips_nan_is_caught(monkeypatch):
+    """np.nanmax-style block maxima hide a NaN: the block gets a finite scale."""
+    orig = quant_mod._block_amax
+
+    def amax(x32, gr, gc):
+        return orig(np.nan_to_num(x32, nan=0.0), gr, gc)
+    monkeypatch.setattr(quant_mod, "_block_amax", amax)
+    _fails(t_quant.test_nonfinite_blocks_follow_ieee_through_the_formulas)

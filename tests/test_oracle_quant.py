@@ -160,3 +160,44 @@ def test_whole_row_and_tensor_groups_roundtrip_and_reach_448(whole):
     assert s.shape == ((rows, 1) if whole == "rows" else (1, 1))
     assert np.array_equal(s.reshape(-1), np.exp2(j[:, 0] if whole == "rows" else j[:1, 0]).astype(np.float32))
     assert np.array_equal(q, codes)
+
+
+def test_nonfinite_blocks_follow_ieee_through_the_formulas():
+    """A block holding a NaN: amax NaN, scale NaN, every quotient NaN, so every
+    e4m3 code is 0x7F and every integer code 0.  A block holding +-inf (no NaN):
+    amax and scale +inf; a finite v gives v / inf = +-0 (codes 0x00 / 0x80, or
+    integer 0) and the infinity gives inf / inf = NaN (0x7F, or 0).  Other
+    blocks are untouched."""
+    x = np.zeros((3, 256), np.float32)
+    x[0, :128] = np.linspace(-3, 3, 128, dtype=np.float32)
+    x[0, 7] = np.nan
+    x[1, :128] = 2.0
+    x[1, 5] = -1.0
+    x[1, 9] = -np.inf
+    x[:, 128:] = 4.0
+    q, s = oracle.fp8_quant_groupwise(x, 1, 128)
+    assert np.isnan(s[0, 0]) and s[1, 0] == np.inf and np.all(s[:, 1] == np.float32(4.0 / 448.0))
+    assert np.all(q[0, :128] == 0x7F)
+    want = np.zeros(128, np.uint8)
+    want[5] = 0x80
+    want[9] = 0x7F
+    assert np.array_equal(q[1, :128], want)
+    assert np.all(q[:, 128:] == 0x7E)
+    q8, s8 = oracle.int8_quant_groupwise(x, 1, 128)
+    assert np.isnan(s8[0, 0]) and s8[1, 0] == np.inf
+    assert np.all(q8[:2, :128] == 0) and np.all(q8[:, 128:] == 127)
+    q4, s4 = oracle.int4_quant_groupwise(x, 128)
+    assert np.isnan(s4[0, 0]) and s4[1, 0] == np.inf
+    assert np.all(q4[:2, :64] == 0) and np.all(q4[:, 64:] == 0x77)
+
+
+def test_nan_scale_comes_from_amax_not_from_the_zero_rule():
+    """The all-zero rule (s = 1) applies to amax == 0 only: a NaN block must not
+    fall into it (a comparison amax > 0 is false for NaN)."""
+    x = np.zeros((1, 128), np.float32)
+    x[0, 3] = np.nan
+    _, s = oracle.fp8_quant_groupwise(x, 1, 128)
+    assert np.isnan(s[0, 0])
+    x[0, 3] = 0.0
+    _, s = oracle.fp8_quant_groupwise(x, 1, 128)
+    assert s[0, 0] == 1.0

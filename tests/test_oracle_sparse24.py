@@ -119,3 +119,77 @@ def test_bf16_prune_matches_f32_of_same_values():
 def test_all_zero_weight_is_supported():
     vals, meta = oracle.prune_compress24(np.zeros((3, 16), np.float32))
     assert np.all(vals == 0) and np.all(meta == 0x44)
+
+
+def _rank_key(v):
+    """(is NaN, |v|): NaN above every number, NaNs equal among themselves."""
+    v = float(v)
+    return (1, 0.0) if v != v else (0, abs(v))
+
+
+def test_prune_brute_force_nonfinite():
+    """Every group over {+-0, +-1, +-inf, +-NaN}: the survivors are the entries
+    beaten by fewer than two others, with NaN ranked above infinity."""
+    alphabet = np.array([0.0, -0.0, 1.0, -1.0, np.inf, -np.inf, np.nan, -np.nan], dtype=np.float32)
+    groups = np.array(list(itertools.product(range(8), repeat=4)))
+    w = alphabet[groups]
+    keep, pruned = oracle.prune24(w)
+    for r in range(w.shape[0]):
+        k = [_rank_key(v) for v in w[r]]
+        want = [i for i in range(4) if sum(1 for j in range(4) if k[j] > k[i] or (k[j] == k[i] and j < i)) < 2]
+        assert list(np.nonzero(keep[r])[0]) == want, w[r]
+    assert np.array_equal(pruned.view(np.uint32)[keep], w.view(np.uint32)[keep])
+
+
+def test_prune_e4m3_codes_rank_like_their_magnitude_bits():
+    """e4m3 codes: with the sign bit cleared a code orders like its magnitude
+    (0x7F, the NaN, above 0x7E = 448), so the survivors follow the counting rule
+    on code & 0x7F -- written on the codes alone, without decoding them."""
+    rng = np.random.default_rng(5)
+    c = rng.integers(0, 256, size=(20000, 4)).astype(np.uint8)
+    c[:2000, :] = rng.choice(np.array([0x00, 0x80, 0x7F, 0xFF, 0x7E, 0xFE], np.uint8), size=(2000, 4))
+    keep, pruned = oracle.prune24(c)
+    for r in range(c.shape[0]):
+        key = [int(v) & 0x7F for v in c[r]]
+        want = [i for i in range(4) if sum(1 for j in range(4) if key[j] > key[i] or (key[j] == key[i] and j < i)) < 2]
+        assert list(np.nonzero(keep[r])[0]) == want, c[r]
+    assert np.all(pruned[~keep] == 0) and np.array_equal(pruned[keep], c[keep])
+    vals, meta = oracle.prune_compress24(c.reshape(-1, 8))
+    assert vals.dtype == np.uint8 and meta.shape == (c.shape[0] // 2, 1)
+
+
+def _golden_nonfinite_rows():
+    rows, cur = [], {}
+    for line in open(os.path.join(GOLDEN, "sparse24_nonfinite_e4m3.txt")):
+        line = line.split("#")[0].strip()
+        if not line:
+            continue
+        key, val = line.split(":", 1)
+        cur[key] = val.split()
+        if key == "meta":
+            rows.append(cur)
+            cur = {}
+    return rows
+
+
+def test_golden_nonfinite_and_e4m3_examples():
+    rows = _golden_nonfinite_rows()
+    assert [r["kind"][0] for r in rows] == ["f32", "f32", "e4m3", "e4m3"]
+    for ex in rows:
+        if ex["kind"][0] == "f32":
+            w = np.array([[float(v) for v in ex["w"]]], dtype=np.float32)
+            want_vals = np.array([float(v) for v in ex["vals"]], dtype=np.float32)
+        else:
+            w = np.array([[int(v, 16) for v in ex["w"]]], dtype=np.uint8)
+            want_vals = np.array([int(v, 16) for v in ex["vals"]], dtype=np.uint8)
+        keep, _ = oracle.prune24(w)
+        for g, pair in enumerate(ex["keep"]):
+            assert tuple(np.nonzero(keep[0, 4 * g:4 * g + 4])[0]) == tuple(int(i) for i in pair.split(","))
+        vals, meta = oracle.prune_compress24(w)
+        if w.dtype == np.uint8:
+            assert np.array_equal(vals[0], want_vals)
+        else:   # NaN != NaN: compare NaN positions, then the rest by value
+            assert np.array_equal(np.isnan(vals[0]), np.isnan(want_vals))
+            ok = ~np.isnan(want_vals)
+            assert np.array_equal(vals[0][ok], want_vals[ok])
+        assert meta[0, 0] == int(ex["meta"][0], 16)
