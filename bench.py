@@ -195,6 +195,22 @@ def rows_report():
             b = sparse_bytes(dm, dn, dk)
             out[f"decode_M{dm}_N{dn}_K{dk}_{form}"] = {"ms": ms, "GB/s": b / ms / 1e6,
                                                      "frac_hbm": b / ms / 1e6 / PEAK_HBM_GBS}
+        # next row: the activation quantisation fused into the GEMM, against
+        # quantise-then-GEMM (two launches); fp32 X in, bf16 Y out
+        y = torch.empty((dm, dn), dtype=torch.bfloat16, device=DEV)
+        bq = sparse_bytes(dm, dn, dk) - dm * dk - 4 * dm * (dk // 128) + 4 * dm * dk   # X read as fp32
+        ms = time_fn(lambda i: sg.fp8_sparse24_gemm_packed_quant_x(
+            xdd, wsets[i % ROTATE_DECODE][1], dn, wsets[i % ROTATE_DECODE][0], 128, y=y), reps=64, warm=16)
+        out[f"next_fused_quant_decode_M{dm}_N{dn}_K{dk}_y"] = {"ms": ms, "GB/s": bq / ms / 1e6,
+                                                               "frac_hbm": bq / ms / 1e6 / PEAK_HBM_GBS}
+
+        def separate(i):
+            sg.fp8_quant_groupwise(xdd, q=xq4, s=sx4)
+            sg.fp8_sparse24_gemm_groupwise_packed(xq4, sx4, wsets[i % ROTATE_DECODE][1], dn,
+                                                  wsets[i % ROTATE_DECODE][0], 1, 128, y=y)
+        ms = time_fn(separate, reps=64, warm=16)
+        out[f"next_quant_then_gemm_decode_M{dm}_N{dn}_K{dk}_y"] = {"ms": ms, "GB/s": bq / ms / 1e6,
+                                                                   "frac_hbm": bq / ms / 1e6 / PEAK_HBM_GBS}
         del wsets
     # one GPU's share of an 8-way tensor-parallel layer (column-parallel
     # up-projection N = 14336 / 8, bf16 out; row-parallel down-projection

@@ -272,6 +272,30 @@ sg_status sg_mixed_gemm_add(int64_t M, int64_t N, int64_t K1, int64_t K2, const 
                             int64_t ldw2, uint16_t* y, int64_t ldy, hipStream_t stream);
 
 /*
+ * sg_fp8_sparse24_gemm_packed_quant_x -- the packed 2:4 FP8 GEMM with the
+ * activation quantisation done inside it.  [T3258] jcaip's review: the
+ * activation is scaled and cast to float8_e4m3fn on its way into the sparse
+ * FP8 kernel.  X (fp32 or bf16) is quantised per 1 x 128 block exactly as
+ * sg_fp8_quant_groupwise(x, gr = 1, gc = 128) does it (block amax, s =
+ * amax / 448 by IEEE divide, codes = e4m3(x / s)), and the GEMM is
+ * sg_fp8_sparse24_gemm_groupwise_packed with those codes, gran_m = 1 and the
+ * same W operands: the result is bit for bit that of the two calls, without
+ * writing the codes and scales to memory.
+ *   x   : [M, K], x_dt SG_F32 or SG_BF16, leading dim ldx (elements).
+ *   wpacked, sw, sw_sn, sw_sk: as for sg_fp8_sparse24_gemm_groupwise_packed,
+ *         gran_n = 128 only.
+ *   y, y_dt, ldy, form: as for the other GEMMs.
+ * Decode sizes only: 1 <= M <= 64 (SG_ERR_UNSUPPORTED above; every workgroup
+ * quantises all of X, which pays off only while X is small against the
+ * weight).  Requires K % 128 == 0, ldx >= K, x 16-byte aligned with rows of a
+ * multiple of 16 bytes, 64 * ldx * sizeof(x_dt) < 2^32.
+ */
+sg_status sg_fp8_sparse24_gemm_packed_quant_x(int64_t M, int64_t N, int64_t K, const void* x, sg_dtype x_dt,
+                                              int64_t ldx, const uint8_t* wpacked, const float* sw, int64_t sw_sn,
+                                              int64_t sw_sk, int gran_n, void* y, sg_dtype y_dt, int64_t ldy,
+                                              sg_form form, hipStream_t stream);
+
+/*
  * int8 x int8 2:4-sparse GEMM ([T3258], jcaip: the existing 2:4 kernels are
  * int8 x int8 and fp8 x fp8).  The page fixes no int8 scheme; this one keeps
  * the FP8 path's groupwise blocks and uses the symmetric int8 grid.

@@ -19,6 +19,7 @@ from ._binding import (
     sparse24_packed_bytes,
     sparse24_pack_gfx950,
     fp8_sparse24_gemm_groupwise_packed,
+    fp8_sparse24_gemm_packed_quant_x,
     mixed_gemm_add,
     int8_quant_groupwise,
     int8_sparse24_gemm_groupwise,
@@ -38,6 +39,7 @@ __all__ = [
     "SgError", "lib", "fp8_quant_groupwise", "int4_quant_groupwise",
     "sparse24_prune_compress", "fp8_gemm_groupwise", "fp8_sparse24_gemm_groupwise",
     "sparse24_packed_bytes", "sparse24_pack_gfx950", "fp8_sparse24_gemm_groupwise_packed",
+    "fp8_sparse24_gemm_packed_quant_x",
     "mixed_gemm_add", "int8_quant_groupwise", "int8_sparse24_gemm_groupwise",
     "int8_sparse24_gemm_groupwise_packed", "probe_matrix_ops", "probe_matrix_rate", "k_constant_scales",
     "fp8_gemm_groupwise_batched", "fp8_sparse24_gemm_groupwise_batched",

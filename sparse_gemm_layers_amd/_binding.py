@@ -37,6 +37,8 @@ _SIGS = {
     "sg_sparse24_pack_gfx950": ([_ptr, _i64, _ptr, _i64, _i64, _i64, _ptr, _ptr], _int),
     "sg_fp8_sparse24_gemm_groupwise_packed": ([_i64, _i64, _i64, _ptr, _i64, _ptr, _i64, _i64, _int, _ptr, _ptr,
                                                _i64, _i64, _int, _ptr, _int, _i64, _int, _ptr], _int),
+    "sg_fp8_sparse24_gemm_packed_quant_x": ([_i64, _i64, _i64, _ptr, _int, _i64, _ptr, _ptr, _i64, _i64, _int,
+                                             _ptr, _int, _i64, _int, _ptr], _int),
     "sg_mixed_gemm_add": ([_i64, _i64, _i64, _i64, _ptr, _i64, _ptr, _i64, _i64, _ptr, _i64, _ptr, _i64, _i64,
                            _ptr, _i64, _ptr, _i64, _ptr, _i64, _ptr], _int),
     "sg_int8_quant_groupwise": ([_ptr, _int, _i64, _i64, _i64, _int, _int, _ptr, _i64, _ptr, _i64, _i64, _ptr], _int),
@@ -596,6 +598,28 @@ def fp8_sparse24_gemm_groupwise_packed(xq, sx, wpacked, n: int, sw, gran_m: int 
                                                      sw.stride(1), gran_n, _p(y), ydt, _row_stride(y), f,
                                                      _stream(xq))
     _check(st, "sg_fp8_sparse24_gemm_groupwise_packed")
+    return y
+
+
+def fp8_sparse24_gemm_packed_quant_x(x, wpacked, n: int, sw, gran_n: int = 128, out_dtype=torch.bfloat16,
+                                     form: str = "y", y=None):
+    """The packed 2:4 FP8 GEMM with X quantised inside it: x float32/bfloat16
+    [M, K] (M <= 64), quantised per 1 x 128 block as fp8_quant_groupwise(x, 1,
+    128) does; the result equals fp8_sparse24_gemm_groupwise_packed on those
+    codes bit for bit."""
+    _gpu2d(x, "x")
+    M, K = x.shape
+    _positive(M=M, N=n, K=K)
+    if K % 128 or gran_n != 128:
+        raise SgError("K must be a multiple of 128 and gran_n 128")
+    _want(x, "x", _FB, (M, K), x.device)
+    _want_packed(wpacked, n, K, x.device)
+    _want_scales(sw, "sw", -(-n // 128), K // 128, x.device)
+    y, f, ydt = _out(y, M, n, out_dtype, form, x.device)
+    st = lib().sg_fp8_sparse24_gemm_packed_quant_x(M, n, K, _p(x), _dtype_code(x, "x"), _row_stride(x), _p(wpacked),
+                                                   _p(sw), sw.stride(0), sw.stride(1), gran_n, _p(y), ydt,
+                                                   _row_stride(y), f, _stream(x))
+    _check(st, "sg_fp8_sparse24_gemm_packed_quant_x")
     return y
 
 

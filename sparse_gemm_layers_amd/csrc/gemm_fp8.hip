@@ -1541,7 +1541,7 @@ __global__ void __launch_bounds__(512) k_gemm_decode(GemmArgs a) {
 // (measured at M = 37, N = 4096, K = 14336: 16.8 against 23.0 us).
 template <int RB, int MT>
 struct DmaCfg {
-  static constexpr bool XR = MT >= 2 && RB == 4;                // X fragments in registers
+  static constexpr bool XR = MT >= 2 && (RB == 4 || MT == 4);   // X fragments in registers
   static constexpr int XOFF = RB * PK_CHUNK;                    // X slices (2 KB each) unless XR
   static constexpr int SXOFF = XOFF + (XR ? 0 : MT * 2048);     // X scales (256 B per sub-tile)
   static constexpr int SWOFF = SXOFF + MT * 256;                // W scales (256 B)
@@ -1606,6 +1606,63 @@ __device__ __forceinline__ void dma_issue(uint8_t* slot, const GemmArgs& a, __am
 #endif
 
 #if SG_DEVICE_PASS
+// The end of a decode workgroup: the 8 waves' partial tiles (each wave summed
+// its own K blocks) are added in wave order through LDS (r0, r1: two arrays of
+// ARR bytes that no load is filling any more) and stored with the bias.
+template <int RB, int MT, int ARR, bool OUT_BF16, bool OUT_T>
+__device__ __forceinline__ void dec_reduce_store(const GemmArgs& a, const v4f (&acc)[RB][MT], uint8_t* r0,
+                                                 uint8_t* r1, int64_t n0, int wave) {
+  const int t = threadIdx.x, l = t & 63;
+  if constexpr (DEC_WAVES * RB * MT * 64 * 16 <= ARR) {   // all partial tiles at once, in r0
+    __syncthreads();
+    float4* red = reinterpret_cast<float4*>(r0);    // [DEC_WAVES][RB * MT][64]
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int j = 0; j < MT; ++j)
+        red[(wave * RB * MT + rb * MT + j) * 64 + l] =
+            make_float4(acc[rb][j][0], acc[rb][j][1], acc[rb][j][2], acc[rb][j][3]);
+    __syncthreads();
+    for (int q = t; q < RB * MT * 64; q += 512) {
+      const int s = q >> 6, ll = q & 63, rb = s / MT, j = s % MT;
+      float4 v4 = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int w = 0; w < DEC_WAVES; ++w) {
+        const float4 v = red[(w * RB * MT + s) * 64 + ll];
+        v4.x += v.x; v4.y += v.y; v4.z += v.z; v4.w += v.w;
+      }
+      const v4f out = {v4.x, v4.y, v4.z, v4.w};
+      store_quad<OUT_BF16, OUT_T>(a, (int64_t)j * 16 + (ll & 15), n0 + 16 * rb + 4 * (ll >> 4),
+                                  with_bias(a, n0 + 16 * rb + 4 * (ll >> 4), out));
+    }
+    return;
+  }
+  // otherwise waves 0-3 hand their partial tiles over in r0, waves 4-7 in r1,
+  // one sub-tile column j at a time: [4][RB][64] float4 each
+  static_assert(4 * RB * 64 * 16 <= ARR, "LDS");
+  float4* const mine = reinterpret_cast<float4*>(wave < 4 ? r0 : r1) + (wave & 3) * RB * 64;
+#pragma unroll
+  for (int j = 0; j < MT; ++j) {
+    __syncthreads();
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+      mine[rb * 64 + l] = make_float4(acc[rb][j][0], acc[rb][j][1], acc[rb][j][2], acc[rb][j][3]);
+    __syncthreads();
+    for (int q = t; q < RB * 64; q += 512) {
+      const int rb = q >> 6, ll = q & 63;
+      float4 v4 = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int w = 0; w < DEC_WAVES; ++w) {
+        const float4 v = reinterpret_cast<const float4*>(w < 4 ? r0 : r1)[((w & 3) * RB + rb) * 64 + ll];
+        v4.x += v.x; v4.y += v.y; v4.z += v.z; v4.w += v.w;
+      }
+      const v4f out = {v4.x, v4.y, v4.z, v4.w};
+      store_quad<OUT_BF16, OUT_T>(a, (int64_t)j * 16 + (ll & 15), n0 + 16 * rb + 4 * (ll >> 4),
+                                  with_bias(a, n0 + 16 * rb + 4 * (ll >> 4), out));
+    }
+  }
+}
+
 // r0, r1: two LDS arrays of at least DmaCfg<RB, MT>::ARR bytes (the ring's
 // slots); bx: the workgroup's block of RB row blocks.
 template <bool I8, int RB, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
@@ -1710,54 +1767,7 @@ __device__ __forceinline__ void decode_dma_body(const GemmArgs& a, uint8_t* r0, 
     }
   }
   wait_vmcnt<0>();
-  if constexpr (DEC_WAVES * RB * MT * 64 * 16 <= C::ARR) {   // all partial tiles at once, in r0
-    __syncthreads();
-    float4* red = reinterpret_cast<float4*>(r0);    // [DEC_WAVES][RB * MT][64]
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int j = 0; j < MT; ++j)
-        red[(wave * RB * MT + rb * MT + j) * 64 + l] =
-            make_float4(acc[rb][j][0], acc[rb][j][1], acc[rb][j][2], acc[rb][j][3]);
-    __syncthreads();
-    for (int q = t; q < RB * MT * 64; q += 512) {
-      const int s = q >> 6, ll = q & 63, rb = s / MT, j = s % MT;
-      float4 v4 = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-      for (int w = 0; w < DEC_WAVES; ++w) {
-        const float4 v = red[(w * RB * MT + s) * 64 + ll];
-        v4.x += v.x; v4.y += v.y; v4.z += v.z; v4.w += v.w;
-      }
-      const v4f out = {v4.x, v4.y, v4.z, v4.w};
-      store_quad<OUT_BF16, OUT_T>(a, (int64_t)j * 16 + (ll & 15), n0 + 16 * rb + 4 * (ll >> 4),
-                                  with_bias(a, n0 + 16 * rb + 4 * (ll >> 4), out));
-    }
-    return;
-  }
-  // otherwise waves 0-3 hand their partial tiles over in r0, waves 4-7 in r1,
-  // one sub-tile column j at a time: [4][RB][64] float4 each
-  static_assert(4 * RB * 64 * 16 <= C::ARR, "LDS");
-  float4* const mine = reinterpret_cast<float4*>(wave < 4 ? r0 : r1) + (wave & 3) * RB * 64;
-#pragma unroll
-  for (int j = 0; j < MT; ++j) {
-    __syncthreads();
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-      mine[rb * 64 + l] = make_float4(acc[rb][j][0], acc[rb][j][1], acc[rb][j][2], acc[rb][j][3]);
-    __syncthreads();
-    for (int q = t; q < RB * 64; q += 512) {
-      const int rb = q >> 6, ll = q & 63;
-      float4 v4 = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-      for (int w = 0; w < DEC_WAVES; ++w) {
-        const float4 v = reinterpret_cast<const float4*>(w < 4 ? r0 : r1)[((w & 3) * RB + rb) * 64 + ll];
-        v4.x += v.x; v4.y += v.y; v4.z += v.z; v4.w += v.w;
-      }
-      const v4f out = {v4.x, v4.y, v4.z, v4.w};
-      store_quad<OUT_BF16, OUT_T>(a, (int64_t)j * 16 + (ll & 15), n0 + 16 * rb + 4 * (ll >> 4),
-                                  with_bias(a, n0 + 16 * rb + 4 * (ll >> 4), out));
-    }
-  }
+  dec_reduce_store<RB, MT, C::ARR, OUT_BF16, OUT_T>(a, acc, r0, r1, n0, wave);
 }
 #endif  // SG_DEVICE_PASS
 
@@ -1807,6 +1817,197 @@ __global__ void __launch_bounds__(512) k_gemm_grouped_tails(GemmArgs a, GroupTab
     if (a.M == 0) return;
     decode_dma_body<false, 4, 4, 128, OUT_BF16, OUT_T>(a, s0, s1, d % tail_gx);
   }
+#endif
+}
+
+// ------------------------------------------- decode kernel, activation quantised in the prologue
+// torchao PR #3258 "Introduce new W8A8-FP-CSR quantization API", jcaip's
+// review: the activation is scaled and cast to float8_e4m3fn on the way into
+// the sparse FP8 GEMM.  Here that cast happens inside the GEMM: X arrives as
+// fp32 or bf16 and every wave quantises the 1 x 128 blocks of the K blocks it
+// multiplies (block amax over the four lanes that hold a row's 128 values, one
+// IEEE divide per value, the e4m3 encoder of the quantiser kernels), so the
+// codes and scales are exactly those sg_fp8_quant_groupwise(gr = 1, gc = 128)
+// writes.  The work split, the K-block order of each wave, the promotion
+// acc += p * (sw * sx) and the reduction over the waves are those of
+// k_gemm_decode_dma, so every output is the same fp32 sum, term by term: the
+// fused call returns bit for bit what quantise-then-GEMM returns.
+//
+// Per wave and K block: the weight chunks and W scales go to a two-slot LDS
+// ring (LDS-DMA, as in k_gemm_decode_dma); the X values go to registers (32
+// per lane and 16-row sub-tile: lane (lr, g) holds row lr, values 32 g ..
+// 32 g + 31 of the block, exactly the bytes of the SMFMAC B fragment it
+// needs).  X of K block t + 1 is requested right after block t is quantised,
+// so its latency hides behind block t's multiplies and the wait for the
+// weight.  Each workgroup quantises all of X, so this pays off only while X is
+// small against the weight: the replicated quantisation costs about
+// (workgroups x M x K) divides.
+template <typename XT>
+struct XVals;
+template <>
+struct XVals<float> {
+  static constexpr int LOADS = 8;   // 16-byte loads per lane and sub-tile (32 values)
+  __device__ static void unpack(const v4i (&r)[LOADS], float (&v)[32]) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[4 * i + e] = __int_as_float(r[i][e]);
+  }
+};
+template <>
+struct XVals<uint16_t> {
+  static constexpr int LOADS = 4;
+  __device__ static void unpack(const v4i (&r)[LOADS], float (&v)[32]) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t u = (uint32_t)r[i][e];
+        v[8 * i + 2 * e] = __uint_as_float(u << 16);
+        v[8 * i + 2 * e + 1] = __uint_as_float(u & 0xffff0000u);
+      }
+  }
+};
+
+template <int RB>
+struct QCfg {
+  static constexpr int SWOFF = RB * PK_CHUNK;    // W scales (256 B)
+  static constexpr int KSZ = SWOFF + 256;        // bytes per wave per K block
+  static constexpr int ARR = DEC_WAVES * KSZ;    // one ring slot of all waves
+  static constexpr int L = 2 * RB + 1;           // LDS-DMA loads per K block
+};
+
+#if SG_DEVICE_PASS
+// One 16-row sub-tile's K block, as the lane's B fragment (32 codes) and its
+// row's scale.
+template <typename XT>
+__device__ __forceinline__ void quantise_block(const v4i (&raw)[XVals<XT>::LOADS], v8i& codes, float& sc) {
+  float v[32];
+  XVals<XT>::unpack(raw, v);
+  float a = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) a = amax_fold(a, v[i]);
+  uint32_t u = __float_as_uint(a);
+  u = max(u, (uint32_t)__shfl_xor((int)u, 16, 64));
+  u = max(u, (uint32_t)__shfl_xor((int)u, 32, 64));
+  sc = block_scale(__uint_as_float(u), 448.0f);
+#pragma unroll
+  for (int d = 0; d < 8; ++d)
+    codes[d] = (int)e4m3_pack4(v[4 * d] / sc, v[4 * d + 1] / sc, v[4 * d + 2] / sc, v[4 * d + 3] / sc);
+}
+
+template <typename XT, int RB, int MT, bool OUT_BF16, bool OUT_T>
+__device__ __forceinline__ void decode_q_body(const GemmArgs& a, uint8_t* r0, uint8_t* r1, int bx) {
+  using C = QCfg<RB>;
+  constexpr int NL = XVals<XT>::LOADS;
+  constexpr int ES = (int)sizeof(XT);
+  const int t = threadIdx.x, l = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int g = l >> 4, lr = l & 15;
+  const int64_t n0 = (int64_t)bx * 16 * RB;
+  const int KB = (int)(a.K >> 7);
+  const int nt = (KB - wave + DEC_WAVES - 1) / DEC_WAVES;    // K blocks of this wave
+  const int rows = (int)min((int64_t)(16 * RB), a.N - n0);
+  const int rbs = (rows + PK_ROWS - 1) / PK_ROWS;
+  const __amdgpu_buffer_rsrc_t rw = rsrc(a.w + (n0 / PK_ROWS) * KB * PK_CHUNK, (uint32_t)(rbs * KB * PK_CHUNK));
+  const __amdgpu_buffer_rsrc_t rw0 = rsrc(a.w, 0);
+  const __amdgpu_buffer_rsrc_t rx = rsrc(a.x, (uint32_t)(a.M * a.ldx * ES));
+  const __amdgpu_buffer_rsrc_t rx0 = rsrc(a.x, 0);
+  const __amdgpu_buffer_rsrc_t rsw = rsrc(a.sw, 0xffffffffu);
+  const uint32_t osw_src = (uint32_t)(((min(n0 + 16 * (l % RB), a.N - 1) >> 7) * a.sw_sn) * 4);
+  const uint32_t wslot = (uint32_t)wave * C::KSZ;
+  const uint32_t oa = wslot + pk_val_off(lr, g), om = wslot + PK_META + pk_meta_word(lr, g);
+  const uint32_t osw = wslot + C::SWOFF;
+  uint32_t xo[MT];   // row 16 j + lr, values 32 g .. of the K block (rows past M read zeros)
+#pragma unroll
+  for (int j = 0; j < MT; ++j) xo[j] = (uint32_t)((16 * j + lr) * a.ldx * ES + 32 * g * ES);
+
+  // K block number tt of this wave (tt >= nt: no memory access, zeros, W
+  // scales of the last block; issued anyway so every slot counts C::L loads)
+  auto issue_w = [&](uint8_t* arr, int tt) {
+    const bool valid = tt < nt;
+    const int kb = wave + DEC_WAVES * min(tt, nt - 1);   // >= 0: only called while nt >= 1
+    const __amdgpu_buffer_rsrc_t r = valid ? rw : rw0;
+    const int ws = valid ? kb * PK_CHUNK : 0;
+    uint8_t* slot = arr + wslot;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      uint8_t* c = slot + rb * PK_CHUNK;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)c, 16, (uint32_t)(rb * KB) * PK_CHUNK + l * 16, ws, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(c + PK_META), 4,
+                                               (uint32_t)(rb * KB) * PK_CHUNK + PK_META + l * 4, ws, 0, 0);
+    }
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, (lds_void*)(slot + C::SWOFF), 4, osw_src,
+                                             (int)(kb * a.sw_sk * 4), 0, 0);
+  };
+  v4i raw[MT][NL];
+  auto issue_x = [&](int tt) {
+    const bool valid = tt < nt;
+    const __amdgpu_buffer_rsrc_t r = valid ? rx : rx0;
+    const int xs = valid ? (wave + DEC_WAVES * tt) * 128 * ES : 0;
+#pragma unroll
+    for (int j = 0; j < MT; ++j)
+#pragma unroll
+      for (int i = 0; i < NL; ++i) raw[j][i] = buf_ld16(r, xo[j] + 16 * i, xs);
+  };
+
+  v4f acc[RB][MT];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int j = 0; j < MT; ++j) acc[rb][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+  // K block tt: its weight is in `sl`, its X values in raw
+  auto step = [&](const uint8_t* sl, int tt) {
+    v8i bxq[MT];
+    float sxv[MT];
+#pragma unroll
+    for (int j = 0; j < MT; ++j) quantise_block<XT>(raw[j], bxq[j], sxv[j]);
+    issue_x(tt + 1);
+    if (tt < nt) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const uint4 av = lds_ld<uint4>(sl, oa + rb * PK_CHUNK);
+        const int idx = lds_ld<int>(sl, om + rb * PK_CHUNK);
+        const float swv = lds_ld<float>(sl, osw + rb * 4);
+        const v4i aa = {(int)av.x, (int)av.y, (int)av.z, (int)av.w};
+#pragma unroll
+        for (int j = 0; j < MT; ++j) {
+          const v4f p = mma_sparse<false>(aa, bxq[j], idx);
+          acc[rb][j] += p * (swv * sxv[j]);
+        }
+      }
+    }
+  };
+
+  // block tt's weight lives in r0 for even tt, r1 for odd tt; the next block's
+  // weight is requested before this block is waited for.  A wave without K
+  // blocks (K < 8 * 128) issues nothing: its "last block" would not exist.
+  if (nt > 0) {
+    issue_w(r0, 0);
+    issue_x(0);
+  }
+  for (int t0 = 0; t0 < nt; t0 += 2) {
+    issue_w(r1, t0 + 1);
+    wait_vmcnt<C::L>();
+    step(r0, t0);
+    if (t0 + 1 < nt) {
+      issue_w(r0, t0 + 2);
+      wait_vmcnt<C::L>();
+      step(r1, t0 + 1);
+    }
+  }
+  wait_vmcnt<0>();
+  dec_reduce_store<RB, MT, C::ARR, OUT_BF16, OUT_T>(a, acc, r0, r1, n0, wave);
+}
+#endif  // SG_DEVICE_PASS
+
+template <typename XT, int RB, int MT, bool OUT_BF16, bool OUT_T>
+__global__ void __launch_bounds__(512) k_gemm_decode_q(GemmArgs a) {
+#if SG_DEVICE_PASS
+  __shared__ __attribute__((aligned(1024))) uint8_t r0[QCfg<RB>::ARR];
+  __shared__ __attribute__((aligned(1024))) uint8_t r1[QCfg<RB>::ARR];
+  decode_q_body<XT, RB, MT, OUT_BF16, OUT_T>(a, r0, r1, blockIdx.x);
 #endif
 }
 
@@ -1862,6 +2063,31 @@ static void launch_decode_mt(const GemmArgs& a, hipStream_t st) {
     k_gemm_decode<SPARSE, I8, PACKED, RB2, MT, GRAN_N, OUT_BF16, OUT_T><<<dec_grid(a, rows16, RB2), 512, 0, st>>>(a);
   else
     k_gemm_decode<SPARSE, I8, PACKED, 1, MT, GRAN_N, OUT_BF16, OUT_T><<<dec_grid(a, rows16, 1), 512, 0, st>>>(a);
+}
+
+// The fused-quantisation decode kernel: row blocks per workgroup as for the
+// other decode kernels (4, 2 or 1, keeping at least 224 workgroups); with
+// four fp32 sub-tiles only 1 (the X values of four sub-tiles fill the
+// registers).
+template <typename XT, int MT, bool OUT_BF16, bool OUT_T>
+static void launch_decode_q_mt(const GemmArgs& a, hipStream_t st) {
+  const int64_t rows16 = cdiv(a.N, 16);
+  if (MT == 4 && sizeof(XT) == 4)
+    k_gemm_decode_q<XT, 1, MT, OUT_BF16, OUT_T><<<dec_grid(a, rows16, 1), 512, 0, st>>>(a);
+  else if (rows16 >= 4 * 224)
+    k_gemm_decode_q<XT, 4, MT, OUT_BF16, OUT_T><<<dec_grid(a, rows16, 4), 512, 0, st>>>(a);
+  else if (rows16 >= 2 * 224)
+    k_gemm_decode_q<XT, 2, MT, OUT_BF16, OUT_T><<<dec_grid(a, rows16, 2), 512, 0, st>>>(a);
+  else
+    k_gemm_decode_q<XT, 1, MT, OUT_BF16, OUT_T><<<dec_grid(a, rows16, 1), 512, 0, st>>>(a);
+}
+
+template <typename XT, bool OUT_BF16, bool OUT_T>
+static void launch_decode_q(const GemmArgs& a, hipStream_t st) {
+  if (a.M <= 16) launch_decode_q_mt<XT, 1, OUT_BF16, OUT_T>(a, st);
+  else if (a.M <= 32) launch_decode_q_mt<XT, 2, OUT_BF16, OUT_T>(a, st);
+  else if (a.M <= 48) launch_decode_q_mt<XT, 3, OUT_BF16, OUT_T>(a, st);
+  else launch_decode_q_mt<XT, 4, OUT_BF16, OUT_T>(a, st);
 }
 
 template <bool SPARSE, bool I8, bool PACKED, int GRAN_N, bool OUT_BF16, bool OUT_T>
@@ -2067,6 +2293,43 @@ extern "C" sg_status sg_fp8_sparse24_gemm_groupwise(int64_t M, int64_t N, int64_
                                                     sg_form form, hipStream_t stream) {
   return sparse24_gemm<false>(M, N, K, xq, ldx, sx, sx_sm, sx_sk, gran_m, wv, ldwv, wmeta, ldwm, sw, sw_sn, sw_sk,
                               gran_n, y, y_dt, ldy, form, Batch{}, stream);
+}
+
+// Activation quantisation fused into the packed 2:4 GEMM (decode sizes,
+// M <= 64): X as fp32 or bf16, quantised per 1 x 128 block inside the kernel.
+extern "C" sg_status sg_fp8_sparse24_gemm_packed_quant_x(int64_t M, int64_t N, int64_t K, const void* x,
+                                                         sg_dtype x_dt, int64_t ldx, const uint8_t* wpacked,
+                                                         const float* sw, int64_t sw_sn, int64_t sw_sk,
+                                                         int gran_n, void* y, sg_dtype y_dt, int64_t ldy,
+                                                         sg_form form, hipStream_t stream) {
+  if (!x || !wpacked || !sw || !y) return SG_ERR_NULL;
+  if (x_dt != SG_F32 && x_dt != SG_BF16) return SG_ERR_UNSUPPORTED;
+  if (gran_n != 128) return SG_ERR_UNSUPPORTED;
+  if (y_dt != SG_F32 && y_dt != SG_BF16) return SG_ERR_UNSUPPORTED;
+  if (form != SG_OUT_Y && form != SG_OUT_YT) return SG_ERR_UNSUPPORTED;
+  if (M <= 0 || N <= 0 || K <= 0 || K % 128 != 0 || ldx < K) return SG_ERR_SHAPE;
+  if (M > 64) return SG_ERR_UNSUPPORTED;
+  if (ldy < (form == SG_OUT_Y ? N : M) || cdiv(N, 16) > 0x7fffffffLL) return SG_ERR_SHAPE;
+  const int64_t es = (int64_t)dtype_size(x_dt);
+  // X rows and K-block offsets are 32-bit buffer offsets
+  if (64 * ldx * es >= (1LL << 32) || K * es >= (1LL << 31) || sw_sn < 0 || sw_sk < 0) return SG_ERR_SHAPE;
+  if (((cdiv(N, 128) - 1) * sw_sn + (K / 128 - 1) * sw_sk) * 4 >= (1LL << 31)) return SG_ERR_SHAPE;
+  if ((K / 128) * (int64_t)(BN / PK_ROWS) * PK_CHUNK > 0x7fffffffLL) return SG_ERR_SHAPE;
+  if (!aligned(x, 16) || (ldx * es) % 16 || !aligned(wpacked, 16) || !aligned(sw, 4) ||
+      !aligned(y, dtype_size(y_dt)))
+    return SG_ERR_ALIGN;
+  GemmArgs a = make_args(M, N, K, static_cast<const uint8_t*>(x), ldx, nullptr, 0, 0, 1, wpacked, 0, nullptr, 0, sw,
+                         sw_sn, sw_sk, gran_n, y, y_dt, ldy, Batch{});
+  const bool bf16 = y_dt == SG_BF16, yt = form == SG_OUT_YT;
+  clear_hip_error();
+  if (x_dt == SG_F32) {
+    if (bf16) yt ? launch_decode_q<float, true, true>(a, stream) : launch_decode_q<float, true, false>(a, stream);
+    else yt ? launch_decode_q<float, false, true>(a, stream) : launch_decode_q<float, false, false>(a, stream);
+  } else {
+    if (bf16) yt ? launch_decode_q<uint16_t, true, true>(a, stream) : launch_decode_q<uint16_t, true, false>(a, stream);
+    else yt ? launch_decode_q<uint16_t, false, true>(a, stream) : launch_decode_q<uint16_t, false, false>(a, stream);
+  }
+  return launch_status();
 }
 
 extern "C" sg_status sg_fp8_sparse24_gemm_groupwise_packed(int64_t M, int64_t N, int64_t K, const uint8_t* xq,

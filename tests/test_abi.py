@@ -44,7 +44,8 @@ def test_header_declares_the_entry_points():
         "sg_int8_quant_groupwise", "sg_int8_sparse24_gemm_groupwise", "sg_int8_sparse24_gemm_groupwise_packed",
         "sg_fp8_gemm_groupwise_batched", "sg_fp8_sparse24_gemm_groupwise_batched",
         "sg_fp8_sparse24_gemm_groupwise_packed_batched", "sg_fp8_sparse24_gemm_groupwise_packed_grouped",
-        "sg_w8a16_sparse24_gemm_groupwise", "sg_w4a16_sparse24_gemm_groupwise"])
+        "sg_w8a16_sparse24_gemm_groupwise", "sg_w4a16_sparse24_gemm_groupwise",
+        "sg_fp8_sparse24_gemm_packed_quant_x"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -384,3 +385,26 @@ def w4a16(**kw):
 ])
 def test_w4a16_validation(kw, code):
     assert w4a16(**kw) == code
+
+
+def quant_x(**kw):
+    a = dict(M=16, N=256, K=256, x=P, xdt=0, ldx=256, w=P2, sw=P3, swn=2, swk=1, gn=128, y=P, ydt=1, ldy=256,
+             form=0)
+    a.update(kw)
+    return sg.lib().sg_fp8_sparse24_gemm_packed_quant_x(a["M"], a["N"], a["K"], a["x"], a["xdt"], a["ldx"], a["w"],
+                                                        a["sw"], a["swn"], a["swk"], a["gn"], a["y"], a["ydt"],
+                                                        a["ldy"], a["form"], None)
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), NULL), (dict(w=None), NULL), (dict(sw=None), NULL), (dict(y=None), NULL),
+    (dict(xdt=2), UNSUP), (dict(xdt=3), UNSUP), (dict(gn=1), UNSUP), (dict(ydt=2), UNSUP), (dict(form=2), UNSUP),
+    (dict(M=65), UNSUP), (dict(M=0), SHAPE), (dict(N=0), SHAPE), (dict(K=0), SHAPE), (dict(K=200), SHAPE),
+    (dict(ldx=128), SHAPE), (dict(ldy=100), SHAPE), (dict(form=1, ldy=8), SHAPE), (dict(swn=-1), SHAPE),
+    (dict(ldx=1 << 26, K=128), SHAPE),
+    (dict(x=ODD), ALIGN), (dict(ldx=258), ALIGN), (dict(xdt=1, ldx=260), ALIGN), (dict(w=ODD), ALIGN),
+    (dict(y=ctypes.c_void_p(0x100001)), ALIGN),
+])
+def test_quant_x_gemm_validation(kw, code):
+    assert quant_x(**kw) == code
