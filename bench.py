@@ -84,11 +84,28 @@ def k_constant(s, rows, k):
     return s[:, None].expand(rows, k // 128)
 
 
+# Row markers for counter runs (--markers): before each timed row, one launch
+# of the streaming-read probe with a grid of 1000 + (row number) workgroups,
+# which the counter summary uses to tell the rows' dispatches apart.
+MARKERS = {"on": False, "n": 0, "buf": None, "sink": None}
+
+
+def _mark_row():
+    if not MARKERS["on"]:
+        return
+    if MARKERS["buf"] is None:
+        MARKERS["buf"] = torch.zeros(16, dtype=torch.uint8, device=DEV)
+        MARKERS["sink"] = torch.empty(4096 * 256, dtype=torch.float32, device=DEV)
+    MARKERS["n"] += 1
+    sg.probe_stream_read(MARKERS["buf"], 1000 + MARKERS["n"], MARKERS["sink"])
+
+
 def time_fn(fn, reps=50, warm=5):
     """Mean GPU time of one call: `reps` calls are queued back to back behind a
     short GPU sleep (so that the host's launch cost, which exceeds the run time
     of the small kernels, stays outside the timed interval) and timed with one
     pair of HIP events; gaps between the kernels are included."""
+    _mark_row()
     for _ in range(warm):
         fn(0)
     torch.cuda.synchronize()
@@ -393,8 +410,18 @@ def cpu_baseline(min_seconds=8.0):
         if time.perf_counter() - t_all >= min_seconds:
             break
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": 2.0 * m * n * k / float(np.mean(times)) / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": model, "logical_cpus": os.cpu_count(),
+            "scope": "the GEMM alone (the GPU value's step also quantises X; the GPU GEMM alone is "
+                     "roofline.achieved)",
             "sample": f"full 2048x4096x4096 2:4 GEMM (fp64 NumPy oracle, {len(times)} runs, "
                       f"{np.mean(times):.2f} s each; quantisation/pruning done beforehand, untimed)"}
 
@@ -406,7 +433,8 @@ def measured_peaks():
     out = {}
     sink = torch.empty(sg._binding.PROBE_WORKGROUPS * 512, dtype=torch.float32, device=DEV)
     clocks = torch.zeros(4 * sg._binding.PROBE_WORKGROUPS, dtype=torch.int64, device=DEV)
-    for kind, iters in (("mfma_fp8", 2000), ("smfmac_fp8", 4000), ("mfma_i8", 4000)):
+    for kind, iters in (("mfma_fp8", 2000), ("smfmac_fp8", 4000), ("mfma_i8", 4000), ("smfmac_promoted", 2000),
+                        ("smfmac_rescaled", 2000)):
         best, ghz = None, None
         for _ in range(3):
             s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -428,6 +456,22 @@ def measured_peaks():
     b.copy_(a)
     ms = time_fn(lambda i: b.copy_(a), reps=10, warm=2)
     out["device_copy_1GiB"] = {"GB/s": round(2 * nbytes / ms / 1e6, 1)}
+    del a, b
+    # a kernel that only streams (sg_probe_stream_read): the decode rows' weight
+    # bytes (16 copies cycled, more than the MALL holds) and 1 GiB, timed like
+    # the rows (launch gaps included)
+    ssink = torch.empty(4096 * 256, dtype=torch.float32, device=DEV)
+    for label, nb, copies in (("stream_read_37MB_16_copies", 37_240_000 // 16 * 16, 16),
+                              ("stream_read_1GiB", 1 << 30, 1)):
+        bufs = [torch.empty(nb, dtype=torch.uint8, device=DEV).fill_(i + 1) for i in range(copies)]
+        best = None
+        for wg in (512, 1024, 4096):
+            ms = time_fn(lambda i: sg.probe_stream_read(bufs[i % copies], wg, ssink),
+                         reps=64 if copies > 1 else 10, warm=8)
+            if best is None or ms < best[0]:
+                best = (ms, wg)
+        out[label] = {"GB/s": round(nb / best[0] / 1e6, 1), "us": round(best[0] * 1e3, 2), "workgroups": best[1]}
+        del bufs
     del a, b
     return out
 
@@ -458,7 +502,7 @@ def write_traffic_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
     """Writes the traffic file of the sparse GEMM from four counter runs (see
     its header for the commands): HBM bytes per launch, each counter scaled by
     what it reads for a plain device copy of known size."""
-    kern = "k_gemm_sparse_x2"
+    kern = "k_gemm_sparse_wr"
     g_f = pmc_kib_per_dispatch(fetch_dir, "FETCH_SIZE", kern)
     g_w = pmc_kib_per_dispatch(write_dir, "WRITE_SIZE", kern)
     # the device-to-device copy (the HIP runtime's blit kernel behind tensor.copy_)
@@ -471,7 +515,10 @@ def write_traffic_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
     cmd = "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {c} -d <repo>/gpurun_out/prof/{d} -o run -- python -u <repo>/bench.py {a}"
     lines = [
         "# HBM traffic of the 2:4 sparse FP8 GEMM, 2048x4096x4096, packed weight, Y form, bf16 output",
-        "# kernel: sg::k_gemm_sparse_x2<true, 128, true, false> (one launch = the whole GEMM)",
+        "# kernel: sg::k_gemm_sparse_wr<128, true, false> (one launch = the whole GEMM)",
+        "# FETCH_SIZE and WRITE_SIZE count the L2's traffic to and from memory behind it: L2 misses",
+        "# (some of them served by the 256 MB MALL, not HBM) and write-backs; the copy calibration",
+        "# converts the counts to bytes, so the figures below are an upper bound on HBM bytes",
         "# commands (from the repository root on an MI355X; one counter per run):",
         "#   " + cmd.format(c="FETCH_SIZE", d="FETCH_SIZE", a="--only gemm --steps 20 --warmup 5"),
         "#   " + cmd.format(c="WRITE_SIZE", d="WRITE_SIZE", a="--only gemm --steps 20 --warmup 5"),
@@ -518,6 +565,105 @@ def traffic_from_profile():
         return None
 
 
+def _dispatch_counters(run_dir):
+    """Every kernel dispatch of a rocprofv3 --pmc run, in dispatch order:
+    (kernel name, grid x, grid y, grid z, {counter: value summed over instances})."""
+    import glob
+    import sqlite3
+    db = sorted(glob.glob(os.path.join(run_dir, "**", "*_results.db"), recursive=True))[0]
+    cur = sqlite3.connect(db).cursor()
+    rows = cur.execute(
+        "select d.id, s.kernel_name, d.grid_size_x, d.grid_size_y, d.grid_size_z, i.name, sum(p.value) "
+        "from rocpd_pmc_event p join rocpd_kernel_dispatch d on p.event_id = d.event_id "
+        "join rocpd_info_kernel_symbol s on d.kernel_id = s.id join rocpd_info_pmc i on p.pmc_id = i.id "
+        "group by d.id, i.name order by d.id").fetchall()
+    out = {}
+    for did, name, gx, gy, gz, cname, v in rows:
+        out.setdefault(did, [name, gx, gy, gz, {}])[4][cname] = float(v)
+    return [tuple(v) for _, v in sorted(out.items())]
+
+
+def _short(name):
+    name = name.split("(")[0]
+    return name[:-len(" [clone .kd]")] if name.endswith(" [clone .kd]") else name
+
+
+def counter_summary(out_file, bench_json, title, command_lines, run_dirs):
+    """Per benchmark row (split by the --markers probe launches) and kernel: the
+    mean of every counter over the row's dispatches of that kernel, merged over
+    the runs, with the derived figures used in the analysis."""
+    order = json.load(open(bench_json))["row_order"]
+    table = {}
+    for rd in run_dirs:
+        row = None
+        for name, gx, gy, gz, cnt in _dispatch_counters(rd):
+            if "k_probe_stream" in name and gx // 256 > 1000:
+                row = order[gx // 256 - 1001]
+                continue
+            if row is None:
+                continue
+            key = (row, _short(name), f"{gx}x{gy}x{gz}")
+            t = table.setdefault(key, {"calls": 0, "sums": {}, "n": {}})
+            for c, v in cnt.items():
+                t["sums"][c] = t["sums"].get(c, 0.0) + v
+                t["n"][c] = t["n"].get(c, 0) + 1
+    lines = [f"# {title}", "# commands (from the repository root on an MI355X; one counter set per run):"]
+    lines += ["#   " + c for c in command_lines]
+    lines += ["# rows: the benchmark row (its name gives the problem shape), kernel, grid in work-items;",
+              "# values: mean per dispatch of each counter, summed over hardware instances.",
+              "#   mfma_util  = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8 XCDs)",
+              "#   valu_per_wave = SQ_INSTS_VALU / SQ_WAVES; lds_confl = SQ_LDS_BANK_CONFLICT / "
+              "(SQ_LDS_IDX_ACTIVE - SQ_LDS_BANK_CONFLICT)",
+              "#   fetch_MiB / write_MiB = FETCH_SIZE / WRITE_SIZE (KiB, L2-to-memory traffic incl. MALL hits) / 1024"]
+    for (row, kern, grid), t in table.items():
+        m = {c: t["sums"][c] / t["n"][c] for c in t["sums"]}
+        d = []
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in m and m.get("GRBM_GUI_ACTIVE"):
+            d.append(f"mfma_util={m['SQ_VALU_MFMA_BUSY_CYCLES'] / (1024 * m['GRBM_GUI_ACTIVE'] / 8):.3f}")
+        if "SQ_INSTS_VALU" in m and m.get("SQ_WAVES"):
+            d.append(f"valu_per_wave={m['SQ_INSTS_VALU'] / m['SQ_WAVES']:.0f}")
+        if "SQ_LDS_BANK_CONFLICT" in m and m.get("SQ_LDS_IDX_ACTIVE"):
+            d.append(f"lds_confl={m['SQ_LDS_BANK_CONFLICT'] / max(m['SQ_LDS_IDX_ACTIVE'] - m['SQ_LDS_BANK_CONFLICT'], 1):.3f}")
+        if "FETCH_SIZE" in m:
+            d.append(f"fetch_MiB={m['FETCH_SIZE'] / 1024:.1f}")
+        if "WRITE_SIZE" in m:
+            d.append(f"write_MiB={m['WRITE_SIZE'] / 1024:.1f}")
+        lines.append(f"{row} | {kern} | grid {grid} | " + " ".join(d))
+        lines.append("    " + " ".join(f"{c}={v:.4g}" for c, v in sorted(m.items())))
+    open(out_file, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def stall_summary(out_file, title, command_lines, run_dirs, kernel_substr):
+    """Where the waves of one kernel spend their cycles (SQ counters, mean per
+    dispatch over the runs): fractions of SQ_WAVE_CYCLES."""
+    m, n = {}, {}
+    for rd in run_dirs:
+        for name, gx, gy, gz, cnt in _dispatch_counters(rd):
+            if kernel_substr not in name:
+                continue
+            for c, v in cnt.items():
+                m[c] = m.get(c, 0.0) + v
+                n[c] = n.get(c, 0) + 1
+    m = {c: m[c] / n[c] for c in m}
+    wc = m.get("SQ_WAVE_CYCLES", 0.0)
+    lines = [f"# {title}", "# commands (from the repository root on an MI355X; one counter set per run):"]
+    lines += ["#   " + c for c in command_lines]
+    lines += ["# mean per dispatch of each counter (summed over hardware instances); fractions are of",
+              "# SQ_WAVE_CYCLES (wave-cycles the kernel's waves were resident; the SQ counts these in",
+              "# units of 4 cycles, as it does the other *_CYCLES / WAIT / ACTIVE counters)"]
+    for c in sorted(m):
+        frac = f"  ({m[c] / wc:.3f} of wave cycles)" if wc and c != "SQ_WAVE_CYCLES" and \
+            (c.startswith("SQ_WAIT") or c.startswith("SQ_ACTIVE") or c.endswith("_CYCLES")) else ""
+        lines.append(f"{c}: {m[c]:.6g}{frac}")
+    if m.get("SQ_WAVES"):
+        for c in ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_VMEM_RD", "SQ_INSTS_SALU"):
+            if c in m:
+                lines.append(f"{c}_per_wave: {m[c] / m['SQ_WAVES']:.1f}")
+    open(out_file, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def copy_calibration():
     """A plain device copy of known size, for scaling the FETCH_SIZE/WRITE_SIZE counters."""
     nbytes = 512 << 20
@@ -540,6 +686,14 @@ def main():
                     help="write the sparse GEMM traffic file from FETCH_SIZE, WRITE_SIZE and the two copy "
                          "calibration counter runs")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--markers", action="store_true",
+                    help="with --only rows: a marker launch before each row, for the counter summary")
+    ap.add_argument("--counter-summary", nargs="+", metavar="ARG", default=None,
+                    help="OUT_FILE BENCH_JSON RUN_DIR...: per-row counter table of --only rows --markers runs")
+    ap.add_argument("--stall-summary", nargs="+", metavar="ARG", default=None,
+                    help="OUT_FILE KERNEL_SUBSTR RUN_DIR...: SQ cycle breakdown of one kernel")
+    ap.add_argument("--title", default="", help="first line of a summary file")
+    ap.add_argument("--command", action="append", default=[], help="a command line recorded in a summary file")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -553,9 +707,20 @@ def main():
     if args.traffic_summary:
         write_traffic_summary(*args.traffic_summary)
         return
+    if args.counter_summary:
+        counter_summary(args.counter_summary[0], args.counter_summary[1], args.title, args.command,
+                        args.counter_summary[2:])
+        return
+    if args.stall_summary:
+        stall_summary(args.stall_summary[0], args.title, args.command, args.stall_summary[2:],
+                      args.stall_summary[1])
+        return
     sg.lib()
     if args.only == "rows":
-        print(json.dumps({"rows": rows_report()}))
+        MARKERS["on"] = args.markers
+        rows = rows_report()
+        assert not args.markers or MARKERS["n"] == len(rows), "one marker per row"
+        print(json.dumps({"rows": rows, "row_order": list(rows.keys()), "markers": MARKERS["n"]}))
         return
     h = headline(args.steps, args.warmup)
     if args.only == "gemm":
@@ -586,7 +751,8 @@ def main():
         "roofline": {
             "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": tb,
-            "kernel": "k_gemm_sparse_x2<packed> (2:4 FP8 GEMM, Y form)", "avg_launch_ms": round(h["gemm_ms"], 5),
+            "kernel": "k_gemm_sparse_wr<128, bf16, Y> (2:4 FP8 GEMM, packed weight, Y form)",
+            "avg_launch_ms": round(h["gemm_ms"], 5),
         },
         "rows": {k: {kk: round(vv, 5) for kk, vv in v.items()} for k, v in rows.items()},
         "measured_peaks": measured_peaks(),

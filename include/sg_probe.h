@@ -26,7 +26,11 @@ extern "C" {
 typedef enum {
   SG_PROBE_MFMA_FP8 = 0,    /* v_mfma_f32_16x16x128_f8f6f4 with e4m3 operands (dense FP8)  */
   SG_PROBE_SMFMAC_FP8 = 1,  /* v_smfmac_f32_16x16x128_fp8_fp8 (2:4-sparse FP8)             */
-  SG_PROBE_MFMA_I8 = 2      /* v_mfma_i32_16x16x64_i8 (the int4 part of the mixed add)       */
+  SG_PROBE_MFMA_I8 = 2,     /* v_mfma_i32_16x16x64_i8 (the int4 part of the mixed add)       */
+  /* The 2:4 GEMM's unit of work, a 16 x 16 x 128 sparse product with its
+   * per-K-block promotion (4 fp32 results per lane): */
+  SG_PROBE_SMFMAC_PROMOTED = 3,  /* from zero, then acc += p * (sw * sx)  (4 FMAs)           */
+  SG_PROBE_SMFMAC_RESCALED = 4   /* acc *= r (4 multiplies), then accumulated in the matrix core */
 } sg_probe_kind;
 
 /* Dense-equivalent operations of one sg_probe_matrix_rate launch (2 per
@@ -45,6 +49,15 @@ int64_t sg_probe_matrix_ops(int kind, int iters);
  * Returns SG_ERR_NULL for a null buffer, SG_ERR_UNSUPPORTED for an unknown
  * kind, SG_ERR_SHAPE for iters < 1. */
 sg_status sg_probe_matrix_rate(int kind, int iters, float* sink, uint64_t* clocks, hipStream_t stream);
+
+/* Streaming read of `bytes` bytes at src (16-byte aligned, bytes a multiple of
+ * 16) by `workgroups` workgroups of 256 threads: each thread reads 16-byte
+ * chunks in a grid-stride loop, four loads in flight, and stores one value
+ * derived from them to sink[workgroups * 256] (device float) so that the
+ * reads cannot be optimised away.  Gives the HBM read rate a kernel that only
+ * streams reaches, for a buffer of a given size.  SG_ERR_NULL, SG_ERR_SHAPE
+ * (bytes < 16 or not a multiple of 16, workgroups < 1) or SG_ERR_ALIGN. */
+sg_status sg_probe_stream_read(const void* src, int64_t bytes, int workgroups, float* sink, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -26,6 +26,7 @@ from ._binding import (
     int8_sparse24_gemm_groupwise_packed,
     probe_matrix_ops,
     probe_matrix_rate,
+    probe_stream_read,
     k_constant_scales,
     fp8_gemm_groupwise_batched,
     fp8_sparse24_gemm_groupwise_batched,
@@ -41,7 +42,7 @@ __all__ = [
     "sparse24_packed_bytes", "sparse24_pack_gfx950", "fp8_sparse24_gemm_groupwise_packed",
     "fp8_sparse24_gemm_packed_quant_x",
     "mixed_gemm_add", "int8_quant_groupwise", "int8_sparse24_gemm_groupwise",
-    "int8_sparse24_gemm_groupwise_packed", "probe_matrix_ops", "probe_matrix_rate", "k_constant_scales",
+    "int8_sparse24_gemm_groupwise_packed", "probe_matrix_ops", "probe_matrix_rate", "probe_stream_read", "k_constant_scales",
     "fp8_gemm_groupwise_batched", "fp8_sparse24_gemm_groupwise_batched",
     "fp8_sparse24_gemm_groupwise_packed_batched", "fp8_sparse24_gemm_groupwise_packed_grouped",
     "w8a16_sparse24_gemm_groupwise", "w4a16_sparse24_gemm_groupwise",

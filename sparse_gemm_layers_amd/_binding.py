@@ -64,6 +64,7 @@ _SIGS = {
                                           _ptr, _ptr, _int, _i64, _int, _ptr], _int),
     "sg_probe_matrix_ops": ([_int, _int], _i64),
     "sg_probe_matrix_rate": ([_int, _int, _ptr, _ptr, _ptr], _int),
+    "sg_probe_stream_read": ([_ptr, _i64, _int, _ptr, _ptr], _int),
 }
 
 _lib = None
@@ -698,7 +699,7 @@ def mixed_gemm_add(x1, sx1, w1, sw1, x2, w2, y=None):
 # ------------------------------------------------------------ measurement helpers
 
 PROBE_WORKGROUPS = 1024
-PROBE_KINDS = {"mfma_fp8": 0, "smfmac_fp8": 1, "mfma_i8": 2}
+PROBE_KINDS = {"mfma_fp8": 0, "smfmac_fp8": 1, "mfma_i8": 2, "smfmac_promoted": 3, "smfmac_rescaled": 4}
 
 
 def probe_matrix_ops(kind, iters):
@@ -716,3 +717,13 @@ def probe_matrix_rate(kind, iters, sink, clocks):
             raise SgError(f"{nm} must be a contiguous device tensor of at least {n} elements")
     st = lib().sg_probe_matrix_rate(PROBE_KINDS[kind], iters, _p(sink), _p(clocks), _stream(sink))
     _check(st, "sg_probe_matrix_rate")
+
+
+def probe_stream_read(src, workgroups, sink):
+    """Enqueues one streaming read of the whole of src (a contiguous device
+    tensor, 16-byte aligned, a multiple of 16 bytes) by `workgroups`
+    workgroups; sink: float32 device tensor of at least workgroups * 256."""
+    if not src.is_cuda or not src.is_contiguous() or not sink.is_cuda or sink.numel() < workgroups * 256:
+        raise SgError("src must be a contiguous device tensor and sink hold workgroups * 256 floats")
+    st = lib().sg_probe_stream_read(_p(src), src.numel() * src.element_size(), workgroups, _p(sink), _stream(src))
+    _check(st, "sg_probe_stream_read")

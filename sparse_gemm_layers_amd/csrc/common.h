@@ -44,6 +44,15 @@ __device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float 
   return ((uint32_t)w & ~nan) | (0x7f7f7f7fu & nan);
 }
 
+// e4m3_pack4 for values known not to be NaN (no NaN patch; infinities still
+// saturate through the clamp).
+__device__ __forceinline__ uint32_t e4m3_pack4_finite(float a, float b, float c, float d) {
+  const auto cl = [](float v) { return fminf(fmaxf(v, -448.0f), 448.0f); };
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(cl(a), cl(b), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(cl(c), cl(d), w, true);
+  return (uint32_t)w;
+}
+
 // |v| folded into a running block maximum a (a >= 0).  Non-negative floats
 // order like their bit patterns and every NaN pattern lies above +inf, so the
 // maximum is taken on the bits: a block holding a NaN gets a NaN maximum

@@ -1878,8 +1878,25 @@ struct QCfg {
 };
 
 #if SG_DEVICE_PASS
+// fl32(v / s) from y = fl32(1 / s) with two FMA corrections (Markstein, "Computation
+// of elementary functions on the IBM RISC System/6000 processor", 1990: with y
+// within half an ulp of 1 / s and q within one ulp of v / s, the residual
+// r = v - s q is exact and fl(q + r y) is the correctly rounded quotient; the
+// first correction brings q0 = fl(v y), which may be 1.5 ulp off, within one
+// ulp).  It holds while nothing underflows: the caller takes it only for
+// 2^-90 <= s < inf, where every quotient that is not far below e4m3's
+// smallest code keeps its residual normal.  The sign is copied from v, so
+// that -0 / s stays -0.
+__device__ __forceinline__ float div_refined(float v, float s, float y) {
+  const float q0 = v * y;
+  const float q1 = fmaf(fmaf(-q0, s, v), y, q0);
+  const float q2 = fmaf(fmaf(-q1, s, v), y, q1);
+  return __uint_as_float((__float_as_uint(q2) & 0x7fffffffu) | (__float_as_uint(v) & 0x80000000u));
+}
+
 // One 16-row sub-tile's K block, as the lane's B fragment (32 codes) and its
-// row's scale.
+// row's scale: the codes of fl32(v / s), as the quantiser kernels compute
+// them with IEEE divides.
 template <typename XT>
 __device__ __forceinline__ void quantise_block(const v4i (&raw)[XVals<XT>::LOADS], v8i& codes, float& sc) {
   float v[32];
@@ -1891,9 +1908,17 @@ __device__ __forceinline__ void quantise_block(const v4i (&raw)[XVals<XT>::LOADS
   u = max(u, (uint32_t)__shfl_xor((int)u, 16, 64));
   u = max(u, (uint32_t)__shfl_xor((int)u, 32, 64));
   sc = block_scale(__uint_as_float(u), 448.0f);
+  if (sc >= 0x1p-90f && sc < __builtin_inff()) {   // finite scale: every v is finite
+    const float y = 1.0f / sc;
 #pragma unroll
-  for (int d = 0; d < 8; ++d)
-    codes[d] = (int)e4m3_pack4(v[4 * d] / sc, v[4 * d + 1] / sc, v[4 * d + 2] / sc, v[4 * d + 3] / sc);
+    for (int d = 0; d < 8; ++d)
+      codes[d] = (int)e4m3_pack4_finite(div_refined(v[4 * d], sc, y), div_refined(v[4 * d + 1], sc, y),
+                                        div_refined(v[4 * d + 2], sc, y), div_refined(v[4 * d + 3], sc, y));
+  } else {   // tiny, infinite or NaN scales: plain IEEE divides
+#pragma unroll
+    for (int d = 0; d < 8; ++d)
+      codes[d] = (int)e4m3_pack4(v[4 * d] / sc, v[4 * d + 1] / sc, v[4 * d + 2] / sc, v[4 * d + 3] / sc);
+  }
 }
 
 template <typename XT, int RB, int MT, bool OUT_BF16, bool OUT_T>

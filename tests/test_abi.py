@@ -45,7 +45,7 @@ def test_header_declares_the_entry_points():
         "sg_fp8_gemm_groupwise_batched", "sg_fp8_sparse24_gemm_groupwise_batched",
         "sg_fp8_sparse24_gemm_groupwise_packed_batched", "sg_fp8_sparse24_gemm_groupwise_packed_grouped",
         "sg_w8a16_sparse24_gemm_groupwise", "sg_w4a16_sparse24_gemm_groupwise",
-        "sg_fp8_sparse24_gemm_packed_quant_x"])
+        "sg_fp8_sparse24_gemm_packed_quant_x", "sg_probe_stream_read"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -253,9 +253,15 @@ def test_probe_rejects_bad_arguments_on_the_host():
     lib = sg.lib()
     assert lib.sg_probe_matrix_rate(0, 10, None, P, None) == NULL
     assert lib.sg_probe_matrix_rate(0, 10, P, None, None) == NULL
-    assert lib.sg_probe_matrix_rate(3, 10, P, P2, None) == UNSUP
+    assert lib.sg_probe_matrix_rate(5, 10, P, P2, None) == UNSUP
     assert lib.sg_probe_matrix_rate(-1, 10, P, P2, None) == UNSUP
     assert lib.sg_probe_matrix_rate(0, 0, P, P2, None) == SHAPE
+    assert lib.sg_probe_stream_read(None, 64, 4, P, None) == NULL
+    assert lib.sg_probe_stream_read(P, 64, 4, None, None) == NULL
+    assert lib.sg_probe_stream_read(P, 8, 4, P2, None) == SHAPE
+    assert lib.sg_probe_stream_read(P, 72, 4, P2, None) == SHAPE
+    assert lib.sg_probe_stream_read(P, 64, 0, P2, None) == SHAPE
+    assert lib.sg_probe_stream_read(ODD, 64, 4, P2, None) == ALIGN
 
 
 def test_probe_operation_counts():

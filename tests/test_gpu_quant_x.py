@@ -110,3 +110,56 @@ def test_strided_rows_zero_and_nonfinite_blocks():
     ok = ~np.isnan(a)
     assert np.array_equal(a[ok].view(np.uint32), b[ok].view(np.uint32))
     assert np.isfinite(a[[0, 1, 2, 3, 4]]).all()
+
+
+def identity_weight(k):
+    """A 2:4 weight whose GEMM is the identity: W = I (N = K) as e4m3 codes 1.0
+    with W scales 1, so y[m, k] = sx[m, k / 128] * e4m3(x_code[m, k]) for one
+    product each -- the dequantise-by-identity check of the torchao PR
+    (jcaip's review), used here to read the fused kernel's codes one by one."""
+    keep_vals, meta = oracle.prune_compress24(np.eye(k, dtype=np.float32))
+    codes = oracle.e4m3_encode(keep_vals)
+    return codes, meta, np.ones((k // 128, k // 128), np.float32)
+
+
+def near_midpoint_rows(rng, m, k):
+    """Rows whose quotients v / s fall on and next to the rounding boundaries of
+    e4m3 (the midpoints between neighbouring codes), for scales with awkward
+    mantissas across a wide exponent range: any quotient that is off by an ulp
+    shows up as a different code."""
+    pos = oracle.e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+    mids = (pos[:-1] + pos[1:]) / 2.0
+    x = np.zeros((m, k), np.float32)
+    for r in range(m):
+        for kb in range(k // 128):
+            s_mant = rng.choice([1.0, 1.5, 2.0 - 2.0 ** -23, 1.0 + 2.0 ** -23, rng.uniform(1, 2)])
+            e = int(rng.integers(-110, 80))     # below 2^-90 the scale takes plain divides
+            amax = np.float32(448.0 * s_mant * 2.0 ** e)
+            s = np.float32(amax / np.float32(448.0))
+            blk = np.empty(128, np.float32)
+            blk[0] = amax
+            mid = rng.choice(mids, 127) * rng.choice([-1.0, 1.0], 127)
+            base = (mid * np.float64(s)).astype(np.float32)
+            step = rng.integers(-2, 3, 127)
+            for i in range(127):
+                v = base[i]
+                for _ in range(abs(int(step[i]))):
+                    v = np.nextafter(v, np.float32(np.inf) if step[i] > 0 else np.float32(-np.inf))
+                blk[1 + i] = v
+            x[r, kb * 128:(kb + 1) * 128] = blk
+    return x
+
+
+@pytest.mark.parametrize("m", [16, 37, 64])
+def test_identity_weight_shows_every_code_near_rounding_boundaries(m):
+    k = 256
+    rng = np.random.default_rng(m)
+    x = near_midpoint_rows(rng, m, k)
+    codes, meta, sw = identity_weight(k)
+    wp = up(oracle.pack24_gfx950(codes, meta))
+    y_f, y_s = fused_and_separate(up(x), wp, k, up_scales(sw), torch.float32, "y")
+    assert_same_bits(y_f, y_s, f"identity M={m}")
+    xq, sx = oracle.fp8_quant_groupwise(x, 1, 128)
+    want = (oracle.e4m3_decode(xq) * np.repeat(sx.astype(np.float64), 128, axis=1)).astype(np.float32)
+    want = want + np.float32(0.0)       # the sum over the waves starts at +0: -0 comes out as +0
+    assert np.array_equal(y_f.cpu().numpy().view(np.uint32), want.view(np.uint32))
