@@ -774,7 +774,8 @@ __device__ __forceinline__ void wr_issue_x(uint8_t* arr, const WrPlan& p, __amdg
 // and GRAN_N = 0 accumulates in the matrix core (scales applied at the end).
 template <int GRAN_N, bool SCALED, typename Issue>
 __device__ __forceinline__ void wr_compute(const uint8_t* st, const WrRegs& w, v4f (&acc)[4][8], uint32_t x0,
-                                           uint32_t x1, uint32_t sxo, int wn, float (&cprev)[8], Issue&& issue) {
+                                           uint32_t x1, uint32_t sxo, int wn, float (&cprev)[8], uint32_t& clo,
+                                           uint32_t& chi, Issue&& issue) {
   float swv = 1.f;
   if (GRAN_N == 128) swv = lds_ld<float>(st, wr::SW_OFF + wn * 256);
 #pragma unroll
@@ -791,6 +792,8 @@ __device__ __forceinline__ void wr_compute(const uint8_t* st, const WrRegs& w, v
       if constexpr (SCALED) {
         const float r = cprev[j] * __builtin_amdgcn_rcpf(c);
         cprev[j] = c;
+        clo = min(clo, __float_as_uint(c));   // the range of the products seen, checked after the K loop
+        chi = max(chi, __float_as_uint(c));
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[i][j] = mma_sparse_acc<false>(w.v[i], bx, acc[i][j] * r, w.idx[i]);
       } else {
@@ -882,29 +885,31 @@ __device__ __forceinline__ void wr_tile(const GemmArgs& a, int tn, int tm, uint8
 
   // W operands: wa / wc for the first K block of even / odd super-periods,
   // wb for the second.  A wave's loads complete in issue order, so every W
-  // load is issued where nothing it must not wait for lies ahead of it: at a
-  // super-period's start (after waiting for its X array and W) come the W of
-  // its second K block (the only loads in flight then), the next X array,
-  // and the W of the next super-period's first K block (needed with that
-  // array).
+  // load is issued where nothing it must not wait for lies behind it: during
+  // a super-period's first K block come, column by column, the W of its
+  // second K block and the W of the next super-period's first K block (both
+  // needed one and two K blocks later), then the next X array.
   WrRegs wa, wb, wc;
-  wr_issue_x(arr0, plan, rx, rs, s_sk, 0, KB, wave);
-  wr_load_w(wa, rw, voff_v, voff_m, wn, q, KB);
+  auto start = [&]() {   // K blocks 0 and 1 of X, the first W, then K blocks 2 and 3 of X
+    wr_issue_x1(arr0, plan, rx, rs, s_sk, 0, 0, KB, wave);
+    wr_issue_x1(arr0, plan, rx, rs, s_sk, 0, 1, KB, wave);
+    wr_load_w(wa, rw, voff_v, voff_m, wn, q, KB);
+    wr_issue_x1(arr0, plan, rx, rs, s_sk, 0, 2, KB, wave);
+    wr_issue_x1(arr0, plan, rx, rs, s_sk, 0, 3, KB, wave);
+  };
 
   // Super-period P: K blocks 4 P .. 4 P + 3 in array P % 2; this wave
-  // multiplies 4 P + q and 4 P + 2 + q.  At its start all but the last
-  // wr::NW loads of the wave (the W of 4 P + q... issued after the array)
-  // have landed when the array has.
+  // multiplies 4 P + q and 4 P + 2 + q.  clo / chi: bit patterns of the
+  // smallest and largest scale product the scaled promotion met.
+  uint32_t clo = 0xffffffffu, chi = 0;
   auto kloop = [&](auto scaled_tag) {
     constexpr bool SCALED = decltype(scaled_tag)::value;
     float cprev[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    // The loads are spread over the multiplies (issued all at once, a wave
-    // stalls until the memory pipeline has taken them): during the first K
-    // block the W of the second (columns 0 .. 3) and the next array (columns
-    // 4 .. 7, one K block each), during the second the W of the next
-    // super-period's first K block (columns 0 .. 3).
+    // The loads are spread over the multiplies of the first K block (issued
+    // all at once, a wave stalls until the memory pipeline has taken them).
     auto period = [&](uint8_t* cur, uint8_t* nxt, WrRegs& w0, WrRegs& w0next, int P) {
-      wait_vmcnt<0>();
+      if (P == 0) wait_vmcnt<6>();   // the first super-period: X K blocks 2, 3 (6 loads) may still fly
+      else wait_vmcnt<0>();
       lds_barrier();
       auto issue0 = [&](int j) {
         if (j < 4) wr_load_w1(wb, j, rw, voff_v, voff_m, wn, 4 * P + 2 + q, KB);
@@ -914,13 +919,17 @@ __device__ __forceinline__ void wr_tile(const GemmArgs& a, int tn, int tm, uint8
         if (j < 4) wr_load_w1(w0next, j, rw, voff_v, voff_m, wn, 4 * (P + 1) + q, KB);
       };
       if (4 * P + q < KB) {
-        wr_compute<GRAN_N, SCALED>(cur + q * wr::KBYTES, w0, acc, x0, x1, sxo, wn, cprev, issue0);
+        wr_compute<GRAN_N, SCALED>(cur + q * wr::KBYTES, w0, acc, x0, x1, sxo, wn, cprev, clo, chi, issue0);
       } else {
 #pragma unroll
         for (int j = 0; j < 8; ++j) issue0(j);
       }
+      if (P == 0) {   // K blocks 2, 3 of X: issued before the 20 loads of the first K block's columns
+        wait_vmcnt<20>();
+        lds_barrier();
+      }
       if (4 * P + 2 + q < KB) {
-        wr_compute<GRAN_N, SCALED>(cur + (2 + q) * wr::KBYTES, wb, acc, x0, x1, sxo, wn, cprev, issue1);
+        wr_compute<GRAN_N, SCALED>(cur + (2 + q) * wr::KBYTES, wb, acc, x0, x1, sxo, wn, cprev, clo, chi, issue1);
       } else {
 #pragma unroll
         for (int j = 0; j < 8; ++j) issue1(j);
@@ -937,15 +946,30 @@ __device__ __forceinline__ void wr_tile(const GemmArgs& a, int tn, int tm, uint8
         for (int j = 0; j < 8; ++j) acc[i][j] *= cprev[j];
     }
   };
+  start();
   if constexpr (GRAN_N == 128) {
-    if (scales_tame<2>(a, m0, n0 + wn * 64, q, KB, l)) kloop(std::true_type{});
-    else kloop(std::false_type{});
+    // The rescaled promotion first; if any wave met a scale product that is
+    // not positive and normal, or products more than 2^60 apart, the whole
+    // tile is computed again with the zero-and-FMA promotion.
+    kloop(std::true_type{});
+    const bool ok = chi < clo ||   // no K block of this wave
+                    (clo >= 0x00800000u && chi <= 0x7f7fffffu && (chi >> 23) - (clo >> 23) <= 60u);
+    wait_vmcnt<0>();   // the last (unused) loads of every wave have landed before the barrier
+    if (__syncthreads_or(!ok)) {   // (also: every wave is done with both arrays)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+      start();
+      kloop(std::false_type{});
+      wait_vmcnt<0>();
+      __syncthreads();
+    }
   } else {
     kloop(std::false_type{});
+    wait_vmcnt<0>();   // the last (unused) W loads
+    __syncthreads();   // every wave is done with both arrays
   }
-
-  wait_vmcnt<0>();   // the last (unused) W loads
-  __syncthreads();   // every wave is done with both arrays
   if (q == 0) wr_send<0>(reinterpret_cast<float4*>(arr1), acc, wn, l);
   else wr_send<1>(reinterpret_cast<float4*>(arr0), acc, wn, l);
   __syncthreads();
