@@ -98,6 +98,7 @@ def _mark_row():
         MARKERS["sink"] = torch.empty(4096 * 256, dtype=torch.float32, device=DEV)
     MARKERS["n"] += 1
     sg.probe_stream_read(MARKERS["buf"], 1000 + MARKERS["n"], MARKERS["sink"])
+    print(f"row {MARKERS['n']}", file=sys.stderr, flush=True)   # progress of long counter runs
 
 
 def time_fn(fn, reps=50, warm=5):
@@ -512,7 +513,7 @@ def write_traffic_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
     rs, ws = each_way_kib / c_f, each_way_kib / c_w
     rd, wr = g_f * 1024 * rs, g_w * 1024 * ws
     m, n, k = 2048, 4096, 4096
-    cmd = "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {c} -d <repo>/gpurun_out/prof/{d} -o run -- python -u <repo>/bench.py {a}"
+    cmd = "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {c} -d <repo>/gpurun_out/prof_after/{d} -o run -- python3 -u <repo>/bench.py {a}"
     lines = [
         "# HBM traffic of the 2:4 sparse FP8 GEMM, 2048x4096x4096, packed weight, Y form, bf16 output",
         "# kernel: sg::k_gemm_sparse_wr<128, true, false> (one launch = the whole GEMM)",
@@ -525,7 +526,7 @@ def write_traffic_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
         "# calibration (a plain 512 MiB device copy, same two counters):",
         "#   " + cmd.format(c="FETCH_SIZE", d="copy_FETCH_SIZE", a="--copy-calibration"),
         "#   " + cmd.format(c="WRITE_SIZE", d="copy_WRITE_SIZE", a="--copy-calibration"),
-        "# this file: python bench.py --traffic-summary gpurun_out/prof/{FETCH_SIZE,WRITE_SIZE,copy_FETCH_SIZE,"
+        "# this file: python bench.py --traffic-summary gpurun_out/prof_after/{FETCH_SIZE,WRITE_SIZE,copy_FETCH_SIZE,"
         "copy_WRITE_SIZE}",
         "# counters are mean KiB per dispatch over the run's dispatches of the kernel",
         f"gemm_FETCH_SIZE_KiB: {g_f:.1f}",
@@ -664,6 +665,29 @@ def stall_summary(out_file, title, command_lines, run_dirs, kernel_substr):
     print("\n".join(lines))
 
 
+def trace_summary(out_file, title, command_lines, run_dir):
+    """Per kernel of a rocprofv3 --kernel-trace run: calls and durations (us),
+    registers and LDS, longest total first."""
+    import glob
+    import sqlite3
+    db = sorted(glob.glob(os.path.join(run_dir, "**", "*_results.db"), recursive=True))[0]
+    cur = sqlite3.connect(db).cursor()
+    rows = cur.execute(
+        "select s.kernel_name, count(*), avg(d.end - d.start), min(d.end - d.start), max(d.end - d.start), "
+        "sum(d.end - d.start), s.arch_vgpr_count, s.accum_vgpr_count, s.group_segment_size "
+        "from rocpd_kernel_dispatch d join rocpd_info_kernel_symbol s on d.kernel_id = s.id "
+        "group by s.kernel_name order by sum(d.end - d.start) desc").fetchall()
+    lines = [f"# {title}", "# command (from the repository root on an MI355X):"]
+    lines += ["#   " + c for c in command_lines]
+    lines += ["# source: rocprofv3 --kernel-trace (rocpd database), durations in microseconds",
+              " calls    avg_us    min_us    max_us   total_us vgpr agpr  lds_B  kernel"]
+    for name, n, avg, mn, mx, tot, vg, ag, lds in rows:
+        lines.append(f"{n:6d} {avg / 1e3:9.2f} {mn / 1e3:9.2f} {mx / 1e3:9.2f} {tot / 1e3:10.1f} {vg:4d} {ag:4d} "
+                     f"{lds:6d}  {_short(name)[:110]}")
+    open(out_file, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def copy_calibration():
     """A plain device copy of known size, for scaling the FETCH_SIZE/WRITE_SIZE counters."""
     nbytes = 512 << 20
@@ -692,6 +716,8 @@ def main():
                     help="OUT_FILE BENCH_JSON RUN_DIR...: per-row counter table of --only rows --markers runs")
     ap.add_argument("--stall-summary", nargs="+", metavar="ARG", default=None,
                     help="OUT_FILE KERNEL_SUBSTR RUN_DIR...: SQ cycle breakdown of one kernel")
+    ap.add_argument("--trace-summary", nargs=2, metavar=("OUT_FILE", "RUN_DIR"), default=None,
+                    help="per-kernel duration table of a rocprofv3 --kernel-trace run")
     ap.add_argument("--title", default="", help="first line of a summary file")
     ap.add_argument("--command", action="append", default=[], help="a command line recorded in a summary file")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -710,6 +736,9 @@ def main():
     if args.counter_summary:
         counter_summary(args.counter_summary[0], args.counter_summary[1], args.title, args.command,
                         args.counter_summary[2:])
+        return
+    if args.trace_summary:
+        trace_summary(args.trace_summary[0], args.title, args.command, args.trace_summary[1])
         return
     if args.stall_summary:
         stall_summary(args.stall_summary[0], args.title, args.command, args.stall_summary[2:],
