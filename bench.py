@@ -84,9 +84,10 @@ def k_constant(s, rows, k):
     return s[:, None].expand(rows, k // 128)
 
 
-# Row markers for counter runs (--markers): before each timed row, one launch
-# of the streaming-read probe with a grid of 1000 + (row number) workgroups,
-# which the counter summary uses to tell the rows' dispatches apart.
+# Row markers for counter runs (--markers): before each timed row one launch
+# of the streaming-read probe with 1000 + (row number) workgroups, after it
+# one with 3000 + (row number), which the counter summary uses to take each
+# row's own dispatches (not the set-up of the next row).
 MARKERS = {"on": False, "n": 0, "buf": None, "sink": None}
 
 
@@ -99,6 +100,11 @@ def _mark_row():
     MARKERS["n"] += 1
     sg.probe_stream_read(MARKERS["buf"], 1000 + MARKERS["n"], MARKERS["sink"])
     print(f"row {MARKERS['n']}", file=sys.stderr, flush=True)   # progress of long counter runs
+
+
+def _end_row():
+    if MARKERS["on"]:
+        sg.probe_stream_read(MARKERS["buf"], 3000 + MARKERS["n"], MARKERS["sink"])
 
 
 def time_fn(fn, reps=50, warm=5):
@@ -117,6 +123,7 @@ def time_fn(fn, reps=50, warm=5):
         fn(i)
     e.record()
     torch.cuda.synchronize()
+    _end_row()
     return s.elapsed_time(e) / reps
 
 
@@ -585,6 +592,17 @@ def _dispatch_counters(run_dir):
 
 
 def _short(name):
+    """Readable kernel name: demangled (c++filt, when present) without its argument list."""
+    name = name[:-3] if name.endswith(".kd") else name
+    if name.startswith("_Z"):
+        import shutil
+        import subprocess
+        tool = shutil.which("c++filt") or shutil.which("llvm-cxxfilt")
+        if tool:
+            try:
+                name = subprocess.run([tool, name], capture_output=True, text=True, timeout=10).stdout.strip() or name
+            except (OSError, subprocess.SubprocessError):
+                pass
     name = name.split("(")[0]
     return name[:-len(" [clone .kd]")] if name.endswith(" [clone .kd]") else name
 
@@ -599,9 +617,9 @@ def counter_summary(out_file, bench_json, title, command_lines, run_dirs):
         row = None
         for name, gx, gy, gz, cnt in _dispatch_counters(rd):
             if "k_probe_stream" in name and gx // 256 > 1000:
-                row = order[gx // 256 - 1001]
+                row = order[gx // 256 - 1001] if gx // 256 < 3000 else None
                 continue
-            if row is None:
+            if row is None or not name.startswith("_ZN2sg"):   # the library's kernels only
                 continue
             key = (row, _short(name), f"{gx}x{gy}x{gz}")
             t = table.setdefault(key, {"calls": 0, "sums": {}, "n": {}})
@@ -610,12 +628,20 @@ def counter_summary(out_file, bench_json, title, command_lines, run_dirs):
                 t["n"][c] = t["n"].get(c, 0) + 1
     lines = [f"# {title}", "# commands (from the repository root on an MI355X; one counter set per run):"]
     lines += ["#   " + c for c in command_lines]
-    lines += ["# rows: the benchmark row (its name gives the problem shape), kernel, grid in work-items;",
-              "# values: mean per dispatch of each counter, summed over hardware instances.",
+    lines += ["# one line per benchmark row (its name gives the problem shape) and library kernel timed in it,",
+              "# grid in work-items; means per dispatch of counters summed over hardware instances:",
               "#   mfma_util  = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8 XCDs)",
               "#   valu_per_wave = SQ_INSTS_VALU / SQ_WAVES; lds_confl = SQ_LDS_BANK_CONFLICT / "
               "(SQ_LDS_IDX_ACTIVE - SQ_LDS_BANK_CONFLICT)",
-              "#   fetch_MiB / write_MiB = FETCH_SIZE / WRITE_SIZE (KiB, L2-to-memory traffic incl. MALL hits) / 1024"]
+              "#   read_MB / write_MB = FETCH_SIZE / WRITE_SIZE (KiB) x the plain-copy calibration of",
+              "#   sparse_gemm_2048x4096x4096_traffic.txt (FETCH_SIZE counts half of a copy's read bytes,",
+              "#   WRITE_SIZE all of its written bytes): L2-to-memory traffic, MALL hits included"]
+    scales = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
+    try:
+        kv = dict(l.split(":", 1) for l in open(TRAFFIC_FILE) if ":" in l and not l.startswith("#"))
+        scales = {"FETCH_SIZE": float(kv["read_scale"]), "WRITE_SIZE": float(kv["write_scale"])}
+    except (OSError, KeyError, ValueError):
+        pass
     for (row, kern, grid), t in table.items():
         m = {c: t["sums"][c] / t["n"][c] for c in t["sums"]}
         d = []
@@ -626,11 +652,10 @@ def counter_summary(out_file, bench_json, title, command_lines, run_dirs):
         if "SQ_LDS_BANK_CONFLICT" in m and m.get("SQ_LDS_IDX_ACTIVE"):
             d.append(f"lds_confl={m['SQ_LDS_BANK_CONFLICT'] / max(m['SQ_LDS_IDX_ACTIVE'] - m['SQ_LDS_BANK_CONFLICT'], 1):.3f}")
         if "FETCH_SIZE" in m:
-            d.append(f"fetch_MiB={m['FETCH_SIZE'] / 1024:.1f}")
+            d.append(f"read_MB={m['FETCH_SIZE'] * 1024 * scales['FETCH_SIZE'] / 1e6:.1f}")
         if "WRITE_SIZE" in m:
-            d.append(f"write_MiB={m['WRITE_SIZE'] / 1024:.1f}")
-        lines.append(f"{row} | {kern} | grid {grid} | " + " ".join(d))
-        lines.append("    " + " ".join(f"{c}={v:.4g}" for c, v in sorted(m.items())))
+            d.append(f"write_MB={m['WRITE_SIZE'] * 1024 * scales['WRITE_SIZE'] / 1e6:.1f}")
+        lines.append(f"{row} | {kern} | {grid} | " + " ".join(d))
     open(out_file, "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
