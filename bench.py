@@ -506,6 +506,18 @@ def pmc_kib_per_dispatch(run_dir, counter, kernel_substr):
     return float(np.mean([v for _, v in rows]))
 
 
+def pmc_kernel_names(run_dir, kernel_substr):
+    """The distinct (demangled) names of the kernels a --pmc run measured whose
+    name contains kernel_substr."""
+    import glob
+    import sqlite3
+    db = sorted(glob.glob(os.path.join(run_dir, "**", "*_results.db"), recursive=True))[0]
+    cur = sqlite3.connect(db).cursor()
+    rows = cur.execute("select distinct s.kernel_name from rocpd_kernel_dispatch d join rocpd_info_kernel_symbol s "
+                       "on d.kernel_id = s.id where s.kernel_name like ?", (f"%{kernel_substr}%",)).fetchall()
+    return sorted({_short(r[0]) for r in rows})
+
+
 def write_traffic_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
     """Writes the traffic file of the sparse GEMM from four counter runs (see
     its header for the commands): HBM bytes per launch, each counter scaled by
@@ -523,7 +535,8 @@ def write_traffic_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
     cmd = "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {c} -d <repo>/gpurun_out/prof_after/{d} -o run -- python3 -u <repo>/bench.py {a}"
     lines = [
         "# HBM traffic of the 2:4 sparse FP8 GEMM, 2048x4096x4096, packed weight, Y form, bf16 output",
-        "# kernel: sg::k_gemm_sparse_wr<128, true, false> (one launch = the whole GEMM)",
+        "# kernel (from the counter database): " + ", ".join(pmc_kernel_names(fetch_dir, kern)) +
+        " (one launch = the whole GEMM)",
         "# FETCH_SIZE and WRITE_SIZE count the L2's traffic to and from memory behind it: L2 misses",
         "# (some of them served by the 256 MB MALL, not HBM) and write-backs; the copy calibration",
         "# converts the counts to bytes, so the figures below are an upper bound on HBM bytes",
