@@ -480,7 +480,6 @@ def measured_peaks():
                 best = (ms, wg)
         out[label] = {"GB/s": round(nb / best[0] / 1e6, 1), "us": round(best[0] * 1e3, 2), "workgroups": best[1]}
         del bufs
-    del a, b
     return out
 
 
