@@ -442,7 +442,7 @@ def measured_peaks():
     sink = torch.empty(sg._binding.PROBE_WORKGROUPS * 512, dtype=torch.float32, device=DEV)
     clocks = torch.zeros(4 * sg._binding.PROBE_WORKGROUPS, dtype=torch.int64, device=DEV)
     for kind, iters in (("mfma_fp8", 2000), ("smfmac_fp8", 4000), ("mfma_i8", 4000), ("smfmac_promoted", 2000),
-                        ("smfmac_rescaled", 2000)):
+                        ("smfmac_rescaled", 2000), ("mfma_fp6", 4000)):
         best, ghz = None, None
         for _ in range(3):
             s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

@@ -30,7 +30,9 @@ typedef enum {
   /* The 2:4 GEMM's unit of work, a 16 x 16 x 128 sparse product with its
    * per-K-block promotion (4 fp32 results per lane): */
   SG_PROBE_SMFMAC_PROMOTED = 3,  /* from zero, then acc += p * (sw * sx)  (4 FMAs)           */
-  SG_PROBE_SMFMAC_RESCALED = 4   /* acc *= r (4 multiplies), then accumulated in the matrix core */
+  SG_PROBE_SMFMAC_RESCALED = 4,  /* acc *= r (4 multiplies), then accumulated in the matrix core */
+  SG_PROBE_MFMA_FP6 = 5          /* v_mfma_f32_16x16x128_f8f6f4 with e3m2 (bf6) operands: the
+                                    exact route for int4 values, whose integers -8..7 e3m2 holds */
 } sg_probe_kind;
 
 /* Dense-equivalent operations of one sg_probe_matrix_rate launch (2 per

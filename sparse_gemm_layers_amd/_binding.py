@@ -699,7 +699,8 @@ def mixed_gemm_add(x1, sx1, w1, sw1, x2, w2, y=None):
 # ------------------------------------------------------------ measurement helpers
 
 PROBE_WORKGROUPS = 1024
-PROBE_KINDS = {"mfma_fp8": 0, "smfmac_fp8": 1, "mfma_i8": 2, "smfmac_promoted": 3, "smfmac_rescaled": 4}
+PROBE_KINDS = {"mfma_fp8": 0, "smfmac_fp8": 1, "mfma_i8": 2, "smfmac_promoted": 3, "smfmac_rescaled": 4,
+               "mfma_fp6": 5}
 
 
 def probe_matrix_ops(kind, iters):

@@ -12,7 +12,22 @@ __global__ void __launch_bounds__(512) k_probe_matrix(int iters, float* sink, ui
   // e4m3 1.0 (0x38) operands; int8 operands 1; sparse index: groups keep elements 0 and 1
   const int fp8_one = 0x38383838, i8_one = 0x01010101;
   float total = 0.f;
-  if constexpr (KIND == SG_PROBE_MFMA_FP8) {
+  if constexpr (KIND == SG_PROBE_MFMA_FP6) {
+    // e3m2 1.0 is 0b001100; any 6-bit pattern serves the rate, so the packed
+    // operand words are filled with one repeated byte
+    const int w0 = 0x0c30c30c, w1 = 0x30c30c30, w2 = (int)0xc30c30c3u;
+    const v8i a = {w0, w1, w2, w0, w1, w2 + (l & 1), 0, 0};
+    const v8i b = {w0, w1, w2, w0, w1, w2, 0, 0};
+    v4f acc[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] = (v4f){0.f, 0.f, 0.f, 0.f};
+    for (int it = 0; it < iters; ++it)
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        acc[k] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[k], 3, 3, 0, 0, 0, 0);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) total += acc[k][0] + acc[k][3];
+  } else if constexpr (KIND == SG_PROBE_MFMA_FP8) {
     const v8i a = {fp8_one, fp8_one, fp8_one, fp8_one, fp8_one, fp8_one, fp8_one, fp8_one + (l & 1)};
     const v8i b = {fp8_one, fp8_one, fp8_one, fp8_one, fp8_one, fp8_one, fp8_one, fp8_one};
     v4f acc[8];
@@ -113,7 +128,8 @@ extern "C" int64_t sg_probe_matrix_ops(int kind, int iters) {
     case SG_PROBE_SMFMAC_FP8: per = 2LL * 16 * 16 * 128; break;
     case SG_PROBE_MFMA_I8: per = 2LL * 16 * 16 * 64; break;
     case SG_PROBE_SMFMAC_PROMOTED:
-    case SG_PROBE_SMFMAC_RESCALED: per = 2LL * 16 * 16 * 128; break;
+    case SG_PROBE_SMFMAC_RESCALED:
+    case SG_PROBE_MFMA_FP6: per = 2LL * 16 * 16 * 128; break;
     default: return -1;
   }
   return per * 8 * iters * 8 * (int64_t)SG_PROBE_WORKGROUPS;   // 8 waves per workgroup, 8 per round
@@ -121,7 +137,7 @@ extern "C" int64_t sg_probe_matrix_ops(int kind, int iters) {
 
 extern "C" sg_status sg_probe_matrix_rate(int kind, int iters, float* sink, uint64_t* clocks, hipStream_t stream) {
   if (!sink || !clocks) return SG_ERR_NULL;
-  if (kind < SG_PROBE_MFMA_FP8 || kind > SG_PROBE_SMFMAC_RESCALED) return SG_ERR_UNSUPPORTED;
+  if (kind < SG_PROBE_MFMA_FP8 || kind > SG_PROBE_MFMA_FP6) return SG_ERR_UNSUPPORTED;
   if (iters < 1) return SG_ERR_SHAPE;
   clear_hip_error();
   constexpr int G = SG_PROBE_WORKGROUPS;
@@ -132,7 +148,10 @@ extern "C" sg_status sg_probe_matrix_rate(int kind, int iters, float* sink, uint
     case SG_PROBE_SMFMAC_PROMOTED:
       k_probe_matrix<SG_PROBE_SMFMAC_PROMOTED><<<G, 512, 0, stream>>>(iters, sink, clocks);
       break;
-    default: k_probe_matrix<SG_PROBE_SMFMAC_RESCALED><<<G, 512, 0, stream>>>(iters, sink, clocks); break;
+    case SG_PROBE_SMFMAC_RESCALED:
+      k_probe_matrix<SG_PROBE_SMFMAC_RESCALED><<<G, 512, 0, stream>>>(iters, sink, clocks);
+      break;
+    default: k_probe_matrix<SG_PROBE_MFMA_FP6><<<G, 512, 0, stream>>>(iters, sink, clocks); break;
   }
   return launch_status();
 }

@@ -253,7 +253,7 @@ def test_probe_rejects_bad_arguments_on_the_host():
     lib = sg.lib()
     assert lib.sg_probe_matrix_rate(0, 10, None, P, None) == NULL
     assert lib.sg_probe_matrix_rate(0, 10, P, None, None) == NULL
-    assert lib.sg_probe_matrix_rate(5, 10, P, P2, None) == UNSUP
+    assert lib.sg_probe_matrix_rate(6, 10, P, P2, None) == UNSUP
     assert lib.sg_probe_matrix_rate(-1, 10, P, P2, None) == UNSUP
     assert lib.sg_probe_matrix_rate(0, 0, P, P2, None) == SHAPE
     assert lib.sg_probe_stream_read(None, 64, 4, P, None) == NULL
@@ -270,7 +270,7 @@ def test_probe_operation_counts():
     assert lib.sg_probe_matrix_ops(0, 1) == 2 * 16 * 16 * 128 * 8 * 8 * 1024
     assert lib.sg_probe_matrix_ops(1, 3) == 3 * 2 * 16 * 16 * 128 * 8 * 8 * 1024
     assert lib.sg_probe_matrix_ops(2, 1) == 2 * 16 * 16 * 64 * 8 * 8 * 1024
-    assert lib.sg_probe_matrix_ops(5, 1) == -1 and lib.sg_probe_matrix_ops(0, 0) == -1
+    assert lib.sg_probe_matrix_ops(6, 1) == -1 and lib.sg_probe_matrix_ops(0, 0) == -1
 
 
 def batched(kind, **kw):
