@@ -1021,9 +1021,13 @@ __device__ __forceinline__ void group_args(GemmArgs& a, const GroupTable& gt, in
   if (a.bias) a.bias += g * a.bbs;
 }
 
-// Large tile b (in the XCD order over T tiles) of a grouped problem.
-template <bool I8, bool PACKED, int GRAN_N, bool OUT_BF16, bool OUT_T>
-__device__ __forceinline__ void x2_grouped_tile(GemmArgs a, const GroupTable& gt, int T, uint8_t* db0, uint8_t* db1) {
+// Large tile b (in the XCD order over T tiles) of a grouped problem (packed
+// FP8 weights): the register-weight tile for 128-row W scale blocks and for
+// scales constant along K, else the two-operand LDS tile.  db0 / db1 hold at
+// least x2::DBL bytes each (more than the register-weight tile's arrays).
+template <int GRAN_N, bool OUT_BF16, bool OUT_T>
+__device__ __forceinline__ void grouped_tile(GemmArgs a, const GroupTable& gt, int T, uint8_t* db0, uint8_t* db1) {
+  static_assert(wr::ARR <= x2::DBL, "the register-weight tile's arrays fit the LDS tile's");
   const int b = xcd_order(blockIdx.x, T);
   int g = 0;
   while (g + 1 < gt.G && gt.tile_start[g + 1] <= b) ++g;   // uniform; empty groups are skipped
@@ -1031,16 +1035,19 @@ __device__ __forceinline__ void x2_grouped_tile(GemmArgs a, const GroupTable& gt
   int tn, tm;
   tile_of(b - gt.tile_start[g], tiles_m, gt.tiles_n, tn, tm);
   group_args<OUT_BF16, OUT_T>(a, gt, g);
-  x2_tile<I8, PACKED, GRAN_N, OUT_BF16, OUT_T>(a, tn, tm, db0, db1);
+  if constexpr (GRAN_N == 128 || GRAN_N == 0)
+    wr_tile<GRAN_N, OUT_BF16, OUT_T>(a, tn, tm, db0, db1);
+  else
+    x2_tile<false, true, GRAN_N, OUT_BF16, OUT_T>(a, tn, tm, db0, db1);
 }
 #endif  // SG_DEVICE_PASS
 
-template <bool I8, bool PACKED, int GRAN_N, bool OUT_BF16, bool OUT_T>
-__global__ void __launch_bounds__(512) k_gemm_sparse_x2_grouped(GemmArgs a, GroupTable gt) {
+template <int GRAN_N, bool OUT_BF16, bool OUT_T>
+__global__ void __launch_bounds__(512) k_gemm_sparse_grouped(GemmArgs a, GroupTable gt) {
 #if SG_DEVICE_PASS
   __shared__ __attribute__((aligned(1024))) uint8_t db0[x2::DBL];
   __shared__ __attribute__((aligned(1024))) uint8_t db1[x2::DBL];
-  x2_grouped_tile<I8, PACKED, GRAN_N, OUT_BF16, OUT_T>(a, gt, gt.tile_start[gt.G], db0, db1);
+  grouped_tile<GRAN_N, OUT_BF16, OUT_T>(a, gt, gt.tile_start[gt.G], db0, db1);
 #endif  // SG_DEVICE_PASS
 }
 
@@ -1807,7 +1814,7 @@ __global__ void __launch_bounds__(512) k_gemm_decode_dma(GemmArgs a) {
 
 // Grouped problems of at most 16 MT rows each (grid y = group): group g's X
 // rows, X scales (one row each), Y rows (columns of Y^T), packed weight, W
-// scales and bias, as in k_gemm_sparse_x2_grouped.  An empty group's
+// scales and bias, as in k_gemm_sparse_grouped.  An empty group's
 // workgroups return at once.
 template <bool I8, int RB, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
 __global__ void __launch_bounds__(512) k_gemm_decode_dma_grouped(GemmArgs a, GroupTable gt) {
@@ -1834,7 +1841,7 @@ __global__ void __launch_bounds__(512) k_gemm_grouped_tails(GemmArgs a, GroupTab
   __shared__ __attribute__((aligned(1024))) uint8_t s0[x2::DBL];
   __shared__ __attribute__((aligned(1024))) uint8_t s1[x2::DBL];
   if ((int)blockIdx.x < T) {
-    x2_grouped_tile<false, true, GRAN_N, OUT_BF16, OUT_T>(a, gt, T, s0, s1);
+    grouped_tile<GRAN_N, OUT_BF16, OUT_T>(a, gt, T, s0, s1);
   } else {
     const int d = (int)blockIdx.x - T;
     group_args<OUT_BF16, OUT_T>(a, gtail, d / tail_gx);
@@ -2443,8 +2450,7 @@ extern "C" sg_status sg_fp8_sparse24_gemm_groupwise_packed_batched(
 // Grouped 2:4 GEMM (one launch over every group's tiles; see GroupTable).
 template <int GRAN_N, bool OUT_BF16, bool OUT_T>
 static void launch_grouped(const GemmArgs& a, const GroupTable& gt, hipStream_t st) {
-  k_gemm_sparse_x2_grouped<false, true, GRAN_N, OUT_BF16, OUT_T>
-      <<<(unsigned)gt.tile_start[gt.G], 512, 0, st>>>(a, gt);
+  k_gemm_sparse_grouped<GRAN_N, OUT_BF16, OUT_T><<<(unsigned)gt.tile_start[gt.G], 512, 0, st>>>(a, gt);
 }
 
 template <int GRAN_N>
