@@ -466,14 +466,16 @@ def measured_peaks():
     out["device_copy_1GiB"] = {"GB/s": round(2 * nbytes / ms / 1e6, 1)}
     del a, b
     # a kernel that only streams (sg_probe_stream_read): the decode rows' weight
-    # bytes (16 copies cycled, more than the MALL holds) and 1 GiB, timed like
-    # the rows (launch gaps included)
+    # bytes (16 copies cycled, more than the MALL holds), the tensor-parallel
+    # share rows' bytes (64 copies) and 1 GiB, timed like the rows (launch gaps
+    # included)
     ssink = torch.empty(4096 * 256, dtype=torch.float32, device=DEV)
     for label, nb, copies in (("stream_read_37MB_16_copies", 37_240_000 // 16 * 16, 16),
+                              ("stream_read_4.7MB_64_copies", 4_700_000 // 16 * 16, 64),
                               ("stream_read_1GiB", 1 << 30, 1)):
         bufs = [torch.empty(nb, dtype=torch.uint8, device=DEV).fill_(i + 1) for i in range(copies)]
         best = None
-        for wg in (512, 1024, 4096):
+        for wg in (256, 512, 1024, 4096):
             ms = time_fn(lambda i: sg.probe_stream_read(bufs[i % copies], wg, ssink),
                          reps=64 if copies > 1 else 10, warm=8)
             if best is None or ms < best[0]:
