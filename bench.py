@@ -531,7 +531,7 @@ def write_traffic_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
     c_w = pmc_kib_per_dispatch(copy_write_dir, "WRITE_SIZE", "copyBuffer")
     each_way_kib = (512 << 20) / 1024
     rs, ws = each_way_kib / c_f, each_way_kib / c_w
-    rd, wr = g_f * 1024 * rs, g_w * 1024 * ws
+    rd, wr = round(g_f * 1024 * rs), round(g_w * 1024 * ws)   # whole bytes; the total is their sum
     m, n, k = 2048, 4096, 4096
     cmd = "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {c} -d <repo>/gpurun_out/prof_after/{d} -o run -- python3 -u <repo>/bench.py {a}"
     lines = [
@@ -557,9 +557,9 @@ def write_traffic_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
         f"copy_bytes_each_way_KiB: {each_way_kib:.0f}",
         f"read_scale: {rs:.5f}",
         f"write_scale: {ws:.5f}",
-        f"hbm_read_bytes_per_launch: {rd:.0f}",
-        f"hbm_write_bytes_per_launch: {wr:.0f}",
-        f"hbm_bytes_per_launch: {rd + wr:.0f}",
+        f"hbm_read_bytes_per_launch: {rd}",
+        f"hbm_write_bytes_per_launch: {wr}",
+        f"hbm_bytes_per_launch: {rd + wr}",
         f"algorithmic_bytes_per_launch: {sparse_bytes(m, n, k)}",
         "# reads are well above the algorithmic input bytes: each of the 8 XCDs' L2 fetches the X",
         "# row panels and W tiles its 32 workgroups use (4 n-tiles x 8 m-tiles per XCD)",
