@@ -533,7 +533,7 @@ def write_traffic_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
     rs, ws = each_way_kib / c_f, each_way_kib / c_w
     rd, wr = round(g_f * 1024 * rs), round(g_w * 1024 * ws)   # whole bytes; the total is their sum
     m, n, k = 2048, 4096, 4096
-    cmd = "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {c} -d <repo>/gpurun_out/prof_after/{d} -o run -- python3 -u <repo>/bench.py {a}"
+    cmd = "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {c} -d <out>/prof_after/{d} -o run -- python3 -u <repo>/bench.py {a}"
     lines = [
         "# HBM traffic of the 2:4 sparse FP8 GEMM, 2048x4096x4096, packed weight, Y form, bf16 output",
         "# kernel (from the counter database): " + ", ".join(pmc_kernel_names(fetch_dir, kern)) +
@@ -547,7 +547,7 @@ def write_traffic_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
         "# calibration (a plain 512 MiB device copy, same two counters):",
         "#   " + cmd.format(c="FETCH_SIZE", d="copy_FETCH_SIZE", a="--copy-calibration"),
         "#   " + cmd.format(c="WRITE_SIZE", d="copy_WRITE_SIZE", a="--copy-calibration"),
-        "# this file: python bench.py --traffic-summary gpurun_out/prof_after/{FETCH_SIZE,WRITE_SIZE,copy_FETCH_SIZE,"
+        "# this file: python bench.py --traffic-summary <out>/prof_after/{FETCH_SIZE,WRITE_SIZE,copy_FETCH_SIZE,"
         "copy_WRITE_SIZE}",
         "# counters are mean KiB per dispatch over the run's dispatches of the kernel",
         f"gemm_FETCH_SIZE_KiB: {g_f:.1f}",
