@@ -281,12 +281,15 @@ __device__ __forceinline__ void compute_stage(const uint8_t* st, v4f (&acc)[8][4
 // cleared first.  On gfx950 the sparse instruction does not overlap VALU work,
 // and clearing the partials costs as much as the multiplies, so this form
 // needs about a third less VALU time per promoted unit.  The true sum is
-// acc * c_last.  Callers use it only when every scale product the wave meets
-// is a positive normal number within a factor 2^60 of the others (see
-// scales_tame), so the rescaled sums stay far inside the fp32 range.
+// acc * c_last.  clo / chi collect the smallest and largest bit pattern of the
+// scale products met; the result stands only if every product was a positive
+// normal number within a factor 2^60 of the others (checked by the caller
+// after the K loop), so that the rescaled sums stay far inside the fp32
+// range.
 template <bool PACKED>
 __device__ __forceinline__ void compute_stage_scaled(const uint8_t* st, v4f (&acc)[8][4], const LaneOffsets& o,
-                                                     int wn, int g, uint32_t msel, float (&cprev)[4]) {
+                                                     int wn, int g, uint32_t msel, float (&cprev)[4], uint32_t& clo,
+                                                     uint32_t& chi) {
   using L = Stage<true>;
   const float swv = lds_ld<float>(st, L::SW_OFF + wn * 512);
   float r[4];
@@ -295,6 +298,8 @@ __device__ __forceinline__ void compute_stage_scaled(const uint8_t* st, v4f (&ac
     const float c = lds_ld<float>(st, o.sx + j * 64) * swv;
     r[j] = cprev[j] * __builtin_amdgcn_rcpf(c);
     cprev[j] = c;
+    clo = min(clo, __float_as_uint(c));
+    chi = max(chi, __float_as_uint(c));
   }
   v8i bx[4];
 #pragma unroll
@@ -322,78 +327,6 @@ __device__ __forceinline__ void compute_stage_scaled(const uint8_t* st, v4f (&ac
     for (int j = 0; j < 4; ++j) acc[i][j] = mma_sparse_acc<false>(aa, bx[j], acc[i][j] * r[j], idx);
   }
 }
-
-#if SG_DEVICE_PASS
-// Whether every scale product c = sx[m, kb] * sw[n-block, kb] of the K blocks
-// kb = k0, k0 + 2, ... that a wave of the large-M kernels multiplies is a
-// positive normal fp32 number, all within a factor 2^60 of each other, for
-// the wave's X rows (lane l checks rows mw0 + l + 64 r, r < NR, clamped to
-// M - 1 as the stage loads are) and its W row block (row nw0, clamped to
-// N - 1).  Then the rescaled accumulator of the promotion stays below
-// 2^60 * 32 * 2^24 in magnitude and its terms above 2^-78: no overflow, no
-// subnormals.  issue() loads the scales of the first 16 K blocks, tame()
-// waits for them, reads any further K blocks (16 at a time) and returns the
-// wave-uniform answer; loads issued between the two (the first stage's)
-// travel with the scan's.
-template <int NR>
-struct ScaleScan {
-  static constexpr int CH = 16;
-  float xs[NR][CH], ws[CH];
-  const float* sxp[NR];
-  const float* swp;
-  int k0, KB;
-
-  __device__ __forceinline__ void load(const GemmArgs& a, int c0) {
-#pragma unroll
-    for (int t = 0; t < CH; ++t) {
-      const int kb = min(c0 + 2 * t, KB - 1 - ((KB - 1 - k0) & 1));   // past the end: the last block of this parity
-#pragma unroll
-      for (int r = 0; r < NR; ++r) xs[r][t] = sxp[r][kb * a.sx_sk];
-      ws[t] = swp[kb * a.sw_sk];
-    }
-    __builtin_amdgcn_sched_barrier(0);   // all loads of the batch before any use
-  }
-
-  __device__ __forceinline__ void issue(const GemmArgs& a, int64_t mw0, int64_t nw0, int k0_, int KB_, int l) {
-    k0 = k0_;
-    KB = KB_;
-#pragma unroll
-    for (int r = 0; r < NR; ++r) sxp[r] = a.sx + (min(mw0 + l + 64 * r, a.M - 1) >> a.gm_shift) * a.sx_sm;
-    swp = a.sw + (min(nw0, a.N - 1) >> a.gn_shift) * a.sw_sn;
-    load(a, k0);
-  }
-
-  __device__ __forceinline__ void reduce(int& emin, int& emax) const {
-#pragma unroll
-    for (int t = 0; t < CH; ++t)
-#pragma unroll
-      for (int r = 0; r < NR; ++r) {
-        const int e = __float_as_int(xs[r][t] * ws[t]) >> 23;   // biased exponent; negative for a negative product
-        emin = min(emin, e);
-        emax = max(emax, e);
-      }
-  }
-
-  __device__ __forceinline__ bool tame(const GemmArgs& a) {
-    __builtin_amdgcn_sched_barrier(0);   // nothing of the check moves above the loads issued since issue()
-    int emin = 255, emax = 0;
-    reduce(emin, emax);   // the first batch, outside the loop: its wait counts only the loads issued since
-    for (int c0 = k0 + 2 * CH; c0 < KB; c0 += 2 * CH) {
-      load(a, c0);
-      reduce(emin, emax);
-    }
-    const bool ok = emin >= 1 && emax <= 254 && emax - emin <= 60;
-    return __builtin_amdgcn_ballot_w64(!ok) == 0;
-  }
-};
-
-template <int NR>
-__device__ __forceinline__ bool scales_tame(const GemmArgs& a, int64_t mw0, int64_t nw0, int k0, int KB, int l) {
-  ScaleScan<NR> s;
-  s.issue(a, mw0, nw0, k0, KB, l);
-  return s.tame(a);
-}
-#endif  // SG_DEVICE_PASS
 
 // Scales constant along K: multiplies the wave's RI x 4 sub-tiles by
 // sx (X row of the lane's column) * sw (W rows 16 i + 4 g .. + 3), read from
@@ -576,6 +509,7 @@ __device__ __forceinline__ void x2_tile(const GemmArgs& a, int tn, int tm, uint8
   issue_double<PACKED>(db0, plan, rx, rw, rm, rsx, rsw, a, 0, KB, wave);
   // The K loop: group q multiplies K block 2 it + q of double stage it.
   // SCALED: the rescaled-accumulator promotion (compute_stage_scaled).
+  uint32_t clo = 0xffffffffu, chi = 0;
   auto kloop = [&](auto scaled_tag) {
     constexpr bool SCALED = decltype(scaled_tag)::value;
     float cprev[4] = {0.f, 0.f, 0.f, 0.f};   // scale product of the last K block multiplied (0: none yet)
@@ -590,7 +524,7 @@ __device__ __forceinline__ void x2_tile(const GemmArgs& a, int tn, int tm, uint8
             issue_double<PACKED>(u == 0 ? db1 : db0, plan, rx, rw, rm, rsx, rsw, a, 2 * (it + 1), KB, wave);
           if (2 * it + q < KB) {
             if constexpr (SCALED)
-              compute_stage_scaled<PACKED>((u == 0 ? db0 : db1) + qoff, acc, lo, wn, g, msel, cprev);
+              compute_stage_scaled<PACKED>((u == 0 ? db0 : db1) + qoff, acc, lo, wn, g, msel, cprev, clo, chi);
             else
               compute_stage<GRAN_N, PACKED, I8>((u == 0 ? db0 : db1) + qoff, acc, lo, wn, g, msel);
           }
@@ -605,11 +539,22 @@ __device__ __forceinline__ void x2_tile(const GemmArgs& a, int tn, int tm, uint8
     }
   };
   // FP8 codes with 128-row W scale blocks take the rescaled-accumulator
-  // promotion where the wave's scale products allow it (a wave-uniform
-  // choice), else the zero-and-FMA promotion.
+  // promotion; if any wave met a scale product that is not positive and
+  // normal, or products more than 2^60 apart, the whole tile is computed
+  // again with the zero-and-FMA promotion.  The last double stage issues no
+  // loads, so nothing is in flight when the K loop ends.
   if constexpr (GRAN_N == 128 && !I8) {
-    if (scales_tame<1>(a, m0 + wm * 64, n0 + wn * 128, q, KB, l)) kloop(std::true_type{});
-    else kloop(std::false_type{});
+    kloop(std::true_type{});
+    const bool ok = chi < clo ||   // no K block of this wave
+                    (clo >= 0x00800000u && chi <= 0x7f7fffffu && (chi >> 23) - (clo >> 23) <= 60u);
+    if (__syncthreads_or(!ok)) {   // (also: every wave is done with both double stages)
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+      issue_double<PACKED>(db0, plan, rx, rw, rm, rsx, rsw, a, 0, KB, wave);
+      kloop(std::false_type{});
+    }
   } else {
     kloop(std::false_type{});
   }
