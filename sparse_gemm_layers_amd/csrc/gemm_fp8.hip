@@ -1782,7 +1782,9 @@ template <int GRAN_N, bool OUT_BF16, bool OUT_T>
 __global__ void __launch_bounds__(512) k_gemm_grouped_tails(GemmArgs a, GroupTable gt, GroupTable gtail, int T,
                                                              int tail_gx) {
 #if SG_DEVICE_PASS
-  static_assert(DmaCfg<4, 4>::ARR <= x2::DBL, "the decode ring fits the tile's LDS arrays");
+  static_assert(DmaCfg<4, 1>::ARR <= x2::DBL && DmaCfg<4, 2>::ARR <= x2::DBL && DmaCfg<4, 3>::ARR <= x2::DBL &&
+                    DmaCfg<4, 4>::ARR <= x2::DBL,
+                "the decode rings fit the tile's LDS arrays");
   __shared__ __attribute__((aligned(1024))) uint8_t s0[x2::DBL];
   __shared__ __attribute__((aligned(1024))) uint8_t s1[x2::DBL];
   if ((int)blockIdx.x < T) {
@@ -1791,7 +1793,11 @@ __global__ void __launch_bounds__(512) k_gemm_grouped_tails(GemmArgs a, GroupTab
     const int d = (int)blockIdx.x - T;
     group_args<OUT_BF16, OUT_T>(a, gtail, d / tail_gx);
     if (a.M == 0) return;
-    decode_dma_body<false, 4, 4, 128, OUT_BF16, OUT_T>(a, s0, s1, d % tail_gx);
+    // as many 16-row sub-tiles as this group's tail needs (uniform per workgroup)
+    if (a.M <= 16) decode_dma_body<false, 4, 1, 128, OUT_BF16, OUT_T>(a, s0, s1, d % tail_gx);
+    else if (a.M <= 32) decode_dma_body<false, 4, 2, 128, OUT_BF16, OUT_T>(a, s0, s1, d % tail_gx);
+    else if (a.M <= 48) decode_dma_body<false, 4, 3, 128, OUT_BF16, OUT_T>(a, s0, s1, d % tail_gx);
+    else decode_dma_body<false, 4, 4, 128, OUT_BF16, OUT_T>(a, s0, s1, d % tail_gx);
   }
 #endif
 }

@@ -418,11 +418,13 @@ def test_grouped_decode_wide(sizes, form):
 
 
 # Ragged groups whose large tiles would need a second round over the CUs:
-# each group's last <= 64 rows take the grouped decode kernel instead (tails
-# of 44 / 40 rows: three sub-tiles; tails of 64 rows: four).
+# each group's last <= 64 rows take the grouped decode kernel instead, with
+# as many 16-row sub-tiles as the tail needs (1 row: one; 20 / 32 rows: two;
+# 44 / 40 rows: three; 64 rows: four).
 @pytest.mark.parametrize("sizes,form,out", [([300] * 6 + [40], "y", torch.bfloat16),
                                             ([320] * 7 + [64], "yt", torch.float32),
-                                            ([0, 300, 1, 300, 300, 300, 300, 300, 44], "y", torch.bfloat16)])
+                                            ([0, 300, 1, 300, 300, 300, 300, 300, 44], "y", torch.bfloat16),
+                                            ([276] * 6 + [20, 160], "yt", torch.bfloat16)])
 def test_grouped_tails_on_the_decode_kernel(sizes, form, out):
     n, k = 4096, 256
     say(f"grouped tails sizes={sizes} N={n} K={k} form={form} {out}")
