@@ -716,13 +716,18 @@ def trace_summary(out_file, title, command_lines, run_dir):
         "sum(d.end - d.start), s.arch_vgpr_count, s.accum_vgpr_count, s.group_segment_size "
         "from rocpd_kernel_dispatch d join rocpd_info_kernel_symbol s on d.kernel_id = s.id "
         "group by s.kernel_name order by sum(d.end - d.start) desc").fetchall()
+    durations = {}
+    for name, dur in cur.execute("select s.kernel_name, d.end - d.start from rocpd_kernel_dispatch d "
+                                 "join rocpd_info_kernel_symbol s on d.kernel_id = s.id"):
+        durations.setdefault(name, []).append(dur)
     lines = [f"# {title}", "# command (from the repository root on an MI355X):"]
     lines += ["#   " + c for c in command_lines]
     lines += ["# source: rocprofv3 --kernel-trace (rocpd database), durations in microseconds",
-              " calls    avg_us    min_us    max_us   total_us vgpr agpr  lds_B  kernel"]
+              " calls    avg_us median_us    min_us    max_us   total_us vgpr agpr  lds_B  kernel"]
     for name, n, avg, mn, mx, tot, vg, ag, lds in rows:
-        lines.append(f"{n:6d} {avg / 1e3:9.2f} {mn / 1e3:9.2f} {mx / 1e3:9.2f} {tot / 1e3:10.1f} {vg:4d} {ag:4d} "
-                     f"{lds:6d}  {_short(name)[:110]}")
+        med = float(np.median(durations[name]))
+        lines.append(f"{n:6d} {avg / 1e3:9.2f} {med / 1e3:9.2f} {mn / 1e3:9.2f} {mx / 1e3:9.2f} {tot / 1e3:10.1f} "
+                     f"{vg:4d} {ag:4d} {lds:6d}  {_short(name)[:110]}")
     open(out_file, "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
