@@ -1541,7 +1541,7 @@ __global__ void __launch_bounds__(512) k_gemm_decode(GemmArgs a) {
 // (measured at M = 37, N = 4096, K = 14336: 16.8 against 23.0 us).
 template <int RB, int MT>
 struct DmaCfg {
-  static constexpr bool XR = MT >= 2 && (RB == 4 || MT == 4);   // X fragments in registers
+  static constexpr bool XR = MT >= 2 && (RB >= 3 || MT == 4);   // X fragments in registers
   static constexpr int XOFF = RB * PK_CHUNK;                    // X slices (2 KB each) unless XR
   static constexpr int SXOFF = XOFF + (XR ? 0 : MT * 2048);     // X scales (256 B per sub-tile)
   static constexpr int SWOFF = SXOFF + MT * 256;                // W scales (256 B)
@@ -1664,16 +1664,16 @@ __device__ __forceinline__ void dec_reduce_store(const GemmArgs& a, const v4f (&
 }
 
 // r0, r1: two LDS arrays of at least DmaCfg<RB, MT>::ARR bytes (the ring's
-// slots); bx: the workgroup's block of RB row blocks.
+// slots); n0: the workgroup's first W row (a multiple of 16; it owns rows
+// n0 .. min(n0 + 16 RB, a.N) - 1).
 template <bool I8, int RB, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
-__device__ __forceinline__ void decode_dma_body(const GemmArgs& a, uint8_t* r0, uint8_t* r1, int bx) {
+__device__ __forceinline__ void decode_dma_body(const GemmArgs& a, uint8_t* r0, uint8_t* r1, int64_t n0) {
   using C = DmaCfg<RB, MT>;
   constexpr int KPS = C::KPS;
   static_assert(MT <= 4 && 2 * C::ARR <= 160 * 1024, "LDS");
   const int t = threadIdx.x, l = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int g = l >> 4, lr = l & 15;
-  const int64_t n0 = (int64_t)bx * 16 * RB;
   const int KB = (int)(a.K >> 7);
   const int nt = (KB - wave + DEC_WAVES - 1) / DEC_WAVES;    // K blocks of this wave
   const int ns = (nt + KPS - 1) / KPS;                         // slots of this wave
@@ -1771,13 +1771,23 @@ __device__ __forceinline__ void decode_dma_body(const GemmArgs& a, uint8_t* r0, 
 }
 #endif  // SG_DEVICE_PASS
 
+// G > 0: the workgroups share the R row blocks of 16 evenly (workgroup b owns
+// row blocks b R / G .. (b + 1) R / G - 1, at most RB of them), so that one
+// workgroup per CU covers a weight whose row blocks are not a multiple of
+// RB per CU; G = 0: workgroup b owns row blocks RB b .. RB b + RB - 1.
 template <bool I8, int RB, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
-__global__ void __launch_bounds__(512) k_gemm_decode_dma(GemmArgs a) {
+__global__ void __launch_bounds__(512) k_gemm_decode_dma(GemmArgs a, int64_t R, int G) {
 #if SG_DEVICE_PASS
   to_batch(a);
   __shared__ __attribute__((aligned(1024))) uint8_t r0[DmaCfg<RB, MT>::ARR];
   __shared__ __attribute__((aligned(1024))) uint8_t r1[DmaCfg<RB, MT>::ARR];
-  decode_dma_body<I8, RB, MT, GRAN_N, OUT_BF16, OUT_T>(a, r0, r1, blockIdx.x);
+  int64_t n0 = (int64_t)blockIdx.x * 16 * RB;
+  if (G > 0) {
+    const int64_t rb0 = (int64_t)blockIdx.x * R / G, rb1 = ((int64_t)blockIdx.x + 1) * R / G;
+    n0 = 16 * rb0;
+    a.N = min(a.N, 16 * rb1);   // the rows past this workgroup's are another's: not loaded, not stored
+  }
+  decode_dma_body<I8, RB, MT, GRAN_N, OUT_BF16, OUT_T>(a, r0, r1, n0);
 #endif
 }
 
@@ -1792,7 +1802,7 @@ __global__ void __launch_bounds__(512) k_gemm_decode_dma_grouped(GemmArgs a, Gro
   if (a.M == 0) return;
   __shared__ __attribute__((aligned(1024))) uint8_t r0[DmaCfg<RB, MT>::ARR];
   __shared__ __attribute__((aligned(1024))) uint8_t r1[DmaCfg<RB, MT>::ARR];
-  decode_dma_body<I8, RB, MT, GRAN_N, OUT_BF16, OUT_T>(a, r0, r1, blockIdx.x);
+  decode_dma_body<I8, RB, MT, GRAN_N, OUT_BF16, OUT_T>(a, r0, r1, (int64_t)blockIdx.x * 16 * RB);
 #endif
 }
 
@@ -1818,10 +1828,10 @@ __global__ void __launch_bounds__(512) k_gemm_grouped_tails(GemmArgs a, GroupTab
     group_args<OUT_BF16, OUT_T>(a, gtail, d / tail_gx);
     if (a.M == 0) return;
     // as many 16-row sub-tiles as this group's tail needs (uniform per workgroup)
-    if (a.M <= 16) decode_dma_body<false, 4, 1, 128, OUT_BF16, OUT_T>(a, s0, s1, d % tail_gx);
-    else if (a.M <= 32) decode_dma_body<false, 4, 2, 128, OUT_BF16, OUT_T>(a, s0, s1, d % tail_gx);
-    else if (a.M <= 48) decode_dma_body<false, 4, 3, 128, OUT_BF16, OUT_T>(a, s0, s1, d % tail_gx);
-    else decode_dma_body<false, 4, 4, 128, OUT_BF16, OUT_T>(a, s0, s1, d % tail_gx);
+    if (a.M <= 16) decode_dma_body<false, 4, 1, 128, OUT_BF16, OUT_T>(a, s0, s1, (int64_t)(d % tail_gx) * 64);
+    else if (a.M <= 32) decode_dma_body<false, 4, 2, 128, OUT_BF16, OUT_T>(a, s0, s1, (int64_t)(d % tail_gx) * 64);
+    else if (a.M <= 48) decode_dma_body<false, 4, 3, 128, OUT_BF16, OUT_T>(a, s0, s1, (int64_t)(d % tail_gx) * 64);
+    else decode_dma_body<false, 4, 4, 128, OUT_BF16, OUT_T>(a, s0, s1, (int64_t)(d % tail_gx) * 64);
   }
 #endif
 }
@@ -2069,7 +2079,7 @@ template <bool I8, int RB, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
 static bool try_decode_dma(const GemmArgs& a, hipStream_t st, int64_t rows16) {
   if constexpr (DmaCfg<RB, MT>::FITS) {
     if (RB == 1 || rows16 >= RB * 224) {
-      k_gemm_decode_dma<I8, RB, MT, GRAN_N, OUT_BF16, OUT_T><<<dec_grid(a, rows16, RB), 512, 0, st>>>(a);
+      k_gemm_decode_dma<I8, RB, MT, GRAN_N, OUT_BF16, OUT_T><<<dec_grid(a, rows16, RB), 512, 0, st>>>(a, 0, 0);
       return true;
     }
   }
@@ -2080,11 +2090,38 @@ static bool try_decode_dma(const GemmArgs& a, hipStream_t st, int64_t rows16) {
 // workgroups and whose operands fit (LDS ring of the streaming kernel, or
 // RB * MT <= 4 for the registers of k_gemm_decode).  Packed 2:4 weights with
 // 128-row W scales take the LDS-streaming kernel when one of its rings fits.
+// One problem with more row blocks than CUs but too few for 224 workgroups of
+// four: one workgroup per CU, each with ceil(R / CUs) or one fewer row blocks
+// (the LDS-streaming kernel's even split).  Measured at M = 16, K = 4096:
+// N = 12288 in 8.8 us against 10.2 us with 384 workgroups of two row blocks;
+// at N = 14336 the 4-row-block workgroups set the time either way (9.9 us),
+// so there the launcher keeps 224 workgroups of four.
+template <bool I8, int RB, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
+static bool try_decode_even(const GemmArgs& a, hipStream_t st, int64_t rows16, int cus) {
+  if constexpr (DmaCfg<RB, MT>::FITS) {
+    k_gemm_decode_dma<I8, RB, MT, GRAN_N, OUT_BF16, OUT_T><<<dim3((unsigned)cus, 1, 1), 512, 0, st>>>(a, rows16, cus);
+    return true;
+  }
+  return false;
+}
+
+template <bool I8, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
+static bool launch_decode_even(const GemmArgs& a, hipStream_t st, int64_t rows16) {
+  const int cus = cu_count();
+  if (a.L != 1 || rows16 <= cus || rows16 >= 4 * 224 || rows16 > 4LL * cus) return false;
+  switch (cdiv(rows16, cus)) {
+    case 2: return try_decode_even<I8, 2, MT, GRAN_N, OUT_BF16, OUT_T>(a, st, rows16, cus);
+    case 3: return try_decode_even<I8, 3, MT, GRAN_N, OUT_BF16, OUT_T>(a, st, rows16, cus);
+    default: return try_decode_even<I8, 4, MT, GRAN_N, OUT_BF16, OUT_T>(a, st, rows16, cus);
+  }
+}
+
 template <bool SPARSE, bool I8, bool PACKED, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
 static void launch_decode_mt(const GemmArgs& a, hipStream_t st) {
   const int64_t rows16 = cdiv(a.N, 16);
   if constexpr (SPARSE && PACKED && GRAN_N == 128) {
-    if (try_decode_dma<I8, 4, MT, GRAN_N, OUT_BF16, OUT_T>(a, st, rows16) ||
+    if (launch_decode_even<I8, MT, GRAN_N, OUT_BF16, OUT_T>(a, st, rows16) ||
+        try_decode_dma<I8, 4, MT, GRAN_N, OUT_BF16, OUT_T>(a, st, rows16) ||
         try_decode_dma<I8, 2, MT, GRAN_N, OUT_BF16, OUT_T>(a, st, rows16) ||
         try_decode_dma<I8, 1, MT, GRAN_N, OUT_BF16, OUT_T>(a, st, rows16))
       return;

@@ -102,6 +102,15 @@ def test_decode_shapes(m, n, k):
     check(True, m, n, k, seed=4, forms=("y", "yt"))
 
 
+# Packed decode with more 16-row blocks than CUs but too few for 224
+# workgroups of four (on a 256-CU device): one workgroup per CU, each with an
+# even share of 2, 3 or 4 row blocks (320, 688, 768 and 813 row blocks here;
+# N = 13000 also ends in a partial row block).
+@pytest.mark.parametrize("m,n,k", [(16, 5120, 1024), (20, 11008, 512), (37, 12288, 512), (64, 13000, 256)])
+def test_packed_decode_even_row_split(m, n, k):
+    check(True, m, n, k, seed=5 + m, forms=("y", "yt"), packed=True)
+
+
 def test_deterministic_and_all_zero_operands():
     d = workloads.sparse_large(seed=8, m=300, n=512, k=512)
     xq, sx, wq, meta, sw = oracle_operands(d["x"], d["w"], 1, 128, True)
