@@ -1771,21 +1771,26 @@ __device__ __forceinline__ void decode_dma_body(const GemmArgs& a, uint8_t* r0, 
 }
 #endif  // SG_DEVICE_PASS
 
-// G > 0: the workgroups share the R row blocks of 16 evenly (workgroup b owns
-// row blocks b R / G .. (b + 1) R / G - 1, at most RB of them), so that one
-// workgroup per CU covers a weight whose row blocks are not a multiple of
-// RB per CU; G = 0: workgroup b owns row blocks RB b .. RB b + RB - 1.
-template <bool I8, int RB, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
-__global__ void __launch_bounds__(512) k_gemm_decode_dma(GemmArgs a, int64_t R, int G) {
+// EVEN: the G workgroups share the R row blocks of 16 evenly, q = R / G and
+// r = R % G: workgroup b owns the q + (b < r) row blocks from b q + min(b, r)
+// on (at most RB), so that one workgroup per CU covers a weight whose row
+// blocks are not a multiple of RB per CU; otherwise workgroup b owns row
+// blocks RB b .. RB b + RB - 1 (q and r unused).  The quotient and remainder
+// come from the host: a division here would be expanded into vector
+// instructions, and the buffer descriptors computed from its result would
+// then be vector values that cost a readfirstlane loop around every load.
+template <bool I8, int RB, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T, bool EVEN>
+__global__ void __launch_bounds__(512) k_gemm_decode_dma(GemmArgs a, int q, int r) {
 #if SG_DEVICE_PASS
   to_batch(a);
   __shared__ __attribute__((aligned(1024))) uint8_t r0[DmaCfg<RB, MT>::ARR];
   __shared__ __attribute__((aligned(1024))) uint8_t r1[DmaCfg<RB, MT>::ARR];
   int64_t n0 = (int64_t)blockIdx.x * 16 * RB;
-  if (G > 0) {
-    const int64_t rb0 = (int64_t)blockIdx.x * R / G, rb1 = ((int64_t)blockIdx.x + 1) * R / G;
-    n0 = 16 * rb0;
-    a.N = min(a.N, 16 * rb1);   // the rows past this workgroup's are another's: not loaded, not stored
+  if constexpr (EVEN) {
+    const int b = (int)blockIdx.x;
+    const int rb0 = b * q + min(b, r), rb1 = rb0 + q + (b < r ? 1 : 0);
+    n0 = 16 * (int64_t)rb0;
+    a.N = min(a.N, 16 * (int64_t)rb1);   // the rows past this workgroup's are another's: not loaded, not stored
   }
   decode_dma_body<I8, RB, MT, GRAN_N, OUT_BF16, OUT_T>(a, r0, r1, n0);
 #endif
@@ -2079,7 +2084,7 @@ template <bool I8, int RB, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
 static bool try_decode_dma(const GemmArgs& a, hipStream_t st, int64_t rows16) {
   if constexpr (DmaCfg<RB, MT>::FITS) {
     if (RB == 1 || rows16 >= RB * 224) {
-      k_gemm_decode_dma<I8, RB, MT, GRAN_N, OUT_BF16, OUT_T><<<dec_grid(a, rows16, RB), 512, 0, st>>>(a, 0, 0);
+      k_gemm_decode_dma<I8, RB, MT, GRAN_N, OUT_BF16, OUT_T, false><<<dec_grid(a, rows16, RB), 512, 0, st>>>(a, 0, 0);
       return true;
     }
   }
@@ -2099,7 +2104,8 @@ static bool try_decode_dma(const GemmArgs& a, hipStream_t st, int64_t rows16) {
 template <bool I8, int RB, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
 static bool try_decode_even(const GemmArgs& a, hipStream_t st, int64_t rows16, int cus) {
   if constexpr (DmaCfg<RB, MT>::FITS) {
-    k_gemm_decode_dma<I8, RB, MT, GRAN_N, OUT_BF16, OUT_T><<<dim3((unsigned)cus, 1, 1), 512, 0, st>>>(a, rows16, cus);
+    k_gemm_decode_dma<I8, RB, MT, GRAN_N, OUT_BF16, OUT_T, true><<<dim3((unsigned)cus, 1, 1), 512, 0, st>>>(
+        a, (int)(rows16 / cus), (int)(rows16 % cus));
     return true;
   }
   return false;

@@ -336,8 +336,13 @@ __device__ __forceinline__ void w8_dma_issue(uint8_t* sl, const W8Args& a, __amd
 }
 #endif  // SG_DEVICE_PASS
 
-template <int CODES, int RB, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
-__global__ void __launch_bounds__(512) k_gemm_w8a16_dma(W8Args a) {
+// EVEN: the G workgroups share the R row blocks of 16 evenly, q = R / G and
+// r = R % G: workgroup b owns the q + (b < r) row blocks from b q + min(b, r)
+// on (at most RB); otherwise workgroup b owns row blocks RB b .. RB b + RB - 1
+// (q and r unused).  q and r come from the host, so that no division here
+// turns the buffer descriptors into vector values.
+template <int CODES, int RB, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T, bool EVEN>
+__global__ void __launch_bounds__(512) k_gemm_w8a16_dma(W8Args a, int q, int r) {
 #if SG_DEVICE_PASS
   using D = W8Dma<CODES, RB, MT>;
   static_assert(D::FITS && 4 * RB * 64 * 16 <= D::ARR, "LDS");
@@ -347,7 +352,13 @@ __global__ void __launch_bounds__(512) k_gemm_w8a16_dma(W8Args a) {
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int g = l >> 4, lr = l & 15;
   const int KB = (int)(a.K >> 7);
-  const int64_t n0 = (int64_t)blockIdx.x * (16 * RB);
+  int64_t n0 = (int64_t)blockIdx.x * (16 * RB);
+  if constexpr (EVEN) {
+    const int b = (int)blockIdx.x;
+    const int rb0 = b * q + min(b, r), rb1 = rb0 + q + (b < r ? 1 : 0);
+    n0 = 16 * (int64_t)rb0;
+    a.N = min(a.N, 16 * (int64_t)rb1);   // the rows past this workgroup's are another's: not loaded, not stored
+  }
   const int64_t wrows = min((int64_t)(16 * RB), a.N - n0);
   const __amdgpu_buffer_rsrc_t rw = w8_rsrc(a.w + n0 * a.ldw, (uint32_t)(wrows * a.ldw));
   const __amdgpu_buffer_rsrc_t rm = w8_rsrc(a.meta + n0 * a.ldm, (uint32_t)(wrows * a.ldm));
@@ -475,11 +486,35 @@ template <int CODES, int RB, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
 static bool try_w8_dma(const W8Args& a, hipStream_t st, int64_t rows16) {
   if constexpr (W8Dma<CODES, RB, MT>::FITS) {
     if (RB == 1 || rows16 >= RB * 224) {
-      k_gemm_w8a16_dma<CODES, RB, MT, GRAN_N, OUT_BF16, OUT_T><<<(unsigned)cdiv(rows16, RB), 512, 0, st>>>(a);
+      k_gemm_w8a16_dma<CODES, RB, MT, GRAN_N, OUT_BF16, OUT_T, false><<<(unsigned)cdiv(rows16, RB), 512, 0, st>>>(a, 0, 0);
       return true;
     }
   }
   return false;
+}
+
+// More 16-row blocks than CUs but too few for 224 workgroups of four: one
+// workgroup per CU with an even share of ceil(R / CUs) or one fewer row
+// blocks (as the FP8 decode kernel).
+template <int CODES, int RB, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
+static bool try_w8_even_rb(const W8Args& a, hipStream_t st, int64_t rows16, int cus) {
+  if constexpr (W8Dma<CODES, RB, MT>::FITS) {
+    k_gemm_w8a16_dma<CODES, RB, MT, GRAN_N, OUT_BF16, OUT_T, true><<<(unsigned)cus, 512, 0, st>>>(a, (int)(rows16 / cus),
+                                                                                      (int)(rows16 % cus));
+    return true;
+  }
+  return false;
+}
+
+template <int CODES, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
+static bool try_w8_even(const W8Args& a, hipStream_t st, int64_t rows16) {
+  const int cus = cu_count();
+  if (rows16 <= cus || rows16 >= 4 * 224 || rows16 > 4LL * cus) return false;
+  switch (cdiv(rows16, cus)) {
+    case 2: return try_w8_even_rb<CODES, 2, MT, GRAN_N, OUT_BF16, OUT_T>(a, st, rows16, cus);
+    case 3: return try_w8_even_rb<CODES, 3, MT, GRAN_N, OUT_BF16, OUT_T>(a, st, rows16, cus);
+    default: return try_w8_even_rb<CODES, 4, MT, GRAN_N, OUT_BF16, OUT_T>(a, st, rows16, cus);
+  }
 }
 
 // --------------------------------------------------------------- large M
@@ -677,8 +712,9 @@ static bool try_w8_tile(const W8Args& a, hipStream_t st) {
   return true;
 }
 
-// Row blocks per workgroup: the largest of 4 (2 for MT > 2), 2, 1 that keeps
-// at least 224 workgroups.  Every workgroup reads its X rows in full, so
+// Row blocks per workgroup: with more 16-row blocks than CUs but under 896, an
+// even share over one workgroup per CU; otherwise the largest of 4 (2 for
+// MT > 2), 2, 1 that keeps at least 224 workgroups.  Every workgroup reads its X rows in full, so
 // fewer, taller workgroups read X fewer times (measured at M = 37 and 64:
 // 1.7x faster than one row block per workgroup).
 template <int CODES, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
@@ -686,7 +722,8 @@ static void launch_w8_mt(const W8Args& a, hipStream_t st) {
   const int64_t rows16 = cdiv(a.N, 16);
   const unsigned gy = (unsigned)cdiv(a.M, 16 * MT);
   if constexpr (MT <= 3) {   // LDS streaming, one workgroup per RB row blocks and all of M
-    if (try_w8_dma<CODES, 4, MT, GRAN_N, OUT_BF16, OUT_T>(a, st, rows16) ||
+    if (try_w8_even<CODES, MT, GRAN_N, OUT_BF16, OUT_T>(a, st, rows16) ||
+        try_w8_dma<CODES, 4, MT, GRAN_N, OUT_BF16, OUT_T>(a, st, rows16) ||
         try_w8_dma<CODES, 2, MT, GRAN_N, OUT_BF16, OUT_T>(a, st, rows16) ||
         try_w8_dma<CODES, 1, MT, GRAN_N, OUT_BF16, OUT_T>(a, st, rows16))
       return;

@@ -84,6 +84,20 @@ def test_w8a16_two_row_blocks_ragged_last():
     check(32, 7208, 512, out=torch.float32, bias=True, seed=25)
 
 
+# More 16-row blocks than CUs but under 896: one workgroup per CU with an even
+# share of two, three or four row blocks (the share's first row not a multiple
+# of the share's size), for one, two and three 16-row sub-tiles of X.
+EVEN_SPLIT = [(16, 5120, 1024, 128), (20, 11008, 512, 128), (37, 12288, 512, 128), (48, 13000, 256, 128),
+              (33, 11000, 256, 1)]
+
+
+@pytest.mark.parametrize("int8", [False, True])
+@pytest.mark.parametrize("m,n,k,gn", EVEN_SPLIT)
+def test_w8a16_decode_even_row_split(m, n, k, gn, int8):
+    check(m, n, k, gn=gn, int8=int8, out=torch.float32 if gn == 1 else torch.bfloat16, bias=gn == 1,
+          seed=m + n + int8)
+
+
 # Large M: the 256 x 128 tile kernel (taken from 192 tiles on), with the last
 # tiles partly past M and N.
 @pytest.mark.parametrize("int8", [False, True])
@@ -187,6 +201,11 @@ def test_w4a16_decode_full_size():
 
 def test_w4a16_decode_m37_full_size():
     check_w4(37, 14336, 4096, forms=("y",), seed=43)
+
+
+@pytest.mark.parametrize("m,n,k", [(16, 5120, 512), (37, 11008, 256)])
+def test_w4a16_decode_even_row_split(m, n, k):
+    check_w4(m, n, k, seed=44 + m)
 
 
 def test_w4a16_large_m_tiles():
