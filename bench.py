@@ -352,6 +352,14 @@ def rows_report():
             b = dn * dk // 2 + dn * dk // 8 + 4 * (dn // 128) * (dk // 128) + dm * dk * 2 + dm * dn * 2
             out[f"next_w8a16_{codes}_decode_M{dm}_N{dn}_K{dk}_y"] = {"ms": ms, "GB/s": b / ms / 1e6,
                                                                    "frac_hbm": b / ms / 1e6 / PEAK_HBM_GBS}
+            # the same weights in the gfx950 packed form (same bytes, same results)
+            psets = [sg.sparse24_pack_gfx950(q, mt) for q, mt, _ in wsets]
+            ms = time_fn(lambda i: sg.w8a16_sparse24_gemm_groupwise_packed(
+                xb, psets[i % ROTATE_DECODE], dn, wsets[i % ROTATE_DECODE][2], 128, int8=codes == "int8", y=y),
+                reps=64, warm=16)
+            out[f"next_w8a16_{codes}_packed_decode_M{dm}_N{dn}_K{dk}_y"] = {"ms": ms, "GB/s": b / ms / 1e6,
+                                                                          "frac_hbm": b / ms / 1e6 / PEAK_HBM_GBS}
+            del psets
         del wsets
     wsets = []
     for i in range(ROTATE_DECODE):
@@ -378,6 +386,11 @@ def rows_report():
     ms = time_fn(lambda i: sg.w8a16_sparse24_gemm_groupwise(xb, wq8, mt8, sw8, 128, y=y), reps=10, warm=2)
     out["next_w8a16_e4m3_gemm_2048x4096x4096_y"] = {"ms": ms, "TFLOP/s": flops / ms / 1e9,
                                                     "frac_bf16_peak": flops / ms / 1e9 / PEAK_BF16_TFLOPS}
+    wp8 = sg.sparse24_pack_gfx950(wq8, mt8)
+    ms = time_fn(lambda i: sg.w8a16_sparse24_gemm_groupwise_packed(xb, wp8, n, sw8, 128, y=y), reps=10, warm=2)
+    out["next_w8a16_e4m3_packed_gemm_2048x4096x4096_y"] = {"ms": ms, "TFLOP/s": flops / ms / 1e9,
+                                                           "frac_bf16_peak": flops / ms / 1e9 / PEAK_BF16_TFLOPS}
+    del wp8
     wq8, sw8 = sg.int8_quant_groupwise(wv8, gr=128, gc=64)
     ms = time_fn(lambda i: sg.w8a16_sparse24_gemm_groupwise(xb, wq8, mt8, sw8, 128, y=y), reps=10, warm=2)
     out["next_w8a16_int8_gemm_2048x4096x4096_y"] = {"ms": ms, "TFLOP/s": flops / ms / 1e9,

@@ -410,6 +410,27 @@ sg_status sg_w8a16_sparse24_gemm_groupwise(int64_t M, int64_t N, int64_t K, cons
                                            hipStream_t stream);
 
 /*
+ * sg_w8a16_sparse24_gemm_groupwise_packed -- sg_w8a16_sparse24_gemm_groupwise
+ * with the weight in the packed form of sg_sparse24_pack_gfx950 (a byte
+ * permutation, so it packs int8 codes as it packs e4m3 ones).  The same
+ * arithmetic in the same order: results equal the unpacked call's bit for
+ * bit.  The packed chunks reach LDS as contiguous 1 KB and 256 B pieces per
+ * wave instruction, where the row-major codes and metadata take 64-byte and
+ * 16-byte pieces of 16 rows.  [T3258] jcaip's review; [I2029] klevzoff (the
+ * hardware's layout straight into the mainloop).
+ *   wpacked : sg_sparse24_packed_bytes(N, K) bytes, 16-byte aligned; w_dt =
+ *             SG_E4M3 or SG_I8, the code type that was packed.
+ *   other arguments as sg_w8a16_sparse24_gemm_groupwise.
+ * Requires K % 128 == 0, ldx >= K, ldx < 2^24, (K / 128) * 16 * 1280 < 2^31,
+ * ceil(M/16) <= 65535; x 16-byte aligned, ldx * 2 a multiple of 16.
+ */
+sg_status sg_w8a16_sparse24_gemm_groupwise_packed(int64_t M, int64_t N, int64_t K, const uint16_t* x, int64_t ldx,
+                                                  const uint8_t* wpacked, sg_dtype w_dt, const float* sw,
+                                                  int64_t sw_sn, int64_t sw_sk, int gran_n, const float* bias,
+                                                  void* y, sg_dtype y_dt, int64_t ldy, sg_form form,
+                                                  hipStream_t stream);
+
+/*
  * sg_w4a16_sparse24_gemm_groupwise -- the same with int4 weight codes: the
  * 2:4-compressed values quantised by sg_int4_quant_groupwise with gc = 64 (one
  * scale per row and 128-wide K block), two per byte.

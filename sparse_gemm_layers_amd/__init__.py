@@ -33,6 +33,7 @@ from ._binding import (
     fp8_sparse24_gemm_groupwise_packed_batched,
     fp8_sparse24_gemm_groupwise_packed_grouped,
     w8a16_sparse24_gemm_groupwise,
+    w8a16_sparse24_gemm_groupwise_packed,
     w4a16_sparse24_gemm_groupwise,
 )
 
@@ -45,5 +46,5 @@ __all__ = [
     "int8_sparse24_gemm_groupwise_packed", "probe_matrix_ops", "probe_matrix_rate", "probe_stream_read", "k_constant_scales",
     "fp8_gemm_groupwise_batched", "fp8_sparse24_gemm_groupwise_batched",
     "fp8_sparse24_gemm_groupwise_packed_batched", "fp8_sparse24_gemm_groupwise_packed_grouped",
-    "w8a16_sparse24_gemm_groupwise", "w4a16_sparse24_gemm_groupwise",
+    "w8a16_sparse24_gemm_groupwise", "w8a16_sparse24_gemm_groupwise_packed", "w4a16_sparse24_gemm_groupwise",
 ]

@@ -60,6 +60,8 @@ _SIGS = {
                                                        _i64, _int, _ptr], _int),
     "sg_w8a16_sparse24_gemm_groupwise": ([_i64, _i64, _i64, _ptr, _i64, _ptr, _i64, _ptr, _i64, _int, _ptr, _i64,
                                           _i64, _int, _ptr, _ptr, _int, _i64, _int, _ptr], _int),
+    "sg_w8a16_sparse24_gemm_groupwise_packed": ([_i64, _i64, _i64, _ptr, _i64, _ptr, _int, _ptr, _i64, _i64, _int,
+                                                 _ptr, _ptr, _int, _i64, _int, _ptr], _int),
     "sg_w4a16_sparse24_gemm_groupwise": ([_i64, _i64, _i64, _ptr, _i64, _ptr, _i64, _ptr, _i64, _ptr, _i64, _i64,
                                           _ptr, _ptr, _int, _i64, _int, _ptr], _int),
     "sg_probe_matrix_ops": ([_int, _int], _i64),
@@ -514,6 +516,33 @@ def w8a16_sparse24_gemm_groupwise(x, wv, wmeta, sw, gran_n: int = 128, out_dtype
                                                 _row_stride(wmeta), wdt, _p(sw), sw.stride(0), sw.stride(1), gran_n,
                                                 bp, _p(y), ydt, _row_stride(y), f, _stream(x))
     _check(st, "sg_w8a16_sparse24_gemm_groupwise")
+    return y
+
+
+def w8a16_sparse24_gemm_groupwise_packed(x, wpacked, n: int, sw, gran_n: int = 128, int8: bool = False,
+                                         out_dtype=torch.bfloat16, form: str = "y", y=None, bias=None):
+    """The weight-only 2:4 GEMM with the weight in the gfx950 packed form
+    (sparse24_pack_gfx950 of the [N, K/2] codes and [N, K/8] metadata): x
+    bfloat16 [M, K]; wpacked uint8 [bytes]; int8 names the packed code type
+    (e4m3 otherwise).  Equals w8a16_sparse24_gemm_groupwise on the unpacked
+    weight bit for bit."""
+    _gpu2d(x, "x")
+    if x.dtype != torch.bfloat16:
+        raise SgError("x must be bfloat16")
+    M, K = x.shape
+    _positive(M=M, N=n, K=K)
+    if K % 128 or gran_n not in (1, 128):
+        raise SgError("K must be a multiple of 128 and gran_n 1 or 128")
+    _want(x, "x", (torch.bfloat16,), (M, K), x.device)
+    _want_packed(wpacked, n, K, x.device)
+    _want_scales(sw, "sw", -(-n // gran_n), K // 128, x.device)
+    y, f, ydt = _out(y, M, n, out_dtype, form, x.device)
+    bp, _ = _bias(bias, n)
+    st = lib().sg_w8a16_sparse24_gemm_groupwise_packed(M, n, K, _p(x), _row_stride(x), _p(wpacked),
+                                                       SG_I8 if int8 else SG_E4M3, _p(sw), sw.stride(0),
+                                                       sw.stride(1), gran_n, bp, _p(y), ydt, _row_stride(y), f,
+                                                       _stream(x))
+    _check(st, "sg_w8a16_sparse24_gemm_groupwise_packed")
     return y
 
 

@@ -111,6 +111,26 @@ __device__ __forceinline__ v4i widen8(int w0, int w1) {
   }
 }
 
+// Packed gfx950 weight (the FP8 kernels' layout: one 1280-byte chunk per 16
+// rows and 128-wide K block, each row's 64 code bytes as 16-byte lane-group
+// pieces and its 16 metadata bytes as lane-group index words).  The 8 code
+// bytes that lane group g of K slice h multiplies here (row bytes
+// 32 h + 8 g .. + 7) are half g >> 1 of the FP8 lane group 2 (g & 1) + h's
+// piece, and their 16-bit index word (metadata bytes 8 h + 2 g, + 1) is half
+// g >> 1 of that lane group's index word.  Offsets inside a chunk, local row r:
+__device__ __forceinline__ int w8pk_code_off(int r, int g, int h) {
+  return pk_val_off(r, 2 * (g & 1) + h) + 8 * (g >> 1);
+}
+__device__ __forceinline__ int w8pk_meta_off(int r, int g, int h) {
+  return PK_META + pk_meta_word(r, 2 * (g & 1) + h) + 2 * (g >> 1);
+}
+// The same index word from local row r's 16 packed metadata bytes m.
+__device__ __forceinline__ int w8pk_meta_half(const v4i& m, int r, int g, int h) {
+  const int q = (pk_meta_word(r, 2 * (g & 1) + h) - 16 * r) >> 2;
+  const uint32_t d = (uint32_t)(q == 0 ? m[0] : q == 1 ? m[1] : q == 2 ? m[2] : m[3]);
+  return (int)((d >> (16 * (g >> 1))) & 0xffffu);
+}
+
 template <int RB, int MT>
 struct W8Ops {
   v4i cw[RB];       // code bytes of W row n0 + 16 rb + lr: 8 for K slice 0, 8 for slice 1
@@ -119,14 +139,22 @@ struct W8Ops {
   float sw4[RB][4];
 };
 
-template <int CODES, int RB, int MT, int GRAN_N>
+// PK: rw covers the workgroup's packed chunks (row block rb's chunk of K
+// block kb at (rb KB + kb) 1280); rm is unused.
+template <int CODES, int RB, int MT, int GRAN_N, bool PK>
 __device__ __forceinline__ void w8_load(const W8Args& a, __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t rm,
                                         __amdgpu_buffer_rsrc_t rx, int64_t n0, int kb, int lr, int g,
                                         W8Ops<RB, MT>& o) {
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const uint32_t r = (uint32_t)(16 * rb + lr);
-    if constexpr (CODES == C_I4) {   // 32 bytes per row and K block: 4 per lane and K slice
+    if constexpr (PK) {
+      const uint32_t c = (uint32_t)(rb * (int)(a.K >> 7) * PK_CHUNK);
+      const v2i c0 = w8_ld8(rw, c + w8pk_code_off(lr, g, 0), kb * PK_CHUNK);
+      const v2i c1 = w8_ld8(rw, c + w8pk_code_off(lr, g, 1), kb * PK_CHUNK);
+      o.cw[rb] = (v4i){c0[0], c0[1], c1[0], c1[1]};
+      o.mw[rb] = w8_ld16(rw, c + PK_META + 16 * lr, kb * PK_CHUNK);
+    } else if constexpr (CODES == C_I4) {   // 32 bytes per row and K block: 4 per lane and K slice
       const int c0 = w8_ld4(rw, r * (uint32_t)a.ldw + 4 * g, kb * 32);
       const int c1 = w8_ld4(rw, r * (uint32_t)a.ldw + 16 + 4 * g, kb * 32);
       o.cw[rb] = (v4i){c0, 0, c1, 0};
@@ -135,7 +163,7 @@ __device__ __forceinline__ void w8_load(const W8Args& a, __amdgpu_buffer_rsrc_t 
       const v2i c1 = w8_ld8(rw, r * (uint32_t)a.ldw + 32 + 8 * g, kb * 64);
       o.cw[rb] = (v4i){c0[0], c0[1], c1[0], c1[1]};
     }
-    o.mw[rb] = w8_ld16(rm, r * (uint32_t)a.ldm, kb * 16);
+    if constexpr (!PK) o.mw[rb] = w8_ld16(rm, r * (uint32_t)a.ldm, kb * 16);
     const int64_t nb = n0 + 16 * rb;   // rows past N read the last row's scale (never stored)
     if (GRAN_N == 128) {
       const float v = a.sw[(min(nb, a.N - 1) >> 7) * a.sw_sn + kb * a.sw_sk];
@@ -159,13 +187,14 @@ __device__ __forceinline__ int meta_half(const v4i& m, int hw) {
   return (int)((d >> (16 * (hw & 1))) & 0xffffu);
 }
 
-template <int CODES, int RB, int MT>
-__device__ __forceinline__ void w8_compute(const W8Ops<RB, MT>& o, int g, v4f (&acc)[RB][MT]) {
+template <int CODES, int RB, int MT, bool PK>
+__device__ __forceinline__ void w8_compute(const W8Ops<RB, MT>& o, int g, int lr, v4f (&acc)[RB][MT]) {
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const v4i a0 = widen8<CODES>(o.cw[rb][0], o.cw[rb][1]);
     const v4i a1 = widen8<CODES>(o.cw[rb][2], o.cw[rb][3]);
-    const int i0 = meta_half(o.mw[rb], g), i1 = meta_half(o.mw[rb], g + 4);
+    const int i0 = PK ? w8pk_meta_half(o.mw[rb], lr, g, 0) : meta_half(o.mw[rb], g);
+    const int i1 = PK ? w8pk_meta_half(o.mw[rb], lr, g, 1) : meta_half(o.mw[rb], g + 4);
 #pragma unroll
     for (int j = 0; j < MT; ++j) {
       const v8i b0 = {o.bx[j][0][0], o.bx[j][0][1], o.bx[j][0][2], o.bx[j][0][3],
@@ -184,7 +213,7 @@ __device__ __forceinline__ void w8_compute(const W8Ops<RB, MT>& o, int g, v4f (&
 }
 #endif  // SG_DEVICE_PASS
 
-template <int CODES, int RB, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
+template <int CODES, int RB, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T, bool PK>
 __global__ void __launch_bounds__(512) k_gemm_w8a16(W8Args a) {
 #if SG_DEVICE_PASS
   constexpr int U = W8_U;
@@ -196,8 +225,11 @@ __global__ void __launch_bounds__(512) k_gemm_w8a16(W8Args a) {
   const int64_t n0 = (int64_t)blockIdx.x * (16 * RB);
   const int64_t m0 = (int64_t)blockIdx.y * (16 * MT);
   const int64_t wrows = min((int64_t)(16 * RB), a.N - n0), xrows = min((int64_t)(16 * MT), a.M - m0);
-  // rows past N or M read as zero
-  const __amdgpu_buffer_rsrc_t rw = w8_rsrc(a.w + n0 * a.ldw, (uint32_t)(wrows * a.ldw));
+  // rows past N or M read as zero (packed: the packer's zero rows)
+  const __amdgpu_buffer_rsrc_t rw =
+      PK ? w8_rsrc(a.w + (n0 / PK_ROWS) * KB * PK_CHUNK,
+                   (uint32_t)(((wrows + PK_ROWS - 1) / PK_ROWS) * KB * PK_CHUNK))
+         : w8_rsrc(a.w + n0 * a.ldw, (uint32_t)(wrows * a.ldw));
   const __amdgpu_buffer_rsrc_t rm = w8_rsrc(a.meta + n0 * a.ldm, (uint32_t)(wrows * a.ldm));
   const __amdgpu_buffer_rsrc_t rx = w8_rsrc(a.x + m0 * a.ldx, (uint32_t)(xrows * a.ldx * 2));
 
@@ -213,10 +245,10 @@ __global__ void __launch_bounds__(512) k_gemm_w8a16(W8Args a) {
   for (int t0 = 0; t0 < nt; t0 += U) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      w8_load<CODES, RB, MT, GRAN_N>(a, rw, rm, rx, n0, wave + W8_WAVES * min(t0 + u, nt - 1), lr, g, ops[u]);
+      w8_load<CODES, RB, MT, GRAN_N, PK>(a, rw, rm, rx, n0, wave + W8_WAVES * min(t0 + u, nt - 1), lr, g, ops[u]);
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      if (t0 + u < nt) w8_compute<CODES, RB, MT>(ops[u], g, acc);
+      if (t0 + u < nt) w8_compute<CODES, RB, MT, PK>(ops[u], g, lr, acc);
   }
 
 #pragma unroll
@@ -284,7 +316,7 @@ struct W8X {
   v4i c[MT][4];
 };
 
-template <int CODES, int RB, int MT, int GRAN_N>
+template <int CODES, int RB, int MT, int GRAN_N, bool PK>
 __device__ __forceinline__ void w8_dma_issue(uint8_t* sl, const W8Args& a, __amdgpu_buffer_rsrc_t rw,
                                              __amdgpu_buffer_rsrc_t rm, __amdgpu_buffer_rsrc_t rx,
                                              __amdgpu_buffer_rsrc_t rsw, int64_t n0, int kb, int l, bool valid,
@@ -301,6 +333,14 @@ __device__ __forceinline__ void w8_dma_issue(uint8_t* sl, const W8Args& a, __amd
   }
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
+    if constexpr (PK) {   // the chunk as stored: codes, then metadata
+      const uint32_t c = (uint32_t)(rb * (int)(a.K >> 7) * PK_CHUNK);
+      const int cs = valid ? kb * PK_CHUNK : 0;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (w8_lds_t*)(sl + rb * D::CB), 16, c + 16 * l, cs, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (w8_lds_t*)(sl + D::MOFF + rb * 256), 4, c + PK_META + 4 * l, cs,
+                                               0, 0);
+      continue;
+    }
     if constexpr (CODES == C_I4) {
 #pragma unroll
       for (int e = 0; e < 2; ++e)
@@ -341,7 +381,9 @@ __device__ __forceinline__ void w8_dma_issue(uint8_t* sl, const W8Args& a, __amd
 // on (at most RB); otherwise workgroup b owns row blocks RB b .. RB b + RB - 1
 // (q and r unused).  q and r come from the host, so that no division here
 // turns the buffer descriptors into vector values.
-template <int CODES, int RB, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T, bool EVEN>
+// PK: the weight in the packed gfx950 form, each chunk copied into the ring
+// as stored (codes at rb * CB, metadata at MOFF + rb * 256).
+template <int CODES, int RB, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T, bool EVEN, bool PK>
 __global__ void __launch_bounds__(512) k_gemm_w8a16_dma(W8Args a, int q, int r) {
 #if SG_DEVICE_PASS
   using D = W8Dma<CODES, RB, MT>;
@@ -360,7 +402,10 @@ __global__ void __launch_bounds__(512) k_gemm_w8a16_dma(W8Args a, int q, int r) 
     a.N = min(a.N, 16 * (int64_t)rb1);   // the rows past this workgroup's are another's: not loaded, not stored
   }
   const int64_t wrows = min((int64_t)(16 * RB), a.N - n0);
-  const __amdgpu_buffer_rsrc_t rw = w8_rsrc(a.w + n0 * a.ldw, (uint32_t)(wrows * a.ldw));
+  const __amdgpu_buffer_rsrc_t rw =
+      PK ? w8_rsrc(a.w + (n0 / PK_ROWS) * KB * PK_CHUNK,
+                   (uint32_t)(((wrows + PK_ROWS - 1) / PK_ROWS) * KB * PK_CHUNK))
+         : w8_rsrc(a.w + n0 * a.ldw, (uint32_t)(wrows * a.ldw));
   const __amdgpu_buffer_rsrc_t rm = w8_rsrc(a.meta + n0 * a.ldm, (uint32_t)(wrows * a.ldm));
   const __amdgpu_buffer_rsrc_t rx = w8_rsrc(a.x, (uint32_t)(a.M * a.ldx * 2));   // rows past M read zero
   const __amdgpu_buffer_rsrc_t rsw = w8_rsrc(a.sw, 0xffffffffu);
@@ -374,7 +419,7 @@ __global__ void __launch_bounds__(512) k_gemm_w8a16_dma(W8Args a, int q, int r) 
     for (int j = 0; j < MT; ++j) acc[rb][j] = (v4f){0.f, 0.f, 0.f, 0.f};
 
   auto issue = [&](uint8_t* arr, W8X<MT>& xr, int tt) {
-    w8_dma_issue<CODES, RB, MT, GRAN_N>(arr + wslot, a, rw, rm, rx, rsw, n0, wave + W8_WAVES * min(tt, nt - 1), l,
+    w8_dma_issue<CODES, RB, MT, GRAN_N, PK>(arr + wslot, a, rw, rm, rx, rsw, n0, wave + W8_WAVES * min(tt, nt - 1), l,
                                         tt < nt, xr);
   };
   auto compute = [&](const uint8_t* arr, const W8X<MT>& xr) {
@@ -400,16 +445,26 @@ __global__ void __launch_bounds__(512) k_gemm_w8a16_dma(W8Args a, int q, int r) 
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       v4i cw;
-      if constexpr (CODES == C_I4) {
-        cw = (v4i){w8_lds<int>(sl, rb * D::CB + lr * 32 + 4 * g), 0, w8_lds<int>(sl, rb * D::CB + lr * 32 + 16 + 4 * g), 0};
-      } else {
-        const uint2 c0 = w8_lds<uint2>(sl, rb * D::CB + lr * 64 + 8 * g);
-        const uint2 c1 = w8_lds<uint2>(sl, rb * D::CB + lr * 64 + 32 + 8 * g);
+      int i0, i1;
+      if constexpr (PK) {   // chunk offsets rebased: codes at rb * CB, metadata at MOFF + rb * 256
+        const uint2 c0 = w8_lds<uint2>(sl, rb * D::CB + w8pk_code_off(lr, g, 0));
+        const uint2 c1 = w8_lds<uint2>(sl, rb * D::CB + w8pk_code_off(lr, g, 1));
         cw = (v4i){(int)c0.x, (int)c0.y, (int)c1.x, (int)c1.y};
+        i0 = w8_lds<uint16_t>(sl, D::MOFF + rb * 256 + w8pk_meta_off(lr, g, 0) - PK_META);
+        i1 = w8_lds<uint16_t>(sl, D::MOFF + rb * 256 + w8pk_meta_off(lr, g, 1) - PK_META);
+      } else {
+        if constexpr (CODES == C_I4) {
+          cw = (v4i){w8_lds<int>(sl, rb * D::CB + lr * 32 + 4 * g), 0,
+                     w8_lds<int>(sl, rb * D::CB + lr * 32 + 16 + 4 * g), 0};
+        } else {
+          const uint2 c0 = w8_lds<uint2>(sl, rb * D::CB + lr * 64 + 8 * g);
+          const uint2 c1 = w8_lds<uint2>(sl, rb * D::CB + lr * 64 + 32 + 8 * g);
+          cw = (v4i){(int)c0.x, (int)c0.y, (int)c1.x, (int)c1.y};
+        }
+        // index words: halfwords g and g + 4 of the row's 16 metadata bytes
+        i0 = w8_lds<uint16_t>(sl, D::MOFF + rb * 256 + lr * 16 + 2 * g);
+        i1 = w8_lds<uint16_t>(sl, D::MOFF + rb * 256 + lr * 16 + 8 + 2 * g);
       }
-      // index words: halfwords g and g + 4 of the row's 16 metadata bytes
-      const int i0 = w8_lds<uint16_t>(sl, D::MOFF + rb * 256 + lr * 16 + 2 * g);
-      const int i1 = w8_lds<uint16_t>(sl, D::MOFF + rb * 256 + lr * 16 + 8 + 2 * g);
       const v4i a0 = widen8<CODES>(cw[0], cw[1]);
       const v4i a1 = widen8<CODES>(cw[2], cw[3]);
       float4 sw;
@@ -482,11 +537,12 @@ __global__ void __launch_bounds__(512) k_gemm_w8a16_dma(W8Args a, int q, int r) 
 // Launches the LDS-streaming kernel with RB row blocks per workgroup if its
 // ring fits LDS and the grid keeps at least 224 workgroups (RB = 1 always
 // qualifies).
-template <int CODES, int RB, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
+template <int CODES, int RB, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T, bool PK>
 static bool try_w8_dma(const W8Args& a, hipStream_t st, int64_t rows16) {
   if constexpr (W8Dma<CODES, RB, MT>::FITS) {
     if (RB == 1 || rows16 >= RB * 224) {
-      k_gemm_w8a16_dma<CODES, RB, MT, GRAN_N, OUT_BF16, OUT_T, false><<<(unsigned)cdiv(rows16, RB), 512, 0, st>>>(a, 0, 0);
+      k_gemm_w8a16_dma<CODES, RB, MT, GRAN_N, OUT_BF16, OUT_T, false, PK>
+          <<<(unsigned)cdiv(rows16, RB), 512, 0, st>>>(a, 0, 0);
       return true;
     }
   }
@@ -496,24 +552,24 @@ static bool try_w8_dma(const W8Args& a, hipStream_t st, int64_t rows16) {
 // More 16-row blocks than CUs but too few for 224 workgroups of four: one
 // workgroup per CU with an even share of ceil(R / CUs) or one fewer row
 // blocks (as the FP8 decode kernel).
-template <int CODES, int RB, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
+template <int CODES, int RB, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T, bool PK>
 static bool try_w8_even_rb(const W8Args& a, hipStream_t st, int64_t rows16, int cus) {
   if constexpr (W8Dma<CODES, RB, MT>::FITS) {
-    k_gemm_w8a16_dma<CODES, RB, MT, GRAN_N, OUT_BF16, OUT_T, true><<<(unsigned)cus, 512, 0, st>>>(a, (int)(rows16 / cus),
-                                                                                      (int)(rows16 % cus));
+    k_gemm_w8a16_dma<CODES, RB, MT, GRAN_N, OUT_BF16, OUT_T, true, PK>
+        <<<(unsigned)cus, 512, 0, st>>>(a, (int)(rows16 / cus), (int)(rows16 % cus));
     return true;
   }
   return false;
 }
 
-template <int CODES, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
+template <int CODES, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T, bool PK>
 static bool try_w8_even(const W8Args& a, hipStream_t st, int64_t rows16) {
   const int cus = cu_count();
   if (rows16 <= cus || rows16 >= 4 * 224 || rows16 > 4LL * cus) return false;
   switch (cdiv(rows16, cus)) {
-    case 2: return try_w8_even_rb<CODES, 2, MT, GRAN_N, OUT_BF16, OUT_T>(a, st, rows16, cus);
-    case 3: return try_w8_even_rb<CODES, 3, MT, GRAN_N, OUT_BF16, OUT_T>(a, st, rows16, cus);
-    default: return try_w8_even_rb<CODES, 4, MT, GRAN_N, OUT_BF16, OUT_T>(a, st, rows16, cus);
+    case 2: return try_w8_even_rb<CODES, 2, MT, GRAN_N, OUT_BF16, OUT_T, PK>(a, st, rows16, cus);
+    case 3: return try_w8_even_rb<CODES, 3, MT, GRAN_N, OUT_BF16, OUT_T, PK>(a, st, rows16, cus);
+    default: return try_w8_even_rb<CODES, 4, MT, GRAN_N, OUT_BF16, OUT_T, PK>(a, st, rows16, cus);
   }
 }
 
@@ -545,7 +601,9 @@ struct Lay {
 }  // namespace w8t
 
 #if SG_DEVICE_PASS
-template <int CODES, int GRAN_N>
+// PK: W and metadata as the tile's 16 packed chunks, each copied as stored
+// (codes of row block b at W_OFF + 1024 b, metadata at M_OFF + 256 b).
+template <int CODES, int GRAN_N, bool PK>
 __device__ __forceinline__ void w8t_issue(uint8_t* st, const W8Args& a, __amdgpu_buffer_rsrc_t rx,
                                           __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t rm,
                                           __amdgpu_buffer_rsrc_t rsw, int64_t n0, int kb, int wave, int l) {
@@ -556,7 +614,22 @@ __device__ __forceinline__ void w8t_issue(uint8_t* st, const W8Args& a, __amdgpu
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (w8_lds_t*)(st + L::X_OFF + s * 1024), 16,
                                              (uint32_t)(r * a.ldx * 2 + c * 16), kb * 256, 0, 0);
   }
-  if constexpr (CODES == C_I4) {   // 512 units: row p >> 1, stored unit p & 1
+  if constexpr (PK) {   // 1024 code units (row block p >> 6), then 256 metadata units (row block p >> 4)
+    const int KB = (int)(a.K >> 7);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int s = 8 * i + wave, p = 64 * s + l;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (w8_lds_t*)(st + L::W_OFF + s * 1024), 16,
+                                               (uint32_t)((p >> 6) * KB * PK_CHUNK + 16 * (p & 63)), kb * PK_CHUNK,
+                                               0, 0);
+    }
+    if (wave < 4) {
+      const int p = 64 * wave + l;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (w8_lds_t*)(st + L::M_OFF + wave * 1024), 16,
+                                               (uint32_t)((p >> 4) * KB * PK_CHUNK + PK_META + 16 * (p & 15)),
+                                               kb * PK_CHUNK, 0, 0);
+    }
+  } else if constexpr (CODES == C_I4) {   // 512 units: row p >> 1, stored unit p & 1
     const int p = 64 * wave + l, r = p >> 1, u = (p & 1) ^ ((r >> 3) & 1);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (w8_lds_t*)(st + L::W_OFF + wave * 1024), 16,
                                              (uint32_t)(r * a.ldw + u * 16), kb * 32, 0, 0);
@@ -569,8 +642,9 @@ __device__ __forceinline__ void w8t_issue(uint8_t* st, const W8Args& a, __amdgpu
     }
   }
   if (wave < 4) {   // metadata: row 64 wave + l
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rm, (w8_lds_t*)(st + L::M_OFF + wave * 1024), 16,
-                                             (uint32_t)((64 * wave + l) * a.ldm), kb * 16, 0, 0);
+    if constexpr (!PK)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rm, (w8_lds_t*)(st + L::M_OFF + wave * 1024), 16,
+                                               (uint32_t)((64 * wave + l) * a.ldm), kb * 16, 0, 0);
   } else {          // W scales: row 64 (wave - 4) + l
     const int64_t n = min(n0 + 64 * (wave - 4) + l, a.N - 1);
     const int64_t row = GRAN_N == 128 ? (n >> 7) : n;
@@ -581,7 +655,7 @@ __device__ __forceinline__ void w8t_issue(uint8_t* st, const W8Args& a, __amdgpu
 
 // Multiplies one stage into the wave's 4 x 4 sub-tiles and promotes each
 // K block's partial with its W scale.
-template <int CODES, int GRAN_N>
+template <int CODES, int GRAN_N, bool PK>
 __device__ __forceinline__ void w8t_compute(const uint8_t* st, int wn, int wm, int g, int lr, v4f (&acc)[4][4]) {
   using L = w8t::Lay<CODES>;
   v8i b0[4], b1[4];
@@ -600,7 +674,15 @@ __device__ __forceinline__ void w8t_compute(const uint8_t* st, int wn, int wm, i
   for (int i = 0; i < 4; ++i) {
     const int r = wn * 64 + 16 * i + lr;   // W row in the tile
     v4i cw;
-    if constexpr (CODES == C_I4) {
+    int i0, i1;
+    if constexpr (PK) {   // row block wn * 4 + i of the tile, local row lr
+      const uint32_t cb = L::W_OFF + (uint32_t)(wn * 4 + i) * 1024, mb = L::M_OFF + (uint32_t)(wn * 4 + i) * 256;
+      const uint2 c0 = w8_lds<uint2>(st, cb + w8pk_code_off(lr, g, 0));
+      const uint2 c1 = w8_lds<uint2>(st, cb + w8pk_code_off(lr, g, 1));
+      cw = (v4i){(int)c0.x, (int)c0.y, (int)c1.x, (int)c1.y};
+      i0 = w8_lds<uint16_t>(st, mb + w8pk_meta_off(lr, g, 0) - PK_META);
+      i1 = w8_lds<uint16_t>(st, mb + w8pk_meta_off(lr, g, 1) - PK_META);
+    } else if constexpr (CODES == C_I4) {
       const int f = (lr >> 3) & 1;
       cw = (v4i){w8_lds<int>(st, L::W_OFF + r * 32 + (f << 4) + 4 * g), 0,
                  w8_lds<int>(st, L::W_OFF + r * 32 + ((1 ^ f) << 4) + 4 * g), 0};
@@ -610,9 +692,10 @@ __device__ __forceinline__ void w8t_compute(const uint8_t* st, int wn, int wm, i
       const uint2 c1 = w8_lds<uint2>(st, L::W_OFF + r * 64 + (((2 + (g >> 1)) ^ f) << 4) + 8 * (g & 1));
       cw = (v4i){(int)c0.x, (int)c0.y, (int)c1.x, (int)c1.y};
     }
-    // index words: halfwords g and g + 4 of the row's 16 metadata bytes
-    const int i0 = w8_lds<uint16_t>(st, L::M_OFF + r * 16 + 2 * g);
-    const int i1 = w8_lds<uint16_t>(st, L::M_OFF + r * 16 + 8 + 2 * g);
+    if constexpr (!PK) {   // index words: halfwords g and g + 4 of the row's 16 metadata bytes
+      i0 = w8_lds<uint16_t>(st, L::M_OFF + r * 16 + 2 * g);
+      i1 = w8_lds<uint16_t>(st, L::M_OFF + r * 16 + 8 + 2 * g);
+    }
     const v4i a0 = widen8<CODES>(cw[0], cw[1]);
     const v4i a1 = widen8<CODES>(cw[2], cw[3]);
     float4 sw;
@@ -634,7 +717,7 @@ __device__ __forceinline__ void w8t_compute(const uint8_t* st, int wn, int wm, i
 }
 #endif  // SG_DEVICE_PASS
 
-template <int CODES, int GRAN_N, bool OUT_BF16, bool OUT_T>
+template <int CODES, int GRAN_N, bool OUT_BF16, bool OUT_T, bool PK>
 __global__ void __launch_bounds__(512) k_gemm_w8a16_tile(W8Args a, int tiles_m, int tiles_n) {
 #if SG_DEVICE_PASS
   using L = w8t::Lay<CODES>;
@@ -651,7 +734,10 @@ __global__ void __launch_bounds__(512) k_gemm_w8a16_tile(W8Args a, int tiles_m, 
   // rows past M or N read as zero (resources sized to the rows that exist)
   const int64_t mrows = min((int64_t)w8t::BM, a.M - m0), nrows = min((int64_t)w8t::BN, a.N - n0);
   const __amdgpu_buffer_rsrc_t rx = w8_rsrc(a.x + m0 * a.ldx, (uint32_t)(mrows * a.ldx * 2));
-  const __amdgpu_buffer_rsrc_t rw = w8_rsrc(a.w + n0 * a.ldw, (uint32_t)(nrows * a.ldw));
+  const __amdgpu_buffer_rsrc_t rw =
+      PK ? w8_rsrc(a.w + (n0 / PK_ROWS) * KB * PK_CHUNK,
+                   (uint32_t)(((nrows + PK_ROWS - 1) / PK_ROWS) * KB * PK_CHUNK))
+         : w8_rsrc(a.w + n0 * a.ldw, (uint32_t)(nrows * a.ldw));
   const __amdgpu_buffer_rsrc_t rm = w8_rsrc(a.meta + n0 * a.ldm, (uint32_t)(nrows * a.ldm));
   const __amdgpu_buffer_rsrc_t rsw = w8_rsrc(a.sw, 0xffffffffu);
 
@@ -664,17 +750,17 @@ __global__ void __launch_bounds__(512) k_gemm_w8a16_tile(W8Args a, int tiles_m, 
   // K block kb lives in s0 for even kb, s1 for odd kb; a wave's only loads in
   // flight at each wait are the next stage's, and the barrier after it also
   // tells every wave that the stage it is about to overwrite has been read
-  w8t_issue<CODES, GRAN_N>(s0, a, rx, rw, rm, rsw, n0, 0, wave, l);
+  w8t_issue<CODES, GRAN_N, PK>(s0, a, rx, rw, rm, rsw, n0, 0, wave, l);
   wait_vmcnt<0>();
   __syncthreads();
   for (int kb = 0; kb < KB; kb += 2) {
-    if (kb + 1 < KB) w8t_issue<CODES, GRAN_N>(s1, a, rx, rw, rm, rsw, n0, kb + 1, wave, l);
-    w8t_compute<CODES, GRAN_N>(s0, wn, wm, g, lr, acc);
+    if (kb + 1 < KB) w8t_issue<CODES, GRAN_N, PK>(s1, a, rx, rw, rm, rsw, n0, kb + 1, wave, l);
+    w8t_compute<CODES, GRAN_N, PK>(s0, wn, wm, g, lr, acc);
     wait_vmcnt<0>();
     __syncthreads();
     if (kb + 1 < KB) {
-      if (kb + 2 < KB) w8t_issue<CODES, GRAN_N>(s0, a, rx, rw, rm, rsw, n0, kb + 2, wave, l);
-      w8t_compute<CODES, GRAN_N>(s1, wn, wm, g, lr, acc);
+      if (kb + 2 < KB) w8t_issue<CODES, GRAN_N, PK>(s0, a, rx, rw, rm, rsw, n0, kb + 2, wave, l);
+      w8t_compute<CODES, GRAN_N, PK>(s1, wn, wm, g, lr, acc);
       wait_vmcnt<0>();
       __syncthreads();
     }
@@ -701,14 +787,14 @@ __global__ void __launch_bounds__(512) k_gemm_w8a16_tile(W8Args a, int tiles_m, 
 // (N = 4096: 24 us at M = 128, 44 us at 256, 66 us at 384; the tile kernel
 // 44-51 us for all three), so the tile kernel wins once
 // ceil(M / 64) * N / 4096 exceeds 4.5 rounds.
-template <int CODES, int GRAN_N, bool OUT_BF16, bool OUT_T>
+template <int CODES, int GRAN_N, bool OUT_BF16, bool OUT_T, bool PK>
 static bool try_w8_tile(const W8Args& a, hipStream_t st) {
   const int64_t tm = cdiv(a.M, w8t::BM), tn = cdiv(a.N, w8t::BN);
   if (tm * tn > 0x7fffffffLL || a.ldx >= (1LL << 22) || a.ldw >= (1LL << 23) || a.ldm >= (1LL << 23))
     return false;
   const int64_t rounds = cdiv(tm * tn, cu_count());
   if (2 * cdiv(a.M, 64) * a.N < 9 * 4096 * rounds) return false;
-  k_gemm_w8a16_tile<CODES, GRAN_N, OUT_BF16, OUT_T><<<(unsigned)(tm * tn), 512, 0, st>>>(a, (int)tm, (int)tn);
+  k_gemm_w8a16_tile<CODES, GRAN_N, OUT_BF16, OUT_T, PK><<<(unsigned)(tm * tn), 512, 0, st>>>(a, (int)tm, (int)tn);
   return true;
 }
 
@@ -717,43 +803,43 @@ static bool try_w8_tile(const W8Args& a, hipStream_t st) {
 // MT > 2), 2, 1 that keeps at least 224 workgroups.  Every workgroup reads its X rows in full, so
 // fewer, taller workgroups read X fewer times (measured at M = 37 and 64:
 // 1.7x faster than one row block per workgroup).
-template <int CODES, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
+template <int CODES, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T, bool PK>
 static void launch_w8_mt(const W8Args& a, hipStream_t st) {
   const int64_t rows16 = cdiv(a.N, 16);
   const unsigned gy = (unsigned)cdiv(a.M, 16 * MT);
   if constexpr (MT <= 3) {   // LDS streaming, one workgroup per RB row blocks and all of M
-    if (try_w8_even<CODES, MT, GRAN_N, OUT_BF16, OUT_T>(a, st, rows16) ||
-        try_w8_dma<CODES, 4, MT, GRAN_N, OUT_BF16, OUT_T>(a, st, rows16) ||
-        try_w8_dma<CODES, 2, MT, GRAN_N, OUT_BF16, OUT_T>(a, st, rows16) ||
-        try_w8_dma<CODES, 1, MT, GRAN_N, OUT_BF16, OUT_T>(a, st, rows16))
+    if (try_w8_even<CODES, MT, GRAN_N, OUT_BF16, OUT_T, PK>(a, st, rows16) ||
+        try_w8_dma<CODES, 4, MT, GRAN_N, OUT_BF16, OUT_T, PK>(a, st, rows16) ||
+        try_w8_dma<CODES, 2, MT, GRAN_N, OUT_BF16, OUT_T, PK>(a, st, rows16) ||
+        try_w8_dma<CODES, 1, MT, GRAN_N, OUT_BF16, OUT_T, PK>(a, st, rows16))
       return;
   }
   constexpr int RB4 = MT <= 2 ? 4 : 2, RB2 = 2;
   if (RB4 == 4 && rows16 * gy >= 4 * 224)
-    k_gemm_w8a16<CODES, RB4, MT, GRAN_N, OUT_BF16, OUT_T><<<dim3((unsigned)cdiv(rows16, RB4), gy), 512, 0, st>>>(a);
+    k_gemm_w8a16<CODES, RB4, MT, GRAN_N, OUT_BF16, OUT_T, PK><<<dim3((unsigned)cdiv(rows16, RB4), gy), 512, 0, st>>>(a);
   else if (RB2 == 2 && rows16 * gy >= 2 * 224)
-    k_gemm_w8a16<CODES, RB2, MT, GRAN_N, OUT_BF16, OUT_T><<<dim3((unsigned)cdiv(rows16, RB2), gy), 512, 0, st>>>(a);
+    k_gemm_w8a16<CODES, RB2, MT, GRAN_N, OUT_BF16, OUT_T, PK><<<dim3((unsigned)cdiv(rows16, RB2), gy), 512, 0, st>>>(a);
   else
-    k_gemm_w8a16<CODES, 1, MT, GRAN_N, OUT_BF16, OUT_T><<<dim3((unsigned)rows16, gy), 512, 0, st>>>(a);
+    k_gemm_w8a16<CODES, 1, MT, GRAN_N, OUT_BF16, OUT_T, PK><<<dim3((unsigned)rows16, gy), 512, 0, st>>>(a);
 }
 
-template <int CODES, int GRAN_N, bool OUT_BF16, bool OUT_T>
+template <int CODES, int GRAN_N, bool OUT_BF16, bool OUT_T, bool PK>
 static void launch_w8_shape(const W8Args& a, hipStream_t st) {
-  if (a.M > 64 && try_w8_tile<CODES, GRAN_N, OUT_BF16, OUT_T>(a, st)) return;
-  if (a.M <= 16) launch_w8_mt<CODES, 1, GRAN_N, OUT_BF16, OUT_T>(a, st);
-  else if (a.M <= 32) launch_w8_mt<CODES, 2, GRAN_N, OUT_BF16, OUT_T>(a, st);
-  else if (a.M <= 48) launch_w8_mt<CODES, 3, GRAN_N, OUT_BF16, OUT_T>(a, st);
-  else launch_w8_mt<CODES, 4, GRAN_N, OUT_BF16, OUT_T>(a, st);
+  if (a.M > 64 && try_w8_tile<CODES, GRAN_N, OUT_BF16, OUT_T, PK>(a, st)) return;
+  if (a.M <= 16) launch_w8_mt<CODES, 1, GRAN_N, OUT_BF16, OUT_T, PK>(a, st);
+  else if (a.M <= 32) launch_w8_mt<CODES, 2, GRAN_N, OUT_BF16, OUT_T, PK>(a, st);
+  else if (a.M <= 48) launch_w8_mt<CODES, 3, GRAN_N, OUT_BF16, OUT_T, PK>(a, st);
+  else launch_w8_mt<CODES, 4, GRAN_N, OUT_BF16, OUT_T, PK>(a, st);
 }
 
-template <int CODES, int GRAN_N>
+template <int CODES, int GRAN_N, bool PK = false>
 static void launch_w8_form(const W8Args& a, bool bf16, bool yt, hipStream_t st) {
   if (bf16) {
-    if (yt) launch_w8_shape<CODES, GRAN_N, true, true>(a, st);
-    else launch_w8_shape<CODES, GRAN_N, true, false>(a, st);
+    if (yt) launch_w8_shape<CODES, GRAN_N, true, true, PK>(a, st);
+    else launch_w8_shape<CODES, GRAN_N, true, false, PK>(a, st);
   } else {
-    if (yt) launch_w8_shape<CODES, GRAN_N, false, true>(a, st);
-    else launch_w8_shape<CODES, GRAN_N, false, false>(a, st);
+    if (yt) launch_w8_shape<CODES, GRAN_N, false, true, PK>(a, st);
+    else launch_w8_shape<CODES, GRAN_N, false, false, PK>(a, st);
   }
 }
 
@@ -797,6 +883,45 @@ extern "C" sg_status sg_w8a16_sparse24_gemm_groupwise(int64_t M, int64_t N, int6
   } else {
     if (gran_n == 128) launch_w8_form<C_E4M3, 128>(a, bf16, yt, stream);
     else launch_w8_form<C_E4M3, 1>(a, bf16, yt, stream);
+  }
+  return launch_status();
+}
+
+extern "C" sg_status sg_w8a16_sparse24_gemm_groupwise_packed(int64_t M, int64_t N, int64_t K, const uint16_t* x,
+                                                             int64_t ldx, const uint8_t* wpacked, sg_dtype w_dt,
+                                                             const float* sw, int64_t sw_sn, int64_t sw_sk,
+                                                             int gran_n, const float* bias, void* y, sg_dtype y_dt,
+                                                             int64_t ldy, sg_form form, hipStream_t stream) {
+  if (!x || !wpacked || !sw || !y) return SG_ERR_NULL;
+  if (w_dt != SG_E4M3 && w_dt != SG_I8) return SG_ERR_UNSUPPORTED;
+  if (gran_n != 1 && gran_n != 128) return SG_ERR_UNSUPPORTED;
+  if (y_dt != SG_F32 && y_dt != SG_BF16) return SG_ERR_UNSUPPORTED;
+  if (form != SG_OUT_Y && form != SG_OUT_YT) return SG_ERR_UNSUPPORTED;
+  if (M <= 0 || N <= 0 || K <= 0 || K % 128 != 0 || ldx < K) return SG_ERR_SHAPE;
+  if (ldy < (form == SG_OUT_Y ? N : M)) return SG_ERR_SHAPE;
+  // 32-bit buffer offsets: 64 X rows, and the 16 row blocks' chunks of a tile
+  if (ldx >= (1LL << 24) || (K / 128) * 16 * PK_CHUNK >= (1LL << 31) || sw_sn < 0 || sw_sk < 0) return SG_ERR_SHAPE;
+  if (((cdiv(N, gran_n) - 1) * sw_sn + (K / 128 - 1) * sw_sk) * 4 >= (1LL << 31)) return SG_ERR_SHAPE;
+  if (cdiv(N, 16) > 0x7fffffffLL || cdiv(M, 16) > 65535) return SG_ERR_SHAPE;
+  if (!aligned(x, 16) || (ldx * 2) % 16 || !aligned(wpacked, 16) || !aligned(sw, 4) || !aligned(bias, 4) ||
+      !aligned(y, dtype_size(y_dt)))
+    return SG_ERR_ALIGN;
+  W8Args a;
+  a.M = M; a.N = N; a.K = K;
+  a.x = x; a.ldx = ldx;
+  a.w = wpacked; a.ldw = 0; a.meta = wpacked; a.ldm = 0;
+  a.sw = sw; a.sw_sn = sw_sn; a.sw_sk = sw_sk; a.gn_shift = gran_n == 128 ? 7 : 0;
+  a.bias = bias;
+  a.y = y; a.ldy = ldy;
+  a.vec_store = (ldy % 4 == 0) && aligned(y, 4 * dtype_size(y_dt));
+  clear_hip_error();
+  const bool bf16 = y_dt == SG_BF16, yt = form == SG_OUT_YT;
+  if (w_dt == SG_I8) {
+    if (gran_n == 128) launch_w8_form<C_I8, 128, true>(a, bf16, yt, stream);
+    else launch_w8_form<C_I8, 1, true>(a, bf16, yt, stream);
+  } else {
+    if (gran_n == 128) launch_w8_form<C_E4M3, 128, true>(a, bf16, yt, stream);
+    else launch_w8_form<C_E4M3, 1, true>(a, bf16, yt, stream);
   }
   return launch_status();
 }

@@ -44,7 +44,8 @@ def test_header_declares_the_entry_points():
         "sg_int8_quant_groupwise", "sg_int8_sparse24_gemm_groupwise", "sg_int8_sparse24_gemm_groupwise_packed",
         "sg_fp8_gemm_groupwise_batched", "sg_fp8_sparse24_gemm_groupwise_batched",
         "sg_fp8_sparse24_gemm_groupwise_packed_batched", "sg_fp8_sparse24_gemm_groupwise_packed_grouped",
-        "sg_w8a16_sparse24_gemm_groupwise", "sg_w4a16_sparse24_gemm_groupwise",
+        "sg_w8a16_sparse24_gemm_groupwise", "sg_w8a16_sparse24_gemm_groupwise_packed",
+        "sg_w4a16_sparse24_gemm_groupwise",
         "sg_fp8_sparse24_gemm_packed_quant_x", "sg_probe_stream_read"])
 
 
@@ -372,6 +373,29 @@ def w8a16(**kw):
 ])
 def test_w8a16_validation(kw, code):
     assert w8a16(**kw) == code
+
+
+def w8a16_packed(**kw):
+    a = dict(M=16, N=256, K=256, x=P, ldx=256, w=P2, wdt=2, sw=P3, swn=2, swk=1, gn=128, bias=None, y=P, ydt=1,
+             ldy=256, form=0)
+    a.update(kw)
+    return sg.lib().sg_w8a16_sparse24_gemm_groupwise_packed(a["M"], a["N"], a["K"], a["x"], a["ldx"], a["w"],
+                                                            a["wdt"], a["sw"], a["swn"], a["swk"], a["gn"],
+                                                            a["bias"], a["y"], a["ydt"], a["ldy"], a["form"], None)
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), NULL), (dict(w=None), NULL), (dict(sw=None), NULL), (dict(y=None), NULL),
+    (dict(wdt=0), UNSUP), (dict(wdt=1), UNSUP), (dict(gn=64), UNSUP), (dict(ydt=2), UNSUP), (dict(form=3), UNSUP),
+    (dict(K=200), SHAPE), (dict(ldx=128), SHAPE), (dict(ldy=100), SHAPE), (dict(M=65535 * 16 + 1), SHAPE),
+    (dict(swk=-1), SHAPE), (dict(M=0), SHAPE), (dict(N=0), SHAPE), (dict(wdt=3, K=0), SHAPE),
+    # (K / 128) * 16 chunks of 1280 bytes must stay below 2^31 (a tile's 32-bit offsets)
+    (dict(K=128 * 104858, ldx=128 * 104858), SHAPE), (dict(ldx=1 << 24, K=256), SHAPE),
+    (dict(x=ODD), ALIGN), (dict(ldx=260), ALIGN), (dict(w=ODD), ALIGN), (dict(bias=ctypes.c_void_p(0x100002)), ALIGN),
+])
+def test_w8a16_packed_validation(kw, code):
+    assert w8a16_packed(**kw) == code
 
 
 def w4a16(**kw):

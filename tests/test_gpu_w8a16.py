@@ -161,6 +161,71 @@ def test_w8a16_from_the_gpu_weight_pipeline():
         assert_within_tolerance(got, ref, bound, f"int8={int8}")
 
 
+# ------------------------------------------------- W8A16, packed weight
+
+def check_packed(m, n, k, gn=128, int8=False, out=torch.bfloat16, forms=("y", "yt"), bias=False, seed=0,
+                 rows=None):
+    """The packed weight-only GEMM against the oracle (on `rows` of the
+    output only, when given), and bit for bit against the same call on the
+    unpacked weight."""
+    say(f"w8a16 packed M={m} N={n} K={k} gn={gn} int8={int8} {out} bias={bias} seed={seed}")
+    x, wv, meta, sw = operands(m, n, k, gn, int8, seed)
+    xbits = x.view(torch.int16).cpu().numpy().view(np.uint16)
+    sel = np.arange(m) if rows is None else np.asarray(rows)
+    ref, bound = oracle.w8a16_sparse24_gemm_groupwise(xbits[sel], wv, meta, sw, gn, "int8" if int8 else "e4m3",
+                                                      bound=True)
+    b = None
+    if bias:
+        bnp = np.random.default_rng(seed + 1).standard_normal(n).astype(np.float32)
+        ref, bound = oracle.add_bias(ref, bound, bnp)
+        b = up(bnp)
+    wvg, mg, swg = up(wv), up(meta), up(sw)
+    wp = sg.sparse24_pack_gfx950(wvg, mg)
+    for form in forms:
+        y = sg.w8a16_sparse24_gemm_groupwise_packed(x, wp, n, swg, gn, int8=int8, out_dtype=out, form=form, bias=b)
+        yc = sg.w8a16_sparse24_gemm_groupwise(x, wvg, mg, swg, gn, out_dtype=out, form=form, bias=b)
+        assert torch.equal(y.view(torch.int16) if out == torch.bfloat16 else y.view(torch.int32),
+                           yc.view(torch.int16) if out == torch.bfloat16 else yc.view(torch.int32)), f"form={form}"
+        got = down(y)
+        got = got.T if form == "yt" else got
+        assert got.shape == (m, n)
+        assert_within_tolerance(got[sel].astype(np.float64), ref, bound, f"form={form}")
+
+
+# the LDS-streaming decode kernel (M <= 48: one, two, three 16-row sub-tiles;
+# N not a multiple of 16, so the packer's zero rows are read; the even split),
+# the register kernel (M = 49..64, and M > 64 where tiles do not pay) and
+# the 256 x 128 tile kernel
+PACKED_SHAPES = [(1, 256, 128), (16, 512, 256), (17, 300, 384), (37, 1000, 512), (48, 13000, 256),
+                 (16, 5120, 1024), (20, 11008, 512), (64, 260, 256), (65, 256, 256), (200, 384, 640),
+                 (1000, 12300, 256)]
+
+
+@pytest.mark.parametrize("int8", [False, True])
+@pytest.mark.parametrize("m,n,k", PACKED_SHAPES)
+def test_w8a16_packed(m, n, k, int8):
+    check_packed(m, n, k, int8=int8, seed=m + n + k + 3 * int8)
+
+
+@pytest.mark.parametrize("m,n,k", [(37, 300, 384), (64, 260, 256), (300, 24580, 128)])
+def test_w8a16_packed_per_row_scales_fp32_bias(m, n, k):
+    check_packed(m, n, k, gn=1, out=torch.float32, bias=True, seed=70 + m)
+
+
+@pytest.mark.parametrize("int8", [False, True])
+def test_w8a16_packed_decode_full_size(int8):
+    """M = 16 and 37, N = 14336, K = 4096 (the benchmark's decode shape)."""
+    check_packed(16, 14336, 4096, int8=int8, forms=("y",), seed=80 + int8)
+    check_packed(37, 14336, 4096, int8=int8, forms=("y",), seed=82 + int8)
+
+
+def test_w8a16_packed_large_m_full_size_sampled_rows():
+    """2048 x 4096 x 4096 on the tile kernel, K = 8192 on a 512-row X; the
+    oracle computes sampled rows, the unpacked call all of them."""
+    check_packed(2048, 4096, 4096, forms=("y",), seed=84, rows=[0, 1, 127, 128, 1000, 2047])
+    check_packed(512, 4096, 8192, forms=("y",), seed=85, rows=[0, 77, 300, 511])
+
+
 # --------------------------------------------------------------- W4A16
 
 def check_w4(m, n, k, out=torch.bfloat16, forms=("y", "yt"), bias=False, seed=0):
