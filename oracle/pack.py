@@ -96,3 +96,49 @@ def unpack24_gfx950(packed, n: int, k: int):
         for j in range(4):
             mb[:, :, midx[g, j]] = packed[mpos[:, :, g] + j]
     return vb.reshape(n, k // 2), mb.reshape(n, k // 8)
+
+
+# ------------------------------------------------------------------ int4
+# The blocked form of a 2:4-compressed int4 weight (codes [N, K/4], two per
+# byte as ``quant.int4_quant_groupwise`` stores them, metadata [N, K/8]): the
+# same row-block / K-block chunking as above, without any permutation inside a
+# chunk.  For 16-row block R and 128-wide K block kb the 768-byte chunk at
+# (R * KB + kb) * 768 holds the 16 rows' 32 code bytes of block kb, row after
+# row (local row lr at lr * 32), then their 16 metadata bytes (lr at
+# 512 + lr * 16); rows past N are zero.  This too is the library's own layout
+# (what its weight-only kernels stream), a byte permutation of the canonical
+# arrays in the spirit of the packing kernels the pages describe.
+
+W4_CHUNK_BYTES = 768
+W4_META_OFF = 512
+
+
+def w4_packed_bytes(n: int, k: int) -> int:
+    return -(-n // ROWS) * (k // 128) * W4_CHUNK_BYTES
+
+
+def pack24_w4_blocked(codes4, meta) -> np.ndarray:
+    """codes4 uint8 [N, K/4] (int4 pairs), meta uint8 [N, K/8] -> blocked uint8."""
+    codes4 = np.asarray(codes4, dtype=np.uint8)
+    meta = np.asarray(meta, dtype=np.uint8)
+    n, quarter = codes4.shape
+    k = 4 * quarter
+    assert k % 128 == 0 and meta.shape == (n, k // 8)
+    kbc, t = k // 128, -(-n // ROWS)
+    c = np.zeros((t * ROWS, quarter), np.uint8)
+    m = np.zeros((t * ROWS, k // 8), np.uint8)
+    c[:n], m[:n] = codes4, meta
+    # [T, 16, KB, 32] -> [T, KB, 16, 32]: one row block's K block is 16 rows of 32 bytes
+    cb = c.reshape(t, ROWS, kbc, 32).transpose(0, 2, 1, 3).reshape(t, kbc, 512)
+    mb = m.reshape(t, ROWS, kbc, 16).transpose(0, 2, 1, 3).reshape(t, kbc, 256)
+    return np.concatenate([cb, mb], axis=2).reshape(-1)
+
+
+def unpack24_w4_blocked(packed, n: int, k: int):
+    """Inverse of ``pack24_w4_blocked``: -> (codes4 [N, K/4], meta [N, K/8])."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    kbc, t = k // 128, -(-n // ROWS)
+    ch = packed.reshape(t, kbc, W4_CHUNK_BYTES)
+    c = ch[:, :, :W4_META_OFF].reshape(t, kbc, ROWS, 32).transpose(0, 2, 1, 3).reshape(t * ROWS, k // 4)
+    m = ch[:, :, W4_META_OFF:].reshape(t, kbc, ROWS, 16).transpose(0, 2, 1, 3).reshape(t * ROWS, k // 8)
+    return c[:n].copy(), m[:n].copy()

@@ -78,3 +78,45 @@ def test_each_lane_group_word_is_its_smfmac_index():
             base = 64 * (g & 1) + 16 * (g >> 1)
             groups = [base // 4 + j for j in range(4)] + [base // 4 + 8 + j for j in range(4)]
             assert [(w >> (4 * j)) & 15 for j in range(8)] == [nib[r, q] for q in groups]
+
+
+# ------------------------------------------------------------- int4 blocked
+
+def test_w4_blocked_bytes_one_by_one():
+    """Every byte of a small blocked weight placed by the position formula,
+    element by element (the oracle reshapes and transposes)."""
+    rng = np.random.default_rng(43)
+    n, k = 37, 384                       # three row blocks, the last one 5 rows long
+    codes = rng.integers(0, 256, size=(n, k // 4)).astype(np.uint8)
+    meta = rng.integers(0, 256, size=(n, k // 8)).astype(np.uint8)
+    p = oracle.pack24_w4_blocked(codes, meta)
+    kbc = k // 128
+    assert p.size == oracle.w4_packed_bytes(n, k) == 3 * kbc * 768
+    want = np.zeros(p.size, np.uint8)
+    for row in range(n):
+        rb, lr = divmod(row, 16)
+        for kb in range(kbc):
+            base = (rb * kbc + kb) * 768
+            for j in range(32):
+                want[base + lr * 32 + j] = codes[row, kb * 32 + j]
+            for j in range(16):
+                want[base + 512 + lr * 16 + j] = meta[row, kb * 16 + j]
+    assert np.array_equal(p, want)
+
+
+def test_w4_blocked_roundtrip_and_zero_rows():
+    rng = np.random.default_rng(44)
+    n, k = 300, 512
+    codes = rng.integers(0, 256, size=(n, k // 4)).astype(np.uint8)
+    meta = rng.integers(0, 256, size=(n, k // 8)).astype(np.uint8)
+    p = oracle.pack24_w4_blocked(codes, meta)
+    c2, m2 = oracle.unpack24_w4_blocked(p, n, k)
+    assert np.array_equal(c2, codes) and np.array_equal(m2, meta)
+    # rows 300..303 (row block 18, local rows 12..15) are zero in every chunk
+    ch = p.reshape(19, k // 128, 768)[18]
+    assert not ch[:, 12 * 32:512].any() and not ch[:, 512 + 12 * 16:].any()
+    # a one-row weight: each chunk holds its 32 + 16 bytes and zeros
+    p1 = oracle.pack24_w4_blocked(codes[:1], meta[:1]).reshape(k // 128, 768)
+    assert np.array_equal(p1[:, :32], codes[0].reshape(k // 128, 32))
+    assert np.array_equal(p1[:, 512:528], meta[0].reshape(k // 128, 16))
+    assert np.count_nonzero(p1[:, 32:512]) == 0 and np.count_nonzero(p1[:, 528:]) == 0
