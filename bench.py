@@ -378,6 +378,13 @@ def rows_report():
         b = dn * dk // 4 + dn * dk // 8 + 4 * dn * (dk // 128) + dm * dk * 2 + dm * dn * 2
         out[f"next_w4a16_decode_M{dm}_N{dn}_K{dk}_y"] = {"ms": ms, "GB/s": b / ms / 1e6,
                                                         "frac_hbm": b / ms / 1e6 / PEAK_HBM_GBS}
+        # the same weights in the blocked form (same bytes, same results)
+        psets = [sg.sparse24_pack_w4(q4, mt) for q4, mt, _ in wsets]
+        ms = time_fn(lambda i: sg.w4a16_sparse24_gemm_groupwise_packed(
+            xb, psets[i % ROTATE_DECODE], dn, wsets[i % ROTATE_DECODE][2], y=y), reps=64, warm=16)
+        out[f"next_w4a16_packed_decode_M{dm}_N{dn}_K{dk}_y"] = {"ms": ms, "GB/s": b / ms / 1e6,
+                                                               "frac_hbm": b / ms / 1e6 / PEAK_HBM_GBS}
+        del psets
     del wsets
     xb = x.to(torch.bfloat16)
     wv8, mt8 = sg.sparse24_prune_compress(torch.from_numpy(workloads.sparse_large(seed=3, m=8, n=n, k=k)["w"]).to(DEV))
@@ -399,6 +406,11 @@ def rows_report():
     ms = time_fn(lambda i: sg.w4a16_sparse24_gemm_groupwise(xb, q4, mt8, s4, y=y), reps=10, warm=2)
     out["next_w4a16_gemm_2048x4096x4096_y"] = {"ms": ms, "TFLOP/s": flops / ms / 1e9,
                                                "frac_bf16_peak": flops / ms / 1e9 / PEAK_BF16_TFLOPS}
+    wp4 = sg.sparse24_pack_w4(q4, mt8)
+    ms = time_fn(lambda i: sg.w4a16_sparse24_gemm_groupwise_packed(xb, wp4, n, s4, y=y), reps=10, warm=2)
+    out["next_w4a16_packed_gemm_2048x4096x4096_y"] = {"ms": ms, "TFLOP/s": flops / ms / 1e9,
+                                                      "frac_bf16_peak": flops / ms / 1e9 / PEAK_BF16_TFLOPS}
+    del wp4
     del xb, wv8, mt8, wq8, q4, s4
     # a7: fused int4 + bf16 add at L=2048, D1=4096, D2=64, D=4096
     dd = workloads.mixed_add(seed=5)

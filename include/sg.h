@@ -444,6 +444,44 @@ sg_status sg_w4a16_sparse24_gemm_groupwise(int64_t M, int64_t N, int64_t K, cons
                                            void* y, sg_dtype y_dt, int64_t ldy, sg_form form, hipStream_t stream);
 
 /*
+ * sg_sparse24_w4_packed_bytes -- bytes of the blocked form of an N x K 2:4
+ * int4 weight: ceil(N/16) * (K/128) * 768, or -1 unless N >= 1, K >= 1 and
+ * K % 128 == 0.
+ *
+ * sg_sparse24_pack_w4 -- the blocked form the weight-only kernels stream: for
+ * 16-row block R and 128-wide K block kb the 768-byte chunk at
+ * (R * K/128 + kb) * 768 holds local row lr's 32 code bytes of block kb at
+ * lr*32 (as stored in wv4) and its 16 metadata bytes at 512 + lr*16; rows past
+ * N (up to the next multiple of 16) are zero.  The chunking of
+ * sg_sparse24_pack_gfx950 without the permutation inside a chunk ([T3258]
+ * jcaip's review: the weight arranged by a packing kernel; [I2029] klevzoff).
+ *   wv4   : [N, K/4] int4 codes as sg_w4a16_sparse24_gemm_groupwise takes them, ld ldwv4.
+ *   wmeta : [N, K/8] metadata, ld ldwm.
+ *   packed: sg_sparse24_w4_packed_bytes(N, K) bytes, 16-byte aligned, written fully.
+ * Requires K % 128 == 0, ldwv4 >= K/4, ldwm >= K/8, multiples of 16; wv4,
+ * wmeta 16-byte aligned.
+ *
+ * sg_w4a16_sparse24_gemm_groupwise_packed -- sg_w4a16_sparse24_gemm_groupwise
+ * with the weight in that blocked form: the same arithmetic in the same order
+ * (results equal the unpacked call's bit for bit), with each chunk reaching
+ * LDS in 256-byte pieces per wave instruction instead of 32- and 16-byte row
+ * pieces.
+ *   wpacked : sg_sparse24_w4_packed_bytes(N, K) bytes, 16-byte aligned.
+ *   other arguments as sg_w4a16_sparse24_gemm_groupwise.
+ * Requires K % 128 == 0, ldx >= K, ldx < 2^24, (K / 128) * 16 * 768 < 2^31,
+ * ceil(M/16) <= 65535; x 16-byte aligned, ldx * 2 a multiple of 16.
+ */
+int64_t sg_sparse24_w4_packed_bytes(int64_t N, int64_t K);
+
+sg_status sg_sparse24_pack_w4(const uint8_t* wv4, int64_t ldwv4, const uint8_t* wmeta, int64_t ldwm, int64_t N,
+                              int64_t K, uint8_t* packed, hipStream_t stream);
+
+sg_status sg_w4a16_sparse24_gemm_groupwise_packed(int64_t M, int64_t N, int64_t K, const uint16_t* x, int64_t ldx,
+                                                  const uint8_t* wpacked, const float* sw, int64_t sw_sn,
+                                                  int64_t sw_sk, const float* bias, void* y, sg_dtype y_dt,
+                                                  int64_t ldy, sg_form form, hipStream_t stream);
+
+/*
  * sg_fp8_sparse24_gemm_groupwise_packed_grouped -- G problems that share N and
  * K but not M (e.g. tokens routed to experts): group g multiplies rows
  * row_off[g] .. row_off[g] + m_sizes[g] - 1 of X (row_off = prefix sums of

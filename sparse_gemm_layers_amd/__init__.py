@@ -35,6 +35,9 @@ from ._binding import (
     w8a16_sparse24_gemm_groupwise,
     w8a16_sparse24_gemm_groupwise_packed,
     w4a16_sparse24_gemm_groupwise,
+    w4a16_sparse24_gemm_groupwise_packed,
+    sparse24_w4_packed_bytes,
+    sparse24_pack_w4,
 )
 
 __all__ = [
@@ -47,4 +50,5 @@ __all__ = [
     "fp8_gemm_groupwise_batched", "fp8_sparse24_gemm_groupwise_batched",
     "fp8_sparse24_gemm_groupwise_packed_batched", "fp8_sparse24_gemm_groupwise_packed_grouped",
     "w8a16_sparse24_gemm_groupwise", "w8a16_sparse24_gemm_groupwise_packed", "w4a16_sparse24_gemm_groupwise",
+    "w4a16_sparse24_gemm_groupwise_packed", "sparse24_w4_packed_bytes", "sparse24_pack_w4",
 ]

@@ -35,6 +35,8 @@ _SIGS = {
                                         _i64, _ptr, _i64, _i64, _int, _ptr, _int, _i64, _int, _ptr], _int),
     "sg_sparse24_packed_bytes": ([_i64, _i64], _i64),
     "sg_sparse24_pack_gfx950": ([_ptr, _i64, _ptr, _i64, _i64, _i64, _ptr, _ptr], _int),
+    "sg_sparse24_w4_packed_bytes": ([_i64, _i64], _i64),
+    "sg_sparse24_pack_w4": ([_ptr, _i64, _ptr, _i64, _i64, _i64, _ptr, _ptr], _int),
     "sg_fp8_sparse24_gemm_groupwise_packed": ([_i64, _i64, _i64, _ptr, _i64, _ptr, _i64, _i64, _int, _ptr, _ptr,
                                                _i64, _i64, _int, _ptr, _int, _i64, _int, _ptr], _int),
     "sg_fp8_sparse24_gemm_packed_quant_x": ([_i64, _i64, _i64, _ptr, _int, _i64, _ptr, _ptr, _i64, _i64, _int,
@@ -62,6 +64,8 @@ _SIGS = {
                                           _i64, _int, _ptr, _ptr, _int, _i64, _int, _ptr], _int),
     "sg_w8a16_sparse24_gemm_groupwise_packed": ([_i64, _i64, _i64, _ptr, _i64, _ptr, _int, _ptr, _i64, _i64, _int,
                                                  _ptr, _ptr, _int, _i64, _int, _ptr], _int),
+    "sg_w4a16_sparse24_gemm_groupwise_packed": ([_i64, _i64, _i64, _ptr, _i64, _ptr, _ptr, _i64, _i64, _ptr, _ptr,
+                                                 _int, _i64, _int, _ptr], _int),
     "sg_w4a16_sparse24_gemm_groupwise": ([_i64, _i64, _i64, _ptr, _i64, _ptr, _i64, _ptr, _i64, _ptr, _i64, _i64,
                                           _ptr, _ptr, _int, _i64, _int, _ptr], _int),
     "sg_probe_matrix_ops": ([_int, _int], _i64),
@@ -570,6 +574,65 @@ def w4a16_sparse24_gemm_groupwise(x, wv4, wmeta, sw, out_dtype=torch.bfloat16, f
                                                 _row_stride(wmeta), _p(sw), sw.stride(0), sw.stride(1), bp, _p(y), ydt,
                                                 _row_stride(y), f, _stream(x))
     _check(st, "sg_w4a16_sparse24_gemm_groupwise")
+    return y
+
+
+def sparse24_w4_packed_bytes(n: int, k: int) -> int:
+    return int(lib().sg_sparse24_w4_packed_bytes(n, k))
+
+
+def _want_w4_packed(wpacked, n, k, device):
+    need = sparse24_w4_packed_bytes(n, k)
+    if need < 0:
+        raise SgError(f"no blocked int4 form for N = {n}, K = {k}")
+    if not isinstance(wpacked, torch.Tensor) or not wpacked.is_cuda or wpacked.dtype != torch.uint8 \
+            or wpacked.dim() != 1 or wpacked.shape[0] < need or wpacked.stride(0) != 1:
+        raise SgError(f"wpacked must be a uint8 GPU tensor [bytes] of at least {need} bytes")
+    if wpacked.device != device:
+        raise SgError(f"wpacked is on {wpacked.device}, the operands on {device}")
+
+
+def sparse24_pack_w4(wv4, wmeta, packed=None):
+    """int4 2:4 codes wv4 uint8 [N, K/4] + metadata uint8 [N, K/8] -> the
+    blocked form (uint8, sparse24_w4_packed_bytes(N, K) bytes) that
+    w4a16_sparse24_gemm_groupwise_packed takes."""
+    _gpu2d(wv4, "wv4")
+    _gpu2d(wmeta, "wmeta")
+    n, k = wv4.shape[0], wv4.shape[1] * 4
+    nbytes = sparse24_w4_packed_bytes(n, k)
+    if nbytes < 0:
+        raise SgError("sparse24_pack_w4: N must be at least 1 and K a positive multiple of 128")
+    _want(wv4, "wv4", (torch.uint8,), (n, k // 4), wv4.device)
+    _want(wmeta, "wmeta", _CODES, (n, k // 8), wv4.device)
+    if packed is None:
+        packed = torch.empty(nbytes, dtype=torch.uint8, device=wv4.device)
+    _want_w4_packed(packed, n, k, wv4.device)
+    st = lib().sg_sparse24_pack_w4(_p(wv4), _row_stride(wv4), _p(wmeta), _row_stride(wmeta), n, k, _p(packed),
+                                   _stream(wv4))
+    _check(st, "sg_sparse24_pack_w4")
+    return packed
+
+
+def w4a16_sparse24_gemm_groupwise_packed(x, wpacked, n: int, sw, out_dtype=torch.bfloat16, form: str = "y", y=None,
+                                         bias=None):
+    """The W4A16 GEMM with the weight in the blocked form of sparse24_pack_w4:
+    x bfloat16 [M, K]; wpacked uint8 [bytes]; sw fp32 [N, K/128].  Equals
+    w4a16_sparse24_gemm_groupwise on the unpacked weight bit for bit."""
+    _gpu2d(x, "x")
+    if x.dtype != torch.bfloat16:
+        raise SgError("x must be bfloat16")
+    M, K = x.shape
+    _positive(M=M, N=n, K=K)
+    if K % 128:
+        raise SgError(f"K must be a multiple of 128, got {K}")
+    _want_w4_packed(wpacked, n, K, x.device)
+    _want_scales(sw, "sw", n, K // 128, x.device)
+    y, f, ydt = _out(y, M, n, out_dtype, form, x.device)
+    bp, _ = _bias(bias, n)
+    st = lib().sg_w4a16_sparse24_gemm_groupwise_packed(M, n, K, _p(x), _row_stride(x), _p(wpacked), _p(sw),
+                                                       sw.stride(0), sw.stride(1), bp, _p(y), ydt, _row_stride(y), f,
+                                                       _stream(x))
+    _check(st, "sg_w4a16_sparse24_gemm_groupwise_packed")
     return y
 
 

@@ -44,6 +44,10 @@ __device__ __forceinline__ int sp_a_off(int g) { return 32 * (g & 1) + 8 * (g >>
 // tile uses the same swizzle with the tile row r (it depends on r mod 16
 // only): values at pk_val_off(r, g), index words at LDS_META + pk_meta_word(r, g).
 constexpr int PK_ROWS = 16, PK_CHUNK = 1280, PK_META = 1024, LDS_META = 16384;
+// Blocked int4 weight (the weight-only kernels' int4 form): one 768-byte chunk
+// per 16-row block and K block at (R * KB + kb) * 768, the 16 rows' 32 code
+// bytes row after row, then their 16 metadata bytes at PK4_META + lr * 16.
+constexpr int PK4_CHUNK = 768, PK4_META = 512;
 __device__ __host__ __forceinline__ int pk_val_off(int r, int g) { return r * 64 + 16 * (g ^ swz4(r)); }
 __device__ __host__ __forceinline__ int pk_meta_word(int r, int g) { return r * 16 + 4 * ((g + 2 * ((r >> 3) & 1)) & 3); }
 

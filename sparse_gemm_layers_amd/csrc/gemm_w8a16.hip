@@ -124,6 +124,13 @@ __device__ __forceinline__ int w8pk_code_off(int r, int g, int h) {
 __device__ __forceinline__ int w8pk_meta_off(int r, int g, int h) {
   return PK_META + pk_meta_word(r, 2 * (g & 1) + h) + 2 * (g >> 1);
 }
+// Bytes per (row block, K block) chunk of a packed weight: the gfx950 form of
+// 8-bit codes, or the blocked int4 form (codes and metadata as stored).
+template <int CODES>
+constexpr int pk_chunk() {
+  return CODES == C_I4 ? PK4_CHUNK : PK_CHUNK;
+}
+
 // The same index word from local row r's 16 packed metadata bytes m.
 __device__ __forceinline__ int w8pk_meta_half(const v4i& m, int r, int g, int h) {
   const int q = (pk_meta_word(r, 2 * (g & 1) + h) - 16 * r) >> 2;
@@ -148,7 +155,14 @@ __device__ __forceinline__ void w8_load(const W8Args& a, __amdgpu_buffer_rsrc_t 
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const uint32_t r = (uint32_t)(16 * rb + lr);
-    if constexpr (PK) {
+    if constexpr (PK && CODES == C_I4) {   // blocked: row lr's 32 code bytes at lr * 32
+      constexpr int CH = PK4_CHUNK;
+      const uint32_t c = (uint32_t)(rb * (int)(a.K >> 7) * CH);
+      const int c0 = w8_ld4(rw, c + lr * 32 + 4 * g, kb * CH);
+      const int c1 = w8_ld4(rw, c + lr * 32 + 16 + 4 * g, kb * CH);
+      o.cw[rb] = (v4i){c0, 0, c1, 0};
+      o.mw[rb] = w8_ld16(rw, c + PK4_META + 16 * lr, kb * CH);
+    } else if constexpr (PK) {
       const uint32_t c = (uint32_t)(rb * (int)(a.K >> 7) * PK_CHUNK);
       const v2i c0 = w8_ld8(rw, c + w8pk_code_off(lr, g, 0), kb * PK_CHUNK);
       const v2i c1 = w8_ld8(rw, c + w8pk_code_off(lr, g, 1), kb * PK_CHUNK);
@@ -193,8 +207,9 @@ __device__ __forceinline__ void w8_compute(const W8Ops<RB, MT>& o, int g, int lr
   for (int rb = 0; rb < RB; ++rb) {
     const v4i a0 = widen8<CODES>(o.cw[rb][0], o.cw[rb][1]);
     const v4i a1 = widen8<CODES>(o.cw[rb][2], o.cw[rb][3]);
-    const int i0 = PK ? w8pk_meta_half(o.mw[rb], lr, g, 0) : meta_half(o.mw[rb], g);
-    const int i1 = PK ? w8pk_meta_half(o.mw[rb], lr, g, 1) : meta_half(o.mw[rb], g + 4);
+    constexpr bool PKM = PK && CODES != C_I4;   // gfx950-packed index words (blocked int4: as stored)
+    const int i0 = PKM ? w8pk_meta_half(o.mw[rb], lr, g, 0) : meta_half(o.mw[rb], g);
+    const int i1 = PKM ? w8pk_meta_half(o.mw[rb], lr, g, 1) : meta_half(o.mw[rb], g + 4);
 #pragma unroll
     for (int j = 0; j < MT; ++j) {
       const v8i b0 = {o.bx[j][0][0], o.bx[j][0][1], o.bx[j][0][2], o.bx[j][0][3],
@@ -227,8 +242,8 @@ __global__ void __launch_bounds__(512) k_gemm_w8a16(W8Args a) {
   const int64_t wrows = min((int64_t)(16 * RB), a.N - n0), xrows = min((int64_t)(16 * MT), a.M - m0);
   // rows past N or M read as zero (packed: the packer's zero rows)
   const __amdgpu_buffer_rsrc_t rw =
-      PK ? w8_rsrc(a.w + (n0 / PK_ROWS) * KB * PK_CHUNK,
-                   (uint32_t)(((wrows + PK_ROWS - 1) / PK_ROWS) * KB * PK_CHUNK))
+      PK ? w8_rsrc(a.w + (n0 / PK_ROWS) * KB * pk_chunk<CODES>(),
+                   (uint32_t)(((wrows + PK_ROWS - 1) / PK_ROWS) * KB * pk_chunk<CODES>()))
          : w8_rsrc(a.w + n0 * a.ldw, (uint32_t)(wrows * a.ldw));
   const __amdgpu_buffer_rsrc_t rm = w8_rsrc(a.meta + n0 * a.ldm, (uint32_t)(wrows * a.ldm));
   const __amdgpu_buffer_rsrc_t rx = w8_rsrc(a.x + m0 * a.ldx, (uint32_t)(xrows * a.ldx * 2));
@@ -333,12 +348,20 @@ __device__ __forceinline__ void w8_dma_issue(uint8_t* sl, const W8Args& a, __amd
   }
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    if constexpr (PK) {   // the chunk as stored: codes, then metadata
-      const uint32_t c = (uint32_t)(rb * (int)(a.K >> 7) * PK_CHUNK);
-      const int cs = valid ? kb * PK_CHUNK : 0;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (w8_lds_t*)(sl + rb * D::CB), 16, c + 16 * l, cs, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (w8_lds_t*)(sl + D::MOFF + rb * 256), 4, c + PK_META + 4 * l, cs,
-                                               0, 0);
+    if constexpr (PK) {   // the chunk as stored: codes, then metadata (int4: the canonical LDS image)
+      constexpr int CH = pk_chunk<CODES>(), META = CODES == C_I4 ? PK4_META : PK_META;
+      const uint32_t c = (uint32_t)(rb * (int)(a.K >> 7) * CH);
+      const int cs = valid ? kb * CH : 0;
+      if constexpr (CODES == C_I4) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (w8_lds_t*)(sl + rb * D::CB + e * 256), 4, c + 256 * e + 4 * l,
+                                                   cs, 0, 0);
+      } else {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (w8_lds_t*)(sl + rb * D::CB), 16, c + 16 * l, cs, 0, 0);
+      }
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (w8_lds_t*)(sl + D::MOFF + rb * 256), 4, c + META + 4 * l, cs, 0,
+                                               0);
       continue;
     }
     if constexpr (CODES == C_I4) {
@@ -403,8 +426,8 @@ __global__ void __launch_bounds__(512) k_gemm_w8a16_dma(W8Args a, int q, int r) 
   }
   const int64_t wrows = min((int64_t)(16 * RB), a.N - n0);
   const __amdgpu_buffer_rsrc_t rw =
-      PK ? w8_rsrc(a.w + (n0 / PK_ROWS) * KB * PK_CHUNK,
-                   (uint32_t)(((wrows + PK_ROWS - 1) / PK_ROWS) * KB * PK_CHUNK))
+      PK ? w8_rsrc(a.w + (n0 / PK_ROWS) * KB * pk_chunk<CODES>(),
+                   (uint32_t)(((wrows + PK_ROWS - 1) / PK_ROWS) * KB * pk_chunk<CODES>()))
          : w8_rsrc(a.w + n0 * a.ldw, (uint32_t)(wrows * a.ldw));
   const __amdgpu_buffer_rsrc_t rm = w8_rsrc(a.meta + n0 * a.ldm, (uint32_t)(wrows * a.ldm));
   const __amdgpu_buffer_rsrc_t rx = w8_rsrc(a.x, (uint32_t)(a.M * a.ldx * 2));   // rows past M read zero
@@ -446,7 +469,7 @@ __global__ void __launch_bounds__(512) k_gemm_w8a16_dma(W8Args a, int q, int r) 
     for (int rb = 0; rb < RB; ++rb) {
       v4i cw;
       int i0, i1;
-      if constexpr (PK) {   // chunk offsets rebased: codes at rb * CB, metadata at MOFF + rb * 256
+      if constexpr (PK && CODES != C_I4) {   // codes at rb * CB, metadata at MOFF + rb * 256
         const uint2 c0 = w8_lds<uint2>(sl, rb * D::CB + w8pk_code_off(lr, g, 0));
         const uint2 c1 = w8_lds<uint2>(sl, rb * D::CB + w8pk_code_off(lr, g, 1));
         cw = (v4i){(int)c0.x, (int)c0.y, (int)c1.x, (int)c1.y};
@@ -614,7 +637,19 @@ __device__ __forceinline__ void w8t_issue(uint8_t* st, const W8Args& a, __amdgpu
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (w8_lds_t*)(st + L::X_OFF + s * 1024), 16,
                                              (uint32_t)(r * a.ldx * 2 + c * 16), kb * 256, 0, 0);
   }
-  if constexpr (PK) {   // 1024 code units (row block p >> 6), then 256 metadata units (row block p >> 4)
+  if constexpr (PK && CODES == C_I4) {   // blocked: the canonical LDS image from row r's place in its chunk
+    const int KB = (int)(a.K >> 7);
+    const int p = 64 * wave + l, r = p >> 1, u = (p & 1) ^ ((r >> 3) & 1);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (w8_lds_t*)(st + L::W_OFF + wave * 1024), 16,
+                                             (uint32_t)((r >> 4) * KB * PK4_CHUNK + (r & 15) * 32 + u * 16),
+                                             kb * PK4_CHUNK, 0, 0);
+    if (wave < 4) {
+      const int rm4 = 64 * wave + l;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (w8_lds_t*)(st + L::M_OFF + wave * 1024), 16,
+                                               (uint32_t)((rm4 >> 4) * KB * PK4_CHUNK + PK4_META + (rm4 & 15) * 16),
+                                               kb * PK4_CHUNK, 0, 0);
+    }
+  } else if constexpr (PK) {   // 1024 code units (row block p >> 6), then 256 metadata units (row block p >> 4)
     const int KB = (int)(a.K >> 7);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -675,7 +710,7 @@ __device__ __forceinline__ void w8t_compute(const uint8_t* st, int wn, int wm, i
     const int r = wn * 64 + 16 * i + lr;   // W row in the tile
     v4i cw;
     int i0, i1;
-    if constexpr (PK) {   // row block wn * 4 + i of the tile, local row lr
+    if constexpr (PK && CODES != C_I4) {   // row block wn * 4 + i of the tile, local row lr
       const uint32_t cb = L::W_OFF + (uint32_t)(wn * 4 + i) * 1024, mb = L::M_OFF + (uint32_t)(wn * 4 + i) * 256;
       const uint2 c0 = w8_lds<uint2>(st, cb + w8pk_code_off(lr, g, 0));
       const uint2 c1 = w8_lds<uint2>(st, cb + w8pk_code_off(lr, g, 1));
@@ -692,7 +727,7 @@ __device__ __forceinline__ void w8t_compute(const uint8_t* st, int wn, int wm, i
       const uint2 c1 = w8_lds<uint2>(st, L::W_OFF + r * 64 + (((2 + (g >> 1)) ^ f) << 4) + 8 * (g & 1));
       cw = (v4i){(int)c0.x, (int)c0.y, (int)c1.x, (int)c1.y};
     }
-    if constexpr (!PK) {   // index words: halfwords g and g + 4 of the row's 16 metadata bytes
+    if constexpr (!PK || CODES == C_I4) {   // index words: halfwords g and g + 4 of the row's 16 metadata bytes
       i0 = w8_lds<uint16_t>(st, L::M_OFF + r * 16 + 2 * g);
       i1 = w8_lds<uint16_t>(st, L::M_OFF + r * 16 + 8 + 2 * g);
     }
@@ -735,8 +770,8 @@ __global__ void __launch_bounds__(512) k_gemm_w8a16_tile(W8Args a, int tiles_m, 
   const int64_t mrows = min((int64_t)w8t::BM, a.M - m0), nrows = min((int64_t)w8t::BN, a.N - n0);
   const __amdgpu_buffer_rsrc_t rx = w8_rsrc(a.x + m0 * a.ldx, (uint32_t)(mrows * a.ldx * 2));
   const __amdgpu_buffer_rsrc_t rw =
-      PK ? w8_rsrc(a.w + (n0 / PK_ROWS) * KB * PK_CHUNK,
-                   (uint32_t)(((nrows + PK_ROWS - 1) / PK_ROWS) * KB * PK_CHUNK))
+      PK ? w8_rsrc(a.w + (n0 / PK_ROWS) * KB * pk_chunk<CODES>(),
+                   (uint32_t)(((nrows + PK_ROWS - 1) / PK_ROWS) * KB * pk_chunk<CODES>()))
          : w8_rsrc(a.w + n0 * a.ldw, (uint32_t)(nrows * a.ldw));
   const __amdgpu_buffer_rsrc_t rm = w8_rsrc(a.meta + n0 * a.ldm, (uint32_t)(nrows * a.ldm));
   const __amdgpu_buffer_rsrc_t rsw = w8_rsrc(a.sw, 0xffffffffu);
@@ -952,5 +987,35 @@ extern "C" sg_status sg_w4a16_sparse24_gemm_groupwise(int64_t M, int64_t N, int6
   a.vec_store = (ldy % 4 == 0) && aligned(y, 4 * dtype_size(y_dt));
   clear_hip_error();
   launch_w8_form<C_I4, 1>(a, y_dt == SG_BF16, form == SG_OUT_YT, stream);
+  return launch_status();
+}
+
+extern "C" sg_status sg_w4a16_sparse24_gemm_groupwise_packed(int64_t M, int64_t N, int64_t K, const uint16_t* x,
+                                                             int64_t ldx, const uint8_t* wpacked, const float* sw,
+                                                             int64_t sw_sn, int64_t sw_sk, const float* bias, void* y,
+                                                             sg_dtype y_dt, int64_t ldy, sg_form form,
+                                                             hipStream_t stream) {
+  if (!x || !wpacked || !sw || !y) return SG_ERR_NULL;
+  if (y_dt != SG_F32 && y_dt != SG_BF16) return SG_ERR_UNSUPPORTED;
+  if (form != SG_OUT_Y && form != SG_OUT_YT) return SG_ERR_UNSUPPORTED;
+  if (M <= 0 || N <= 0 || K <= 0 || K % 128 != 0 || ldx < K) return SG_ERR_SHAPE;
+  if (ldy < (form == SG_OUT_Y ? N : M)) return SG_ERR_SHAPE;
+  // 32-bit buffer offsets: 64 X rows, and the 16 row blocks' chunks of a tile
+  if (ldx >= (1LL << 24) || (K / 128) * 16 * PK4_CHUNK >= (1LL << 31) || sw_sn < 0 || sw_sk < 0) return SG_ERR_SHAPE;
+  if (((N - 1) * sw_sn + (K / 128 - 1) * sw_sk) * 4 >= (1LL << 31)) return SG_ERR_SHAPE;
+  if (cdiv(N, 16) > 0x7fffffffLL || cdiv(M, 16) > 65535) return SG_ERR_SHAPE;
+  if (!aligned(x, 16) || (ldx * 2) % 16 || !aligned(wpacked, 16) || !aligned(sw, 4) || !aligned(bias, 4) ||
+      !aligned(y, dtype_size(y_dt)))
+    return SG_ERR_ALIGN;
+  W8Args a;
+  a.M = M; a.N = N; a.K = K;
+  a.x = x; a.ldx = ldx;
+  a.w = wpacked; a.ldw = 0; a.meta = wpacked; a.ldm = 0;
+  a.sw = sw; a.sw_sn = sw_sn; a.sw_sk = sw_sk; a.gn_shift = 0;
+  a.bias = bias;
+  a.y = y; a.ldy = ldy;
+  a.vec_store = (ldy % 4 == 0) && aligned(y, 4 * dtype_size(y_dt));
+  clear_hip_error();
+  launch_w8_form<C_I4, 1, true>(a, y_dt == SG_BF16, form == SG_OUT_YT, stream);
   return launch_status();
 }

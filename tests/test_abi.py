@@ -45,7 +45,8 @@ def test_header_declares_the_entry_points():
         "sg_fp8_gemm_groupwise_batched", "sg_fp8_sparse24_gemm_groupwise_batched",
         "sg_fp8_sparse24_gemm_groupwise_packed_batched", "sg_fp8_sparse24_gemm_groupwise_packed_grouped",
         "sg_w8a16_sparse24_gemm_groupwise", "sg_w8a16_sparse24_gemm_groupwise_packed",
-        "sg_w4a16_sparse24_gemm_groupwise",
+        "sg_w4a16_sparse24_gemm_groupwise", "sg_w4a16_sparse24_gemm_groupwise_packed",
+        "sg_sparse24_w4_packed_bytes", "sg_sparse24_pack_w4",
         "sg_fp8_sparse24_gemm_packed_quant_x", "sg_probe_stream_read"])
 
 
@@ -396,6 +397,46 @@ def w8a16_packed(**kw):
 ])
 def test_w8a16_packed_validation(kw, code):
     assert w8a16_packed(**kw) == code
+
+
+def test_w4_packed_bytes():
+    lib = sg.lib()
+    assert lib.sg_sparse24_w4_packed_bytes(14336, 4096) == 896 * 32 * 768
+    assert lib.sg_sparse24_w4_packed_bytes(300, 384) == 19 * 3 * 768
+    assert lib.sg_sparse24_w4_packed_bytes(0, 128) == -1 and lib.sg_sparse24_w4_packed_bytes(10, 100) == -1
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,code", [
+    (dict(wv=None), NULL), (dict(meta=None), NULL), (dict(packed=None), NULL), (dict(K=100), SHAPE),
+    (dict(ldwv=16), SHAPE), (dict(ldwm=8), SHAPE), (dict(ldwv=40), ALIGN), (dict(ldwm=24), ALIGN),
+    (dict(packed=ODD), ALIGN), (dict(wv=ODD), ALIGN), (dict(N=0), SHAPE),
+])
+def test_pack_w4_validation(kw, code):
+    a = dict(wv=P, ldwv=32, meta=P2, ldwm=16, N=8, K=128, packed=P3)
+    a.update(kw)
+    assert sg.lib().sg_sparse24_pack_w4(a["wv"], a["ldwv"], a["meta"], a["ldwm"], a["N"], a["K"], a["packed"],
+                                        None) == code
+
+
+def w4a16_packed(**kw):
+    a = dict(M=16, N=256, K=256, x=P, ldx=256, w=P2, sw=P3, swn=2, swk=1, bias=None, y=P, ydt=1, ldy=256, form=0)
+    a.update(kw)
+    return sg.lib().sg_w4a16_sparse24_gemm_groupwise_packed(a["M"], a["N"], a["K"], a["x"], a["ldx"], a["w"],
+                                                            a["sw"], a["swn"], a["swk"], a["bias"], a["y"],
+                                                            a["ydt"], a["ldy"], a["form"], None)
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), NULL), (dict(w=None), NULL), (dict(sw=None), NULL), (dict(y=None), NULL),
+    (dict(ydt=2), UNSUP), (dict(form=2), UNSUP), (dict(K=200), SHAPE), (dict(ldx=128), SHAPE),
+    (dict(ldy=100), SHAPE), (dict(swn=-1), SHAPE), (dict(M=0), SHAPE), (dict(N=0), SHAPE),
+    (dict(M=65535 * 16 + 1), SHAPE), (dict(K=128 * 174763, ldx=128 * 174763), SHAPE),
+    (dict(x=ODD), ALIGN), (dict(ldx=260), ALIGN), (dict(w=ODD), ALIGN),
+])
+def test_w4a16_packed_validation(kw, code):
+    assert w4a16_packed(**kw) == code
 
 
 def w4a16(**kw):

@@ -293,3 +293,56 @@ def test_w4a16_from_the_gpu_weight_pipeline():
     ref, bound = oracle.w4a16_sparse24_gemm_groupwise(x.view(torch.int16).cpu().numpy().view(np.uint16), oq4, ometa,
                                                       os4, bound=True)
     assert_within_tolerance(got, ref, bound, "pipeline")
+
+
+
+# ------------------------------------------------- W4A16, blocked weight
+
+def check_w4_packed(m, n, k, out=torch.bfloat16, forms=("y", "yt"), bias=False, seed=0, rows=None):
+    """The GPU packer against the oracle's blocked layout byte for byte, then
+    the blocked-weight W4A16 GEMM against the oracle (on `rows` only, when
+    given) and bit for bit against the same call on the unpacked weight."""
+    say(f"w4a16 blocked M={m} N={n} K={k} {out} bias={bias} seed={seed}")
+    d = workloads.sparse_large(seed=seed, m=m, n=n, k=k)
+    x = up(d["x"]).to(torch.bfloat16)
+    xbits = x.view(torch.int16).cpu().numpy().view(np.uint16)
+    v32, meta = oracle.prune_compress24(d["w"])
+    q4, s4 = oracle.int4_quant_groupwise(v32, 64)
+    sel = np.arange(m) if rows is None else np.asarray(rows)
+    ref, bound = oracle.w4a16_sparse24_gemm_groupwise(xbits[sel], q4, meta, s4, bound=True)
+    b = None
+    if bias:
+        bnp = np.random.default_rng(seed + 1).standard_normal(n).astype(np.float32) * 0.1
+        ref, bound = oracle.add_bias(ref, bound, bnp)
+        b = up(bnp)
+    qg, mg, sg4 = up(q4), up(meta), up(s4)
+    wp = sg.sparse24_pack_w4(qg, mg)
+    assert np.array_equal(down(wp), oracle.pack24_w4_blocked(q4, meta))
+    for form in forms:
+        y = sg.w4a16_sparse24_gemm_groupwise_packed(x, wp, n, sg4, out_dtype=out, form=form, bias=b)
+        yc = sg.w4a16_sparse24_gemm_groupwise(x, qg, mg, sg4, out_dtype=out, form=form, bias=b)
+        iv = torch.int16 if out == torch.bfloat16 else torch.int32
+        assert torch.equal(y.view(iv), yc.view(iv)), f"form={form}"
+        got = down(y)
+        got = got.T if form == "yt" else got
+        assert got.shape == (m, n)
+        assert_within_tolerance(got[sel].astype(np.float64), ref, bound, f"form={form}")
+
+
+@pytest.mark.parametrize("m,n,k", PACKED_SHAPES)
+def test_w4a16_packed(m, n, k):
+    check_w4_packed(m, n, k, seed=90 + m + n)
+
+
+@pytest.mark.parametrize("m,n,k", [(37, 300, 384), (64, 260, 256), (300, 24580, 128)])
+def test_w4a16_packed_fp32_bias(m, n, k):
+    check_w4_packed(m, n, k, out=torch.float32, bias=True, seed=95 + m)
+
+
+def test_w4a16_packed_decode_full_size():
+    check_w4_packed(16, 14336, 4096, forms=("y",), seed=96)
+    check_w4_packed(37, 14336, 4096, forms=("y",), seed=97)
+
+
+def test_w4a16_packed_large_m_sampled_rows():
+    check_w4_packed(2048, 4096, 4096, forms=("y",), seed=98, rows=[0, 1, 127, 128, 1000, 2047])
