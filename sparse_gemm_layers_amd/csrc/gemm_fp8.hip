@@ -1943,14 +1943,13 @@ __device__ __forceinline__ void quantise_block(const v4i (&raw)[XVals<XT>::LOADS
 }
 
 template <typename XT, int RB, int MT, bool OUT_BF16, bool OUT_T>
-__device__ __forceinline__ void decode_q_body(const GemmArgs& a, uint8_t* r0, uint8_t* r1, int bx) {
+__device__ __forceinline__ void decode_q_body(const GemmArgs& a, uint8_t* r0, uint8_t* r1, int64_t n0) {
   using C = QCfg<RB>;
   constexpr int NL = XVals<XT>::LOADS;
   constexpr int ES = (int)sizeof(XT);
   const int t = threadIdx.x, l = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int g = l >> 4, lr = l & 15;
-  const int64_t n0 = (int64_t)bx * 16 * RB;
   const int KB = (int)(a.K >> 7);
   const int nt = (KB - wave + DEC_WAVES - 1) / DEC_WAVES;    // K blocks of this wave
   const int rows = (int)min((int64_t)(16 * RB), a.N - n0);
@@ -2048,12 +2047,22 @@ __device__ __forceinline__ void decode_q_body(const GemmArgs& a, uint8_t* r0, ui
 }
 #endif  // SG_DEVICE_PASS
 
-template <typename XT, int RB, int MT, bool OUT_BF16, bool OUT_T>
-__global__ void __launch_bounds__(512) k_gemm_decode_q(GemmArgs a) {
+// EVEN: the row blocks shared over the workgroups as in k_gemm_decode_dma
+// (q = R / G and r = R % G from the host).  Every workgroup quantises all of
+// X, so fewer, taller workgroups also mean less repeated quantisation.
+template <typename XT, int RB, int MT, bool OUT_BF16, bool OUT_T, bool EVEN>
+__global__ void __launch_bounds__(512) k_gemm_decode_q(GemmArgs a, int q, int r) {
 #if SG_DEVICE_PASS
   __shared__ __attribute__((aligned(1024))) uint8_t r0[QCfg<RB>::ARR];
   __shared__ __attribute__((aligned(1024))) uint8_t r1[QCfg<RB>::ARR];
-  decode_q_body<XT, RB, MT, OUT_BF16, OUT_T>(a, r0, r1, blockIdx.x);
+  int64_t n0 = (int64_t)blockIdx.x * 16 * RB;
+  if constexpr (EVEN) {
+    const int b = (int)blockIdx.x;
+    const int rb0 = b * q + min(b, r), rb1 = rb0 + q + (b < r ? 1 : 0);
+    n0 = 16 * (int64_t)rb0;
+    a.N = min(a.N, 16 * (int64_t)rb1);   // the rows past this workgroup's are another's: not loaded, not stored
+  }
+  decode_q_body<XT, RB, MT, OUT_BF16, OUT_T>(a, r0, r1, n0);
 #endif
 }
 
@@ -2148,14 +2157,29 @@ static void launch_decode_mt(const GemmArgs& a, hipStream_t st) {
 template <typename XT, int MT, bool OUT_BF16, bool OUT_T>
 static void launch_decode_q_mt(const GemmArgs& a, hipStream_t st) {
   const int64_t rows16 = cdiv(a.N, 16);
+  const int cus = cu_count();
+  if constexpr (!(MT == 4 && sizeof(XT) == 4)) {
+    // more row blocks than CUs but under 224 workgroups of four: one
+    // workgroup per CU with an even share (N = 11008, M = 16, K = 4096:
+    // 15.0 us against 23.9 us for 344 workgroups of two row blocks)
+    if (a.L == 1 && rows16 > cus && rows16 < 4 * 224 && rows16 <= 4LL * cus) {
+      const dim3 grid((unsigned)cus, 1, 1);
+      const int q = (int)(rows16 / cus), r = (int)(rows16 % cus);
+      switch (cdiv(rows16, cus)) {
+        case 2: k_gemm_decode_q<XT, 2, MT, OUT_BF16, OUT_T, true><<<grid, 512, 0, st>>>(a, q, r); return;
+        case 3: k_gemm_decode_q<XT, 3, MT, OUT_BF16, OUT_T, true><<<grid, 512, 0, st>>>(a, q, r); return;
+        default: k_gemm_decode_q<XT, 4, MT, OUT_BF16, OUT_T, true><<<grid, 512, 0, st>>>(a, q, r); return;
+      }
+    }
+  }
   if (MT == 4 && sizeof(XT) == 4)
-    k_gemm_decode_q<XT, 1, MT, OUT_BF16, OUT_T><<<dec_grid(a, rows16, 1), 512, 0, st>>>(a);
+    k_gemm_decode_q<XT, 1, MT, OUT_BF16, OUT_T, false><<<dec_grid(a, rows16, 1), 512, 0, st>>>(a, 0, 0);
   else if (rows16 >= 4 * 224)
-    k_gemm_decode_q<XT, 4, MT, OUT_BF16, OUT_T><<<dec_grid(a, rows16, 4), 512, 0, st>>>(a);
+    k_gemm_decode_q<XT, 4, MT, OUT_BF16, OUT_T, false><<<dec_grid(a, rows16, 4), 512, 0, st>>>(a, 0, 0);
   else if (rows16 >= 2 * 224)
-    k_gemm_decode_q<XT, 2, MT, OUT_BF16, OUT_T><<<dec_grid(a, rows16, 2), 512, 0, st>>>(a);
+    k_gemm_decode_q<XT, 2, MT, OUT_BF16, OUT_T, false><<<dec_grid(a, rows16, 2), 512, 0, st>>>(a, 0, 0);
   else
-    k_gemm_decode_q<XT, 1, MT, OUT_BF16, OUT_T><<<dec_grid(a, rows16, 1), 512, 0, st>>>(a);
+    k_gemm_decode_q<XT, 1, MT, OUT_BF16, OUT_T, false><<<dec_grid(a, rows16, 1), 512, 0, st>>>(a, 0, 0);
 }
 
 template <typename XT, bool OUT_BF16, bool OUT_T>

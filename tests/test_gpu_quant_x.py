@@ -73,7 +73,9 @@ def test_decode_shapes_match_quantise_then_gemm(m, n, k, form):
 
 
 SMALL = [(1, 256, 128), (5, 130, 384), (16, 512, 1024), (17, 300, 256), (32, 1000, 512), (33, 256, 640),
-         (48, 384, 128), (49, 512, 384), (64, 1024, 256), (64, 15000, 256)]
+         (48, 384, 128), (49, 512, 384), (64, 1024, 256), (64, 15000, 256),
+         # more row blocks than CUs: one workgroup per CU, 2, 3 or 4 row blocks each
+         (16, 5120, 256), (20, 11008, 256), (37, 12288, 128), (60, 13000, 256)]
 
 
 @pytest.mark.parametrize("m,n,k", SMALL)
