@@ -2151,9 +2151,10 @@ static void launch_decode_mt(const GemmArgs& a, hipStream_t st) {
 }
 
 // The fused-quantisation decode kernel: row blocks per workgroup as for the
-// other decode kernels (4, 2 or 1, keeping at least 224 workgroups); with
-// four fp32 sub-tiles only 1 (the X values of four sub-tiles fill the
-// registers).
+// LDS-streaming decode kernel (an even share over one workgroup per CU
+// between 256 and 895 row blocks, else 4, 2 or 1 keeping at least 224
+// workgroups); with four fp32 sub-tiles only 1 (the X values of four
+// sub-tiles fill the registers).
 template <typename XT, int MT, bool OUT_BF16, bool OUT_T>
 static void launch_decode_q_mt(const GemmArgs& a, hipStream_t st) {
   const int64_t rows16 = cdiv(a.N, 16);
