@@ -343,7 +343,7 @@ def rows_report():
             q, s8 = qf(v, gr=128, gc=64)
             wsets.append((q, mt, s8))
             del v
-        for dm in (16, 37):
+        for dm in (16, 37, 64):
             xb = torch.from_numpy(workloads.decode(seed=4, m=dm, n=8, k=dk)["x"]).to(DEV).to(torch.bfloat16)
             y = torch.empty((dm, dn), dtype=torch.bfloat16, device=DEV)
             ms = time_fn(lambda i: sg.w8a16_sparse24_gemm_groupwise(

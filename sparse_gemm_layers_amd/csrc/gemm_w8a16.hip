@@ -424,6 +424,12 @@ __global__ void __launch_bounds__(512) k_gemm_w8a16_dma(W8Args a, int q, int r) 
     n0 = 16 * (int64_t)rb0;
     a.N = min(a.N, 16 * (int64_t)rb1);   // the rows past this workgroup's are another's: not loaded, not stored
   }
+  if (blockIdx.y > 0) {   // grid row y: X rows and output columns from 16 MT y on
+    const int64_t m0 = (int64_t)blockIdx.y * (16 * MT);
+    a.x += m0 * a.ldx;
+    a.M -= m0;
+    a.y = static_cast<uint8_t*>(a.y) + (OUT_T ? m0 : m0 * a.ldy) * (OUT_BF16 ? 2 : 4);
+  }
   const int64_t wrows = min((int64_t)(16 * RB), a.N - n0);
   const __amdgpu_buffer_rsrc_t rw =
       PK ? w8_rsrc(a.w + (n0 / PK_ROWS) * KB * pk_chunk<CODES>(),
@@ -561,11 +567,11 @@ __global__ void __launch_bounds__(512) k_gemm_w8a16_dma(W8Args a, int q, int r) 
 // ring fits LDS and the grid keeps at least 224 workgroups (RB = 1 always
 // qualifies).
 template <int CODES, int RB, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T, bool PK>
-static bool try_w8_dma(const W8Args& a, hipStream_t st, int64_t rows16) {
+static bool try_w8_dma(const W8Args& a, hipStream_t st, int64_t rows16, unsigned gy = 1) {
   if constexpr (W8Dma<CODES, RB, MT>::FITS) {
     if (RB == 1 || rows16 >= RB * 224) {
       k_gemm_w8a16_dma<CODES, RB, MT, GRAN_N, OUT_BF16, OUT_T, false, PK>
-          <<<(unsigned)cdiv(rows16, RB), 512, 0, st>>>(a, 0, 0);
+          <<<dim3((unsigned)cdiv(rows16, RB), gy), 512, 0, st>>>(a, 0, 0);
       return true;
     }
   }
@@ -576,23 +582,23 @@ static bool try_w8_dma(const W8Args& a, hipStream_t st, int64_t rows16) {
 // workgroup per CU with an even share of ceil(R / CUs) or one fewer row
 // blocks (as the FP8 decode kernel).
 template <int CODES, int RB, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T, bool PK>
-static bool try_w8_even_rb(const W8Args& a, hipStream_t st, int64_t rows16, int cus) {
+static bool try_w8_even_rb(const W8Args& a, hipStream_t st, int64_t rows16, int cus, unsigned gy) {
   if constexpr (W8Dma<CODES, RB, MT>::FITS) {
     k_gemm_w8a16_dma<CODES, RB, MT, GRAN_N, OUT_BF16, OUT_T, true, PK>
-        <<<(unsigned)cus, 512, 0, st>>>(a, (int)(rows16 / cus), (int)(rows16 % cus));
+        <<<dim3((unsigned)cus, gy), 512, 0, st>>>(a, (int)(rows16 / cus), (int)(rows16 % cus));
     return true;
   }
   return false;
 }
 
 template <int CODES, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T, bool PK>
-static bool try_w8_even(const W8Args& a, hipStream_t st, int64_t rows16) {
+static bool try_w8_even(const W8Args& a, hipStream_t st, int64_t rows16, unsigned gy = 1) {
   const int cus = cu_count();
   if (rows16 <= cus || rows16 >= 4 * 224 || rows16 > 4LL * cus) return false;
   switch (cdiv(rows16, cus)) {
-    case 2: return try_w8_even_rb<CODES, 2, MT, GRAN_N, OUT_BF16, OUT_T, PK>(a, st, rows16, cus);
-    case 3: return try_w8_even_rb<CODES, 3, MT, GRAN_N, OUT_BF16, OUT_T, PK>(a, st, rows16, cus);
-    default: return try_w8_even_rb<CODES, 4, MT, GRAN_N, OUT_BF16, OUT_T, PK>(a, st, rows16, cus);
+    case 2: return try_w8_even_rb<CODES, 2, MT, GRAN_N, OUT_BF16, OUT_T, PK>(a, st, rows16, cus, gy);
+    case 3: return try_w8_even_rb<CODES, 3, MT, GRAN_N, OUT_BF16, OUT_T, PK>(a, st, rows16, cus, gy);
+    default: return try_w8_even_rb<CODES, 4, MT, GRAN_N, OUT_BF16, OUT_T, PK>(a, st, rows16, cus, gy);
   }
 }
 
@@ -835,7 +841,8 @@ static bool try_w8_tile(const W8Args& a, hipStream_t st) {
 
 // Row blocks per workgroup: with more 16-row blocks than CUs but under 896, an
 // even share over one workgroup per CU; otherwise the largest of 4 (2 for
-// MT > 2), 2, 1 that keeps at least 224 workgroups.  Every workgroup reads its X rows in full, so
+// MT > 2), 2, 1 that keeps at least 224 workgroups.  M <= 48 streams the
+// weight through LDS; M = 49..64 does so in two grid rows when N is wide.  Every workgroup reads its X rows in full, so
 // fewer, taller workgroups read X fewer times (measured at M = 37 and 64:
 // 1.7x faster than one row block per workgroup).
 template <int CODES, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T, bool PK>
@@ -847,6 +854,16 @@ static void launch_w8_mt(const W8Args& a, hipStream_t st) {
         try_w8_dma<CODES, 4, MT, GRAN_N, OUT_BF16, OUT_T, PK>(a, st, rows16) ||
         try_w8_dma<CODES, 2, MT, GRAN_N, OUT_BF16, OUT_T, PK>(a, st, rows16) ||
         try_w8_dma<CODES, 1, MT, GRAN_N, OUT_BF16, OUT_T, PK>(a, st, rows16))
+      return;
+  } else if (a.M <= 64 && rows16 > cu_count()) {
+    // M = 49..64 over more row blocks than CUs: two grid rows of the
+    // LDS-streaming kernel, 32 X rows each (N = 14336, K = 4096: 25.6 against
+    // 38.4 us packed on the register kernel; at N = 4096 that kernel is the
+    // faster one)
+    if (try_w8_even<CODES, 2, GRAN_N, OUT_BF16, OUT_T, PK>(a, st, rows16, 2) ||
+        try_w8_dma<CODES, 4, 2, GRAN_N, OUT_BF16, OUT_T, PK>(a, st, rows16, 2) ||
+        try_w8_dma<CODES, 2, 2, GRAN_N, OUT_BF16, OUT_T, PK>(a, st, rows16, 2) ||
+        try_w8_dma<CODES, 1, 2, GRAN_N, OUT_BF16, OUT_T, PK>(a, st, rows16, 2))
       return;
   }
   constexpr int RB4 = MT <= 2 ? 4 : 2, RB2 = 2;

@@ -51,7 +51,10 @@ def check(m, n, k, gn=128, int8=False, out=torch.bfloat16, forms=("y", "yt"), bi
 
 
 SHAPES = [(1, 256, 128), (16, 512, 256), (17, 300, 384), (37, 1000, 512), (64, 260, 256), (65, 256, 256),
-          (200, 384, 640)]
+          (200, 384, 640),
+          # M = 49..64: two grid rows of 32 X rows (the second partial), with
+          # 224+ workgroups, with the even split, and with one row block each
+          (49, 14336, 256), (64, 11008, 256), (60, 4100, 384)]
 
 
 @pytest.mark.parametrize("int8", [False, True])
@@ -198,7 +201,7 @@ def check_packed(m, n, k, gn=128, int8=False, out=torch.bfloat16, forms=("y", "y
 # the 256 x 128 tile kernel
 PACKED_SHAPES = [(1, 256, 128), (16, 512, 256), (17, 300, 384), (37, 1000, 512), (48, 13000, 256),
                  (16, 5120, 1024), (20, 11008, 512), (64, 260, 256), (65, 256, 256), (200, 384, 640),
-                 (1000, 12300, 256)]
+                 (1000, 12300, 256), (49, 14336, 256), (64, 11008, 256), (60, 4100, 384)]
 
 
 @pytest.mark.parametrize("int8", [False, True])
