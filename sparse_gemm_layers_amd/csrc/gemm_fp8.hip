@@ -1451,8 +1451,10 @@ __device__ __forceinline__ void dec_compute(const DecOps<RB, MT>& o, v4f (&acc)[
     }
 }
 
-template <bool SPARSE, bool I8, bool PACKED, int RB, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
-__global__ void __launch_bounds__(512) k_gemm_decode(GemmArgs a) {
+// EVEN: the row blocks shared over the workgroups as in k_gemm_decode_dma
+// (one problem; q = R / G and r = R % G from the host).
+template <bool SPARSE, bool I8, bool PACKED, int RB, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T, bool EVEN>
+__global__ void __launch_bounds__(512) k_gemm_decode(GemmArgs a, int q, int r) {
 #if SG_DEVICE_PASS
   constexpr int U = DEC_U;
   __shared__ __attribute__((aligned(16))) float red[DEC_WAVES][RB * MT][64][4];
@@ -1460,7 +1462,13 @@ __global__ void __launch_bounds__(512) k_gemm_decode(GemmArgs a) {
   const int t = threadIdx.x, l = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int g = l >> 4, lr = l & 15;
-  const int64_t n0 = (int64_t)blockIdx.x * 16 * RB;
+  int64_t n0 = (int64_t)blockIdx.x * 16 * RB;
+  if constexpr (EVEN) {
+    const int b = (int)blockIdx.x;
+    const int rb0 = b * q + min(b, r), rb1 = rb0 + q + (b < r ? 1 : 0);
+    n0 = 16 * (int64_t)rb0;
+    a.N = min(a.N, 16 * (int64_t)rb1);   // the rows past this workgroup's are another's: not loaded, not stored
+  }
   const int KB = (int)(a.K >> 7);
   const int nt = (KB - wave + DEC_WAVES - 1) / DEC_WAVES;   // K blocks of this wave
   const int rows = (int)min((int64_t)(16 * RB), a.N - n0);  // W rows of this workgroup that exist
@@ -2142,12 +2150,39 @@ static void launch_decode_mt(const GemmArgs& a, hipStream_t st) {
       return;
   }
   constexpr int RB4 = MT == 1 ? 4 : 1, RB2 = MT <= 2 ? 2 : 1;
+  // one problem over more row blocks than CUs but too few for 224 workgroups
+  // of the largest share: one workgroup per CU with an even share, where
+  // RB * MT <= 4 leaves the registers room
+  constexpr int RBE = MT == 1 ? 4 : 2;   // the largest even share the registers hold
+  const int cus = cu_count();
+  if (MT <= 2 && a.L == 1 && rows16 > cus && rows16 < (int64_t)RBE * 224 && rows16 <= (int64_t)RBE * cus) {
+    const dim3 grid((unsigned)cus, 1, 1);
+    const int q = (int)(rows16 / cus), r = (int)(rows16 % cus);
+    const int64_t rb = cdiv(rows16, cus);
+    if constexpr (MT == 1) {
+      if (rb == 3) {
+        k_gemm_decode<SPARSE, I8, PACKED, 3, MT, GRAN_N, OUT_BF16, OUT_T, true><<<grid, 512, 0, st>>>(a, q, r);
+        return;
+      }
+      if (rb == 4) {
+        k_gemm_decode<SPARSE, I8, PACKED, 4, MT, GRAN_N, OUT_BF16, OUT_T, true><<<grid, 512, 0, st>>>(a, q, r);
+        return;
+      }
+    }
+    if (rb == 2) {
+      k_gemm_decode<SPARSE, I8, PACKED, 2, MT, GRAN_N, OUT_BF16, OUT_T, true><<<grid, 512, 0, st>>>(a, q, r);
+      return;
+    }
+  }
   if (RB4 == 4 && rows16 >= 4 * 224)
-    k_gemm_decode<SPARSE, I8, PACKED, RB4, MT, GRAN_N, OUT_BF16, OUT_T><<<dec_grid(a, rows16, RB4), 512, 0, st>>>(a);
+    k_gemm_decode<SPARSE, I8, PACKED, RB4, MT, GRAN_N, OUT_BF16, OUT_T, false>
+        <<<dec_grid(a, rows16, RB4), 512, 0, st>>>(a, 0, 0);
   else if (RB2 == 2 && rows16 >= 2 * 224)
-    k_gemm_decode<SPARSE, I8, PACKED, RB2, MT, GRAN_N, OUT_BF16, OUT_T><<<dec_grid(a, rows16, RB2), 512, 0, st>>>(a);
+    k_gemm_decode<SPARSE, I8, PACKED, RB2, MT, GRAN_N, OUT_BF16, OUT_T, false>
+        <<<dec_grid(a, rows16, RB2), 512, 0, st>>>(a, 0, 0);
   else
-    k_gemm_decode<SPARSE, I8, PACKED, 1, MT, GRAN_N, OUT_BF16, OUT_T><<<dec_grid(a, rows16, 1), 512, 0, st>>>(a);
+    k_gemm_decode<SPARSE, I8, PACKED, 1, MT, GRAN_N, OUT_BF16, OUT_T, false>
+        <<<dec_grid(a, rows16, 1), 512, 0, st>>>(a, 0, 0);
 }
 
 // The fused-quantisation decode kernel: row blocks per workgroup as for the

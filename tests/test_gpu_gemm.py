@@ -111,6 +111,18 @@ def test_packed_decode_even_row_split(m, n, k):
     check(True, m, n, k, seed=5 + m, forms=("y", "yt"), packed=True)
 
 
+# The register decode kernel (dense, canonical 2:4, and packed with per-row W
+# scales) with the same split: 2, 3 and 4 row blocks per workgroup for one
+# 16-row X sub-tile, 2 for two (N = 13000 ends in a partial row block).
+@pytest.mark.parametrize("kind", ["dense", "sparse", "packed_rows"])
+@pytest.mark.parametrize("m,n,k", [(16, 5120, 512), (9, 11008, 256), (16, 13000, 256), (20, 5120, 256)])
+def test_register_decode_even_row_split(kind, m, n, k):
+    if kind == "packed_rows":
+        check(True, m, n, k, gn=1, seed=11 + m, packed=True)
+    else:
+        check(kind == "sparse", m, n, k, seed=13 + m + n)
+
+
 def test_deterministic_and_all_zero_operands():
     d = workloads.sparse_large(seed=8, m=300, n=512, k=512)
     xq, sx, wq, meta, sw = oracle_operands(d["x"], d["w"], 1, 128, True)
