@@ -201,7 +201,9 @@ def check_packed(m, n, k, gn=128, int8=False, out=torch.bfloat16, forms=("y", "y
 # the 256 x 128 tile kernel
 PACKED_SHAPES = [(1, 256, 128), (16, 512, 256), (17, 300, 384), (37, 1000, 512), (48, 13000, 256),
                  (16, 5120, 1024), (20, 11008, 512), (64, 260, 256), (65, 256, 256), (200, 384, 640),
-                 (1000, 12300, 256), (49, 14336, 256), (64, 11008, 256), (60, 4100, 384)]
+                 (1000, 12300, 256), (49, 14336, 256), (64, 11008, 256), (60, 4100, 384),
+                 # fewer than 16 W rows: one partial row block (the packer's zero rows)
+                 (5, 7, 128), (70, 9, 256)]
 
 
 @pytest.mark.parametrize("int8", [False, True])
