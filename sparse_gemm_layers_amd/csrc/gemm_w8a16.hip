@@ -147,7 +147,7 @@ struct W8Ops {
 };
 
 // PK: rw covers the workgroup's packed chunks (row block rb's chunk of K
-// block kb at (rb KB + kb) 1280); rm is unused.
+// block kb at (rb KB + kb) pk_chunk<CODES>()); rm is unused.
 template <int CODES, int RB, int MT, int GRAN_N, bool PK>
 __device__ __forceinline__ void w8_load(const W8Args& a, __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t rm,
                                         __amdgpu_buffer_rsrc_t rx, int64_t n0, int kb, int lr, int g,
@@ -404,8 +404,9 @@ __device__ __forceinline__ void w8_dma_issue(uint8_t* sl, const W8Args& a, __amd
 // on (at most RB); otherwise workgroup b owns row blocks RB b .. RB b + RB - 1
 // (q and r unused).  q and r come from the host, so that no division here
 // turns the buffer descriptors into vector values.
-// PK: the weight in the packed gfx950 form, each chunk copied into the ring
-// as stored (codes at rb * CB, metadata at MOFF + rb * 256).
+// PK: the weight in its packed form (gfx950 chunks of 8-bit codes, blocked
+// int4 chunks), each chunk copied into the ring as stored (codes at rb * CB,
+// metadata at MOFF + rb * 256).
 template <int CODES, int RB, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T, bool EVEN, bool PK>
 __global__ void __launch_bounds__(512) k_gemm_w8a16_dma(W8Args a, int q, int r) {
 #if SG_DEVICE_PASS
@@ -841,10 +842,11 @@ static bool try_w8_tile(const W8Args& a, hipStream_t st) {
 
 // Row blocks per workgroup: with more 16-row blocks than CUs but under 896, an
 // even share over one workgroup per CU; otherwise the largest of 4 (2 for
-// MT > 2), 2, 1 that keeps at least 224 workgroups.  M <= 48 streams the
-// weight through LDS; M = 49..64 does so in two grid rows when N is wide.  Every workgroup reads its X rows in full, so
-// fewer, taller workgroups read X fewer times (measured at M = 37 and 64:
-// 1.7x faster than one row block per workgroup).
+// MT > 2), 2, 1 that keeps at least 224 workgroups.  Every workgroup reads
+// its X rows in full, so fewer, taller workgroups read X fewer times
+// (measured at M = 37 and 64: 1.7x faster than one row block per workgroup).
+// M <= 48 streams the weight through LDS; M = 49..64 does so in two grid
+// rows when N is wide.
 template <int CODES, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T, bool PK>
 static void launch_w8_mt(const W8Args& a, hipStream_t st) {
   const int64_t rows16 = cdiv(a.N, 16);
