@@ -2151,15 +2151,17 @@ static void launch_decode_mt(const GemmArgs& a, hipStream_t st) {
   }
   constexpr int RB4 = MT == 1 ? 4 : 1, RB2 = MT <= 2 ? 2 : 1;
   // one problem over more row blocks than CUs but too few for 224 workgroups
-  // of the largest share: one workgroup per CU with an even share, where
-  // RB * MT <= 4 leaves the registers room
-  constexpr int RBE = MT == 1 ? 4 : 2;   // the largest even share the registers hold
+  // of the largest share: one workgroup per CU with an even share of up to 4
+  // row blocks (2 with four X sub-tiles); at most 98 of the 256 registers a
+  // lane may hold at this occupancy were in use with 4 row blocks and one
+  // sub-tile, 86 with 2 and two
+  constexpr int RBE = MT <= 3 ? 4 : 2;
   const int cus = cu_count();
-  if (MT <= 2 && a.L == 1 && rows16 > cus && rows16 < (int64_t)RBE * 224 && rows16 <= (int64_t)RBE * cus) {
+  if (a.L == 1 && rows16 > cus && rows16 < (int64_t)RBE * 224 && rows16 <= (int64_t)RBE * cus) {
     const dim3 grid((unsigned)cus, 1, 1);
     const int q = (int)(rows16 / cus), r = (int)(rows16 % cus);
     const int64_t rb = cdiv(rows16, cus);
-    if constexpr (MT == 1) {
+    if constexpr (RBE == 4) {
       if (rb == 3) {
         k_gemm_decode<SPARSE, I8, PACKED, 3, MT, GRAN_N, OUT_BF16, OUT_T, true><<<grid, 512, 0, st>>>(a, q, r);
         return;
@@ -2169,10 +2171,8 @@ static void launch_decode_mt(const GemmArgs& a, hipStream_t st) {
         return;
       }
     }
-    if (rb == 2) {
-      k_gemm_decode<SPARSE, I8, PACKED, 2, MT, GRAN_N, OUT_BF16, OUT_T, true><<<grid, 512, 0, st>>>(a, q, r);
-      return;
-    }
+    k_gemm_decode<SPARSE, I8, PACKED, 2, MT, GRAN_N, OUT_BF16, OUT_T, true><<<grid, 512, 0, st>>>(a, q, r);
+    return;
   }
   if (RB4 == 4 && rows16 >= 4 * 224)
     k_gemm_decode<SPARSE, I8, PACKED, RB4, MT, GRAN_N, OUT_BF16, OUT_T, false>

@@ -112,10 +112,11 @@ def test_packed_decode_even_row_split(m, n, k):
 
 
 # The register decode kernel (dense, canonical 2:4, and packed with per-row W
-# scales) with the same split: 2, 3 and 4 row blocks per workgroup for one
-# 16-row X sub-tile, 2 for two (N = 13000 ends in a partial row block).
+# scales) with the same split: 2, 3 and 4 row blocks per workgroup for up to
+# three 16-row X sub-tiles, 2 for four (N = 13000 ends in a partial row block).
 @pytest.mark.parametrize("kind", ["dense", "sparse", "packed_rows"])
-@pytest.mark.parametrize("m,n,k", [(16, 5120, 512), (9, 11008, 256), (16, 13000, 256), (20, 5120, 256)])
+@pytest.mark.parametrize("m,n,k", [(16, 5120, 512), (9, 11008, 256), (16, 13000, 256), (20, 5120, 256),
+                                   (20, 11008, 256), (37, 12288, 128), (64, 5120, 256)])
 def test_register_decode_even_row_split(kind, m, n, k):
     if kind == "packed_rows":
         check(True, m, n, k, gn=1, seed=11 + m, packed=True)
