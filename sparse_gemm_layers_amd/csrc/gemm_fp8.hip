@@ -2109,8 +2109,9 @@ static bool try_decode_dma(const GemmArgs& a, hipStream_t st, int64_t rows16) {
 }
 
 // Row blocks per workgroup: the largest of 4, 2, 1 that keeps at least 224
-// workgroups and whose operands fit (LDS ring of the streaming kernel, or
-// RB * MT <= 4 for the registers of k_gemm_decode).  Packed 2:4 weights with
+// workgroups and whose operands fit (LDS ring of the streaming kernel; for
+// the registers of k_gemm_decode up to 4 with three X sub-tiles, 2 with
+// four).  Packed 2:4 weights with
 // 128-row W scales take the LDS-streaming kernel when one of its rings fits.
 // One problem with more row blocks than CUs but too few for 224 workgroups of
 // four: one workgroup per CU, each with ceil(R / CUs) or one fewer row blocks
@@ -2149,7 +2150,7 @@ static void launch_decode_mt(const GemmArgs& a, hipStream_t st) {
         try_decode_dma<I8, 1, MT, GRAN_N, OUT_BF16, OUT_T>(a, st, rows16))
       return;
   }
-  constexpr int RB4 = MT == 1 ? 4 : 1, RB2 = MT <= 2 ? 2 : 1;
+  constexpr int RB4 = MT <= 3 ? 4 : 1, RB2 = 2;
   // one problem over more row blocks than CUs but too few for 224 workgroups
   // of the largest share: one workgroup per CU with an even share of up to 4
   // row blocks (2 with four X sub-tiles); at most 98 of the 256 registers a
