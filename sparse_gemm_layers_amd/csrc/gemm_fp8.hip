@@ -1800,6 +1800,13 @@ __global__ void __launch_bounds__(512) k_gemm_decode_dma(GemmArgs a, int q, int 
     n0 = 16 * (int64_t)rb0;
     a.N = min(a.N, 16 * (int64_t)rb1);   // the rows past this workgroup's are another's: not loaded, not stored
   }
+  if (blockIdx.y > 0) {   // grid row y (one problem, M <= 64): X rows, X scales and outputs from 16 MT y on
+    const int64_t m0 = (int64_t)blockIdx.y * 16 * MT;
+    a.x += m0 * a.ldx;
+    a.sx += (m0 >> a.gm_shift) * a.sx_sm;
+    a.M -= m0;
+    a.y = static_cast<uint8_t*>(a.y) + (OUT_T ? m0 : m0 * a.ldy) * (OUT_BF16 ? 2 : 4);
+  }
   decode_dma_body<I8, RB, MT, GRAN_N, OUT_BF16, OUT_T>(a, r0, r1, n0);
 #endif
 }
@@ -2143,6 +2150,14 @@ static bool launch_decode_even(const GemmArgs& a, hipStream_t st, int64_t rows16
 template <bool SPARSE, bool I8, bool PACKED, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
 static void launch_decode_mt(const GemmArgs& a, hipStream_t st) {
   const int64_t rows16 = cdiv(a.N, 16);
+  if constexpr (SPARSE && PACKED && GRAN_N == 128 && MT == 4) {
+    // M = 49..64 over no more row blocks than CUs: two grid rows of 32 X rows
+    // (the four-sub-tile ring keeps X in registers, and ran slower)
+    if (a.L == 1 && rows16 <= cu_count()) {
+      k_gemm_decode_dma<I8, 1, 2, GRAN_N, OUT_BF16, OUT_T, false><<<dim3((unsigned)rows16, 2, 1), 512, 0, st>>>(a, 0, 0);
+      return;
+    }
+  }
   if constexpr (SPARSE && PACKED && GRAN_N == 128) {
     if (launch_decode_even<I8, MT, GRAN_N, OUT_BF16, OUT_T>(a, st, rows16) ||
         try_decode_dma<I8, 4, MT, GRAN_N, OUT_BF16, OUT_T>(a, st, rows16) ||

@@ -111,6 +111,15 @@ def test_packed_decode_even_row_split(m, n, k):
     check(True, m, n, k, seed=5 + m, forms=("y", "yt"), packed=True)
 
 
+# Packed decode at M = 49..64 over no more row blocks than CUs: two grid rows
+# of 32 X rows (the second 17..32 rows), per-row and 128-row X scales.
+@pytest.mark.parametrize("m,n,k,gm", [(64, 4096, 512, 1), (50, 1000, 256, 1), (64, 300, 384, 128),
+                                      (49, 4096, 1024, 128)])
+def test_packed_decode_two_grid_rows(m, n, k, gm):
+    check(True, m, n, k, gm=gm, seed=21 + m + n, forms=("y", "yt"), packed=True)
+    check(True, m, n, k, gm=gm, seed=22 + m + n, forms=("y",), packed=True, out_dtype=torch.float32)
+
+
 # The register decode kernel (dense, canonical 2:4, and packed with per-row W
 # scales) with the same split: 2, 3 and 4 row blocks per workgroup for up to
 # three 16-row X sub-tiles, 2 for four (N = 13000 ends in a partial row block).
