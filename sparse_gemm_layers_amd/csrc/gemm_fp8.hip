@@ -2077,6 +2077,12 @@ __global__ void __launch_bounds__(512) k_gemm_decode_q(GemmArgs a, int q, int r)
     n0 = 16 * (int64_t)rb0;
     a.N = min(a.N, 16 * (int64_t)rb1);   // the rows past this workgroup's are another's: not loaded, not stored
   }
+  if (blockIdx.y > 0) {   // grid row y (one problem, M <= 64): X rows and outputs from 16 MT y on
+    const int64_t m0 = (int64_t)blockIdx.y * 16 * MT;
+    a.x += m0 * a.ldx * (int64_t)sizeof(XT);
+    a.M -= m0;
+    a.y = static_cast<uint8_t*>(a.y) + (OUT_T ? m0 : m0 * a.ldy) * (OUT_BF16 ? 2 : 4);
+  }
   decode_q_body<XT, RB, MT, OUT_BF16, OUT_T>(a, r0, r1, n0);
 #endif
 }
@@ -2204,10 +2210,12 @@ static void launch_decode_mt(const GemmArgs& a, hipStream_t st) {
 // The fused-quantisation decode kernel: row blocks per workgroup as for the
 // LDS-streaming decode kernel (an even share over one workgroup per CU
 // between 256 and 895 row blocks, else 4, 2 or 1 keeping at least 224
-// workgroups); with four fp32 sub-tiles only 1 (the X values of four
-// sub-tiles fill the registers).
+// workgroups); gy grid rows of 16 MT X rows each.  Four fp32 sub-tiles would
+// take one row block per workgroup (their X values fill the registers), so
+// fp32 X beyond 48 rows runs as two grid rows of two sub-tiles (M = 64,
+// N = 14336, K = 4096: 49.6 against 171 us).
 template <typename XT, int MT, bool OUT_BF16, bool OUT_T>
-static void launch_decode_q_mt(const GemmArgs& a, hipStream_t st) {
+static void launch_decode_q_mt(const GemmArgs& a, hipStream_t st, unsigned gy = 1) {
   const int64_t rows16 = cdiv(a.N, 16);
   const int cus = cu_count();
   if constexpr (!(MT == 4 && sizeof(XT) == 4)) {
@@ -2215,7 +2223,7 @@ static void launch_decode_q_mt(const GemmArgs& a, hipStream_t st) {
     // workgroup per CU with an even share (N = 11008, M = 16, K = 4096:
     // 15.0 us against 23.9 us for 344 workgroups of two row blocks)
     if (a.L == 1 && rows16 > cus && rows16 < 4 * 224 && rows16 <= 4LL * cus) {
-      const dim3 grid((unsigned)cus, 1, 1);
+      const dim3 grid((unsigned)cus, gy, 1);
       const int q = (int)(rows16 / cus), r = (int)(rows16 % cus);
       switch (cdiv(rows16, cus)) {
         case 2: k_gemm_decode_q<XT, 2, MT, OUT_BF16, OUT_T, true><<<grid, 512, 0, st>>>(a, q, r); return;
@@ -2224,14 +2232,15 @@ static void launch_decode_q_mt(const GemmArgs& a, hipStream_t st) {
       }
     }
   }
+  auto grid = [&](int rb) { return dim3((unsigned)cdiv(rows16, rb), gy, (unsigned)a.L); };
   if (MT == 4 && sizeof(XT) == 4)
-    k_gemm_decode_q<XT, 1, MT, OUT_BF16, OUT_T, false><<<dec_grid(a, rows16, 1), 512, 0, st>>>(a, 0, 0);
+    k_gemm_decode_q<XT, 1, MT, OUT_BF16, OUT_T, false><<<grid(1), 512, 0, st>>>(a, 0, 0);
   else if (rows16 >= 4 * 224)
-    k_gemm_decode_q<XT, 4, MT, OUT_BF16, OUT_T, false><<<dec_grid(a, rows16, 4), 512, 0, st>>>(a, 0, 0);
+    k_gemm_decode_q<XT, 4, MT, OUT_BF16, OUT_T, false><<<grid(4), 512, 0, st>>>(a, 0, 0);
   else if (rows16 >= 2 * 224)
-    k_gemm_decode_q<XT, 2, MT, OUT_BF16, OUT_T, false><<<dec_grid(a, rows16, 2), 512, 0, st>>>(a, 0, 0);
+    k_gemm_decode_q<XT, 2, MT, OUT_BF16, OUT_T, false><<<grid(2), 512, 0, st>>>(a, 0, 0);
   else
-    k_gemm_decode_q<XT, 1, MT, OUT_BF16, OUT_T, false><<<dec_grid(a, rows16, 1), 512, 0, st>>>(a, 0, 0);
+    k_gemm_decode_q<XT, 1, MT, OUT_BF16, OUT_T, false><<<grid(1), 512, 0, st>>>(a, 0, 0);
 }
 
 template <typename XT, bool OUT_BF16, bool OUT_T>
@@ -2239,6 +2248,9 @@ static void launch_decode_q(const GemmArgs& a, hipStream_t st) {
   if (a.M <= 16) launch_decode_q_mt<XT, 1, OUT_BF16, OUT_T>(a, st);
   else if (a.M <= 32) launch_decode_q_mt<XT, 2, OUT_BF16, OUT_T>(a, st);
   else if (a.M <= 48) launch_decode_q_mt<XT, 3, OUT_BF16, OUT_T>(a, st);
+  // four fp32 sub-tiles fill the registers at one row block per workgroup:
+  // two grid rows of 32 X rows instead (each workgroup quantises half of X)
+  else if (sizeof(XT) == 4 && a.L == 1) launch_decode_q_mt<XT, 2, OUT_BF16, OUT_T>(a, st, 2);
   else launch_decode_q_mt<XT, 4, OUT_BF16, OUT_T>(a, st);
 }
 
