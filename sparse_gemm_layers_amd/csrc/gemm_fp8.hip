@@ -1469,6 +1469,13 @@ __global__ void __launch_bounds__(512) k_gemm_decode(GemmArgs a, int q, int r) {
     n0 = 16 * (int64_t)rb0;
     a.N = min(a.N, 16 * (int64_t)rb1);   // the rows past this workgroup's are another's: not loaded, not stored
   }
+  if (blockIdx.y > 0) {   // grid row y (one problem, M <= 64): X rows, X scales and outputs from 16 MT y on
+    const int64_t m0 = (int64_t)blockIdx.y * 16 * MT;
+    a.x += m0 * a.ldx;
+    a.sx += (m0 >> a.gm_shift) * a.sx_sm;
+    a.M -= m0;
+    a.y = static_cast<uint8_t*>(a.y) + (OUT_T ? m0 : m0 * a.ldy) * (OUT_BF16 ? 2 : 4);
+  }
   const int KB = (int)(a.K >> 7);
   const int nt = (KB - wave + DEC_WAVES - 1) / DEC_WAVES;   // K blocks of this wave
   const int rows = (int)min((int64_t)(16 * RB), a.N - n0);  // W rows of this workgroup that exist
@@ -2172,6 +2179,16 @@ static void launch_decode_mt(const GemmArgs& a, hipStream_t st) {
       return;
   }
   constexpr int RB4 = MT <= 3 ? 4 : 1, RB2 = 2;
+  if constexpr (MT == 4) {
+    // M = 49..64 over at most half as many row blocks as CUs: two grid rows
+    // of 32 X rows (K = 4096, dense: N = 1792 8.3 against 12.6 us; at
+    // N = 4096, 256 row blocks, slower: 14.8 against 13.7 us)
+    if (a.L == 1 && 2 * rows16 <= cu_count()) {
+      k_gemm_decode<SPARSE, I8, PACKED, 1, 2, GRAN_N, OUT_BF16, OUT_T, false>
+          <<<dim3((unsigned)rows16, 2, 1), 512, 0, st>>>(a, 0, 0);
+      return;
+    }
+  }
   // one problem over more row blocks than CUs but too few for 224 workgroups
   // of the largest share: one workgroup per CU with an even share of up to 4
   // row blocks (2 with four X sub-tiles); at most 98 of the 256 registers a

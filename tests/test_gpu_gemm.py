@@ -120,6 +120,15 @@ def test_packed_decode_two_grid_rows(m, n, k, gm):
     check(True, m, n, k, gm=gm, seed=22 + m + n, forms=("y",), packed=True, out_dtype=torch.float32)
 
 
+@pytest.mark.parametrize("kind", ["dense", "sparse", "packed_rows"])
+@pytest.mark.parametrize("m,n,k,gm", [(64, 4096, 512, 1), (50, 1000, 256, 128)])
+def test_register_decode_two_grid_rows(kind, m, n, k, gm):
+    if kind == "packed_rows":
+        check(True, m, n, k, gm=gm, gn=1, seed=31 + m, packed=True)
+    else:
+        check(kind == "sparse", m, n, k, gm=gm, seed=33 + m + n)
+
+
 # The register decode kernel (dense, canonical 2:4, and packed with per-row W
 # scales) with the same split: 2, 3 and 4 row blocks per workgroup for up to
 # three 16-row X sub-tiles, 2 for four (N = 13000 ends in a partial row block).
