@@ -857,11 +857,11 @@ static void launch_w8_mt(const W8Args& a, hipStream_t st) {
         try_w8_dma<CODES, 2, MT, GRAN_N, OUT_BF16, OUT_T, PK>(a, st, rows16) ||
         try_w8_dma<CODES, 1, MT, GRAN_N, OUT_BF16, OUT_T, PK>(a, st, rows16))
       return;
-  } else if (a.M <= 64 && rows16 > cu_count()) {
-    // M = 49..64 over more row blocks than CUs: two grid rows of the
-    // LDS-streaming kernel, 32 X rows each (N = 14336, K = 4096: 25.6 against
-    // 38.4 us packed on the register kernel; at N = 4096 that kernel is the
-    // faster one)
+  } else if (a.M <= 64 && (rows16 > cu_count() || 2 * rows16 <= cu_count())) {
+    // M = 49..64 over more row blocks than CUs, or at most half as many: two
+    // grid rows of the LDS-streaming kernel, 32 X rows each (N = 14336,
+    // K = 4096: 25.6 against 38.4 us packed on the register kernel; at
+    // N = 4096 that kernel is the faster one)
     if (try_w8_even<CODES, 2, GRAN_N, OUT_BF16, OUT_T, PK>(a, st, rows16, 2) ||
         try_w8_dma<CODES, 4, 2, GRAN_N, OUT_BF16, OUT_T, PK>(a, st, rows16, 2) ||
         try_w8_dma<CODES, 2, 2, GRAN_N, OUT_BF16, OUT_T, PK>(a, st, rows16, 2) ||
