@@ -2163,11 +2163,15 @@ static bool launch_decode_even(const GemmArgs& a, hipStream_t st, int64_t rows16
 template <bool SPARSE, bool I8, bool PACKED, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T>
 static void launch_decode_mt(const GemmArgs& a, hipStream_t st) {
   const int64_t rows16 = cdiv(a.N, 16);
-  if constexpr (SPARSE && PACKED && GRAN_N == 128 && MT == 4) {
-    // M = 49..64 over no more row blocks than CUs: two grid rows of 32 X rows
-    // (the four-sub-tile ring keeps X in registers, and ran slower)
-    if (a.L == 1 && rows16 <= cu_count()) {
-      k_gemm_decode_dma<I8, 1, 2, GRAN_N, OUT_BF16, OUT_T, false><<<dim3((unsigned)rows16, 2, 1), 512, 0, st>>>(a, 0, 0);
+  if constexpr (SPARSE && PACKED && GRAN_N == 128 && MT >= 2) {
+    // Two grid rows of ceil(MT / 2) sub-tiles: at M = 49..64 over no more row
+    // blocks than CUs (the four-sub-tile ring keeps X in registers, and ran
+    // slower), and at M = 17..48 over at most half as many row blocks as CUs
+    // (the other half of the CUs would idle)
+    constexpr int MH = (MT + 1) / 2;
+    if (a.L == 1 && (MT == 4 ? rows16 <= cu_count() : 2 * rows16 <= cu_count())) {
+      k_gemm_decode_dma<I8, 1, MH, GRAN_N, OUT_BF16, OUT_T, false>
+          <<<dim3((unsigned)rows16, (unsigned)cdiv(a.M, 16 * MH), 1), 512, 0, st>>>(a, 0, 0);
       return;
     }
   }

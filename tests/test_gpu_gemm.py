@@ -114,7 +114,9 @@ def test_packed_decode_even_row_split(m, n, k):
 # Packed decode at M = 49..64 over no more row blocks than CUs: two grid rows
 # of 32 X rows (the second 17..32 rows), per-row and 128-row X scales.
 @pytest.mark.parametrize("m,n,k,gm", [(64, 4096, 512, 1), (50, 1000, 256, 1), (64, 300, 384, 128),
-                                      (49, 4096, 1024, 128)])
+                                      (49, 4096, 1024, 128),
+                                      # M = 17..48 over at most 128 row blocks: two rows of 2 or 1 sub-tiles
+                                      (37, 1792, 512, 1), (20, 1000, 256, 1), (40, 300, 384, 128)])
 def test_packed_decode_two_grid_rows(m, n, k, gm):
     check(True, m, n, k, gm=gm, seed=21 + m + n, forms=("y", "yt"), packed=True)
     check(True, m, n, k, gm=gm, seed=22 + m + n, forms=("y",), packed=True, out_dtype=torch.float32)
