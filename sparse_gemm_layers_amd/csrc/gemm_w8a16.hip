@@ -851,6 +851,14 @@ template <int CODES, int MT, int GRAN_N, bool OUT_BF16, bool OUT_T, bool PK>
 static void launch_w8_mt(const W8Args& a, hipStream_t st) {
   const int64_t rows16 = cdiv(a.N, 16);
   const unsigned gy = (unsigned)cdiv(a.M, 16 * MT);
+  if constexpr (MT >= 2 && MT <= 3) {
+    // at most half as many row blocks as CUs: two grid rows of ceil(MT / 2)
+    // sub-tiles, so that the other half of the CUs has work
+    constexpr int MH = (MT + 1) / 2;
+    if (2 * rows16 <= cu_count() &&
+        try_w8_dma<CODES, 1, MH, GRAN_N, OUT_BF16, OUT_T, PK>(a, st, rows16, (unsigned)cdiv(a.M, 16 * MH)))
+      return;
+  }
   if constexpr (MT <= 3) {   // LDS streaming, one workgroup per RB row blocks and all of M
     if (try_w8_even<CODES, MT, GRAN_N, OUT_BF16, OUT_T, PK>(a, st, rows16) ||
         try_w8_dma<CODES, 4, MT, GRAN_N, OUT_BF16, OUT_T, PK>(a, st, rows16) ||

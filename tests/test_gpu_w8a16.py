@@ -54,7 +54,9 @@ SHAPES = [(1, 256, 128), (16, 512, 256), (17, 300, 384), (37, 1000, 512), (64, 2
           (200, 384, 640),
           # M = 49..64: two grid rows of 32 X rows (the second partial), with
           # 224+ workgroups, with the even split, and with one row block each
-          (49, 14336, 256), (64, 11008, 256), (60, 4100, 384), (64, 1792, 256)]
+          (49, 14336, 256), (64, 11008, 256), (60, 4100, 384), (64, 1792, 256),
+          # M = 17..48 over at most 128 row blocks: two grid rows of 2 or 1 sub-tiles
+          (37, 1792, 384), (20, 1000, 256)]
 
 
 @pytest.mark.parametrize("int8", [False, True])
