@@ -2183,13 +2183,14 @@ static void launch_decode_mt(const GemmArgs& a, hipStream_t st) {
       return;
   }
   constexpr int RB4 = MT <= 3 ? 4 : 1, RB2 = 2;
-  if constexpr (MT == 4) {
-    // M = 49..64 over at most half as many row blocks as CUs: two grid rows
-    // of 32 X rows (K = 4096, dense: N = 1792 8.3 against 12.6 us; at
-    // N = 4096, 256 row blocks, slower: 14.8 against 13.7 us)
+  if constexpr (MT >= 2) {
+    // over at most half as many row blocks as CUs: two grid rows of
+    // ceil(MT / 2) sub-tiles (K = 4096, dense, M = 64: N = 1792 8.3 against
+    // 12.6 us; at N = 4096, 256 row blocks, slower: 14.8 against 13.7 us)
+    constexpr int MH = (MT + 1) / 2;
     if (a.L == 1 && 2 * rows16 <= cu_count()) {
-      k_gemm_decode<SPARSE, I8, PACKED, 1, 2, GRAN_N, OUT_BF16, OUT_T, false>
-          <<<dim3((unsigned)rows16, 2, 1), 512, 0, st>>>(a, 0, 0);
+      k_gemm_decode<SPARSE, I8, PACKED, 1, MH, GRAN_N, OUT_BF16, OUT_T, false>
+          <<<dim3((unsigned)rows16, (unsigned)cdiv(a.M, 16 * MH), 1), 512, 0, st>>>(a, 0, 0);
       return;
     }
   }

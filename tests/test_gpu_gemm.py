@@ -123,7 +123,8 @@ def test_packed_decode_two_grid_rows(m, n, k, gm):
 
 
 @pytest.mark.parametrize("kind", ["dense", "sparse", "packed_rows"])
-@pytest.mark.parametrize("m,n,k,gm", [(64, 4096, 512, 1), (50, 1000, 256, 128)])
+@pytest.mark.parametrize("m,n,k,gm", [(64, 4096, 512, 1), (50, 1000, 256, 128), (37, 1792, 256, 1),
+                                      (20, 1000, 384, 128)])
 def test_register_decode_two_grid_rows(kind, m, n, k, gm):
     if kind == "packed_rows":
         check(True, m, n, k, gm=gm, gn=1, seed=31 + m, packed=True)
